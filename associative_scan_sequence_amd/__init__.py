@@ -1,0 +1,14 @@
+"""MI355X-native masked second-order Higher-order Linear Attention.
+
+The computation lives in libhla.so (hand-written HIP kernels for gfx950,
+C ABI in include/hla.h); this package is its thin Python binding:
+
+* :func:`forward_chunked` -- chunk-parallel masked forward (``hla_forward_chunked``)
+* :func:`decode_step` -- one streaming token per state (``hla_decode_step``)
+* :func:`state_compose` -- masked semidirect-product composition (``hla_state_compose``)
+"""
+from ._binding import (EXPORTED, LIB_PATH, HlaError, State, decode_step, forward_chunked, load,
+                       state_compose, workspace_size)
+
+__all__ = ["EXPORTED", "LIB_PATH", "HlaError", "State", "decode_step", "forward_chunked", "load",
+           "state_compose", "workspace_size"]

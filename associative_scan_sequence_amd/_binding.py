@@ -1,0 +1,248 @@
+"""ctypes binding of libhla.so (include/hla.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device addresses and the current HIP stream are passed to
+the C ABI, and a non-OK status is raised as :class:`HlaError`.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback, and
+a missing library raises at load time.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhla.so")
+
+HLA_F32, HLA_BF16 = 0, 1
+STATUS = {0: "HLA_OK", 1: "HLA_ERR_INVALID_ARGUMENT", 2: "HLA_ERR_UNSUPPORTED",
+          3: "HLA_ERR_ALIGNMENT", 4: "HLA_ERR_WORKSPACE", 5: "HLA_ERR_DEVICE"}
+EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_decode_step",
+            "hla_state_compose", "hla_status_string", "hla_last_error")
+
+
+class CState(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in ("S", "C", "m", "G", "h", "rho")]
+
+
+class CParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("gamma", ctypes.POINTER(ctypes.c_float)),
+                ("ridge", ctypes.c_float), ("normalize", ctypes.c_int32)]
+
+
+class HlaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {detail}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libhla.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m associative_scan_sequence_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    pp, ps = ctypes.POINTER(CParams), ctypes.POINTER(CState)
+    lib.hla_forward_workspace_size.argtypes = [pp]
+    lib.hla_forward_workspace_size.restype = sz
+    lib.hla_forward_chunked.argtypes = [pp, vp, vp, vp, vp, vp, ps, ps, vp, sz, vp]
+    lib.hla_forward_chunked.restype = ctypes.c_int
+    lib.hla_decode_step.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
+    lib.hla_decode_step.restype = ctypes.c_int
+    lib.hla_state_compose.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ps, ps, ps, vp]
+    lib.hla_state_compose.restype = ctypes.c_int
+    lib.hla_status_string.argtypes = [ctypes.c_int]
+    lib.hla_status_string.restype = ctypes.c_char_p
+    lib.hla_last_error.argtypes = []
+    lib.hla_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise HlaError(status, load().hla_last_error().decode())
+
+
+@dataclass
+class State:
+    """Segment summary for B*H heads, fp32 device tensors:
+    S [N,d,d], C [N,d,dv], m [N,d], G [N,d,dv], h [N,d], rho [N] (or None)."""
+    S: torch.Tensor
+    C: torch.Tensor
+    m: torch.Tensor
+    G: torch.Tensor
+    h: torch.Tensor
+    rho: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def empty(N: int, d: int, dv: int, device, with_rho: bool = True) -> "State":
+        f = dict(dtype=torch.float32, device=device)
+        return State(torch.empty(N, d, d, **f), torch.empty(N, d, dv, **f), torch.empty(N, d, **f),
+                     torch.empty(N, d, dv, **f), torch.empty(N, d, **f),
+                     torch.empty(N, **f) if with_rho else None)
+
+    @staticmethod
+    def zeros(N: int, d: int, dv: int, device) -> "State":
+        s = State.empty(N, d, dv, device)
+        for t in (s.S, s.C, s.m, s.G, s.h):
+            t.zero_()
+        s.rho.fill_(1.0)
+        return s
+
+    def tensors(self):
+        return (self.S, self.C, self.m, self.G, self.h, self.rho)
+
+    def c(self) -> CState:
+        for t in self.tensors():
+            if t is not None:
+                _need(t, "state", (torch.float32,))
+        return CState(*[t.data_ptr() if t is not None else None for t in self.tensors()])
+
+    def clone(self) -> "State":
+        return State(*[t.clone() if t is not None else None for t in self.tensors()])
+
+
+def _need(t: torch.Tensor, name: str, dtypes):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _params(B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize):
+    if dtype == torch.bfloat16:
+        dt = HLA_BF16
+    elif dtype == torch.float32:
+        dt = HLA_F32
+    else:
+        raise TypeError(f"q/k/v dtype must be bfloat16 or float32, got {dtype}")
+    garr = None
+    keep = None
+    if gamma is not None:
+        g = [float(x) for x in (gamma if isinstance(gamma, Sequence) or hasattr(gamma, "__len__") else [gamma] * H)]
+        if len(g) == 1 and H > 1:
+            g = g * H
+        if len(g) != H:
+            raise ValueError(f"gamma has {len(g)} entries for H={H}")
+        keep = (ctypes.c_float * H)(*g)
+        garr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    p = CParams(B, H, n, d, dv, int(chunk), dt, garr, float(ridge), int(bool(normalize)))
+    return p, keep
+
+
+def workspace_size(B, H, n, d, dv, *, chunk=0, dtype=torch.bfloat16, gamma=None, ridge=0.0,
+                   normalize=False) -> int:
+    p, _keep = _params(B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize)
+    return int(load().hla_forward_workspace_size(ctypes.byref(p)))
+
+
+def forward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=None,
+                    ridge: float = 0.0, normalize: bool = False, chunk: int = 0,
+                    init: Optional[State] = None, return_state: bool = False,
+                    return_den: bool = False, out: Optional[torch.Tensor] = None,
+                    den: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Masked second-order HLA forward through ``hla_forward_chunked``.
+
+    q, k: [B,H,n,d]; v: [B,H,n,dv] (bf16 or fp32, same dtype, on one device).
+    Returns (out [B,H,n,dv] fp32, den [B,H,n] fp32 or None, final State or None).
+    """
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (torch.bfloat16, torch.float32))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}: "
+                         "expected q,k [B,H,n,d] and v [B,H,n,dv]")
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    p, _keep = _params(B, H, n, d, dv, chunk, q.dtype, gamma, ridge, normalize)
+    need = int(lib.hla_forward_workspace_size(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty(B, H, n, dv, dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,))
+    if den is None and return_den:
+        den = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    if den is not None:
+        _need(den, "den", (torch.float32,))
+    fin = State.empty(B * H, d, dv, dev) if return_state else None
+    ini_c = init.c() if init is not None else None
+    fin_c = fin.c() if fin is not None else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.hla_forward_chunked(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 out.data_ptr(), den.data_ptr() if den is not None else None,
+                                 ctypes.byref(ini_c) if ini_c is not None else None,
+                                 ctypes.byref(fin_c) if fin_c is not None else None,
+                                 ws_ptr, ws_bytes, _stream(dev))
+    _check(st)
+    return out, den, fin
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: State, *, gamma=None,
+                ridge: float = 0.0, normalize: bool = False, return_den: bool = False,
+                out: Optional[torch.Tensor] = None, den: Optional[torch.Tensor] = None):
+    """One token per state through ``hla_decode_step``; ``state`` is updated in
+    place.  q, k: [B,H,d]; v: [B,H,dv].  Returns (out [B,H,dv], den [B,H] or None)."""
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (torch.bfloat16, torch.float32))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q,k [B,H,d] and v [B,H,dv]")
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    p, _keep = _params(B, H, 1, d, dv, 0, q.dtype, gamma, ridge, normalize)
+    if out is None:
+        out = torch.empty(B, H, dv, dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,))
+    if den is None and return_den:
+        den = torch.empty(B, H, dtype=torch.float32, device=dev)
+    sc = state.c()
+    st = lib.hla_decode_step(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             ctypes.byref(sc), out.data_ptr(),
+                             den.data_ptr() if den is not None else None, _stream(dev))
+    _check(st)
+    return out, den
+
+
+def state_compose(earlier: State, later: State, result: Optional[State] = None) -> State:
+    """Masked semidirect product (earlier, then later) through ``hla_state_compose``."""
+    lib = load()
+    N, d, dv = earlier.C.shape
+    if result is None:
+        result = State.empty(N, d, dv, earlier.C.device)
+    a, b, r = earlier.c(), later.c(), result.c()
+    st = lib.hla_state_compose(N, d, dv, ctypes.byref(a), ctypes.byref(b), ctypes.byref(r),
+                               _stream(earlier.C.device))
+    _check(st)
+    return result

@@ -1,0 +1,588 @@
+// fwd_generic.hip -- chunked masked second-order HLA forward for any
+// supported width (d, dv, w in {16, 32, 64, 128}) and fp32 or bf16 inputs.
+//
+// Higher-order Linear Attention, paperlayer.ai summary sec. 4 and 5: token
+// deltas feed an exclusive scan inside each chunk, every token forms its
+// inclusive state and output, and chunk summaries are scanned with the same
+// operator to give each chunk its carry-in.  The masked semidirect product
+// (sec. 4.2) carries the cross term S_later C_earlier; here it is carried in
+// the equivalent corrected form X = S C - G, y = S m - h, for which the
+// per-token update is X_t = g^2 X_{t-1} + S_t q_t v_t^T (it follows from the
+// G, h updates).  Splitting the scan into a linear pass over (S, C, m) and a
+// second linear pass over (X, y) removes every state-by-state product from
+// the inter-chunk scan:
+//
+//   per chunk c (L tokens, local index t, s; carry (S0, C0, m0, X0, y0)):
+//     e_t = g^(t+1), f_s = g^(L-1-s), rho = g^L
+//     A = (Q K^T) o D_g o L          (D_g[t,s] = g^(t-s), L: s <= t)
+//     U = diag(e) Q S0 + A K         row s = S_{s} q_s (inclusive S times q)
+//     P = (Q U^T) o D_{g^2} o L + lambda (Q Q^T) o D_g o L
+//     num = P V + diag(e^2) Q X0 + lambda diag(e) Q C0
+//     den = P 1 + diag(e^2) Q y0 + lambda diag(e) Q m0
+//   carry:  S0' = rho S0 + K^T diag(f) K,  C0' = rho C0 + Q^T diag(f) V,
+//           m0' = rho m0 + Q^T f,  X0' = rho^2 X0 + U^T diag(f^2) V,
+//           y0' = rho^2 y0 + U^T f^2
+//
+// Kernels (one workgroup of 256 threads per chunk unless stated):
+//   k_init_slot   per head: slot 0 = init (X = S C - G) or zeros
+//   k_chunk_sums  K^T diag(f) K, Q^T diag(f) V, Q^T f     -> slot c+1
+//   k_prefix      per head, elementwise: slot c+1 = rho^p slot c + slot c+1
+//   k_chunk_uz    A, U (kept for the output pass), U^T diag(f^2) V, U^T f^2
+//   k_chunk_out   P, num, den, ratio
+//   k_final       per head: final (S, C, m), G = S C - X, h = S m - y, rho
+// Everything is fp32; bf16 inputs are widened exactly on load.
+#include "device_common.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxW = 128;
+
+struct Slots {
+    float *S, *C, *m, *X, *y;  // [BH][nc+1][...]: slot c = state before chunk c
+    float *U;                  // [BH][nc][w][d]
+};
+
+struct GenArgs {
+    int H, n, d, dv, w, nc;
+    float ridge;
+    int normalize;
+    const void *q, *k, *v;
+    float *out, *den;
+    hla_state init, fin;
+    Slots ws;
+    GammaTab gam;
+};
+
+__device__ __forceinline__ size_t slot_index(const GenArgs &a, int bh, int slot) {
+    return static_cast<size_t>(bh) * (a.nc + 1) + slot;
+}
+
+// Out = S*C - In and outv = S*m - inv for one head; S [D][D], C/In/Out [D][DV].
+template <int D, int DV>
+__device__ void s_times_c_minus(const float *S, const float *C, const float *In, float *Out,
+                                const float *m, const float *inv, float *outv) {
+    constexpr int MR = D / 16, MC = DV / 16;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    float acc[MR][MC] = {};
+    for (int l = 0; l < D; ++l) {
+        float sr[MR], cc[MC];
+#pragma unroll
+        for (int i = 0; i < MR; ++i) sr[i] = S[(ty + 16 * i) * D + l];
+#pragma unroll
+        for (int j = 0; j < MC; ++j) cc[j] = C[l * DV + tx + 16 * j];
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+#pragma unroll
+            for (int j = 0; j < MC; ++j) acc[i][j] += sr[i] * cc[j];
+    }
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int j = 0; j < MC; ++j) {
+            const int o = (ty + 16 * i) * DV + tx + 16 * j;
+            Out[o] = acc[i][j] - In[o];
+        }
+    if (tid < D) {
+        float s = 0.0f;
+        for (int l = 0; l < D; ++l) s += S[tid * D + l] * m[l];
+        outv[tid] = s - inv[tid];
+    }
+}
+
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_init_slot(GenArgs a) {
+    const int bh = blockIdx.x;
+    const size_t sl = slot_index(a, bh, 0);
+    float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
+    float *X = a.ws.X + sl * D * DV, *y = a.ws.y + sl * D;
+    const int tid = threadIdx.x;
+    if (a.init.S == nullptr) {
+        for (int i = tid; i < D * D; i += kThreads) S[i] = 0.0f;
+        for (int i = tid; i < D * DV; i += kThreads) C[i] = 0.0f, X[i] = 0.0f;
+        if (tid < D) m[tid] = 0.0f, y[tid] = 0.0f;
+        return;
+    }
+    const float *iS = a.init.S + static_cast<size_t>(bh) * D * D;
+    const float *iC = a.init.C + static_cast<size_t>(bh) * D * DV;
+    const float *iG = a.init.G + static_cast<size_t>(bh) * D * DV;
+    const float *im = a.init.m + static_cast<size_t>(bh) * D;
+    const float *ih = a.init.h + static_cast<size_t>(bh) * D;
+    for (int i = tid; i < D * D; i += kThreads) S[i] = iS[i];
+    for (int i = tid; i < D * DV; i += kThreads) C[i] = iC[i];
+    if (tid < D) m[tid] = im[tid];
+    s_times_c_minus<D, DV>(iS, iC, iG, X, im, ih, y);
+}
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_chunk_sums(GenArgs a) {
+    constexpr int TB = 32, MR = D / 16, MC = DV / 16;
+    __shared__ float ks[TB][D], qs[TB][D], vs[TB][DV], fs[TB];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const T *k = static_cast<const T *>(a.k) + tok * D;
+    const T *v = static_cast<const T *>(a.v) + tok * DV;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    float aS[MR][MR] = {}, aC[MR][MC] = {}, am = 0.0f;
+    for (int b0 = 0; b0 < L; b0 += TB) {
+        const int nb = min(TB, L - b0);
+        for (int i = tid; i < nb * D; i += kThreads) {
+            ks[i / D][i % D] = Elem<T>::get(k, static_cast<size_t>(b0) * D + i);
+            qs[i / D][i % D] = Elem<T>::get(q, static_cast<size_t>(b0) * D + i);
+        }
+        for (int i = tid; i < nb * DV; i += kThreads)
+            vs[i / DV][i % DV] = Elem<T>::get(v, static_cast<size_t>(b0) * DV + i);
+        if (tid < nb) fs[tid] = gpow(g, L - 1 - (b0 + tid));
+        __syncthreads();
+        for (int s = 0; s < nb; ++s) {
+            const float f = fs[s];
+            float kr[MR], kc[MR], qr[MR], vc[MC];
+#pragma unroll
+            for (int i = 0; i < MR; ++i) kr[i] = ks[s][ty + 16 * i], qr[i] = qs[s][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < MR; ++j) kc[j] = ks[s][tx + 16 * j];
+#pragma unroll
+            for (int j = 0; j < MC; ++j) vc[j] = vs[s][tx + 16 * j];
+            // f * (k_a k_b): the product k_a k_b is symmetric in (a, b), so S stays
+            // exactly symmetric.
+#pragma unroll
+            for (int i = 0; i < MR; ++i)
+#pragma unroll
+                for (int j = 0; j < MR; ++j) aS[i][j] += f * (kr[i] * kc[j]);
+#pragma unroll
+            for (int i = 0; i < MR; ++i)
+#pragma unroll
+                for (int j = 0; j < MC; ++j) aC[i][j] += f * (qr[i] * vc[j]);
+            if (tid < D) am += f * qs[s][tid];
+        }
+        __syncthreads();
+    }
+    const size_t sl = slot_index(a, bh, c + 1);
+    float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int j = 0; j < MR; ++j) S[(ty + 16 * i) * D + tx + 16 * j] = aS[i][j];
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int j = 0; j < MC; ++j) C[(ty + 16 * i) * DV + tx + 16 * j] = aC[i][j];
+    if (tid < D) m[tid] = am;
+}
+
+// Exclusive-to-inclusive decayed prefix over the chunk slots, elementwise:
+// slot c+1 = rho_c^power * slot c + slot c+1.  Up to three arrays per launch
+// (their element ranges are concatenated along blockIdx.x).
+struct ScanSeg {
+    float *base;
+    int E;
+};
+
+__global__ __launch_bounds__(kThreads) void k_prefix(GenArgs a, ScanSeg s0, ScanSeg s1,
+                                                     ScanSeg s2, int power) {
+    const int bh = blockIdx.y;
+    int e = blockIdx.x * kThreads + threadIdx.x;
+    ScanSeg seg = s0;
+    if (e >= s0.E) {
+        e -= s0.E;
+        seg = s1;
+        if (e >= s1.E) {
+            e -= s1.E;
+            seg = s2;
+            if (e >= s2.E) return;
+        }
+    }
+    if (a.nc == 0) return;
+    const float g = head_gamma(a.gam, bh % a.H);
+    const int Llast = a.n - (a.nc - 1) * a.w;
+    const float rf = gpow(g, power * a.w), rl = gpow(g, power * Llast);
+    float *p = seg.base + static_cast<size_t>(bh) * (a.nc + 1) * seg.E + e;
+    float run = p[0];
+    for (int c = 0; c < a.nc; ++c) {
+        const float r = (c == a.nc - 1) ? rl : rf;
+        float *slot = p + static_cast<size_t>(c + 1) * seg.E;
+        run = r * run + *slot;
+        *slot = run;
+    }
+}
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_chunk_uz(GenArgs a) {
+    constexpr int MC = D / 16, MZ = DV / 16, MA = D / 16;
+    __shared__ float buf[kMaxW * kMaxW];  // A (L x L, stride kMaxW), then U (L x D)
+    __shared__ float es[kMaxW], f2s[kMaxW];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const T *k = static_cast<const T *>(a.k) + tok * D;
+    const T *v = static_cast<const T *>(a.v) + tok * DV;
+    const float *S0 = a.ws.S + slot_index(a, bh, c) * D * D;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    if (tid < L) {
+        es[tid] = gpow(g, tid + 1);
+        const float f = gpow(g, L - 1 - tid);
+        f2s[tid] = f * f;
+    }
+    // A[t][s] = g^(t-s) (q_t . k_s) for s <= t
+    {
+        float acc[8][8] = {};
+        for (int l = 0; l < D; ++l) {
+            float qa[8], kb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int t = ty + 16 * i;
+                qa[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int s = tx + 16 * j;
+                kb[j] = s < L ? Elem<T>::get(k, static_cast<size_t>(s) * D + l) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] += qa[i] * kb[j];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = ty + 16 * i, s = tx + 16 * j;
+                if (t < L && s < L) buf[t * kMaxW + s] = (s <= t) ? gpow(g, t - s) * acc[i][j] : 0.0f;
+            }
+    }
+    __syncthreads();
+    // U[t][:] = e_t (S0 q_t) + sum_{s<=t} A[t][s] k_s
+    float u[8][MC] = {};
+    for (int l = 0; l < D; ++l) {
+        float qa[8], sb[MC];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = ty + 16 * i;
+            qa[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < MC; ++j) sb[j] = S0[l * D + tx + 16 * j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < MC; ++j) u[i][j] += qa[i] * sb[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = ty + 16 * i;
+        const float e = t < L ? es[t] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < MC; ++j) u[i][j] *= e;
+    }
+    for (int s = 0; s < L; ++s) {
+        float av[8], kv[MC];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = ty + 16 * i;
+            av[i] = t < L ? buf[t * kMaxW + s] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < MC; ++j) kv[j] = Elem<T>::get(k, static_cast<size_t>(s) * D + tx + 16 * j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < MC; ++j) u[i][j] += av[i] * kv[j];
+    }
+    __syncthreads();  // A no longer needed
+    float *Ug = a.ws.U + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = ty + 16 * i;
+        if (t < L) {
+#pragma unroll
+            for (int j = 0; j < MC; ++j) {
+                buf[t * D + tx + 16 * j] = u[i][j];
+                Ug[t * D + tx + 16 * j] = u[i][j];
+            }
+        }
+    }
+    __syncthreads();
+    // Z = U^T diag(f^2) V, z = U^T f^2
+    float z[MA][MZ] = {};
+    for (int s = 0; s < L; ++s) {
+        const float f2 = f2s[s];
+        float ur[MA], vc[MZ];
+#pragma unroll
+        for (int i = 0; i < MA; ++i) ur[i] = f2 * buf[s * D + ty + 16 * i];
+#pragma unroll
+        for (int j = 0; j < MZ; ++j) vc[j] = Elem<T>::get(v, static_cast<size_t>(s) * DV + tx + 16 * j);
+#pragma unroll
+        for (int i = 0; i < MA; ++i)
+#pragma unroll
+            for (int j = 0; j < MZ; ++j) z[i][j] += ur[i] * vc[j];
+    }
+    const size_t sl = slot_index(a, bh, c + 1);
+    float *X = a.ws.X + sl * D * DV, *y = a.ws.y + sl * D;
+#pragma unroll
+    for (int i = 0; i < MA; ++i)
+#pragma unroll
+        for (int j = 0; j < MZ; ++j) X[(ty + 16 * i) * DV + tx + 16 * j] = z[i][j];
+    if (tid < D) {
+        float acc = 0.0f;
+        for (int s = 0; s < L; ++s) acc += f2s[s] * buf[s * D + tid];
+        y[tid] = acc;
+    }
+}
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
+    constexpr int MC = DV / 16;
+    __shared__ float P[kMaxW * kMaxW];
+    __shared__ float es[kMaxW], dens[kMaxW];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const float lam = a.ridge;
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const T *v = static_cast<const T *>(a.v) + tok * DV;
+    const float *U = a.ws.U + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    const size_t sl = slot_index(a, bh, c);
+    const float *X0 = a.ws.X + sl * D * DV, *C0 = a.ws.C + sl * D * DV;
+    const float *y0 = a.ws.y + sl * D, *m0 = a.ws.m + sl * D;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    if (tid < L) es[tid] = gpow(g, tid + 1);
+    // P[t][s] = g^(2(t-s)) (q_t . u_s) + lambda g^(t-s) (q_t . q_s), s <= t
+    {
+        float ap[8][8] = {}, ar[8][8] = {};
+        for (int l = 0; l < D; ++l) {
+            float qa[8], ub[8], qb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int t = ty + 16 * i;
+                qa[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int s = tx + 16 * j;
+                ub[j] = s < L ? U[s * D + l] : 0.0f;
+                qb[j] = s < L ? Elem<T>::get(q, static_cast<size_t>(s) * D + l) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ap[i][j] += qa[i] * ub[j];
+                    ar[i][j] += qa[i] * qb[j];
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = ty + 16 * i, s = tx + 16 * j;
+                if (t < L && s < L) {
+                    float p = 0.0f;
+                    if (s <= t) {
+                        const float dg = gpow(g, t - s);
+                        p = dg * dg * ap[i][j] + lam * dg * ar[i][j];
+                    }
+                    P[t * kMaxW + s] = p;
+                }
+            }
+    }
+    __syncthreads();
+    // den_t = sum_s P[t][s] + e_t^2 (q_t . y0) + lambda e_t (q_t . m0)
+    if (tid < L) {
+        const int t = tid;
+        float ps = 0.0f, qy = 0.0f, qm = 0.0f;
+        for (int s = 0; s <= t; ++s) ps += P[t * kMaxW + s];
+        for (int l = 0; l < D; ++l) {
+            const float ql = Elem<T>::get(q, static_cast<size_t>(t) * D + l);
+            qy += ql * y0[l];
+            qm += ql * m0[l];
+        }
+        const float e = es[t];
+        const float dn = ps + e * e * qy + lam * e * qm;
+        dens[t] = dn;
+        if (a.den) a.den[tok + t] = dn;
+    }
+    __syncthreads();
+    // num = P V + diag(e^2) Q X0 + lambda diag(e) Q C0; the row scales are
+    // folded into the loaded q values so one accumulator serves all three.
+    float acc[8][MC] = {};
+    for (int s = 0; s < L; ++s) {
+        float pa[8], vb[MC];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = ty + 16 * i;
+            pa[i] = t < L ? P[t * kMaxW + s] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < MC; ++j) vb[j] = Elem<T>::get(v, static_cast<size_t>(s) * DV + tx + 16 * j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < MC; ++j) acc[i][j] += pa[i] * vb[j];
+    }
+    float e2[8], le[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = ty + 16 * i;
+        const float e = t < L ? es[t] : 0.0f;
+        e2[i] = e * e;
+        le[i] = lam * e;
+    }
+    for (int l = 0; l < D; ++l) {
+        float qx[8], xb[MC];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = ty + 16 * i;
+            qx[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < MC; ++j) xb[j] = X0[l * DV + tx + 16 * j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < MC; ++j) acc[i][j] += (e2[i] * qx[i]) * xb[j];
+        if (lam != 0.0f) {
+            float cb[MC];
+#pragma unroll
+            for (int j = 0; j < MC; ++j) cb[j] = C0[l * DV + tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < MC; ++j) acc[i][j] += (le[i] * qx[i]) * cb[j];
+        }
+    }
+    float *out = a.out + tok * DV;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = ty + 16 * i;
+        if (t < L) {
+            const float dn = dens[t];
+#pragma unroll
+            for (int j = 0; j < MC; ++j) {
+                const float num = acc[i][j];
+                out[static_cast<size_t>(t) * DV + tx + 16 * j] = a.normalize ? num / dn : num;
+            }
+        }
+    }
+}
+
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
+    const int bh = blockIdx.x;
+    const size_t sl = slot_index(a, bh, a.nc);
+    const float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
+    const float *X = a.ws.X + sl * D * DV, *y = a.ws.y + sl * D;
+    float *fS = a.fin.S + static_cast<size_t>(bh) * D * D;
+    float *fC = a.fin.C + static_cast<size_t>(bh) * D * DV;
+    float *fm = a.fin.m + static_cast<size_t>(bh) * D;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < D * D; i += kThreads) fS[i] = S[i];
+    for (int i = tid; i < D * DV; i += kThreads) fC[i] = C[i];
+    if (tid < D) fm[tid] = m[tid];
+    s_times_c_minus<D, DV>(S, C, X, a.fin.G + static_cast<size_t>(bh) * D * DV, m, y,
+                           a.fin.h + static_cast<size_t>(bh) * D);
+    if (tid == 0 && a.fin.rho) {
+        const float g = head_gamma(a.gam, bh % a.H);
+        const float r0 = (a.init.S && a.init.rho) ? a.init.rho[bh] : 1.0f;
+        a.fin.rho[bh] = r0 * gpow(g, a.n);
+    }
+}
+
+template <typename T, int D, int DV>
+hipError_t launch_all(const GenArgs &a, int BH, hipStream_t st) {
+    const dim3 blk(kThreads);
+    hipLaunchKernelGGL((k_init_slot<D, DV>), dim3(BH), blk, 0, st, a);
+    if (a.nc > 0) {
+        hipLaunchKernelGGL((k_chunk_sums<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
+        const ScanSeg sS{a.ws.S, D * D}, sC{a.ws.C, D * DV}, sm{a.ws.m, D};
+        const int e1 = D * D + D * DV + D;
+        hipLaunchKernelGGL(k_prefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sS, sC,
+                           sm, 1);
+        hipLaunchKernelGGL((k_chunk_uz<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
+        const ScanSeg sX{a.ws.X, D * DV}, sy{a.ws.y, D}, none{nullptr, 0};
+        const int e2 = D * DV + D;
+        hipLaunchKernelGGL(k_prefix, dim3((e2 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sX, sy,
+                           none, 2);
+        hipLaunchKernelGGL((k_chunk_out<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
+    }
+    if (a.fin.S) hipLaunchKernelGGL((k_final<D, DV>), dim3(BH), blk, 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t pick_dv(const GenArgs &a, int BH, hipStream_t st) {
+    switch (a.dv) {
+        case 16: return launch_all<T, D, 16>(a, BH, st);
+        case 32: return launch_all<T, D, 32>(a, BH, st);
+        case 64: return launch_all<T, D, 64>(a, BH, st);
+        case 128: return launch_all<T, D, 128>(a, BH, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t pick_d(const GenArgs &a, int BH, hipStream_t st) {
+    switch (a.d) {
+        case 16: return pick_dv<T, 16>(a, BH, st);
+        case 32: return pick_dv<T, 32>(a, BH, st);
+        case 64: return pick_dv<T, 64>(a, BH, st);
+        case 128: return pick_dv<T, 128>(a, BH, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+    size_t S, C, m, X, y, U, total;
+};
+
+WsLayout layout(int BH, int n, int d, int dv, int w) {
+    const size_t nc = (static_cast<size_t>(n) + w - 1) / w;
+    const size_t slots = static_cast<size_t>(BH) * (nc + 1);
+    WsLayout L{};
+    size_t off = 0;
+    L.S = off; off = align256(off + slots * d * d * sizeof(float));
+    L.C = off; off = align256(off + slots * d * dv * sizeof(float));
+    L.m = off; off = align256(off + slots * d * sizeof(float));
+    L.X = off; off = align256(off + slots * d * dv * sizeof(float));
+    L.y = off; off = align256(off + slots * d * sizeof(float));
+    L.U = off; off = align256(off + static_cast<size_t>(BH) * nc * w * d * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+size_t generic_workspace_bytes(int BH, int n, int d, int dv, int w) {
+    return layout(BH, n, d, dv, w).total;
+}
+
+hipError_t generic_forward(const FwdProblem &p, hipStream_t st) {
+    const int BH = p.B * p.H;
+    const WsLayout L = layout(BH, p.n, p.d, p.dv, p.w);
+    char *base = static_cast<char *>(p.ws);
+    GenArgs a{};
+    a.H = p.H; a.n = p.n; a.d = p.d; a.dv = p.dv; a.w = p.w; a.nc = p.nc;
+    a.ridge = p.ridge; a.normalize = p.normalize;
+    a.q = p.q; a.k = p.k; a.v = p.v; a.out = p.out; a.den = p.den;
+    a.init = p.init; a.fin = p.fin; a.gam = p.gam;
+    a.ws.S = reinterpret_cast<float *>(base + L.S);
+    a.ws.C = reinterpret_cast<float *>(base + L.C);
+    a.ws.m = reinterpret_cast<float *>(base + L.m);
+    a.ws.X = reinterpret_cast<float *>(base + L.X);
+    a.ws.y = reinterpret_cast<float *>(base + L.y);
+    a.ws.U = reinterpret_cast<float *>(base + L.U);
+    if (p.dtype == HLA_BF16) return pick_d<uint16_t>(a, BH, st);
+    return pick_d<float>(a, BH, st);
+}
+
+}  // namespace hla

@@ -1,0 +1,289 @@
+// hla_api.cpp -- the extern "C" entry points declared in include/hla.h:
+// host-only validation (nothing is enqueued on a bad argument), then dispatch
+// to the HIP kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "hla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hla_status fail(hla_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+hla_status ok() {
+    g_last_error.clear();
+    return HLA_OK;
+}
+
+bool width_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    std::string name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const std::string &name, const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{name, lo, lo + bytes};
+}
+
+bool overlaps(const Span &a, const Span &b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Every span in `outs` must be disjoint from every other span in `outs` and
+// from every span in `ins`.
+bool first_overlap(const std::vector<Span> &outs, const std::vector<Span> &ins,
+                   std::string *detail) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j])) {
+                *detail = outs[i].name + " overlaps " + outs[j].name;
+                return true;
+            }
+        for (const Span &in : ins)
+            if (overlaps(outs[i], in)) {
+                *detail = outs[i].name + " overlaps " + in.name;
+                return true;
+            }
+    }
+    return false;
+}
+
+hla_status check_state(const hla_state *s, const char *what) {
+    const float *ptrs[5] = {s->S, s->C, s->m, s->G, s->h};
+    const char *names[5] = {"S", "C", "m", "G", "h"};
+    for (int i = 0; i < 5; ++i) {
+        if (!ptrs[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s->%s is NULL", what, names[i]);
+        if (!aligned16(ptrs[i]))
+            return fail(HLA_ERR_ALIGNMENT, "%s->%s is not 16-byte aligned", what, names[i]);
+    }
+    if (s->rho && (reinterpret_cast<uintptr_t>(s->rho) & 3u))
+        return fail(HLA_ERR_ALIGNMENT, "%s->rho is not 4-byte aligned", what);
+    return HLA_OK;
+}
+
+void state_spans(const hla_state *s, const char *prefix, size_t N, int d, int dv,
+                 std::vector<Span> *out) {
+    const char *tags[6] = {"S", "C", "m", "G", "h", "rho"};
+    const float *ptrs[6] = {s->S, s->C, s->m, s->G, s->h, s->rho};
+    const size_t sizes[6] = {N * d * d, N * d * dv, N * d, N * d * dv, N * d, N};
+    for (int i = 0; i < 6; ++i)
+        if (ptrs[i]) out->push_back(span(std::string(prefix) + "." + tags[i], ptrs[i], sizes[i] * sizeof(float)));
+}
+
+hla_status check_common(int H, int d, int dv, hla_dtype dtype, const float *gamma, float ridge,
+                        int normalize, hla::GammaTab *tab) {
+    if (!width_ok(d) || !width_ok(dv))
+        return fail(HLA_ERR_UNSUPPORTED, "d=%d, dv=%d: each must be 16, 32, 64 or 128", d, dv);
+    if (dtype != HLA_F32 && dtype != HLA_BF16) return fail(HLA_ERR_INVALID_ARGUMENT, "bad dtype %d", int(dtype));
+    if (!std::isfinite(ridge) || ridge < 0.0f)
+        return fail(HLA_ERR_INVALID_ARGUMENT, "ridge must be finite and >= 0");
+    if (normalize != 0 && normalize != 1) return fail(HLA_ERR_INVALID_ARGUMENT, "normalize must be 0 or 1");
+    tab->per_head = 0;
+    tab->g[0] = 1.0f;
+    if (gamma) {
+        if (H > hla::kMaxGammaHeads)
+            return fail(HLA_ERR_UNSUPPORTED, "per-head gamma supports at most %d heads (H=%d)",
+                        hla::kMaxGammaHeads, H);
+        for (int h = 0; h < H; ++h) {
+            const float g = gamma[h];
+            if (!std::isfinite(g) || !(g > 0.0f) || g > 1.0f)
+                return fail(HLA_ERR_INVALID_ARGUMENT, "gamma[%d] = %g is not in (0, 1]", h, double(g));
+            tab->g[h] = g;
+        }
+        tab->per_head = 1;
+    }
+    return HLA_OK;
+}
+
+int default_chunk(int d) { return d > 64 ? 128 : 64; }
+
+struct Geometry {
+    int w, nc;
+};
+
+hla_status forward_geometry(const hla_params *p, Geometry *geo) {
+    if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (p->B < 1 || p->H < 1) return fail(HLA_ERR_INVALID_ARGUMENT, "B=%d, H=%d must be >= 1", p->B, p->H);
+    if (p->n < 0) return fail(HLA_ERR_INVALID_ARGUMENT, "n=%d must be >= 0", p->n);
+    const int w = p->chunk == 0 ? default_chunk(p->d) : p->chunk;
+    if (!width_ok(w)) return fail(HLA_ERR_UNSUPPORTED, "chunk=%d must be 0, 16, 32, 64 or 128", p->chunk);
+    const uint64_t BH = static_cast<uint64_t>(p->B) * p->H;
+    if (BH > 65535) return fail(HLA_ERR_UNSUPPORTED, "B*H=%llu exceeds 65535", (unsigned long long)BH);
+    const uint64_t wide = p->d > p->dv ? p->d : p->dv;
+    if (BH * static_cast<uint64_t>(p->n) * wide > 0x7fffffffull)
+        return fail(HLA_ERR_UNSUPPORTED, "B*H*n*max(d,dv) exceeds 2^31-1 elements");
+    geo->w = w;
+    geo->nc = (p->n + w - 1) / w;
+    return HLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hla_status_string(hla_status s) {
+    switch (s) {
+        case HLA_OK: return "HLA_OK";
+        case HLA_ERR_INVALID_ARGUMENT: return "HLA_ERR_INVALID_ARGUMENT";
+        case HLA_ERR_UNSUPPORTED: return "HLA_ERR_UNSUPPORTED";
+        case HLA_ERR_ALIGNMENT: return "HLA_ERR_ALIGNMENT";
+        case HLA_ERR_WORKSPACE: return "HLA_ERR_WORKSPACE";
+        case HLA_ERR_DEVICE: return "HLA_ERR_DEVICE";
+    }
+    return "HLA_UNKNOWN_STATUS";
+}
+
+const char *hla_last_error(void) { return g_last_error.c_str(); }
+
+size_t hla_forward_workspace_size(const hla_params *p) {
+    Geometry geo{};
+    if (forward_geometry(p, &geo) != HLA_OK) return 0;
+    if (!width_ok(p->d) || !width_ok(p->dv)) return 0;
+    return hla::generic_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w);
+}
+
+hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
+                               float *out, float *den, const hla_state *init,
+                               hla_state *final_state, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    Geometry geo{};
+    hla_status s = forward_geometry(p, &geo);
+    if (s != HLA_OK) return s;
+    hla::FwdProblem fp{};
+    s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &fp.gam);
+    if (s != HLA_OK) return s;
+    const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
+    const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
+    if (n > 0) {
+        const void *req[4] = {q, k, v, out};
+        const char *nm[4] = {"q", "k", "v", "out"};
+        for (int i = 0; i < 4; ++i) {
+            if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
+            if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
+        }
+        if (den && !aligned16(den)) return fail(HLA_ERR_ALIGNMENT, "den is not 16-byte aligned");
+    }
+    if (init && (s = check_state(init, "init")) != HLA_OK) return s;
+    if (final_state && (s = check_state(final_state, "final_state")) != HLA_OK) return s;
+    const size_t need = hla::generic_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
+    if (need > 0) {
+        if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(HLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(HLA_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+    }
+    // aliasing: outputs must be disjoint from each other and from the inputs
+    std::vector<Span> outs, ins;
+    if (n > 0) {
+        outs.push_back(span("out", out, BH * n * p->dv * 4));
+        if (den) outs.push_back(span("den", den, BH * n * 4));
+        ins.push_back(span("q", q, BH * n * p->d * esz));
+        ins.push_back(span("k", k, BH * n * p->d * esz));
+        ins.push_back(span("v", v, BH * n * p->dv * esz));
+    }
+    if (need > 0) outs.push_back(span("workspace", workspace, need));
+    if (final_state) state_spans(final_state, "final_state", BH, p->d, p->dv, &outs);
+    if (init) state_spans(init, "init", BH, p->d, p->dv, &ins);
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+
+    fp.B = p->B; fp.H = p->H; fp.n = p->n; fp.d = p->d; fp.dv = p->dv;
+    fp.w = geo.w; fp.nc = geo.nc;
+    fp.dtype = p->dtype; fp.ridge = p->ridge; fp.normalize = p->normalize;
+    fp.q = q; fp.k = k; fp.v = v; fp.out = out; fp.den = den;
+    if (init) fp.init = *init;
+    if (final_state) fp.fin = *final_state;
+    fp.ws = workspace; fp.ws_bytes = workspace_bytes;
+    if (n == 0 && !final_state) return ok();
+    const hipError_t e = hla::generic_forward(fp, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "forward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+hla_status hla_decode_step(const hla_params *p, const void *q, const void *k, const void *v,
+                           hla_state *state, float *out, float *den, hipStream_t stream) {
+    if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (p->B < 1 || p->H < 1) return fail(HLA_ERR_INVALID_ARGUMENT, "B=%d, H=%d must be >= 1", p->B, p->H);
+    if (p->n != 1) return fail(HLA_ERR_INVALID_ARGUMENT, "decode needs n = 1 (got %d)", p->n);
+    hla::DecodeProblem dp{};
+    hla_status s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &dp.gam);
+    if (s != HLA_OK) return s;
+    const uint64_t N = static_cast<uint64_t>(p->B) * p->H;
+    if (N > 0x7fffffffull / (128ull * 128ull))
+        return fail(HLA_ERR_UNSUPPORTED, "B*H=%llu too large", (unsigned long long)N);
+    const void *req[4] = {q, k, v, out};
+    const char *nm[4] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i) {
+        if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
+        if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
+    }
+    if (den && !aligned16(den)) return fail(HLA_ERR_ALIGNMENT, "den is not 16-byte aligned");
+    if (!state) return fail(HLA_ERR_INVALID_ARGUMENT, "state is NULL");
+    if ((s = check_state(state, "state")) != HLA_OK) return s;
+    const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
+    std::vector<Span> outs, ins;
+    outs.push_back(span("out", out, N * p->dv * 4));
+    if (den) outs.push_back(span("den", den, N * 4));
+    state_spans(state, "state", N, p->d, p->dv, &outs);
+    ins.push_back(span("q", q, N * p->d * esz));
+    ins.push_back(span("k", k, N * p->d * esz));
+    ins.push_back(span("v", v, N * p->dv * esz));
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    dp.B = p->B; dp.H = p->H; dp.d = p->d; dp.dv = p->dv; dp.dtype = p->dtype;
+    dp.ridge = p->ridge; dp.normalize = p->normalize;
+    dp.q = q; dp.k = k; dp.v = v; dp.st = *state; dp.out = out; dp.den = den;
+    const hipError_t e = hla::decode_step(dp, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+hla_status hla_state_compose(int32_t count, int32_t d, int32_t dv, const hla_state *earlier,
+                             const hla_state *later, hla_state *result, hipStream_t stream) {
+    if (count < 0) return fail(HLA_ERR_INVALID_ARGUMENT, "count=%d must be >= 0", count);
+    if (!width_ok(d) || !width_ok(dv))
+        return fail(HLA_ERR_UNSUPPORTED, "d=%d, dv=%d: each must be 16, 32, 64 or 128", d, dv);
+    if (!earlier || !later || !result) return fail(HLA_ERR_INVALID_ARGUMENT, "a state pointer is NULL");
+    if (count == 0) return ok();
+    if (static_cast<uint64_t>(count) * 128ull * 128ull > 0x7fffffffull)
+        return fail(HLA_ERR_UNSUPPORTED, "count=%d too large", count);
+    hla_status s;
+    if ((s = check_state(earlier, "earlier")) != HLA_OK) return s;
+    if ((s = check_state(later, "later")) != HLA_OK) return s;
+    if ((s = check_state(result, "result")) != HLA_OK) return s;
+    std::vector<Span> outs, ins;
+    state_spans(result, "result", size_t(count), d, dv, &outs);
+    state_spans(earlier, "earlier", size_t(count), d, dv, &ins);
+    state_spans(later, "later", size_t(count), d, dv, &ins);
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    const hipError_t e = hla::state_compose(count, d, dv, *earlier, *later, *result, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "compose launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// hla_internal.h -- declarations shared by the host dispatch (hla_api.cpp)
+// and the HIP kernel files of the library.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hla.h"
+
+namespace hla {
+
+// Per-head decays travel by value in kernel arguments.
+constexpr int kMaxGammaHeads = 256;
+
+struct GammaTab {
+    float g[kMaxGammaHeads];
+    int per_head;  // 0: g[0] applies to every head
+};
+
+__host__ __device__ inline float head_gamma(const GammaTab &t, int h) {
+    return t.g[t.per_head ? h : 0];
+}
+
+// Everything a forward launch needs, validated by the host.
+struct FwdProblem {
+    int B, H, n, d, dv, w, nc;
+    hla_dtype dtype;
+    float ridge;
+    int normalize;
+    const void *q, *k, *v;
+    float *out, *den;  // den may be null
+    hla_state init;    // init.S == nullptr: zero state
+    hla_state fin;     // fin.S == nullptr: not requested
+    GammaTab gam;
+    void *ws;
+    size_t ws_bytes;
+};
+
+// Generic chunked forward: any d, dv, w in {16,32,64,128}, fp32 or bf16,
+// several kernels over a per-chunk workspace.
+size_t generic_workspace_bytes(int BH, int n, int d, int dv, int w);
+hipError_t generic_forward(const FwdProblem &p, hipStream_t s);
+
+struct DecodeProblem {
+    int B, H, d, dv;
+    hla_dtype dtype;
+    float ridge;
+    int normalize;
+    const void *q, *k, *v;
+    hla_state st;
+    float *out, *den;
+    GammaTab gam;
+};
+hipError_t decode_step(const DecodeProblem &p, hipStream_t s);
+
+hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,
+                         const hla_state &r, hipStream_t s);
+
+}  // namespace hla

@@ -1,0 +1,159 @@
+/*
+ * hla.h -- C ABI of the MI355X (gfx950) library for masked second-order
+ * Higher-order Linear Attention (HLA).
+ *
+ * Sources.  "Higher-order Linear Attention" (Zhang, Qin, Gu), as summarised
+ * on three web pages:
+ *   [SUM]  paperlayer.ai section-by-section summary;
+ *   [EXP]  gist.science explainer, "Technische Zusammenfassung";
+ *   [SKL]  skillmd.com skill page "Scale Attention to Long Contexts via
+ *          Linear-Time Matrix Interactions" (its listings are NOT followed:
+ *          they use a softmax feature map and a token-count normaliser that
+ *          the other pages do not have).
+ *
+ * What the library computes, per head h with decay g = gamma[h] and ridge
+ * lambda, for tokens t = 0..n-1 (all accumulation in fp32):
+ *   S_t = g S_{t-1} + k_t k_t^T            key second moment, d x d
+ *   C_t = g C_{t-1} + q_t v_t^T            query-value accumulator, d x dv
+ *   m_t = g m_{t-1} + q_t                  query mass, d
+ *   G_t = g^2 G_{t-1} + g k_t (k_t^T C_{t-1})   cross summary, d x dv
+ *   h_t = g^2 h_{t-1} + g k_t (k_t . m_{t-1})   cross summary, d
+ *   num_t = q_t^T ((S_t + lambda I) C_t - G_t)
+ *   den_t = q_t^T ((S_t + lambda I) m_t - h_t)
+ *   out_t = num_t (default) or num_t / den_t (normalize = 1)
+ * [EXP] "Methodik" item 1 (prefix summaries S, C, m; cross summaries G, h
+ * that remove the future terms of the naive product S C; output
+ * q^T(S C - G); ratio with a masked denominator); [SUM] sec. 3.1 (mask keeps
+ * j <= t), sec. 4.3 (fixed decay as an attenuation factor), sec. 5.1 (ridge
+ * lambda I, unnormalised output by default).  Equivalently
+ *   num_t = sum_{j<=t} sum_{i<=j} g^(2t-i-j) (q_t.k_i)(k_i.q_j) v_j
+ *           + lambda sum_{j<=t} g^(t-j) (q_t.q_j) v_j.
+ * No epsilon is added to the denominator; a zero denominator gives IEEE
+ * inf/NaN in the ratio.  NaN/Inf inputs propagate.
+ *
+ * Conventions shared by every entry point.
+ *   - Device pointers are plain HIP device addresses, 16-byte aligned.
+ *     Tensors are contiguous, row-major.  The state index of batch b,
+ *     head h is b*H + h.
+ *   - The caller owns all memory.  The library allocates and frees nothing
+ *     and keeps no state between calls beyond its loaded code.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *     synchronise.  Validation is host-only and happens before anything is
+ *     enqueued; on any error nothing is enqueued and no output is touched.
+ *   - Errors are returned as hla_status; hla_last_error() gives a
+ *     thread-local detail string for the last failing call on that thread.
+ *     A launch failure reported by the HIP runtime is HLA_ERR_DEVICE.
+ *   - All entry points are thread-safe; calls that share output, state or
+ *     workspace memory must be ordered on one stream by the caller.
+ */
+#ifndef HLA_H_
+#define HLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t only */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HLA_OK = 0,
+    HLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad gamma/ridge, aliasing */
+    HLA_ERR_UNSUPPORTED = 2,      /* a size or width the library has no kernel for   */
+    HLA_ERR_ALIGNMENT = 3,        /* a device pointer not 16-byte aligned             */
+    HLA_ERR_WORKSPACE = 4,        /* workspace missing or smaller than required       */
+    HLA_ERR_DEVICE = 5            /* the HIP runtime reported a launch error          */
+} hla_status;
+
+typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
+
+/* A segment summary for BH = B*H heads ([SUM] sec. 4.2: the masked state
+ * tuple (S, C, m, G, h); rho is the segment's attenuation g^len, [SUM]
+ * sec. 4.3).  All fp32 device arrays, contiguous:
+ *   S [BH,d,d] (symmetric), C [BH,d,dv], m [BH,d], G [BH,d,dv], h [BH,d],
+ *   rho [BH] (may be NULL: read as 1, not written). */
+typedef struct {
+    float *S;
+    float *C;
+    float *m;
+    float *G;
+    float *h;
+    float *rho;
+} hla_state;
+
+typedef struct {
+    int32_t B, H;        /* batch and heads, >= 1                                 */
+    int32_t n;           /* tokens per head, >= 0 (decode: must be 1)             */
+    int32_t d, dv;       /* key/query width and value width, each 16, 32, 64, 128 */
+    int32_t chunk;       /* chunk width w: 16, 32, 64 or 128; 0 = default: 64,    */
+                         /* or 128 when d = 128                                   */
+    hla_dtype dtype;     /* element type of q, k, v                               */
+    const float *gamma;  /* HOST array [H] of decays in (0, 1]; NULL = no decay   */
+    float ridge;         /* lambda >= 0                                           */
+    int32_t normalize;   /* 0: out = numerator; 1: out = numerator / denominator  */
+} hla_params;
+
+/* Bytes of device workspace hla_forward_chunked needs for these params
+ * (0 for an invalid p).  The workspace holds per-chunk partial summaries;
+ * its contents between calls are unspecified. */
+size_t hla_forward_workspace_size(const hla_params *p);
+
+/* Chunk-parallel masked forward ([SUM] sec. 4 and 5: token deltas feed an
+ * exclusive scan inside each chunk, each token forms its inclusive state and
+ * output, and chunk summaries are scanned with the same operator to give
+ * carry-ins; the result equals the serial recurrence above up to fp32
+ * rounding order).
+ *   q, k  [B,H,n,d], v [B,H,n,dv] in p->dtype      (inputs, not modified)
+ *   out   [B,H,n,dv] fp32                           (output)
+ *   den   [B,H,n] fp32 or NULL                      (output: den_t)
+ *   init  NULL = zero state, else the state at position -1 (all of S, C, m,
+ *         G, h set; rho optional and only used to form final_state->rho)
+ *   final_state  NULL, or receives the state after token n-1, with
+ *         rho = (init rho or 1) * g^n
+ *   workspace    device memory of at least hla_forward_workspace_size(p)
+ *         bytes (may be NULL when that size is 0).
+ * out and den must not overlap q, k, v, init or the workspace; init and
+ * final_state must not overlap.  With n = 0 only final_state is written. */
+hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k,
+                               const void *v, float *out, float *den,
+                               const hla_state *init, hla_state *final_state,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* One streaming decode step ([SUM] sec. 1 and 2: constant-size state,
+ * O(d^2 + d dv) work per token): applies token (q, k, v) to `state` in place
+ * and writes its output.  p->n must be 1.
+ *   q, k [B,H,d], v [B,H,dv] in p->dtype
+ *   state  in/out, all of S, C, m, G, h set; S must be symmetric (as the
+ *          method produces it); rho, if set, is multiplied by g
+ *   out    [B,H,dv] fp32; den [B,H] fp32 or NULL
+ * Each of S, C, G is read once and written once. */
+hla_status hla_decode_step(const hla_params *p, const void *q, const void *k,
+                           const void *v, hla_state *state, float *out, float *den,
+                           hipStream_t stream);
+
+/* Masked semidirect-product composition of `count` segment pairs, earlier
+ * segment a then later segment b ([SUM] sec. 4.2; [EXP] "Assoziative
+ * Operatoren", cross term S_B C_A):
+ *   S = rho_b S_a + S_b       C = rho_b C_a + C_b       m = rho_b m_a + m_b
+ *   G = rho_b^2 G_a + G_b + rho_b S_b C_a
+ *   h = rho_b^2 h_a + h_b + rho_b S_b m_a            rho = rho_a rho_b
+ * All three states hold `count` entries of width d x dv (d, dv in
+ * {16,32,64,128}); result must not overlap either input. */
+hla_status hla_state_compose(int32_t count, int32_t d, int32_t dv,
+                             const hla_state *earlier, const hla_state *later,
+                             hla_state *result, hipStream_t stream);
+
+/* Static name of a status code. */
+const char *hla_status_string(hla_status s);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char *hla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H_ */

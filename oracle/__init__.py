@@ -72,6 +72,16 @@ def _ptr(a: Optional[np.ndarray]):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped
+    at 16 (the CPU share of one GPU on the GPU hosts)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _f64(a) -> np.ndarray:
     """Exact conversion to a contiguous float64 array (bf16/fp32 -> fp64 is exact)."""
     try:
@@ -138,7 +148,7 @@ def forward(q, k, v, gamma=None, lam: float = 0.0, normalize: bool = False,
     N = B * H
     ini = _as_state(init, N, d, dv) if init is not None else None
     fin = State.zeros(N, d, dv) if want_state else None
-    threads = threads or (os.cpu_count() or 1)
+    threads = threads or default_threads()
     ip = [None] * 6 if ini is None else [_ptr(x) for x in ini.flat()]
     fp = [None] * 6 if fin is None else [_ptr(x) for x in fin.flat()]
     rc = lib.hla_oracle_forward(B, H, n, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
@@ -162,7 +172,7 @@ def decode(state: State, q, k, v, gamma=None, lam: float = 0.0,
     g = None if gamma is None else _f64(np.asarray(gamma, dtype=np.float64).reshape(H))
     out = np.empty((B, H, dv))
     den = np.empty((B, H))
-    threads = threads or (os.cpu_count() or 1)
+    threads = threads or default_threads()
     rc = lib.hla_oracle_decode(B, H, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                float(lam), int(bool(normalize)),
                                *[_ptr(x) for x in st.flat()], _ptr(out), _ptr(den),

@@ -1,0 +1,212 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/hla.h declares, and rejects bad arguments on the host before any HIP
+call (no test here launches a kernel, so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import associative_scan_sequence_amd as hla
+from associative_scan_sequence_amd._binding import CParams, CState
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hla.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+
+# Fake, 256-byte aligned, non-overlapping "device" addresses: validation only
+# compares and range-checks them; every call below fails before any launch.
+BASE = 0x7F0000000000
+
+
+def addr(i):
+    return BASE + i * (1 << 34)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hla.load()
+
+
+def test_header_declares_the_three_entry_points():
+    fns = declared_functions()
+    for name in ("hla_forward_chunked", "hla_decode_step", "hla_state_compose"):
+        assert name in fns
+    assert set(fns) == set(hla.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", hla.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hla_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing else with the public prefix leaks out
+    assert exported == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code, name in hla._binding.STATUS.items():
+        assert lib.hla_status_string(code).decode() == name
+
+
+def params(**kw):
+    d = dict(B=2, H=3, n=100, d=64, dv=32, chunk=0, dtype=1, gamma=None, ridge=0.0, normalize=0)
+    d.update(kw)
+    return CParams(d["B"], d["H"], d["n"], d["d"], d["dv"], d["chunk"], d["dtype"], d["gamma"],
+                   d["ridge"], d["normalize"])
+
+
+def fwd(lib, p, q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None, init=None, fin=None,
+        ws=None, ws_bytes=None):
+    need = lib.hla_forward_workspace_size(ctypes.byref(p))
+    if ws is None:
+        ws = addr(5)
+    if ws_bytes is None:
+        ws_bytes = need
+    return lib.hla_forward_chunked(ctypes.byref(p), q, k, v, out, den,
+                                   ctypes.byref(init) if init is not None else None,
+                                   ctypes.byref(fin) if fin is not None else None, ws, ws_bytes, None)
+
+
+def last(lib):
+    return lib.hla_last_error().decode()
+
+
+def test_workspace_size(lib):
+    assert lib.hla_forward_workspace_size(ctypes.byref(params())) > 0
+    assert lib.hla_forward_workspace_size(None) == 0
+    assert lib.hla_forward_workspace_size(ctypes.byref(params(d=48))) == 0
+    # grows with n and with the chunk count
+    a = lib.hla_forward_workspace_size(ctypes.byref(params(n=1000)))
+    b = lib.hla_forward_workspace_size(ctypes.byref(params(n=2000)))
+    assert b > a
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(B=0), INVALID, "B="),
+    (dict(H=0), INVALID, "H="),
+    (dict(n=-1), INVALID, "n="),
+    (dict(d=48), UNSUPPORTED, "d=48"),
+    (dict(dv=256), UNSUPPORTED, "dv=256"),
+    (dict(chunk=24), UNSUPPORTED, "chunk"),
+    (dict(dtype=7), INVALID, "dtype"),
+    (dict(ridge=-1.0), INVALID, "ridge"),
+    (dict(ridge=float("nan")), INVALID, "ridge"),
+    (dict(normalize=2), INVALID, "normalize"),
+    (dict(B=300, H=300), UNSUPPORTED, "65535"),
+])
+def test_forward_rejects_bad_params(lib, kw, code, frag):
+    p = params(**kw)
+    assert fwd(lib, p) == code
+    assert frag in last(lib)
+
+
+@pytest.mark.parametrize("g", [0.0, -0.5, 1.5, float("nan"), float("inf")])
+def test_forward_rejects_bad_gamma(lib, g):
+    arr = (ctypes.c_float * 3)(0.9, g, 0.9)
+    p = params(gamma=ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)))
+    assert fwd(lib, p) == INVALID
+    assert "gamma[1]" in last(lib)
+
+
+def test_forward_rejects_null_and_misaligned(lib):
+    p = params()
+    assert fwd(lib, p, q=None) == INVALID and "q is NULL" in last(lib)
+    assert fwd(lib, p, out=None) == INVALID and "out is NULL" in last(lib)
+    assert fwd(lib, p, k=addr(2) + 4) == ALIGN and "k is not" in last(lib)
+    assert fwd(lib, p, den=addr(6) + 8) == ALIGN and "den" in last(lib)
+
+
+def test_forward_rejects_small_or_missing_workspace(lib):
+    p = params()
+    need = lib.hla_forward_workspace_size(ctypes.byref(p))
+    assert fwd(lib, p, ws_bytes=need - 1) == WORKSPACE
+    assert lib.hla_forward_chunked(ctypes.byref(p), addr(1), addr(2), addr(3), addr(4), None, None,
+                                   None, None, need, None) == WORKSPACE
+    assert fwd(lib, p, ws=addr(5) + 16) == ALIGN
+
+
+def test_forward_rejects_aliasing(lib):
+    p = params()
+    # out overlapping q
+    assert fwd(lib, p, out=addr(1) + 256) == INVALID and "out overlaps q" in last(lib)
+    # den overlapping out
+    assert fwd(lib, p, den=addr(4) + 1024) == INVALID and "overlaps" in last(lib)
+    # workspace overlapping v
+    assert fwd(lib, p, ws=addr(3)) == INVALID and "workspace overlaps v" in last(lib)
+    # final state overlapping init
+    st = CState(addr(7), addr(8), addr(9), addr(10), addr(11), None)
+    st2 = CState(addr(12), addr(13), addr(14), addr(10), addr(15), None)
+    assert fwd(lib, p, init=st, fin=st2) == INVALID and "overlaps init.G" in last(lib)
+
+
+def test_forward_rejects_incomplete_state(lib):
+    p = params()
+    st = CState(addr(7), addr(8), None, addr(10), addr(11), None)
+    assert fwd(lib, p, init=st) == INVALID and "init->m is NULL" in last(lib)
+    st = CState(addr(7), addr(8), addr(9), addr(10) + 4, addr(11), None)
+    assert fwd(lib, p, fin=st) == ALIGN and "final_state->G" in last(lib)
+
+
+def test_forward_empty_sequence_without_state_is_a_no_op(lib):
+    p = params(n=0)
+    assert lib.hla_forward_chunked(ctypes.byref(p), None, None, None, None, None, None, None,
+                                   addr(5), lib.hla_forward_workspace_size(ctypes.byref(p)),
+                                   None) == OK
+
+
+def dec(lib, p, state, q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None):
+    return lib.hla_decode_step(ctypes.byref(p), q, k, v,
+                               ctypes.byref(state) if state is not None else None, out, den, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    st = CState(addr(7), addr(8), addr(9), addr(10), addr(11), addr(12))
+    assert dec(lib, params(n=2), st) == INVALID and "n = 1" in last(lib)
+    assert dec(lib, params(n=1, d=8), st) == UNSUPPORTED
+    assert dec(lib, params(n=1), None) == INVALID
+    assert dec(lib, params(n=1), st, q=None) == INVALID
+    assert dec(lib, params(n=1), st, out=addr(8)) == INVALID and "overlaps" in last(lib)
+    assert dec(lib, params(n=1), CState(addr(7), addr(8), addr(9), None, addr(11), None)) == INVALID
+    assert dec(lib, params(n=1), st, v=addr(3) + 2) == ALIGN
+
+
+def test_compose_rejects_bad_arguments(lib):
+    a = CState(addr(1), addr(2), addr(3), addr(4), addr(5), None)
+    b = CState(addr(6), addr(7), addr(8), addr(9), addr(10), None)
+    r = CState(addr(11), addr(12), addr(13), addr(14), addr(15), None)
+    comp = lambda cnt, d, dv, x, y, z: lib.hla_state_compose(  # noqa: E731
+        cnt, d, dv, ctypes.byref(x) if x else None, ctypes.byref(y) if y else None,
+        ctypes.byref(z) if z else None, None)
+    assert comp(-1, 64, 64, a, b, r) == INVALID
+    assert comp(4, 64, 80, a, b, r) == UNSUPPORTED
+    assert comp(4, 64, 64, a, None, r) == INVALID
+    assert comp(0, 64, 64, a, b, r) == OK  # empty batch: nothing to do
+    assert comp(4, 64, 64, a, b, CState(addr(11), addr(2), addr(13), addr(14), addr(15), None)) == INVALID
+    assert "result.C overlaps earlier.C" in last(lib)
+
+
+def test_last_error_is_cleared_by_success(lib):
+    assert fwd(lib, params(B=0)) == INVALID
+    assert last(lib) != ""
+    p = params(n=0)
+    assert lib.hla_forward_chunked(ctypes.byref(p), None, None, None, None, None, None, None,
+                                   addr(5), 1 << 30, None) == OK
+    assert last(lib) == ""
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(ValueError, match="HIP device"):
+        hla.forward_chunked(q, q, q)

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+identical seeded inputs.  Every test here needs an MI355X and the built
+libhla.so; none falls back to anything else.
+
+Tolerances (tests/parity.py): 2e-3 for bf16 inputs, 1e-5 for fp32 inputs, on
+the row error of outputs and the slab error of denominators and states.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import associative_scan_sequence_amd as hla
+import hla_inputs as inputs
+from parity import TOL, ratio_err, row_err, slab_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sys.stdout.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stdout.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def on_gpu(*ts):
+    return [t.to(DEV).contiguous() for t in ts]
+
+
+def state_np(st: hla.State):
+    return {k: getattr(st, k).cpu().double().numpy() for k in ("S", "C", "m", "G", "h", "rho")}
+
+
+def check_state(gpu: hla.State, ref, tol, names=("S", "C", "m", "G", "h")):
+    g = state_np(gpu)
+    for k in names:
+        e = slab_err(g[k], getattr(ref, k))
+        assert e <= tol, f"state {k}: slab error {e:.3e} > {tol:.0e}"
+    assert np.allclose(g["rho"], ref.rho, rtol=1e-5, atol=0), "rho"
+
+
+def run_both(q, k, v, *, gamma=None, ridge=0.0, normalize=False, chunk=0, init_gpu=None,
+             init_ref=None):
+    qg, kg, vg = on_gpu(q, k, v)
+    out, den, fin = hla.forward_chunked(qg, kg, vg, gamma=gamma, ridge=ridge, normalize=normalize,
+                                        chunk=chunk, init=init_gpu, return_state=True,
+                                        return_den=True)
+    torch.cuda.synchronize()
+    import oracle
+    r_out, r_den, r_fin = oracle.forward(q, k, v, gamma=gamma, lam=ridge, normalize=normalize,
+                                         init=init_ref)
+    return (out.cpu(), den.cpu(), fin), (r_out, r_den, r_fin)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at their full sizes
+
+@pytest.mark.parametrize("chunk", [16, 64])
+@pytest.mark.parametrize("seed", [1000, 2000, 3000])
+def test_small_fp32_workload(chunk, seed):
+    w = inputs.SMALL_FP32
+    q, k, v = inputs.workload_qkv(w, seed)
+    (o, d, f), (ro, rd, rf) = run_both(q, k, v, chunk=chunk)
+    tol = TOL[torch.float32]
+    assert row_err(o, ro) <= tol
+    assert slab_err(d, rd, lead=2) <= tol
+    check_state(f, rf, tol)
+
+
+@pytest.mark.parametrize("seed", [1001, 2001])
+def test_fwd_d64_workload(seed):
+    w = inputs.FWD_D64
+    q, k, v = inputs.workload_qkv(w, seed)
+    (o, d, f), (ro, rd, rf) = run_both(q, k, v, chunk=w.chunk)
+    tol = TOL[torch.bfloat16]
+    e = row_err(o, ro)
+    print(f"row error {e:.3e}")
+    assert e <= tol
+    assert slab_err(d, rd, lead=2) <= tol
+    check_state(f, rf, tol)
+
+
+def test_ratio_decay_ridge_d64_workload():
+    w = inputs.RATIO_DECAY_D64
+    q, k, v = inputs.workload_qkv(w, 1002)
+    (o, d, f), (ro, rd, rf) = run_both(q, k, v, gamma=w.gamma, ridge=w.ridge, normalize=True,
+                                       chunk=w.chunk)
+    tol = TOL[torch.bfloat16]
+    e, excluded = ratio_err(o, ro, rd)
+    print(f"ratio row error {e:.3e}, excluded rows {excluded}")
+    assert e <= tol
+    assert slab_err(d, rd, lead=2) <= tol
+    check_state(f, rf, tol)
+    # the numerator alone, gated row-wise
+    qg, kg, vg = on_gpu(q, k, v)
+    num, _, _ = hla.forward_chunked(qg, kg, vg, gamma=w.gamma, ridge=w.ridge, chunk=w.chunk)
+    import oracle
+    rnum, _, _ = oracle.forward(q, k, v, gamma=w.gamma, lam=w.ridge, want_state=False)
+    assert row_err(num.cpu(), rnum) <= tol
+
+
+def test_long_d128_workload():
+    w = inputs.LONG_D128
+    q, k, v = inputs.workload_qkv(w, 1003)
+    (o, d, f), (ro, rd, rf) = run_both(q, k, v, gamma=w.gamma, chunk=w.chunk)
+    tol = TOL[torch.bfloat16]
+    e = row_err(o, ro)
+    print(f"row error {e:.3e}")
+    assert e <= tol
+    assert slab_err(d, rd, lead=2) <= tol
+    check_state(f, rf, tol)
+
+
+def decode_setup(B, H, prefix, d, dv, seed, gamma=None, ridge=0.0):
+    """Fold a prefix with the oracle (fp64), round the states to fp32, and hand
+    the same fp32 states to both sides."""
+    import oracle
+    (q, k, v), tok = inputs.decode_inputs(B, H, prefix, d, dv, torch.bfloat16, seed)
+    _, _, st = oracle.forward(q, k, v, gamma=gamma, lam=ridge)
+    st32 = {n: torch.from_numpy(getattr(st, n)).float() for n in ("S", "C", "m", "G", "h", "rho")}
+    ref = oracle.State(*(st32[n].double().numpy() for n in ("S", "C", "m", "G", "h", "rho")))
+    gpu = hla.State(*(st32[n].to(DEV) for n in ("S", "C", "m", "G", "h", "rho")))
+    return tok, gpu, ref
+
+
+def test_decode_workload():
+    w = inputs.DECODE_D128
+    tok, gpu, ref = decode_setup(w.B, w.H, w.n, w.d, w.dv, 1004)
+    q1, k1, v1 = tok
+    qg, kg, vg = on_gpu(q1, k1, v1)
+    out, den = hla.decode_step(qg, kg, vg, gpu, return_den=True)
+    torch.cuda.synchronize()
+    import oracle
+    r_out, r_den, r_st = oracle.decode(ref, q1, k1, v1)
+    tol = TOL[torch.bfloat16]
+    e = row_err(out.cpu(), r_out)
+    print(f"decode row error {e:.3e}")
+    assert e <= tol
+    assert slab_err(den.cpu().reshape(-1, 1), r_den.reshape(-1, 1)) <= tol
+    check_state(gpu, r_st, 1e-5)
+
+
+@pytest.mark.parametrize("gamma,ridge,normalize", [(None, 0.0, False), (0.95, 0.5, True),
+                                                   ("per_head", 1e-3, False)])
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 32), (16, 128)])
+def test_decode_variants(d, dv, gamma, ridge, normalize):
+    B, H = 2, 8
+    g = None
+    if gamma == "per_head":
+        g = inputs.gamma_list_fp32([1 - 2.0 ** -(3 + h) for h in range(H)])
+    elif gamma is not None:
+        g = inputs.gamma_list_fp32([gamma] * H)
+    tok, gpu, ref = decode_setup(B, H, 64, d, dv, 77 + d + dv, gamma=g, ridge=ridge)
+    qg, kg, vg = on_gpu(*tok)
+    out, den = hla.decode_step(qg, kg, vg, gpu, gamma=g, ridge=ridge, normalize=normalize,
+                               return_den=True)
+    import oracle
+    r_out, r_den, r_st = oracle.decode(ref, *tok, gamma=g, lam=ridge, normalize=normalize)
+    tol = TOL[torch.bfloat16]
+    assert row_err(out.cpu(), r_out) <= tol
+    check_state(gpu, r_st, 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# shape and option sweep at small sizes (several chunks and a ragged tail)
+
+SWEEP = [
+    # B, H, n,   d,   dv,  w,  dtype,           gamma,      ridge, normalize
+    (1, 2, 100, 16, 16, 16, torch.float32, None, 0.0, False),
+    (2, 2, 77, 32, 64, 32, torch.float32, "decay", 0.0, False),
+    (1, 3, 130, 64, 16, 64, torch.float32, "per_head", 1.0, False),
+    (1, 1, 300, 128, 128, 128, torch.float32, "decay", 0.0, True),
+    (2, 2, 129, 64, 64, 64, torch.bfloat16, None, 0.0, False),
+    (1, 2, 200, 64, 64, 16, torch.bfloat16, "per_head", 1e-3, True),
+    (1, 2, 257, 128, 64, 128, torch.bfloat16, "decay", 0.0, False),
+    (2, 1, 95, 16, 32, 32, torch.bfloat16, None, 1.0, True),
+    (1, 2, 64, 64, 128, 64, torch.bfloat16, "decay", 0.0, False),
+    (1, 1, 1, 64, 64, 64, torch.bfloat16, None, 0.3, False),
+    (1, 2, 33, 32, 32, 128, torch.float32, None, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"B{c[0]}H{c[1]}n{c[2]}d{c[3]}dv{c[4]}w{c[5]}"
+                                              f"{'bf16' if c[6] == torch.bfloat16 else 'f32'}"
+                                              f"{'-'+c[7] if c[7] else ''}-l{c[8]}{'-norm' if c[9] else ''}"
+                                              for c in SWEEP])
+def test_sweep(case):
+    B, H, n, d, dv, w, dtype, gk, ridge, normalize = case
+    q, k, v = inputs.qkv(B, H, n, d, dv, dtype, seed=500 + n + d + dv + w)
+    g = None
+    if gk == "decay":
+        g = inputs.gamma_list_fp32([0.97] * H)
+    elif gk == "per_head":
+        g = inputs.gamma_list_fp32([1 - 2.0 ** -(3 + h) for h in range(H)])
+    ridge = inputs.ridge_fp32(ridge)
+    (o, dn, f), (ro, rd, rf) = run_both(q, k, v, gamma=g, ridge=ridge, normalize=normalize, chunk=w)
+    tol = TOL[dtype]
+    if normalize:
+        e, _ = ratio_err(o, ro, rd)
+    else:
+        e = row_err(o, ro)
+    assert e <= tol, f"output error {e:.3e}"
+    assert slab_err(dn, rd, lead=2) <= tol
+    check_state(f, rf, max(tol, 1e-5))
+
+
+# ---------------------------------------------------------------------------
+# streaming, state algebra and edge cases
+
+def test_split_point_continuation_on_gpu():
+    B, H, n, d, dv = 2, 4, 300, 64, 64
+    q, k, v = inputs.qkv(B, H, n, d, dv, torch.bfloat16, seed=41)
+    g = inputs.gamma_list_fp32([0.99, 0.995, 1.0, 0.98])
+    qg, kg, vg = on_gpu(q, k, v)
+    p = 133
+    o1, _, s1 = hla.forward_chunked(qg[:, :, :p].contiguous(), kg[:, :, :p].contiguous(),
+                                    vg[:, :, :p].contiguous(), gamma=g, return_state=True)
+    o2, _, s2 = hla.forward_chunked(qg[:, :, p:].contiguous(), kg[:, :, p:].contiguous(),
+                                    vg[:, :, p:].contiguous(), gamma=g, init=s1, return_state=True)
+    import oracle
+    ro, _, rf = oracle.forward(q, k, v, gamma=g)
+    tol = TOL[torch.bfloat16]
+    assert row_err(torch.cat([o1, o2], dim=2).cpu(), ro) <= tol
+    check_state(s2, rf, tol)
+
+
+def test_forward_last_row_equals_decode_on_gpu():
+    B, H, n, d, dv = 1, 4, 200, 64, 64
+    q, k, v = inputs.qkv(B, H, n + 1, d, dv, torch.bfloat16, seed=42)
+    qg, kg, vg = on_gpu(q, k, v)
+    out, _, _ = hla.forward_chunked(qg, kg, vg)
+    _, _, st = hla.forward_chunked(qg[:, :, :n].contiguous(), kg[:, :, :n].contiguous(),
+                                   vg[:, :, :n].contiguous(), return_state=True)
+    o1, _ = hla.decode_step(qg[:, :, n].contiguous(), kg[:, :, n].contiguous(),
+                            vg[:, :, n].contiguous(), st)
+    assert row_err(o1.cpu(), out[:, :, n].cpu()) <= 1e-4
+
+
+def test_compose_matches_oracle():
+    import oracle
+    N, d, dv = 6, 64, 32
+    a = inputs.random_state_fp32(N, d, dv, 1)
+    b = inputs.random_state_fp32(N, d, dv, 2)
+    ga = hla.State(*(t.to(DEV) for t in a))
+    gb = hla.State(*(t.to(DEV) for t in b))
+    r = hla.state_compose(ga, gb)
+    ra = oracle.State(*(t.double().numpy() for t in a))
+    rb = oracle.State(*(t.double().numpy() for t in b))
+    rr = oracle.compose(ra, rb)
+    check_state(r, rr, 1e-5)
+
+
+@pytest.mark.parametrize("d,dv", [(16, 16), (128, 128), (32, 64)])
+def test_compose_of_gpu_segments_equals_whole(d, dv):
+    B, H, n = 1, 2, 150
+    q, k, v = inputs.qkv(B, H, n, d, dv, torch.bfloat16, seed=43)
+    g = inputs.gamma_list_fp32([0.98, 1.0])
+    qg, kg, vg = on_gpu(q, k, v)
+    p = 70
+    _, _, sa = hla.forward_chunked(qg[:, :, :p].contiguous(), kg[:, :, :p].contiguous(),
+                                   vg[:, :, :p].contiguous(), gamma=g, return_state=True)
+    _, _, sb = hla.forward_chunked(qg[:, :, p:].contiguous(), kg[:, :, p:].contiguous(),
+                                   vg[:, :, p:].contiguous(), gamma=g, return_state=True)
+    sab = hla.state_compose(sa, sb)
+    import oracle
+    _, _, rf = oracle.forward(q, k, v, gamma=g)
+    check_state(sab, rf, TOL[torch.bfloat16])
+
+
+def test_empty_sequence_returns_init():
+    N, d, dv = 3, 32, 16
+    a = inputs.random_state_fp32(N, d, dv, 5)
+    init = hla.State(*(t.to(DEV) for t in a))
+    q = torch.empty(1, 3, 0, d, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(1, 3, 0, dv, dtype=torch.bfloat16, device=DEV)
+    out, _, fin = hla.forward_chunked(q, q.clone(), v, init=init, return_state=True,
+                                      gamma=[0.9, 0.8, 0.7])
+    assert out.shape == (1, 3, 0, dv)
+    for name in ("S", "C", "m"):
+        assert torch.equal(getattr(fin, name), getattr(init, name))
+    import oracle
+    # G and h are rebuilt from X = S C - G on the way through: equal to rounding
+    ref = oracle.State(*(t.double().numpy() for t in a))
+    check_state(fin, ref, 1e-5)
+    _, _, z = hla.forward_chunked(q, q.clone(), v, return_state=True)
+    for t in z.tensors()[:5]:
+        assert torch.count_nonzero(t) == 0
+    assert torch.all(z.rho == 1)
+
+
+def test_causality_bitwise():
+    B, H, n, d, dv = 1, 2, 256, 64, 64
+    q, k, v = inputs.qkv(B, H, n, d, dv, torch.bfloat16, seed=44)
+    g = inputs.gamma_list_fp32([0.97, 1.0])
+    qg, kg, vg = on_gpu(q, k, v)
+    out, den, _ = hla.forward_chunked(qg, kg, vg, gamma=g, ridge=0.01, return_den=True)
+    for t in (0, 63, 64, 100, 254):
+        q2, k2, v2 = qg.clone(), kg.clone(), vg.clone()
+        gen = torch.Generator(device="cpu").manual_seed(t)
+        for x in (q2, k2, v2):
+            noise = torch.randn(x[:, :, t + 1:].shape, generator=gen).to(x.dtype).to(DEV)
+            x[:, :, t + 1:] += noise
+        o2, d2, _ = hla.forward_chunked(q2, k2, v2, gamma=g, ridge=0.01, return_den=True)
+        assert torch.equal(o2[:, :, : t + 1], out[:, :, : t + 1]), t
+        assert torch.equal(d2[:, :, : t + 1], den[:, :, : t + 1]), t
+        assert not torch.equal(o2[:, :, t + 1:], out[:, :, t + 1:])
+
+
+def test_deterministic_and_writes_every_output():
+    w = inputs.FWD_D64
+    q, k, v = on_gpu(*inputs.workload_qkv(w, 7))
+    out1 = torch.full((w.B, w.H, w.n, w.dv), float("nan"), device=DEV)
+    den1 = torch.full((w.B, w.H, w.n), float("nan"), device=DEV)
+    hla.forward_chunked(q, k, v, chunk=w.chunk, out=out1, den=den1)
+    out2, den2, _ = hla.forward_chunked(q, k, v, chunk=w.chunk, return_den=True)
+    assert torch.isfinite(out1).all() and torch.isfinite(den1).all()
+    assert torch.equal(out1, out2) and torch.equal(den1, den2)
+
+
+def test_bad_arguments_raise_before_launch():
+    q = torch.zeros(1, 1, 8, 48, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(hla.HlaError, match="UNSUPPORTED"):
+        hla.forward_chunked(q, q, q)
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(hla.HlaError, match="gamma"):
+        hla.forward_chunked(q, q, q, gamma=[1.5])
