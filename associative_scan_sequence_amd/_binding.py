@@ -155,6 +155,7 @@ def _params(B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize):
 
 def workspace_size(B, H, n, d, dv, *, chunk=0, dtype=torch.bfloat16, gamma=None, ridge=0.0,
                    normalize=False) -> int:
+    """Bytes of forward workspace; allocate it zero-filled (``torch.zeros``)."""
     p, _keep = _params(B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize)
     return int(load().hla_forward_workspace_size(ctypes.byref(p)))
 
@@ -184,7 +185,7 @@ def forward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=
     p, _keep = _params(B, H, n, d, dv, chunk, q.dtype, gamma, ridge, normalize)
     need = int(lib.hla_forward_workspace_size(ctypes.byref(p)))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty(B, H, n, dv, dtype=torch.float32, device=dev)
     _need(out, "out", (torch.float32,))

@@ -117,6 +117,10 @@ hla_status check_common(int H, int d, int dv, hla_dtype dtype, const float *gamm
 
 int default_chunk(int d) { return d > 64 ? 128 : 64; }
 
+// Kernel path for a forward call.  init/fin/den only matter for the choice.
+enum class FwdPath { Generic, Fused64 };
+
+
 struct Geometry {
     int w, nc;
 };
@@ -135,6 +139,31 @@ hla_status forward_geometry(const hla_params *p, Geometry *geo) {
     geo->w = w;
     geo->nc = (p->n + w - 1) / w;
     return HLA_OK;
+}
+
+FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *init,
+                    const hla_state *fin, const float *den) {
+    hla::FwdProblem fp{};
+    fp.dtype = p->dtype; fp.d = p->d; fp.dv = p->dv; fp.w = geo.w; fp.n = p->n;
+    fp.ridge = p->ridge; fp.normalize = p->normalize; fp.den = const_cast<float *>(den);
+    if (init) fp.init = *init;
+    if (fin) fp.fin = *fin;
+    if (hla::fused64_supported(fp)) return FwdPath::Fused64;
+    return FwdPath::Generic;
+}
+
+// Workspace bytes for the call: the control block, then the path's data.
+// With state/den unknown (the size query), the largest of the candidate
+// paths is returned.
+size_t workspace_need(const hla_params *p, const Geometry &geo, const hla_state *init,
+                      const hla_state *fin, const float *den) {
+    const int BH = p->B * p->H;
+    const size_t gen = hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w);
+    size_t fused = 0;
+    if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0)
+        fused = hla::fused64_workspace_bytes(BH, p->n);
+    (void)init; (void)fin; (void)den;
+    return hla::kCtrlBytes + (gen > fused ? gen : fused);
 }
 
 }  // namespace
@@ -159,7 +188,7 @@ size_t hla_forward_workspace_size(const hla_params *p) {
     Geometry geo{};
     if (forward_geometry(p, &geo) != HLA_OK) return 0;
     if (!width_ok(p->d) || !width_ok(p->dv)) return 0;
-    return hla::generic_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w);
+    return workspace_need(p, geo, nullptr, nullptr, nullptr);
 }
 
 hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
@@ -185,7 +214,7 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     }
     if (init && (s = check_state(init, "init")) != HLA_OK) return s;
     if (final_state && (s = check_state(final_state, "final_state")) != HLA_OK) return s;
-    const size_t need = hla::generic_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
+    const size_t need = workspace_need(p, geo, init, final_state, den);
     if (need > 0) {
         if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (workspace_bytes < need)
@@ -217,7 +246,15 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     if (final_state) fp.fin = *final_state;
     fp.ws = workspace; fp.ws_bytes = workspace_bytes;
     if (n == 0 && !final_state) return ok();
-    const hipError_t e = hla::generic_forward(fp, stream);
+    char *ws = static_cast<char *>(workspace);
+    hipError_t e;
+    if (choose_path(p, geo, init, final_state, den) == FwdPath::Fused64) {
+        e = hla::fused64_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
+    } else {
+        fp.ws = ws + hla::kCtrlBytes;
+        fp.ws_bytes = workspace_bytes - hla::kCtrlBytes;
+        e = hla::generic_forward(fp, stream);
+    }
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "forward launch: %s", hipGetErrorString(e));
     return ok();
 }

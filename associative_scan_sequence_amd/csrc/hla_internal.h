@@ -37,10 +37,22 @@ struct FwdProblem {
     size_t ws_bytes;
 };
 
+// Every forward workspace starts with a control block of kCtrlBytes: words
+// that the one-launch kernels keep valid across calls (ticket counter,
+// finished-workgroup counter, launch epoch, wait-timeout count).  It must be
+// zero before the first call; path data follows it.
+constexpr size_t kCtrlBytes = 256;
+
 // Generic chunked forward: any d, dv, w in {16,32,64,128}, fp32 or bf16,
 // several kernels over a per-chunk workspace.
 size_t generic_workspace_bytes(int BH, int n, int d, int dv, int w);
 hipError_t generic_forward(const FwdProblem &p, hipStream_t s);
+
+// One-launch MFMA forward for bf16, d = dv = w = 64 (no ridge, denominator,
+// normalisation, init or final state).
+bool fused64_supported(const FwdProblem &p);
+size_t fused64_workspace_bytes(int BH, int n);
+hipError_t fused64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
 
 struct DecodeProblem {
     int B, H, d, dv;

@@ -96,8 +96,10 @@ typedef struct {
 } hla_params;
 
 /* Bytes of device workspace hla_forward_chunked needs for these params
- * (0 for an invalid p).  The workspace holds per-chunk partial summaries;
- * its contents between calls are unspecified. */
+ * (0 for an invalid p).  Its first 256 bytes are a control block (launch
+ * ticket and epoch counters) that the library keeps valid from call to call:
+ * zero-fill the workspace once before its first use and do not write it
+ * afterwards.  The rest holds per-chunk or per-segment partial summaries. */
 size_t hla_forward_workspace_size(const hla_params *p);
 
 /* Chunk-parallel masked forward ([SUM] sec. 4 and 5: token deltas feed an
