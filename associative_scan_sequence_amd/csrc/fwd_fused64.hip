@@ -6,41 +6,61 @@
 // w x w products, and chunk summaries are scanned to give carry-ins.  The
 // carry is held in the corrected form (S, X = S C - G), for which
 //   X_t = g^2 X_{t-1} + S_t q_t v_t^T,   num_t = q_t^T X_t,
-// so both S and X are *linear* scans once S is known (see fwd_generic.hip
-// for the per-chunk formulas).  Per chunk (local token indices t, s):
+// so both S and X are *linear* scans once S is known (fwd_generic.hip gives
+// the per-chunk formulas).  Per chunk (local token indices t, s; length L;
+// e_t = g^(t+1), f_s = g^(L-1-s)):
 //   A   = (Q K^T) o D_g o L                       masked scores
 //   U   = diag(e) Q S0 + A K                      row s = S_s q_s
 //   P   = (Q U^T) o D_{g^2} o L
 //   num = P V + diag(e^2) Q X0
-//   S0 <- g^w S0 + K^T diag(f) K,   X0 <- g^2w X0 + U^T diag(f^2) V
+//   S0 <- g^L S0 + K^T diag(f) K,   X0 <- g^2L X0 + U^T diag(f^2) V
+// U is kept scaled as Us = diag(f^2) U.  Then the X update needs no further
+// scaling, and since g^(2(t-s)) / f_s^2 = 1 / f_t^2 the masked P is
+// (Q Us^T) o L scaled by 1 / f_t^2 per row.  (The kernel is used for
+// g >= 0.75, so f^2 >= 0.75^126 and no scaled value leaves the normal range.)
 //
 // Parallel structure.  One workgroup owns a segment of up to four
 // consecutive chunks of one head and runs two groups of four waves; group 0
 // walks the segment's first two chunks and group 1 the last two, at the same
-// time, so every SIMD holds two waves that hide each other's latency.  Group
-// 1 starts from the key moment and X increment that group 0 accumulates,
-// handed over through LDS.  Three phases, two device-wide rounds:
-//   A: the segment's own key moment sum S_seg (chunk recurrence from 0);
-//      publish it.  Round 1: wait for every earlier segment of the head and
-//      sum their decayed S_seg -> the segment's S carry.
-//   B: walk the chunks with the true S carry and a local X starting at 0:
-//      all masked products, the local part of num (kept in registers), and
-//      the segment's X increment Z_seg; publish it.  Round 2: sum the
-//      decayed Z_seg of every earlier segment -> the segment's X carry.
-//   C: add diag(e^2 g^(2*offset)) Q X_start to num and store.
+// time.  Group 1 starts from the key moment and X increment that group 0
+// accumulates, handed over through LDS.  Two device-wide rounds:
+//   A: the segment's key moment sum S_seg (both chunks, from zero); publish.
+//      While the predecessors' sums travel, compute the carry-free parts of
+//      every chunk: the masked scores A and A K.
+//      Round 1: sum the decayed S_seg of every earlier segment -> S carry.
+//   B: per chunk, U with the true S carry, P, the local part of num (kept in
+//      registers) and the segment's X increment Z_seg; publish.
+//      Round 2: sum the decayed Z_seg of every earlier segment -> X carry.
+//   C: add diag(e^2) Q X0 to num for every chunk and store.
 // Both rounds are plain decayed sums of published aggregates (no serial
-// chain between segments).  Workgroups take logical ids from a ticket
-// counter, so a workgroup only waits on workgroups that started before it.
+// chain between segments).  Heads are dealt to 16 cohorts (head mod 16),
+// each with its own ticket counter in its own control line; a ticket names a
+// (head, segment) with segments handed out in order, so a workgroup only
+// waits on segments that a running workgroup already owns.  Inputs are
+// fetched for the segment the dispatch order predicts while the ticket is in
+// flight.  Flags carry a per-cohort launch epoch, so stale or foreign words
+// in the flag area are never mistaken for a publication; the cohort's last
+// workgroup resets its counters and advances its epoch.
 //
 // Precision.  q, k, v are exact in bf16.  Every operand formed in fp32 (A,
-// U, P, S0, X0, and f-scaled K) is split as x = hi + lo with hi = bf16(x),
+// Us, P, S0, X0, and f-scaled K) is split as x = hi + lo with hi = bf16(x),
 // lo = bf16(x - hi); each such product is two bf16 MFMAs with fp32
 // accumulation, leaving ~2^-16 relative operand error.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16.  Lane l = 16 g + r holds A-operand row r,
-// k = 8g..8g+7; B-operand column r, k = 8g..8g+7; accumulator rows 4g..4g+3
-// of column r.  Each wave owns a 16-token slice of its group's chunk (or a
-// 16-row slice of S and X), so most operands stay wave-private.
+// MFMA v_mfma_f32_16x16x32_bf16: lane l = 16 g + r supplies row r of the A
+// operand and column r of the B operand at k = 8g .. 8g+7, and receives
+// accumulator rows 4g .. 4g+3 of column r.  Two consequences are used:
+//  * an accumulator pair (row blocks 2j, 2j+1) is directly a k-block operand
+//    for a contraction over its row index, with k slot 8g+e holding row
+//    32j+4g+e (e < 4) or 32j+16+4g+(e-4); the other operand is read with the
+//    same slot order;
+//  * operands whose k index runs down the rows of a row-major LDS tile (K,
+//    V, Us read as transposes) are fetched with ds_read_b64_tr_b16: within
+//    each 16-lane group, lane i receives element i&3 of the 8-byte pieces
+//    addressed by lanes (i>>2)+4e, e = 0..3.
+// Each wave owns a 16-token slice of its group's chunk; group 1 takes the
+// slices in reverse order, so every SIMD pairs a light and a heavy slice of
+// the masked (triangular) products.
 #include "device_common.h"
 #include "hla_internal.h"
 
@@ -48,22 +68,30 @@ namespace hla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int W = 64;        // chunk width = d = dv
-constexpr int LDR = 72;      // padded LDS row, in bf16 elements (144 bytes)
+constexpr int W = 64;          // chunk width = d = dv
+constexpr int LDR = 72;        // padded LDS row, in bf16 elements (144 bytes)
 constexpr int kThreads = 512;  // two groups of four waves
 constexpr int kPerGroup = 2;   // chunks per wave group
 constexpr int kMaxL = 4;       // chunks per workgroup
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kCohorts = 16;   // ticket counters
+constexpr int kLine = 64;      // words per 256-byte control line
+constexpr float kMinGamma = 0.75f;
+static_assert(kCtrlBytes >= (1 + kCohorts) * kLine * 4, "control block too small");
 
 struct FusedArgs {
     int H, n, nc, P, L, BH;
     const uint16_t *q, *k, *v;
     float *out;
-    uint32_t *ctrl;   // [0] ticket, [1] done, [2] epoch, [3] wait-timeout count
-    uint32_t *flag1, *flag2;  // [BH * P]
-    float *aggS, *aggZ;       // [BH * P][4096], in accumulator-tile order
+    uint32_t *ctrl;     // line 0: [2] launch count, [3] wait-timeout count;
+                        // line 1+i, cohort i: [0] ticket, [1] finished, [2] epoch
+    uint32_t *flags;    // [BH * P][2]: epoch when the S sum / X increment was published
+    float *aggS, *aggX; // [BH * P][4096], in accumulator order
     GammaTab gam;
 };
 
@@ -71,57 +99,76 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 8 consecutive bf16 of one LDS row
 __device__ __forceinline__ bf16x8 ld8(const __bf16 *base, int row, int col) {
     return *reinterpret_cast<const bf16x8 *>(base + row * LDR + col);
 }
 
-// hi = bf16(x), lo = bf16(x - hi), 4 values
-__device__ __forceinline__ void split4(const f32x4 &x, uint2 &hi, uint2 &lo) {
-    typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-    bf4 h, l;
+// Transposed operand: lane (g, r) receives M[rb1 + e][col0 + r] (k slots 8g+e,
+// e < 4) and M[rb2 + e][col0 + r] (slots 8g+4+e); rb1, rb2 may depend on g.
+__device__ __forceinline__ bf16x8 tr8(const __bf16 *M, int rb1, int rb2, int col0, int r) {
+    const int col = col0 + 4 * (r & 3);
+    const __bf16 *p1 = M + (rb1 + (r >> 2)) * LDR + col;
+    const __bf16 *p2 = M + (rb2 + (r >> 2)) * LDR + col;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p2));
+    bf16x8 x;
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        h[i] = static_cast<__bf16>(x[i]);
-        l[i] = static_cast<__bf16>(x[i] - static_cast<float>(h[i]));
+        x[i] = ab[i];
+        x[4 + i] = bb[i];
     }
-    hi = *reinterpret_cast<uint2 *>(&h);
-    lo = *reinterpret_cast<uint2 *>(&l);
+    return x;
 }
 
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+// hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         hi[i] = static_cast<__bf16>(x[i]);
         lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
     }
 }
 
-__device__ __forceinline__ void st4(__bf16 *base, int row, int col, uint2 v) {
-    *reinterpret_cast<uint2 *>(base + row * LDR + col) = v;
+// k-block operand from an accumulator pair (rows 32j+4g+e, 32j+16+4g+e)
+__device__ __forceinline__ void pair_operand(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
+    bf16x4 h0, l0, h1, l1;
+    split4(t0, h0, l0);
+    split4(t1, h1, l1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = h0[i];
+        hi[4 + i] = h1[i];
+        lo[i] = l0[i];
+        lo[4 + i] = l1[i];
+    }
 }
 
-__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u + 1013904223u; }
+__device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4 &v) {
+    *reinterpret_cast<bf16x4 *>(base + row * LDR + col) = v;
+}
 
 // Cross-workgroup hand-off without cache maintenance: aggregates and flags
-// are written and read with agent-scope relaxed atomics, which gfx950 issues
-// as device-coherent (sc1) accesses, so no L2 write-back or invalidate is
-// needed.  The writer waits for its stores to complete (vmcnt 0) before the
-// workgroup barrier that precedes the flag store; readers poll the flag and
-// only then load the aggregate.
+// are written and read as device-coherent (sc1) accesses, so no L2
+// write-back or invalidate is needed.  The writer waits for its stores to
+// complete (vmcnt 0) before the workgroup barrier that precedes the flag
+// store; readers poll the flag and only then load the aggregate.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e, int cohort) {
+    return e * 1664525u + (1013904223u + 2u * static_cast<uint32_t>(cohort));  // one LCG stream per cohort
+}
 
 __device__ bool wait_flag(const uint32_t *f, uint32_t want) {
     for (int it = 0; it < kSpinLimit; ++it) {
         if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(1);
     }
     return false;
 }
 
-// 16 floats of this thread's accumulator tiles, stored and loaded as 16-byte
-// device-coherent (sc1) buffer accesses.  Each aggregate slot is 16 KB; the
-// thread's 64 bytes sit at byte offset 64 * tid.
-constexpr int kSc1 = 16;  // cache policy: sc1 (device scope)
+constexpr int kSc1 = 16;  // buffer cache policy: sc1 (device scope)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
     // slot addresses are uniform across the wave; say so, so the descriptor is scalar
@@ -132,17 +179,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, 16384, 0x00020000);
 }
 
-__device__ __forceinline__ void put16(const float *slot, int tid, const f32x4 (&x)[4]) {
+// A group's 16 floats per thread (4 accumulator tiles) <-> a 16 KB slot; the
+// thread's 64 bytes sit at byte offset 64 * xi, xi = its tile position.
+__device__ __forceinline__ void put16(const float *slot, int xi, const f32x4 (&x)[4]) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 64 * tid + 16 * b, 0, kSc1);
+    for (int b = 0; b < 4; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 64 * xi + 16 * b, 0, kSc1);
 }
 
-// acc += sum over n slots of scale[i] * slot_i (this thread's 16 floats);
-// all loads of a batch are issued before the first add.
+// acc += sum over n slots of scale[i] * slot_i; all loads of a batch are
+// issued before the first add.
 template <int NB>
 __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&slots)[NB],
-                                          const float (&scale)[NB], int n, int tid) {
+                                          const float (&scale)[NB], int n, int xi) {
     f32x4 v[NB][4];
 #pragma unroll
     for (int s = 0; s < NB; ++s)
@@ -150,7 +199,7 @@ __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&
             const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slots[s]);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                v[s][b] = __builtin_amdgcn_raw_buffer_load_b128(rs, 64 * tid + 16 * b, 0, kSc1);
+                v[s][b] = __builtin_amdgcn_raw_buffer_load_b128(rs, 64 * xi + 16 * b, 0, kSc1);
         }
 #pragma unroll
     for (int s = 0; s < NB; ++s)
@@ -162,186 +211,223 @@ __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&
 
 // LDS of one wave group: 8 padded 64 x 64 bf16 tiles (72 KB).
 struct GroupLds {
-    __bf16 KT[W * LDR];   // K^T [a][s]
-    __bf16 VT[W * LDR];   // V^T [j][s]
-    __bf16 APh[W * LDR];  // A then P, [t][s] (rows private to the owning wave)
-    __bf16 APl[W * LDR];
-    __bf16 Uh[W * LDR];   // staging: K rows (Uh) and V rows (Ul); then U [s][a]
+    __bf16 K[kPerGroup][W * LDR];  // key rows [s][a] of the group's chunks
+    __bf16 V[kPerGroup][W * LDR];  // value rows [s][j]
+    __bf16 Uh[W * LDR];            // Us rows [s][b], hi and lo
     __bf16 Ul[W * LDR];
-    __bf16 STh[W * LDR];  // S0 (symmetric, [a][b]) then X0^T ([j][a]) of the chunk
-    __bf16 STl[W * LDR];
+    __bf16 Sh[W * LDR];            // S0 (symmetric) of the chunk; in phase C X0 as [a][j]
+    __bf16 Sl[W * LDR];
 };
 
 struct Smem {
     GroupLds grp[2];
-    float pw[2 * W + 2];  // g^k, k = 0 .. 2W+1
-    uint32_t misc[4];
+    int ticket;
+    uint32_t epoch;
 };
 
+template <bool DECAY>
 __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, grp = tid >> 8, wt = tid & 255;
-    const int w = wt >> 6, l = wt & 63, r = l & 15, g = l >> 4;
+    const int wv = wt >> 6, l = wt & 63, r = l & 15, g = l >> 4;
+    const int w = grp == 0 ? wv : 3 - wv;  // this wave's 16-token slice
+    const int xi = 64 * w + l;  // position of this thread's tiles in exchanges and aggregate slots
     GroupLds &G = sm.grp[grp];
-    const int total = a.BH * a.P;
-
-    // ---- logical workgroup id from the ticket counter, and the launch epoch
+    // ---- ticket: (head, segment) from the cohort counter of the predicted head
+    const int hslot = static_cast<int>(blockIdx.x) % a.BH;
+    const int coh = hslot % kCohorts;
+    const int hc = (a.BH - 1 - coh) / kCohorts + 1;  // heads in this cohort
+    const int guess = (static_cast<int>(blockIdx.x) / a.BH) * hc + hslot / kCohorts;
+    uint32_t *cl = a.ctrl + kLine * (1 + coh);
+    uint32_t tk_raw = 0, ep_raw = 0;
     if (tid == 0) {
-        sm.misc[0] = __hip_atomic_fetch_add(&a.ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.misc[1] = next_epoch(__hip_atomic_load(&a.ctrl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        tk_raw = __hip_atomic_fetch_add(&cl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ep_raw = __hip_atomic_load(&cl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- global loads of this group's chunks (issued for the predicted segment)
+    uint4 kreg[kPerGroup][2], vreg[kPerGroup][2];
+    bf16x8 qn[kPerGroup][2];  // q of token 16w+r, features 32ks+8g..: B operand
+    const int t = 16 * w + r;  // this lane's token (column of the B operand)
+    auto issue_loads = [&](int tk) {
+        const int bh_ = coh + kCohorts * (tk % hc), p_ = tk / hc;
+        const size_t head_tok_ = static_cast<size_t>(bh_) * a.n;
+        const int c0_ = p_ * a.L;
+        const int Lseg_ = min(a.L, a.nc - c0_);
+#pragma unroll
+        for (int jj = 0; jj < kPerGroup; ++jj) {
+            const int j = kPerGroup * grp + jj;
+            const int Lc = j < Lseg_ ? min(W, a.n - (c0_ + j) * W) : 0;
+            const size_t tok0 = head_tok_ + static_cast<size_t>(c0_ + j) * W;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
+                if (row < Lc) {
+                    kreg[jj][u] = *reinterpret_cast<const uint4 *>(a.k + (tok0 + row) * W + cg * 8);
+                    vreg[jj][u] = *reinterpret_cast<const uint4 *>(a.v + (tok0 + row) * W + cg * 8);
+                } else {
+                    kreg[jj][u] = make_uint4(0, 0, 0, 0);
+                    vreg[jj][u] = make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint4 x = make_uint4(0, 0, 0, 0);
+                if (t < Lc) x = *reinterpret_cast<const uint4 *>(a.q + (tok0 + t) * W + 32 * ks + 8 * g);
+                qn[jj][ks] = __builtin_bit_cast(bf16x8, x);
+            }
+        }
+    };
+    issue_loads(guess);
+    if (tid == 0) {
+        sm.ticket = static_cast<int>(tk_raw);
+        sm.epoch = next_epoch(ep_raw, coh);
     }
     __syncthreads();
-    // wave-uniform (SGPR) copies, so slot addresses and buffer descriptors stay scalar
-    const int ticket = __builtin_amdgcn_readfirstlane(static_cast<int>(sm.misc[0]));
-    const uint32_t epoch = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.misc[1])));
-    const int p = ticket / a.BH, bh = ticket % a.BH;
-    const int c0 = p * a.L;
-    const int Lseg = min(a.L, a.nc - c0);           // chunks in this segment (>= 1)
-    const int jbase = kPerGroup * grp;               // first segment-local chunk of this group
-    const int nmine = max(0, min(kPerGroup, Lseg - jbase));
+    const int tk = __builtin_amdgcn_readfirstlane(sm.ticket);
+    const uint32_t epoch = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch)));
+    if (tk < 0 || tk >= hc * a.P) {  // a control block that was not zero: do nothing, report it
+        if (tid == 0) __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (tk != guess) issue_loads(tk);  // dispatch order differed from the prediction
+    const int bh = coh + kCohorts * (tk % hc), p = tk / hc;
+    const size_t head_tok = static_cast<size_t>(bh) * a.n;
     const float gam = head_gamma(a.gam, bh % a.H);
-    const bool decay = gam != 1.0f;
-    for (int i = tid; i < 2 * W + 2; i += kThreads) sm.pw[i] = gpow(gam, i);
+    const float lg = DECAY ? log2f(gam) : 0.0f;
+    auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
+
+    const int c0 = p * a.L;
+    const int Lseg = min(a.L, a.nc - c0);  // chunks in this segment (>= 1)
+    const int jbase = kPerGroup * grp;
+    const int nmine = max(0, min(kPerGroup, Lseg - jbase));
     auto chunk_len = [&](int j) { return min(W, a.n - (c0 + j) * W); };
     int lenA = 0, lenB = 0;  // tokens covered by group 0 and group 1
     for (int j = 0; j < Lseg; ++j) (j < kPerGroup ? lenA : lenB) += chunk_len(j);
+    const int len0 = nmine > 0 ? chunk_len(jbase) : 0;  // this group's first chunk
 
-    // ---- issue every global load of this group's chunks up front
-    uint4 kreg[kPerGroup][2], vreg[kPerGroup][2];
-    bf16x8 qf[kPerGroup][2];
-    const size_t head_tok = static_cast<size_t>(bh) * a.n;
-    const int t = 16 * w + r;  // this lane's token (column of the transposed tiles)
+    // ---- stage key and value rows
 #pragma unroll
-    for (int jj = 0; jj < kPerGroup; ++jj) {
-        const int c = c0 + jbase + jj;
-        const int Lc = (jj < nmine) ? chunk_len(jbase + jj) : 0;
-        const size_t tok0 = head_tok + static_cast<size_t>(c) * W;
+    for (int jj = 0; jj < kPerGroup; ++jj)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-            if (row < Lc) {
-                kreg[jj][u] = *reinterpret_cast<const uint4 *>(a.k + (tok0 + row) * W + cg * 8);
-                vreg[jj][u] = *reinterpret_cast<const uint4 *>(a.v + (tok0 + row) * W + cg * 8);
-            } else {
-                kreg[jj][u] = make_uint4(0, 0, 0, 0);
-                vreg[jj][u] = make_uint4(0, 0, 0, 0);
-            }
+            *reinterpret_cast<uint4 *>(&G.K[jj][row * LDR + cg * 8]) = kreg[jj][u];
+            *reinterpret_cast<uint4 *>(&G.V[jj][row * LDR + cg * 8]) = vreg[jj][u];
         }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (t < Lc) x = *reinterpret_cast<const uint4 *>(a.q + (tok0 + t) * W + 32 * ks + 8 * g);
-            qf[jj][ks] = *reinterpret_cast<bf16x8 *>(&x);
-        }
-    }
-    __syncthreads();  // pw ready
-
-    // Staging a chunk: K rows (Uh) and V rows (Ul) are written row-major with
-    // 16-byte stores; after a barrier every thread gathers 8 consecutive
-    // tokens of one feature (conflict-free 2-byte reads along a row) into one
-    // 16-byte row of K^T and V^T.
-    auto stage_rows = [&](int jj, bool with_v) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-            *reinterpret_cast<uint4 *>(&G.Uh[row * LDR + cg * 8]) = kreg[jj][u];
-            if (with_v) *reinterpret_cast<uint4 *>(&G.Ul[row * LDR + cg * 8]) = vreg[jj][u];
-        }
-    };
-    auto stage_transpose = [&](bool with_v) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int task = wt + 256 * u, f = task & 63, blk = task >> 6;
-            bf16x8 x;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = G.Uh[(8 * blk + i) * LDR + f];
-            *reinterpret_cast<bf16x8 *>(&G.KT[f * LDR + 8 * blk]) = x;
-            if (with_v) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = G.Ul[(8 * blk + i) * LDR + f];
-                *reinterpret_cast<bf16x8 *>(&G.VT[f * LDR + 8 * blk]) = x;
-            }
-        }
-    };
-    // acc[bb] (rows 16w.., cols 16bb..) = rho * acc + K^T diag(f) K over the staged chunk
-    auto s_update = [&](f32x4 (&acc)[4], int Lc) {
-        const float rho = sm.pw[Lc];
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) acc[bb] *= rho;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 kt = ld8(G.KT, 16 * w + r, 32 * ks + 8 * g);
-            bf16x8 kb[4];
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) kb[bb] = ld8(G.KT, 16 * bb + r, 32 * ks + 8 * g);
-            if (!decay) {
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(kt, kb[bb], acc[bb]);
-            } else {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int s = 32 * ks + 8 * g + i;
-                    const float f = s < Lc ? sm.pw[Lc - 1 - s] : 0.0f;
-                    x[i] = f * static_cast<float>(kt[i]);
-                }
-                bf16x8 h, lo;
-                split8(x, h, lo);
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(h, kb[bb], acc[bb]);
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(lo, kb[bb], acc[bb]);
-            }
-        }
-    };
-    // a 16-float accumulator set <-> a float scratch area in LDS (group exchange)
-    float *xch = reinterpret_cast<float *>(sm.grp[1].STh);  // 16 KB inside group 1's ST tiles
-    auto put_xch = [&](const f32x4 (&x)[4]) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch + wt * 16 + 4 * b) = x[b];
-    };
-    auto get_xch = [&](f32x4 (&x)[4]) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) x[b] = *reinterpret_cast<const f32x4 *>(xch + wt * 16 + 4 * b);
-    };
+    __syncthreads();
     const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ================= phase A: the segment's key moment sum ==================
-    // Each group sums its own chunks; group 1 then adds group 0's sum.
-    f32x4 sacc[4], part[4];
+    // acc (rows a = 16w+4g+c, cols b = 16bb+r) = K^T diag(f) K of one chunk
+    f32x4 sc0[4], sg[4];  // first chunk's sum, group sum
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) sacc[bb] = zero4;
+    for (int bb = 0; bb < 4; ++bb) sc0[bb] = sg[bb] = zero4;
 #pragma unroll
     for (int jj = 0; jj < kPerGroup; ++jj) {
-        const bool valid = jj < nmine;
-        if (valid) stage_rows(jj, false);
-        __syncthreads();
-        if (valid) stage_transpose(false);
-        __syncthreads();
-        if (valid) s_update(sacc, chunk_len(jbase + jj));
+        if (jj < nmine) {
+            const int Lc = chunk_len(jbase + jj);
+            f32x4 acc[4];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) acc[bb] = zero4;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rb = 32 * ks + 8 * g;
+                const bf16x8 ka = tr8(G.K[jj], rb, rb + 4, 16 * w, r);
+                bf16x8 kb[4];
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) kb[bb] = tr8(G.K[jj], rb, rb + 4, 16 * bb, r);
+                if (!DECAY) {
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(ka, kb[bb], acc[bb]);
+                } else {
+                    f32x4 x0, x1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x0[e] = gp(static_cast<float>(Lc - 1 - (rb + e))) * static_cast<float>(ka[e]);
+                        x1[e] = gp(static_cast<float>(Lc - 1 - (rb + 4 + e))) * static_cast<float>(ka[4 + e]);
+                    }
+                    bf16x8 h, lo;
+                    pair_operand(x0, x1, h, lo);
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(h, kb[bb], acc[bb]);
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(lo, kb[bb], acc[bb]);
+                }
+            }
+            const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                if (jj == 0) sc0[bb] = acc[bb];
+                sg[bb] = rho * sg[bb] + acc[bb];
+            }
+        }
     }
-    __syncthreads();  // group 1's ST tiles are free for the exchange
-    if (grp == 0) put_xch(sacc);
+    // group 0 hands its sum to group 1, which publishes the segment sum
+    float *xch = reinterpret_cast<float *>(sm.grp[1].Uh);  // 16 KB inside group 1's U tiles
+    if (grp == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch + xi * 16 + 4 * b) = sg[b];
+    }
     __syncthreads();
     const size_t slot = static_cast<size_t>(bh) * a.P + p;
+    f32x4 partA[4];  // group 0's sum (group 1 only)
     if (grp == 1) {
-        get_xch(part);  // group 0's sum S_A
-        f32x4 seg[4];
-        const float rhoB = sm.pw[lenB];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) seg[b] = rhoB * part[b] + sacc[b];
-        put16(a.aggS + slot * 4096, wt, seg);
+        for (int b = 0; b < 4; ++b) partA[b] = *reinterpret_cast<const f32x4 *>(xch + xi * 16 + 4 * b);
+        f32x4 seg[4];
+        const float rhoB = gp(static_cast<float>(lenB));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) seg[b] = rhoB * partA[b] + sg[b];
+        put16(a.aggS + slot * 4096, xi, seg);
         wait_stores();
     }
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(&a.flag1[slot], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&a.flags[2 * slot], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // ---- round 1: S carry = sum over earlier segments of g^(gap) S_seg
+    // ---- carry-free work while the predecessors' sums travel:
+    // A^T tiles of this wave's tokens, then Uloc^T = K^T A^T (rows b, cols t)
+    f32x4 uloc[kPerGroup][4];
+#pragma unroll
+    for (int jj = 0; jj < kPerGroup; ++jj) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) uloc[jj][bb] = zero4;
+        if (jj < nmine) {
+            f32x4 at[4];  // A^T[i = 16ib+4g+c][t], masked and decayed
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                at[ib] = zero4;
+                if (ib <= w) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) at[ib] = mfma(ld8(G.K[jj], 16 * ib + r, 32 * ks + 8 * g), qn[jj][ks], at[ib]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int i = 16 * ib + 4 * g + c;
+                        at[ib][c] = i <= t ? gp(static_cast<float>(t - i)) * at[ib][c] : 0.0f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks <= w) {
+                    bf16x8 ah, al;
+                    pair_operand(at[2 * ks], at[2 * ks + 1], ah, al);
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) {
+                        const bf16x8 kt = tr8(G.K[jj], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * bb, r);
+                        uloc[jj][bb] = mfma(kt, ah, uloc[jj][bb]);
+                        uloc[jj][bb] = mfma(kt, al, uloc[jj][bb]);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- carry = sum over earlier segments pp of g^(pw * gap) * agg[pp] (gap =
+    // tokens between); the groups each load every other predecessor and swap
+    // their partial sums through LDS (the U tiles, unused here).
     const int seg_tokens = a.L * W;
-    // carry = sum over earlier segments pp of g^(pwr * gap) * agg[pp] (gap = tokens
-    // between).  The two groups each load every other predecessor and swap their
-    // partial sums through LDS, so each aggregate is read once per workgroup.
-    auto sum_earlier = [&](f32x4 (&acc)[4], const float *agg, int pwr) {
+    auto sum_earlier = [&](f32x4 (&acc)[4], const float *agg, int pw) {
         constexpr int NB = 4;
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[b] = zero4;
@@ -354,335 +440,251 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                 const int pp = min(p0 + 2 * s2, p - 1);
                 if (p0 + 2 * s2 < p) ++cnt;
                 slots[s2] = agg + (static_cast<size_t>(bh) * a.P + pp) * 4096;
-                scale[s2] = decay ? powf(gam, static_cast<float>(pwr * (p - 1 - pp) * seg_tokens)) : 1.0f;
+                scale[s2] = gp(static_cast<float>(pw * (p - 1 - pp) * seg_tokens));
             }
-            add_slots<NB>(acc, slots, scale, cnt, wt);
+            add_slots<NB>(acc, slots, scale, cnt, xi);
         }
-        float *mine = reinterpret_cast<float *>(sm.grp[grp].STh);
-        const float *other = reinterpret_cast<const float *>(sm.grp[grp ^ 1].STh);
-        __syncthreads();  // both ST areas free
+        float *mine = reinterpret_cast<float *>(sm.grp[grp].Uh);
+        const float *other = reinterpret_cast<const float *>(sm.grp[grp ^ 1].Uh);
+        __syncthreads();  // both U areas free
 #pragma unroll
-        for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(mine + wt * 16 + 4 * b) = acc[b];
+        for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(mine + xi * 16 + 4 * b) = acc[b];
         __syncthreads();
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[b] += *reinterpret_cast<const f32x4 *>(other + wt * 16 + 4 * b);
+        for (int b = 0; b < 4; ++b) acc[b] += *reinterpret_cast<const f32x4 *>(other + xi * 16 + 4 * b);
+        __syncthreads();  // U areas may be written again
     };
-    for (int pp = tid; pp < p; pp += kThreads)
-        if (!wait_flag(&a.flag1[static_cast<size_t>(bh) * a.P + pp], epoch))
-            __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+    auto wait_round = [&](int which) {
+        for (int pp = tid; pp < p; pp += kThreads)
+            if (!wait_flag(&a.flags[2 * (static_cast<size_t>(bh) * a.P + pp) + which], epoch))
+                __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+    };
+
+    // ---- round 1: the S carry at this group's first chunk
+    wait_round(0);
+    f32x4 s0[4];
     {
         f32x4 carry[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) carry[b] = zero4;
         sum_earlier(carry, a.aggS, 1);
-        const float rhoA = sm.pw[lenA];
+        const float rhoA = gp(static_cast<float>(lenA));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) sacc[b] = grp == 0 ? carry[b] : rhoA * carry[b] + part[b];
+        for (int b = 0; b < 4; ++b) s0[b] = grp == 0 ? carry[b] : rhoA * carry[b] + partA[b];
     }
-    __syncthreads();  // exchange area read; ST tiles may be written
-    // S0 (symmetric) -> ST as hi/lo: element (row 16w+4g+i, col 16bb+r) stored at [16bb+r][16w+4g+i]
-    auto write_s = [&]() {
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            uint2 h, lo;
-            split4(sacc[bb], h, lo);
-            st4(G.STh, 16 * bb + r, 16 * w + 4 * g, h);
-            st4(G.STl, 16 * bb + r, 16 * w + 4 * g, lo);
-        }
-    };
-    f32x4 xacc[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) xacc[jb] = zero4;
-    // X0 -> ST as hi/lo transposed: element (row a=16w+4g+i, col j=16jb+r) at [j][a]
-    auto write_x = [&]() {
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            uint2 h, lo;
-            split4(xacc[jb], h, lo);
-            st4(G.STh, 16 * jb + r, 16 * w + 4 * g, h);
-            st4(G.STl, 16 * jb + r, 16 * w + 4 * g, lo);
-        }
-    };
-    write_s();
 
     // ================= phase B: each group walks its chunks ===================
-    // num keeps P V only; the X0 term of each chunk is added in phase C, so the
-    // local X at the start of the group's second chunk is saved here.
     f32x4 num[kPerGroup][4];
-    f32x4 xsave[4];
+    f32x4 xacc[4], xsave[4];  // X^T increment, rows j = 16w+4g+c, cols a = 16ab+r
 #pragma unroll
-    for (int b = 0; b < 4; ++b) xsave[b] = zero4;
+    for (int b = 0; b < 4; ++b) xacc[b] = xsave[b] = zero4;
 #pragma unroll
     for (int jj = 0; jj < kPerGroup; ++jj) {
         const bool valid = jj < nmine;
-        const bool x0_local_save = jj == 1;
         const int Lc = valid ? chunk_len(jbase + jj) : 0;
-        if (valid) stage_rows(jj, true);
-        __syncthreads();  // (1) rows staged; S0 of this chunk in ST
-        // transposes, and P1: A^T[:, t] = K q_t, masked and decayed -> A rows.
-        // All four key blocks are computed: the last wave needs all of them, so
-        // skipping masked blocks in the others would not shorten the chunk.
+        // S0 -> LDS as hi/lo; lane holds S0[a = 16w+4g+c][b = 16bb+r] = S0[b][a]
         if (valid) {
-            stage_transpose(true);
-            f32x4 acc[4];
-            bf16x8 kf[2][4];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) kf[ks][sb] = ld8(G.Uh, 16 * sb + r, 32 * ks + 8 * g);
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) acc[sb] = mfma(kf[ks][sb], qf[jj][ks], acc[sb]);
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                if (decay) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * sb + 4 * g + i;
-                        acc[sb][i] = (s <= t) ? sm.pw[t - s] * acc[sb][i] : 0.0f;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[sb][i] = (16 * sb + 4 * g + i <= t) ? acc[sb][i] : 0.0f;
-                }
-                uint2 h, lo;
-                split4(acc[sb], h, lo);
-                st4(G.APh, t, 16 * sb + 4 * g, h);
-                st4(G.APl, t, 16 * sb + 4 * g, lo);
+            for (int bb = 0; bb < 4; ++bb) {
+                bf16x4 h, lo;
+                split4(s0[bb], h, lo);
+                st4(G.Sh, 16 * bb + r, 16 * w + 4 * g, h);
+                st4(G.Sl, 16 * bb + r, 16 * w + 4 * g, lo);
             }
         }
-        __syncthreads();  // (2) K^T, V^T ready; staging rows consumed
-        // P2: U^T[:, t] = e_t S0 q_t + K^T A^T[:, t]  -> U rows
+        __syncthreads();  // (1) S0 ready; previous chunk's Us reads done
         if (valid) {
-            const float e = sm.pw[t + 1];
-            f32x4 acc[4];
+            // U^T[b][t] = e_t (S0 q_t)[b] + Uloc^T[b][t]; stored as Us = f_t^2 U rows
+            const float e = gp(static_cast<float>(t + 1));
+            const float f2 = t < Lc ? gp(static_cast<float>(2 * (Lc - 1 - t))) : 0.0f;
 #pragma unroll
-            for (int ab = 0; ab < 4; ++ab) acc[ab] = zero4;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 sh[4], sl[4];
-#pragma unroll
-                for (int ab = 0; ab < 4; ++ab) {
-                    sh[ab] = ld8(G.STh, 16 * ab + r, 32 * ks + 8 * g);
-                    sl[ab] = ld8(G.STl, 16 * ab + r, 32 * ks + 8 * g);
-                }
-#pragma unroll
-                for (int ab = 0; ab < 4; ++ab) acc[ab] = mfma(sh[ab], qf[jj][ks], acc[ab]);
-#pragma unroll
-                for (int ab = 0; ab < 4; ++ab) acc[ab] = mfma(sl[ab], qf[jj][ks], acc[ab]);
-            }
-#pragma unroll
-            for (int ab = 0; ab < 4; ++ab) acc[ab] *= e;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ah = ld8(G.APh, t, 32 * ks + 8 * g);
-                const bf16x8 al = ld8(G.APl, t, 32 * ks + 8 * g);
-                bf16x8 kt[4];
-#pragma unroll
-                for (int ab = 0; ab < 4; ++ab) kt[ab] = ld8(G.KT, 16 * ab + r, 32 * ks + 8 * g);
-#pragma unroll
-                for (int ab = 0; ab < 4; ++ab) acc[ab] = mfma(kt[ab], ah, acc[ab]);
-#pragma unroll
-                for (int ab = 0; ab < 4; ++ab) acc[ab] = mfma(kt[ab], al, acc[ab]);
-            }
-#pragma unroll
-            for (int ab = 0; ab < 4; ++ab) {
-                uint2 h, lo;
-                split4(acc[ab], h, lo);
-                st4(G.Uh, t, 16 * ab + 4 * g, h);
-                st4(G.Ul, t, 16 * ab + 4 * g, lo);
-            }
-        }
-        __syncthreads();  // (3) all rows of U; S0 reads done
-        // P3: P^T[:, t] = U q_t, masked, decayed by g^(2(t-s)) -> P rows (private)
-        // P4: num^T[:, t] = V^T P^T[:, t]  (the X0 term is added in phase C)
-        if (x0_local_save) xsave[0] = xacc[0], xsave[1] = xacc[1], xsave[2] = xacc[2], xsave[3] = xacc[3];
-        if (valid) {
-            {
-                f32x4 acc[4];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4;
+            for (int bb = 0; bb < 4; ++bb) {
+                f32x4 acc = zero4;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 uh[4], ul[4];
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) {
-                        uh[sb] = ld8(G.Uh, 16 * sb + r, 32 * ks + 8 * g);
-                        ul[sb] = ld8(G.Ul, 16 * sb + r, 32 * ks + 8 * g);
-                    }
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) acc[sb] = mfma(uh[sb], qf[jj][ks], acc[sb]);
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) acc[sb] = mfma(ul[sb], qf[jj][ks], acc[sb]);
+                    acc = mfma(ld8(G.Sh, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
+                    acc = mfma(ld8(G.Sl, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
                 }
+                const f32x4 us = f2 * (e * acc + uloc[jj][bb]);
+                bf16x4 h, lo;
+                split4(us, h, lo);
+                st4(G.Uh, t, 16 * bb + 4 * g, h);
+                st4(G.Ul, t, 16 * bb + 4 * g, lo);
+            }
+        }
+        __syncthreads();  // (2) every Us row ready
+        if (valid) {
+            // P^T[s][t] = (Us_s . q_t) / f_t^2 for s <= t
+            const float inv_f2 = t < Lc ? gp(static_cast<float>(-2 * (Lc - 1 - t))) : 0.0f;
+            f32x4 pt[4];
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    if (decay) {
+            for (int sb = 0; sb < 4; ++sb) {
+                pt[sb] = zero4;
+                if (sb <= w) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int s = 16 * sb + 4 * g + i;
-                            acc[sb][i] = (s <= t) ? sm.pw[2 * (t - s)] * acc[sb][i] : 0.0f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[sb][i] = (16 * sb + 4 * g + i <= t) ? acc[sb][i] : 0.0f;
+                    for (int kb = 0; kb < 2; ++kb) {
+                        pt[sb] = mfma(ld8(G.Uh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                        pt[sb] = mfma(ld8(G.Ul, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
                     }
-                    uint2 h, lo;
-                    split4(acc[sb], h, lo);
-                    st4(G.APh, t, 16 * sb + 4 * g, h);
-                    st4(G.APl, t, 16 * sb + 4 * g, lo);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) pt[sb][c] = 16 * sb + 4 * g + c <= t ? inv_f2 * pt[sb][c] : 0.0f;
                 }
             }
-            f32x4 acc[4];
+            // num^T[j][t] = sum_s V^T[j][s] P[t][s]
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4;
+            for (int jb = 0; jb < 4; ++jb) num[jj][jb] = zero4;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ph = ld8(G.APh, t, 32 * ks + 8 * g);
-                const bf16x8 pl = ld8(G.APl, t, 32 * ks + 8 * g);
-                bf16x8 vt[4];
+                if (2 * ks <= w) {
+                    bf16x8 ph, pl;
+                    pair_operand(pt[2 * ks], pt[2 * ks + 1], ph, pl);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) vt[jb] = ld8(G.VT, 16 * jb + r, 32 * ks + 8 * g);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma(vt[jb], ph, acc[jb]);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma(vt[jb], pl, acc[jb]);
+                    for (int jb = 0; jb < 4; ++jb) {
+                        const bf16x8 vt = tr8(G.V[jj], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        num[jj][jb] = mfma(vt, ph, num[jj][jb]);
+                        num[jj][jb] = mfma(vt, pl, num[jj][jb]);
+                    }
+                }
             }
+            // X^T <- g^2L X^T + V^T Us  (rows j = 16w.., all a)
+            const float rho2 = gp(static_cast<float>(2 * Lc));
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) num[jj][jb] = acc[jb];
+            for (int ab = 0; ab < 4; ++ab) xacc[ab] *= rho2;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rb = 32 * ks + 8 * g;
+                const bf16x8 vt = tr8(G.V[jj], rb, rb + 4, 16 * w, r);
+#pragma unroll
+                for (int ab = 0; ab < 4; ++ab) {
+                    xacc[ab] = mfma(vt, tr8(G.Uh, rb, rb + 4, 16 * ab, r), xacc[ab]);
+                    xacc[ab] = mfma(vt, tr8(G.Ul, rb, rb + 4, 16 * ab, r), xacc[ab]);
+                }
+            }
+            if (jj == 0) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) xsave[b] = xacc[b];
+            }
+            // S0 of the next chunk
+            const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) s0[b] = rho * s0[b] + sc0[b];
         } else {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) num[jj][jb] = zero4;
         }
-        // P5: S0 <- rho S0 + K^T diag(f) K (next chunk's S0 into ST; this chunk's
-        // S0 was last read before barrier (3))
-        // P6: X0 <- rho^2 X0 + (diag(f^2) U)^T V, with U read column-wise from its rows
-        if (valid) {
-            s_update(sacc, Lc);
-            write_s();
-            const float rho2 = sm.pw[2 * Lc];
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) xacc[jb] *= rho2;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int s = 32 * ks + 8 * g + i;
-                    const float f2 = s < Lc ? sm.pw[2 * (Lc - 1 - s)] : 0.0f;
-                    const int o = s * LDR + 16 * w + r;
-                    x[i] = f2 * (static_cast<float>(G.Uh[o]) + static_cast<float>(G.Ul[o]));
-                }
-                bf16x8 uh, ul;
-                split8(x, uh, ul);
-                bf16x8 vt[4];
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) vt[jb] = ld8(G.VT, 16 * jb + r, 32 * ks + 8 * g);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) xacc[jb] = mfma(uh, vt[jb], xacc[jb]);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) xacc[jb] = mfma(ul, vt[jb], xacc[jb]);
-            }
-        }
-        __syncthreads();  // (6) chunk done; LDS may be restaged
     }
+    __syncthreads();  // U tiles free for the exchange
 
-    // ---- group 1 adds group 0's X increment; publish Z_seg; round 2: X carry
-    if (grp == 0) put_xch(xacc);
+    // ---- group 1 adds group 0's X increment, publishes Z_seg; round 2
+    if (grp == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch + xi * 16 + 4 * b) = xacc[b];
+    }
     __syncthreads();
     if (grp == 1) {
-        get_xch(part);  // group 0's increment Z_A
-        f32x4 seg[4];
-        const float rhoB2 = sm.pw[lenB] * sm.pw[lenB];  // lenB <= 2W: square the in-table power
 #pragma unroll
-        for (int b = 0; b < 4; ++b) seg[b] = rhoB2 * part[b] + xacc[b];
-        put16(a.aggZ + slot * 4096, wt, seg);
+        for (int b = 0; b < 4; ++b) partA[b] = *reinterpret_cast<const f32x4 *>(xch + xi * 16 + 4 * b);
+        f32x4 seg[4];
+        const float rhoB2 = gp(static_cast<float>(2 * lenB));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) seg[b] = rhoB2 * partA[b] + xacc[b];
+        put16(a.aggX + slot * 4096, xi, seg);
         wait_stores();
     }
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(&a.flag2[slot], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int pp = tid; pp < p; pp += kThreads)
-        if (!wait_flag(&a.flag2[static_cast<size_t>(bh) * a.P + pp], epoch))
-            __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&a.flags[2 * slot + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_round(1);
+    f32x4 xstart[4];
     {
         f32x4 carry[4];
+        sum_earlier(carry, a.aggX, 2);
+        const float rhoA2 = gp(static_cast<float>(2 * lenA));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) carry[b] = zero4;
-        sum_earlier(carry, a.aggZ, 2);
-        const float rhoA2 = sm.pw[lenA] * sm.pw[lenA];
-        // X at this group's start: the carry, or (group 1) carry decayed over group 0 plus Z_A
-#pragma unroll
-        for (int b = 0; b < 4; ++b) xacc[b] = grp == 0 ? carry[b] : rhoA2 * carry[b] + part[b];
+        for (int b = 0; b < 4; ++b) xstart[b] = grp == 0 ? carry[b] : rhoA2 * carry[b] + partA[b];
     }
+
     // ================= phase C: add e_t^2 q_t^T X0 of each chunk and store ===
-    // X0 of the group's chunk jj = g^(2*64*jj) X_start + (local X before chunk jj)
-    const f32x4 xstart[4] = {xacc[0], xacc[1], xacc[2], xacc[3]};
 #pragma unroll
     for (int jj = 0; jj < kPerGroup; ++jj) {
-        __syncthreads();  // exchange area / previous X0 reads done
         const bool valid = jj < nmine;
         if (valid) {
-            const float d2 = jj == 0 ? 1.0f : sm.pw[2 * chunk_len(jbase)] ;
+            // X0 of chunk jj = g^(2 len0 jj) X_start + (local X before chunk jj);
+            // lane holds X0^T[j = 16w+4g+c][a = 16ab+r] -> LDS X0[a][j]
+            const float d2 = jj == 0 ? 1.0f : gp(static_cast<float>(2 * len0));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) xacc[b] = d2 * xstart[b] + (jj == 0 ? zero4 : xsave[b]);
-            write_x();
+            for (int ab = 0; ab < 4; ++ab) {
+                const f32x4 x0 = d2 * xstart[ab] + (jj == 0 ? zero4 : xsave[ab]);
+                bf16x4 h, lo;
+                split4(x0, h, lo);
+                st4(G.Sh, 16 * ab + r, 16 * w + 4 * g, h);
+                st4(G.Sl, 16 * ab + r, 16 * w + 4 * g, lo);
+            }
         }
         __syncthreads();
         if (valid) {
-            const int j = jbase + jj;
-            const int Lc = chunk_len(j);
-            const float e2 = sm.pw[2 * t + 2];
-            float *orow = a.out + (head_tok + static_cast<size_t>(c0 + j) * W + t) * W;
+            const int Lc = chunk_len(jbase + jj);
+            const float e = gp(static_cast<float>(t + 1));
+            const float e2 = e * e;
+            float *orow = a.out + (head_tok + static_cast<size_t>(c0 + jbase + jj) * W + t) * W;
             f32x4 acc[4];
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 xh[4], xl[4];
+                const int rb = 32 * ks + 8 * g;
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
-                    xh[jb] = ld8(G.STh, 16 * jb + r, 32 * ks + 8 * g);
-                    xl[jb] = ld8(G.STl, 16 * jb + r, 32 * ks + 8 * g);
+                    acc[jb] = mfma(tr8(G.Sh, rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                    acc[jb] = mfma(tr8(G.Sl, rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
                 }
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma(xh[jb], qf[jj][ks], acc[jb]);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma(xl[jb], qf[jj][ks], acc[jb]);
             }
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
                 const f32x4 o = num[jj][jb] + e2 * acc[jb];
-                if (t < Lc)
-                    *reinterpret_cast<float4 *>(orow + 16 * jb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+                if (t < Lc) *reinterpret_cast<float4 *>(orow + 16 * jb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
             }
         }
+        __syncthreads();  // X0 reads done before the next chunk's X0 is written
     }
 
-    // ---- the last workgroup resets the ticket and advances the epoch
+    // ---- the cohort's last workgroup resets its counters and advances its epoch
     if (tid == 0) {
         // kernel completion publishes these to the next launch on the stream
-        const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == static_cast<uint32_t>(total - 1)) {
-            __hip_atomic_store(&a.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[2], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t done = __hip_atomic_fetch_add(&cl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == static_cast<uint32_t>(hc * a.P - 1)) {
+            __hip_atomic_store(&cl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&cl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&cl[2], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        if (blockIdx.x == 0) __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+struct Layout {
+    size_t flags, aggS, aggX, total;
+};
+
+Layout layout(int BH, int P) {
+    Layout L{};
+    const size_t slots = static_cast<size_t>(BH) * P;
+    L.flags = 0;
+    L.aggS = L.flags + align256(2 * slots * sizeof(uint32_t));
+    L.aggX = L.aggS + slots * 4096 * sizeof(float);
+    L.total = L.aggX + slots * 4096 * sizeof(float);
+    return L;
+}
+
 }  // namespace
 
 bool fused64_supported(const FwdProblem &p) {
-    return p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.ridge == 0.0f &&
-           !p.normalize && p.den == nullptr && p.init.S == nullptr && p.fin.S == nullptr &&
-           p.n > 0;
+    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.ridge == 0.0f && !p.normalize &&
+          p.den == nullptr && p.init.S == nullptr && p.fin.S == nullptr && p.n > 0))
+        return false;
+    const int nh = p.gam.per_head ? p.H : 1;
+    for (int h = 0; h < nh; ++h)
+        if (p.gam.g[h] < kMinGamma) return false;
+    return true;
 }
 
 void fused64_geometry(int BH, int nc, int *P, int *L) {
@@ -698,8 +700,7 @@ size_t fused64_workspace_bytes(int BH, int n) {
     const int nc = (n + W - 1) / W;
     int P, L;
     fused64_geometry(BH, nc, &P, &L);
-    const size_t slots = static_cast<size_t>(BH) * P;
-    return align256(2 * slots * sizeof(uint32_t)) + 2 * slots * 4096 * sizeof(float);
+    return layout(BH, P).total;
 }
 
 hipError_t fused64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
@@ -711,14 +712,20 @@ hipError_t fused64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipS
     a.v = static_cast<const uint16_t *>(p.v);
     a.out = p.out;
     a.ctrl = ctrl;
-    const size_t slots = static_cast<size_t>(a.BH) * a.P;
+    const Layout L = layout(a.BH, a.P);
     char *base = static_cast<char *>(data);
-    a.flag1 = reinterpret_cast<uint32_t *>(base);
-    a.flag2 = a.flag1 + slots;
-    a.aggS = reinterpret_cast<float *>(base + align256(2 * slots * sizeof(uint32_t)));
-    a.aggZ = a.aggS + slots * 4096;
+    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    a.aggS = reinterpret_cast<float *>(base + L.aggS);
+    a.aggX = reinterpret_cast<float *>(base + L.aggX);
     a.gam = p.gam;
-    hipLaunchKernelGGL(k_fused64, dim3(static_cast<unsigned>(slots)), dim3(kThreads), 0, st, a);
+    const int nh = p.gam.per_head ? p.H : 1;
+    bool decay = false;
+    for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
+    const dim3 grid(static_cast<unsigned>(static_cast<size_t>(a.BH) * a.P));
+    if (decay)
+        hipLaunchKernelGGL(k_fused64<true>, grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_fused64<false>, grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -142,9 +142,10 @@ hla_status forward_geometry(const hla_params *p, Geometry *geo) {
 }
 
 FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *init,
-                    const hla_state *fin, const float *den) {
+                    const hla_state *fin, const float *den, const hla::GammaTab &gam) {
     hla::FwdProblem fp{};
-    fp.dtype = p->dtype; fp.d = p->d; fp.dv = p->dv; fp.w = geo.w; fp.n = p->n;
+    fp.dtype = p->dtype; fp.d = p->d; fp.dv = p->dv; fp.w = geo.w; fp.n = p->n; fp.H = p->H;
+    fp.gam = gam;
     fp.ridge = p->ridge; fp.normalize = p->normalize; fp.den = const_cast<float *>(den);
     if (init) fp.init = *init;
     if (fin) fp.fin = *fin;
@@ -248,7 +249,7 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     if (n == 0 && !final_state) return ok();
     char *ws = static_cast<char *>(workspace);
     hipError_t e;
-    if (choose_path(p, geo, init, final_state, den) == FwdPath::Fused64) {
+    if (choose_path(p, geo, init, final_state, den, fp.gam) == FwdPath::Fused64) {
         e = hla::fused64_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
     } else {
         fp.ws = ws + hla::kCtrlBytes;

@@ -38,10 +38,12 @@ struct FwdProblem {
 };
 
 // Every forward workspace starts with a control block of kCtrlBytes: words
-// that the one-launch kernels keep valid across calls (ticket counter,
-// finished-workgroup counter, launch epoch, wait-timeout count).  It must be
-// zero before the first call; path data follows it.
-constexpr size_t kCtrlBytes = 256;
+// that the one-launch kernels keep valid across calls (ticket counters,
+// finished-workgroup counters and launch epochs, one 256-byte line each, a
+// launch count and a wait-timeout count).  It must be zero before the first
+// call; no kernel writes it except through those counters.  Path data
+// follows it.
+constexpr size_t kCtrlBytes = 8192;
 
 // Generic chunked forward: any d, dv, w in {16,32,64,128}, fp32 or bf16,
 // several kernels over a per-chunk workspace.
