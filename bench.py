@@ -16,7 +16,11 @@ against the eager result of the same calls.
 Printed: one JSON line with tokens/s (B*n per second), the roofline of the
 path (algorithmic q/k/v/out bytes per step over the measured step time,
 against 8 TB/s), and the fp64 CPU oracle timed on the host on a bounded
-sample of the same workload.
+sample of the same workload.  The line also carries ``workloads``: the
+other parts of the hot path (the ratio-normalised forward with decay and
+ridge, the long d=128 forward, the streaming decode step, state composition,
+the small fp32 forward), each timed with HIP events on its launch stream and
+set against its own HBM roofline (``--headline-only`` skips them).
 """
 import argparse
 import json
@@ -40,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--seed", type=int, default=1001)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the secondary workloads")
     return ap.parse_args()
 
 
@@ -47,6 +53,111 @@ def algorithmic_bytes(w) -> int:
     # q, k (d each) and v (dv) in bf16 read once, out (dv) in fp32 written once
     per_token = 2 * (2 * w.d + w.dv) + 4 * w.dv
     return w.B * w.H * w.n * per_token
+
+
+def time_calls(fn, stream, reps, warmup=3):
+    """Mean microseconds per call of fn(i), HIP events on ``stream``."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def roof(bytes_per_call, us):
+    gbs = bytes_per_call / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": bytes_per_call}
+
+
+def secondary_workloads(dev, stream):
+    """The other parts of the hot path at their workload sizes."""
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    res = []
+    # ratio-normalised forward with per-head decay and ridge (out and den)
+    w = inputs.RATIO_DECAY_D64
+    per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv + 4
+    copies = max(2, math.ceil(2 * MALL_BYTES / (w.B * w.H * w.n * per_tok)))
+    sets = []
+    for c in range(copies):
+        q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5000 + c, dev)
+        out = torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev)
+        den = torch.empty(w.B, w.H, w.n, dtype=torch.float32, device=dev)
+        ws = torch.zeros(hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, chunk=w.chunk, gamma=w.gamma,
+                                            ridge=w.ridge, normalize=True), dtype=torch.uint8, device=dev)
+        sets.append((q, k, v, out, den, ws))
+
+    def ratio_call(i):
+        q, k, v, out, den, ws = sets[i % copies]
+        hla.forward_chunked(q, k, v, gamma=w.gamma, ridge=w.ridge, normalize=True, chunk=w.chunk,
+                            out=out, den=den, workspace=ws)
+    us = time_calls(ratio_call, stream, 20)
+    tok = w.B * w.H * w.n
+    res.append({"workload": w.name, "entry": "hla_forward_chunked (out + den)", "us_per_call": us,
+                "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
+    del sets
+    # long d = 128 forward with decay
+    w = inputs.LONG_D128
+    per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv
+    q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5100, dev)
+    out = torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev)
+    ws = torch.zeros(hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, chunk=w.chunk, gamma=w.gamma),
+                     dtype=torch.uint8, device=dev)
+    us = time_calls(lambda i: hla.forward_chunked(q, k, v, gamma=w.gamma, chunk=w.chunk, out=out,
+                                                  workspace=ws), stream, 5, warmup=2)
+    tok = w.B * w.H * w.n
+    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us,
+                "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
+    del q, k, v, out, ws
+    # streaming decode: 4096 states seeded from a 512-token prefix
+    w = inputs.DECODE_D128
+    q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5200, dev)
+    _, _, st = hla.forward_chunked(q, k, v, return_state=True)
+    del q, k, v
+    q1, k1, v1 = (x[:, :, 0] .contiguous() for x in
+                  inputs.qkv_on_device(w.B, w.H, 1, w.d, w.dv, w.dtype, 5201, dev))
+    o1 = torch.empty(w.B, w.H, w.dv, dtype=torch.float32, device=dev)
+    us = time_calls(lambda i: hla.decode_step(q1, k1, v1, st, out=o1), stream, 30)
+    N = w.B * w.H
+    state_b = 4 * (w.d * w.d + 2 * w.d * w.dv + 2 * w.d)
+    per_state = 2 * state_b + 2 * (2 * w.d + w.dv) + 4 * w.dv
+    res.append({"workload": w.name, "entry": "hla_decode_step", "us_per_call": us,
+                "states_per_s": N / (us * 1e-6), "roofline": roof(N * per_state, us)})
+    # state composition of 4096 segment pairs at d = dv = 128
+    b = hla.State.empty(N, w.d, w.dv, dev)
+    for name in ("S", "C", "m", "G", "h", "rho"):
+        getattr(b, name).copy_(getattr(st, name))
+    r = hla.State.empty(N, w.d, w.dv, dev)
+    us = time_calls(lambda i: hla.state_compose(st, b, r), stream, 30)
+    per_pair = 3 * (state_b + 4)
+    res.append({"workload": "masked_hla_compose_4096_pairs_d128", "entry": "hla_state_compose",
+                "us_per_call": us, "pairs_per_s": N / (us * 1e-6), "roofline": roof(N * per_pair, us)})
+    del st, b, r
+    # small fp32 forward (launch-bound: a correctness workload)
+    w = inputs.SMALL_FP32
+    q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5300, dev)
+    out = torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev)
+    ws = torch.zeros(hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, dtype=w.dtype), dtype=torch.uint8,
+                     device=dev)
+    us = time_calls(lambda i: hla.forward_chunked(q, k, v, out=out, workspace=ws), stream, 50)
+    per_tok = 4 * (2 * w.d + 2 * w.dv)
+    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us,
+                "tokens_per_s": w.B * w.n / (us * 1e-6),
+                "roofline": roof(w.B * w.H * w.n * per_tok, us)})
+    return res
 
 
 def cpu_baseline(w, q, k, v):
@@ -180,6 +291,10 @@ def main():
         "eager_ms_per_step": eager_ms,
         "parity_guard_row_error": err,
     }
+    if not args.headline_only:
+        del sets
+        torch.cuda.empty_cache()
+        rec["workloads"] = secondary_workloads(dev, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(rec))

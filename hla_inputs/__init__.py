@@ -83,6 +83,21 @@ def workload_qkv(w: Workload, seed: int):
     return qkv(w.B, w.H, w.n, w.d, w.dv, w.dtype, seed)
 
 
+def qkv_on_device(B: int, H: int, n: int, d: int, dv: int, dtype: torch.dtype, seed: int,
+                  device) -> tuple:
+    """Same distribution as ``qkv`` but drawn by a seeded generator on
+    ``device`` (for timing runs whose inputs are too large to draw on the
+    host quickly; values differ from ``qkv``'s)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    s = 1.0 / math.sqrt(d)
+    out = []
+    for shape in ((B, H, n, d), (B, H, n, d), (B, H, n, dv)):
+        x = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device) * s
+        out.append(x.to(dtype) if dtype != torch.float32 else x)
+    return tuple(out)
+
+
 def decode_inputs(B: int, H: int, prefix: int, d: int, dv: int, dtype: torch.dtype, seed: int):
     """Prefix q/k/v [B,H,prefix,·] then the new token's q/k/v [B,H,·]."""
     gen = torch.Generator(device="cpu")
