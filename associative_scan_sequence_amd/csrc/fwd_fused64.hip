@@ -14,6 +14,12 @@
 //   P   = (Q U^T) o D_{g^2} o L
 //   num = P V + diag(e^2) Q X0
 //   S0 <- g^L S0 + K^T diag(f) K,   X0 <- g^2L X0 + U^T diag(f^2) V
+// With ridge lambda and the denominator (y = S m - h is carried like X with
+// v = 1; C and m are plain decayed sums):
+//   R   = (Q Q^T) o D_g o L,   P' = P + lambda R
+//   num = P' V + diag(e^2) Q X0 + lambda diag(e) Q C0
+//   den = P' 1 + diag(e^2) Q y0 + lambda diag(e) Q m0,   out = num or num / den
+//   C0 <- g^L C0 + Q^T diag(f) V,  m0 <- g^L m0 + Q^T f,  y0 <- g^2L y0 + Us^T 1
 // U is kept scaled as Us = diag(f^2) U.  Then the X update needs no further
 // scaling, and since g^(2(t-s)) / f_s^2 = 1 / f_t^2 the masked P is
 // (Q Us^T) o L scaled by 1 / f_t^2 per row.  (The kernel is used for
@@ -31,7 +37,9 @@
 //   B: per chunk, U with the true S carry, P, the local part of num (kept in
 //      registers) and the segment's X increment Z_seg; publish.
 //      Round 2: sum the decayed Z_seg of every earlier segment -> X carry.
-//   C: add diag(e^2) Q X0 to num for every chunk and store.
+//   C: add diag(e^2) Q X0 (and the ridge and denominator carry terms) for
+//      every chunk, divide if normalising, and store.
+// C and m need no S carry; they travel with X in round 2.
 // Both rounds are plain decayed sums of published aggregates (no serial
 // chain between segments).  Heads are dealt to 16 cohorts (head mod 16),
 // each with its own ticket counter in its own control line; a ticket names a
@@ -87,11 +95,13 @@ static_assert(kCtrlBytes >= (1 + kCohorts) * kLine * 4, "control block too small
 struct FusedArgs {
     int H, n, nc, P, L, BH;
     const uint16_t *q, *k, *v;
-    float *out;
+    float *out, *den;   // den may be null
+    float ridge;
     uint32_t *ctrl;     // line 0: [2] launch count, [3] wait-timeout count;
                         // line 1+i, cohort i: [0] ticket, [1] finished, [2] epoch
     uint32_t *flags;    // [BH * P][2]: epoch when the S sum / X increment was published
-    float *aggS, *aggX; // [BH * P][4096], in accumulator order
+    float *aggS, *aggX, *aggC;  // [BH * P][4096], in accumulator order
+    float *aggV;        // [BH * P][128]: y then m
     GammaTab gam;
 };
 
@@ -147,6 +157,20 @@ __device__ __forceinline__ void pair_operand(const f32x4 &t0, const f32x4 &t1, b
 
 __device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4 &v) {
     *reinterpret_cast<bf16x4 *>(base + row * LDR + col) = v;
+}
+
+template <int CTL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTL, 0xF, 0xF, true));
+}
+
+// sum over the 16 lanes of a DPP row; every lane of the row receives it
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return v;
 }
 
 // Cross-workgroup hand-off without cache maintenance: aggregates and flags
@@ -221,12 +245,18 @@ struct GroupLds {
 
 struct Smem {
     GroupLds grp[2];
+    float vpart[2][2][4][64];  // [group][y, m][wave]: per-wave sums of one chunk
+    float vec[2][8][64];       // [group]: y, y after chunk 0, m, m after chunk 0,
+                               //          chunk y0, chunk m0, group start y, m
+    float vcar[2][64];         // y and m carries of the segment
     int ticket;
     uint32_t epoch;
 };
 
-template <bool DECAY>
+template <bool DECAY, bool RIDGE, bool DEN, bool NORM>
 __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
+    static_assert(!NORM || DEN, "the ratio needs the denominator");
+    constexpr bool MV = RIDGE && DEN;  // the query mass m is only read by the ridge denominator term
     __shared__ Smem sm;
     const int tid = threadIdx.x, grp = tid >> 8, wt = tid & 255;
     const int wv = wt >> 6, l = wt & 63, r = l & 15, g = l >> 4;
@@ -473,10 +503,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
     }
 
     // ================= phase B: each group walks its chunks ===================
+    const float lam = a.ridge;
     f32x4 num[kPerGroup][4];
     f32x4 xacc[4], xsave[4];  // X^T increment, rows j = 16w+4g+c, cols a = 16ab+r
+    f32x4 cacc[4], csave[4];  // C^T increment (ridge), same layout
+    float dl[kPerGroup];      // this lane's part of sum_s P'[t][s] (denominator)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) xacc[b] = xsave[b] = zero4;
+    for (int b = 0; b < 4; ++b) xacc[b] = xsave[b] = cacc[b] = csave[b] = zero4;
+#pragma unroll
+    for (int jj = 0; jj < kPerGroup; ++jj) dl[jj] = 0.0f;
+    if (RIDGE) {  // the key tiles are no longer read: they now hold the query rows
+#pragma unroll
+        for (int jj = 0; jj < kPerGroup; ++jj)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                *reinterpret_cast<bf16x8 *>(&G.K[jj][t * LDR + 32 * ks + 8 * g]) = qn[jj][ks];
+    }
+    if (DEN && wt < 64) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.vec[grp][i][wt] = 0.0f;
+    }
 #pragma unroll
     for (int jj = 0; jj < kPerGroup; ++jj) {
         const bool valid = jj < nmine;
@@ -509,24 +555,61 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                 split4(us, h, lo);
                 st4(G.Uh, t, 16 * bb + 4 * g, h);
                 st4(G.Ul, t, 16 * bb + 4 * g, lo);
+                if (DEN) {  // y increment: sum over this wave's tokens of Us rows
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float sum = row_sum16(us[c]);
+                        if (r == 0) sm.vpart[grp][0][w][16 * bb + 4 * g + c] = sum;
+                    }
+                }
+            }
+            if (MV) {  // m increment: sum over this wave's tokens of f_t q_t
+                const float f = t < Lc ? gp(static_cast<float>(Lc - 1 - t)) : 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e8 = 0; e8 < 8; ++e8) {
+                        const float sum = row_sum16(f * static_cast<float>(qn[jj][ks][e8]));
+                        if (r == 0) sm.vpart[grp][1][w][32 * ks + 8 * g + e8] = sum;
+                    }
             }
         }
         __syncthreads();  // (2) every Us row ready
+        if (DEN && valid && wt < 64) {  // fold the per-wave sums in a fixed order
+            const float (*vp)[4][64] = sm.vpart[grp];
+            const float yinc = (vp[0][0][wt] + vp[0][1][wt]) + (vp[0][2][wt] + vp[0][3][wt]);
+            float *v = &sm.vec[grp][0][0];
+            v[wt] = gp(static_cast<float>(2 * Lc)) * v[wt] + yinc;
+            if (jj == 0) v[64 + wt] = v[wt];
+            if (MV) {
+                const float minc = (vp[1][0][wt] + vp[1][1][wt]) + (vp[1][2][wt] + vp[1][3][wt]);
+                v[128 + wt] = gp(static_cast<float>(Lc)) * v[128 + wt] + minc;
+                if (jj == 0) v[192 + wt] = v[128 + wt];
+            }
+        }
         if (valid) {
-            // P^T[s][t] = (Us_s . q_t) / f_t^2 for s <= t
+            // P'^T[s][t] = (Us_s . q_t) / f_t^2 + lambda g^(t-s) (q_s . q_t) for s <= t
             const float inv_f2 = t < Lc ? gp(static_cast<float>(-2 * (Lc - 1 - t))) : 0.0f;
             f32x4 pt[4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 pt[sb] = zero4;
                 if (sb <= w) {
+                    f32x4 rt = zero4;
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
                         pt[sb] = mfma(ld8(G.Uh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
                         pt[sb] = mfma(ld8(G.Ul, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                        if (RIDGE) rt = mfma(ld8(G.K[jj], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], rt);
                     }
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) pt[sb][c] = 16 * sb + 4 * g + c <= t ? inv_f2 * pt[sb][c] : 0.0f;
+                    for (int c = 0; c < 4; ++c) {
+                        const int sidx = 16 * sb + 4 * g + c;
+                        float x = inv_f2 * pt[sb][c];
+                        if (RIDGE) x += lam * gp(static_cast<float>(t - sidx)) * rt[c];
+                        pt[sb][c] = sidx <= t ? x : 0.0f;
+                    }
+                    if (DEN) dl[jj] += (pt[sb][0] + pt[sb][1]) + (pt[sb][2] + pt[sb][3]);
                 }
             }
             // num^T[j][t] = sum_s V^T[j][s] P[t][s]
@@ -563,6 +646,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b) xsave[b] = xacc[b];
             }
+            if (RIDGE) {  // C^T <- g^L C^T + (diag(f) V)^T Q  (rows j = 16w.., all a)
+                const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+                for (int ab = 0; ab < 4; ++ab) cacc[ab] *= rho;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 vt = tr8(G.V[jj], rb, rb + 4, 16 * w, r);
+                    bf16x8 vh = vt, vl;
+                    if (DECAY) {
+                        f32x4 x0, x1;
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            x0[e4] = gp(static_cast<float>(Lc - 1 - (rb + e4))) * static_cast<float>(vt[e4]);
+                            x1[e4] = gp(static_cast<float>(Lc - 1 - (rb + 4 + e4))) * static_cast<float>(vt[4 + e4]);
+                        }
+                        pair_operand(x0, x1, vh, vl);
+                    }
+#pragma unroll
+                    for (int ab = 0; ab < 4; ++ab) {
+                        const bf16x8 qt = tr8(G.K[jj], rb, rb + 4, 16 * ab, r);
+                        cacc[ab] = mfma(vh, qt, cacc[ab]);
+                        if (DECAY) cacc[ab] = mfma(vl, qt, cacc[ab]);
+                    }
+                }
+                if (jj == 0) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) csave[b] = cacc[b];
+                }
+            }
             // S0 of the next chunk
             const float rho = gp(static_cast<float>(Lc));
 #pragma unroll
@@ -574,12 +687,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
     }
     __syncthreads();  // U tiles free for the exchange
 
-    // ---- group 1 adds group 0's X increment, publishes Z_seg; round 2
+    // ---- group 1 adds group 0's increments, publishes the segment's X (and
+    // C, y, m) increments; round 2
+    float *xch2 = reinterpret_cast<float *>(sm.grp[1].Sh);  // 16 KB inside group 1's S tiles
     if (grp == 0) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch + xi * 16 + 4 * b) = xacc[b];
+        if (RIDGE) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch2 + xi * 16 + 4 * b) = cacc[b];
+        }
     }
     __syncthreads();
+    f32x4 partC[4];  // group 0's C increment (group 1 only)
     if (grp == 1) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) partA[b] = *reinterpret_cast<const f32x4 *>(xch + xi * 16 + 4 * b);
@@ -588,27 +708,71 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) seg[b] = rhoB2 * partA[b] + xacc[b];
         put16(a.aggX + slot * 4096, xi, seg);
+        if (RIDGE) {
+            const float rhoB = gp(static_cast<float>(lenB));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                partC[b] = *reinterpret_cast<const f32x4 *>(xch2 + xi * 16 + 4 * b);
+                seg[b] = rhoB * partC[b] + cacc[b];
+            }
+            put16(a.aggC + slot * 4096, xi, seg);
+        }
+        if (DEN && wt < 64) {
+            const float ys = gp(static_cast<float>(2 * lenB)) * sm.vec[0][0][wt] + sm.vec[1][0][wt];
+            __hip_atomic_store(&a.aggV[slot * 128 + wt], ys, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (MV) {
+                const float ms = gp(static_cast<float>(lenB)) * sm.vec[0][2][wt] + sm.vec[1][2][wt];
+                __hip_atomic_store(&a.aggV[slot * 128 + 64 + wt], ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
         wait_stores();
     }
     __syncthreads();
     if (tid == 0) __hip_atomic_store(&a.flags[2 * slot + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_round(1);
-    f32x4 xstart[4];
+    f32x4 xstart[4], cstart[4];
     {
         f32x4 carry[4];
         sum_earlier(carry, a.aggX, 2);
         const float rhoA2 = gp(static_cast<float>(2 * lenA));
 #pragma unroll
         for (int b = 0; b < 4; ++b) xstart[b] = grp == 0 ? carry[b] : rhoA2 * carry[b] + partA[b];
+        if (RIDGE) {
+            sum_earlier(carry, a.aggC, 1);
+            const float rhoA = gp(static_cast<float>(lenA));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) cstart[b] = grp == 0 ? carry[b] : rhoA * carry[b] + partC[b];
+        }
+    }
+    if (DEN) {
+        // vector carries: group 0 sums y, group 1 sums m over earlier segments
+        if (wt < 64 && (grp == 0 || MV)) {
+            float acc = 0.0f;
+            for (int pp = 0; pp < p; ++pp) {
+                const float x = __hip_atomic_load(&a.aggV[(static_cast<size_t>(bh) * a.P + pp) * 128 + 64 * grp + wt],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc += gp(static_cast<float>((2 - grp) * (p - 1 - pp) * seg_tokens)) * x;
+            }
+            sm.vcar[grp][wt] = acc;
+        }
+        __syncthreads();
+        if (wt < 64) {  // this group's start: the carry, or (group 1) carried over group 0 plus its sums
+            float *v = &sm.vec[grp][0][0];
+            v[6 * 64 + wt] = grp == 0 ? sm.vcar[0][wt]
+                                      : gp(static_cast<float>(2 * lenA)) * sm.vcar[0][wt] + sm.vec[0][0][wt];
+            if (MV)
+                v[7 * 64 + wt] = grp == 0 ? sm.vcar[1][wt]
+                                          : gp(static_cast<float>(lenA)) * sm.vcar[1][wt] + sm.vec[0][2][wt];
+        }
     }
 
-    // ================= phase C: add e_t^2 q_t^T X0 of each chunk and store ===
+    // ================= phase C: carry terms of each chunk, ratio, store ======
 #pragma unroll
     for (int jj = 0; jj < kPerGroup; ++jj) {
         const bool valid = jj < nmine;
         if (valid) {
-            // X0 of chunk jj = g^(2 len0 jj) X_start + (local X before chunk jj);
-            // lane holds X0^T[j = 16w+4g+c][a = 16ab+r] -> LDS X0[a][j]
+            // carries of chunk jj = decayed group start + (local sums before chunk jj);
+            // lane holds X0^T[j = 16w+4g+c][a = 16ab+r] -> LDS X0[a][j] (C0 likewise)
             const float d2 = jj == 0 ? 1.0f : gp(static_cast<float>(2 * len0));
 #pragma unroll
             for (int ab = 0; ab < 4; ++ab) {
@@ -618,16 +782,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                 st4(G.Sh, 16 * ab + r, 16 * w + 4 * g, h);
                 st4(G.Sl, 16 * ab + r, 16 * w + 4 * g, lo);
             }
+            if (RIDGE) {
+                const float d1 = jj == 0 ? 1.0f : gp(static_cast<float>(len0));
+#pragma unroll
+                for (int ab = 0; ab < 4; ++ab) {
+                    const f32x4 c0v = d1 * cstart[ab] + (jj == 0 ? zero4 : csave[ab]);
+                    bf16x4 h, lo;
+                    split4(c0v, h, lo);
+                    st4(G.Uh, 16 * ab + r, 16 * w + 4 * g, h);
+                    st4(G.Ul, 16 * ab + r, 16 * w + 4 * g, lo);
+                }
+            }
+            if (DEN && wt < 64) {
+                float *v = &sm.vec[grp][0][0];
+                v[4 * 64 + wt] = jj == 0 ? v[6 * 64 + wt] : d2 * v[6 * 64 + wt] + v[64 + wt];
+                if (MV)
+                    v[5 * 64 + wt] = jj == 0 ? v[7 * 64 + wt]
+                                             : gp(static_cast<float>(len0)) * v[7 * 64 + wt] + v[3 * 64 + wt];
+            }
         }
         __syncthreads();
         if (valid) {
             const int Lc = chunk_len(jbase + jj);
             const float e = gp(static_cast<float>(t + 1));
             const float e2 = e * e;
-            float *orow = a.out + (head_tok + static_cast<size_t>(c0 + jbase + jj) * W + t) * W;
-            f32x4 acc[4];
+            const size_t trow = head_tok + static_cast<size_t>(c0 + jbase + jj) * W + t;
+            float *orow = a.out + trow * W;
+            f32x4 acc[4], accc[4];
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4;
+            for (int jb = 0; jb < 4; ++jb) acc[jb] = accc[jb] = zero4;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int rb = 32 * ks + 8 * g;
@@ -635,15 +818,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                 for (int jb = 0; jb < 4; ++jb) {
                     acc[jb] = mfma(tr8(G.Sh, rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
                     acc[jb] = mfma(tr8(G.Sl, rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                    if (RIDGE) {
+                        accc[jb] = mfma(tr8(G.Uh, rb, rb + 4, 16 * jb, r), qn[jj][ks], accc[jb]);
+                        accc[jb] = mfma(tr8(G.Ul, rb, rb + 4, 16 * jb, r), qn[jj][ks], accc[jb]);
+                    }
                 }
+            }
+            float den = 0.0f;
+            if (DEN) {
+                // den_t = sum_s P'[t][s] + e^2 q_t . y0 + lambda e q_t . m0, summed over the 4 lane rows
+                const float *y0 = sm.vec[grp][4];
+                const float *m0 = sm.vec[grp][5];
+                float part = dl[jj];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e8 = 0; e8 < 8; ++e8) {
+                        const int ai = 32 * ks + 8 * g + e8;
+                        float coef = e2 * y0[ai];
+                        if (MV) coef += lam * e * m0[ai];
+                        part += coef * static_cast<float>(qn[jj][ks][e8]);
+                    }
+                part += __shfl_xor(part, 16);
+                den = part + __shfl_xor(part, 32);
             }
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
-                const f32x4 o = num[jj][jb] + e2 * acc[jb];
+                f32x4 o = num[jj][jb] + e2 * acc[jb];
+                if (RIDGE) o += (lam * e) * accc[jb];
+                if (NORM) o = o / den;
                 if (t < Lc) *reinterpret_cast<float4 *>(orow + 16 * jb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
             }
+            if (DEN && a.den != nullptr && g == 0 && t < Lc) a.den[trow] = den;
         }
-        __syncthreads();  // X0 reads done before the next chunk's X0 is written
+        __syncthreads();  // carry reads done before the next chunk's carries are written
     }
 
     // ---- the cohort's last workgroup resets its counters and advances its epoch
@@ -662,7 +870,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-    size_t flags, aggS, aggX, total;
+    size_t flags, aggS, aggX, aggC, aggV, total;
 };
 
 Layout layout(int BH, int P) {
@@ -671,15 +879,35 @@ Layout layout(int BH, int P) {
     L.flags = 0;
     L.aggS = L.flags + align256(2 * slots * sizeof(uint32_t));
     L.aggX = L.aggS + slots * 4096 * sizeof(float);
-    L.total = L.aggX + slots * 4096 * sizeof(float);
+    L.aggC = L.aggX + slots * 4096 * sizeof(float);
+    L.aggV = L.aggC + slots * 4096 * sizeof(float);
+    L.total = L.aggV + slots * 128 * sizeof(float);
     return L;
+}
+
+template <bool D, bool R, bool Dn, bool N>
+void launch(const FusedArgs &a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((k_fused64<D, R, Dn, N>), grid, dim3(kThreads), 0, st, a);
+}
+
+template <bool D>
+void launch_opts(const FusedArgs &a, dim3 grid, hipStream_t st, bool ridge, bool den, bool norm) {
+    if (ridge) {
+        if (norm) launch<D, true, true, true>(a, grid, st);
+        else if (den) launch<D, true, true, false>(a, grid, st);
+        else launch<D, true, false, false>(a, grid, st);
+    } else {
+        if (norm) launch<D, false, true, true>(a, grid, st);
+        else if (den) launch<D, false, true, false>(a, grid, st);
+        else launch<D, false, false, false>(a, grid, st);
+    }
 }
 
 }  // namespace
 
 bool fused64_supported(const FwdProblem &p) {
-    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.ridge == 0.0f && !p.normalize &&
-          p.den == nullptr && p.init.S == nullptr && p.fin.S == nullptr && p.n > 0))
+    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.init.S == nullptr &&
+          p.fin.S == nullptr && p.n > 0))
         return false;
     const int nh = p.gam.per_head ? p.H : 1;
     for (int h = 0; h < nh; ++h)
@@ -711,21 +939,26 @@ hipError_t fused64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipS
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
     a.out = p.out;
+    a.den = p.den;
+    a.ridge = p.ridge;
     a.ctrl = ctrl;
     const Layout L = layout(a.BH, a.P);
     char *base = static_cast<char *>(data);
     a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
     a.aggS = reinterpret_cast<float *>(base + L.aggS);
     a.aggX = reinterpret_cast<float *>(base + L.aggX);
+    a.aggC = reinterpret_cast<float *>(base + L.aggC);
+    a.aggV = reinterpret_cast<float *>(base + L.aggV);
     a.gam = p.gam;
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
+    const bool ridge = p.ridge != 0.0f, norm = p.normalize != 0, den = norm || p.den != nullptr;
     const dim3 grid(static_cast<unsigned>(static_cast<size_t>(a.BH) * a.P));
     if (decay)
-        hipLaunchKernelGGL(k_fused64<true>, grid, dim3(kThreads), 0, st, a);
+        launch_opts<true>(a, grid, st, ridge, den, norm);
     else
-        hipLaunchKernelGGL(k_fused64<false>, grid, dim3(kThreads), 0, st, a);
+        launch_opts<false>(a, grid, st, ridge, den, norm);
     return hipGetLastError();
 }
 

@@ -50,8 +50,8 @@ constexpr size_t kCtrlBytes = 8192;
 size_t generic_workspace_bytes(int BH, int n, int d, int dv, int w);
 hipError_t generic_forward(const FwdProblem &p, hipStream_t s);
 
-// One-launch MFMA forward for bf16, d = dv = w = 64 (no ridge, denominator,
-// normalisation, init or final state).
+// One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
+// ridge, denominator and normalisation (no init or final state).
 bool fused64_supported(const FwdProblem &p);
 size_t fused64_workspace_bytes(int BH, int n);
 hipError_t fused64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t s);

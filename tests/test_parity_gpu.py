@@ -385,10 +385,71 @@ def test_fused_matches_generic_path():
     B, H, n = 2, 4, 700
     q, k, v = on_gpu(*inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=31))
     g = inputs.gamma_list_fp32([0.99, 0.999, 1.0, 0.98])
-    fused, _, _ = hla.forward_chunked(q, k, v, gamma=g, chunk=64)
-    # asking for the denominator routes the same call through the generic kernels
-    generic, den, _ = hla.forward_chunked(q, k, v, gamma=g, chunk=64, return_den=True)
+    fused, fden, _ = hla.forward_chunked(q, k, v, gamma=g, ridge=1e-3, chunk=64, return_den=True)
+    # asking for the final state routes the same call through the generic kernels
+    generic, gden, _ = hla.forward_chunked(q, k, v, gamma=g, ridge=1e-3, chunk=64, return_den=True,
+                                           return_state=True)
     assert row_err(fused.cpu(), generic.cpu()) <= 2e-4
+    assert slab_err(fden.cpu(), gden.cpu(), lead=2) <= 2e-4
+
+
+@pytest.mark.parametrize("gk", [None, "per_head"])
+@pytest.mark.parametrize("ridge,den,normalize", [
+    (0.0, True, False), (1e-3, False, False), (1e-3, True, True), (1.0, True, False),
+    (0.0, False, True),
+])
+def test_fused_options(gk, ridge, den, normalize):
+    """Ridge, denominator and ratio on the one-launch path: several segments
+    per head, a ragged tail, and group 1 with one chunk."""
+    B, H, n = 2, 3, 64 * 13 + 37
+    q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=700 + int(1000 * ridge) + H)
+    g = None if gk is None else inputs.gamma_list_fp32([1 - 2.0 ** -(5 + h) for h in range(H)])
+    lam = inputs.ridge_fp32(ridge)
+    qg, kg, vg = on_gpu(q, k, v)
+    ws = torch.zeros(hla.workspace_size(B, H, n, 64, 64, chunk=64), dtype=torch.uint8, device=DEV)
+    before = ctrl_words(ws)
+    out, dg, _ = hla.forward_chunked(qg, kg, vg, gamma=g, ridge=lam, normalize=normalize, chunk=64,
+                                     return_den=den, workspace=ws)
+    torch.cuda.synchronize()
+    after = ctrl_words(ws)
+    assert after[2] != before[2], "the one-launch path did not run"
+    assert after[3] == 0, after
+    import oracle
+    ro, rd, _ = oracle.forward(q, k, v, gamma=g, lam=lam, normalize=normalize, want_state=False)
+    tol = TOL[torch.bfloat16]
+    if normalize:
+        e, excluded = ratio_err(out.cpu(), ro, rd)
+        print(f"ratio row error {e:.3e} ({excluded} rows excluded)")
+    else:
+        e = row_err(out.cpu(), ro)
+        print(f"row error {e:.3e}")
+    assert e <= tol
+    if den:
+        ed = slab_err(dg.cpu(), rd, lead=2)
+        print(f"den slab error {ed:.3e}")
+        assert ed <= tol
+
+
+def test_fused_ratio_workload():
+    """The ratio-normalised workload with per-head decay and ridge (B8 H8 n4096)
+    through the one-launch path: out and den, no final state."""
+    w = inputs.RATIO_DECAY_D64
+    q, k, v = inputs.workload_qkv(w, 1002)
+    qg, kg, vg = on_gpu(q, k, v)
+    ws = torch.zeros(hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, chunk=w.chunk), dtype=torch.uint8,
+                     device=DEV)
+    before = ctrl_words(ws)
+    out, den, _ = hla.forward_chunked(qg, kg, vg, gamma=w.gamma, ridge=w.ridge, normalize=True,
+                                      chunk=w.chunk, return_den=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert ctrl_words(ws)[2] != before[2], "the one-launch path did not run"
+    import oracle
+    ro, rd, _ = oracle.forward(q, k, v, gamma=w.gamma, lam=w.ridge, normalize=True, want_state=False)
+    tol = TOL[torch.bfloat16]
+    e, excluded = ratio_err(out.cpu(), ro, rd)
+    ed = slab_err(den.cpu(), rd, lead=2)
+    print(f"ratio row error {e:.3e} ({excluded} rows excluded), den slab error {ed:.3e}")
+    assert e <= tol and ed <= tol
 
 
 def test_fused_workspace_shared_across_shapes():
