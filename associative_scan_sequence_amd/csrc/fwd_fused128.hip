@@ -1,0 +1,651 @@
+// fwd_fused128.hip -- one-launch masked second-order HLA forward for
+// d = dv = 128, bf16 q/k/v, on gfx950 MFMA; long sequences over few heads.
+//
+// Method (Higher-order Linear Attention, paperlayer.ai summary sec. 4 and 5;
+// the chunk algebra of fwd_fused64.hip): with the carry held as
+// (S, X = S C - G), per 64-token chunk (local t, s; length L; e_t = g^(t+1),
+// f_s = g^(L-1-s); Us = diag(f^2) U)
+//   A   = (Q K^T) o D_g o L,   U = diag(e) Q S0 + A K,
+//   num = P V + diag(e^2) Q X0,  P = (Q Us^T) o L scaled by 1/f_t^2 per row,
+//   S0 <- g^L S0 + K^T diag(f) K,   X0 <- g^2L X0 + Us^T V.
+// (The chunk width the caller names only changes rounding order: this
+// kernel always works in 64-token chunks.)
+//
+// Segments.  A head of n tokens is cut into P segments of L chunks, one per
+// workgroup.  Segment outputs need the carries (S0, X0) at the segment
+// start.  S0 is a decayed sum of the earlier segments' key moments; X0 is a
+// decayed sum of their X increments, and the X increment of a segment that
+// starts from carry S0 is affine in S0:
+//   Z = S0 Ct + Lz,   Ct = sum_s g^(2 Lseg - 1 - s) q_s v_s^T  (s = position
+//   in the segment),  Lz = the X increment computed from a zero S carry.
+// So each workgroup walks its segment twice.  Pass 1 starts from zero
+// carries and yields the segment's key moment S_seg, Ct and Lz; S_seg is
+// published (round 1), the S carry is summed from the earlier segments,
+// Z = S0 Ct + Lz is formed (one fp32 product) and published (round 2), and
+// the X carry is summed likewise.  Pass 2 walks again from the true carries
+// and writes the outputs.  With P = 1 (many heads, or short sequences) pass
+// 1 and both rounds are skipped.  Rounds, tickets and epochs work as in
+// fwd_fused64.hip (cohort ticket counters, device-coherent aggregates).
+//
+// Layout.  512 threads = 8 waves; wave w owns feature block w (16 of 128):
+// the columns b = 16w.. of S (= its rows, S being symmetric), the columns
+// j = 16w.. of X and Ct, the rows b of U^T and the rows j of num^T.  Every
+// state lives in registers as accumulator tiles (lane l = 16g + r holds rows
+// 16ab+4g..+3 of column 16w+r), and enters a contraction over its row index
+// directly as an operand: an accumulator pair (row blocks 2k, 2k+1) gives
+// the k slots 8g+e <-> row 32k+4g+e (e < 4) or 32k+16+4g+(e-4), and the
+// other operand (q) is read from LDS in the same slot order.  The masked
+// 64 x 64 products (A, then P) are spread over the waves as tiles and pass
+// through LDS.  Transposed operands (K^T, V^T, Us^T, Q^T) come from
+// row-major LDS tiles through ds_read_b64_tr_b16.  Precision: every fp32
+// operand is split into bf16 hi + lo (two MFMAs); the one fp32 x fp32
+// product (S0 Ct) takes hi*hi + hi*lo + lo*hi.  Us enters P with a third
+// term (x = hi + mid + lo to ~2^-26): q_t . Us_s cancels heavily when q_t is
+// nearly orthogonal to S_s q_s (at t = s = 0 the value is (q.k)^2), and a
+// two-term Us would leave an error of ~2^-18 / cos(q, S q) there.
+#include "device_common.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int W = 64;          // tokens per chunk
+constexpr int D = 128;         // d = dv
+constexpr int LDW = 136;       // padded LDS row of 128 bf16 (272 bytes)
+constexpr int LDN = 72;        // padded LDS row of 64 bf16 (144 bytes)
+constexpr int kThreads = 512;  // eight waves
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kCohorts = 16;
+constexpr int kLine = 64;
+constexpr int kSlot = 16384;   // floats per published 128 x 128 aggregate
+constexpr float kMinGamma = 0.75f;
+static_assert(kCtrlBytes >= (1 + kCohorts) * kLine * 4, "control block too small");
+
+struct Args128 {
+    int H, n, nc, P, L, BH;
+    const uint16_t *q, *k, *v;
+    float *out;
+    uint32_t *ctrl;     // as in fwd_fused64.hip
+    uint32_t *flags;    // [BH * P][2]
+    float *aggS, *aggZ; // [BH * P][kSlot]
+    GammaTab gam;
+};
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int LD>
+__device__ __forceinline__ bf16x8 ld8(const __bf16 *base, int row, int col) {
+    return *reinterpret_cast<const bf16x8 *>(base + row * LD + col);
+}
+
+// two 4-element pieces of one LDS row: slots 0..3 at col1, 4..7 at col2
+template <int LD>
+__device__ __forceinline__ bf16x8 ld44(const __bf16 *base, int row, int col1, int col2) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(base + row * LD + col1);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(base + row * LD + col2);
+    bf16x8 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+    }
+    return x;
+}
+
+// Transposed operand: lane (g, r) receives M[rb1 + e][col0 + r] (slots 8g+e,
+// e < 4) and M[rb2 + e][col0 + r] (slots 8g+4+e).
+template <int LD>
+__device__ __forceinline__ bf16x8 tr8(const __bf16 *M, int rb1, int rb2, int col0, int r) {
+    const int col = col0 + 4 * (r & 3);
+    const __bf16 *p1 = M + (rb1 + (r >> 2)) * LD + col;
+    const __bf16 *p2 = M + (rb2 + (r >> 2)) * LD + col;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p2));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+    bf16x8 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = ab[i];
+        x[4 + i] = bb[i];
+    }
+    return x;
+}
+
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = static_cast<__bf16>(x[i]);
+        lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
+    }
+}
+
+// three-term split: x = hi + mid + lo to ~2^-26 relative
+__device__ __forceinline__ void split3(const f32x4 &x, bf16x4 &hi, bf16x4 &mid, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = static_cast<__bf16>(x[i]);
+        const float r1 = x[i] - static_cast<float>(hi[i]);
+        mid[i] = static_cast<__bf16>(r1);
+        lo[i] = static_cast<__bf16>(r1 - static_cast<float>(mid[i]));
+    }
+}
+
+__device__ __forceinline__ void pair_operand(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
+    bf16x4 h0, l0, h1, l1;
+    split4(t0, h0, l0);
+    split4(t1, h1, l1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = h0[i];
+        hi[4 + i] = h1[i];
+        lo[i] = l0[i];
+        lo[4 + i] = l1[i];
+    }
+}
+
+// scale the 8 slots of an operand whose slot e holds row (rb + e) or
+// (rb + 4 + e - 4) by w(row), then split
+template <typename F>
+__device__ __forceinline__ void scaled_split(const bf16x8 &x, int rb, F wfun, bf16x8 &hi, bf16x8 &lo) {
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a[e] = wfun(rb + e) * static_cast<float>(x[e]);
+        b[e] = wfun(rb + 4 + e) * static_cast<float>(x[4 + e]);
+    }
+    pair_operand(a, b, hi, lo);
+}
+
+template <int LD>
+__device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4 &v) {
+    *reinterpret_cast<bf16x4 *>(base + row * LD + col) = v;
+}
+
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e, int cohort) {
+    return e * 1664525u + (1013904223u + 2u * static_cast<uint32_t>(cohort));
+}
+
+__device__ bool wait_flag(const uint32_t *f, uint32_t want) {
+    for (int it = 0; it < kSpinLimit; ++it) {
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+constexpr int kSc1 = 16;  // buffer cache policy: sc1 (device scope)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(slot);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(addr)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(addr >> 32)));
+    float *base = reinterpret_cast<float *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, kSlot * 4, 0x00020000);
+}
+
+// a thread's 32 floats (8 tiles) <-> its 128 bytes of a 64 KB slot
+__device__ __forceinline__ void put32(const float *slot, int tid, const f32x4 (&x)[8]) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 128 * tid + 16 * b, 0, kSc1);
+}
+
+// acc = sum over earlier segments pp < p of scale(pp) * slot(pp)
+template <typename F>
+__device__ void sum_slots(f32x4 (&acc)[8], const float *agg, int first, int p, int tid, F scale) {
+    constexpr int NB = 4;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < p; p0 += NB) {
+        f32x4 v[NB][8];
+#pragma unroll
+        for (int s = 0; s < NB; ++s)
+            if (p0 + s < p) {
+                const __amdgpu_buffer_rsrc_t rs = slot_rsrc(agg + static_cast<size_t>(first + p0 + s) * kSlot);
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    v[s][b] = __builtin_amdgcn_raw_buffer_load_b128(rs, 128 * tid + 16 * b, 0, kSc1);
+            }
+#pragma unroll
+        for (int s = 0; s < NB; ++s)
+            if (p0 + s < p) {
+                const float sc = scale(p0 + s);
+#pragma unroll
+                for (int b = 0; b < 8; ++b) acc[b] += sc * v[s][b];
+            }
+    }
+}
+
+struct Smem128 {
+    __bf16 K[W * LDW];   // chunk rows [s][a]
+    __bf16 V[W * LDW];   // [s][j]
+    __bf16 Q[W * LDW];   // [t][a]
+    __bf16 Uh[W * LDW];  // Us rows [s][b]: hi, mid and a third term
+    __bf16 Ul[W * LDW];
+    __bf16 Ux[W * LDW];
+    __bf16 Ah[W * LDN];  // masked scores A[t][i], then P[t][s], hi and lo
+    __bf16 Al[W * LDN];
+    int ticket;
+    uint32_t epoch;
+};
+// the S0 tiles of the Z product (128 rows, hi and lo) overlay K .. Uh
+static_assert(4 * W * LDW >= 2 * D * LDW, "S0 overlay does not fit");
+
+// The ten unmasked (t-block, i-block) tiles of a 64 x 64 masked product,
+// then the two masked tiles whose zeros a k-block read also covers.
+__device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
+    constexpr int kTb[12] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 2};
+    constexpr int kIb[12] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 3};
+    tb = kTb[idx];
+    ib = kIb[idx];
+}
+
+template <bool DECAY>
+__global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
+    __shared__ Smem128 sm;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+
+    // ---- ticket (head, segment), as in fwd_fused64.hip
+    const int hslot = static_cast<int>(blockIdx.x) % a.BH;
+    const int coh = hslot % kCohorts;
+    const int hc = (a.BH - 1 - coh) / kCohorts + 1;
+    const int guess = (static_cast<int>(blockIdx.x) / a.BH) * hc + hslot / kCohorts;
+    uint32_t *cl = a.ctrl + kLine * (1 + coh);
+    if (tid == 0) {
+        sm.ticket = static_cast<int>(__hip_atomic_fetch_add(&cl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        sm.epoch = next_epoch(__hip_atomic_load(&cl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), coh);
+    }
+    __syncthreads();
+    const int tk = __builtin_amdgcn_readfirstlane(sm.ticket);
+    const uint32_t epoch = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch)));
+    (void)guess;
+    if (tk < 0 || tk >= hc * a.P) {
+        if (tid == 0) __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int bh = coh + kCohorts * (tk % hc), p = tk / hc;
+    const size_t head_tok = static_cast<size_t>(bh) * a.n;
+    const float gam = head_gamma(a.gam, bh % a.H);
+    const float lg = DECAY ? log2f(gam) : 0.0f;
+    auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
+    const int c0 = p * a.L;
+    const int Lseg = min(a.L, a.nc - c0);
+    const int seg_tokens = a.L * W;
+    const size_t slot0 = static_cast<size_t>(bh) * a.P;
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- chunk inputs: each thread fetches two 16-byte pieces of q, k and v
+    uint4 pre[3][2];
+    auto fetch = [&](int j) {  // chunk j of the segment
+        const int Lc = j < Lseg ? min(W, a.n - (c0 + j) * W) : 0;
+        const size_t tok0 = head_tok + static_cast<size_t>(c0 + j) * W;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = tid + kThreads * u, row = idx >> 4, cg = idx & 15;
+            const size_t off = (tok0 + row) * D + cg * 8;
+            if (row < Lc) {
+                pre[0][u] = *reinterpret_cast<const uint4 *>(a.q + off);
+                pre[1][u] = *reinterpret_cast<const uint4 *>(a.k + off);
+                pre[2][u] = *reinterpret_cast<const uint4 *>(a.v + off);
+            } else {
+                pre[0][u] = pre[1][u] = pre[2][u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = tid + kThreads * u, row = idx >> 4, cg = idx & 15;
+            *reinterpret_cast<uint4 *>(&sm.Q[row * LDW + cg * 8]) = pre[0][u];
+            *reinterpret_cast<uint4 *>(&sm.K[row * LDW + cg * 8]) = pre[1][u];
+            *reinterpret_cast<uint4 *>(&sm.V[row * LDW + cg * 8]) = pre[2][u];
+        }
+    };
+
+    f32x4 sacc[8], xacc[8], cacc[8];  // S[a][b = 16w+r], X[a][j = 16w+r], Ct[a][j]
+#pragma unroll
+    for (int b = 0; b < 8; ++b) sacc[b] = xacc[b] = cacc[b] = zero4;
+
+    // One walk over the segment.  OUT: pass 2 (outputs); else pass 1 (Ct too).
+    auto walk = [&](auto out_tag) {
+        constexpr bool OUT = decltype(out_tag)::value;
+        fetch(0);
+        int pos = 0;  // token offset of the chunk in the segment
+        for (int jc = 0; jc < Lseg; ++jc) {
+            const int Lc = min(W, a.n - (c0 + jc) * W);
+            __syncthreads();  // (0) previous chunk's tile reads done
+            stage();
+            if (jc + 1 < Lseg) fetch(jc + 1);
+            __syncthreads();  // (1) chunk tiles ready
+
+            // -- masked scores A^T tiles -> A rows (hi/lo) in LDS
+            for (int idx = w; idx < 12; idx += 8) {
+                int tb, ib;
+                tri_tile(idx, tb, ib);
+                f32x4 at = zero4;
+                if (idx < 10) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        at = mfma(ld8<LDW>(sm.K, 16 * ib + r, 32 * ks + 8 * g),
+                                  ld8<LDW>(sm.Q, 16 * tb + r, 32 * ks + 8 * g), at);
+                    const int t = 16 * tb + r;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int i = 16 * ib + 4 * g + c;
+                        at[c] = i <= t ? gp(static_cast<float>(t - i)) * at[c] : 0.0f;
+                    }
+                }
+                bf16x4 h, lo;
+                split4(at, h, lo);
+                st4<LDN>(sm.Ah, 16 * tb + r, 16 * ib + 4 * g, h);
+                st4<LDN>(sm.Al, 16 * tb + r, 16 * ib + 4 * g, lo);
+            }
+            // -- S0 q part of U^T (rows b = 16w.., all t), from the S registers
+            f32x4 us_[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) us_[tb] = zero4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 sh, sl;
+                pair_operand(sacc[2 * kk], sacc[2 * kk + 1], sh, sl);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const bf16x8 qp = ld44<LDW>(sm.Q, 16 * tb + r, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                    us_[tb] = mfma(sh, qp, us_[tb]);
+                    us_[tb] = mfma(sl, qp, us_[tb]);
+                }
+            }
+            __syncthreads();  // (2) A rows ready
+            // -- U^T = e_t (S0 q_t) + K^T A^T; Us = f_t^2 U -> rows in LDS
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + r;
+                f32x4 ak = zero4;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (2 * ks <= tb) {
+                        const int rb = 32 * ks + 8 * g;
+                        const bf16x8 kt = tr8<LDW>(sm.K, rb, rb + 4, 16 * w, r);
+                        ak = mfma(kt, ld8<LDN>(sm.Ah, t, 32 * ks + 8 * g), ak);
+                        ak = mfma(kt, ld8<LDN>(sm.Al, t, 32 * ks + 8 * g), ak);
+                    }
+                }
+                const float e = gp(static_cast<float>(t + 1));
+                const float f2 = t < Lc ? gp(static_cast<float>(2 * (Lc - 1 - t))) : 0.0f;
+                const f32x4 us = f2 * (e * us_[tb] + ak);
+                bf16x4 h, mid, lo;
+                split3(us, h, mid, lo);
+                st4<LDW>(sm.Uh, t, 16 * w + 4 * g, h);
+                st4<LDW>(sm.Ul, t, 16 * w + 4 * g, mid);
+                st4<LDW>(sm.Ux, t, 16 * w + 4 * g, lo);
+            }
+            __syncthreads();  // (3) Us rows ready; A reads done
+            if constexpr (OUT) {
+                // -- P^T tiles -> P rows (hi/lo) in LDS (over the A rows)
+                for (int idx = w; idx < 12; idx += 8) {
+                    int tb, sb;
+                    tri_tile(idx, tb, sb);
+                    f32x4 pt = zero4;
+                    if (idx < 10) {
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            const bf16x8 qv = ld8<LDW>(sm.Q, 16 * tb + r, 32 * kb + 8 * g);
+                            pt = mfma(ld8<LDW>(sm.Uh, 16 * sb + r, 32 * kb + 8 * g), qv, pt);
+                            pt = mfma(ld8<LDW>(sm.Ul, 16 * sb + r, 32 * kb + 8 * g), qv, pt);
+                            pt = mfma(ld8<LDW>(sm.Ux, 16 * sb + r, 32 * kb + 8 * g), qv, pt);
+                        }
+                        const int t = 16 * tb + r;
+                        const float inv_f2 = t < Lc ? gp(static_cast<float>(-2 * (Lc - 1 - t))) : 0.0f;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) pt[c] = 16 * sb + 4 * g + c <= t ? inv_f2 * pt[c] : 0.0f;
+                    }
+                    bf16x4 h, lo;
+                    split4(pt, h, lo);
+                    st4<LDN>(sm.Ah, 16 * tb + r, 16 * sb + 4 * g, h);
+                    st4<LDN>(sm.Al, 16 * tb + r, 16 * sb + 4 * g, lo);
+                }
+                // -- the X0 part of num^T (rows j = 16w.., all t), from the X registers
+                f32x4 qx[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) qx[tb] = zero4;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    bf16x8 xh, xl;
+                    pair_operand(xacc[2 * kk], xacc[2 * kk + 1], xh, xl);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        const bf16x8 qp = ld44<LDW>(sm.Q, 16 * tb + r, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                        qx[tb] = mfma(xh, qp, qx[tb]);
+                        qx[tb] = mfma(xl, qp, qx[tb]);
+                    }
+                }
+                __syncthreads();  // (4) P rows ready
+                // -- num^T = V^T P^T + e_t^2 X0^T q_t; store
+                const size_t tok0 = head_tok + static_cast<size_t>(c0 + jc) * W;
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int t = 16 * tb + r;
+                    f32x4 pv = zero4;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (2 * ks <= tb) {
+                            const int rb = 32 * ks + 8 * g;
+                            const bf16x8 vt = tr8<LDW>(sm.V, rb, rb + 4, 16 * w, r);
+                            pv = mfma(vt, ld8<LDN>(sm.Ah, t, 32 * ks + 8 * g), pv);
+                            pv = mfma(vt, ld8<LDN>(sm.Al, t, 32 * ks + 8 * g), pv);
+                        }
+                    }
+                    const float e = gp(static_cast<float>(t + 1));
+                    const f32x4 o = pv + (e * e) * qx[tb];
+                    if (t < Lc)
+                        *reinterpret_cast<float4 *>(a.out + (tok0 + t) * D + 16 * w + 4 * g) =
+                            make_float4(o[0], o[1], o[2], o[3]);
+                }
+            }
+            // -- S <- g^L S + K^T diag(f) K   (columns b = 16w..)
+            {
+                const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab) sacc[ab] *= rho;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 kb = tr8<LDW>(sm.K, rb, rb + 4, 16 * w, r);
+                    bf16x8 kh = kb, kl;
+                    if (DECAY)
+                        scaled_split(kb, rb, [&](int s) { return gp(static_cast<float>(Lc - 1 - s)); }, kh, kl);
+#pragma unroll
+                    for (int ab = 0; ab < 8; ++ab) {
+                        const bf16x8 ka = tr8<LDW>(sm.K, rb, rb + 4, 16 * ab, r);
+                        sacc[ab] = mfma(ka, kh, sacc[ab]);
+                        if (DECAY) sacc[ab] = mfma(ka, kl, sacc[ab]);
+                    }
+                }
+            }
+            // -- X <- g^2L X + Us^T V   (columns j = 16w..)
+            {
+                const float rho2 = gp(static_cast<float>(2 * Lc));
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab) xacc[ab] *= rho2;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 vt = tr8<LDW>(sm.V, rb, rb + 4, 16 * w, r);
+#pragma unroll
+                    for (int ab = 0; ab < 8; ++ab) {
+                        xacc[ab] = mfma(tr8<LDW>(sm.Uh, rb, rb + 4, 16 * ab, r), vt, xacc[ab]);
+                        xacc[ab] = mfma(tr8<LDW>(sm.Ul, rb, rb + 4, 16 * ab, r), vt, xacc[ab]);
+                    }
+                }
+            }
+            if constexpr (!OUT) {
+                // -- Ct <- g^2L Ct + Q^T diag(g^(pos + 2L - 1 - s)) V   (columns j = 16w..)
+                const float rho2 = gp(static_cast<float>(2 * Lc));
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab) cacc[ab] *= rho2;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 vt = tr8<LDW>(sm.V, rb, rb + 4, 16 * w, r);
+                    bf16x8 vh = vt, vl;
+                    if (DECAY)
+                        scaled_split(vt, rb, [&](int s) { return gp(static_cast<float>(pos + 2 * Lc - 1 - s)); }, vh,
+                                     vl);
+#pragma unroll
+                    for (int ab = 0; ab < 8; ++ab) {
+                        const bf16x8 qa = tr8<LDW>(sm.Q, rb, rb + 4, 16 * ab, r);
+                        cacc[ab] = mfma(qa, vh, cacc[ab]);
+                        if (DECAY) cacc[ab] = mfma(qa, vl, cacc[ab]);
+                    }
+                }
+            }
+            pos += Lc;
+        }
+    };
+
+    if (a.P > 1) {
+        walk(std::integral_constant<bool, false>{});
+        // ---- round 1: publish the segment's key moment; S carry from the earlier segments
+        put32(a.aggS + (slot0 + p) * kSlot, tid, sacc);
+        wait_stores();
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(&a.flags[2 * (slot0 + p)], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int pp = tid; pp < p; pp += kThreads)
+            if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch))
+                __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        sum_slots(sacc, a.aggS, static_cast<int>(slot0), p, tid,
+                  [&](int pp) { return gp(static_cast<float>((p - 1 - pp) * seg_tokens)); });
+        // ---- Z = S0 Ct + Lz: S0 -> LDS rows (hi/lo); lane holds S0[a][b = 16w+r] = S0[b][a]
+        __bf16 *S0h = sm.K, *S0l = sm.K + D * LDW;
+#pragma unroll
+        for (int ab = 0; ab < 8; ++ab) {
+            bf16x4 h, lo;
+            split4(sacc[ab], h, lo);
+            st4<LDW>(S0h, 16 * w + r, 16 * ab + 4 * g, h);
+            st4<LDW>(S0l, 16 * w + r, 16 * ab + 4 * g, lo);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 ch, cl2;
+            pair_operand(cacc[2 * kk], cacc[2 * kk + 1], ch, cl2);
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab) {
+                const int row = 16 * ab + r;
+                const bf16x8 s0h = ld44<LDW>(S0h, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                const bf16x8 s0l = ld44<LDW>(S0l, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                xacc[ab] = mfma(s0h, ch, xacc[ab]);
+                xacc[ab] = mfma(s0h, cl2, xacc[ab]);
+                xacc[ab] = mfma(s0l, ch, xacc[ab]);
+            }
+        }
+        // ---- round 2: publish Z; X carry from the earlier segments
+        put32(a.aggZ + (slot0 + p) * kSlot, tid, xacc);
+        wait_stores();
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(&a.flags[2 * (slot0 + p) + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int pp = tid; pp < p; pp += kThreads)
+            if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch))
+                __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        sum_slots(xacc, a.aggZ, static_cast<int>(slot0), p, tid,
+                  [&](int pp) { return gp(static_cast<float>(2 * (p - 1 - pp) * seg_tokens)); });
+    }
+    walk(std::integral_constant<bool, true>{});
+
+    // ---- the cohort's last workgroup resets its counters and advances its epoch
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&cl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == static_cast<uint32_t>(hc * a.P - 1)) {
+            __hip_atomic_store(&cl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&cl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&cl[2], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (blockIdx.x == 0) __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+void geometry(int BH, int nc, int *P, int *L) {
+    // about one workgroup per CU: P segments per head of L chunks each
+    int p = (256 + BH - 1) / BH;
+    if (p > nc) p = nc;
+    if (p < 1) p = 1;
+    *L = (nc + p - 1) / p;
+    *P = (nc + *L - 1) / *L;
+}
+
+struct Layout128 {
+    size_t flags, aggS, aggZ, total;
+};
+
+Layout128 layout(int BH, int P) {
+    Layout128 L{};
+    const size_t slots = static_cast<size_t>(BH) * P;
+    L.flags = 0;
+    L.aggS = align256(2 * slots * sizeof(uint32_t));
+    L.aggZ = L.aggS + (P > 1 ? slots * kSlot * sizeof(float) : 0);
+    L.total = L.aggZ + (P > 1 ? slots * kSlot * sizeof(float) : 0);
+    return L;
+}
+
+}  // namespace
+
+bool fused128_supported(const FwdProblem &p) {
+    if (!(p.dtype == HLA_BF16 && p.d == 128 && p.dv == 128 && p.ridge == 0.0f && !p.normalize &&
+          p.den == nullptr && p.init.S == nullptr && p.fin.S == nullptr && p.n > 0))
+        return false;
+    const int nh = p.gam.per_head ? p.H : 1;
+    for (int h = 0; h < nh; ++h)
+        if (p.gam.g[h] < kMinGamma) return false;
+    return true;
+}
+
+size_t fused128_workspace_bytes(int BH, int n) {
+    const int nc = (n + W - 1) / W;
+    int P, L;
+    geometry(BH, nc, &P, &L);
+    return layout(BH, P).total;
+}
+
+hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+    Args128 a{};
+    a.H = p.H; a.n = p.n; a.BH = p.B * p.H;
+    a.nc = (p.n + W - 1) / W;
+    geometry(a.BH, a.nc, &a.P, &a.L);
+    a.q = static_cast<const uint16_t *>(p.q);
+    a.k = static_cast<const uint16_t *>(p.k);
+    a.v = static_cast<const uint16_t *>(p.v);
+    a.out = p.out;
+    a.ctrl = ctrl;
+    const Layout128 L = layout(a.BH, a.P);
+    char *base = static_cast<char *>(data);
+    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    a.aggS = reinterpret_cast<float *>(base + L.aggS);
+    a.aggZ = reinterpret_cast<float *>(base + L.aggZ);
+    a.gam = p.gam;
+    const int nh = p.gam.per_head ? p.H : 1;
+    bool decay = false;
+    for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
+    const dim3 grid(static_cast<unsigned>(static_cast<size_t>(a.BH) * a.P));
+    if (decay)
+        hipLaunchKernelGGL(k_fused128<true>, grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_fused128<false>, grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace hla

@@ -53,7 +53,11 @@
 // Precision.  q, k, v are exact in bf16.  Every operand formed in fp32 (A,
 // Us, P, S0, X0, and f-scaled K) is split as x = hi + lo with hi = bf16(x),
 // lo = bf16(x - hi); each such product is two bf16 MFMAs with fp32
-// accumulation, leaving ~2^-16 relative operand error.
+// accumulation, leaving ~2^-17 relative operand error.  Us enters P with a
+// third term (x = hi + mid + lo to ~2^-26), held in the S0-hi tile once the
+// S0 reads are done: q_t . Us_s cancels heavily when q_t is nearly
+// orthogonal to S_s q_s (at t = s = 0 the value is (q.k)^2), where a
+// two-term Us would leave an error of ~2^-18 / cos(q, S q).
 //
 // MFMA v_mfma_f32_16x16x32_bf16: lane l = 16 g + r supplies row r of the A
 // operand and column r of the B operand at k = 8g .. 8g+7, and receives
@@ -138,6 +142,17 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
     for (int i = 0; i < 4; ++i) {
         hi[i] = static_cast<__bf16>(x[i]);
         lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
+    }
+}
+
+// three-term split: x = hi + mid + lo to ~2^-26 relative
+__device__ __forceinline__ void split3(const f32x4 &x, bf16x4 &hi, bf16x4 &mid, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = static_cast<__bf16>(x[i]);
+        const float r1 = x[i] - static_cast<float>(hi[i]);
+        mid[i] = static_cast<__bf16>(r1);
+        lo[i] = static_cast<__bf16>(r1 - static_cast<float>(mid[i]));
     }
 }
 
@@ -538,6 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             }
         }
         __syncthreads();  // (1) S0 ready; previous chunk's Us reads done
+        f32x4 usv[4];  // Us^T[b = 16bb+4g+c][t] of this wave's tokens
         if (valid) {
             // U^T[b][t] = e_t (S0 q_t)[b] + Uloc^T[b][t]; stored as Us = f_t^2 U rows
             const float e = gp(static_cast<float>(t + 1));
@@ -550,11 +566,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     acc = mfma(ld8(G.Sh, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
                     acc = mfma(ld8(G.Sl, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
                 }
-                const f32x4 us = f2 * (e * acc + uloc[jj][bb]);
-                bf16x4 h, lo;
-                split4(us, h, lo);
+                usv[bb] = f2 * (e * acc + uloc[jj][bb]);
+            }
+        }
+        __syncthreads();  // (1b) S0 reads done: the S0-hi tile takes Us's third term
+        if (valid) {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const f32x4 us = usv[bb];
+                bf16x4 h, mid, lo;
+                split3(us, h, mid, lo);
                 st4(G.Uh, t, 16 * bb + 4 * g, h);
-                st4(G.Ul, t, 16 * bb + 4 * g, lo);
+                st4(G.Ul, t, 16 * bb + 4 * g, mid);
+                st4(G.Sh, t, 16 * bb + 4 * g, lo);
                 if (DEN) {  // y increment: sum over this wave's tokens of Us rows
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
@@ -600,6 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     for (int kb = 0; kb < 2; ++kb) {
                         pt[sb] = mfma(ld8(G.Uh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
                         pt[sb] = mfma(ld8(G.Ul, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                        pt[sb] = mfma(ld8(G.Sh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
                         if (RIDGE) rt = mfma(ld8(G.K[jj], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], rt);
                     }
 #pragma unroll
@@ -684,6 +709,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) num[jj][jb] = zero4;
         }
+        __syncthreads();  // (2b) the third Us term in the S0-hi tile is read
     }
     __syncthreads();  // U tiles free for the exchange
 

@@ -118,7 +118,7 @@ hla_status check_common(int H, int d, int dv, hla_dtype dtype, const float *gamm
 int default_chunk(int d) { return d > 64 ? 128 : 64; }
 
 // Kernel path for a forward call.  init/fin/den only matter for the choice.
-enum class FwdPath { Generic, Fused64 };
+enum class FwdPath { Generic, Fused64, Fused128 };
 
 
 struct Geometry {
@@ -150,6 +150,7 @@ FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *i
     if (init) fp.init = *init;
     if (fin) fp.fin = *fin;
     if (hla::fused64_supported(fp)) return FwdPath::Fused64;
+    if (hla::fused128_supported(fp)) return FwdPath::Fused128;
     return FwdPath::Generic;
 }
 
@@ -163,6 +164,8 @@ size_t workspace_need(const hla_params *p, const Geometry &geo, const hla_state 
     size_t fused = 0;
     if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0)
         fused = hla::fused64_workspace_bytes(BH, p->n);
+    if (p->dtype == HLA_BF16 && p->d == 128 && p->dv == 128 && p->n > 0)
+        fused = hla::fused128_workspace_bytes(BH, p->n);
     (void)init; (void)fin; (void)den;
     return hla::kCtrlBytes + (gen > fused ? gen : fused);
 }
@@ -249,8 +252,11 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     if (n == 0 && !final_state) return ok();
     char *ws = static_cast<char *>(workspace);
     hipError_t e;
-    if (choose_path(p, geo, init, final_state, den, fp.gam) == FwdPath::Fused64) {
+    const FwdPath path = choose_path(p, geo, init, final_state, den, fp.gam);
+    if (path == FwdPath::Fused64) {
         e = hla::fused64_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
+    } else if (path == FwdPath::Fused128) {
+        e = hla::fused128_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
     } else {
         fp.ws = ws + hla::kCtrlBytes;
         fp.ws_bytes = workspace_bytes - hla::kCtrlBytes;

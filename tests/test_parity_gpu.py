@@ -120,6 +120,17 @@ def test_long_d128_workload():
     assert e <= tol
     assert slab_err(d, rd, lead=2) <= tol
     check_state(f, rf, tol)
+    # the output alone takes the one-launch d = 128 path (two walks per segment)
+    qg, kg, vg = on_gpu(q, k, v)
+    ws = torch.zeros(hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, chunk=w.chunk), dtype=torch.uint8,
+                     device=DEV)
+    before = ctrl_words(ws)
+    fo, _, _ = hla.forward_chunked(qg, kg, vg, gamma=w.gamma, chunk=w.chunk, workspace=ws)
+    torch.cuda.synchronize()
+    assert ctrl_words(ws)[2] != before[2], "the one-launch d=128 path did not run"
+    ef = row_err(fo.cpu(), ro)
+    print(f"fused d128 row error {ef:.3e}")
+    assert ef <= tol
 
 
 def decode_setup(B, H, prefix, d, dv, seed, gamma=None, ridge=0.0):
@@ -353,6 +364,7 @@ def ctrl_words(ws):
     (3, 5, 4095, "decay"),         # many segments, ragged
     (8, 8, 4096, "per_head"),      # more workgroups than CUs
     (1, 1, 16384, "decay"),        # one head, long
+    (4, 64, 256, None),            # 256 heads: the tail of q_0 . k_0 near zero at t = 0
 ])
 def test_fused_forward(B, H, n, gk):
     q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=900 + n + H)
@@ -472,4 +484,53 @@ def test_fused_causality_bitwise():
         for x in (q2, k2, v2):
             x[:, :, t + 1:] = -x[:, :, t + 1:]
         o2, _, _ = hla.forward_chunked(q2, k2, v2, chunk=64)
+        assert torch.equal(o2[:, :, : t + 1], out[:, :, : t + 1]), t
+
+
+# ---------------------------------------------------------------------------
+# the one-launch d = dv = 128 path (bf16, out only)
+
+@pytest.mark.parametrize("B,H,n,gk", [
+    (1, 2, 64, None),           # one chunk, one segment: a single walk
+    (1, 3, 1, "decay"),         # one token
+    (4, 64, 256, None),         # 256 heads: one segment per head, no rounds
+    (1, 16, 4096, "decay"),     # 16 segments of 4 chunks per head
+    (2, 3, 1000, "per_head"),   # ragged, one chunk per segment
+    (1, 1, 5000, "decay"),      # one head, 79 segments, ragged tail
+    (1, 4, 300, None),          # ragged tail inside the only chunk row
+])
+def test_fused128_forward(B, H, n, gk):
+    q, k, v = inputs.qkv(B, H, n, 128, 128, torch.bfloat16, seed=1300 + n + H)
+    g = None
+    if gk == "decay":
+        g = inputs.gamma_list_fp32([0.999] * H)
+    elif gk == "per_head":
+        g = inputs.gamma_list_fp32([1 - 2.0 ** -(5 + h % 8) for h in range(H)])
+    qg, kg, vg = on_gpu(q, k, v)
+    ws = torch.zeros(hla.workspace_size(B, H, n, 128, 128), dtype=torch.uint8, device=DEV)
+    before = ctrl_words(ws)
+    out, _, _ = hla.forward_chunked(qg, kg, vg, gamma=g, workspace=ws)
+    torch.cuda.synchronize()
+    after = ctrl_words(ws)
+    assert after[2] != before[2], "the one-launch d=128 path did not run"
+    assert after[3] == 0, after
+    import oracle
+    ro, _, _ = oracle.forward(q, k, v, gamma=g, want_state=False)
+    e = row_err(out.cpu(), ro)
+    print(f"fused d128 row error {e:.3e}")
+    assert e <= TOL[torch.bfloat16]
+    out2, _, _ = hla.forward_chunked(qg, kg, vg, gamma=g, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_fused128_causality_bitwise():
+    B, H, n = 1, 2, 700
+    q, k, v = on_gpu(*inputs.qkv(B, H, n, 128, 128, torch.bfloat16, seed=46))
+    out, _, _ = hla.forward_chunked(q, k, v)
+    for t in (5, 64, 300, 650):
+        q2, k2, v2 = q.clone(), k.clone(), v.clone()
+        for x in (q2, k2, v2):
+            x[:, :, t + 1:] = -x[:, :, t + 1:]
+        o2, _, _ = hla.forward_chunked(q2, k2, v2)
         assert torch.equal(o2[:, :, : t + 1], out[:, :, : t + 1]), t
