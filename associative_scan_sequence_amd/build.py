@@ -25,6 +25,9 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     # packed fp32 instructions are disabled in every device compile
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # ticket atomics are single-lane; wave-level aggregation would consume their
+    # result (and wait for it) before the input loads that follow are issued
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

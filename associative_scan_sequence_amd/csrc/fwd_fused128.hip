@@ -24,8 +24,9 @@
 // Z = S0 Ct + Lz is formed (one fp32 product) and published (round 2), and
 // the X carry is summed likewise.  Pass 2 walks again from the true carries
 // and writes the outputs.  With P = 1 (many heads, or short sequences) pass
-// 1 and both rounds are skipped.  Rounds, tickets and epochs work as in
-// fwd_fused64.hip (cohort ticket counters, device-coherent aggregates).
+// 1 and both rounds are skipped.  Rounds, segment order and epochs work as
+// in fwd_fused64.hip (a resident grid walking segments in increasing order,
+// device-coherent aggregates, a launch epoch on the flags).
 //
 // Layout.  512 threads = 8 waves; wave w owns feature block w (16 of 128):
 // the columns b = 16w.. of S (= its rows, S being symmetric), the columns
@@ -53,6 +54,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int W = 64;          // tokens per chunk
@@ -61,14 +63,13 @@ constexpr int LDW = 136;       // padded LDS row of 128 bf16 (272 bytes)
 constexpr int LDN = 72;        // padded LDS row of 64 bf16 (144 bytes)
 constexpr int kThreads = 512;  // eight waves
 constexpr int kSpinLimit = 1 << 22;
-constexpr int kCohorts = 16;
 constexpr int kLine = 64;
 constexpr int kSlot = 16384;   // floats per published 128 x 128 aggregate
 constexpr float kMinGamma = 0.75f;
-static_assert(kCtrlBytes >= (1 + kCohorts) * kLine * 4, "control block too small");
+static_assert(kCtrlBytes >= 2 * kLine * 4, "control block too small");
 
 struct Args128 {
-    int H, n, nc, P, L, BH;
+    int H, n, nc, P, L, BH, segs;  // segs = BH * P
     const uint16_t *q, *k, *v;
     float *out;
     uint32_t *ctrl;     // as in fwd_fused64.hip
@@ -171,9 +172,7 @@ __device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4
 
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
-__device__ __forceinline__ uint32_t next_epoch(uint32_t e, int cohort) {
-    return e * 1664525u + (1013904223u + 2u * static_cast<uint32_t>(cohort));
-}
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u + 1013904223u; }
 
 __device__ bool wait_flag(const uint32_t *f, uint32_t want) {
     for (int it = 0; it < kSpinLimit; ++it) {
@@ -235,7 +234,6 @@ struct Smem128 {
     __bf16 Ux[W * LDW];
     __bf16 Ah[W * LDN];  // masked scores A[t][i], then P[t][s], hi and lo
     __bf16 Al[W * LDN];
-    int ticket;
     uint32_t epoch;
 };
 // the S0 tiles of the Z product (128 rows, hi and lo) overlay K .. Uh
@@ -250,65 +248,54 @@ __device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
     ib = kIb[idx];
 }
 
-template <bool DECAY>
+// LOOP = false: one segment per workgroup (segs <= grid); true: workgroup b
+// takes segments b, b + grid, ... (grid = CU count < segs).
+template <bool DECAY, bool LOOP>
 __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     __shared__ Smem128 sm;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
 
-    // ---- ticket (head, segment), as in fwd_fused64.hip
-    const int hslot = static_cast<int>(blockIdx.x) % a.BH;
-    const int coh = hslot % kCohorts;
-    const int hc = (a.BH - 1 - coh) / kCohorts + 1;
-    const int guess = (static_cast<int>(blockIdx.x) / a.BH) * hc + hslot / kCohorts;
-    uint32_t *cl = a.ctrl + kLine * (1 + coh);
-    if (tid == 0) {
-        sm.ticket = static_cast<int>(__hip_atomic_fetch_add(&cl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        sm.epoch = next_epoch(__hip_atomic_load(&cl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), coh);
-    }
+    // ---- launch epoch (flags of this launch carry it)
+    if (tid == 0) sm.epoch = next_epoch(__hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     __syncthreads();
-    const int tk = __builtin_amdgcn_readfirstlane(sm.ticket);
     const uint32_t epoch = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch)));
-    (void)guess;
-    if (tk < 0 || tk >= hc * a.P) {
-        if (tid == 0) __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
-    const int bh = coh + kCohorts * (tk % hc), p = tk / hc;
-    const size_t head_tok = static_cast<size_t>(bh) * a.n;
-    const float gam = head_gamma(a.gam, bh % a.H);
-    const float lg = DECAY ? log2f(gam) : 0.0f;
+    float lg = 0.0f;
     auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto seg_body = [&](const int seg) __attribute__((always_inline)) {
+    const int bh = seg % a.BH, p = seg / a.BH;
+    const size_t head_tok = static_cast<size_t>(bh) * a.n;
+    lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
     const int c0 = p * a.L;
     const int Lseg = min(a.L, a.nc - c0);
     const int seg_tokens = a.L * W;
     const size_t slot0 = static_cast<size_t>(bh) * a.P;
-    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- chunk inputs: each thread fetches two 16-byte pieces of q, k and v
-    uint4 pre[3][2];
-    auto fetch = [&](int j) {  // chunk j of the segment
+    u32x4 pre[3][2];
+    auto fetch = [&](int j) __attribute__((always_inline)) {  // chunk j of the segment
+        // unconditional loads (rows past the chunk read the head's first row);
+        // they are masked to zero when staged
         const int Lc = j < Lseg ? min(W, a.n - (c0 + j) * W) : 0;
         const size_t tok0 = head_tok + static_cast<size_t>(c0 + j) * W;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int idx = tid + kThreads * u, row = idx >> 4, cg = idx & 15;
-            const size_t off = (tok0 + row) * D + cg * 8;
-            if (row < Lc) {
-                pre[0][u] = *reinterpret_cast<const uint4 *>(a.q + off);
-                pre[1][u] = *reinterpret_cast<const uint4 *>(a.k + off);
-                pre[2][u] = *reinterpret_cast<const uint4 *>(a.v + off);
-            } else {
-                pre[0][u] = pre[1][u] = pre[2][u] = make_uint4(0, 0, 0, 0);
-            }
+            const size_t off = (row < Lc ? tok0 + row : head_tok) * D + cg * 8;
+            pre[0][u] = *reinterpret_cast<const u32x4 *>(a.q + off);
+            pre[1][u] = *reinterpret_cast<const u32x4 *>(a.k + off);
+            pre[2][u] = *reinterpret_cast<const u32x4 *>(a.v + off);
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](int Lc) __attribute__((always_inline)) {
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int idx = tid + kThreads * u, row = idx >> 4, cg = idx & 15;
-            *reinterpret_cast<uint4 *>(&sm.Q[row * LDW + cg * 8]) = pre[0][u];
-            *reinterpret_cast<uint4 *>(&sm.K[row * LDW + cg * 8]) = pre[1][u];
-            *reinterpret_cast<uint4 *>(&sm.V[row * LDW + cg * 8]) = pre[2][u];
+            const bool ok = row < Lc;
+            *reinterpret_cast<u32x4 *>(&sm.Q[row * LDW + cg * 8]) = ok ? pre[0][u] : z;
+            *reinterpret_cast<u32x4 *>(&sm.K[row * LDW + cg * 8]) = ok ? pre[1][u] : z;
+            *reinterpret_cast<u32x4 *>(&sm.V[row * LDW + cg * 8]) = ok ? pre[2][u] : z;
         }
     };
 
@@ -324,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         for (int jc = 0; jc < Lseg; ++jc) {
             const int Lc = min(W, a.n - (c0 + jc) * W);
             __syncthreads();  // (0) previous chunk's tile reads done
-            stage();
+            stage(Lc);
             if (jc + 1 < Lseg) fetch(jc + 1);
             __syncthreads();  // (1) chunk tiles ready
 
@@ -565,15 +552,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     }
     walk(std::integral_constant<bool, true>{});
 
-    // ---- the cohort's last workgroup resets its counters and advances its epoch
+    __syncthreads();  // this segment's LDS reads are done before the next one is staged
+    };
+    // (a loop around the body costs registers even when it runs once, so the
+    // one-segment-per-workgroup launch calls it straight)
+    if constexpr (LOOP) {
+        for (int seg = static_cast<int>(blockIdx.x); seg < a.segs; seg += static_cast<int>(gridDim.x)) seg_body(seg);
+    } else {
+        seg_body(static_cast<int>(blockIdx.x));
+    }
+
+    // ---- the last workgroup to finish resets the counter and advances the epoch
     if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&cl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == static_cast<uint32_t>(hc * a.P - 1)) {
-            __hip_atomic_store(&cl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&cl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&cl[2], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (blockIdx.x == 0) __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -626,6 +622,7 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     a.H = p.H; a.n = p.n; a.BH = p.B * p.H;
     a.nc = (p.n + W - 1) / W;
     geometry(a.BH, a.nc, &a.P, &a.L);
+    a.segs = a.BH * a.P;
     a.q = static_cast<const uint16_t *>(p.q);
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
@@ -640,11 +637,20 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
-    const dim3 grid(static_cast<unsigned>(static_cast<size_t>(a.BH) * a.P));
-    if (decay)
-        hipLaunchKernelGGL(k_fused128<true>, grid, dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL(k_fused128<false>, grid, dim3(kThreads), 0, st, a);
+    // one workgroup per CU at most (its LDS fills the CU), so the whole grid is resident
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const bool loop = a.segs > cus;
+    const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
+    if (decay) {
+        if (loop) hipLaunchKernelGGL((k_fused128<true, true>), grid, dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_fused128<true, false>), grid, dim3(kThreads), 0, st, a);
+    } else {
+        if (loop) hipLaunchKernelGGL((k_fused128<false, true>), grid, dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_fused128<false, false>), grid, dim3(kThreads), 0, st, a);
+    }
     return hipGetLastError();
 }
 
