@@ -46,7 +46,44 @@ def parse():
     ap.add_argument("--seed", type=int, default=1001)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the secondary workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device copies of 256 MiB (for scaling HBM counters)")
     return ap.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fused64_B4_H8_n2048_d64_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "associative_scan_sequence_amd", "csrc", "fwd_fused64.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the d=64 kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    m_hash = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    m_bytes = re.search(r"HBM bytes per launch: ([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src:
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_calibration():
+    """Plain 256 MiB device-to-device copies: the counters FETCH_SIZE and
+    WRITE_SIZE of these dispatches give the scale from counter KiB to bytes."""
+    import torch
+
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "copies": 5}))
 
 
 def algorithmic_bytes(w) -> int:
@@ -191,6 +228,9 @@ def main():
     import hla_inputs as inputs
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     w = inputs.FWD_D64
     q, k, v = inputs.workload_qkv(w, args.seed)
@@ -285,7 +325,7 @@ def main():
                    "timing": "eager" if args.eager else "hip_graph",
                    "input_copies_rotated": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "k_fused64 (the whole hla_forward_chunked call is one launch)",
                      "algorithmic_bytes_per_step": alg},
         "eager_ms_per_step": eager_ms,
