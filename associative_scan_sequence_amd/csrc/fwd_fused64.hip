@@ -295,8 +295,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
         const int t = 16 * w + r;   // this lane's token (column of the B operand)
         GroupLds &G = sm.grp[grp];
         const int jbase = kPerGroup * grp;
-        // ---- global loads of this group's chunks (issued for the predicted segment):
-        // keys first (phase A needs only them), then queries, then values.  The
+        // ---- global loads of this group's chunks: keys and queries now, values
+        // once the segment's key moment is published (the publishing stores must
+        // not wait behind them, and phase B is the first to read them).  The
         // loads are unconditional (rows past the chunk read the head's first row)
         // and are masked to zero only where they are used, so each use waits for
         // its own loads alone.
@@ -329,14 +330,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     const size_t src = t < Lcs[jj] ? tok0s[jj] + t : head_tok_;
                     qx[jj][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
                 }
+        };
+        auto issue_v_loads = [&](int sg_) __attribute__((always_inline)) {
+            const int bh_ = sg_ % a.BH, p_ = sg_ / a.BH;
+            const size_t head_tok_ = static_cast<size_t>(bh_) * a.n;
+            const int c0_ = p_ * a.L;
+            const int Lseg_ = min(a.L, a.nc - c0_);
 #pragma unroll
-            for (int jj = 0; jj < kPerGroup; ++jj)
+            for (int jj = 0; jj < kPerGroup; ++jj) {
+                const int j = kPerGroup * grp + jj;
+                const int Lc = j < Lseg_ ? min(W, a.n - (c0_ + j) * W) : 0;
+                const size_t tok0 = head_tok_ + static_cast<size_t>(c0_ + j) * W;
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-                    const size_t src = row < Lcs[jj] ? tok0s[jj] + row : head_tok_;
+                    const size_t src = row < Lc ? tok0 + row : head_tok_;
                     vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
                 }
+            }
         };
         issue_loads(seg);
         const int bh = seg % a.BH, p = seg / a.BH;
@@ -352,7 +363,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
         int lc_of[kPerGroup];  // tokens in this group's chunk jj (0 if none)
 #pragma unroll
         for (int jj = 0; jj < kPerGroup; ++jj) lc_of[jj] = jj < nmine ? chunk_len(jbase + jj) : 0;
-        if (tid == 0 && seg == static_cast<int>(blockIdx.x)) sm.epoch = ep_raw;
         f32x4 sc0[4], sg[4];  // first chunk's key moment, group sum
 
         // ---- stage key rows (values follow once phase A and the carry-free work are issued)
@@ -410,29 +420,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             }
         }
 
-        if (seg == static_cast<int>(blockIdx.x))
-            epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch))));
         // group 0 hands its sum to group 1, which publishes the segment sum
         float *xch = reinterpret_cast<float *>(sm.grp[1].Uh);  // 16 KB inside group 1's U tiles
         if (grp == 0) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch + xi * 16 + 4 * b) = sg[b];
         }
+        // the launch epoch (read at the start; its load has long returned)
+        if (tid == 0 && seg == static_cast<int>(blockIdx.x)) sm.epoch = ep_raw;
         __syncthreads();
+        if (seg == static_cast<int>(blockIdx.x))
+            epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch))));
         const size_t slot = static_cast<size_t>(bh) * a.P + p;
         f32x4 partA[4];  // group 0's sum (group 1 only)
         if (grp == 1) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) partA[b] = *reinterpret_cast<const f32x4 *>(xch + xi * 16 + 4 * b);
-            f32x4 seg[4];
+            f32x4 agg[4];
             const float rhoB = gp(static_cast<float>(lenB));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) seg[b] = rhoB * partA[b] + sg[b];
-            put16(a.aggS + slot * 4096, xi, seg);
+            for (int b = 0; b < 4; ++b) agg[b] = rhoB * partA[b] + sg[b];
+            put16(a.aggS + slot * 4096, xi, agg);
             wait_stores();
         }
         __syncthreads();
         if (tid == 0) __hip_atomic_store(&a.flags[2 * slot], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        issue_v_loads(seg);
 
         bf16x8 qn[kPerGroup][2];  // q of token 16w+r, features 32ks+8g..: B operand
 #pragma unroll
@@ -587,7 +600,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     usv[bb] = f2 * (e * acc + uloc[jj][bb]);
                 }
             }
-            __syncthreads();  // (1b) S0 reads done: the S0-hi tile takes Us's third term
+            // Us's third term goes to the key tile (free in phase B) or, with the
+            // ridge (query rows there), to the S0-hi tile once its reads are done
+            __bf16 *Ux = RIDGE ? G.Sh : G.K[jj];
+            if (RIDGE) __syncthreads();  // (1b)
             if (valid) {
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
@@ -596,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     split3(us, h, mid, lo);
                     st4(G.Uh, t, 16 * bb + 4 * g, h);
                     st4(G.Ul, t, 16 * bb + 4 * g, mid);
-                    st4(G.Sh, t, 16 * bb + 4 * g, lo);
+                    st4(Ux, t, 16 * bb + 4 * g, lo);
                     if (DEN) {  // y increment: sum over this wave's tokens of Us rows
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
@@ -642,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                         for (int kb = 0; kb < 2; ++kb) {
                             pt[sb] = mfma(ld8(G.Uh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
                             pt[sb] = mfma(ld8(G.Ul, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                            pt[sb] = mfma(ld8(G.Sh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                            pt[sb] = mfma(ld8(Ux, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
                             if (RIDGE) rt = mfma(ld8(G.K[jj], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], rt);
                         }
 #pragma unroll
@@ -727,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) num[jj][jb] = zero4;
             }
-            __syncthreads();  // (2b) the third Us term in the S0-hi tile is read
+            if (RIDGE) __syncthreads();  // (2b) the third Us term in the S0-hi tile is read
         }
         __syncthreads();  // U tiles free for the exchange
 
@@ -747,19 +763,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
         if (grp == 1) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) partA[b] = *reinterpret_cast<const f32x4 *>(xch + xi * 16 + 4 * b);
-            f32x4 seg[4];
+            f32x4 agg[4];
             const float rhoB2 = gp(static_cast<float>(2 * lenB));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) seg[b] = rhoB2 * partA[b] + xacc[b];
-            put16(a.aggX + slot * 4096, xi, seg);
+            for (int b = 0; b < 4; ++b) agg[b] = rhoB2 * partA[b] + xacc[b];
+            put16(a.aggX + slot * 4096, xi, agg);
             if (RIDGE) {
                 const float rhoB = gp(static_cast<float>(lenB));
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     partC[b] = *reinterpret_cast<const f32x4 *>(xch2 + xi * 16 + 4 * b);
-                    seg[b] = rhoB * partC[b] + cacc[b];
+                    agg[b] = rhoB * partC[b] + cacc[b];
                 }
-                put16(a.aggC + slot * 4096, xi, seg);
+                put16(a.aggC + slot * 4096, xi, agg);
             }
             if (DEN && wt < 64) {
                 const float ys = gp(static_cast<float>(2 * lenB)) * sm.vec[0][0][wt] + sm.vec[1][0][wt];
