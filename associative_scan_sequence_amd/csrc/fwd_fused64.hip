@@ -93,8 +93,11 @@ constexpr int kPerGroup = 2;   // chunks per wave group
 constexpr int kMaxL = 4;       // chunks per workgroup
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kLine = 64;      // words per 256-byte control line
+constexpr int kTabWord = 2 * kLine;  // XCD table: one 64-bit entry per workgroup from this word
+constexpr int kTabCap = static_cast<int>(kCtrlBytes / 8) - kTabWord / 2;
+constexpr int kFlagStride = 32;  // words between flags (one 128-byte line each)
 constexpr float kMinGamma = 0.75f;
-static_assert(kCtrlBytes >= 2 * kLine * 4, "control block too small");
+static_assert(kCtrlBytes >= 2 * kLine * 4 + 256 * 8, "control block too small");
 
 struct FusedArgs {
     int H, n, nc, P, L, BH, segs;  // segs = BH * P
@@ -102,8 +105,10 @@ struct FusedArgs {
     float *out, *den;   // den may be null
     float ridge;
     uint32_t *ctrl;     // line 0: [2] launch count, [3] wait-timeout count;
-                        // line 1: [0] finished workgroups, [1] launch epoch
-    uint32_t *flags;    // [BH * P][2]: epoch when the S sum / X increment was published
+                        // line 1: [0] finished workgroups, [1] launch epoch;
+                        // from word kTabWord: [workgroup] (epoch << 32) | XCD id
+    uint32_t *flags;    // [BH * P][2] at kFlagStride words: epoch when the S sum /
+                        // X increment was published
     float *aggS, *aggX, *aggC;  // [BH * P][4096], in accumulator order
     float *aggV;        // [BH * P][128]: y then m
     GammaTab gam;
@@ -197,13 +202,33 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F7
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u + 1013904223u; }
 
-__device__ bool wait_flag(const uint32_t *f, uint32_t want) {
+// local: the writer and every reader run on one XCD, so its L2 is the point
+// of coherence and the flag is read where it lives, by an atomic (always
+// executed in L2, never served by a CU's L1).  Otherwise the flag is read
+// device-coherently.
+__device__ bool wait_flag(uint32_t *f, uint32_t want, bool local) {
     for (int it = 0; it < kSpinLimit; ++it) {
-        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
+        uint32_t v;
+        if (local) {
+            v = want;
+            __hip_atomic_compare_exchange_strong(f, &v, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+            v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (v == want) return true;
         __builtin_amdgcn_s_sleep(1);
     }
     return false;
 }
+
+__device__ __forceinline__ void set_flag(uint32_t *f, uint32_t v, bool local) {
+    if (local) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu; }
 
 constexpr int kSc1 = 16;  // buffer cache policy: sc1 (device scope)
 
@@ -218,15 +243,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
 
 // A group's 16 floats per thread (4 accumulator tiles) <-> a 16 KB slot; the
 // thread's 64 bytes sit at byte offset 64 * xi, xi = its tile position.
-__device__ __forceinline__ void put16(const float *slot, int xi, const f32x4 (&x)[4]) {
+// (local: plain stores, which the XCD's L2 holds; else written through)
+__device__ __forceinline__ void put16(const float *slot, int xi, const f32x4 (&x)[4], bool local) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
+    if (local) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 64 * xi + 16 * b, 0, kSc1);
+        for (int b = 0; b < 4; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 64 * xi + 16 * b, 0, 0);
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 64 * xi + 16 * b, 0, kSc1);
+    }
 }
 
 // acc += sum over n slots of scale[i] * slot_i; all loads of a batch are
 // issued before the first add.
-template <int NB>
+template <int NB, int POL>
 __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&slots)[NB],
                                           const float (&scale)[NB], int n, int xi) {
     f32x4 v[NB][4];
@@ -236,7 +267,7 @@ __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&
             const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slots[s]);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                v[s][b] = __builtin_amdgcn_raw_buffer_load_b128(rs, 64 * xi + 16 * b, 0, kSc1);
+                v[s][b] = __builtin_amdgcn_raw_buffer_load_b128(rs, 64 * xi + 16 * b, 0, POL);
         }
 #pragma unroll
     for (int s = 0; s < NB; ++s)
@@ -262,8 +293,8 @@ struct Smem {
     float vec[2][8][64];       // [group]: y, y after chunk 0, m, m after chunk 0,
                                //          chunk y0, chunk m0, group start y, m
     float vcar[2][64];         // y and m carries of the segment
-    int ticket;
     uint32_t epoch;
+    int local;
 };
 
 // LOOP = false: one segment per workgroup (segs <= grid); true: workgroup b
@@ -350,6 +381,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             }
         };
         issue_loads(seg);
+        const bool first = seg == static_cast<int>(blockIdx.x);
+        uint64_t *const xtab = reinterpret_cast<uint64_t *>(a.ctrl + kTabWord);
+        const bool tab_ok = static_cast<int>(gridDim.x) <= kTabCap;
+        if (tid == 0 && first && tab_ok)  // this workgroup's XCD, tagged with the launch epoch
+            __hip_atomic_store(xtab + blockIdx.x, (static_cast<uint64_t>(next_epoch(ep_raw)) << 32) | 0x100u | xcd_id(),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int bh = seg % a.BH, p = seg / a.BH;
         const size_t head_tok = static_cast<size_t>(bh) * a.n;
         lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
@@ -374,6 +411,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                 *reinterpret_cast<u32x4 *>(&G.K[jj][row * LDR + cg * 8]) = row < lc_of[jj] ? kx[jj][u] : z4;
             }
         __syncthreads();
+        // ---- wave 0 fetches the XCD entries of the workgroups that hold this
+        // head's segments (segment s runs on workgroup s mod grid); they were
+        // written at the start, and are checked after phase A
+        uint64_t tabv = 0;
+        if (tid < 64 && tid < a.P && tab_ok)
+            tabv = __hip_atomic_load(xtab + (tid * a.BH + bh) % static_cast<int>(gridDim.x), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
 
         // ================= phase A: the segment's key moment sum ==================
         // acc (rows a = 16w+4g+c, cols b = 16bb+r) = K^T diag(f) K of one chunk
@@ -420,6 +464,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             }
         }
 
+        // ---- the exchange with other segments of this head goes through the
+        // XCD's L2 when every one of them runs on this XCD, else device-coherently;
+        // all of them read the same entries, so they all take the same choice
+        if (tid < 64) {
+            const uint32_t ep_now = first ? next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))))
+                                          : epoch;
+            const uint32_t me = 0x100u | xcd_id();
+            bool ok = tab_ok;
+            for (int i = tid; ok && i < a.P; i += 64) {
+                uint64_t *ent = xtab + (i * a.BH + bh) % static_cast<int>(gridDim.x);
+                uint64_t v = i == tid ? tabv : __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int it = 0; static_cast<uint32_t>(v >> 32) != ep_now && it < kSpinLimit; ++it) {
+                    __builtin_amdgcn_s_sleep(1);
+                    v = __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                ok = static_cast<uint32_t>(v >> 32) == ep_now && static_cast<uint32_t>(v) == me;
+            }
+            const bool all = __builtin_amdgcn_ballot_w64(!ok) == 0;
+            if (tid == 0) sm.local = all ? 1 : 0;
+        }
         // group 0 hands its sum to group 1, which publishes the segment sum
         float *xch = reinterpret_cast<float *>(sm.grp[1].Uh);  // 16 KB inside group 1's U tiles
         if (grp == 0) {
@@ -427,10 +491,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4 *>(xch + xi * 16 + 4 * b) = sg[b];
         }
         // the launch epoch (read at the start; its load has long returned)
-        if (tid == 0 && seg == static_cast<int>(blockIdx.x)) sm.epoch = ep_raw;
+        if (tid == 0 && first) sm.epoch = ep_raw;
         __syncthreads();
-        if (seg == static_cast<int>(blockIdx.x))
+        if (first)
             epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch))));
+        const bool local = __builtin_amdgcn_readfirstlane(sm.local) != 0;
         const size_t slot = static_cast<size_t>(bh) * a.P + p;
         f32x4 partA[4];  // group 0's sum (group 1 only)
         if (grp == 1) {
@@ -440,11 +505,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             const float rhoB = gp(static_cast<float>(lenB));
 #pragma unroll
             for (int b = 0; b < 4; ++b) agg[b] = rhoB * partA[b] + sg[b];
-            put16(a.aggS + slot * 4096, xi, agg);
+            put16(a.aggS + slot * 4096, xi, agg, local);
             wait_stores();
         }
         __syncthreads();
-        if (tid == 0) __hip_atomic_store(&a.flags[2 * slot], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) set_flag(&a.flags[2 * slot * kFlagStride], epoch, local);
         issue_v_loads(seg);
 
         bf16x8 qn[kPerGroup][2];  // q of token 16w+r, features 32ks+8g..: B operand
@@ -510,7 +575,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     slots[s2] = agg + (static_cast<size_t>(bh) * a.P + pp) * 4096;
                     scale[s2] = gp(static_cast<float>(pw * (p - 1 - pp) * seg_tokens));
                 }
-                add_slots<NB>(acc, slots, scale, cnt, xi);
+                if (local) add_slots<NB, 0>(acc, slots, scale, cnt, xi);
+                else add_slots<NB, kSc1>(acc, slots, scale, cnt, xi);
             }
             float *mine = reinterpret_cast<float *>(sm.grp[grp].Uh);
             const float *other = reinterpret_cast<const float *>(sm.grp[grp ^ 1].Uh);
@@ -524,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
         };
         auto wait_round = [&](int which) {
             for (int pp = tid; pp < p; pp += kThreads)
-                if (!wait_flag(&a.flags[2 * (static_cast<size_t>(bh) * a.P + pp) + which], epoch))
+                if (!wait_flag(&a.flags[(2 * (static_cast<size_t>(bh) * a.P + pp) + which) * kFlagStride], epoch, local))
                     __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
         };
@@ -767,7 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             const float rhoB2 = gp(static_cast<float>(2 * lenB));
 #pragma unroll
             for (int b = 0; b < 4; ++b) agg[b] = rhoB2 * partA[b] + xacc[b];
-            put16(a.aggX + slot * 4096, xi, agg);
+            put16(a.aggX + slot * 4096, xi, agg, local);
             if (RIDGE) {
                 const float rhoB = gp(static_cast<float>(lenB));
 #pragma unroll
@@ -775,20 +841,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     partC[b] = *reinterpret_cast<const f32x4 *>(xch2 + xi * 16 + 4 * b);
                     agg[b] = rhoB * partC[b] + cacc[b];
                 }
-                put16(a.aggC + slot * 4096, xi, agg);
+                put16(a.aggC + slot * 4096, xi, agg, local);
             }
             if (DEN && wt < 64) {
                 const float ys = gp(static_cast<float>(2 * lenB)) * sm.vec[0][0][wt] + sm.vec[1][0][wt];
-                __hip_atomic_store(&a.aggV[slot * 128 + wt], ys, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (local) __hip_atomic_store(&a.aggV[slot * 128 + wt], ys, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                else __hip_atomic_store(&a.aggV[slot * 128 + wt], ys, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (MV) {
                     const float ms = gp(static_cast<float>(lenB)) * sm.vec[0][2][wt] + sm.vec[1][2][wt];
-                    __hip_atomic_store(&a.aggV[slot * 128 + 64 + wt], ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (local) __hip_atomic_store(&a.aggV[slot * 128 + 64 + wt], ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    else __hip_atomic_store(&a.aggV[slot * 128 + 64 + wt], ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             wait_stores();
         }
         __syncthreads();
-        if (tid == 0) __hip_atomic_store(&a.flags[2 * slot + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) set_flag(&a.flags[(2 * slot + 1) * kFlagStride], epoch, local);
         wait_round(1);
         f32x4 xstart[4], cstart[4];
         {
@@ -809,8 +877,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             if (wt < 64 && (grp == 0 || MV)) {
                 float acc = 0.0f;
                 for (int pp = 0; pp < p; ++pp) {
-                    const float x = __hip_atomic_load(&a.aggV[(static_cast<size_t>(bh) * a.P + pp) * 128 + 64 * grp + wt],
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    float *src = &a.aggV[(static_cast<size_t>(bh) * a.P + pp) * 128 + 64 * grp + wt];
+                    const float x = local ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                          : __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     acc += gp(static_cast<float>((2 - grp) * (p - 1 - pp) * seg_tokens)) * x;
                 }
                 sm.vcar[grp][wt] = acc;
@@ -954,7 +1023,7 @@ Layout layout(int BH, int P) {
     Layout L{};
     const size_t slots = static_cast<size_t>(BH) * P;
     L.flags = 0;
-    L.aggS = L.flags + align256(2 * slots * sizeof(uint32_t));
+    L.aggS = L.flags + align256(2 * slots * kFlagStride * sizeof(uint32_t));
     L.aggX = L.aggS + slots * 4096 * sizeof(float);
     L.aggC = L.aggX + slots * 4096 * sizeof(float);
     L.aggV = L.aggC + slots * 4096 * sizeof(float);

@@ -38,11 +38,11 @@ struct FwdProblem {
 };
 
 // Every forward workspace starts with a control block of kCtrlBytes: words
-// that the one-launch kernels keep valid across calls (ticket counters,
-// finished-workgroup counters and launch epochs, one 256-byte line each, a
-// launch count and a wait-timeout count).  It must be zero before the first
-// call; no kernel writes it except through those counters.  Path data
-// follows it.
+// that the one-launch kernels keep valid across calls (a finished-workgroup
+// counter and the launch epoch, a launch count and a wait-timeout count, and
+// a table of epoch-tagged XCD ids, one per workgroup of the last launch).
+// It must be zero before the first call; no kernel writes it except through
+// those words.  Path data follows it.
 constexpr size_t kCtrlBytes = 8192;
 
 // Generic chunked forward: any d, dv, w in {16,32,64,128}, fp32 or bf16,
