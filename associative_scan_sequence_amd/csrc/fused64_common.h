@@ -1,0 +1,180 @@
+// fused64_common.h -- device helpers shared by the one-launch d = 64
+// forwards (k_fused64, k_fast64): bf16 MFMA operand plumbing on padded LDS
+// tiles, operand splits, and the cross-workgroup hand-off.
+#pragma once
+
+#include "device_common.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int W = 64;          // chunk width = d = dv
+constexpr int LDR = 72;        // padded LDS row, in bf16 elements (144 bytes)
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kLine = 64;      // words per 256-byte control line
+constexpr int kTabWord = 2 * kLine;  // XCD table: one 64-bit entry per workgroup from this word
+constexpr int kTabCap = static_cast<int>(kCtrlBytes / 8) - kTabWord / 2;
+constexpr int kFlagStride = 32;  // words between flags (one 128-byte line each)
+constexpr float kMinGamma = 0.75f;
+static_assert(kCtrlBytes >= 2 * kLine * 4 + 256 * 8, "control block too small");
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 consecutive bf16 of one LDS row
+__device__ __forceinline__ bf16x8 ld8(const __bf16 *base, int row, int col) {
+    return *reinterpret_cast<const bf16x8 *>(base + row * LDR + col);
+}
+
+// Transposed operand: lane (g, r) receives M[rb1 + e][col0 + r] (k slots 8g+e,
+// e < 4) and M[rb2 + e][col0 + r] (slots 8g+4+e); rb1, rb2 may depend on g.
+__device__ __forceinline__ bf16x8 tr8(const __bf16 *M, int rb1, int rb2, int col0, int r) {
+    const int col = col0 + 4 * (r & 3);
+    const __bf16 *p1 = M + (rb1 + (r >> 2)) * LDR + col;
+    const __bf16 *p2 = M + (rb2 + (r >> 2)) * LDR + col;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p2));
+    bf16x8 x;
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = ab[i];
+        x[4 + i] = bb[i];
+    }
+    return x;
+}
+
+// hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = static_cast<__bf16>(x[i]);
+        lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
+    }
+}
+
+// three-term split: x = hi + mid + lo to ~2^-26 relative
+__device__ __forceinline__ void split3(const f32x4 &x, bf16x4 &hi, bf16x4 &mid, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = static_cast<__bf16>(x[i]);
+        const float r1 = x[i] - static_cast<float>(hi[i]);
+        mid[i] = static_cast<__bf16>(r1);
+        lo[i] = static_cast<__bf16>(r1 - static_cast<float>(mid[i]));
+    }
+}
+
+// k-block operand from an accumulator pair (rows 32j+4g+e, 32j+16+4g+e)
+__device__ __forceinline__ void pair_operand(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
+    bf16x4 h0, l0, h1, l1;
+    split4(t0, h0, l0);
+    split4(t1, h1, l1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = h0[i];
+        hi[4 + i] = h1[i];
+        lo[i] = l0[i];
+        lo[4 + i] = l1[i];
+    }
+}
+
+__device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4 &v) {
+    *reinterpret_cast<bf16x4 *>(base + row * LDR + col) = v;
+}
+
+template <int CTL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTL, 0xF, 0xF, true));
+}
+
+// sum over the 16 lanes of a DPP row; every lane of the row receives it
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Cross-workgroup hand-off without cache maintenance: aggregates and flags
+// are written and read as device-coherent (sc1) accesses, so no L2
+// write-back or invalidate is needed.  The writer waits for its stores to
+// complete (vmcnt 0) before the workgroup barrier that precedes the flag
+// store; readers poll the flag and only then load the aggregate.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u + 1013904223u; }
+
+// local: the writer and every reader run on one XCD, so its L2 is the point
+// of coherence and the flag is read where it lives, by an atomic (always
+// executed in L2, never served by a CU's L1).  Otherwise the flag is read
+// device-coherently.
+__device__ bool wait_flag(uint32_t *f, uint32_t want, bool local) {
+    for (int it = 0; it < kSpinLimit; ++it) {
+        uint32_t v;
+        if (local) {
+            v = want;
+            __hip_atomic_compare_exchange_strong(f, &v, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+            v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (v == want) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+__device__ __forceinline__ void set_flag(uint32_t *f, uint32_t v, bool local) {
+    if (local) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu; }
+
+constexpr int kSc1 = 16;  // buffer cache policy: sc1 (device scope)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
+    // slot addresses are uniform across the wave; say so, so the descriptor is scalar
+    const uint64_t addr = reinterpret_cast<uint64_t>(slot);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(addr)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(addr >> 32)));
+    float *base = reinterpret_cast<float *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, 16384, 0x00020000);
+}
+
+// Decides, in wave 0, whether every workgroup that holds a segment of head
+// bh runs on this workgroup's XCD.  Segment s = i * BH + bh runs on
+// workgroup s mod grid; each workgroup wrote (epoch << 32) | 0x100 | XCD id
+// to xtab at its start.  tabv is the entry for i = lane, loaded earlier by
+// the caller (any value if lane >= P).  Every segment of the head reads the
+// same entries, so all of them reach the same answer.
+__device__ bool head_on_one_xcd(uint64_t *xtab, bool tab_ok, int P, int BH, int bh, uint32_t ep_now,
+                                uint64_t tabv) {
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    const uint32_t me = 0x100u | xcd_id();
+    bool ok = tab_ok;
+    for (int i = lane; ok && i < P; i += 64) {
+        uint64_t *ent = xtab + (i * BH + bh) % static_cast<int>(gridDim.x);
+        uint64_t v = i == lane ? tabv : __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int it = 0; static_cast<uint32_t>(v >> 32) != ep_now && it < kSpinLimit; ++it) {
+            __builtin_amdgcn_s_sleep(1);
+            v = __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ok = static_cast<uint32_t>(v >> 32) == ep_now && static_cast<uint32_t>(v) == me;
+    }
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+}
+
+}  // namespace
+}  // namespace hla

@@ -1,0 +1,617 @@
+// fwd_fast64.hip -- one-launch masked second-order HLA forward for
+// d = dv = 64, chunk w = 64, bf16 q/k/v, without ridge, denominator or
+// state I/O (the plain numerator q_t^T (S_t C_t - G_t)), on gfx950 MFMA.
+//
+// Method (Higher-order Linear Attention, paperlayer.ai summary sec. 4 and 5)
+// and per-chunk algebra as in fwd_fused64.hip: with the corrected carry
+// X = S C - G, per chunk (e_t = g^(t+1), f_s = g^(L-1-s))
+//   A = (Q K^T) o D_g o L,  U = diag(e) Q S0 + A K,  Us = diag(f^2) U,
+//   P = (Q Us^T) o L / f_t^2,  out = P V + diag(e^2) Q X0,
+//   S0 <- g^L S0 + K^T diag(f) K,  X0 <- g^2L X0 + Us^T V.
+// Same precision scheme: fp32 operands split into bf16 hi + lo, Us into
+// three terms for the P product.
+//
+// Division of work.  A workgroup (eight waves) owns a segment of up to four
+// consecutive chunks of one head.  Two roles per wave:
+//  * slice role: wave v works on a 16-token slice of two chunks (waves 0-3
+//    chunks 0, 1; waves 4-7 chunks 2, 3, slices in reverse order so that each
+//    SIMD pairs a light and a heavy slice of the triangular products): the
+//    scores, U, P, the local numerator and the output;
+//  * tile role: wave v owns tiles 2v, 2v+1 of a 64 x 64 moment (row block
+//    v/2, column blocks 2(v%2), 2(v%2)+1), summed over every chunk of the
+//    segment: the key moment S, the X increment, and the carries built from
+//    the aggregates other segments publish.  No partial sums are exchanged
+//    between waves, and wave v of a segment reads only what wave v of its
+//    predecessors wrote, so every wave publishes and waits on its own flags.
+// Order per segment (LDS holds sixteen 64 x 72 bf16 tiles T):
+//   stage K_c -> T[c]; S_seg by tiles; publish S
+//   carry-free A^T and Uloc^T = K^T A^T by slices; stage V_c -> T[4+c]
+//   round 1: S0 of every chunk -> T[8+2c] (hi), T[9+2c] (lo)
+//   U, Us of both slice chunks -> Us hi, mid in T[8+2c], T[9+2c], lo in T[c]
+//   Z_seg = sum_c decayed V_c^T Us_c by tiles; publish Z
+//   P and the local numerator by slices, while round 2 travels
+//   round 2: X0 of every chunk -> T[8+2c], T[9+2c]; out = num + e^2 Q X0
+// Segment s = p * BH + head runs on workgroup s mod grid; the grid never
+// exceeds the CU count and a workgroup fills a CU, so every workgroup is
+// resident and waits only on smaller segments of its head, which are running
+// or done.  When every workgroup holding a segment of a head runs on one XCD
+// (checked at run time from the XCD table in the control block), aggregates
+// and flags go through that XCD's L2; otherwise they are device-coherent.
+#include "fused64_common.h"
+
+namespace hla {
+namespace {
+
+constexpr int kFThreads = 512;
+constexpr int kFMaxL = 4;   // chunks per segment
+constexpr int kWaves = 8;
+
+struct FastArgs {
+    int H, n, nc, P, L, BH, segs;  // segs = BH * P
+    const uint16_t *q, *k, *v;
+    float *out;
+    uint32_t *ctrl;   // control block (epoch, done counter, XCD table)
+    uint32_t *flags;  // [BH * P][2 rounds][8 waves] at kFlagStride words: publication epoch
+    float *aggS, *aggX;  // [BH * P][16 tiles][64 lanes][4]
+    GammaTab gam;
+};
+
+struct FastSmem {
+    __bf16 T[16][W * LDR];
+    uint32_t epoch;
+};
+
+// wave v's two tiles <-> a 16 KB slot: tile i at tile index 2v+i, lane l's
+// 16 bytes at byte ((2v+i) * 64 + l) * 16
+__device__ __forceinline__ void put_tiles(const float *slot, int v, int l, const f32x4 (&x)[2], bool local) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
+    if (local) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
+    }
+}
+
+// acc += sum over n slots of scale[s] * (wave v's tiles of slot s); all
+// loads are issued before the first add
+template <int NB, int POL>
+__device__ __forceinline__ void add_tiles(f32x4 (&acc)[2], const float *const (&slots)[NB],
+                                          const float (&scale)[NB], int n, int v, int l) {
+    f32x4 x[NB][2];
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+        if (s < n) {
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slots[s]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) x[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((2 * v + i) * 64 + l) * 16, 0, POL);
+        }
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+        if (s < n) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[i] += scale[s] * x[s][i];
+        }
+}
+
+template <bool DECAY, bool LOOP>
+__global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
+    __shared__ FastSmem sm;
+    const int tid = threadIdx.x;
+    // launch epoch: read now, first needed when the segment sum is published
+    uint32_t ep_raw = 0;
+    if (tid == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    uint32_t epoch = 0;
+    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lg = 0.0f;
+    auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
+    uint64_t *const xtab = reinterpret_cast<uint64_t *>(a.ctrl + kTabWord);
+    const bool tab_ok = static_cast<int>(gridDim.x) <= kTabCap;
+
+    auto seg_body = [&](const int seg) __attribute__((always_inline)) {
+        // lane indices, laundered per pass in the looped launch so that the
+        // address arithmetic built on them is not hoisted out of the loop
+        int tid_l = static_cast<int>(threadIdx.x);
+        if constexpr (LOOP) asm volatile("" : "+v"(tid_l));
+        const int wave = tid_l >> 6, l = tid_l & 63, r = l & 15, g = l >> 4;
+        const int grp = wave >> 2, wv = wave & 3, wt = tid_l & 255;
+        const int w = grp == 0 ? wv : 3 - wv;  // slice role: tokens 16w.. of chunks 2grp, 2grp+1
+        const int t = 16 * w + r;              // this lane's token
+        const int tb = wave >> 1, cb = 2 * (wave & 1);  // tile role: row block, first column block
+
+        // ---- global loads of the slice chunks: keys and queries now, values
+        // once the key moment is published.  Unconditional (rows past the
+        // chunk read the head's first row), masked where used.
+        u32x4 kx[2][2], qx[2][2], vx[2][2];
+        auto chunk_rows = [&](int sg_, int jj, int &Lc_, size_t &tok0_, size_t &head_) {
+            const int bh_ = sg_ % a.BH, p_ = sg_ / a.BH;
+            head_ = static_cast<size_t>(bh_) * a.n;
+            const int c0_ = p_ * a.L, Lseg_ = min(a.L, a.nc - c0_), j = 2 * grp + jj;
+            Lc_ = j < Lseg_ ? min(W, a.n - (c0_ + j) * W) : 0;
+            tok0_ = head_ + static_cast<size_t>(c0_ + j) * W;
+        };
+        auto issue_kq = [&](int sg_) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                int Lc_;
+                size_t tok0_, head_;
+                chunk_rows(sg_, jj, Lc_, tok0_, head_);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
+                    const size_t src = row < Lc_ ? tok0_ + row : head_;
+                    kx[jj][u] = *reinterpret_cast<const u32x4 *>(a.k + src * W + cg * 8);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                int Lc_;
+                size_t tok0_, head_;
+                chunk_rows(sg_, jj, Lc_, tok0_, head_);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const size_t src = t < Lc_ ? tok0_ + t : head_;
+                    qx[jj][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
+                }
+            }
+        };
+        auto issue_v = [&](int sg_) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                int Lc_;
+                size_t tok0_, head_;
+                chunk_rows(sg_, jj, Lc_, tok0_, head_);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
+                    const size_t src = row < Lc_ ? tok0_ + row : head_;
+                    vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
+                }
+            }
+        };
+        issue_kq(seg);
+        const bool first = seg == static_cast<int>(blockIdx.x);
+        if (tid == 0 && first && tab_ok)  // this workgroup's XCD, tagged with the launch epoch
+            __hip_atomic_store(xtab + blockIdx.x, (static_cast<uint64_t>(next_epoch(ep_raw)) << 32) | 0x100u | xcd_id(),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int bh = seg % a.BH, p = seg / a.BH;
+        lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
+        const int c0 = p * a.L;
+        const int Lseg = min(a.L, a.nc - c0);  // chunks in this segment (1..4)
+        auto chunk_len = [&](int j) { return min(W, a.n - (c0 + j) * W); };
+        int lc_of[2];  // tokens in slice chunk jj (0 if none)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) lc_of[jj] = 2 * grp + jj < Lseg ? chunk_len(2 * grp + jj) : 0;
+        const size_t slot = static_cast<size_t>(bh) * a.P + p;
+        const bool publish = p + 1 < a.P;  // the last segment of a head has no readers
+
+        // ---- stage key rows
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
+                *reinterpret_cast<u32x4 *>(&sm.T[2 * grp + jj][row * LDR + cg * 8]) = row < lc_of[jj] ? kx[jj][u] : z4;
+            }
+        if (tid == 0 && first) sm.epoch = ep_raw;
+        __syncthreads();
+        if (first) epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch))));
+        // XCD entries of the workgroups holding this head's segments (checked after phase A)
+        uint64_t tabv = 0;
+        if (l < a.P && tab_ok)
+            tabv = __hip_atomic_load(xtab + (l * a.BH + bh) % static_cast<int>(gridDim.x), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+
+        // ================= phase A (tiles): key moments ===========================
+        // spre[c] = moment of chunks 0..c-1 at chunk c's start; srun ends as S_seg.
+        // Tile (a = 16tb+4g+e, b = 16(cb+i)+r) = sum_s K[s][a] f_s K[s][b].
+        f32x4 spre[kFMaxL][2], srun[2] = {zero4, zero4};
+#pragma unroll
+        for (int c = 0; c < kFMaxL; ++c) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) spre[c][i] = srun[i];
+            if (c < Lseg) {
+                const int Lc = chunk_len(c);
+                f32x4 acc[2] = {zero4, zero4};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 ka = tr8(sm.T[c], rb, rb + 4, 16 * tb, r);
+                    bf16x8 kb[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) kb[i] = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
+                    if (!DECAY) {
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) acc[i] = mfma(ka, kb[i], acc[i]);
+                    } else {
+                        f32x4 x0, x1;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x0[e] = gp(static_cast<float>(Lc - 1 - (rb + e))) * static_cast<float>(ka[e]);
+                            x1[e] = gp(static_cast<float>(Lc - 1 - (rb + 4 + e))) * static_cast<float>(ka[4 + e]);
+                        }
+                        bf16x8 h, lo;
+                        pair_operand(x0, x1, h, lo);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            acc[i] = mfma(h, kb[i], acc[i]);
+                            acc[i] = mfma(lo, kb[i], acc[i]);
+                        }
+                    }
+                }
+                const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+                for (int i = 0; i < 2; ++i) srun[i] = rho * srun[i] + acc[i];
+            }
+        }
+        // the exchange goes through the XCD's L2 when every workgroup holding
+        // a segment of this head runs on this XCD (every wave decides alike)
+        const bool local = head_on_one_xcd(xtab, tab_ok, a.P, a.BH, bh, epoch, tabv);
+        auto flag_of = [&](size_t sl, int round) { return &a.flags[((sl * 2 + round) * kWaves + wave) * kFlagStride]; };
+        if (publish) {
+            put_tiles(a.aggS + slot * 4096, wave, l, srun, local);
+            wait_stores();
+            if (l == 0) set_flag(flag_of(slot, 0), epoch, local);
+        }
+        issue_v(seg);
+
+        bf16x8 qn[2][2];  // q of token t, features 32ks+8g..: B operand
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) qn[jj][ks] = __builtin_bit_cast(bf16x8, t < lc_of[jj] ? qx[jj][ks] : z4);
+
+        // ================= carry-free slice work ====================================
+        // A^T tiles of this slice, then Uloc^T = K^T A^T (rows b, cols t)
+        f32x4 uloc[2][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 2 * grp + jj;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) uloc[jj][bb] = zero4;
+            if (lc_of[jj] > 0) {
+                f32x4 at[4];  // A^T[i = 16ib+4g+e][t], masked and decayed
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    at[ib] = zero4;
+                    if (ib <= w) {
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) at[ib] = mfma(ld8(sm.T[c], 16 * ib + r, 32 * ks + 8 * g), qn[jj][ks], at[ib]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 16 * ib + 4 * g + e;
+                            at[ib][e] = i <= t ? gp(static_cast<float>(t - i)) * at[ib][e] : 0.0f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (2 * ks <= w) {
+                        bf16x8 ah, al;
+                        pair_operand(at[2 * ks], at[2 * ks + 1], ah, al);
+#pragma unroll
+                        for (int bb = 0; bb < 4; ++bb) {
+                            const bf16x8 kt = tr8(sm.T[c], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * bb, r);
+                            uloc[jj][bb] = mfma(kt, ah, uloc[jj][bb]);
+                            uloc[jj][bb] = mfma(kt, al, uloc[jj][bb]);
+                        }
+                    }
+                }
+            }
+        }
+        // ---- value rows (read after the next barrier)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
+                *reinterpret_cast<u32x4 *>(&sm.T[4 + 2 * grp + jj][row * LDR + cg * 8]) = row < lc_of[jj] ? vx[jj][u] : z4;
+            }
+
+        // ---- carry = sum over earlier segments pp of g^(pw * gap) * (wave's
+        // tiles of agg[pp]), gap = tokens between; waits on this wave's flags only
+        const int seg_tokens = a.L * W;
+        auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int round, int pw) {
+            for (int pp = l; pp < p; pp += 64)
+                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local))
+                    __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            constexpr int NB = 8;
+            acc[0] = acc[1] = zero4;
+            for (int p0 = 0; p0 < p; p0 += NB) {
+                const float *slots[NB];
+                float scale[NB];
+#pragma unroll
+                for (int s2 = 0; s2 < NB; ++s2) {
+                    const int pp = min(p0 + s2, p - 1);
+                    slots[s2] = agg + (static_cast<size_t>(bh) * a.P + pp) * 4096;
+                    scale[s2] = gp(static_cast<float>(pw * (p - 1 - pp) * seg_tokens));
+                }
+                const int cnt = min(NB, p - p0);
+                if (local) add_tiles<NB, 0>(acc, slots, scale, cnt, wave, l);
+                else add_tiles<NB, kSc1>(acc, slots, scale, cnt, wave, l);
+            }
+        };
+
+        // ================= round 1: S0 of every chunk -> LDS ========================
+        {
+            f32x4 s0seg[2];
+            carry_tiles(s0seg, a.aggS, 0, 1);
+#pragma unroll
+            for (int c = 0; c < kFMaxL; ++c) {
+                if (c < Lseg) {
+                    const float d1 = gp(static_cast<float>(W * c));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        bf16x4 h, lo;
+                        split4(d1 * s0seg[i] + spre[c][i], h, lo);
+                        // lane holds S0[a = 16tb+4g+e][b = 16(cb+i)+r]; tile rows b
+                        st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                        st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // S0 and value tiles ready
+
+        // ================= U and Us of both slice chunks ============================
+        f32x4 usv[2][4];  // Us^T[b = 16bb+4g+e][t]
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 2 * grp + jj, Lc = lc_of[jj];
+            if (Lc > 0) {
+                const float e = gp(static_cast<float>(t + 1));
+                const float f2 = t < Lc ? gp(static_cast<float>(2 * (Lc - 1 - t))) : 0.0f;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    f32x4 acc = zero4;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        acc = mfma(ld8(sm.T[8 + 2 * c], 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
+                        acc = mfma(ld8(sm.T[9 + 2 * c], 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
+                    }
+                    usv[jj][bb] = f2 * (e * acc + uloc[jj][bb]);
+                }
+            }
+        }
+        __syncthreads();  // S0 reads done: their tiles take Us
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 2 * grp + jj;
+            if (lc_of[jj] > 0) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    bf16x4 h, mid, lo;
+                    split3(usv[jj][bb], h, mid, lo);
+                    st4(sm.T[8 + 2 * c], t, 16 * bb + 4 * g, h);
+                    st4(sm.T[9 + 2 * c], t, 16 * bb + 4 * g, mid);
+                    st4(sm.T[c], t, 16 * bb + 4 * g, lo);
+                }
+            }
+        }
+        __syncthreads();  // every Us row ready
+
+        // ================= Z_seg (tiles): the segment's X increment ================
+        // xpre[c] = increment of chunks 0..c-1 at chunk c's start; xrun ends as Z.
+        // Tile X^T (j = 16tb+4g+e, a = 16(cb+i)+r) = sum_s V[s][j] Us[s][a].
+        f32x4 xpre[kFMaxL][2], xrun[2] = {zero4, zero4};
+#pragma unroll
+        for (int c = 0; c < kFMaxL; ++c) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xpre[c][i] = xrun[i];
+            if (c < Lseg) {
+                const float rho2 = gp(static_cast<float>(2 * chunk_len(c)));
+#pragma unroll
+                for (int i = 0; i < 2; ++i) xrun[i] *= rho2;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        xrun[i] = mfma(vt, tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
+                        xrun[i] = mfma(vt, tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
+                    }
+                }
+            }
+        }
+        if (publish) {
+            put_tiles(a.aggX + slot * 4096, wave, l, xrun, local);
+            wait_stores();
+            if (l == 0) set_flag(flag_of(slot, 1), epoch, local);
+        }
+
+        // ================= P and the local numerator (slices) ======================
+        // P^T[s][t] = (Us_s . q_t) / f_t^2 for s <= t;  num^T[j][t] = sum_s V[s][j] P[t][s]
+        f32x4 num[2][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 2 * grp + jj, Lc = lc_of[jj];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) num[jj][jb] = zero4;
+            if (Lc > 0) {
+                const float inv_f2 = t < Lc ? gp(static_cast<float>(-2 * (Lc - 1 - t))) : 0.0f;
+                f32x4 pt[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    pt[sb] = zero4;
+                    if (sb <= w) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            pt[sb] = mfma(ld8(sm.T[8 + 2 * c], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                            pt[sb] = mfma(ld8(sm.T[9 + 2 * c], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                            pt[sb] = mfma(ld8(sm.T[c], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pt[sb][e] = 16 * sb + 4 * g + e <= t ? inv_f2 * pt[sb][e] : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (2 * ks <= w) {
+                        bf16x8 ph, pl;
+                        pair_operand(pt[2 * ks], pt[2 * ks + 1], ph, pl);
+#pragma unroll
+                        for (int jb = 0; jb < 4; ++jb) {
+                            const bf16x8 vt = tr8(sm.T[4 + c], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                            num[jj][jb] = mfma(vt, ph, num[jj][jb]);
+                            num[jj][jb] = mfma(vt, pl, num[jj][jb]);
+                        }
+                    }
+                }
+            }
+        }
+
+        // ================= round 2: X0 of every chunk -> LDS ========================
+        f32x4 x0seg[2];
+        carry_tiles(x0seg, a.aggX, 1, 2);
+        __syncthreads();  // every Us read done: the tiles take X0
+#pragma unroll
+        for (int c = 0; c < kFMaxL; ++c) {
+            if (c < Lseg) {
+                const float d2 = gp(static_cast<float>(2 * W * c));
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    bf16x4 h, lo;
+                    split4(d2 * x0seg[i] + xpre[c][i], h, lo);
+                    // lane holds X0^T[j = 16tb+4g+e][a = 16(cb+i)+r]; tile rows a
+                    st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                    st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= output: num + e^2 q_t^T X0 =============================
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 2 * grp + jj, Lc = lc_of[jj];
+            if (Lc > 0) {
+                const float e = gp(static_cast<float>(t + 1));
+                const float e2 = e * e;
+                f32x4 acc[4];
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) {
+                        acc[jb] = mfma(tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                        acc[jb] = mfma(tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                    }
+                }
+                if (t < Lc) {
+                    float *orow = a.out + ((static_cast<size_t>(bh) * a.n) + static_cast<size_t>(c0 + c) * W + t) * W;
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) {
+                        const f32x4 o = num[jj][jb] + e2 * acc[jb];
+                        *reinterpret_cast<float4 *>(orow + 16 * jb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // this segment's LDS reads are done before the next one is staged
+    };
+    // A loop around the body costs registers even when it runs once, so the
+    // one-segment launch calls the body straight.
+    if constexpr (LOOP) {
+        for (int seg = static_cast<int>(blockIdx.x); seg < a.segs; seg += static_cast<int>(gridDim.x)) seg_body(seg);
+    } else {
+        seg_body(static_cast<int>(blockIdx.x));
+    }
+
+    // ---- the last workgroup to finish resets the counter and advances the epoch
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct FastLayout {
+    size_t flags, aggS, aggX, total;
+};
+
+FastLayout fast_layout(int BH, int P) {
+    FastLayout L{};
+    const size_t slots = static_cast<size_t>(BH) * P;
+    L.flags = 0;
+    L.aggS = L.flags + align256(slots * 2 * kWaves * kFlagStride * sizeof(uint32_t));
+    L.aggX = L.aggS + slots * 4096 * sizeof(float);
+    L.total = L.aggX + slots * 4096 * sizeof(float);
+    return L;
+}
+
+void fast64_geometry(int BH, int nc, int *P, int *L) {
+    // about one workgroup per CU; at most four chunks per workgroup
+    const int target = (256 + BH - 1) / BH;
+    int l = (nc + target - 1) / target;
+    l = l < 1 ? 1 : (l > kFMaxL ? kFMaxL : l);
+    *L = l;
+    *P = (nc + l - 1) / l;
+}
+
+}  // namespace
+
+bool fast64_supported(const FwdProblem &p) {
+    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.init.S == nullptr &&
+          p.fin.S == nullptr && p.n > 0 && p.ridge == 0.0f && p.den == nullptr && !p.normalize))
+        return false;
+    const int nh = p.gam.per_head ? p.H : 1;
+    for (int h = 0; h < nh; ++h)
+        if (p.gam.g[h] < kMinGamma) return false;
+    return true;
+}
+
+size_t fast64_workspace_bytes(int BH, int n) {
+    const int nc = (n + W - 1) / W;
+    int P, L;
+    fast64_geometry(BH, nc, &P, &L);
+    return fast_layout(BH, P).total;
+}
+
+hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+    FastArgs a{};
+    a.H = p.H; a.n = p.n; a.nc = p.nc; a.BH = p.B * p.H;
+    fast64_geometry(a.BH, a.nc, &a.P, &a.L);
+    a.segs = a.BH * a.P;
+    a.q = static_cast<const uint16_t *>(p.q);
+    a.k = static_cast<const uint16_t *>(p.k);
+    a.v = static_cast<const uint16_t *>(p.v);
+    a.out = p.out;
+    a.ctrl = ctrl;
+    const FastLayout L = fast_layout(a.BH, a.P);
+    char *base = static_cast<char *>(data);
+    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    a.aggS = reinterpret_cast<float *>(base + L.aggS);
+    a.aggX = reinterpret_cast<float *>(base + L.aggX);
+    a.gam = p.gam;
+    const int nh = p.gam.per_head ? p.H : 1;
+    bool decay = false;
+    for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
+    // one workgroup per CU at most (its LDS fills the CU), so the whole grid is resident
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const bool loop = a.segs > cus;
+    const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs)), block(kFThreads);
+    if (decay) {
+        if (loop) hipLaunchKernelGGL((k_fast64<true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<true, false>), grid, block, 0, st, a);
+    } else {
+        if (loop) hipLaunchKernelGGL((k_fast64<false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<false, false>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hla
