@@ -13,21 +13,22 @@
 //
 // Division of work.  A workgroup (eight waves) owns a segment of up to four
 // consecutive chunks of one head.  Two roles per wave:
-//  * slice role: wave v works on a 16-token slice of two chunks (waves 0-3
-//    chunks 0, 1; waves 4-7 chunks 2, 3, slices in reverse order so that each
-//    SIMD pairs a light and a heavy slice of the triangular products): the
-//    scores, U, P, the local numerator and the output;
+//  * slice role: wave v works on 32 tokens (two 16-token blocks) of chunk
+//    v/2, so every operand it reads from LDS serves both blocks; the two
+//    waves of a SIMD (v, v+4) take opposite halves of their chunks, pairing a
+//    light and a heavy share of the triangular products: the scores, U, P,
+//    the local numerator and the output;
 //  * tile role: wave v owns tiles 2v, 2v+1 of a 64 x 64 moment (row block
 //    v/2, column blocks 2(v%2), 2(v%2)+1), summed over every chunk of the
 //    segment: the key moment S, the X increment, and the carries built from
 //    the aggregates other segments publish.  No partial sums are exchanged
 //    between waves, and wave v of a segment reads only what wave v of its
 //    predecessors wrote, so every wave publishes and waits on its own flags.
-// Order per segment (LDS holds sixteen 64 x 72 bf16 tiles T):
+// Order per segment (LDS holds sixteen 64 x 64 bf16 tiles T):
 //   stage K_c -> T[c]; S_seg by tiles; publish S
 //   carry-free A^T and Uloc^T = K^T A^T by slices; stage V_c -> T[4+c]
 //   round 1: S0 of every chunk -> T[8+2c] (hi), T[9+2c] (lo)
-//   U, Us of both slice chunks -> Us hi, mid in T[8+2c], T[9+2c], lo in T[c]
+//   U, Us of every chunk -> Us hi, mid in T[8+2c], T[9+2c], lo in T[c]
 //   Z_seg = sum_c decayed V_c^T Us_c by tiles; publish Z
 //   P and the local numerator by slices, while round 2 travels
 //   round 2: X0 of every chunk -> T[8+2c], T[9+2c]; out = num + e^2 Q X0
@@ -41,6 +42,11 @@
 
 namespace hla {
 namespace {
+
+template <int V>
+struct IC {  // an int as a type, to instantiate a lambda for each half
+    static constexpr int value = V;
+};
 
 constexpr int kFThreads = 512;
 constexpr int kFMaxL = 4;   // chunks per segment
@@ -57,7 +63,7 @@ struct FastArgs {
 };
 
 struct FastSmem {
-    __bf16 T[16][W * LDR];
+    __bf16 T[16][kTile];
     uint32_t epoch;
 };
 
@@ -117,9 +123,11 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         int tid_l = static_cast<int>(threadIdx.x);
         if constexpr (LOOP) asm volatile("" : "+v"(tid_l));
         const int wave = tid_l >> 6, l = tid_l & 63, r = l & 15, g = l >> 4;
-        const int grp = wave >> 2, wv = wave & 3, wt = tid_l & 255;
-        const int w = grp == 0 ? wv : 3 - wv;  // slice role: tokens 16w.. of chunks 2grp, 2grp+1
-        const int t = 16 * w + r;              // this lane's token
+        const int grp = wave >> 2, wt = tid_l & 255;  // staging: group grp stages chunks 2grp, 2grp+1
+        // slice role: chunk sc, token blocks 2hh and 2hh+1 (the two waves of a
+        // SIMD take opposite halves of the triangular work)
+        const int sc = wave >> 1, hh = (wave ^ (wave >> 2)) & 1;
+        const int t0 = 32 * hh + r;  // this lane's token in block 2hh; t0 + 16 in block 2hh+1
         const int tb = wave >> 1, cb = 2 * (wave & 1);  // tile role: row block, first column block
 
         // ---- global loads of the slice chunks: keys and queries now, values
@@ -146,16 +154,20 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                     kx[jj][u] = *reinterpret_cast<const u32x4 *>(a.k + src * W + cg * 8);
                 }
             }
+            {
+                const int bh_ = sg_ % a.BH, p_ = sg_ / a.BH;
+                const size_t head_ = static_cast<size_t>(bh_) * a.n;
+                const int c0_ = p_ * a.L, Lseg_ = min(a.L, a.nc - c0_);
+                const int Lc_ = sc < Lseg_ ? min(W, a.n - (c0_ + sc) * W) : 0;
+                const size_t tok0_ = head_ + static_cast<size_t>(c0_ + sc) * W;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                int Lc_;
-                size_t tok0_, head_;
-                chunk_rows(sg_, jj, Lc_, tok0_, head_);
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const size_t src = t < Lc_ ? tok0_ + t : head_;
-                    qx[jj][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
-                }
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const int tt = t0 + 16 * i;
+                        const size_t src = tt < Lc_ ? tok0_ + tt : head_;
+                        qx[i][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
+                    }
             }
         };
         auto issue_v = [&](int sg_) __attribute__((always_inline)) {
@@ -182,9 +194,15 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         const int c0 = p * a.L;
         const int Lseg = min(a.L, a.nc - c0);  // chunks in this segment (1..4)
         auto chunk_len = [&](int j) { return min(W, a.n - (c0 + j) * W); };
-        int lc_of[2];  // tokens in slice chunk jj (0 if none)
+        int lc_of[2];  // tokens in staged chunk 2grp+jj (0 if none)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) lc_of[jj] = 2 * grp + jj < Lseg ? chunk_len(2 * grp + jj) : 0;
+        const int Lcs = sc < Lseg ? chunk_len(sc) : 0;  // tokens in the slice chunk (0 if none)
+        int lcc[kFMaxL];  // tokens per chunk of the segment, 0 past its end (absent
+                          // chunks have zero key, value and Us tiles, so the tile
+                          // sums below need no branch on them)
+#pragma unroll
+        for (int c = 0; c < kFMaxL; ++c) lcc[c] = c < Lseg ? chunk_len(c) : 0;
         const size_t slot = static_cast<size_t>(bh) * a.P + p;
         const bool publish = p + 1 < a.P;  // the last segment of a head has no readers
 
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
-                *reinterpret_cast<u32x4 *>(&sm.T[2 * grp + jj][row * LDR + cg * 8]) = row < lc_of[jj] ? kx[jj][u] : z4;
+                st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
             }
         if (tid == 0 && first) sm.epoch = ep_raw;
         __syncthreads();
@@ -213,39 +231,37 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         for (int c = 0; c < kFMaxL; ++c) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) spre[c][i] = srun[i];
-            if (c < Lseg) {
-                const int Lc = chunk_len(c);
-                f32x4 acc[2] = {zero4, zero4};
+            const int Lc = lcc[c];
+            f32x4 acc[2] = {zero4, zero4};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int rb = 32 * ks + 8 * g;
-                    const bf16x8 ka = tr8(sm.T[c], rb, rb + 4, 16 * tb, r);
-                    bf16x8 kb[2];
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rb = 32 * ks + 8 * g;
+                const bf16x8 ka = tr8(sm.T[c], rb, rb + 4, 16 * tb, r);
+                bf16x8 kb[2];
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) kb[i] = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
-                    if (!DECAY) {
+                for (int i = 0; i < 2; ++i) kb[i] = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
+                if (!DECAY) {
 #pragma unroll
-                        for (int i = 0; i < 2; ++i) acc[i] = mfma(ka, kb[i], acc[i]);
-                    } else {
-                        f32x4 x0, x1;
+                    for (int i = 0; i < 2; ++i) acc[i] = mfma(ka, kb[i], acc[i]);
+                } else {
+                    f32x4 x0, x1;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            x0[e] = gp(static_cast<float>(Lc - 1 - (rb + e))) * static_cast<float>(ka[e]);
-                            x1[e] = gp(static_cast<float>(Lc - 1 - (rb + 4 + e))) * static_cast<float>(ka[4 + e]);
-                        }
-                        bf16x8 h, lo;
-                        pair_operand(x0, x1, h, lo);
+                    for (int e = 0; e < 4; ++e) {
+                        x0[e] = gp(static_cast<float>(Lc - 1 - (rb + e))) * static_cast<float>(ka[e]);
+                        x1[e] = gp(static_cast<float>(Lc - 1 - (rb + 4 + e))) * static_cast<float>(ka[4 + e]);
+                    }
+                    bf16x8 h, lo;
+                    pair_operand(x0, x1, h, lo);
 #pragma unroll
-                        for (int i = 0; i < 2; ++i) {
-                            acc[i] = mfma(h, kb[i], acc[i]);
-                            acc[i] = mfma(lo, kb[i], acc[i]);
-                        }
+                    for (int i = 0; i < 2; ++i) {
+                        acc[i] = mfma(h, kb[i], acc[i]);
+                        acc[i] = mfma(lo, kb[i], acc[i]);
                     }
                 }
-                const float rho = gp(static_cast<float>(Lc));
-#pragma unroll
-                for (int i = 0; i < 2; ++i) srun[i] = rho * srun[i] + acc[i];
             }
+            const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) srun[i] = rho * srun[i] + acc[i];
         }
         // the exchange goes through the XCD's L2 when every workgroup holding
         // a segment of this head runs on this XCD (every wave decides alike)
@@ -258,49 +274,67 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         }
         issue_v(seg);
 
-        bf16x8 qn[2][2];  // q of token t, features 32ks+8g..: B operand
+        bf16x8 qn[2][2];  // q of token t0 + 16i, features 32ks+8g..: B operand
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) qn[jj][ks] = __builtin_bit_cast(bf16x8, t < lc_of[jj] ? qx[jj][ks] : z4);
+            for (int ks = 0; ks < 2; ++ks) qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
 
         // ================= carry-free slice work ====================================
-        // A^T tiles of this slice, then Uloc^T = K^T A^T (rows b, cols t)
+        // A^T tiles (rows s, cols t) of both token blocks, then Uloc^T = K^T A^T
+        // (rows b, cols t).  Block i (tokens 16(2hh+i)..) needs s-blocks <= 2hh+i;
+        // operands read from LDS serve both blocks.
         f32x4 uloc[2][4];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = 2 * grp + jj;
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) uloc[jj][bb] = zero4;
-            if (lc_of[jj] > 0) {
-                f32x4 at[4];  // A^T[i = 16ib+4g+e][t], masked and decayed
+            for (int bb = 0; bb < 4; ++bb) uloc[i][bb] = zero4;
+        auto carry_free = [&](auto hc) __attribute__((always_inline)) {
+            constexpr int HH = decltype(hc)::value;
+            f32x4 at[2][4];
 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    at[ib] = zero4;
-                    if (ib <= w) {
+            for (int ib = 0; ib < 4; ++ib) {
+                at[0][ib] = at[1][ib] = zero4;
+                if (ib <= 2 * HH + 1) {
+                    const bf16x8 k0 = ld8(sm.T[sc], 16 * ib + r, 8 * g), k1 = ld8(sm.T[sc], 16 * ib + r, 32 + 8 * g);
 #pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) at[ib] = mfma(ld8(sm.T[c], 16 * ib + r, 32 * ks + 8 * g), qn[jj][ks], at[ib]);
+                    for (int i = 0; i < 2; ++i) {
+                        if (ib <= 2 * HH + i) {
+                            at[i][ib] = mfma(k1, qn[i][1], mfma(k0, qn[i][0], zero4));
+                            const int tt = 32 * HH + 16 * i + r;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int i = 16 * ib + 4 * g + e;
-                            at[ib][e] = i <= t ? gp(static_cast<float>(t - i)) * at[ib][e] : 0.0f;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (2 * ks <= w) {
-                        bf16x8 ah, al;
-                        pair_operand(at[2 * ks], at[2 * ks + 1], ah, al);
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb) {
-                            const bf16x8 kt = tr8(sm.T[c], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * bb, r);
-                            uloc[jj][bb] = mfma(kt, ah, uloc[jj][bb]);
-                            uloc[jj][bb] = mfma(kt, al, uloc[jj][bb]);
+                            for (int e = 0; e < 4; ++e) {
+                                const int si = 16 * ib + 4 * g + e;
+                                at[i][ib][e] = si <= tt ? gp(static_cast<float>(tt - si)) * at[i][ib][e] : 0.0f;
+                            }
                         }
                     }
                 }
             }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks <= 2 * HH + 1) {
+                    bf16x8 kt[4];
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) kt[bb] = tr8(sm.T[sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * bb, r);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        if (2 * ks <= 2 * HH + i) {
+                            bf16x8 ah, al;
+                            pair_operand(at[i][2 * ks], at[i][2 * ks + 1], ah, al);
+#pragma unroll
+                            for (int bb = 0; bb < 4; ++bb) {
+                                uloc[i][bb] = mfma(kt[bb], ah, uloc[i][bb]);
+                                uloc[i][bb] = mfma(kt[bb], al, uloc[i][bb]);
+                            }
+                        }
+                    }
+                }
+            }
+        };
+        if (Lcs > 0) {
+            if (hh) carry_free(IC<1>{});
+            else carry_free(IC<0>{});
         }
         // ---- value rows (read after the next barrier)
 #pragma unroll
@@ -308,7 +342,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
-                *reinterpret_cast<u32x4 *>(&sm.T[4 + 2 * grp + jj][row * LDR + cg * 8]) = row < lc_of[jj] ? vx[jj][u] : z4;
+                st16(sm.T[4 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
             }
 
         // ---- carry = sum over earlier segments pp of g^(pw * gap) * (wave's
@@ -356,40 +390,54 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         }
         __syncthreads();  // S0 and value tiles ready
 
-        // ================= U and Us of both slice chunks ============================
-        f32x4 usv[2][4];  // Us^T[b = 16bb+4g+e][t]
+        // ================= U and Us of the slice ===================================
+        f32x4 usv[2][4];  // Us^T[b = 16bb+4g+e][t0 + 16i]
+        if (Lcs > 0) {
+            f32x4 acc[2][4];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = 2 * grp + jj, Lc = lc_of[jj];
-            if (Lc > 0) {
-                const float e = gp(static_cast<float>(t + 1));
-                const float f2 = t < Lc ? gp(static_cast<float>(2 * (Lc - 1 - t))) : 0.0f;
+            for (int bb = 0; bb < 4; ++bb) {
+                acc[0][bb] = acc[1][bb] = zero4;
 #pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    f32x4 acc = zero4;
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 sh = ld8(sm.T[8 + 2 * sc], 16 * bb + r, 32 * ks + 8 * g);
+                    const bf16x8 sl = ld8(sm.T[9 + 2 * sc], 16 * bb + r, 32 * ks + 8 * g);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        acc = mfma(ld8(sm.T[8 + 2 * c], 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
-                        acc = mfma(ld8(sm.T[9 + 2 * c], 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
+                    for (int i = 0; i < 2; ++i) {
+                        acc[i][bb] = mfma(sh, qn[i][ks], acc[i][bb]);
+                        acc[i][bb] = mfma(sl, qn[i][ks], acc[i][bb]);
                     }
-                    usv[jj][bb] = f2 * (e * acc + uloc[jj][bb]);
                 }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = t0 + 16 * i;
+                const float e = gp(static_cast<float>(tt + 1));
+                const float f2 = tt < Lcs ? gp(static_cast<float>(2 * (Lcs - 1 - tt))) : 0.0f;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) usv[i][bb] = f2 * (e * acc[i][bb] + uloc[i][bb]);
             }
         }
         __syncthreads();  // S0 reads done: their tiles take Us
+        if (Lcs > 0) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = 2 * grp + jj;
-            if (lc_of[jj] > 0) {
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
                     bf16x4 h, mid, lo;
-                    split3(usv[jj][bb], h, mid, lo);
-                    st4(sm.T[8 + 2 * c], t, 16 * bb + 4 * g, h);
-                    st4(sm.T[9 + 2 * c], t, 16 * bb + 4 * g, mid);
-                    st4(sm.T[c], t, 16 * bb + 4 * g, lo);
+                    split3(usv[i][bb], h, mid, lo);
+                    st4(sm.T[8 + 2 * sc], t0 + 16 * i, 16 * bb + 4 * g, h);
+                    st4(sm.T[9 + 2 * sc], t0 + 16 * i, 16 * bb + 4 * g, mid);
+                    st4(sm.T[sc], t0 + 16 * i, 16 * bb + 4 * g, lo);
                 }
-            }
+        } else {  // an absent chunk: zero Us hi, mid (its value tile is zero too)
+            const bf16x4 z = __builtin_bit_cast(bf16x4, uint64_t{0});
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    st4(sm.T[8 + 2 * sc], t0 + 16 * i, 16 * bb + 4 * g, z);
+                    st4(sm.T[9 + 2 * sc], t0 + 16 * i, 16 * bb + 4 * g, z);
+                }
         }
         __syncthreads();  // every Us row ready
 
@@ -401,19 +449,17 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         for (int c = 0; c < kFMaxL; ++c) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) xpre[c][i] = xrun[i];
-            if (c < Lseg) {
-                const float rho2 = gp(static_cast<float>(2 * chunk_len(c)));
+            const float rho2 = gp(static_cast<float>(2 * lcc[c]));
 #pragma unroll
-                for (int i = 0; i < 2; ++i) xrun[i] *= rho2;
+            for (int i = 0; i < 2; ++i) xrun[i] *= rho2;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int rb = 32 * ks + 8 * g;
-                    const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rb = 32 * ks + 8 * g;
+                const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        xrun[i] = mfma(vt, tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
-                        xrun[i] = mfma(vt, tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
-                    }
+                for (int i = 0; i < 2; ++i) {
+                    xrun[i] = mfma(vt, tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
+                    xrun[i] = mfma(vt, tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
                 }
             }
         }
@@ -423,45 +469,69 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             if (l == 0) set_flag(flag_of(slot, 1), epoch, local);
         }
 
-        // ================= P and the local numerator (slices) ======================
+        // ================= P and the local numerator (slice) ======================
         // P^T[s][t] = (Us_s . q_t) / f_t^2 for s <= t;  num^T[j][t] = sum_s V[s][j] P[t][s]
         f32x4 num[2][4];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = 2 * grp + jj, Lc = lc_of[jj];
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) num[jj][jb] = zero4;
-            if (Lc > 0) {
-                const float inv_f2 = t < Lc ? gp(static_cast<float>(-2 * (Lc - 1 - t))) : 0.0f;
-                f32x4 pt[4];
+            for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
+        auto p_num = [&](auto hc) __attribute__((always_inline)) {
+            constexpr int HH = decltype(hc)::value;
+            f32x4 pt[2][4];
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    pt[sb] = zero4;
-                    if (sb <= w) {
+            for (int sb = 0; sb < 4; ++sb) {
+                pt[0][sb] = pt[1][sb] = zero4;
+                if (sb <= 2 * HH + 1) {
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) {
-                            pt[sb] = mfma(ld8(sm.T[8 + 2 * c], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                            pt[sb] = mfma(ld8(sm.T[9 + 2 * c], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                            pt[sb] = mfma(ld8(sm.T[c], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                        }
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const bf16x8 u1 = ld8(sm.T[8 + 2 * sc], 16 * sb + r, 32 * kb + 8 * g);
+                        const bf16x8 u2 = ld8(sm.T[9 + 2 * sc], 16 * sb + r, 32 * kb + 8 * g);
+                        const bf16x8 u3 = ld8(sm.T[sc], 16 * sb + r, 32 * kb + 8 * g);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pt[sb][e] = 16 * sb + 4 * g + e <= t ? inv_f2 * pt[sb][e] : 0.0f;
-                    }
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (2 * ks <= w) {
-                        bf16x8 ph, pl;
-                        pair_operand(pt[2 * ks], pt[2 * ks + 1], ph, pl);
-#pragma unroll
-                        for (int jb = 0; jb < 4; ++jb) {
-                            const bf16x8 vt = tr8(sm.T[4 + c], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
-                            num[jj][jb] = mfma(vt, ph, num[jj][jb]);
-                            num[jj][jb] = mfma(vt, pl, num[jj][jb]);
+                        for (int i = 0; i < 2; ++i) {
+                            if (sb <= 2 * HH + i) {
+                                pt[i][sb] = mfma(u1, qn[i][kb], pt[i][sb]);
+                                pt[i][sb] = mfma(u2, qn[i][kb], pt[i][sb]);
+                                pt[i][sb] = mfma(u3, qn[i][kb], pt[i][sb]);
+                            }
                         }
                     }
                 }
             }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = 32 * HH + 16 * i + r;
+                const float inv_f2 = tt < Lcs ? gp(static_cast<float>(-2 * (Lcs - 1 - tt))) : 0.0f;
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pt[i][sb][e] = 16 * sb + 4 * g + e <= tt ? inv_f2 * pt[i][sb][e] : 0.0f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks <= 2 * HH + 1) {
+                    bf16x8 vt[4];
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        if (2 * ks <= 2 * HH + i) {
+                            bf16x8 ph, pl;
+                            pair_operand(pt[i][2 * ks], pt[i][2 * ks + 1], ph, pl);
+#pragma unroll
+                            for (int jb = 0; jb < 4; ++jb) {
+                                num[i][jb] = mfma(vt[jb], ph, num[i][jb]);
+                                num[i][jb] = mfma(vt[jb], pl, num[i][jb]);
+                            }
+                        }
+                    }
+                }
+            }
+        };
+        if (Lcs > 0) {
+            if (hh) p_num(IC<1>{});
+            else p_num(IC<0>{});
         }
 
         // ================= round 2: X0 of every chunk -> LDS ========================
@@ -485,29 +555,33 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         __syncthreads();
 
         // ================= output: num + e^2 q_t^T X0 =============================
+        if (Lcs > 0) {
+            f32x4 acc[2][4];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = 2 * grp + jj, Lc = lc_of[jj];
-            if (Lc > 0) {
-                const float e = gp(static_cast<float>(t + 1));
-                const float e2 = e * e;
-                f32x4 acc[4];
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4;
+            for (int jb = 0; jb < 4; ++jb) {
+                acc[0][jb] = acc[1][jb] = zero4;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int rb = 32 * ks + 8 * g;
+                    const bf16x8 xh = tr8(sm.T[8 + 2 * sc], rb, rb + 4, 16 * jb, r);
+                    const bf16x8 xl = tr8(sm.T[9 + 2 * sc], rb, rb + 4, 16 * jb, r);
 #pragma unroll
-                    for (int jb = 0; jb < 4; ++jb) {
-                        acc[jb] = mfma(tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
-                        acc[jb] = mfma(tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                    for (int i = 0; i < 2; ++i) {
+                        acc[i][jb] = mfma(xh, qn[i][ks], acc[i][jb]);
+                        acc[i][jb] = mfma(xl, qn[i][ks], acc[i][jb]);
                     }
                 }
-                if (t < Lc) {
-                    float *orow = a.out + ((static_cast<size_t>(bh) * a.n) + static_cast<size_t>(c0 + c) * W + t) * W;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = t0 + 16 * i;
+                if (tt < Lcs) {
+                    const float e = gp(static_cast<float>(tt + 1));
+                    const float e2 = e * e;
+                    float *orow = a.out + ((static_cast<size_t>(bh) * a.n) + static_cast<size_t>(c0 + sc) * W + tt) * W;
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
-                        const f32x4 o = num[jj][jb] + e2 * acc[jb];
+                        const f32x4 o = num[i][jb] + e2 * acc[i][jb];
                         *reinterpret_cast<float4 *>(orow + 16 * jb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
                     }
                 }

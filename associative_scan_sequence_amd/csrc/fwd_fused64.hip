@@ -133,14 +133,14 @@ __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&
         }
 }
 
-// LDS of one wave group: 8 padded 64 x 64 bf16 tiles (72 KB).
+// LDS of one wave group: 8 swizzled 64 x 64 bf16 tiles (64 KB).
 struct GroupLds {
-    __bf16 K[kPerGroup][W * LDR];  // key rows [s][a] of the group's chunks
-    __bf16 V[kPerGroup][W * LDR];  // value rows [s][j]
-    __bf16 Uh[W * LDR];            // Us rows [s][b], hi and lo
-    __bf16 Ul[W * LDR];
-    __bf16 Sh[W * LDR];            // S0 (symmetric) of the chunk; in phase C X0 as [a][j]
-    __bf16 Sl[W * LDR];
+    __bf16 K[kPerGroup][kTile];  // key rows [s][a] of the group's chunks
+    __bf16 V[kPerGroup][kTile];  // value rows [s][j]
+    __bf16 Uh[kTile];            // Us rows [s][b], hi and lo
+    __bf16 Ul[kTile];
+    __bf16 Sh[kTile];            // S0 (symmetric) of the chunk; in phase C X0 as [a][j]
+    __bf16 Sl[kTile];
 };
 
 struct Smem {
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-                *reinterpret_cast<u32x4 *>(&G.K[jj][row * LDR + cg * 8]) = row < lc_of[jj] ? kx[jj][u] : z4;
+                st16(G.K[jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
             }
         __syncthreads();
         // ---- wave 0 fetches the XCD entries of the workgroups that hold this
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-                *reinterpret_cast<u32x4 *>(&G.V[jj][row * LDR + cg * 8]) = row < lc_of[jj] ? vx[jj][u] : z4;
+                st16(G.V[jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
             }
         // ---- round 1: the S carry at this group's first chunk
         wait_round(0);
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             for (int jj = 0; jj < kPerGroup; ++jj)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    *reinterpret_cast<bf16x8 *>(&G.K[jj][t * LDR + 32 * ks + 8 * g]) = qn[jj][ks];
+                    st16(G.K[jj], t, 32 * ks + 8 * g, __builtin_bit_cast(u32x4, qn[jj][ks]));
         }
         if (DEN && wt < 64) {
 #pragma unroll

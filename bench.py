@@ -51,20 +51,29 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fused64_B4_H8_n2048_d64_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "associative_scan_sequence_amd", "csrc", "fwd_fused64.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fast64_B4_H8_n2048_d64_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "associative_scan_sequence_amd", "csrc", f)
+                  for f in ("fwd_fast64.hip", "fused64_common.h")]
+
+
+def kernel_source_hash():
+    """sha256 over the headline kernel's sources, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the d=64 kernel from the committed counter
     summary, or None when the kernel source changed since it was taken."""
-    import hashlib
     import re
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
         return None
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    src = kernel_source_hash()
     m_hash = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
     m_bytes = re.search(r"HBM bytes per launch: ([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != src:
@@ -326,7 +335,7 @@ def main():
                    "input_copies_rotated": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "k_fused64 (the whole hla_forward_chunked call is one launch)",
+                     "kernel": "k_fast64 (the whole hla_forward_chunked call is one launch)",
                      "algorithmic_bytes_per_step": alg},
         "eager_ms_per_step": eager_ms,
         "parity_guard_row_error": err,
