@@ -63,7 +63,7 @@ struct FastArgs {
 };
 
 struct FastSmem {
-    __bf16 T[16][kTile];
+    __bf16 T[16][kTileElems<kSwizzled>];
     uint32_t epoch;
 };
 
@@ -582,7 +582,8 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
                         const f32x4 o = num[i][jb] + e2 * acc[i][jb];
-                        *reinterpret_cast<float4 *>(orow + 16 * jb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+                        // streamed past the caches: nothing is left to write back when the kernel ends
+                        __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(orow + 16 * jb + 4 * g));
                     }
                 }
             }

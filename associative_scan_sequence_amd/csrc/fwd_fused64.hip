@@ -78,6 +78,7 @@
 namespace hla {
 namespace {
 
+constexpr int kLay = kPadded;  // LDS tile layout (this kernel is short of registers)
 constexpr int kThreads = 512;  // two groups of four waves
 constexpr int kPerGroup = 2;   // chunks per wave group
 constexpr int kMaxL = 4;       // chunks per workgroup
@@ -133,14 +134,14 @@ __device__ __forceinline__ void add_slots(f32x4 (&acc)[4], const float *const (&
         }
 }
 
-// LDS of one wave group: 8 swizzled 64 x 64 bf16 tiles (64 KB).
+// LDS of one wave group: 8 padded 64 x 64 bf16 tiles (72 KB).
 struct GroupLds {
-    __bf16 K[kPerGroup][kTile];  // key rows [s][a] of the group's chunks
-    __bf16 V[kPerGroup][kTile];  // value rows [s][j]
-    __bf16 Uh[kTile];            // Us rows [s][b], hi and lo
-    __bf16 Ul[kTile];
-    __bf16 Sh[kTile];            // S0 (symmetric) of the chunk; in phase C X0 as [a][j]
-    __bf16 Sl[kTile];
+    __bf16 K[kPerGroup][kTileElems<kLay>];  // key rows [s][a] of the group's chunks
+    __bf16 V[kPerGroup][kTileElems<kLay>];  // value rows [s][j]
+    __bf16 Uh[kTileElems<kLay>];            // Us rows [s][b], hi and lo
+    __bf16 Ul[kTileElems<kLay>];
+    __bf16 Sh[kTileElems<kLay>];            // S0 (symmetric) of the chunk; in phase C X0 as [a][j]
+    __bf16 Sl[kTileElems<kLay>];
 };
 
 struct Smem {
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-                st16(G.K[jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
+                st16<kLay>(G.K[jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
             }
         __syncthreads();
         // ---- wave 0 fetches the XCD entries of the workgroups that hold this
@@ -289,10 +290,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
     #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int rb = 32 * ks + 8 * g;
-                    const bf16x8 ka = tr8(G.K[jj], rb, rb + 4, 16 * w, r);
+                    const bf16x8 ka = tr8<kLay>(G.K[jj], rb, rb + 4, 16 * w, r);
                     bf16x8 kb[4];
     #pragma unroll
-                    for (int bb = 0; bb < 4; ++bb) kb[bb] = tr8(G.K[jj], rb, rb + 4, 16 * bb, r);
+                    for (int bb = 0; bb < 4; ++bb) kb[bb] = tr8<kLay>(G.K[jj], rb, rb + 4, 16 * bb, r);
                     if (!DECAY) {
     #pragma unroll
                         for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma(ka, kb[bb], acc[bb]);
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     at[ib] = zero4;
                     if (ib <= w) {
 #pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) at[ib] = mfma(ld8(G.K[jj], 16 * ib + r, 32 * ks + 8 * g), qn[jj][ks], at[ib]);
+                        for (int ks = 0; ks < 2; ++ks) at[ib] = mfma(ld8<kLay>(G.K[jj], 16 * ib + r, 32 * ks + 8 * g), qn[jj][ks], at[ib]);
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
                             const int i = 16 * ib + 4 * g + c;
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                         pair_operand(at[2 * ks], at[2 * ks + 1], ah, al);
 #pragma unroll
                         for (int bb = 0; bb < 4; ++bb) {
-                            const bf16x8 kt = tr8(G.K[jj], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * bb, r);
+                            const bf16x8 kt = tr8<kLay>(G.K[jj], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * bb, r);
                             uloc[jj][bb] = mfma(kt, ah, uloc[jj][bb]);
                             uloc[jj][bb] = mfma(kt, al, uloc[jj][bb]);
                         }
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int idx = wt + 256 * u, row = idx >> 3, cg = idx & 7;
-                st16(G.V[jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
+                st16<kLay>(G.V[jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
             }
         // ---- round 1: the S carry at this group's first chunk
         wait_round(0);
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
             for (int jj = 0; jj < kPerGroup; ++jj)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    st16(G.K[jj], t, 32 * ks + 8 * g, __builtin_bit_cast(u32x4, qn[jj][ks]));
+                    st16<kLay>(G.K[jj], t, 32 * ks + 8 * g, __builtin_bit_cast(u32x4, qn[jj][ks]));
         }
         if (DEN && wt < 64) {
 #pragma unroll
@@ -490,8 +491,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                 for (int bb = 0; bb < 4; ++bb) {
                     bf16x4 h, lo;
                     split4(s0[bb], h, lo);
-                    st4(G.Sh, 16 * bb + r, 16 * w + 4 * g, h);
-                    st4(G.Sl, 16 * bb + r, 16 * w + 4 * g, lo);
+                    st4<kLay>(G.Sh, 16 * bb + r, 16 * w + 4 * g, h);
+                    st4<kLay>(G.Sl, 16 * bb + r, 16 * w + 4 * g, lo);
                 }
             }
             __syncthreads();  // (1) S0 ready; previous chunk's Us reads done
@@ -505,8 +506,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     f32x4 acc = zero4;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
-                        acc = mfma(ld8(G.Sh, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
-                        acc = mfma(ld8(G.Sl, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
+                        acc = mfma(ld8<kLay>(G.Sh, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
+                        acc = mfma(ld8<kLay>(G.Sl, 16 * bb + r, 32 * ks + 8 * g), qn[jj][ks], acc);
                     }
                     usv[bb] = f2 * (e * acc + uloc[jj][bb]);
                 }
@@ -521,9 +522,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     const f32x4 us = usv[bb];
                     bf16x4 h, mid, lo;
                     split3(us, h, mid, lo);
-                    st4(G.Uh, t, 16 * bb + 4 * g, h);
-                    st4(G.Ul, t, 16 * bb + 4 * g, mid);
-                    st4(Ux, t, 16 * bb + 4 * g, lo);
+                    st4<kLay>(G.Uh, t, 16 * bb + 4 * g, h);
+                    st4<kLay>(G.Ul, t, 16 * bb + 4 * g, mid);
+                    st4<kLay>(Ux, t, 16 * bb + 4 * g, lo);
                     if (DEN) {  // y increment: sum over this wave's tokens of Us rows
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
@@ -567,10 +568,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                         f32x4 rt = zero4;
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb) {
-                            pt[sb] = mfma(ld8(G.Uh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                            pt[sb] = mfma(ld8(G.Ul, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                            pt[sb] = mfma(ld8(Ux, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
-                            if (RIDGE) rt = mfma(ld8(G.K[jj], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], rt);
+                            pt[sb] = mfma(ld8<kLay>(G.Uh, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                            pt[sb] = mfma(ld8<kLay>(G.Ul, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                            pt[sb] = mfma(ld8<kLay>(Ux, 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], pt[sb]);
+                            if (RIDGE) rt = mfma(ld8<kLay>(G.K[jj], 16 * sb + r, 32 * kb + 8 * g), qn[jj][kb], rt);
                         }
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                         pair_operand(pt[2 * ks], pt[2 * ks + 1], ph, pl);
 #pragma unroll
                         for (int jb = 0; jb < 4; ++jb) {
-                            const bf16x8 vt = tr8(G.V[jj], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                            const bf16x8 vt = tr8<kLay>(G.V[jj], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
                             num[jj][jb] = mfma(vt, ph, num[jj][jb]);
                             num[jj][jb] = mfma(vt, pl, num[jj][jb]);
                         }
@@ -605,11 +606,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int rb = 32 * ks + 8 * g;
-                    const bf16x8 vt = tr8(G.V[jj], rb, rb + 4, 16 * w, r);
+                    const bf16x8 vt = tr8<kLay>(G.V[jj], rb, rb + 4, 16 * w, r);
 #pragma unroll
                     for (int ab = 0; ab < 4; ++ab) {
-                        xacc[ab] = mfma(vt, tr8(G.Uh, rb, rb + 4, 16 * ab, r), xacc[ab]);
-                        xacc[ab] = mfma(vt, tr8(G.Ul, rb, rb + 4, 16 * ab, r), xacc[ab]);
+                        xacc[ab] = mfma(vt, tr8<kLay>(G.Uh, rb, rb + 4, 16 * ab, r), xacc[ab]);
+                        xacc[ab] = mfma(vt, tr8<kLay>(G.Ul, rb, rb + 4, 16 * ab, r), xacc[ab]);
                     }
                 }
                 if (jj == 0) {
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         const int rb = 32 * ks + 8 * g;
-                        const bf16x8 vt = tr8(G.V[jj], rb, rb + 4, 16 * w, r);
+                        const bf16x8 vt = tr8<kLay>(G.V[jj], rb, rb + 4, 16 * w, r);
                         bf16x8 vh = vt, vl;
                         if (DECAY) {
                             f32x4 x0, x1;
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                         }
 #pragma unroll
                         for (int ab = 0; ab < 4; ++ab) {
-                            const bf16x8 qt = tr8(G.K[jj], rb, rb + 4, 16 * ab, r);
+                            const bf16x8 qt = tr8<kLay>(G.K[jj], rb, rb + 4, 16 * ab, r);
                             cacc[ab] = mfma(vh, qt, cacc[ab]);
                             if (DECAY) cacc[ab] = mfma(vl, qt, cacc[ab]);
                         }
@@ -757,8 +758,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     const f32x4 x0 = d2 * xstart[ab] + (jj == 0 ? zero4 : xsave[ab]);
                     bf16x4 h, lo;
                     split4(x0, h, lo);
-                    st4(xt(jj, 0), 16 * ab + r, 16 * w + 4 * g, h);
-                    st4(xt(jj, 1), 16 * ab + r, 16 * w + 4 * g, lo);
+                    st4<kLay>(xt(jj, 0), 16 * ab + r, 16 * w + 4 * g, h);
+                    st4<kLay>(xt(jj, 1), 16 * ab + r, 16 * w + 4 * g, lo);
                 }
                 if (RIDGE) {
                     const float d1 = jj == 0 ? 1.0f : gp(static_cast<float>(len0));
@@ -767,8 +768,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                         const f32x4 c0v = d1 * cstart[ab] + (jj == 0 ? zero4 : csave[ab]);
                         bf16x4 h, lo;
                         split4(c0v, h, lo);
-                        st4(ct(jj, 0), 16 * ab + r, 16 * w + 4 * g, h);
-                        st4(ct(jj, 1), 16 * ab + r, 16 * w + 4 * g, lo);
+                        st4<kLay>(ct(jj, 0), 16 * ab + r, 16 * w + 4 * g, h);
+                        st4<kLay>(ct(jj, 1), 16 * ab + r, 16 * w + 4 * g, lo);
                     }
                 }
                 if (DEN && wt < 64) {
@@ -799,11 +800,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused64(FusedArgs a) {
                     const int rb = 32 * ks + 8 * g;
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
-                        acc[jb] = mfma(tr8(xt(jj, 0), rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
-                        acc[jb] = mfma(tr8(xt(jj, 1), rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                        acc[jb] = mfma(tr8<kLay>(xt(jj, 0), rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
+                        acc[jb] = mfma(tr8<kLay>(xt(jj, 1), rb, rb + 4, 16 * jb, r), qn[jj][ks], acc[jb]);
                         if (RIDGE) {
-                            accc[jb] = mfma(tr8(ct(jj, 0), rb, rb + 4, 16 * jb, r), qn[jj][ks], accc[jb]);
-                            accc[jb] = mfma(tr8(ct(jj, 1), rb, rb + 4, 16 * jb, r), qn[jj][ks], accc[jb]);
+                            accc[jb] = mfma(tr8<kLay>(ct(jj, 0), rb, rb + 4, 16 * jb, r), qn[jj][ks], accc[jb]);
+                            accc[jb] = mfma(tr8<kLay>(ct(jj, 1), rb, rb + 4, 16 * jb, r), qn[jj][ks], accc[jb]);
                         }
                     }
                 }
