@@ -363,6 +363,8 @@ def ctrl_words(ws):
     (1, 4, 1000, "per_head"),      # ragged, several segments per head
     (3, 5, 4095, "decay"),         # many segments, ragged
     (8, 8, 4096, "per_head"),      # more workgroups than CUs
+    (8, 8, 4096, None),            # more workgroups than CUs, no decay
+    (1, 2, 8192, None),            # more than eight earlier segments to sum, no decay
     (1, 1, 16384, "decay"),        # one head, long
     (4, 64, 256, None),            # 256 heads: the tail of q_0 . k_0 near zero at t = 0
 ])
