@@ -1,6 +1,6 @@
-// fused64_common.h -- device helpers shared by the one-launch d = 64
-// forwards (k_fused64, k_fast64): bf16 MFMA operand plumbing on padded LDS
-// tiles, operand splits, and the cross-workgroup hand-off.
+// fast64_common.h -- device helpers of the one-launch d = 64 forward
+// (k_fast64): bf16 MFMA operand plumbing on swizzled 64 x 64 LDS tiles,
+// operand splits, and the cross-workgroup hand-off.
 #pragma once
 
 #include "device_common.h"
@@ -17,11 +17,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int W = 64;          // chunk width = d = dv
-// LDS tile layouts: kSwizzled (64 rows of 128 bytes, pieces permuted, see
-// tile_off) or kPadded (rows of 72 elements, 144 bytes).
-constexpr int kSwizzled = 1, kPadded = 0;
-template <int LY>
-constexpr int kTileElems = LY == kSwizzled ? W * W : W * 72;
+constexpr int kTileElems = W * W;  // one LDS tile: 64 rows of 64 bf16, see tile_off
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kLine = 64;      // words per 256-byte control line
 constexpr int kTabWord = 2 * kLine;  // XCD table: one 64-bit entry per workgroup from this word
@@ -40,36 +36,31 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 // column groups, transposed 8-byte reads of 4+4 or 8 consecutive rows, 8-byte
 // row writes, 16-byte staging writes) touches each of the 64 LDS banks at
 // most once per cycle.  Pieces keep their pairs (XOR on index bits 1-3), so
-// 16-byte accesses at 8-element columns stay contiguous and aligned.
-// The padded layout needs fewer address registers, for kernels short of them;
-// it costs 2x on 16-byte row reads and ~1.75x on transposed reads.
-template <int LY = kSwizzled>
+// 16-byte accesses at 8-element columns stay contiguous and aligned.  (Rows
+// padded to 72 elements would cost 2x on 16-byte row reads and ~1.75x on
+// transposed reads.)
 __device__ __forceinline__ int tile_off(int row, int col) {
-    if (LY == kPadded) return row * 72 + col;
     const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
     const int h = b3 | ((b1 ^ b3) << 1) | ((b2 ^ b3) << 2);
     return row * W + ((((col >> 2) ^ (h << 1))) << 2) + (col & 3);
 }
 
 // 8 consecutive bf16 of one tile row (col a multiple of 8)
-template <int LY = kSwizzled>
 __device__ __forceinline__ bf16x8 ld8(const __bf16 *base, int row, int col) {
-    return *reinterpret_cast<const bf16x8 *>(base + tile_off<LY>(row, col));
+    return *reinterpret_cast<const bf16x8 *>(base + tile_off(row, col));
 }
 
 // 8 consecutive bf16 (16 bytes) written to one tile row (col a multiple of 8)
-template <int LY = kSwizzled>
 __device__ __forceinline__ void st16(__bf16 *base, int row, int col, const u32x4 &v) {
-    *reinterpret_cast<u32x4 *>(base + tile_off<LY>(row, col)) = v;
+    *reinterpret_cast<u32x4 *>(base + tile_off(row, col)) = v;
 }
 
 // Transposed operand: lane (g, r) receives M[rb1 + e][col0 + r] (k slots 8g+e,
 // e < 4) and M[rb2 + e][col0 + r] (slots 8g+4+e); rb1, rb2 may depend on g.
-template <int LY = kSwizzled>
 __device__ __forceinline__ bf16x8 tr8(const __bf16 *M, int rb1, int rb2, int col0, int r) {
     const int col = col0 + 4 * (r & 3);
-    const __bf16 *p1 = M + tile_off<LY>(rb1 + (r >> 2), col);
-    const __bf16 *p2 = M + tile_off<LY>(rb2 + (r >> 2), col);
+    const __bf16 *p1 = M + tile_off(rb1 + (r >> 2), col);
+    const __bf16 *p2 = M + tile_off(rb2 + (r >> 2), col);
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p2));
     bf16x8 x;
@@ -116,9 +107,8 @@ __device__ __forceinline__ void pair_operand(const f32x4 &t0, const f32x4 &t1, b
     }
 }
 
-template <int LY = kSwizzled>
 __device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4 &v) {
-    *reinterpret_cast<bf16x4 *>(base + tile_off<LY>(row, col)) = v;
+    *reinterpret_cast<bf16x4 *>(base + tile_off(row, col)) = v;
 }
 
 template <int CTL>

@@ -1,44 +1,63 @@
 // fwd_fast64.hip -- one-launch masked second-order HLA forward for
-// d = dv = 64, chunk w = 64, bf16 q/k/v, without ridge, denominator or
-// state I/O (the plain numerator q_t^T (S_t C_t - G_t)), on gfx950 MFMA.
+// d = dv = 64, chunk w = 64, bf16 q/k/v, on gfx950 MFMA: the numerator
+// q_t^T ((S_t + lambda I) C_t - G_t), optionally the denominator and the
+// ratio (no state input or output).
 //
 // Method (Higher-order Linear Attention, paperlayer.ai summary sec. 4 and 5)
-// and per-chunk algebra as in fwd_fused64.hip: with the corrected carry
-// X = S C - G, per chunk (e_t = g^(t+1), f_s = g^(L-1-s))
+// and per-chunk algebra: with the corrected carry X = S C - G, per chunk
+// (e_t = g^(t+1), f_s = g^(L-1-s))
 //   A = (Q K^T) o D_g o L,  U = diag(e) Q S0 + A K,  Us = diag(f^2) U,
 //   P = (Q Us^T) o L / f_t^2,  out = P V + diag(e^2) Q X0,
 //   S0 <- g^L S0 + K^T diag(f) K,  X0 <- g^2L X0 + Us^T V.
-// Same precision scheme: fp32 operands split into bf16 hi + lo, Us into
-// three terms for the P product.
+// The ridge adds first-order attention with the queries as keys, and the
+// denominator is the same sum with every value equal to one (y = S m - h is
+// carried like X, m like C):
+//   R = (Q Q^T) o D_g o L,  P' = P + lambda R,
+//   num = P' V + diag(e^2) Q X0 + lambda diag(e) Q C0,
+//   den = P' 1 + diag(e^2) Q y0 + lambda diag(e) Q m0,   out = num or num / den,
+//   C0 <- g^L C0 + Q^T diag(f) V,  m0 <- g^L m0 + Q^T f,  y0 <- g^2L y0 + Us^T 1.
+// Precision: fp32 operands split into bf16 hi + lo, Us into three terms
+// for the P product (q_t . Us_s cancels heavily when q_t is nearly
+// orthogonal to S_s q_s; a two-term Us would leave ~2^-18 / cos(q, S q)).
+// With the denominator, S0 in U and Us in y take three terms as well: the
+// ratio magnifies the absolute error of den where |den| is small.
 //
 // Division of work.  A workgroup (eight waves) owns a segment of up to four
 // consecutive chunks of one head.  Two roles per wave:
 //  * slice role: wave v works on 32 tokens (two 16-token blocks) of chunk
 //    v/2, so every operand it reads from LDS serves both blocks; the two
 //    waves of a SIMD (v, v+4) take opposite halves of their chunks, pairing a
-//    light and a heavy share of the triangular products: the scores, U, P,
-//    the local numerator and the output;
+//    light and a heavy share of the triangular products: the scores, U, P
+//    (and R), the local numerator, the denominator and the output;
 //  * tile role: wave v owns tiles 2v, 2v+1 of a 64 x 64 moment (row block
 //    v/2, column blocks 2(v%2), 2(v%2)+1), summed over every chunk of the
-//    segment: the key moment S, the X increment, and the carries built from
-//    the aggregates other segments publish.  No partial sums are exchanged
-//    between waves, and wave v of a segment reads only what wave v of its
-//    predecessors wrote, so every wave publishes and waits on its own flags.
-// Order per segment (LDS holds sixteen 64 x 64 bf16 tiles T):
+//    segment: the key moment S, the X increment (and C), and the carries
+//    built from the aggregates other segments publish.  Waves 0-1 also own
+//    the y vector, waves 2-3 the m vector (column sums taken on the MFMA
+//    with a ones operand).  No partial sums are exchanged between waves,
+//    and wave v of a segment reads only what wave v of its predecessors
+//    wrote, so every wave publishes and waits on its own flags.
+// Order per segment (LDS holds sixteen 64 x 64 bf16 tiles T, twenty with the
+// ridge):
 //   stage K_c -> T[c]; S_seg by tiles; publish S
-//   carry-free A^T and Uloc^T = K^T A^T by slices; stage V_c -> T[4+c]
-//   round 1: S0 of every chunk -> T[8+2c] (hi), T[9+2c] (lo)
+//   carry-free A^T and Uloc^T = K^T A^T by slices (ridge: Q_c -> T[16+c]);
+//   stage V_c -> T[4+c]
+//   round 1: S0 of every chunk -> T[8+2c] (hi), T[9+2c] (lo) (with the
+//   denominator a third term in T[c])
 //   U, Us of every chunk -> Us hi, mid in T[8+2c], T[9+2c], lo in T[c]
-//   Z_seg = sum_c decayed V_c^T Us_c by tiles; publish Z
-//   P and the local numerator by slices, while round 2 travels
-//   round 2: X0 of every chunk -> T[8+2c], T[9+2c]; out = num + e^2 Q X0
+//   Z_seg = sum_c decayed V_c^T Us_c by tiles (and C_seg, y_seg, m_seg);
+//   publish
+//   P (P') and the local numerator by slices, while round 2 travels
+//   round 2: X0 of every chunk -> T[8+2c], T[9+2c] (C0 -> T[c], T[4+c],
+//   y0 and m0 -> a vector area); out = num + e^2 Q X0 (+ the ridge and
+//   denominator terms)
 // Segment s = p * BH + head runs on workgroup s mod grid; the grid never
 // exceeds the CU count and a workgroup fills a CU, so every workgroup is
 // resident and waits only on smaller segments of its head, which are running
 // or done.  When every workgroup holding a segment of a head runs on one XCD
 // (checked at run time from the XCD table in the control block), aggregates
 // and flags go through that XCD's L2; otherwise they are device-coherent.
-#include "fused64_common.h"
+#include "fast64_common.h"
 
 namespace hla {
 namespace {
@@ -52,19 +71,23 @@ constexpr int kFThreads = 512;
 constexpr int kFMaxL = 4;   // chunks per segment
 constexpr int kWaves = 8;
 
+constexpr int kVecSlot = 128;  // floats per published vector pair (y, m)
+
 struct FastArgs {
     int H, n, nc, P, L, BH, segs;  // segs = BH * P
     const uint16_t *q, *k, *v;
-    float *out;
+    float *out, *den;  // den may be null
+    float ridge;
     uint32_t *ctrl;   // control block (epoch, done counter, XCD table)
     uint32_t *flags;  // [BH * P][2 rounds][8 waves] at kFlagStride words: publication epoch
-    float *aggS, *aggX;  // [BH * P][16 tiles][64 lanes][4]
+    float *aggS, *aggX, *aggC;  // [BH * P][16 tiles][64 lanes][4]
+    float *aggV;                // [BH * P][kVecSlot]: y increment, then m increment
     GammaTab gam;
 };
 
+template <int NT>
 struct FastSmem {
-    __bf16 T[16][kTileElems<kSwizzled>];
-    uint32_t epoch;
+    __bf16 T[NT][kTileElems];
 };
 
 // wave v's two tiles <-> a 16 KB slot: tile i at tile index 2v+i, lane l's
@@ -101,14 +124,33 @@ __device__ __forceinline__ void add_tiles(f32x4 (&acc)[2], const float *const (&
         }
 }
 
-template <bool DECAY, bool LOOP>
-__global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
-    __shared__ FastSmem sm;
-    const int tid = threadIdx.x;
-    // launch epoch: read now, first needed when the segment sum is published
-    uint32_t ep_raw = 0;
-    if (tid == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// stores one float per lane into a published slot
+__device__ __forceinline__ void put_float(const float *slot, int idx, float x, bool local) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
+    const uint32_t u = __float_as_uint(x);
+    if (local) __builtin_amdgcn_raw_buffer_store_b32(u, rs, 4 * idx, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(u, rs, 4 * idx, 0, kSc1);
+}
 
+__device__ __forceinline__ float get_float(const float *slot, int idx, bool local) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
+    const uint32_t u = local ? __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * idx, 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * idx, 0, kSc1);
+    return __uint_as_float(u);
+}
+
+// RIDGE: lambda terms; DEN: the denominator (written to den when it is
+// given); NORM: out = num / den.
+template <bool DECAY, bool LOOP, bool RIDGE, bool DEN, bool NORM>
+__global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
+    static_assert(!NORM || DEN, "the ratio needs the denominator");
+    constexpr bool MV = RIDGE && DEN;  // the query mass m only enters the ridge part of den
+    __shared__ FastSmem<RIDGE ? 20 : 16> sm;
+    const int tid = threadIdx.x;
+    // launch epoch, read by every wave: read now, first needed when the
+    // segment sum is published
+    uint32_t ep_raw = 0;
+    if ((tid & 63) == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t epoch = 0;
     const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
     const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -214,9 +256,8 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
                 st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
             }
-        if (tid == 0 && first) sm.epoch = ep_raw;
         __syncthreads();
-        if (first) epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sm.epoch))));
+        if (first) epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))));
         // XCD entries of the workgroups holding this head's segments (checked after phase A)
         uint64_t tabv = 0;
         if (l < a.P && tab_ok)
@@ -279,6 +320,13 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
+        if constexpr (RIDGE) {  // query rows of the slice chunk (zero past its end), read after round 1
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    st16(sm.T[16 + sc], t0 + 16 * i, 32 * ks + 8 * g, __builtin_bit_cast(u32x4, qn[i][ks]));
+        }
 
         // ================= carry-free slice work ====================================
         // A^T tiles (rows s, cols t) of both token blocks, then Uloc^T = K^T A^T
@@ -348,10 +396,12 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // ---- carry = sum over earlier segments pp of g^(pw * gap) * (wave's
         // tiles of agg[pp]), gap = tokens between; waits on this wave's flags only
         const int seg_tokens = a.L * W;
-        auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int round, int pw) {
+        auto wait_round = [&](int round) {
             for (int pp = l; pp < p; pp += 64)
                 if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local))
                     __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int pw) {
             constexpr int NB = 8;
             acc[0] = acc[1] = zero4;
             for (int p0 = 0; p0 < p; p0 += NB) {
@@ -368,22 +418,57 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 else add_tiles<NB, kSc1>(acc, slots, scale, cnt, wave, l);
             }
         };
+        // the same for entries off + 16(cb+i) + r of the published vectors
+        auto carry_vec = [&](float (&acc)[2], int off, int pw) {
+            constexpr int NB = 8;
+            acc[0] = acc[1] = 0.0f;
+            for (int p0 = 0; p0 < p; p0 += NB) {
+                float x[NB][2];
+#pragma unroll
+                for (int s2 = 0; s2 < NB; ++s2) {
+                    const float *vs = a.aggV + (static_cast<size_t>(bh) * a.P + min(p0 + s2, p - 1)) * kVecSlot;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) x[s2][i] = get_float(vs, off + 16 * (cb + i) + r, local);
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < NB; ++s2)
+                    if (p0 + s2 < p) {
+                        const float sc2 = gp(static_cast<float>(pw * (p - 1 - (p0 + s2)) * seg_tokens));
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) acc[i] += sc2 * x[s2][i];
+                    }
+            }
+        };
 
         // ================= round 1: S0 of every chunk -> LDS ========================
         {
             f32x4 s0seg[2];
-            carry_tiles(s0seg, a.aggS, 0, 1);
+            wait_round(0);
+            carry_tiles(s0seg, a.aggS, 1);
+            // With the denominator, S0 takes a third term (in the key tile: no
+            // key is read after the carry-free stage).  The ratio amplifies the
+            // absolute error of den where |den| is small, and a two-term S0 in U
+            // is by far its largest source.
+            if constexpr (DEN) __syncthreads();
 #pragma unroll
             for (int c = 0; c < kFMaxL; ++c) {
                 if (c < Lseg) {
                     const float d1 = gp(static_cast<float>(W * c));
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        bf16x4 h, lo;
-                        split4(d1 * s0seg[i] + spre[c][i], h, lo);
                         // lane holds S0[a = 16tb+4g+e][b = 16(cb+i)+r]; tile rows b
-                        st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
-                        st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                        if constexpr (DEN) {
+                            bf16x4 h, mid, lo;
+                            split3(d1 * s0seg[i] + spre[c][i], h, mid, lo);
+                            st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                            st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, mid);
+                            st4(sm.T[c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                        } else {
+                            bf16x4 h, lo;
+                            split4(d1 * s0seg[i] + spre[c][i], h, lo);
+                            st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                            st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                        }
                     }
                 }
             }
@@ -401,10 +486,13 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8 sh = ld8(sm.T[8 + 2 * sc], 16 * bb + r, 32 * ks + 8 * g);
                     const bf16x8 sl = ld8(sm.T[9 + 2 * sc], 16 * bb + r, 32 * ks + 8 * g);
+                    bf16x8 sx;
+                    if constexpr (DEN) sx = ld8(sm.T[sc], 16 * bb + r, 32 * ks + 8 * g);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         acc[i][bb] = mfma(sh, qn[i][ks], acc[i][bb]);
                         acc[i][bb] = mfma(sl, qn[i][ks], acc[i][bb]);
+                        if constexpr (DEN) acc[i][bb] = mfma(sx, qn[i][ks], acc[i][bb]);
                     }
                 }
             }
@@ -444,56 +532,127 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // ================= Z_seg (tiles): the segment's X increment ================
         // xpre[c] = increment of chunks 0..c-1 at chunk c's start; xrun ends as Z.
         // Tile X^T (j = 16tb+4g+e, a = 16(cb+i)+r) = sum_s V[s][j] Us[s][a].
+        // Ridge: C^T (same tiles) = sum_s V[s][j] f_s Q[s][a].  Vectors (row 0
+        // of an accumulator, lanes 0-15, from a ones operand in row 0): waves
+        // 0-1 y[a] = sum_s Us[s][a] (the three-term Us, lo in T[c]), waves 2-3
+        // m[a] = sum_s f_s Q[s][a].
+        const int tbu = __builtin_amdgcn_readfirstlane(tb);
+        const bool yw = DEN && tbu == 0, mw = MV && tbu == 1;
+        const int voff = tbu == 0 ? 0 : 64;  // the vector's place in a published pair
+        bf16x8 ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(r == 0 ? 1.0f : 0.0f);
         f32x4 xpre[kFMaxL][2], xrun[2] = {zero4, zero4};
+        f32x4 cpre[kFMaxL][2], crun[2] = {zero4, zero4};
+        float vpre[kFMaxL][2];
+        f32x4 vrun[2] = {zero4, zero4};
 #pragma unroll
         for (int c = 0; c < kFMaxL; ++c) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) xpre[c][i] = xrun[i];
-            const float rho2 = gp(static_cast<float>(2 * lcc[c]));
+            const float rho = gp(static_cast<float>(lcc[c])), rho2 = gp(static_cast<float>(2 * lcc[c]));
 #pragma unroll
             for (int i = 0; i < 2; ++i) xrun[i] *= rho2;
+            if constexpr (RIDGE) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    cpre[c][i] = crun[i];
+                    crun[i] *= rho;
+                }
+            }
+            if constexpr (DEN) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    vpre[c][i] = vrun[i][0];
+                    vrun[i] *= yw ? rho2 : rho;
+                }
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int rb = 32 * ks + 8 * g;
                 const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    xrun[i] = mfma(vt, tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
-                    xrun[i] = mfma(vt, tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * (cb + i), r), xrun[i]);
+                    const bf16x8 uh = tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * (cb + i), r);
+                    const bf16x8 um = tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * (cb + i), r);
+                    xrun[i] = mfma(vt, uh, xrun[i]);
+                    xrun[i] = mfma(vt, um, xrun[i]);
+                    if (yw) {  // all three terms: den cancels more than num near small values
+                        vrun[i] = mfma(ones, uh, vrun[i]);
+                        vrun[i] = mfma(ones, um, vrun[i]);
+                        vrun[i] = mfma(ones, tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r), vrun[i]);
+                    }
+                }
+                if constexpr (RIDGE) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const bf16x8 qt = tr8(sm.T[16 + c], rb, rb + 4, 16 * (cb + i), r);
+                        if (!DECAY) {
+                            crun[i] = mfma(vt, qt, crun[i]);
+                            if (mw) vrun[i] = mfma(ones, qt, vrun[i]);
+                        } else {
+                            f32x4 x0, x1;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                x0[e] = gp(static_cast<float>(lcc[c] - 1 - (rb + e))) * static_cast<float>(qt[e]);
+                                x1[e] = gp(static_cast<float>(lcc[c] - 1 - (rb + 4 + e))) * static_cast<float>(qt[4 + e]);
+                            }
+                            bf16x8 h, lo;
+                            pair_operand(x0, x1, h, lo);
+                            crun[i] = mfma(vt, h, crun[i]);
+                            crun[i] = mfma(vt, lo, crun[i]);
+                            if (mw) {
+                                vrun[i] = mfma(ones, h, vrun[i]);
+                                vrun[i] = mfma(ones, lo, vrun[i]);
+                            }
+                        }
+                    }
                 }
             }
         }
         if (publish) {
             put_tiles(a.aggX + slot * 4096, wave, l, xrun, local);
+            if constexpr (RIDGE) put_tiles(a.aggC + slot * 4096, wave, l, crun, local);
+            if ((yw || mw) && l < 16) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) put_float(a.aggV + slot * kVecSlot, voff + 16 * (cb + i) + r, vrun[i][0], local);
+            }
             wait_stores();
             if (l == 0) set_flag(flag_of(slot, 1), epoch, local);
         }
 
         // ================= P and the local numerator (slice) ======================
-        // P^T[s][t] = (Us_s . q_t) / f_t^2 for s <= t;  num^T[j][t] = sum_s V[s][j] P[t][s]
+        // P^T[s][t] = (Us_s . q_t) / f_t^2 for s <= t (ridge: + lambda g^(t-s)
+        // q_s . q_t);  num^T[j][t] = sum_s V[s][j] P[t][s]
+        const float lam = a.ridge;
         f32x4 num[2][4];
+        float dl[2] = {0.0f, 0.0f};  // this lane's part of sum_s P[t][s] (denominator)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
         auto p_num = [&](auto hc) __attribute__((always_inline)) {
             constexpr int HH = decltype(hc)::value;
-            f32x4 pt[2][4];
+            f32x4 pt[2][4], rt[2][4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 pt[0][sb] = pt[1][sb] = zero4;
+                if constexpr (RIDGE) rt[0][sb] = rt[1][sb] = zero4;
                 if (sb <= 2 * HH + 1) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
                         const bf16x8 u1 = ld8(sm.T[8 + 2 * sc], 16 * sb + r, 32 * kb + 8 * g);
                         const bf16x8 u2 = ld8(sm.T[9 + 2 * sc], 16 * sb + r, 32 * kb + 8 * g);
                         const bf16x8 u3 = ld8(sm.T[sc], 16 * sb + r, 32 * kb + 8 * g);
+                        bf16x8 qs;
+                        if constexpr (RIDGE) qs = ld8(sm.T[16 + sc], 16 * sb + r, 32 * kb + 8 * g);
 #pragma unroll
                         for (int i = 0; i < 2; ++i) {
                             if (sb <= 2 * HH + i) {
                                 pt[i][sb] = mfma(u1, qn[i][kb], pt[i][sb]);
                                 pt[i][sb] = mfma(u2, qn[i][kb], pt[i][sb]);
                                 pt[i][sb] = mfma(u3, qn[i][kb], pt[i][sb]);
+                                if constexpr (RIDGE) rt[i][sb] = mfma(qs, qn[i][kb], rt[i][sb]);
                             }
                         }
                     }
@@ -506,7 +665,13 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) pt[i][sb][e] = 16 * sb + 4 * g + e <= tt ? inv_f2 * pt[i][sb][e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) {
+                        const int si = 16 * sb + 4 * g + e;
+                        float x = inv_f2 * pt[i][sb][e];
+                        if constexpr (RIDGE) x += lam * gp(static_cast<float>(tt - si)) * rt[i][sb][e];
+                        pt[i][sb][e] = si <= tt ? x : 0.0f;
+                        if constexpr (DEN) dl[i] += pt[i][sb][e];
+                    }
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -535,9 +700,16 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         }
 
         // ================= round 2: X0 of every chunk -> LDS ========================
-        f32x4 x0seg[2];
-        carry_tiles(x0seg, a.aggX, 1, 2);
-        __syncthreads();  // every Us read done: the tiles take X0
+        // (ridge: C0 -> T[c] hi, T[4+c] lo; denominator: y0 and m0 of chunk c
+        // at vec[c * kVecSlot], the m0 half at +64)
+        f32x4 x0seg[2], c0seg[2];
+        float v0seg[2];
+        wait_round(1);
+        carry_tiles(x0seg, a.aggX, 2);
+        if constexpr (RIDGE) carry_tiles(c0seg, a.aggC, 1);
+        if (yw || mw) carry_vec(v0seg, voff, yw ? 2 : 1);
+        float *const vec = reinterpret_cast<float *>(sm.T[RIDGE ? 16 : 0]);
+        __syncthreads();  // every Us, value and query read done: the tiles take X0 (C0, vectors)
 #pragma unroll
         for (int c = 0; c < kFMaxL; ++c) {
             if (c < Lseg) {
@@ -549,6 +721,21 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                     // lane holds X0^T[j = 16tb+4g+e][a = 16(cb+i)+r]; tile rows a
                     st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
                     st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                }
+                if constexpr (RIDGE) {
+                    const float d1 = gp(static_cast<float>(W * c));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        bf16x4 h, lo;
+                        split4(d1 * c0seg[i] + cpre[c][i], h, lo);
+                        st4(sm.T[c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                        st4(sm.T[4 + c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                    }
+                }
+                if ((yw || mw) && l < 16) {
+                    const float dv = gp(static_cast<float>((yw ? 2 : 1) * W * c));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) vec[c * kVecSlot + voff + 16 * (cb + i) + r] = dv * v0seg[i] + vpre[c][i];
                 }
             }
         }
@@ -572,19 +759,71 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                     }
                 }
             }
+            f32x4 accc[2][4];  // ridge: C0^T q_t
+            if constexpr (RIDGE) {
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    accc[0][jb] = accc[1][jb] = zero4;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const int rb = 32 * ks + 8 * g;
+                        const bf16x8 ch = tr8(sm.T[sc], rb, rb + 4, 16 * jb, r);
+                        const bf16x8 cl = tr8(sm.T[4 + sc], rb, rb + 4, 16 * jb, r);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            accc[i][jb] = mfma(ch, qn[i][ks], accc[i][jb]);
+                            accc[i][jb] = mfma(cl, qn[i][ks], accc[i][jb]);
+                        }
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int tt = t0 + 16 * i;
+                const float e = gp(static_cast<float>(tt + 1));
+                const float e2 = e * e;
+                // den_t = sum_s P[t][s] + q_t . (e^2 y0 + lambda e m0); this lane
+                // holds features 32ks+8g.. of q_t, the other three quarters are
+                // in lanes l^16, l^32, l^48
+                float den = 0.0f;
+                if constexpr (DEN) {
+                    const float *y0 = vec + sc * kVecSlot;
+                    float part = dl[i];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const f32x4 ya = *reinterpret_cast<const f32x4 *>(y0 + 32 * ks + 8 * g);
+                        const f32x4 yb = *reinterpret_cast<const f32x4 *>(y0 + 32 * ks + 8 * g + 4);
+                        f32x4 ma = zero4, mb = zero4;
+                        if constexpr (MV) {
+                            ma = *reinterpret_cast<const f32x4 *>(y0 + 64 + 32 * ks + 8 * g);
+                            mb = *reinterpret_cast<const f32x4 *>(y0 + 64 + 32 * ks + 8 * g + 4);
+                        }
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            float wa = e2 * ya[e4], wb = e2 * yb[e4];
+                            if constexpr (MV) {
+                                wa += (lam * e) * ma[e4];
+                                wb += (lam * e) * mb[e4];
+                            }
+                            part += static_cast<float>(qn[i][ks][e4]) * wa + static_cast<float>(qn[i][ks][4 + e4]) * wb;
+                        }
+                    }
+                    part += __shfl_xor(part, 16);
+                    den = part + __shfl_xor(part, 32);
+                }
                 if (tt < Lcs) {
-                    const float e = gp(static_cast<float>(tt + 1));
-                    const float e2 = e * e;
-                    float *orow = a.out + ((static_cast<size_t>(bh) * a.n) + static_cast<size_t>(c0 + sc) * W + tt) * W;
+                    const size_t tok = static_cast<size_t>(bh) * a.n + static_cast<size_t>(c0 + sc) * W + tt;
+                    float *orow = a.out + tok * W;
+                    const float rd = NORM ? 1.0f / den : 1.0f;
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
-                        const f32x4 o = num[i][jb] + e2 * acc[i][jb];
+                        f32x4 o = num[i][jb] + e2 * acc[i][jb];
+                        if constexpr (RIDGE) o += (lam * e) * accc[i][jb];
+                        if constexpr (NORM) o *= rd;
                         // streamed past the caches: nothing is left to write back when the kernel ends
                         __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(orow + 16 * jb + 4 * g));
                     }
+                    if (DEN && a.den != nullptr && g == 0) a.den[tok] = den;
                 }
             }
         }
@@ -612,7 +851,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct FastLayout {
-    size_t flags, aggS, aggX, total;
+    size_t flags, aggS, aggX, aggC, aggV, total;
 };
 
 FastLayout fast_layout(int BH, int P) {
@@ -621,8 +860,24 @@ FastLayout fast_layout(int BH, int P) {
     L.flags = 0;
     L.aggS = L.flags + align256(slots * 2 * kWaves * kFlagStride * sizeof(uint32_t));
     L.aggX = L.aggS + slots * 4096 * sizeof(float);
-    L.total = L.aggX + slots * 4096 * sizeof(float);
+    L.aggC = L.aggX + slots * 4096 * sizeof(float);
+    L.aggV = L.aggC + slots * 4096 * sizeof(float);
+    L.total = L.aggV + slots * kVecSlot * sizeof(float);
     return L;
+}
+
+template <bool DECAY, bool LOOP>
+void launch_fast(const FastArgs &a, dim3 grid, hipStream_t st, bool ridge, bool den, bool norm) {
+    const dim3 block(kFThreads);
+    if (ridge) {
+        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true>), grid, block, 0, st, a);
+        else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, false, false>), grid, block, 0, st, a);
+    } else {
+        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, true, true>), grid, block, 0, st, a);
+        else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, false, false>), grid, block, 0, st, a);
+    }
 }
 
 void fast64_geometry(int BH, int nc, int *P, int *L) {
@@ -638,7 +893,7 @@ void fast64_geometry(int BH, int nc, int *P, int *L) {
 
 bool fast64_supported(const FwdProblem &p) {
     if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.init.S == nullptr &&
-          p.fin.S == nullptr && p.n > 0 && p.ridge == 0.0f && p.den == nullptr && !p.normalize))
+          p.fin.S == nullptr && p.n > 0))
         return false;
     const int nh = p.gam.per_head ? p.H : 1;
     for (int h = 0; h < nh; ++h)
@@ -662,12 +917,16 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
     a.out = p.out;
+    a.den = p.den;
+    a.ridge = p.ridge;
     a.ctrl = ctrl;
     const FastLayout L = fast_layout(a.BH, a.P);
     char *base = static_cast<char *>(data);
     a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
     a.aggS = reinterpret_cast<float *>(base + L.aggS);
     a.aggX = reinterpret_cast<float *>(base + L.aggX);
+    a.aggC = reinterpret_cast<float *>(base + L.aggC);
+    a.aggV = reinterpret_cast<float *>(base + L.aggV);
     a.gam = p.gam;
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
@@ -678,13 +937,14 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     const bool loop = a.segs > cus;
-    const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs)), block(kFThreads);
+    const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
+    const bool ridge = p.ridge != 0.0f, norm = p.normalize != 0, den = norm || p.den != nullptr;
     if (decay) {
-        if (loop) hipLaunchKernelGGL((k_fast64<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fast64<true, false>), grid, block, 0, st, a);
+        if (loop) launch_fast<true, true>(a, grid, st, ridge, den, norm);
+        else launch_fast<true, false>(a, grid, st, ridge, den, norm);
     } else {
-        if (loop) hipLaunchKernelGGL((k_fast64<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fast64<false, false>), grid, block, 0, st, a);
+        if (loop) launch_fast<false, true>(a, grid, st, ridge, den, norm);
+        else launch_fast<false, false>(a, grid, st, ridge, den, norm);
     }
     return hipGetLastError();
 }

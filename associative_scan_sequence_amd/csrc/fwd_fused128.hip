@@ -2,7 +2,7 @@
 // d = dv = 128, bf16 q/k/v, on gfx950 MFMA; long sequences over few heads.
 //
 // Method (Higher-order Linear Attention, paperlayer.ai summary sec. 4 and 5;
-// the chunk algebra of fwd_fused64.hip): with the carry held as
+// the chunk algebra of fwd_fast64.hip): with the carry held as
 // (S, X = S C - G), per 64-token chunk (local t, s; length L; e_t = g^(t+1),
 // f_s = g^(L-1-s); Us = diag(f^2) U)
 //   A   = (Q K^T) o D_g o L,   U = diag(e) Q S0 + A K,
@@ -25,7 +25,7 @@
 // the X carry is summed likewise.  Pass 2 walks again from the true carries
 // and writes the outputs.  With P = 1 (many heads, or short sequences) pass
 // 1 and both rounds are skipped.  Rounds, segment order and epochs work as
-// in fwd_fused64.hip (a resident grid walking segments in increasing order,
+// in fwd_fast64.hip (a resident grid walking segments in increasing order,
 // device-coherent aggregates, a launch epoch on the flags).
 //
 // Layout.  512 threads = 8 waves; wave w owns feature block w (16 of 128):
@@ -72,7 +72,7 @@ struct Args128 {
     int H, n, nc, P, L, BH, segs;  // segs = BH * P
     const uint16_t *q, *k, *v;
     float *out;
-    uint32_t *ctrl;     // as in fwd_fused64.hip
+    uint32_t *ctrl;     // as in fwd_fast64.hip
     uint32_t *flags;    // [BH * P][2]
     float *aggS, *aggZ; // [BH * P][kSlot]
     GammaTab gam;

@@ -118,7 +118,7 @@ hla_status check_common(int H, int d, int dv, hla_dtype dtype, const float *gamm
 int default_chunk(int d) { return d > 64 ? 128 : 64; }
 
 // Kernel path for a forward call.  init/fin/den only matter for the choice.
-enum class FwdPath { Generic, Fast64, Fused64, Fused128 };
+enum class FwdPath { Generic, Fast64, Fused128 };
 
 
 struct Geometry {
@@ -150,7 +150,6 @@ FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *i
     if (init) fp.init = *init;
     if (fin) fp.fin = *fin;
     if (hla::fast64_supported(fp)) return FwdPath::Fast64;
-    if (hla::fused64_supported(fp)) return FwdPath::Fused64;
     if (hla::fused128_supported(fp)) return FwdPath::Fused128;
     return FwdPath::Generic;
 }
@@ -164,8 +163,7 @@ size_t workspace_need(const hla_params *p, const Geometry &geo, const hla_state 
     const size_t gen = hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w);
     size_t fused = 0;
     if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0) {
-        const size_t a = hla::fused64_workspace_bytes(BH, p->n), b = hla::fast64_workspace_bytes(BH, p->n);
-        fused = a > b ? a : b;
+        fused = hla::fast64_workspace_bytes(BH, p->n);
     }
     if (p->dtype == HLA_BF16 && p->d == 128 && p->dv == 128 && p->n > 0)
         fused = hla::fused128_workspace_bytes(BH, p->n);
@@ -258,8 +256,6 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     const FwdPath path = choose_path(p, geo, init, final_state, den, fp.gam);
     if (path == FwdPath::Fast64) {
         e = hla::fast64_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
-    } else if (path == FwdPath::Fused64) {
-        e = hla::fused64_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
     } else if (path == FwdPath::Fused128) {
         e = hla::fused128_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
     } else {

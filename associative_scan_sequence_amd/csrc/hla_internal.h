@@ -52,12 +52,6 @@ hipError_t generic_forward(const FwdProblem &p, hipStream_t s);
 
 // One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
 // ridge, denominator and normalisation (no init or final state).
-bool fused64_supported(const FwdProblem &p);
-size_t fused64_workspace_bytes(int BH, int n);
-hipError_t fused64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
-
-// One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, the plain
-// numerator only (no ridge, denominator, normalisation, init or final state).
 bool fast64_supported(const FwdProblem &p);
 size_t fast64_workspace_bytes(int BH, int n);
 hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t s);

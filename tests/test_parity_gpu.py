@@ -407,15 +407,16 @@ def test_fused_matches_generic_path():
     assert slab_err(fden.cpu(), gden.cpu(), lead=2) <= 2e-4
 
 
+@pytest.mark.parametrize("B,H,n", [(2, 3, 64 * 13 + 37), (4, 8, 64 * 32 + 37)])
 @pytest.mark.parametrize("gk", [None, "per_head"])
 @pytest.mark.parametrize("ridge,den,normalize", [
     (0.0, True, False), (1e-3, False, False), (1e-3, True, True), (1.0, True, False),
     (0.0, False, True),
 ])
-def test_fused_options(gk, ridge, den, normalize):
-    """Ridge, denominator and ratio on the one-launch path: several segments
-    per head, a ragged tail, and group 1 with one chunk."""
-    B, H, n = 2, 3, 64 * 13 + 37
+def test_fused_options(B, H, n, gk, ridge, den, normalize):
+    """Ridge, denominator and ratio on the one-launch path, with a ragged
+    tail: 14 one-chunk segments per head (6 heads), or 9 segments of four
+    chunks per head, the last one a partial chunk (32 heads)."""
     q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=700 + int(1000 * ridge) + H)
     g = None if gk is None else inputs.gamma_list_fp32([1 - 2.0 ** -(5 + h) for h in range(H)])
     lam = inputs.ridge_fp32(ridge)
