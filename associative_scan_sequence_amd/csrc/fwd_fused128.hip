@@ -44,16 +44,14 @@
 // term (x = hi + mid + lo to ~2^-26): q_t . Us_s cancels heavily when q_t is
 // nearly orthogonal to S_s q_s (at t = s = 0 the value is (q.k)^2), and a
 // two-term Us would leave an error of ~2^-18 / cos(q, S q) there.
+#include "bf16_split.h"
 #include "device_common.h"
 #include "hla_internal.h"
 
 namespace hla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -118,38 +116,6 @@ __device__ __forceinline__ bf16x8 tr8(const __bf16 *M, int rb1, int rb2, int col
         x[4 + i] = bb[i];
     }
     return x;
-}
-
-__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = static_cast<__bf16>(x[i]);
-        lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
-    }
-}
-
-// three-term split: x = hi + mid + lo to ~2^-26 relative
-__device__ __forceinline__ void split3(const f32x4 &x, bf16x4 &hi, bf16x4 &mid, bf16x4 &lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = static_cast<__bf16>(x[i]);
-        const float r1 = x[i] - static_cast<float>(hi[i]);
-        mid[i] = static_cast<__bf16>(r1);
-        lo[i] = static_cast<__bf16>(r1 - static_cast<float>(mid[i]));
-    }
-}
-
-__device__ __forceinline__ void pair_operand(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
-    bf16x4 h0, l0, h1, l1;
-    split4(t0, h0, l0);
-    split4(t1, h1, l1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = h0[i];
-        hi[4 + i] = h1[i];
-        lo[i] = l0[i];
-        lo[4 + i] = l1[i];
-    }
 }
 
 // scale the 8 slots of an operand whose slot e holds row (rb + e) or

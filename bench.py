@@ -53,7 +53,7 @@ def parse():
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fast64_B4_H8_n2048_d64_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "associative_scan_sequence_amd", "csrc", f)
-                  for f in ("fwd_fast64.hip", "fast64_common.h")]
+                  for f in ("fwd_fast64.hip", "fast64_common.h", "bf16_split.h")]
 
 
 def kernel_source_hash():
