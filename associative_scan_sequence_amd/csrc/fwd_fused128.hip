@@ -57,8 +57,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int W = 64;          // tokens per chunk
 constexpr int D = 128;         // d = dv
-constexpr int LDW = 136;       // padded LDS row of 128 bf16 (272 bytes)
+constexpr int LDW = -1;        // 128-wide tiles: the shifted-row layout of off()
 constexpr int LDN = 72;        // padded LDS row of 64 bf16 (144 bytes)
+constexpr int kBlk128 = 2432;  // elements per 16-row block of a 128-wide tile
+constexpr int kTile128 = 4 * kBlk128;  // a 64-row 128-wide tile
 constexpr int kThreads = 512;  // eight waves
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kLine = 64;
@@ -80,16 +82,32 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Element offset of (row, col) in a tile.  LD > 0: rows padded to LD
+// elements.  LD == LDW (128-wide tiles): rows of 256 bytes in blocks of 16,
+// row r of a block shifted by 32 (r & 3) + 272 b2 + 384 b3 bytes (b2, b3 its
+// bits 2 and 3) and each block followed by 768 spare bytes.  The 16-byte slot
+// a row starts in is then 2 (r & 3) + b2 + 8 b3 (mod 256 bytes): transposed
+// reads (rows R..R+3 and R+8..R+11, 32 bytes each) and 8-byte row reads (16
+// rows) hit every bank once, and since the shift depends only on row bits that
+// are lane constants or compile-time in every access here, each address is a
+// lane base plus an immediate (no per-access arithmetic, unlike an XOR swizzle).
+template <int LD>
+__device__ __forceinline__ int off(int row, int col) {
+    if constexpr (LD > 0) return row * LD + col;
+    return (row >> 4) * kBlk128 + (row & 15) * 128 + 16 * (row & 3) + 136 * ((row >> 2) & 1) +
+           192 * ((row >> 3) & 1) + col;
+}
+
 template <int LD>
 __device__ __forceinline__ bf16x8 ld8(const __bf16 *base, int row, int col) {
-    return *reinterpret_cast<const bf16x8 *>(base + row * LD + col);
+    return *reinterpret_cast<const bf16x8 *>(base + off<LD>(row, col));
 }
 
 // two 4-element pieces of one LDS row: slots 0..3 at col1, 4..7 at col2
 template <int LD>
 __device__ __forceinline__ bf16x8 ld44(const __bf16 *base, int row, int col1, int col2) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(base + row * LD + col1);
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(base + row * LD + col2);
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(base + off<LD>(row, col1));
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(base + off<LD>(row, col2));
     bf16x8 x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -104,8 +122,8 @@ __device__ __forceinline__ bf16x8 ld44(const __bf16 *base, int row, int col1, in
 template <int LD>
 __device__ __forceinline__ bf16x8 tr8(const __bf16 *M, int rb1, int rb2, int col0, int r) {
     const int col = col0 + 4 * (r & 3);
-    const __bf16 *p1 = M + (rb1 + (r >> 2)) * LD + col;
-    const __bf16 *p2 = M + (rb2 + (r >> 2)) * LD + col;
+    const __bf16 *p1 = M + off<LD>(rb1 + (r >> 2), col);
+    const __bf16 *p2 = M + off<LD>(rb2 + (r >> 2), col);
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p2));
     const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
@@ -133,7 +151,7 @@ __device__ __forceinline__ void scaled_split(const bf16x8 &x, int rb, F wfun, bf
 
 template <int LD>
 __device__ __forceinline__ void st4(__bf16 *base, int row, int col, const bf16x4 &v) {
-    *reinterpret_cast<bf16x4 *>(base + row * LD + col) = v;
+    *reinterpret_cast<bf16x4 *>(base + off<LD>(row, col)) = v;
 }
 
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
@@ -192,18 +210,18 @@ __device__ void sum_slots(f32x4 (&acc)[8], const float *agg, int first, int p, i
 }
 
 struct Smem128 {
-    __bf16 K[W * LDW];   // chunk rows [s][a]
-    __bf16 V[W * LDW];   // [s][j]
-    __bf16 Q[W * LDW];   // [t][a]
-    __bf16 Uh[W * LDW];  // Us rows [s][b]: hi, mid and a third term
-    __bf16 Ul[W * LDW];
-    __bf16 Ux[W * LDW];
+    __bf16 K[kTile128];   // chunk rows [s][a]
+    __bf16 V[kTile128];   // [s][j]
+    __bf16 Q[kTile128];   // [t][a]
+    __bf16 Uh[kTile128];  // Us rows [s][b]: hi, mid and a third term
+    __bf16 Ul[kTile128];
+    __bf16 Ux[kTile128];
     __bf16 Ah[W * LDN];  // masked scores A[t][i], then P[t][s], hi and lo
     __bf16 Al[W * LDN];
     uint32_t epoch;
 };
 // the S0 tiles of the Z product (128 rows, hi and lo) overlay K .. Uh
-static_assert(4 * W * LDW >= 2 * D * LDW, "S0 overlay does not fit");
+static_assert(4 * kTile128 >= 2 * (2 * kTile128), "S0 overlay does not fit");
 
 // The ten unmasked (t-block, i-block) tiles of a 64 x 64 masked product,
 // then the two masked tiles whose zeros a k-block read also covers.
@@ -259,9 +277,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         for (int u = 0; u < 2; ++u) {
             const int idx = tid + kThreads * u, row = idx >> 4, cg = idx & 15;
             const bool ok = row < Lc;
-            *reinterpret_cast<u32x4 *>(&sm.Q[row * LDW + cg * 8]) = ok ? pre[0][u] : z;
-            *reinterpret_cast<u32x4 *>(&sm.K[row * LDW + cg * 8]) = ok ? pre[1][u] : z;
-            *reinterpret_cast<u32x4 *>(&sm.V[row * LDW + cg * 8]) = ok ? pre[2][u] : z;
+            *reinterpret_cast<u32x4 *>(&sm.Q[off<LDW>(row, cg * 8)]) = ok ? pre[0][u] : z;
+            *reinterpret_cast<u32x4 *>(&sm.K[off<LDW>(row, cg * 8)]) = ok ? pre[1][u] : z;
+            *reinterpret_cast<u32x4 *>(&sm.V[off<LDW>(row, cg * 8)]) = ok ? pre[2][u] : z;
         }
     };
 
@@ -480,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         sum_slots(sacc, a.aggS, static_cast<int>(slot0), p, tid,
                   [&](int pp) { return gp(static_cast<float>((p - 1 - pp) * seg_tokens)); });
         // ---- Z = S0 Ct + Lz: S0 -> LDS rows (hi/lo); lane holds S0[a][b = 16w+r] = S0[b][a]
-        __bf16 *S0h = sm.K, *S0l = sm.K + D * LDW;
+        __bf16 *S0h = sm.K, *S0l = sm.K + 2 * kTile128;  // 128-row tiles over K, V and Q, Uh
 #pragma unroll
         for (int ab = 0; ab < 8; ++ab) {
             bf16x4 h, lo;
