@@ -36,6 +36,9 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
+SECONDARY = ("ratio", "long", "decode", "compose", "small")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -48,6 +51,8 @@ def parse():
                     help="skip the secondary workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of 256 MiB (for scaling HBM counters)")
+    ap.add_argument("--only", choices=SECONDARY,
+                    help="only time this secondary workload and print its record (for profiling)")
     return ap.parse_args()
 
 
@@ -125,14 +130,17 @@ def roof(bytes_per_call, us):
             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": bytes_per_call}
 
 
-def secondary_workloads(dev, stream):
-    """The other parts of the hot path at their workload sizes."""
+def secondary_workloads(dev, stream, only=None):
+    """The other parts of the hot path at their workload sizes (all, or the
+    one named by ``only``)."""
     import torch
 
     import associative_scan_sequence_amd as hla
     import hla_inputs as inputs
 
     res = []
+    if only not in (None, "ratio"):
+        return res + secondary_rest(dev, stream, only)
     # ratio-normalised forward with per-head decay and ridge (out and den)
     w = inputs.RATIO_DECAY_D64
     per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv + 4
@@ -155,6 +163,20 @@ def secondary_workloads(dev, stream):
     res.append({"workload": w.name, "entry": "hla_forward_chunked (out + den)", "us_per_call": us,
                 "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
     del sets
+    if only is not None:
+        return res
+    return res + secondary_rest(dev, stream, None)
+
+
+def secondary_rest(dev, stream, only):
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    res = []
+    if only not in (None, "long"):
+        return res + secondary_states(dev, stream, only)
     # long d = 128 forward with decay
     w = inputs.LONG_D128
     per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv
@@ -168,6 +190,20 @@ def secondary_workloads(dev, stream):
     res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us,
                 "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
     del q, k, v, out, ws
+    if only is not None:
+        return res
+    return res + secondary_states(dev, stream, None)
+
+
+def secondary_states(dev, stream, only):
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    res = []
+    if only == "small":
+        return res + secondary_small(dev, stream)
     # streaming decode: 4096 states seeded from a 512-token prefix
     w = inputs.DECODE_D128
     q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5200, dev)
@@ -176,12 +212,15 @@ def secondary_workloads(dev, stream):
     q1, k1, v1 = (x[:, :, 0] .contiguous() for x in
                   inputs.qkv_on_device(w.B, w.H, 1, w.d, w.dv, w.dtype, 5201, dev))
     o1 = torch.empty(w.B, w.H, w.dv, dtype=torch.float32, device=dev)
-    us = time_calls(lambda i: hla.decode_step(q1, k1, v1, st, out=o1), stream, 30)
     N = w.B * w.H
     state_b = 4 * (w.d * w.d + 2 * w.d * w.dv + 2 * w.d)
-    per_state = 2 * state_b + 2 * (2 * w.d + w.dv) + 4 * w.dv
-    res.append({"workload": w.name, "entry": "hla_decode_step", "us_per_call": us,
-                "states_per_s": N / (us * 1e-6), "roofline": roof(N * per_state, us)})
+    if only in (None, "decode"):
+        us = time_calls(lambda i: hla.decode_step(q1, k1, v1, st, out=o1), stream, 30)
+        per_state = 2 * state_b + 2 * (2 * w.d + w.dv) + 4 * w.dv
+        res.append({"workload": w.name, "entry": "hla_decode_step", "us_per_call": us,
+                    "states_per_s": N / (us * 1e-6), "roofline": roof(N * per_state, us)})
+    if only == "decode":
+        return res
     # state composition of 4096 segment pairs at d = dv = 128
     b = hla.State.empty(N, w.d, w.dv, dev)
     for name in ("S", "C", "m", "G", "h", "rho"):
@@ -192,6 +231,18 @@ def secondary_workloads(dev, stream):
     res.append({"workload": "masked_hla_compose_4096_pairs_d128", "entry": "hla_state_compose",
                 "us_per_call": us, "pairs_per_s": N / (us * 1e-6), "roofline": roof(N * per_pair, us)})
     del st, b, r
+    if only is not None:
+        return res
+    return res + secondary_small(dev, stream)
+
+
+def secondary_small(dev, stream):
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    res = []
     # small fp32 forward (launch-bound: a correctness workload)
     w = inputs.SMALL_FP32
     q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5300, dev)
@@ -241,6 +292,10 @@ def main():
         copy_calibration()
         return
     dev = torch.device("cuda:0")
+    if args.only:
+        for rec in secondary_workloads(dev, torch.cuda.Stream(device=dev), only=args.only):
+            print(json.dumps(rec))
+        return
     w = inputs.FWD_D64
     q, k, v = inputs.workload_qkv(w, args.seed)
     alg = algorithmic_bytes(w)
