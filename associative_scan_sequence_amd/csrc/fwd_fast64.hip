@@ -176,8 +176,10 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // values once the queries are in.  The key moment and its flag are on
         // every segment's critical path, and the flag must wait for all of the
         // wave's outstanding memory operations, so nothing else is in flight
-        // before it.  Unconditional (rows past the chunk read the head's first
-        // row), masked where used.
+        // before it.  (With the ridge the queries come with the keys and the
+        // values follow the flag: later query loads made those variants spill.)
+        // Unconditional (rows past the chunk read the head's first row), masked
+        // where used.
         u32x4 kx[2][2], qx[2][2], vx[2][2];
         auto chunk_rows = [&](int sg_, int jj, int &Lc_, size_t &tok0_, size_t &head_) {
             const int bh_ = sg_ % a.BH, p_ = sg_ / a.BH;
@@ -232,6 +234,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             }
         };
         issue_k(seg);
+        if constexpr (RIDGE) issue_q(seg);
         const bool first = seg == static_cast<int>(blockIdx.x);
         if (tid == 0 && first && tab_ok)  // this workgroup's XCD, tagged with the launch epoch
             __hip_atomic_store(xtab + blockIdx.x, (static_cast<uint64_t>(next_epoch(ep_raw)) << 32) | 0x100u | xcd_id(),
@@ -318,16 +321,19 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             wait_stores();
             if (l == 0) set_flag(flag_of(slot, 0), epoch, local);
         }
-        issue_q(seg);
+        if constexpr (RIDGE) issue_v(seg);
+        else issue_q(seg);
 
         bf16x8 qn[2][2];  // q of token t0 + 16i, features 32ks+8g..: B operand
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
-        // the value loads go out once the queries (first and last load) are in
-        asm volatile("" : "+v"(qn[0][0]), "+v"(qn[1][1])::"memory");
-        issue_v(seg);
+        if constexpr (!RIDGE) {
+            // the value loads go out once the queries (first and last load) are in
+            asm volatile("" : "+v"(qn[0][0]), "+v"(qn[1][1])::"memory");
+            issue_v(seg);
+        }
         if constexpr (RIDGE) {  // query rows of the slice chunk (zero past its end), read after round 1
 #pragma unroll
             for (int i = 0; i < 2; ++i)
