@@ -96,10 +96,20 @@ typedef struct {
 } hla_params;
 
 /* Bytes of device workspace hla_forward_chunked needs for these params
- * (0 for an invalid p).  Its first 256 bytes are a control block (launch
- * ticket and epoch counters) that the library keeps valid from call to call:
+ * (0 for an invalid p).  Its first 8192 bytes are a control block that the
+ * library keeps valid from call to call (32-bit words: 2 = launches of the
+ * one-launch kernels, 3 = waits that hit the spin limit, 64 = finished-
+ * workgroup counter, 65 = launch epoch, then a table of XCD ids):
  * zero-fill the workspace once before its first use and do not write it
- * afterwards.  The rest holds per-chunk or per-segment partial summaries. */
+ * afterwards.  The rest holds per-chunk or per-segment partial summaries.
+ *
+ * The one-launch kernels (bf16, d = dv = 64 or 128, no init or final state)
+ * hand partial sums between workgroups of one launch and rely on all of
+ * them being resident at once (at most one per CU).  Kernels that other
+ * streams run at the same time can delay that; a wait that exceeds a fixed
+ * spin limit (about 4M polls) gives up, adds one to word 3 and the outputs
+ * of that call are then not reliable.  A caller that shares the device
+ * can check word 3. */
 size_t hla_forward_workspace_size(const hla_params *p);
 
 /* Chunk-parallel masked forward ([SUM] sec. 4 and 5: token deltas feed an
