@@ -18,7 +18,10 @@
 // One workgroup of 256 threads per state.  Rows of each matrix are read as
 // float4 with a row split over W/4 lanes, so every wave touches whole
 // contiguous rows; column partial sums are reduced through LDS.  S must be
-// symmetric (the method keeps it so): a = S_t q is formed column-wise.
+// symmetric (the method keeps it so): a = S_t q is formed column-wise, and
+// for d >= 64 only the 32 x 32 tiles on and above the diagonal are read (at
+// d = 128, 40 of 64 KB); each tile below it is written as the transpose of
+// its partner through LDS.
 #include "device_common.h"
 #include "hla_internal.h"
 
@@ -66,6 +69,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
     __shared__ float qs[D], ks[D], ms[D], hs[D], as[D], vs[DV];
     __shared__ float rs[DV], acs[DV], qgs[DV];
     __shared__ float red[2 * 1024];
+    // transposed copies of the tiles above the diagonal (d >= 64)
+    __shared__ float tb[D >= 64 ? (D / 32) * (D / 32 - 1) / 2 : 1][32 * 33];
     __shared__ float scal[4];
     const int b = blockIdx.x;  // state index b*H + h
     const float g = head_gamma(a.gam, b % a.H), g2 = g * g, lam = a.ridge;
@@ -85,6 +90,114 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
     __syncthreads();
 
     // pass 1: S_t = g S + k k^T ; a = S_t q (column form, S symmetric)
+    if constexpr (D >= 64) {
+        // Tiles (I, J), I <= J, of 32 x 32; thread (row, c4) = (tid / 8, tid % 8)
+        // holds elements (row, 4 c4 .. 4 c4 + 3) of each.  Column sums over a
+        // tile give a[32 J + col]; the transposed tile (J, I), I < J, below
+        // the diagonal gives a[32 I + row] as row sums.
+        constexpr int NT = D / 32, NU = NT * (NT + 1) / 2, NOFF = NU - NT;
+        const int row = tid >> 3, c4 = tid & 7;
+        float4 x[NU];
+        int ti[NU], tj[NU];
+        {
+            int u = 0;
+#pragma unroll
+            for (int I = 0; I < NT; ++I)
+#pragma unroll
+                for (int J = I; J < NT; ++J) {
+                    ti[u] = I;
+                    tj[u] = J;
+                    ++u;
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+            x[u] = *reinterpret_cast<const float4 *>(S + (32 * ti[u] + row) * D + 32 * tj[u] + c4 * 4);
+        float4 accc[NT];
+        float accr[NT];
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+            accc[J] = make_float4(0.f, 0.f, 0.f, 0.f);
+            accr[J] = 0.0f;
+        }
+        int off = 0;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int I = ti[u], J = tj[u];
+            const float kr = ks[32 * I + row], qr = qs[32 * I + row];
+            const int cb = 32 * J + c4 * 4;
+            float4 y;
+            y.x = g * x[u].x + kr * ks[cb];
+            y.y = g * x[u].y + kr * ks[cb + 1];
+            y.z = g * x[u].z + kr * ks[cb + 2];
+            y.w = g * x[u].w + kr * ks[cb + 3];
+            *reinterpret_cast<float4 *>(S + (32 * I + row) * D + cb) = y;
+            accc[J].x += y.x * qr; accc[J].y += y.y * qr; accc[J].z += y.z * qr; accc[J].w += y.w * qr;
+            if (I < J) {  // the mirrored tile: row sums, and its transpose staged for the lower write
+                accr[I] += (y.x * qs[cb] + y.y * qs[cb + 1]) + (y.z * qs[cb + 2] + y.w * qs[cb + 3]);
+                float *t = tb[off];
+                t[row * 33 + c4 * 4] = y.x;
+                t[row * 33 + c4 * 4 + 1] = y.y;
+                t[row * 33 + c4 * 4 + 2] = y.z;
+                t[row * 33 + c4 * 4 + 3] = y.w;
+                ++off;
+            }
+        }
+        // column sums: over the 8 rows of this wave (lanes 8 apart), then the 4 waves
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+#pragma unroll
+            for (int sh = 8; sh < 64; sh <<= 1) {
+                accc[J].x += __shfl_xor(accc[J].x, sh, 64);
+                accc[J].y += __shfl_xor(accc[J].y, sh, 64);
+                accc[J].z += __shfl_xor(accc[J].z, sh, 64);
+                accc[J].w += __shfl_xor(accc[J].w, sh, 64);
+            }
+            // row sums: over the 8 lanes of a row
+#pragma unroll
+            for (int sh = 1; sh < 8; sh <<= 1) accr[J] += __shfl_xor(accr[J], sh, 64);
+        }
+        if (lane < 8) {
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+                float *cs = red + (wv * NT + J) * 32 + c4 * 4;
+                cs[0] = accc[J].x; cs[1] = accc[J].y; cs[2] = accc[J].z; cs[3] = accc[J].w;
+            }
+        }
+        if (c4 == 0) {
+#pragma unroll
+            for (int I = 0; I < NT; ++I) red[1024 + 32 * I + row] = accr[I];
+        }
+        __syncthreads();
+        // the lower tiles: row r2 of tile (J, I) is column r2 of tile (I, J)
+        {
+            int o = 0;
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int I = ti[u], J = tj[u];
+                if (I < J) {
+                    const float *t = tb[o];
+                    float4 z;
+                    z.x = t[(c4 * 4) * 33 + row];
+                    z.y = t[(c4 * 4 + 1) * 33 + row];
+                    z.z = t[(c4 * 4 + 2) * 33 + row];
+                    z.w = t[(c4 * 4 + 3) * 33 + row];
+                    *reinterpret_cast<float4 *>(S + (32 * J + row) * D + 32 * I + c4 * 4) = z;
+                    ++o;
+                }
+            }
+        }
+        if (tid < D) {
+            const int J = tid >> 5, col = tid & 31;
+            float sum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) sum += red[(w * NT + J) * 32 + col];
+            // row sums exist for tile rows above the last
+            as[tid] = sum + (J < NT - 1 ? red[1024 + tid] : 0.0f) + lam * qs[tid];
+        }
+        __syncthreads();
+        (void)NOFF;
+    } else {
     {
         constexpr int LPR = D / 4, RPI = kThreads / LPR, IT = (D + RPI - 1) / RPI;
         const int c4 = tid % LPR, r0 = tid / LPR;
@@ -113,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
         reduce_cols<D>(acc, red, as);
         if (tid < D) as[tid] += lam * qs[tid];
         __syncthreads();
+    }
     }
     // scalars: s = k . m_{t-1}, a.q, q.k
     if (wv < 3) {
