@@ -225,11 +225,13 @@ static_assert(4 * kTile128 >= 2 * (2 * kTile128), "S0 overlay does not fit");
 
 // The ten unmasked (t-block, i-block) tiles of a 64 x 64 masked product,
 // then the two masked tiles whose zeros a k-block read also covers.
+// Entry idx of each table sits in bits 2idx, 2idx+1 of a constant, so the
+// lookup is a shift of a wave-uniform index (no memory read):
+//   tb = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 2}, ib = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 3}.
 __device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
-    constexpr int kTb[12] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 2};
-    constexpr int kIb[12] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 3};
-    tb = kTb[idx];
-    ib = kIb[idx];
+    constexpr uint32_t kTb = 0x8ffa94u, kIb = 0xde4910u;
+    tb = static_cast<int>((kTb >> (2 * idx)) & 3u);
+    ib = static_cast<int>((kIb >> (2 * idx)) & 3u);
 }
 
 // LOOP = false: one segment per workgroup (segs <= grid); true: workgroup b
@@ -237,7 +239,8 @@ __device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
 template <bool DECAY, bool LOOP>
 __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     __shared__ Smem128 sm;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
 
     // ---- launch epoch (flags of this launch carry it)
     if (tid == 0) sm.epoch = next_epoch(__hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));

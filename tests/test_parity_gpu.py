@@ -501,6 +501,9 @@ def test_fused_causality_bitwise():
     (2, 3, 1000, "per_head"),   # ragged, one chunk per segment
     (1, 1, 5000, "decay"),      # one head, 79 segments, ragged tail
     (1, 4, 300, None),          # ragged tail inside the only chunk row
+    (5, 64, 70, "per_head"),    # 320 heads > 256 CUs: workgroups walk several heads
+    (3, 96, 130, None),         # 288 heads, no decay, ragged third chunk
+    (1, 100, 150, "decay"),     # 3 one-chunk segments per head: 300 > 256, with the exchange
 ])
 def test_fused128_forward(B, H, n, gk):
     q, k, v = inputs.qkv(B, H, n, 128, 128, torch.bfloat16, seed=1300 + n + H)
