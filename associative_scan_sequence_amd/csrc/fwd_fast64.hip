@@ -156,6 +156,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
     float lg = 0.0f;
     auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
+    auto gpl = [&](float el) { return DECAY ? __builtin_amdgcn_exp2f(el) : 1.0f; };   // g^e from e log2(g)
     uint64_t *const xtab = reinterpret_cast<uint64_t *>(a.ctrl + kTabWord);
     const bool tab_ok = static_cast<int>(gridDim.x) <= kTabCap;
 
@@ -241,6 +242,15 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int bh = seg % a.BH, p = seg / a.BH;
         lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
+        // Per-element decay exponents are formed as fma(constant, log2 g, lane base):
+        // in a masked 16 x 16 tile t - s = (block offset - e) + (r - 4g), and a
+        // transposed operand's token is 32ks + 8g + e (+4).  The bases are formed
+        // where they are used (kept from being merged into one long-lived value).
+        auto lane_base = [&](int off) __attribute__((always_inline)) {
+            if (!DECAY) return 0.0f;
+            asm volatile("" : "+v"(off));
+            return static_cast<float>(off) * lg;
+        };
         const int c0 = p * a.L;
         const int Lseg = min(a.L, a.nc - c0);  // chunks in this segment (1..4)
         auto chunk_len = [&](int j) { return min(W, a.n - (c0 + j) * W); };
@@ -293,11 +303,13 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) acc[i] = mfma(ka, kb[i], acc[i]);
                 } else {
+                    // f_s = g^(Lc - 1 - s) for the tokens s = 32ks + 8g + e (+4)
+                    const float base = fmaf(static_cast<float>(Lc - 1), lg, lane_base(-8 * g));
                     f32x4 x0, x1;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        x0[e] = gp(static_cast<float>(Lc - 1 - (rb + e))) * static_cast<float>(ka[e]);
-                        x1[e] = gp(static_cast<float>(Lc - 1 - (rb + 4 + e))) * static_cast<float>(ka[4 + e]);
+                        x0[e] = gpl(fmaf(static_cast<float>(-(32 * ks + e)), lg, base)) * static_cast<float>(ka[e]);
+                        x1[e] = gpl(fmaf(static_cast<float>(-(32 * ks + 4 + e)), lg, base)) * static_cast<float>(ka[4 + e]);
                     }
                     bf16x8 h, lo;
                     pair_operand(x0, x1, h, lo);
@@ -353,6 +365,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             for (int bb = 0; bb < 4; ++bb) uloc[i][bb] = zero4;
         auto carry_free = [&](auto hc) __attribute__((always_inline)) {
             constexpr int HH = decltype(hc)::value;
+            const float lg_rg = lane_base(r - 4 * g);
             f32x4 at[2][4];
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
@@ -363,11 +376,12 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                     for (int i = 0; i < 2; ++i) {
                         if (ib <= 2 * HH + i) {
                             at[i][ib] = mfma(k1, qn[i][1], mfma(k0, qn[i][0], zero4));
-                            const int tt = 32 * HH + 16 * i + r;
+                            // g^(t - s), t = 32HH + 16i + r, s = 16ib + 4g + e; s > t only in the diagonal tile
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const int si = 16 * ib + 4 * g + e;
-                                at[i][ib][e] = si <= tt ? gp(static_cast<float>(tt - si)) * at[i][ib][e] : 0.0f;
+                                const float dec = gpl(fmaf(static_cast<float>(32 * HH + 16 * i - 16 * ib - e), lg, lg_rg));
+                                if (ib == 2 * HH + i) at[i][ib][e] = 4 * g + e <= r ? dec * at[i][ib][e] : 0.0f;
+                                else at[i][ib][e] *= dec;
                             }
                         }
                     }
@@ -605,11 +619,12 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                             crun[i] = mfma(vt, qt, crun[i]);
                             if (mw) vrun[i] = mfma(ones, qt, vrun[i]);
                         } else {
+                            const float base = fmaf(static_cast<float>(lcc[c] - 1), lg, lane_base(-8 * g));
                             f32x4 x0, x1;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                x0[e] = gp(static_cast<float>(lcc[c] - 1 - (rb + e))) * static_cast<float>(qt[e]);
-                                x1[e] = gp(static_cast<float>(lcc[c] - 1 - (rb + 4 + e))) * static_cast<float>(qt[4 + e]);
+                                x0[e] = gpl(fmaf(static_cast<float>(-(32 * ks + e)), lg, base)) * static_cast<float>(qt[e]);
+                                x1[e] = gpl(fmaf(static_cast<float>(-(32 * ks + 4 + e)), lg, base)) * static_cast<float>(qt[4 + e]);
                             }
                             bf16x8 h, lo;
                             pair_operand(x0, x1, h, lo);
@@ -647,6 +662,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
         auto p_num = [&](auto hc) __attribute__((always_inline)) {
             constexpr int HH = decltype(hc)::value;
+            const float lg_rg = RIDGE ? lane_base(r - 4 * g) : 0.0f;
             f32x4 pt[2][4], rt[2][4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
@@ -677,15 +693,19 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 const int tt = 32 * HH + 16 * i + r;
                 const float inv_f2 = tt < Lcs ? gp(static_cast<float>(-2 * (Lcs - 1 - tt))) : 0.0f;
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
+                for (int sb = 0; sb < 4; ++sb) {
+                    if (sb > 2 * HH + i) continue;  // tiles past the diagonal stay zero
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int si = 16 * sb + 4 * g + e;
+                        // s = 16sb + 4g + e; s > t only in the diagonal tile
                         float x = inv_f2 * pt[i][sb][e];
-                        if constexpr (RIDGE) x += lam * gp(static_cast<float>(tt - si)) * rt[i][sb][e];
-                        pt[i][sb][e] = si <= tt ? x : 0.0f;
-                        if constexpr (DEN) dl[i] += pt[i][sb][e];
+                        if constexpr (RIDGE)
+                            x += lam * gpl(fmaf(static_cast<float>(32 * HH + 16 * i - 16 * sb - e), lg, lg_rg)) * rt[i][sb][e];
+                        if (sb == 2 * HH + i) x = 4 * g + e <= r ? x : 0.0f;
+                        pt[i][sb][e] = x;
+                        if constexpr (DEN) dl[i] += x;
                     }
+                }
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
