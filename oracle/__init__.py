@@ -15,6 +15,9 @@ Functions (each follows the pages' identities; see ``hla_oracle.c``):
 * :func:`decode` -- the same update for one new token per state.
 * :func:`compose` -- the masked semidirect product of two segment summaries,
   paperlayer.ai page sec. 4.2 and gist.science page "Assoziative Operatoren".
+* :func:`oracle.backward.backward` (module ``backward.py``) -- gradients of
+  sum(out * dout) with respect to q, k, v: fp64 torch autograd through the
+  same serial recurrence written with plain tensor ops.
 
 Parity of every function is pinned by the ``-m "not gpu"`` tests against a
 brute-force evaluation of the masked definition, closed forms and invariants.

@@ -1,0 +1,115 @@
+"""Pins for the backward oracle (oracle/backward.py): fp64 autograd through the
+serial recurrence is checked against things other than itself -- the C
+oracle's forward, central finite differences of that forward, the exact
+linearity of the output in v, and hand-derived closed forms for one token and
+for the vanishing-decay limit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import backward as ob
+
+
+def rnd(seed, *shapes, scale=0.5):
+    r = np.random.default_rng(seed)
+    return [r.standard_normal(s) * scale for s in shapes]
+
+
+def loss(oracle_mod, q, k, v, dout, g, lam, norm):
+    out, _, _ = oracle_mod.forward(q, k, v, gamma=g, lam=lam, normalize=norm, want_state=False)
+    return float((out * dout).sum())
+
+
+CASES = [  # (gamma per head, ridge, normalize)
+    (None, 0.0, False),
+    ([0.9, 0.6], 0.0, False),
+    ([0.95, 0.8], 0.25, False),
+    ([0.97, 0.85], 0.25, True),
+    (None, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("g,lam,norm", CASES)
+def test_forward_recurrence_matches_c_oracle(oracle_mod, g, lam, norm):
+    q, k, v = rnd(11, (2, 2, 17, 5), (2, 2, 17, 5), (2, 2, 17, 3))
+    out, den = ob.forward_recurrence(*(torch.tensor(x) for x in (q, k, v)), g, lam, norm)
+    ro, rd, _ = oracle_mod.forward(q, k, v, gamma=g, lam=lam, normalize=norm, want_state=False)
+    assert np.abs(out.numpy() - ro).max() <= 1e-12 * max(1.0, np.abs(ro).max())
+    assert np.abs(den.numpy() - rd).max() <= 1e-12 * max(1.0, np.abs(rd).max())
+
+
+@pytest.mark.parametrize("g,lam,norm", CASES)
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_gradients_match_finite_differences(oracle_mod, g, lam, norm, which):
+    """Directional derivative of the C oracle's loss along a random direction of
+    one input (central difference, O(eps^2) truncation) against <grad, u>."""
+    B, H, n, d, dv = 1, 2, 11, 4, 3
+    q, k, v, dout = rnd(21 + which, (B, H, n, d), (B, H, n, d), (B, H, n, dv), (B, H, n, dv))
+    if norm:  # keep denominators away from zero: positive-leaning q, k
+        q, k = np.abs(q) + 0.3, np.abs(k) + 0.3
+    grads = ob.backward(q, k, v, dout, g, lam, norm)
+    xs = [q, k, v]
+    u = rnd(31 + which, xs[which].shape, scale=1.0)[0]
+    eps = 1e-5
+    plus = [x.copy() for x in xs]; minus = [x.copy() for x in xs]
+    plus[which] += eps * u; minus[which] -= eps * u
+    fd = (loss(oracle_mod, *plus, dout, g, lam, norm) - loss(oracle_mod, *minus, dout, g, lam, norm)) / (2 * eps)
+    an = float((grads[which] * u).sum())
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("g,lam", [(None, 0.0), ([0.9, 0.7], 0.3)])
+def test_dv_is_exact_for_the_linear_map(oracle_mod, g, lam):
+    """Without the ratio, out is linear in v: L(v + u) - L(v) = <dv, u> exactly
+    (no truncation error), for any u."""
+    q, k, v, dout, u = rnd(41, (1, 2, 23, 4), (1, 2, 23, 4), (1, 2, 23, 3), (1, 2, 23, 3), (1, 2, 23, 3))
+    _, _, dv = ob.backward(q, k, v, dout, g, lam, False)
+    lhs = loss(oracle_mod, q, k, v + u, dout, g, lam, False) - loss(oracle_mod, q, k, v, dout, g, lam, False)
+    assert abs(lhs - float((dv * u).sum())) <= 1e-11 * max(1.0, abs(lhs))
+
+
+def test_single_token_closed_form():
+    """One token: out = ((q.k)^2 + lam |q|^2) v, so with a = v . dout,
+    dv = ((q.k)^2 + lam |q|^2) dout, dq = (2 (q.k) k + 2 lam q) a, dk = 2 (q.k) q a."""
+    q, k, v, dout = rnd(51, (1, 1, 1, 6), (1, 1, 1, 6), (1, 1, 1, 4), (1, 1, 1, 4))
+    lam = 0.7
+    dq, dk, dv = ob.backward(q, k, v, dout, [0.8], lam, False)
+    qk = float(q.ravel() @ k.ravel())
+    a = float(v.ravel() @ dout.ravel())
+    np.testing.assert_allclose(dv.ravel(), (qk * qk + lam * float(q.ravel() @ q.ravel())) * dout.ravel(), rtol=1e-13)
+    np.testing.assert_allclose(dq.ravel(), (2 * qk * k.ravel() + 2 * lam * q.ravel()) * a, rtol=1e-13)
+    np.testing.assert_allclose(dk.ravel(), 2 * qk * q.ravel() * a, rtol=1e-13)
+
+
+def test_vanishing_decay_is_tokenwise():
+    """With g -> 0 every token sees only itself, so each row follows the
+    one-token closed form (g = 1e-30: cross-token terms are below 1e-30)."""
+    n = 9
+    q, k, v, dout = rnd(61, (1, 1, n, 3), (1, 1, n, 3), (1, 1, n, 2), (1, 1, n, 2))
+    dq, dk, dv = ob.backward(q, k, v, dout, [1e-30], 0.0, False)
+    for t in range(n):
+        qt, kt, vt, gt = q[0, 0, t], k[0, 0, t], v[0, 0, t], dout[0, 0, t]
+        qk, a = qt @ kt, vt @ gt
+        np.testing.assert_allclose(dv[0, 0, t], qk * qk * gt, rtol=1e-12, atol=1e-25)
+        np.testing.assert_allclose(dq[0, 0, t], 2 * qk * kt * a, rtol=1e-12, atol=1e-25)
+        np.testing.assert_allclose(dk[0, 0, t], 2 * qk * qt * a, rtol=1e-12, atol=1e-25)
+
+
+def test_empty_sequence():
+    dq, dk, dv = ob.backward(np.zeros((1, 2, 0, 4)), np.zeros((1, 2, 0, 4)), np.zeros((1, 2, 0, 3)),
+                             np.zeros((1, 2, 0, 3)))
+    assert dq.shape == (1, 2, 0, 4) and dk.shape == (1, 2, 0, 4) and dv.shape == (1, 2, 0, 3)
+
+
+def test_causality_of_gradients():
+    """dout at token t only reaches inputs at tokens <= t."""
+    n, t = 12, 6
+    q, k, v = rnd(71, (1, 1, n, 4), (1, 1, n, 4), (1, 1, n, 3))
+    dout = np.zeros((1, 1, n, 3)); dout[0, 0, t] = 1.0
+    grads = ob.backward(q, k, v, dout, [0.9], 0.2, False)
+    for gr in grads:
+        assert np.all(gr[0, 0, t + 1:] == 0.0)
+        assert np.any(gr[0, 0, :t + 1] != 0.0)
