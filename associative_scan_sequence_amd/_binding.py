@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(_PKG, "libhla.so")
 HLA_F32, HLA_BF16 = 0, 1
 STATUS = {0: "HLA_OK", 1: "HLA_ERR_INVALID_ARGUMENT", 2: "HLA_ERR_UNSUPPORTED",
           3: "HLA_ERR_ALIGNMENT", 4: "HLA_ERR_WORKSPACE", 5: "HLA_ERR_DEVICE"}
-EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_decode_step",
-            "hla_state_compose", "hla_status_string", "hla_last_error")
+EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_backward_workspace_size",
+            "hla_backward_chunked", "hla_decode_step", "hla_state_compose", "hla_status_string",
+            "hla_last_error")
 
 
 class CState(ctypes.Structure):
@@ -61,6 +62,10 @@ def load(path: str = LIB_PATH):
     lib.hla_forward_workspace_size.restype = sz
     lib.hla_forward_chunked.argtypes = [pp, vp, vp, vp, vp, vp, ps, ps, vp, sz, vp]
     lib.hla_forward_chunked.restype = ctypes.c_int
+    lib.hla_backward_workspace_size.argtypes = [pp]
+    lib.hla_backward_workspace_size.restype = sz
+    lib.hla_backward_chunked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hla_backward_chunked.restype = ctypes.c_int
     lib.hla_decode_step.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
     lib.hla_decode_step.restype = ctypes.c_int
     lib.hla_state_compose.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ps, ps, ps, vp]
@@ -205,6 +210,51 @@ def forward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=
                                  ws_ptr, ws_bytes, _stream(dev))
     _check(st)
     return out, den, fin
+
+
+def backward_workspace_size(B, H, n, d, dv, *, chunk=0, dtype=torch.bfloat16, gamma=None,
+                            ridge=0.0, normalize=False) -> int:
+    """Bytes of backward workspace (any contents; no zero fill needed)."""
+    p, _keep = _params(B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize)
+    return int(load().hla_backward_workspace_size(ctypes.byref(p)))
+
+
+def backward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *,
+                     gamma=None, ridge: float = 0.0, normalize: bool = False, chunk: int = 0,
+                     workspace: Optional[torch.Tensor] = None, grads=None):
+    """Gradients of sum(out * dout) through ``hla_backward_chunked`` (zero
+    initial state).  q, k: [B,H,n,d]; v, dout: [B,H,n,dv] (dout fp32).
+    Returns (dq, dk, dv), fp32, shaped like q, k, v; ``grads`` may supply them."""
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (torch.bfloat16, torch.float32))
+    _need(dout, "dout", (torch.float32,))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3] \
+            or dout.shape != v.shape:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} "
+                         f"dout{tuple(dout.shape)}: expected q,k [B,H,n,d], v,dout [B,H,n,dv]")
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    p, _keep = _params(B, H, n, d, dv, chunk, q.dtype, gamma, ridge, normalize)
+    need = int(lib.hla_backward_workspace_size(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if grads is None:
+        grads = (torch.empty(B, H, n, d, dtype=torch.float32, device=dev),
+                 torch.empty(B, H, n, d, dtype=torch.float32, device=dev),
+                 torch.empty(B, H, n, dv, dtype=torch.float32, device=dev))
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        _need(t, name, (torch.float32,))
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.hla_backward_chunked(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                                  grads[2].data_ptr(), ws_ptr, ws_bytes, _stream(dev))
+    _check(st)
+    return grads
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: State, *, gamma=None,

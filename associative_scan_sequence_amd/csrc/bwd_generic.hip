@@ -1,0 +1,606 @@
+// bwd_generic.hip -- chunked backward of the masked second-order HLA forward:
+// gradients of sum_t <out_t, dout_t> with respect to q, k and v, for any
+// d, dv, w in {16, 32, 64, 128} and fp32 or bf16 inputs, fp32 throughout.
+//
+// Higher-order Linear Attention, paperlayer.ai summary sec. 4 and 5 (the scan
+// trains chunk-parallel; outputs and summaries are linear in the prefix
+// states).  Written with the value rows widened by a constant 1 (V^ = [V | 1])
+// and the upstream gradient of token t as g^_t = [dnum_t | dden_t] (dout and 0
+// for the plain output; dout/den and -(dout . out)/den for the ratio), num and
+// den are one linear map of V^ and the gradient is itself a masked
+// second-order scan, run from the last token to the first:
+//
+//   u_j  = S_j q_j                                     (forward, kept per chunk)
+//   Gb_j = sum_{t>=j} g^(2(t-j)) q_t g^_t^T            Cb_j: the same with g^(t-j)
+//   w_j  = Gb_j v^_j        T_i = sum_{j>=i} g^(j-i) (w_j q_j^T + q_j w_j^T)
+//   dq_t = X^_t g^_t + S_t w_t + lambda (C^_t g^_t + Cb_t v^_t)
+//   dk_i = T_i k_i          dv_j = Gb_j^T u_j + lambda Cb_j^T q_j   (first dv columns)
+//
+// Per chunk of L tokens (local t, s; e_t = g^(t+1), eh_t = g^(L-t); carries
+// from the left (S0, X0, y0, C0, m0) of the forward, from the right Gb', Cb', T'):
+//   Gam = Gn V^T + gd 1^T (masked s <= t)
+//   W   = (Gam o D_{g^2})^T Q + diag(eh^2)(V Gbn'^T + 1 gbd'^T)
+//   dQ  = diag(e^2)(Gn X0^T + gd y0^T) + (Gam o D_{g^2}) U + diag(e) W S0
+//         + ((W K^T) o D_g o L) K + lambda [diag(e)(Gn C0^T + gd m0^T)
+//         + (Gam o D_g) Q + (Gam o D_g)^T Q + diag(eh)(V Cbn'^T + 1 cbd'^T)]
+//   dK  = ((K Q^T) o Mu) W + ((K W^T) o Mu) Q + diag(eh) K T'   (Mu = (D_g o L)^T)
+//   dV  = P^T Gn + diag(eh^2) U Gbn' + lambda diag(eh) Q Cbn'     (P: the forward's matrix)
+//   right carries: Gb <- Q^T diag(g^(2t)) G^ + g^(2L) Gb', Cb with g^t, g^L;
+//                  T  <- W^T diag(g^t) Q + Q^T diag(g^t) W + g^L T'
+//
+// Kernels (one workgroup of 256 threads per chunk unless stated):
+//   generic forward  left carries, U, out and den (into this call's workspace)
+//   k_bwd_prep       per token: Gn, gd of the ratio
+//   k_bwd_sums       Q^T diag(g^(2t)) G^ (and the ridge's g^t sums) -> right slot c
+//   k_rprefix        per head, elementwise: slot c = g^(pL_c) slot c+1 + slot c
+//   k_bwd_w          W (kept) and the exact T increment -> T slot c
+//   k_bwd_dq, k_bwd_dk, k_bwd_dv
+#include "device_common.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxW = 128;
+
+struct BwdArgs {
+    int H, n, d, dv, w, nc;
+    float ridge;
+    int normalize;
+    const void *q, *k, *v;
+    const float *dout;
+    float *gq, *gk, *gv;  // dq, dk, dv
+    const float *S, *C, *m, *X, *y, *U;  // forward slots [BH][nc+1][..], U [BH][nc][w][d]
+    const float *out, *den;              // forward output and denominator
+    const float *Gn;                     // dnum rows: dout, or dout / den with the ratio
+    float *Gw, *gd;                      // ratio only: Gn storage, and dden (else gd = null)
+    float *RG, *rg, *RC, *rc, *T;        // right slots [BH][nc+1][..]; slot c = state at chunk c's start
+    float *W;                            // [BH][nc][w][d]
+    GammaTab gam;
+};
+
+__device__ __forceinline__ size_t slot(const BwdArgs &a, int bh, int c) {
+    return static_cast<size_t>(bh) * (a.nc + 1) + c;
+}
+
+// g^k for k = 0..2w in LDS (each entry rounded once from powf)
+__device__ __forceinline__ void pow_table(float *gt, float g, int w) {
+    for (int k = threadIdx.x; k <= 2 * w; k += kThreads) gt[k] = gpow(g, k);
+    __syncthreads();
+}
+
+// buf[t][s] (stride kMaxW) = fin(t, s, sum_l A(t, l) B(s, l)) for t, s < L.
+// Thread (ty, tx) holds rows ty + 16i and columns tx + 16j.
+template <int K, typename FA, typename FB, typename FF>
+__device__ __forceinline__ void gram_to_lds(float *buf, int L, FA A, FB B, FF fin) {
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    float acc[8][8] = {};
+    for (int l = 0; l < K; ++l) {
+        float av[8], bv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) av[i] = ty + 16 * i < L ? A(ty + 16 * i, l) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = tx + 16 * j < L ? B(tx + 16 * j, l) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] += av[i] * bv[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = ty + 16 * i, s = tx + 16 * j;
+            if (t < L && s < L) buf[t * kMaxW + s] = fin(t, s, acc[i][j]);
+        }
+}
+
+// acc[i][j] += sum_{s < K} M(t_i, s) X(s, col_j) for rows t_i = ty + 16i < L,
+// columns tx + 16j
+template <int NC, typename FM, typename FX>
+__device__ __forceinline__ void mm_acc_k(float (&acc)[8][NC], int L, int K, FM M, FX X) {
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    for (int s = 0; s < K; ++s) {
+        float mv[8], xv[NC];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mv[i] = ty + 16 * i < L ? M(ty + 16 * i, s) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) xv[j] = X(s, tx + 16 * j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) acc[i][j] += mv[i] * xv[j];
+    }
+}
+
+template <int NC, typename FM, typename FX>
+__device__ __forceinline__ void mm_acc(float (&acc)[8][NC], int L, FM M, FX X) {
+    mm_acc_k<NC>(acc, L, L, M, X);
+}
+
+template <int NC>
+__device__ __forceinline__ void store_rows(float *dst, int L, int width, const float (&acc)[8][NC]) {
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = ty + 16 * i;
+        if (t < L) {
+#pragma unroll
+            for (int j = 0; j < NC; ++j) dst[static_cast<size_t>(t) * width + tx + 16 * j] = acc[i][j];
+        }
+    }
+}
+
+// ---- ratio: Gn = dout / den, gd = -(dout . out) / den, one thread per token
+template <int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_prep(BwdArgs a, size_t tokens) {
+    const size_t t = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (t >= tokens) return;
+    const float inv = 1.0f / a.den[t];
+    const float *g = a.dout + t * DV, *o = a.out + t * DV;
+    float *gn = a.Gw + t * DV;
+    float dot = 0.0f;
+    for (int j = 0; j < DV; ++j) {
+        dot += g[j] * o[j];
+        gn[j] = g[j] * inv;
+    }
+    a.gd[t] = -dot * inv;
+}
+
+// ---- right-slot increments of chunk c: Q^T diag(g^(2t)) [Gn | gd], and with the
+// ridge Q^T diag(g^t) [Gn | gd]; the last chunk also clears slot nc of every
+// right-slot array
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_sums(BwdArgs a) {
+    constexpr int TB = 32, MR = D / 16, MC = DV / 16;
+    __shared__ float qs[TB][D], gs[TB][DV], w2s[TB], w1s[TB], gds[TB];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const float *gn = a.Gn + tok * DV;
+    const bool ridge = a.ridge != 0.0f;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    float aG[MR][MC] = {}, aC[MR][MC] = {}, ag = 0.0f, ac = 0.0f;
+    for (int b0 = 0; b0 < L; b0 += TB) {
+        const int nb = min(TB, L - b0);
+        for (int i = tid; i < nb * D; i += kThreads) qs[i / D][i % D] = Elem<T>::get(q, static_cast<size_t>(b0) * D + i);
+        for (int i = tid; i < nb * DV; i += kThreads) gs[i / DV][i % DV] = gn[static_cast<size_t>(b0) * DV + i];
+        if (tid < nb) {
+            w2s[tid] = gpow(g, 2 * (b0 + tid));
+            w1s[tid] = gpow(g, b0 + tid);
+            gds[tid] = a.gd ? a.gd[tok + b0 + tid] : 0.0f;
+        }
+        __syncthreads();
+        for (int s = 0; s < nb; ++s) {
+            float qr[MR], gc[MC];
+#pragma unroll
+            for (int i = 0; i < MR; ++i) qr[i] = qs[s][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < MC; ++j) gc[j] = gs[s][tx + 16 * j];
+            const float w2 = w2s[s], w1 = w1s[s];
+#pragma unroll
+            for (int i = 0; i < MR; ++i)
+#pragma unroll
+                for (int j = 0; j < MC; ++j) {
+                    aG[i][j] += w2 * (qr[i] * gc[j]);
+                    if (ridge) aC[i][j] += w1 * (qr[i] * gc[j]);
+                }
+            if (tid < D) {
+                ag += w2 * (qs[s][tid] * gds[s]);
+                if (ridge) ac += w1 * (qs[s][tid] * gds[s]);
+            }
+        }
+        __syncthreads();
+    }
+    const size_t sl = slot(a, bh, c);
+    float *RG = a.RG + sl * D * DV, *RC = a.RC + sl * D * DV;
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int j = 0; j < MC; ++j) {
+            const int o = (ty + 16 * i) * DV + tx + 16 * j;
+            RG[o] = aG[i][j];
+            if (ridge) RC[o] = aC[i][j];
+        }
+    if (tid < D) {
+        a.rg[sl * D + tid] = ag;
+        if (ridge) a.rc[sl * D + tid] = ac;
+    }
+    if (c == a.nc - 1) {  // slot nc: nothing to the right of the last token
+        const size_t se = slot(a, bh, a.nc);
+        for (int i = tid; i < D * DV; i += kThreads) {
+            a.RG[se * D * DV + i] = 0.0f;
+            if (ridge) a.RC[se * D * DV + i] = 0.0f;
+        }
+        for (int i = tid; i < D * D; i += kThreads) a.T[se * D * D + i] = 0.0f;
+        if (tid < D) {
+            a.rg[se * D + tid] = 0.0f;
+            if (ridge) a.rc[se * D + tid] = 0.0f;
+        }
+    }
+}
+
+// Right-to-left decayed prefix over the slots, elementwise:
+// slot c = g^(power L_c) slot c+1 + slot c, for c = nc-1 .. 0.
+struct RScan {
+    float *base;
+    int E;
+};
+
+__global__ __launch_bounds__(kThreads) void k_rprefix(BwdArgs a, RScan s0, RScan s1, int power) {
+    const int bh = blockIdx.y;
+    int e = blockIdx.x * kThreads + threadIdx.x;
+    RScan sg = s0;
+    if (e >= s0.E) {
+        e -= s0.E;
+        sg = s1;
+        if (e >= s1.E) return;
+    }
+    const float g = head_gamma(a.gam, bh % a.H);
+    const int Llast = a.n - (a.nc - 1) * a.w;
+    const float rf = gpow(g, power * a.w), rl = gpow(g, power * Llast);
+    float *p = sg.base + static_cast<size_t>(bh) * (a.nc + 1) * sg.E + e;
+    float run = p[static_cast<size_t>(a.nc) * sg.E];
+    for (int c = a.nc - 1; c >= 0; --c) {
+        float *sl = p + static_cast<size_t>(c) * sg.E;
+        run = (c == a.nc - 1 ? rl : rf) * run + *sl;
+        *sl = run;
+    }
+}
+
+// ---- W = (Gam o D_{g^2})^T Q + diag(eh^2)(V Gbn'^T + 1 gbd'^T), kept; T increment
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_w(BwdArgs a) {
+    constexpr int MA = D / 16;
+    __shared__ float buf[kMaxW * kMaxW];
+    __shared__ float gt[2 * kMaxW + 1];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const T *v = static_cast<const T *>(a.v) + tok * DV;
+    const float *gn = a.Gn + tok * DV;
+    const float *gd = a.gd ? a.gd + tok : nullptr;
+    const size_t sr = slot(a, bh, c + 1);
+    const float *RGn = a.RG + sr * D * DV, *rgd = a.rg + sr * D;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    pow_table(gt, g, a.w);
+    // Gam2[t][s] = g^(2(t-s)) (gn_t . v_s + gd_t), s <= t
+    gram_to_lds<DV>(
+        buf, L, [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; },
+        [&](int s, int l) { return Elem<T>::get(v, static_cast<size_t>(s) * DV + l); },
+        [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * (x + (gd ? gd[t] : 0.0f)) : 0.0f; });
+    __syncthreads();
+    // W[s][a] = sum_{t >= s} Gam2[t][s] q_t[a]
+    float wacc[8][MA] = {};
+    mm_acc<MA>(wacc, L, [&](int s, int t) { return buf[t * kMaxW + s]; },
+               [&](int t, int col) { return Elem<T>::get(q, static_cast<size_t>(t) * D + col); });
+    // + eh_s^2 (Gbn' v_s + gbd')
+    mm_acc_k<MA>(wacc, L, DV, [&](int s, int l) { return gt[2 * (L - s)] * Elem<T>::get(v, static_cast<size_t>(s) * DV + l); },
+                 [&](int l, int col) { return RGn[col * DV + l]; });
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int s = ty + 16 * i;
+        if (s >= L) continue;
+#pragma unroll
+        for (int j = 0; j < MA; ++j) wacc[i][j] += gt[2 * (L - s)] * rgd[tx + 16 * j];
+    }
+    __syncthreads();  // Gam2 reads done
+    float *Wg = a.W + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    store_rows<MA>(Wg, L, D, wacc);
+    store_rows<MA>(buf, L, D, wacc);  // W rows, stride D
+    __syncthreads();
+    // T increment: sum_t g^t (w_t q_t^T + q_t w_t^T), d x d
+    float tacc[MA][MA] = {};
+    for (int t = 0; t < L; ++t) {
+        const float wt = gt[t];
+        float wr[MA], qr[MA], wc[MA], qc[MA];
+#pragma unroll
+        for (int i = 0; i < MA; ++i) {
+            wr[i] = buf[t * D + ty + 16 * i];
+            qr[i] = Elem<T>::get(q, static_cast<size_t>(t) * D + ty + 16 * i);
+            wc[i] = buf[t * D + tx + 16 * i];
+            qc[i] = Elem<T>::get(q, static_cast<size_t>(t) * D + tx + 16 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < MA; ++i)
+#pragma unroll
+            for (int j = 0; j < MA; ++j) tacc[i][j] += wt * (wr[i] * qc[j] + qr[i] * wc[j]);
+    }
+    float *Tc = a.T + slot(a, bh, c) * D * D;
+#pragma unroll
+    for (int i = 0; i < MA; ++i)
+#pragma unroll
+        for (int j = 0; j < MA; ++j) Tc[(ty + 16 * i) * D + tx + 16 * j] = tacc[i][j];
+}
+
+// ---- dQ
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
+    constexpr int MA = D / 16;
+    __shared__ float buf[kMaxW * kMaxW];
+    __shared__ float gt[2 * kMaxW + 1];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const float lam = a.ridge;
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const T *k = static_cast<const T *>(a.k) + tok * D;
+    const T *v = static_cast<const T *>(a.v) + tok * DV;
+    const float *gn = a.Gn + tok * DV;
+    const float *gd = a.gd ? a.gd + tok : nullptr;
+    const float *U = a.U + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    const float *Wc = a.W + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    const size_t sl = slot(a, bh, c), sr = slot(a, bh, c + 1);
+    const float *S0 = a.S + sl * D * D, *X0 = a.X + sl * D * DV, *y0 = a.y + sl * D;
+    const float *C0 = a.C + sl * D * DV, *m0 = a.m + sl * D;
+    const float *RCn = a.RC + sr * D * DV, *rcd = a.rc + sr * D;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    pow_table(gt, g, a.w);
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    // Gam[t][s] = gn_t . v_s + gd_t for s <= t (no decay)
+    gram_to_lds<DV>(
+        buf, L, [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; },
+        [&](int s, int l) { return Elem<T>::get(v, static_cast<size_t>(s) * DV + l); },
+        [&](int t, int s, float x) { return s <= t ? x + (gd ? gd[t] : 0.0f) : 0.0f; });
+    __syncthreads();
+    float acc[8][MA] = {};
+    // (Gam o D_{g^2}) U
+    mm_acc<MA>(acc, L, [&](int t, int s) { return s <= t ? gt[2 * (t - s)] * buf[t * kMaxW + s] : 0.0f; },
+               [&](int s, int col) { return U[s * D + col]; });
+    if (lam != 0.0f) {  // lambda ((Gam o D_g) + (Gam o D_g)^T) Q
+        mm_acc<MA>(acc, L,
+                   [&](int t, int s) {
+                       float x = s <= t ? gt[t - s] * buf[t * kMaxW + s] : 0.0f;
+                       if (s >= t) x += gt[s - t] * buf[s * kMaxW + t];
+                       return lam * x;
+                   },
+                   qe);
+    }
+    __syncthreads();  // Gam reads done
+    // ((W K^T) o D_g o L) K
+    gram_to_lds<D>(
+        buf, L, [&](int t, int l) { return Wc[t * D + l]; },
+        [&](int s, int l) { return Elem<T>::get(k, static_cast<size_t>(s) * D + l); },
+        [&](int t, int s, float x) { return s <= t ? gt[t - s] * x : 0.0f; });
+    __syncthreads();
+    mm_acc<MA>(acc, L, [&](int t, int s) { return buf[t * kMaxW + s]; },
+               [&](int s, int col) { return Elem<T>::get(k, static_cast<size_t>(s) * D + col); });
+    // carries: e^2 (Gn X0^T + gd y0^T) + e W S0 + lambda [e (Gn C0^T + gd m0^T) + eh (V Cbn'^T + cbd')]
+    auto gne = [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; };
+    mm_acc_k<MA>(acc, L, DV, [&](int t, int l) { return gt[2 * (t + 1)] * gne(t, l); },
+                 [&](int l, int col) { return X0[col * DV + l]; });
+    mm_acc_k<MA>(acc, L, D, [&](int t, int b) { return gt[t + 1] * Wc[t * D + b]; },
+                 [&](int b, int col) { return S0[b * D + col]; });
+    if (lam != 0.0f) {
+        mm_acc_k<MA>(acc, L, DV, [&](int t, int l) { return lam * gt[t + 1] * gne(t, l); },
+                     [&](int l, int col) { return C0[col * DV + l]; });
+        mm_acc_k<MA>(acc, L, DV,
+                     [&](int t, int l) { return lam * gt[L - t] * Elem<T>::get(v, static_cast<size_t>(t) * DV + l); },
+                     [&](int l, int col) { return RCn[col * DV + l]; });
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = ty + 16 * i;
+        if (t >= L) continue;
+        const float e = gt[t + 1], eh = gt[L - t], gdt = gd ? gd[t] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < MA; ++j) {
+            const int col = tx + 16 * j;
+            float x = e * e * gdt * y0[col];
+            if (lam != 0.0f) x += lam * (e * gdt * m0[col] + eh * rcd[col]);
+            acc[i][j] += x;
+        }
+    }
+    store_rows<MA>(a.gq + tok * D, L, D, acc);
+}
+
+// ---- dK = ((K Q^T) o Mu) W + ((K W^T) o Mu) Q + diag(eh) K T'
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_dk(BwdArgs a) {
+    constexpr int MA = D / 16;
+    __shared__ float buf[kMaxW * kMaxW];
+    __shared__ float gt[2 * kMaxW + 1];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const T *k = static_cast<const T *>(a.k) + tok * D;
+    const float *Wc = a.W + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    const float *Tr = a.T + slot(a, bh, c + 1) * D * D;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    pow_table(gt, g, a.w);
+    auto ke = [&](int t, int l) { return Elem<T>::get(k, static_cast<size_t>(t) * D + l); };
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto we = [&](int t, int l) { return Wc[t * D + l]; };
+    auto upper = [&](int t, int s, float x) { return s >= t ? gt[s - t] * x : 0.0f; };
+    float acc[8][MA] = {};
+    gram_to_lds<D>(buf, L, ke, qe, upper);
+    __syncthreads();
+    mm_acc<MA>(acc, L, [&](int t, int s) { return buf[t * kMaxW + s]; }, we);
+    __syncthreads();
+    gram_to_lds<D>(buf, L, ke, we, upper);
+    __syncthreads();
+    mm_acc<MA>(acc, L, [&](int t, int s) { return buf[t * kMaxW + s]; }, qe);
+    mm_acc_k<MA>(acc, L, D, [&](int t, int b) { return gt[L - t] * ke(t, b); },
+                 [&](int b, int col) { return Tr[b * D + col]; });
+    store_rows<MA>(a.gk + tok * D, L, D, acc);
+}
+
+// ---- dV = P^T Gn + diag(eh^2) U Gbn' + lambda diag(eh) Q Cbn'
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
+    constexpr int MC = DV / 16;
+    __shared__ float buf[kMaxW * kMaxW];
+    __shared__ float gt[2 * kMaxW + 1];
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H);
+    const float lam = a.ridge;
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const float *gn = a.Gn + tok * DV;
+    const float *U = a.U + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    const size_t sr = slot(a, bh, c + 1);
+    const float *RGn = a.RG + sr * D * DV, *RCn = a.RC + sr * D * DV;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    pow_table(gt, g, a.w);
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    // P[t][s] = g^(2(t-s)) (q_t . u_s) + lambda g^(t-s) (q_t . q_s), s <= t
+    gram_to_lds<D>(
+        buf, L, qe, [&](int s, int l) { return U[s * D + l]; },
+        [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * x : 0.0f; });
+    __syncthreads();
+    if (lam != 0.0f) {  // add the ridge part in place (each entry is owned by one thread)
+        float acc[8][8] = {};
+        for (int l = 0; l < D; ++l) {
+            float av[8], bv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) av[i] = ty + 16 * i < L ? qe(ty + 16 * i, l) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = tx + 16 * j < L ? qe(tx + 16 * j, l) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] += av[i] * bv[j];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = ty + 16 * i, s = tx + 16 * j;
+                if (t < L && s <= t) buf[t * kMaxW + s] += lam * gt[t - s] * acc[i][j];
+            }
+        __syncthreads();
+    }
+    float acc[8][MC] = {};
+    mm_acc<MC>(acc, L, [&](int s, int t) { return buf[t * kMaxW + s]; },
+               [&](int t, int col) { return gn[static_cast<size_t>(t) * DV + col]; });
+    mm_acc_k<MC>(acc, L, D, [&](int s, int l) { return gt[2 * (L - s)] * U[s * D + l]; },
+                 [&](int l, int col) { return RGn[l * DV + col]; });
+    if (lam != 0.0f)
+        mm_acc_k<MC>(acc, L, D, [&](int s, int l) { return lam * gt[L - s] * qe(s, l); },
+                     [&](int l, int col) { return RCn[l * DV + col]; });
+    store_rows<MC>(a.gv + tok * DV, L, DV, acc);
+}
+
+template <typename T, int D, int DV>
+hipError_t launch_bwd(const BwdArgs &a, int BH, hipStream_t st) {
+    const dim3 blk(kThreads), grid(a.nc, BH);
+    if (a.normalize) {
+        const size_t tokens = static_cast<size_t>(BH) * a.n;
+        hipLaunchKernelGGL((k_bwd_prep<DV>), dim3((tokens + kThreads - 1) / kThreads), blk, 0, st, a, tokens);
+    }
+    hipLaunchKernelGGL((k_bwd_sums<T, D, DV>), grid, blk, 0, st, a);
+    const RScan sG{a.RG, D * DV}, sg{a.rg, D}, sC{a.RC, D * DV}, sc{a.rc, D}, sT{a.T, D * D}, none{nullptr, 0};
+    const int e1 = D * DV + D;
+    hipLaunchKernelGGL(k_rprefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sG, sg, 2);
+    if (a.ridge != 0.0f)
+        hipLaunchKernelGGL(k_rprefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sC, sc, 1);
+    hipLaunchKernelGGL((k_bwd_w<T, D, DV>), grid, blk, 0, st, a);
+    hipLaunchKernelGGL(k_rprefix, dim3((D * D + kThreads - 1) / kThreads, BH), blk, 0, st, a, sT, none, 1);
+    hipLaunchKernelGGL((k_bwd_dq<T, D, DV>), grid, blk, 0, st, a);
+    hipLaunchKernelGGL((k_bwd_dk<T, D, DV>), grid, blk, 0, st, a);
+    hipLaunchKernelGGL((k_bwd_dv<T, D, DV>), grid, blk, 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t pick_dv(const BwdArgs &a, int BH, hipStream_t st) {
+    switch (a.dv) {
+        case 16: return launch_bwd<T, D, 16>(a, BH, st);
+        case 32: return launch_bwd<T, D, 32>(a, BH, st);
+        case 64: return launch_bwd<T, D, 64>(a, BH, st);
+        case 128: return launch_bwd<T, D, 128>(a, BH, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t pick_d(const BwdArgs &a, int BH, hipStream_t st) {
+    switch (a.d) {
+        case 16: return pick_dv<T, 16>(a, BH, st);
+        case 32: return pick_dv<T, 32>(a, BH, st);
+        case 64: return pick_dv<T, 64>(a, BH, st);
+        case 128: return pick_dv<T, 128>(a, BH, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct BwdLayout {
+    size_t fwd, out, den, Gn, gd, RG, rg, RC, rc, T, W, total;
+};
+
+BwdLayout layout(int BH, int n, int d, int dv, int w) {
+    const size_t nc = (static_cast<size_t>(n) + w - 1) / w;
+    const size_t slots = static_cast<size_t>(BH) * (nc + 1), tok = static_cast<size_t>(BH) * n;
+    BwdLayout L{};
+    size_t off = 0;
+    L.fwd = off; off = align256(off + generic_workspace_bytes(BH, n, d, dv, w));
+    L.out = off; off = align256(off + tok * dv * sizeof(float));
+    L.den = off; off = align256(off + tok * sizeof(float));
+    L.Gn = off; off = align256(off + tok * dv * sizeof(float));
+    L.gd = off; off = align256(off + tok * sizeof(float));
+    L.RG = off; off = align256(off + slots * d * dv * sizeof(float));
+    L.rg = off; off = align256(off + slots * d * sizeof(float));
+    L.RC = off; off = align256(off + slots * d * dv * sizeof(float));
+    L.rc = off; off = align256(off + slots * d * sizeof(float));
+    L.T = off; off = align256(off + slots * d * d * sizeof(float));
+    L.W = off; off = align256(off + static_cast<size_t>(BH) * nc * w * d * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+size_t generic_backward_workspace_bytes(int BH, int n, int d, int dv, int w) {
+    return layout(BH, n, d, dv, w).total;
+}
+
+hipError_t generic_backward(const BwdProblem &p, hipStream_t st) {
+    const FwdProblem &f = p.f;
+    const int BH = f.B * f.H;
+    if (f.nc == 0) return hipSuccess;
+    const BwdLayout L = layout(BH, f.n, f.d, f.dv, f.w);
+    char *base = static_cast<char *>(f.ws);
+    // the forward: left carries, U, out and den
+    FwdProblem fw = f;
+    fw.ws = base + L.fwd;
+    fw.ws_bytes = generic_workspace_bytes(BH, f.n, f.d, f.dv, f.w);
+    fw.out = reinterpret_cast<float *>(base + L.out);
+    fw.den = reinterpret_cast<float *>(base + L.den);
+    fw.init = hla_state{};
+    fw.fin = hla_state{};
+    hipError_t e = generic_forward(fw, st);
+    if (e != hipSuccess) return e;
+    const GenericSlots sl = generic_slots(fw);
+    BwdArgs a{};
+    a.H = f.H; a.n = f.n; a.d = f.d; a.dv = f.dv; a.w = f.w; a.nc = f.nc;
+    a.ridge = f.ridge; a.normalize = f.normalize;
+    a.q = f.q; a.k = f.k; a.v = f.v;
+    a.dout = p.dout; a.gq = p.dq; a.gk = p.dk; a.gv = p.dv;
+    a.S = sl.S; a.C = sl.C; a.m = sl.m; a.X = sl.X; a.y = sl.y; a.U = sl.U;
+    a.out = fw.out; a.den = fw.den;
+    a.Gw = reinterpret_cast<float *>(base + L.Gn);
+    a.gd = f.normalize ? reinterpret_cast<float *>(base + L.gd) : nullptr;
+    a.Gn = f.normalize ? a.Gw : p.dout;
+    a.RG = reinterpret_cast<float *>(base + L.RG);
+    a.rg = reinterpret_cast<float *>(base + L.rg);
+    a.RC = reinterpret_cast<float *>(base + L.RC);
+    a.rc = reinterpret_cast<float *>(base + L.rc);
+    a.T = reinterpret_cast<float *>(base + L.T);
+    a.W = reinterpret_cast<float *>(base + L.W);
+    a.gam = f.gam;
+    if (f.dtype == HLA_BF16) return pick_d<uint16_t>(a, BH, st);
+    return pick_d<float>(a, BH, st);
+}
+
+}  // namespace hla

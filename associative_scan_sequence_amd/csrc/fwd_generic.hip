@@ -566,6 +566,14 @@ size_t generic_workspace_bytes(int BH, int n, int d, int dv, int w) {
     return layout(BH, n, d, dv, w).total;
 }
 
+GenericSlots generic_slots(const FwdProblem &p) {
+    const WsLayout L = layout(p.B * p.H, p.n, p.d, p.dv, p.w);
+    char *base = static_cast<char *>(p.ws);
+    return GenericSlots{reinterpret_cast<float *>(base + L.S), reinterpret_cast<float *>(base + L.C),
+                        reinterpret_cast<float *>(base + L.m), reinterpret_cast<float *>(base + L.X),
+                        reinterpret_cast<float *>(base + L.y), reinterpret_cast<float *>(base + L.U)};
+}
+
 hipError_t generic_forward(const FwdProblem &p, hipStream_t st) {
     const int BH = p.B * p.H;
     const WsLayout L = layout(BH, p.n, p.d, p.dv, p.w);

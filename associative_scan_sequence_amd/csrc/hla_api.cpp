@@ -267,6 +267,62 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     return ok();
 }
 
+size_t hla_backward_workspace_size(const hla_params *p) {
+    Geometry geo{};
+    if (forward_geometry(p, &geo) != HLA_OK) return 0;
+    if (!width_ok(p->d) || !width_ok(p->dv)) return 0;
+    if (p->n == 0) return 0;
+    return hla::generic_backward_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w);
+}
+
+hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
+                                const float *dout, float *dq, float *dk, float *dv, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    Geometry geo{};
+    hla_status s = forward_geometry(p, &geo);
+    if (s != HLA_OK) return s;
+    hla::BwdProblem bp{};
+    hla::FwdProblem &fp = bp.f;
+    s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &fp.gam);
+    if (s != HLA_OK) return s;
+    const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
+    if (n == 0) return ok();
+    const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
+    const void *req[7] = {q, k, v, dout, dq, dk, dv};
+    const char *nm[7] = {"q", "k", "v", "dout", "dq", "dk", "dv"};
+    for (int i = 0; i < 7; ++i) {
+        if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
+        if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
+    }
+    const size_t need = hla::generic_backward_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
+    if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(HLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(HLA_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+    std::vector<Span> outs, ins;
+    outs.push_back(span("dq", dq, BH * n * p->d * 4));
+    outs.push_back(span("dk", dk, BH * n * p->d * 4));
+    outs.push_back(span("dv", dv, BH * n * p->dv * 4));
+    outs.push_back(span("workspace", workspace, need));
+    ins.push_back(span("q", q, BH * n * p->d * esz));
+    ins.push_back(span("k", k, BH * n * p->d * esz));
+    ins.push_back(span("v", v, BH * n * p->dv * esz));
+    ins.push_back(span("dout", dout, BH * n * p->dv * 4));
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    fp.B = p->B; fp.H = p->H; fp.n = p->n; fp.d = p->d; fp.dv = p->dv;
+    fp.w = geo.w; fp.nc = geo.nc;
+    fp.dtype = p->dtype; fp.ridge = p->ridge; fp.normalize = p->normalize;
+    fp.q = q; fp.k = k; fp.v = v;
+    fp.ws = workspace; fp.ws_bytes = workspace_bytes;
+    bp.dout = dout; bp.dq = dq; bp.dk = dk; bp.dv = dv;
+    const hipError_t e = hla::generic_backward(bp, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 hla_status hla_decode_step(const hla_params *p, const void *q, const void *k, const void *v,
                            hla_state *state, float *out, float *den, hipStream_t stream) {
     if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");

@@ -50,6 +50,24 @@ constexpr size_t kCtrlBytes = 8192;
 size_t generic_workspace_bytes(int BH, int n, int d, int dv, int w);
 hipError_t generic_forward(const FwdProblem &p, hipStream_t s);
 
+// Where the generic forward keeps its per-chunk products inside p.ws: slots
+// [BH][nc+1] of S, C, m, X = S C - G, y = S m - h (slot c = the state before
+// chunk c) and U [BH][nc][w][d] (row s = S_s q_s).  The backward reads them.
+struct GenericSlots {
+    float *S, *C, *m, *X, *y, *U;
+};
+GenericSlots generic_slots(const FwdProblem &p);
+
+// Chunked backward: gradients of sum(out * dout) with respect to q, k, v for
+// the zero initial state, any d, dv, w in {16,32,64,128}, fp32 or bf16.
+struct BwdProblem {
+    FwdProblem f;        // the forward call (init, fin, den unused); f.ws = backward data area
+    const float *dout;   // [B,H,n,dv]
+    float *dq, *dk, *dv; // [B,H,n,d], [B,H,n,d], [B,H,n,dv]
+};
+size_t generic_backward_workspace_bytes(int BH, int n, int d, int dv, int w);
+hipError_t generic_backward(const BwdProblem &p, hipStream_t s);
+
 // One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
 // ridge, denominator and normalisation (no init or final state).
 bool fast64_supported(const FwdProblem &p);

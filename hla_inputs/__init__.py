@@ -98,6 +98,14 @@ def qkv_on_device(B: int, H: int, n: int, d: int, dv: int, dtype: torch.dtype, s
     return tuple(out)
 
 
+def upstream(B: int, H: int, n: int, dv: int, seed: int) -> torch.Tensor:
+    """A seeded upstream gradient dout [B,H,n,dv] in fp32 (standard normal draws
+    from a CPU generator; the gradient of the loss with respect to out)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return torch.randn(B, H, n, dv, generator=gen, dtype=torch.float32)
+
+
 def decode_inputs(B: int, H: int, prefix: int, d: int, dv: int, dtype: torch.dtype, seed: int):
     """Prefix q/k/v [B,H,prefix,·] then the new token's q/k/v [B,H,·]."""
     gen = torch.Generator(device="cpu")

@@ -134,6 +134,35 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Bytes of device workspace hla_backward_chunked needs for these params (0
+ * for an invalid p).  Unlike the forward's, it holds no control block: its
+ * contents need no initialisation and are overwritten by every call. */
+size_t hla_backward_workspace_size(const hla_params *p);
+
+/* Gradients of the chunked forward from the zero initial state: with
+ * L = sum_t <out_t, dout_t>, writes dq = dL/dq, dk = dL/dk, dv = dL/dv for
+ * every option of p (decay per head, ridge, normalize).  [SUM] sec. 4 and 5
+ * (the scan trains chunk-parallel).  The gradient is itself a masked
+ * second-order scan, run from the last token to the first: with
+ * Gb_j = sum_{t>=j} g^(2(t-j)) q_t dnum_t^T (and its den column),
+ * w_j = Gb_j v_j and T_i = sum_{j>=i} g^(j-i) (w_j q_j^T + q_j w_j^T),
+ *   dq_t = X_t dnum_t + S_t w_t (+ ridge terms),  dk_i = T_i k_i,
+ *   dv_j = Gb_j^T S_j q_j (+ ridge terms),
+ * where X = S C - G is the forward's corrected carry; for the ratio
+ * dnum = dout/den and the den column carries -(dout . out)/den.  The forward
+ * is recomputed inside the call (its out and den are not inputs).
+ *   q, k  [B,H,n,d], v [B,H,n,dv] in p->dtype       (inputs, not modified)
+ *   dout  [B,H,n,dv] fp32                            (input)
+ *   dq, dk [B,H,n,d], dv [B,H,n,dv] fp32             (outputs)
+ *   workspace  device memory of at least hla_backward_workspace_size(p)
+ *         bytes, 256-byte aligned (may be NULL when n = 0).
+ * Outputs must not overlap each other, the inputs or the workspace.  With the
+ * ratio, a zero denominator gives IEEE inf/NaN gradients. */
+hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k,
+                                const void *v, const float *dout, float *dq, float *dk,
+                                float *dv, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* One streaming decode step ([SUM] sec. 1 and 2: constant-size state,
  * O(d^2 + d dv) work per token): applies token (q, k, v) to `state` in place
  * and writes its output.  p->n must be 1.

@@ -38,7 +38,7 @@ def lib():
 
 def test_header_declares_the_three_entry_points():
     fns = declared_functions()
-    for name in ("hla_forward_chunked", "hla_decode_step", "hla_state_compose"):
+    for name in ("hla_forward_chunked", "hla_backward_chunked", "hla_decode_step", "hla_state_compose"):
         assert name in fns
     assert set(fns) == set(hla.EXPORTED)
 
@@ -163,6 +163,64 @@ def test_forward_empty_sequence_without_state_is_a_no_op(lib):
     assert lib.hla_forward_chunked(ctypes.byref(p), None, None, None, None, None, None, None,
                                    addr(5), lib.hla_forward_workspace_size(ctypes.byref(p)),
                                    None) == OK
+
+
+def bwd(lib, p, q=addr(1), k=addr(2), v=addr(3), dout=addr(4), dq=addr(5), dk=addr(6), dv=addr(7),
+        ws=None, ws_bytes=None):
+    need = lib.hla_backward_workspace_size(ctypes.byref(p))
+    if ws is None:
+        ws = addr(8)
+    if ws_bytes is None:
+        ws_bytes = need
+    return lib.hla_backward_chunked(ctypes.byref(p), q, k, v, dout, dq, dk, dv, ws, ws_bytes, None)
+
+
+def test_backward_workspace_size(lib):
+    assert lib.hla_backward_workspace_size(ctypes.byref(params())) > 0
+    assert lib.hla_backward_workspace_size(None) == 0
+    assert lib.hla_backward_workspace_size(ctypes.byref(params(d=48))) == 0
+    assert lib.hla_backward_workspace_size(ctypes.byref(params(n=0))) == 0
+    a = lib.hla_backward_workspace_size(ctypes.byref(params(n=1000)))
+    assert lib.hla_backward_workspace_size(ctypes.byref(params(n=2000))) > a
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(B=0), INVALID, "B="),
+    (dict(n=-1), INVALID, "n="),
+    (dict(d=48), UNSUPPORTED, "d=48"),
+    (dict(chunk=24), UNSUPPORTED, "chunk"),
+    (dict(ridge=-1.0), INVALID, "ridge"),
+    (dict(normalize=2), INVALID, "normalize"),
+])
+def test_backward_rejects_bad_params(lib, kw, code, frag):
+    assert bwd(lib, params(**kw)) == code
+    assert frag in last(lib)
+
+
+def test_backward_rejects_bad_pointers_and_workspace(lib):
+    p = params()
+    assert bwd(lib, p, dout=None) == INVALID and "dout is NULL" in last(lib)
+    assert bwd(lib, p, dk=None) == INVALID and "dk is NULL" in last(lib)
+    assert bwd(lib, p, dv=addr(7) + 4) == ALIGN and "dv is not" in last(lib)
+    need = lib.hla_backward_workspace_size(ctypes.byref(p))
+    assert bwd(lib, p, ws_bytes=need - 1) == WORKSPACE
+    assert bwd(lib, p, ws=addr(8) + 16) == ALIGN and "256-byte" in last(lib)
+    assert lib.hla_backward_chunked(ctypes.byref(p), addr(1), addr(2), addr(3), addr(4), addr(5),
+                                    addr(6), addr(7), None, need, None) == WORKSPACE
+
+
+def test_backward_rejects_aliasing(lib):
+    p = params()
+    assert bwd(lib, p, dq=addr(1) + 256) == INVALID and "dq overlaps q" in last(lib)
+    assert bwd(lib, p, dk=addr(5) + 512) == INVALID and "overlaps" in last(lib)
+    assert bwd(lib, p, dv=addr(4)) == INVALID and "dv overlaps dout" in last(lib)
+    assert bwd(lib, p, ws=addr(2)) == INVALID and "workspace overlaps k" in last(lib)
+
+
+def test_backward_empty_sequence_is_a_no_op(lib):
+    p = params(n=0)
+    assert lib.hla_backward_chunked(ctypes.byref(p), None, None, None, None, None, None, None, None,
+                                    0, None) == OK
 
 
 def dec(lib, p, state, q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None):

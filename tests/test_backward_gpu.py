@@ -1,0 +1,148 @@
+"""GPU parity of the backward (hla_backward_chunked through the C ABI) against
+the fp64 autograd oracle (oracle/backward.py) on identical seeded inputs.
+
+The backward computes in fp32 from exactly widened inputs, so bf16 and fp32
+inputs share one gate: slab error (per (b, h), max |x - ref| / max |ref|)
+of each gradient at most 1e-5 (fp32 accumulation over a few hundred terms
+of mixed sign; see the tolerance reading in the design notes).  With the
+ratio, q and k are drawn positive (|x| + 0.1 of the seeded draws) so that
+every denominator is bounded away from zero.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import associative_scan_sequence_amd as hla
+import hla_inputs as inputs
+from parity import row_err, slab_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+GTOL = 1e-5
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sys.stdout.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stdout.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def make(B, H, n, d, dv, dtype, gk, norm, seed):
+    q, k, v = inputs.qkv(B, H, n, d, dv, dtype, seed=seed)
+    if norm:
+        q, k = (x.float().abs().add(0.1).to(dtype) for x in (q, k))
+    g = None
+    if gk == "decay":
+        g = inputs.gamma_list_fp32([0.97] * H)
+    elif gk == "per_head":
+        g = inputs.gamma_list_fp32([1 - 2.0 ** -(3 + h % 6) for h in range(H)])
+    dout = inputs.upstream(B, H, n, dv, seed=seed + 7)
+    return q, k, v, dout, g
+
+
+def run_gpu(q, k, v, dout, g, lam, norm, chunk):
+    qg, kg, vg, dg = (x.to(DEV).contiguous() for x in (q, k, v, dout))
+    out = hla.backward_chunked(qg, kg, vg, dg, gamma=g, ridge=lam, normalize=norm, chunk=chunk)
+    torch.cuda.synchronize()
+    return [x.cpu() for x in out]
+
+
+def check(got, ref, names=("dq", "dk", "dv")):
+    errs = {}
+    for name, x, r in zip(names, got, ref):
+        e = slab_err(x, r, lead=2)
+        errs[name] = e
+        print(f"{name}: slab {e:.3e} row {row_err(x, r):.3e}")
+    for name, e in errs.items():
+        assert e <= GTOL, f"{name}: slab error {e:.3e} > {GTOL:.0e}"
+
+
+CASES = [
+    # B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize
+    (1, 2, 150, 32, 32, 64, torch.float32, "per_head", 0.0, False),
+    (1, 2, 150, 32, 32, 64, torch.float32, "per_head", 0.3, False),
+    (1, 2, 150, 32, 32, 64, torch.float32, "per_head", 0.3, True),
+    (2, 3, 257, 64, 64, 64, torch.bfloat16, "decay", 0.0, False),
+    (1, 2, 300, 128, 128, 128, torch.bfloat16, "decay", 1e-3, True),
+    (1, 1, 33, 16, 128, 16, torch.float32, None, 0.0, False),
+    (1, 2, 70, 128, 32, 32, torch.float32, None, 0.2, False),
+    (2, 2, 1, 64, 64, 64, torch.bfloat16, None, 0.0, False),
+    (1, 1, 64, 16, 16, 16, torch.float32, "decay", 0.0, True),
+    (1, 3, 200, 64, 16, 128, torch.bfloat16, "per_head", 0.5, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}d{c[3]}dv{c[4]}w{c[5]}"
+                         f"{'bf16' if c[6] == torch.bfloat16 else 'f32'}-{c[7]}-l{c[8]}-r{int(c[9])}")
+def test_backward_matches_oracle(case):
+    B, H, n, d, dv, chunk, dtype, gk, lam, norm = case
+    q, k, v, dout, g = make(B, H, n, d, dv, dtype, gk, norm, seed=500 + n + d)
+    lam = inputs.ridge_fp32(lam)
+    got = run_gpu(q, k, v, dout, g, lam, norm, chunk)
+    from oracle import backward as ob
+    ref = ob.backward(q, k, v, dout, g, lam, norm)
+    check(got, ref)
+
+
+def test_backward_headline_shape_sampled_heads():
+    """The B4 H8 n2048 d64 bf16 workload at full size; the oracle checks two
+    (b, h) slabs (heads are independent)."""
+    w = inputs.FWD_D64
+    q, k, v = inputs.workload_qkv(w, seed=1001)
+    dout = inputs.upstream(w.B, w.H, w.n, w.dv, seed=1008)
+    got = run_gpu(q, k, v, dout, None, 0.0, False, w.chunk)
+    from oracle import backward as ob
+    for b, h in ((0, 0), (3, 7)):
+        sl = lambda x: x[b:b + 1, h:h + 1]  # noqa: E731
+        ref = ob.backward(sl(q), sl(k), sl(v), sl(dout))
+        check([sl(x) for x in got], ref)
+
+
+def test_backward_deterministic_and_causal():
+    B, H, n, d, dv = 1, 2, 200, 64, 64
+    q, k, v, dout, g = make(B, H, n, d, dv, torch.bfloat16, "decay", False, seed=77)
+    a = run_gpu(q, k, v, dout, g, 0.1, False, 64)
+    b = run_gpu(q, k, v, dout, g, 0.1, False, 64)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    t = 90  # upstream gradient only up to token t: nothing after t receives any
+    d2 = dout.clone()
+    d2[:, :, t + 1:] = 0
+    c = run_gpu(q, k, v, d2, g, 0.1, False, 64)
+    for x in c:
+        assert torch.count_nonzero(x[:, :, t + 1:]) == 0
+        assert torch.count_nonzero(x[:, :, :t + 1]) > 0
+
+
+def test_backward_agrees_with_forward_difference():
+    """<grad, u> against differences of the GPU forward itself along a random
+    direction (consistency of the two entry points, independent of the
+    oracle).  Without the ratio, out is of degree 5 in (q, k, v) (q_t, k_i,
+    k_i, q_j, v_j), so L(x + h u) is a quintic in h, the central difference is
+    D(h) = a1 + a3 h^2 + a5 h^4, and two Richardson steps give the derivative
+    a1 exactly; only the forward's fp32 rounding remains."""
+    B, H, n, d, dv = 1, 2, 96, 32, 32
+    q, k, v, dout, g = make(B, H, n, d, dv, torch.float32, "per_head", False, seed=88)
+    grads = run_gpu(q, k, v, dout, g, 0.2, False, 32)
+    gen = torch.Generator().manual_seed(5)
+    u = [torch.randn(x.shape, generator=gen) * 0.1 for x in (q, k, v)]
+
+    def L(h):
+        xs = [(x + h * du).to(DEV) for x, du in zip((q, k, v), u)]
+        out, _, _ = hla.forward_chunked(*xs, gamma=g, ridge=0.2, chunk=32)
+        return float((out.double().cpu() * dout.double()).sum())
+
+    def D(h):
+        return (L(h) - L(-h)) / (2 * h)
+
+    def R1(h):
+        return (4 * D(h / 2) - D(h)) / 3
+    h = 1.0
+    fd = (16 * R1(h / 2) - R1(h)) / 15
+    an = sum(float((gr.double() * du.double()).sum()) for gr, du in zip(grads, u))
+    assert abs(fd - an) <= 2e-4 * abs(an), (fd, an)
