@@ -19,7 +19,7 @@ against 8 TB/s), and the fp64 CPU oracle timed on the host on a bounded
 sample of the same workload.  The line also carries ``workloads``: the
 other parts of the hot path (the ratio-normalised forward with decay and
 ridge, the long d=128 forward, the streaming decode step, state composition,
-the small fp32 forward), each timed with HIP events on its launch stream and
+the small fp32 forward) and the backward at the headline shape, each timed with HIP events on its launch stream and
 set against its own HBM roofline (``--headline-only`` skips them).
 """
 import argparse
@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
-SECONDARY = ("ratio", "long", "decode", "compose", "small")
+SECONDARY = ("ratio", "long", "decode", "compose", "small", "backward")
 
 
 def parse():
@@ -202,8 +202,8 @@ def secondary_states(dev, stream, only):
     import hla_inputs as inputs
 
     res = []
-    if only == "small":
-        return res + secondary_small(dev, stream)
+    if only in ("small", "backward"):
+        return res + secondary_small(dev, stream, only)
     # streaming decode: 4096 states seeded from a 512-token prefix
     w = inputs.DECODE_D128
     q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5200, dev)
@@ -233,10 +233,53 @@ def secondary_states(dev, stream, only):
     del st, b, r
     if only is not None:
         return res
-    return res + secondary_small(dev, stream)
+    return res + secondary_small(dev, stream, None)
 
 
-def secondary_small(dev, stream):
+def secondary_small(dev, stream, only):
+    res = []
+    if only in (None, "small"):
+        res += small_forward(dev, stream)
+    if only in (None, "backward"):
+        res += backward_headline_shape(dev, stream)
+    return res
+
+
+def backward_headline_shape(dev, stream):
+    """hla_backward_chunked at B4 H8 n2048 d64 bf16: read q, k, v (bf16) and
+    dout (fp32), write dq, dk, dv (fp32): 1408 B per head-token."""
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    w = inputs.FWD_D64
+    per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv + 4 * (2 * w.d + w.dv)
+    tok = w.B * w.H * w.n
+    need = hla.backward_workspace_size(w.B, w.H, w.n, w.d, w.dv, chunk=w.chunk)
+    copies = max(2, math.ceil(2 * MALL_BYTES / (tok * per_tok + need)))
+    sets = []
+    for c in range(copies):
+        q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5400 + c, dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5500 + c)
+        dout = torch.randn(w.B, w.H, w.n, w.dv, generator=gen, dtype=torch.float32, device=dev)
+        grads = (torch.empty(w.B, w.H, w.n, w.d, dtype=torch.float32, device=dev),
+                 torch.empty(w.B, w.H, w.n, w.d, dtype=torch.float32, device=dev),
+                 torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        sets.append((q, k, v, dout, grads, ws))
+
+    def call(i):
+        q, k, v, dout, grads, ws = sets[i % copies]
+        hla.backward_chunked(q, k, v, dout, chunk=w.chunk, workspace=ws, grads=grads)
+    us = time_calls(call, stream, 10, warmup=2)
+    return [{"workload": "masked_hla_bwd_B4_H8_n2048_d64_bf16_w64", "entry": "hla_backward_chunked",
+             "us_per_call": us, "tokens_per_s": w.B * w.n / (us * 1e-6),
+             "roofline": roof(tok * per_tok, us)}]
+
+
+def small_forward(dev, stream):
     import torch
 
     import associative_scan_sequence_amd as hla
