@@ -70,64 +70,118 @@ __device__ __forceinline__ void pow_table(float *gt, float g, int w) {
     __syncthreads();
 }
 
-// buf[t][s] (stride kMaxW) = fin(t, s, sum_l A(t, l) B(s, l)) for t, s < L.
-// Thread (ty, tx) holds rows ty + 16i and columns tx + 16j.
-template <int K, typename FA, typename FB, typename FF>
-__device__ __forceinline__ void gram_to_lds(float *buf, int L, FA A, FB B, FF fin) {
+// Products are formed from LDS: operands are staged in k-blocks of KB,
+// transposed ([k][row], rows padded by 4 floats), and every thread owns a
+// contiguous block of output rows (RM per thread, rows RM*ty ..) and columns
+// (NC per thread, columns NC*tx ..), so its operand reads are 16-byte vectors.
+constexpr int KB = 16;
+constexpr int kStageW = kMaxW + 4;
+
+struct alignas(16) Stage {
+    float a[KB][kStageW];
+    float b[KB][kStageW];
+};
+
+template <int N>
+__device__ __forceinline__ void read_vec(const float *p, float (&v)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(p + i);
+            v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = p[i];
+    }
+}
+
+// buf[t][s] (row stride BW) = fin(t, s, sum_{l<K} A(t, l) B(s, l)) for t, s < L;
+// thread (ty, tx) forms rows RT*ty .. and columns RT*tx .. (RT*16 >= L).
+template <int RT, int K, typename FA, typename FB, typename FF>
+__device__ __forceinline__ void gram(float *buf, int BW, int L, Stage &st, FA A, FB B, FF fin) {
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    float acc[8][8] = {};
-    for (int l = 0; l < K; ++l) {
-        float av[8], bv[8];
+    float acc[RT][RT] = {};
+    for (int l0 = 0; l0 < K; l0 += KB) {
+        for (int idx = tid; idx < L * KB; idx += kThreads) {  // k fastest: row-major operands
+            const int row = idx / KB, kk = idx % KB;
+            st.a[kk][row] = A(row, l0 + kk);
+            st.b[kk][row] = B(row, l0 + kk);
+        }
+        __syncthreads();
+        if (RT * ty < L && RT * tx < L) {
+#pragma unroll 4
+            for (int kk = 0; kk < KB; ++kk) {
+                float av[RT], bv[RT];
+                read_vec<RT>(&st.a[kk][RT * ty], av);
+                read_vec<RT>(&st.b[kk][RT * tx], bv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) av[i] = ty + 16 * i < L ? A(ty + 16 * i, l) : 0.0f;
+                for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = tx + 16 * j < L ? B(tx + 16 * j, l) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] += av[i] * bv[j];
+                    for (int j = 0; j < RT; ++j) acc[i][j] += av[i] * bv[j];
+            }
+        }
+        __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = ty + 16 * i, s = tx + 16 * j;
-            if (t < L && s < L) buf[t * kMaxW + s] = fin(t, s, acc[i][j]);
+        for (int j = 0; j < RT; ++j) {
+            const int t = RT * ty + i, s = RT * tx + j;
+            if (t < L && s < L) buf[t * BW + s] = fin(t, s, acc[i][j]);
         }
 }
 
-// acc[i][j] += sum_{s < K} M(t_i, s) X(s, col_j) for rows t_i = ty + 16i < L,
-// columns tx + 16j
-template <int NC, typename FM, typename FX>
-__device__ __forceinline__ void mm_acc_k(float (&acc)[8][NC], int L, int K, FM M, FX X) {
+// acc[i][j] += sum_{k<K} M(r_i, k) X(k, c_j) for rows r_i = RM*ty + i < nrows and
+// columns c_j = NC*tx + j (16*NC columns).  ROWFAST stages M with the row index
+// fastest (for M read as a transpose, M(r, k) = P[k][r]); else k fastest.
+template <int RM, int NC, bool ROWFAST, typename FM, typename FX>
+__device__ __forceinline__ void mm(float (&acc)[RM][NC], int nrows, int K, Stage &st, FM M, FX X) {
+    constexpr int NCOL = 16 * NC;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    for (int s = 0; s < K; ++s) {
-        float mv[8], xv[NC];
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        if constexpr (ROWFAST) {
+            for (int idx = tid; idx < nrows * KB; idx += kThreads) {
+                const int row = idx % nrows, kk = idx / nrows;
+                st.a[kk][row] = k0 + kk < K ? M(row, k0 + kk) : 0.0f;
+            }
+        } else {
+            for (int idx = tid; idx < nrows * KB; idx += kThreads) {
+                const int row = idx / KB, kk = idx % KB;
+                st.a[kk][row] = k0 + kk < K ? M(row, k0 + kk) : 0.0f;
+            }
+        }
+        for (int idx = tid; idx < KB * NCOL; idx += kThreads) {
+            const int kk = idx / NCOL, col = idx % NCOL;
+            st.b[kk][col] = k0 + kk < K ? X(k0 + kk, col) : 0.0f;
+        }
+        __syncthreads();
+        if (RM * ty < nrows) {
+#pragma unroll 4
+            for (int kk = 0; kk < KB; ++kk) {
+                float av[RM], xv[NC];
+                read_vec<RM>(&st.a[kk][RM * ty], av);
+                read_vec<NC>(&st.b[kk][NC * tx], xv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mv[i] = ty + 16 * i < L ? M(ty + 16 * i, s) : 0.0f;
+                for (int i = 0; i < RM; ++i)
 #pragma unroll
-        for (int j = 0; j < NC; ++j) xv[j] = X(s, tx + 16 * j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < NC; ++j) acc[i][j] += mv[i] * xv[j];
+                    for (int j = 0; j < NC; ++j) acc[i][j] += av[i] * xv[j];
+            }
+        }
+        __syncthreads();
     }
 }
 
-template <int NC, typename FM, typename FX>
-__device__ __forceinline__ void mm_acc(float (&acc)[8][NC], int L, FM M, FX X) {
-    mm_acc_k<NC>(acc, L, L, M, X);
-}
-
-template <int NC>
-__device__ __forceinline__ void store_rows(float *dst, int L, int width, const float (&acc)[8][NC]) {
+// dst[r][c] = acc for the rows and columns the thread owns in mm's layout
+template <int RM, int NC>
+__device__ __forceinline__ void store_tile(float *dst, int nrows, int width, const float (&acc)[RM][NC]) {
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = ty + 16 * i;
-        if (t < L) {
+    for (int i = 0; i < RM; ++i) {
+        const int r = RM * ty + i;
+        if (r < nrows) {
 #pragma unroll
-            for (int j = 0; j < NC; ++j) dst[static_cast<size_t>(t) * width + tx + 16 * j] = acc[i][j];
+            for (int j = 0; j < NC; ++j) dst[static_cast<size_t>(r) * width + NC * tx + j] = acc[i][j];
         }
     }
 }
@@ -252,11 +306,12 @@ __global__ __launch_bounds__(kThreads) void k_rprefix(BwdArgs a, RScan s0, RScan
 }
 
 // ---- W = (Gam o D_{g^2})^T Q + diag(eh^2)(V Gbn'^T + 1 gbd'^T), kept; T increment
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_bwd_w(BwdArgs a) {
-    constexpr int MA = D / 16;
-    __shared__ float buf[kMaxW * kMaxW];
+    constexpr int MA = D / 16, BW = 16 * RT;
+    __shared__ float buf[BW * kMaxW];  // Gam2 (stride BW), then W rows (stride D)
     __shared__ float gt[2 * kMaxW + 1];
+    __shared__ Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -269,61 +324,43 @@ __global__ __launch_bounds__(kThreads) void k_bwd_w(BwdArgs a) {
     const float *RGn = a.RG + sr * D * DV, *rgd = a.rg + sr * D;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     pow_table(gt, g, a.w);
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto ve = [&](int t, int l) { return Elem<T>::get(v, static_cast<size_t>(t) * DV + l); };
     // Gam2[t][s] = g^(2(t-s)) (gn_t . v_s + gd_t), s <= t
-    gram_to_lds<DV>(
-        buf, L, [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; },
-        [&](int s, int l) { return Elem<T>::get(v, static_cast<size_t>(s) * DV + l); },
-        [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * (x + (gd ? gd[t] : 0.0f)) : 0.0f; });
+    gram<RT, DV>(buf, BW, L, st, [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; }, ve,
+                 [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * (x + (gd ? gd[t] : 0.0f)) : 0.0f; });
     __syncthreads();
-    // W[s][a] = sum_{t >= s} Gam2[t][s] q_t[a]
-    float wacc[8][MA] = {};
-    mm_acc<MA>(wacc, L, [&](int s, int t) { return buf[t * kMaxW + s]; },
-               [&](int t, int col) { return Elem<T>::get(q, static_cast<size_t>(t) * D + col); });
-    // + eh_s^2 (Gbn' v_s + gbd')
-    mm_acc_k<MA>(wacc, L, DV, [&](int s, int l) { return gt[2 * (L - s)] * Elem<T>::get(v, static_cast<size_t>(s) * DV + l); },
-                 [&](int l, int col) { return RGn[col * DV + l]; });
+    // W[s][:] = sum_{t >= s} Gam2[t][s] q_t + eh_s^2 (Gbn' v_s + gbd')
+    float wacc[RT][MA] = {};
+    mm<RT, MA, true>(wacc, L, L, st, [&](int s, int t) { return buf[t * BW + s]; }, qe);
+    mm<RT, MA, false>(wacc, L, DV, st, [&](int s, int l) { return gt[2 * (L - s)] * ve(s, l); },
+                      [&](int l, int col) { return RGn[col * DV + l]; });
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int s = ty + 16 * i;
+    for (int i = 0; i < RT; ++i) {
+        const int s = RT * ty + i;
         if (s >= L) continue;
 #pragma unroll
-        for (int j = 0; j < MA; ++j) wacc[i][j] += gt[2 * (L - s)] * rgd[tx + 16 * j];
+        for (int j = 0; j < MA; ++j) wacc[i][j] += gt[2 * (L - s)] * rgd[MA * tx + j];
     }
-    __syncthreads();  // Gam2 reads done
     float *Wg = a.W + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
-    store_rows<MA>(Wg, L, D, wacc);
-    store_rows<MA>(buf, L, D, wacc);  // W rows, stride D
+    store_tile<RT, MA>(Wg, L, D, wacc);
+    store_tile<RT, MA>(buf, L, D, wacc);  // W rows, stride D (Gam2 reads ended in mm)
     __syncthreads();
     // T increment: sum_t g^t (w_t q_t^T + q_t w_t^T), d x d
     float tacc[MA][MA] = {};
-    for (int t = 0; t < L; ++t) {
-        const float wt = gt[t];
-        float wr[MA], qr[MA], wc[MA], qc[MA];
-#pragma unroll
-        for (int i = 0; i < MA; ++i) {
-            wr[i] = buf[t * D + ty + 16 * i];
-            qr[i] = Elem<T>::get(q, static_cast<size_t>(t) * D + ty + 16 * i);
-            wc[i] = buf[t * D + tx + 16 * i];
-            qc[i] = Elem<T>::get(q, static_cast<size_t>(t) * D + tx + 16 * i);
-        }
-#pragma unroll
-        for (int i = 0; i < MA; ++i)
-#pragma unroll
-            for (int j = 0; j < MA; ++j) tacc[i][j] += wt * (wr[i] * qc[j] + qr[i] * wc[j]);
-    }
-    float *Tc = a.T + slot(a, bh, c) * D * D;
-#pragma unroll
-    for (int i = 0; i < MA; ++i)
-#pragma unroll
-        for (int j = 0; j < MA; ++j) Tc[(ty + 16 * i) * D + tx + 16 * j] = tacc[i][j];
+    mm<MA, MA, true>(tacc, D, L, st, [&](int r, int t) { return gt[t] * buf[t * D + r]; }, qe);
+    mm<MA, MA, true>(tacc, D, L, st, [&](int r, int t) { return gt[t] * qe(t, r); },
+                     [&](int t, int col) { return buf[t * D + col]; });
+    store_tile<MA, MA>(a.T + slot(a, bh, c) * D * D, D, D, tacc);
 }
 
 // ---- dQ
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
-    constexpr int MA = D / 16;
-    __shared__ float buf[kMaxW * kMaxW];
+    constexpr int MA = D / 16, BW = 16 * RT;
+    __shared__ float buf[BW * BW];
     __shared__ float gt[2 * kMaxW + 1];
+    __shared__ Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -343,69 +380,66 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     pow_table(gt, g, a.w);
     auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto ke = [&](int t, int l) { return Elem<T>::get(k, static_cast<size_t>(t) * D + l); };
+    auto ve = [&](int t, int l) { return Elem<T>::get(v, static_cast<size_t>(t) * DV + l); };
+    auto gne = [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; };
     // Gam[t][s] = gn_t . v_s + gd_t for s <= t (no decay)
-    gram_to_lds<DV>(
-        buf, L, [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; },
-        [&](int s, int l) { return Elem<T>::get(v, static_cast<size_t>(s) * DV + l); },
-        [&](int t, int s, float x) { return s <= t ? x + (gd ? gd[t] : 0.0f) : 0.0f; });
+    gram<RT, DV>(buf, BW, L, st, gne, ve,
+                 [&](int t, int s, float x) { return s <= t ? x + (gd ? gd[t] : 0.0f) : 0.0f; });
     __syncthreads();
-    float acc[8][MA] = {};
+    float acc[RT][MA] = {};
     // (Gam o D_{g^2}) U
-    mm_acc<MA>(acc, L, [&](int t, int s) { return s <= t ? gt[2 * (t - s)] * buf[t * kMaxW + s] : 0.0f; },
-               [&](int s, int col) { return U[s * D + col]; });
+    mm<RT, MA, false>(acc, L, L, st, [&](int t, int s) { return s <= t ? gt[2 * (t - s)] * buf[t * BW + s] : 0.0f; },
+                      [&](int s, int col) { return U[s * D + col]; });
     if (lam != 0.0f) {  // lambda ((Gam o D_g) + (Gam o D_g)^T) Q
-        mm_acc<MA>(acc, L,
-                   [&](int t, int s) {
-                       float x = s <= t ? gt[t - s] * buf[t * kMaxW + s] : 0.0f;
-                       if (s >= t) x += gt[s - t] * buf[s * kMaxW + t];
-                       return lam * x;
-                   },
-                   qe);
+        mm<RT, MA, false>(acc, L, L, st,
+                          [&](int t, int s) {
+                              float x = s <= t ? gt[t - s] * buf[t * BW + s] : 0.0f;
+                              if (s >= t) x += gt[s - t] * buf[s * BW + t];
+                              return lam * x;
+                          },
+                          qe);
     }
     __syncthreads();  // Gam reads done
     // ((W K^T) o D_g o L) K
-    gram_to_lds<D>(
-        buf, L, [&](int t, int l) { return Wc[t * D + l]; },
-        [&](int s, int l) { return Elem<T>::get(k, static_cast<size_t>(s) * D + l); },
-        [&](int t, int s, float x) { return s <= t ? gt[t - s] * x : 0.0f; });
+    gram<RT, D>(buf, BW, L, st, [&](int t, int l) { return Wc[t * D + l]; }, ke,
+                [&](int t, int s, float x) { return s <= t ? gt[t - s] * x : 0.0f; });
     __syncthreads();
-    mm_acc<MA>(acc, L, [&](int t, int s) { return buf[t * kMaxW + s]; },
-               [&](int s, int col) { return Elem<T>::get(k, static_cast<size_t>(s) * D + col); });
+    mm<RT, MA, false>(acc, L, L, st, [&](int t, int s) { return buf[t * BW + s]; }, ke);
     // carries: e^2 (Gn X0^T + gd y0^T) + e W S0 + lambda [e (Gn C0^T + gd m0^T) + eh (V Cbn'^T + cbd')]
-    auto gne = [&](int t, int l) { return gn[static_cast<size_t>(t) * DV + l]; };
-    mm_acc_k<MA>(acc, L, DV, [&](int t, int l) { return gt[2 * (t + 1)] * gne(t, l); },
-                 [&](int l, int col) { return X0[col * DV + l]; });
-    mm_acc_k<MA>(acc, L, D, [&](int t, int b) { return gt[t + 1] * Wc[t * D + b]; },
-                 [&](int b, int col) { return S0[b * D + col]; });
+    mm<RT, MA, false>(acc, L, DV, st, [&](int t, int l) { return gt[2 * (t + 1)] * gne(t, l); },
+                      [&](int l, int col) { return X0[col * DV + l]; });
+    mm<RT, MA, false>(acc, L, D, st, [&](int t, int b) { return gt[t + 1] * Wc[t * D + b]; },
+                      [&](int b, int col) { return S0[b * D + col]; });
     if (lam != 0.0f) {
-        mm_acc_k<MA>(acc, L, DV, [&](int t, int l) { return lam * gt[t + 1] * gne(t, l); },
-                     [&](int l, int col) { return C0[col * DV + l]; });
-        mm_acc_k<MA>(acc, L, DV,
-                     [&](int t, int l) { return lam * gt[L - t] * Elem<T>::get(v, static_cast<size_t>(t) * DV + l); },
-                     [&](int l, int col) { return RCn[col * DV + l]; });
+        mm<RT, MA, false>(acc, L, DV, st, [&](int t, int l) { return lam * gt[t + 1] * gne(t, l); },
+                          [&](int l, int col) { return C0[col * DV + l]; });
+        mm<RT, MA, false>(acc, L, DV, st, [&](int t, int l) { return lam * gt[L - t] * ve(t, l); },
+                          [&](int l, int col) { return RCn[col * DV + l]; });
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = ty + 16 * i;
+    for (int i = 0; i < RT; ++i) {
+        const int t = RT * ty + i;
         if (t >= L) continue;
         const float e = gt[t + 1], eh = gt[L - t], gdt = gd ? gd[t] : 0.0f;
 #pragma unroll
         for (int j = 0; j < MA; ++j) {
-            const int col = tx + 16 * j;
+            const int col = MA * tx + j;
             float x = e * e * gdt * y0[col];
             if (lam != 0.0f) x += lam * (e * gdt * m0[col] + eh * rcd[col]);
             acc[i][j] += x;
         }
     }
-    store_rows<MA>(a.gq + tok * D, L, D, acc);
+    store_tile<RT, MA>(a.gq + tok * D, L, D, acc);
 }
 
 // ---- dK = ((K Q^T) o Mu) W + ((K W^T) o Mu) Q + diag(eh) K T'
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_bwd_dk(BwdArgs a) {
-    constexpr int MA = D / 16;
-    __shared__ float buf[kMaxW * kMaxW];
+    constexpr int MA = D / 16, BW = 16 * RT;
+    __shared__ float buf[BW * BW];
     __shared__ float gt[2 * kMaxW + 1];
+    __shared__ Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -414,31 +448,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dk(BwdArgs a) {
     const T *k = static_cast<const T *>(a.k) + tok * D;
     const float *Wc = a.W + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
     const float *Tr = a.T + slot(a, bh, c + 1) * D * D;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     pow_table(gt, g, a.w);
     auto ke = [&](int t, int l) { return Elem<T>::get(k, static_cast<size_t>(t) * D + l); };
     auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
     auto we = [&](int t, int l) { return Wc[t * D + l]; };
     auto upper = [&](int t, int s, float x) { return s >= t ? gt[s - t] * x : 0.0f; };
-    float acc[8][MA] = {};
-    gram_to_lds<D>(buf, L, ke, qe, upper);
+    float acc[RT][MA] = {};
+    gram<RT, D>(buf, BW, L, st, ke, qe, upper);
     __syncthreads();
-    mm_acc<MA>(acc, L, [&](int t, int s) { return buf[t * kMaxW + s]; }, we);
+    mm<RT, MA, false>(acc, L, L, st, [&](int t, int s) { return buf[t * BW + s]; }, we);
     __syncthreads();
-    gram_to_lds<D>(buf, L, ke, we, upper);
+    gram<RT, D>(buf, BW, L, st, ke, we, upper);
     __syncthreads();
-    mm_acc<MA>(acc, L, [&](int t, int s) { return buf[t * kMaxW + s]; }, qe);
-    mm_acc_k<MA>(acc, L, D, [&](int t, int b) { return gt[L - t] * ke(t, b); },
-                 [&](int b, int col) { return Tr[b * D + col]; });
-    store_rows<MA>(a.gk + tok * D, L, D, acc);
+    mm<RT, MA, false>(acc, L, L, st, [&](int t, int s) { return buf[t * BW + s]; }, qe);
+    mm<RT, MA, false>(acc, L, D, st, [&](int t, int b) { return gt[L - t] * ke(t, b); },
+                      [&](int b, int col) { return Tr[b * D + col]; });
+    store_tile<RT, MA>(a.gk + tok * D, L, D, acc);
 }
 
 // ---- dV = P^T Gn + diag(eh^2) U Gbn' + lambda diag(eh) Q Cbn'
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
-    constexpr int MC = DV / 16;
-    __shared__ float buf[kMaxW * kMaxW];
+    constexpr int MC = DV / 16, BW = 16 * RT;
+    __shared__ float buf[BW * BW];
     __shared__ float gt[2 * kMaxW + 1];
+    __shared__ Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -449,45 +483,26 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
     const float *U = a.U + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
     const size_t sr = slot(a, bh, c + 1);
     const float *RGn = a.RG + sr * D * DV, *RCn = a.RC + sr * D * DV;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     pow_table(gt, g, a.w);
     auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
     // P[t][s] = g^(2(t-s)) (q_t . u_s) + lambda g^(t-s) (q_t . q_s), s <= t
-    gram_to_lds<D>(
-        buf, L, qe, [&](int s, int l) { return U[s * D + l]; },
-        [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * x : 0.0f; });
+    gram<RT, D>(buf, BW, L, st, qe, [&](int s, int l) { return U[s * D + l]; },
+                [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * x : 0.0f; });
     __syncthreads();
-    if (lam != 0.0f) {  // add the ridge part in place (each entry is owned by one thread)
-        float acc[8][8] = {};
-        for (int l = 0; l < D; ++l) {
-            float av[8], bv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) av[i] = ty + 16 * i < L ? qe(ty + 16 * i, l) : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bv[j] = tx + 16 * j < L ? qe(tx + 16 * j, l) : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] += av[i] * bv[j];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = ty + 16 * i, s = tx + 16 * j;
-                if (t < L && s <= t) buf[t * kMaxW + s] += lam * gt[t - s] * acc[i][j];
-            }
+    if (lam != 0.0f) {  // add the ridge part (each entry is read and written by its owner)
+        gram<RT, D>(buf, BW, L, st, qe, qe,
+                    [&](int t, int s, float x) { return s <= t ? buf[t * BW + s] + lam * gt[t - s] * x : 0.0f; });
         __syncthreads();
     }
-    float acc[8][MC] = {};
-    mm_acc<MC>(acc, L, [&](int s, int t) { return buf[t * kMaxW + s]; },
-               [&](int t, int col) { return gn[static_cast<size_t>(t) * DV + col]; });
-    mm_acc_k<MC>(acc, L, D, [&](int s, int l) { return gt[2 * (L - s)] * U[s * D + l]; },
-                 [&](int l, int col) { return RGn[l * DV + col]; });
+    float acc[RT][MC] = {};
+    mm<RT, MC, true>(acc, L, L, st, [&](int s, int t) { return buf[t * BW + s]; },
+                     [&](int t, int col) { return gn[static_cast<size_t>(t) * DV + col]; });
+    mm<RT, MC, false>(acc, L, D, st, [&](int s, int l) { return gt[2 * (L - s)] * U[s * D + l]; },
+                      [&](int l, int col) { return RGn[l * DV + col]; });
     if (lam != 0.0f)
-        mm_acc_k<MC>(acc, L, D, [&](int s, int l) { return lam * gt[L - s] * qe(s, l); },
-                     [&](int l, int col) { return RCn[l * DV + col]; });
-    store_rows<MC>(a.gv + tok * DV, L, DV, acc);
+        mm<RT, MC, false>(acc, L, D, st, [&](int s, int l) { return lam * gt[L - s] * qe(s, l); },
+                          [&](int l, int col) { return RCn[l * DV + col]; });
+    store_tile<RT, MC>(a.gv + tok * DV, L, DV, acc);
 }
 
 template <typename T, int D, int DV>
@@ -503,11 +518,22 @@ hipError_t launch_bwd(const BwdArgs &a, int BH, hipStream_t st) {
     hipLaunchKernelGGL(k_rprefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sG, sg, 2);
     if (a.ridge != 0.0f)
         hipLaunchKernelGGL(k_rprefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sC, sc, 1);
-    hipLaunchKernelGGL((k_bwd_w<T, D, DV>), grid, blk, 0, st, a);
+    // register tile: 4 x 4 per thread for chunks up to 64 tokens, 8 x 8 for 128
+    if (a.w > 64) {
+        hipLaunchKernelGGL((k_bwd_w<T, D, DV, 8>), grid, blk, 0, st, a);
+    } else {
+        hipLaunchKernelGGL((k_bwd_w<T, D, DV, 4>), grid, blk, 0, st, a);
+    }
     hipLaunchKernelGGL(k_rprefix, dim3((D * D + kThreads - 1) / kThreads, BH), blk, 0, st, a, sT, none, 1);
-    hipLaunchKernelGGL((k_bwd_dq<T, D, DV>), grid, blk, 0, st, a);
-    hipLaunchKernelGGL((k_bwd_dk<T, D, DV>), grid, blk, 0, st, a);
-    hipLaunchKernelGGL((k_bwd_dv<T, D, DV>), grid, blk, 0, st, a);
+    if (a.w > 64) {
+        hipLaunchKernelGGL((k_bwd_dq<T, D, DV, 8>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_bwd_dk<T, D, DV, 8>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_bwd_dv<T, D, DV, 8>), grid, blk, 0, st, a);
+    } else {
+        hipLaunchKernelGGL((k_bwd_dq<T, D, DV, 4>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_bwd_dk<T, D, DV, 4>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_bwd_dv<T, D, DV, 4>), grid, blk, 0, st, a);
+    }
     return hipGetLastError();
 }
 
