@@ -37,12 +37,17 @@
 //   k_bwd_dq, k_bwd_dk, k_bwd_dv
 #include "device_common.h"
 #include "hla_internal.h"
+#include "tile_fp32.h"
 
 namespace hla {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxW = 128;
+constexpr int kThreads = tile::kThreads;
+constexpr int kMaxW = tile::kMaxW;
+using tile::gram;
+using tile::mm;
+using tile::Stage;
+using tile::store_tile;
 
 struct BwdArgs {
     int H, n, d, dv, w, nc;
@@ -68,122 +73,6 @@ __device__ __forceinline__ size_t slot(const BwdArgs &a, int bh, int c) {
 __device__ __forceinline__ void pow_table(float *gt, float g, int w) {
     for (int k = threadIdx.x; k <= 2 * w; k += kThreads) gt[k] = gpow(g, k);
     __syncthreads();
-}
-
-// Products are formed from LDS: operands are staged in k-blocks of KB,
-// transposed ([k][row], rows padded by 4 floats), and every thread owns a
-// contiguous block of output rows (RM per thread, rows RM*ty ..) and columns
-// (NC per thread, columns NC*tx ..), so its operand reads are 16-byte vectors.
-constexpr int KB = 16;
-constexpr int kStageW = kMaxW + 4;
-
-struct alignas(16) Stage {
-    float a[KB][kStageW];
-    float b[KB][kStageW];
-};
-
-template <int N>
-__device__ __forceinline__ void read_vec(const float *p, float (&v)[N]) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(p + i);
-            v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) v[i] = p[i];
-    }
-}
-
-// buf[t][s] (row stride BW) = fin(t, s, sum_{l<K} A(t, l) B(s, l)) for t, s < L;
-// thread (ty, tx) forms rows RT*ty .. and columns RT*tx .. (RT*16 >= L).
-template <int RT, int K, typename FA, typename FB, typename FF>
-__device__ __forceinline__ void gram(float *buf, int BW, int L, Stage &st, FA A, FB B, FF fin) {
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    float acc[RT][RT] = {};
-    for (int l0 = 0; l0 < K; l0 += KB) {
-        for (int idx = tid; idx < L * KB; idx += kThreads) {  // k fastest: row-major operands
-            const int row = idx / KB, kk = idx % KB;
-            st.a[kk][row] = A(row, l0 + kk);
-            st.b[kk][row] = B(row, l0 + kk);
-        }
-        __syncthreads();
-        if (RT * ty < L && RT * tx < L) {
-#pragma unroll 4
-            for (int kk = 0; kk < KB; ++kk) {
-                float av[RT], bv[RT];
-                read_vec<RT>(&st.a[kk][RT * ty], av);
-                read_vec<RT>(&st.b[kk][RT * tx], bv);
-#pragma unroll
-                for (int i = 0; i < RT; ++i)
-#pragma unroll
-                    for (int j = 0; j < RT; ++j) acc[i][j] += av[i] * bv[j];
-            }
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-            const int t = RT * ty + i, s = RT * tx + j;
-            if (t < L && s < L) buf[t * BW + s] = fin(t, s, acc[i][j]);
-        }
-}
-
-// acc[i][j] += sum_{k<K} M(r_i, k) X(k, c_j) for rows r_i = RM*ty + i < nrows and
-// columns c_j = NC*tx + j (16*NC columns).  ROWFAST stages M with the row index
-// fastest (for M read as a transpose, M(r, k) = P[k][r]); else k fastest.
-template <int RM, int NC, bool ROWFAST, typename FM, typename FX>
-__device__ __forceinline__ void mm(float (&acc)[RM][NC], int nrows, int K, Stage &st, FM M, FX X) {
-    constexpr int NCOL = 16 * NC;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    for (int k0 = 0; k0 < K; k0 += KB) {
-        if constexpr (ROWFAST) {
-            for (int idx = tid; idx < nrows * KB; idx += kThreads) {
-                const int row = idx % nrows, kk = idx / nrows;
-                st.a[kk][row] = k0 + kk < K ? M(row, k0 + kk) : 0.0f;
-            }
-        } else {
-            for (int idx = tid; idx < nrows * KB; idx += kThreads) {
-                const int row = idx / KB, kk = idx % KB;
-                st.a[kk][row] = k0 + kk < K ? M(row, k0 + kk) : 0.0f;
-            }
-        }
-        for (int idx = tid; idx < KB * NCOL; idx += kThreads) {
-            const int kk = idx / NCOL, col = idx % NCOL;
-            st.b[kk][col] = k0 + kk < K ? X(k0 + kk, col) : 0.0f;
-        }
-        __syncthreads();
-        if (RM * ty < nrows) {
-#pragma unroll 4
-            for (int kk = 0; kk < KB; ++kk) {
-                float av[RM], xv[NC];
-                read_vec<RM>(&st.a[kk][RM * ty], av);
-                read_vec<NC>(&st.b[kk][NC * tx], xv);
-#pragma unroll
-                for (int i = 0; i < RM; ++i)
-#pragma unroll
-                    for (int j = 0; j < NC; ++j) acc[i][j] += av[i] * xv[j];
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// dst[r][c] = acc for the rows and columns the thread owns in mm's layout
-template <int RM, int NC>
-__device__ __forceinline__ void store_tile(float *dst, int nrows, int width, const float (&acc)[RM][NC]) {
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-#pragma unroll
-    for (int i = 0; i < RM; ++i) {
-        const int r = RM * ty + i;
-        if (r < nrows) {
-#pragma unroll
-            for (int j = 0; j < NC; ++j) dst[static_cast<size_t>(r) * width + NC * tx + j] = acc[i][j];
-        }
-    }
 }
 
 // ---- ratio: Gn = dout / den, gd = -(dout . out) / den, one thread per token

@@ -33,12 +33,13 @@
 // Everything is fp32; bf16 inputs are widened exactly on load.
 #include "device_common.h"
 #include "hla_internal.h"
+#include "tile_fp32.h"
 
 namespace hla {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxW = 128;
+constexpr int kThreads = tile::kThreads;
+constexpr int kMaxW = tile::kMaxW;
 
 struct Slots {
     float *S, *C, *m, *X, *y;  // [BH][nc+1][...]: slot c = state before chunk c
@@ -211,11 +212,14 @@ __global__ __launch_bounds__(kThreads) void k_prefix(GenArgs a, ScanSeg s0, Scan
     }
 }
 
-template <typename T, int D, int DV>
+// A, U (kept for the output pass), Z = U^T diag(f^2) V and z = U^T f^2 of chunk c
+// (products from LDS, tile_fp32.h; RT x RT register tiles, 16 RT >= w)
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_chunk_uz(GenArgs a) {
-    constexpr int MC = D / 16, MZ = DV / 16, MA = D / 16;
-    __shared__ float buf[kMaxW * kMaxW];  // A (L x L, stride kMaxW), then U (L x D)
-    __shared__ float es[kMaxW], f2s[kMaxW];
+    constexpr int MC = D / 16, MZ = DV / 16, BW = 16 * RT;
+    __shared__ float buf[BW * kMaxW];  // A (L x L, stride BW), then U rows (stride D)
+    __shared__ float gt[2 * kMaxW + 1];
+    __shared__ tile::Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -224,124 +228,43 @@ __global__ __launch_bounds__(kThreads) void k_chunk_uz(GenArgs a) {
     const T *k = static_cast<const T *>(a.k) + tok * D;
     const T *v = static_cast<const T *>(a.v) + tok * DV;
     const float *S0 = a.ws.S + slot_index(a, bh, c) * D * D;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    if (tid < L) {
-        es[tid] = gpow(g, tid + 1);
-        const float f = gpow(g, L - 1 - tid);
-        f2s[tid] = f * f;
-    }
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= 2 * a.w; i += kThreads) gt[i] = gpow(g, i);
+    __syncthreads();
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto ke = [&](int t, int l) { return Elem<T>::get(k, static_cast<size_t>(t) * D + l); };
+    auto ve = [&](int t, int l) { return Elem<T>::get(v, static_cast<size_t>(t) * DV + l); };
     // A[t][s] = g^(t-s) (q_t . k_s) for s <= t
-    {
-        float acc[8][8] = {};
-        for (int l = 0; l < D; ++l) {
-            float qa[8], kb[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = ty + 16 * i;
-                qa[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int s = tx + 16 * j;
-                kb[j] = s < L ? Elem<T>::get(k, static_cast<size_t>(s) * D + l) : 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] += qa[i] * kb[j];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = ty + 16 * i, s = tx + 16 * j;
-                if (t < L && s < L) buf[t * kMaxW + s] = (s <= t) ? gpow(g, t - s) * acc[i][j] : 0.0f;
-            }
-    }
+    tile::gram<RT, D>(buf, BW, L, st, qe, ke, [&](int t, int s, float x) { return s <= t ? gt[t - s] * x : 0.0f; });
     __syncthreads();
-    // U[t][:] = e_t (S0 q_t) + sum_{s<=t} A[t][s] k_s
-    float u[8][MC] = {};
-    for (int l = 0; l < D; ++l) {
-        float qa[8], sb[MC];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = ty + 16 * i;
-            qa[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < MC; ++j) sb[j] = S0[l * D + tx + 16 * j];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < MC; ++j) u[i][j] += qa[i] * sb[j];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = ty + 16 * i;
-        const float e = t < L ? es[t] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < MC; ++j) u[i][j] *= e;
-    }
-    for (int s = 0; s < L; ++s) {
-        float av[8], kv[MC];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = ty + 16 * i;
-            av[i] = t < L ? buf[t * kMaxW + s] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < MC; ++j) kv[j] = Elem<T>::get(k, static_cast<size_t>(s) * D + tx + 16 * j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < MC; ++j) u[i][j] += av[i] * kv[j];
-    }
-    __syncthreads();  // A no longer needed
+    // U[t][:] = e_t (S0 q_t) + sum_{s<=t} A[t][s] k_s, e_t = g^(t+1)
+    float u[RT][MC] = {};
+    tile::mm<RT, MC, false>(u, L, D, st, [&](int t, int l) { return gt[t + 1] * qe(t, l); },
+                            [&](int l, int col) { return S0[l * D + col]; });
+    tile::mm<RT, MC, false>(u, L, L, st, [&](int t, int s) { return buf[t * BW + s]; }, ke);
     float *Ug = a.ws.U + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = ty + 16 * i;
-        if (t < L) {
-#pragma unroll
-            for (int j = 0; j < MC; ++j) {
-                buf[t * D + tx + 16 * j] = u[i][j];
-                Ug[t * D + tx + 16 * j] = u[i][j];
-            }
-        }
-    }
+    tile::store_tile<RT, MC>(Ug, L, D, u);
+    tile::store_tile<RT, MC>(buf, L, D, u);  // the A reads ended inside mm
     __syncthreads();
-    // Z = U^T diag(f^2) V, z = U^T f^2
-    float z[MA][MZ] = {};
-    for (int s = 0; s < L; ++s) {
-        const float f2 = f2s[s];
-        float ur[MA], vc[MZ];
-#pragma unroll
-        for (int i = 0; i < MA; ++i) ur[i] = f2 * buf[s * D + ty + 16 * i];
-#pragma unroll
-        for (int j = 0; j < MZ; ++j) vc[j] = Elem<T>::get(v, static_cast<size_t>(s) * DV + tx + 16 * j);
-#pragma unroll
-        for (int i = 0; i < MA; ++i)
-#pragma unroll
-            for (int j = 0; j < MZ; ++j) z[i][j] += ur[i] * vc[j];
-    }
+    // Z = U^T diag(f^2) V, f_s^2 = g^(2(L-1-s)); z = U^T f^2
+    float z[MC][MZ] = {};
+    tile::mm<MC, MZ, true>(z, D, L, st, [&](int r, int s) { return gt[2 * (L - 1 - s)] * buf[s * D + r]; }, ve);
     const size_t sl = slot_index(a, bh, c + 1);
-    float *X = a.ws.X + sl * D * DV, *y = a.ws.y + sl * D;
-#pragma unroll
-    for (int i = 0; i < MA; ++i)
-#pragma unroll
-        for (int j = 0; j < MZ; ++j) X[(ty + 16 * i) * DV + tx + 16 * j] = z[i][j];
+    tile::store_tile<MC, MZ>(a.ws.X + sl * D * DV, D, DV, z);
     if (tid < D) {
         float acc = 0.0f;
-        for (int s = 0; s < L; ++s) acc += f2s[s] * buf[s * D + tid];
-        y[tid] = acc;
+        for (int s = 0; s < L; ++s) acc += gt[2 * (L - 1 - s)] * buf[s * D + tid];
+        a.ws.y[sl * D + tid] = acc;
     }
 }
 
-template <typename T, int D, int DV>
+// P, num, den and the ratio of chunk c (products from LDS, tile_fp32.h)
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
-    constexpr int MC = DV / 16;
-    __shared__ float P[kMaxW * kMaxW];
-    __shared__ float es[kMaxW], dens[kMaxW];
+    constexpr int MC = DV / 16, BW = 16 * RT, PS = BW + 1;  // odd stride: row walks hit distinct banks
+    __shared__ float P[BW * PS];
+    __shared__ float gt[2 * kMaxW + 1], dens[kMaxW];
+    __shared__ tile::Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -354,122 +277,53 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
     const float *X0 = a.ws.X + sl * D * DV, *C0 = a.ws.C + sl * D * DV;
     const float *y0 = a.ws.y + sl * D, *m0 = a.ws.m + sl * D;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    if (tid < L) es[tid] = gpow(g, tid + 1);
+    for (int i = tid; i <= 2 * a.w; i += kThreads) gt[i] = gpow(g, i);
+    __syncthreads();
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto ve = [&](int t, int l) { return Elem<T>::get(v, static_cast<size_t>(t) * DV + l); };
     // P[t][s] = g^(2(t-s)) (q_t . u_s) + lambda g^(t-s) (q_t . q_s), s <= t
-    {
-        float ap[8][8] = {}, ar[8][8] = {};
-        for (int l = 0; l < D; ++l) {
-            float qa[8], ub[8], qb[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = ty + 16 * i;
-                qa[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int s = tx + 16 * j;
-                ub[j] = s < L ? U[s * D + l] : 0.0f;
-                qb[j] = s < L ? Elem<T>::get(q, static_cast<size_t>(s) * D + l) : 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    ap[i][j] += qa[i] * ub[j];
-                    ar[i][j] += qa[i] * qb[j];
-                }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = ty + 16 * i, s = tx + 16 * j;
-                if (t < L && s < L) {
-                    float p = 0.0f;
-                    if (s <= t) {
-                        const float dg = gpow(g, t - s);
-                        p = dg * dg * ap[i][j] + lam * dg * ar[i][j];
-                    }
-                    P[t * kMaxW + s] = p;
-                }
-            }
+    tile::gram<RT, D>(P, PS, L, st, qe, [&](int s, int l) { return U[s * D + l]; },
+                      [&](int t, int s, float x) { return s <= t ? gt[2 * (t - s)] * x : 0.0f; });
+    if (lam != 0.0f) {  // each entry is read and written by the thread that owns it
+        __syncthreads();
+        tile::gram<RT, D>(P, PS, L, st, qe, qe,
+                          [&](int t, int s, float x) { return s <= t ? P[t * PS + s] + lam * gt[t - s] * x : 0.0f; });
     }
     __syncthreads();
     // den_t = sum_s P[t][s] + e_t^2 (q_t . y0) + lambda e_t (q_t . m0)
     if (tid < L) {
         const int t = tid;
         float ps = 0.0f, qy = 0.0f, qm = 0.0f;
-        for (int s = 0; s <= t; ++s) ps += P[t * kMaxW + s];
+        for (int s = 0; s <= t; ++s) ps += P[t * PS + s];
         for (int l = 0; l < D; ++l) {
-            const float ql = Elem<T>::get(q, static_cast<size_t>(t) * D + l);
+            const float ql = qe(t, l);
             qy += ql * y0[l];
             qm += ql * m0[l];
         }
-        const float e = es[t];
+        const float e = gt[t + 1];
         const float dn = ps + e * e * qy + lam * e * qm;
         dens[t] = dn;
         if (a.den) a.den[tok + t] = dn;
     }
     __syncthreads();
-    // num = P V + diag(e^2) Q X0 + lambda diag(e) Q C0; the row scales are
-    // folded into the loaded q values so one accumulator serves all three.
-    float acc[8][MC] = {};
-    for (int s = 0; s < L; ++s) {
-        float pa[8], vb[MC];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = ty + 16 * i;
-            pa[i] = t < L ? P[t * kMaxW + s] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < MC; ++j) vb[j] = Elem<T>::get(v, static_cast<size_t>(s) * DV + tx + 16 * j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < MC; ++j) acc[i][j] += pa[i] * vb[j];
-    }
-    float e2[8], le[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = ty + 16 * i;
-        const float e = t < L ? es[t] : 0.0f;
-        e2[i] = e * e;
-        le[i] = lam * e;
-    }
-    for (int l = 0; l < D; ++l) {
-        float qx[8], xb[MC];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = ty + 16 * i;
-            qx[i] = t < L ? Elem<T>::get(q, static_cast<size_t>(t) * D + l) : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < MC; ++j) xb[j] = X0[l * DV + tx + 16 * j];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < MC; ++j) acc[i][j] += (e2[i] * qx[i]) * xb[j];
-        if (lam != 0.0f) {
-            float cb[MC];
-#pragma unroll
-            for (int j = 0; j < MC; ++j) cb[j] = C0[l * DV + tx + 16 * j];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < MC; ++j) acc[i][j] += (le[i] * qx[i]) * cb[j];
-        }
-    }
+    // num = P V + diag(e^2) Q X0 + lambda diag(e) Q C0
+    float acc[RT][MC] = {};
+    tile::mm<RT, MC, false>(acc, L, L, st, [&](int t, int s) { return P[t * PS + s]; }, ve);
+    tile::mm<RT, MC, false>(acc, L, D, st, [&](int t, int l) { return gt[2 * (t + 1)] * qe(t, l); },
+                            [&](int l, int col) { return X0[l * DV + col]; });
+    if (lam != 0.0f)
+        tile::mm<RT, MC, false>(acc, L, D, st, [&](int t, int l) { return lam * gt[t + 1] * qe(t, l); },
+                                [&](int l, int col) { return C0[l * DV + col]; });
     float *out = a.out + tok * DV;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = ty + 16 * i;
-        if (t < L) {
-            const float dn = dens[t];
+    for (int i = 0; i < RT; ++i) {
+        const int t = RT * ty + i;
+        if (t >= L) continue;
+        const float dn = dens[t];
 #pragma unroll
-            for (int j = 0; j < MC; ++j) {
-                const float num = acc[i][j];
-                out[static_cast<size_t>(t) * DV + tx + 16 * j] = a.normalize ? num / dn : num;
-            }
+        for (int j = 0; j < MC; ++j) {
+            const float num = acc[i][j];
+            out[static_cast<size_t>(t) * DV + MC * tx + j] = a.normalize ? num / dn : num;
         }
     }
 }
@@ -506,12 +360,18 @@ hipError_t launch_all(const GenArgs &a, int BH, hipStream_t st) {
         const int e1 = D * D + D * DV + D;
         hipLaunchKernelGGL(k_prefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sS, sC,
                            sm, 1);
-        hipLaunchKernelGGL((k_chunk_uz<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
+        if (a.w > 64)
+            hipLaunchKernelGGL((k_chunk_uz<T, D, DV, 8>), dim3(a.nc, BH), blk, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_chunk_uz<T, D, DV, 4>), dim3(a.nc, BH), blk, 0, st, a);
         const ScanSeg sX{a.ws.X, D * DV}, sy{a.ws.y, D}, none{nullptr, 0};
         const int e2 = D * DV + D;
         hipLaunchKernelGGL(k_prefix, dim3((e2 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sX, sy,
                            none, 2);
-        hipLaunchKernelGGL((k_chunk_out<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
+        if (a.w > 64)
+            hipLaunchKernelGGL((k_chunk_out<T, D, DV, 8>), dim3(a.nc, BH), blk, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_chunk_out<T, D, DV, 4>), dim3(a.nc, BH), blk, 0, st, a);
     }
     if (a.fin.S) hipLaunchKernelGGL((k_final<D, DV>), dim3(BH), blk, 0, st, a);
     return hipGetLastError();
