@@ -96,59 +96,41 @@ __global__ __launch_bounds__(kThreads) void k_bwd_prep(BwdArgs a, size_t tokens)
 // right-slot array
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_bwd_sums(BwdArgs a) {
-    constexpr int TB = 32, MR = D / 16, MC = DV / 16;
-    __shared__ float qs[TB][D], gs[TB][DV], w2s[TB], w1s[TB], gds[TB];
+    constexpr int MR = D / 16, MC = DV / 16;
+    __shared__ float gt[2 * kMaxW + 1];
+    __shared__ Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
     const size_t tok = static_cast<size_t>(bh) * a.n + s0;
     const T *q = static_cast<const T *>(a.q) + tok * D;
     const float *gn = a.Gn + tok * DV;
+    const float *gd = a.gd ? a.gd + tok : nullptr;
     const bool ridge = a.ridge != 0.0f;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    float aG[MR][MC] = {}, aC[MR][MC] = {}, ag = 0.0f, ac = 0.0f;
-    for (int b0 = 0; b0 < L; b0 += TB) {
-        const int nb = min(TB, L - b0);
-        for (int i = tid; i < nb * D; i += kThreads) qs[i / D][i % D] = Elem<T>::get(q, static_cast<size_t>(b0) * D + i);
-        for (int i = tid; i < nb * DV; i += kThreads) gs[i / DV][i % DV] = gn[static_cast<size_t>(b0) * DV + i];
-        if (tid < nb) {
-            w2s[tid] = gpow(g, 2 * (b0 + tid));
-            w1s[tid] = gpow(g, b0 + tid);
-            gds[tid] = a.gd ? a.gd[tok + b0 + tid] : 0.0f;
-        }
-        __syncthreads();
-        for (int s = 0; s < nb; ++s) {
-            float qr[MR], gc[MC];
-#pragma unroll
-            for (int i = 0; i < MR; ++i) qr[i] = qs[s][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < MC; ++j) gc[j] = gs[s][tx + 16 * j];
-            const float w2 = w2s[s], w1 = w1s[s];
-#pragma unroll
-            for (int i = 0; i < MR; ++i)
-#pragma unroll
-                for (int j = 0; j < MC; ++j) {
-                    aG[i][j] += w2 * (qr[i] * gc[j]);
-                    if (ridge) aC[i][j] += w1 * (qr[i] * gc[j]);
-                }
-            if (tid < D) {
-                ag += w2 * (qs[s][tid] * gds[s]);
-                if (ridge) ac += w1 * (qs[s][tid] * gds[s]);
+    const int tid = threadIdx.x;
+    pow_table(gt, g, a.w);
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto gne = [&](int t, int col) { return gn[static_cast<size_t>(t) * DV + col]; };
+    const size_t sl = slot(a, bh, c);
+    {
+        float aG[MR][MC] = {};
+        mm<MR, MC, true>(aG, D, L, st, [&](int r, int t) { return gt[2 * t] * qe(t, r); }, gne);
+        store_tile<MR, MC>(a.RG + sl * D * DV, D, DV, aG);
+    }
+    if (ridge) {
+        float aC[MR][MC] = {};
+        mm<MR, MC, true>(aC, D, L, st, [&](int r, int t) { return gt[t] * qe(t, r); }, gne);
+        store_tile<MR, MC>(a.RC + sl * D * DV, D, DV, aC);
+    }
+    if (tid < D) {
+        float ag = 0.0f, ac = 0.0f;
+        if (gd) {
+            for (int t = 0; t < L; ++t) {
+                const float x = qe(t, tid) * gd[t];
+                ag += gt[2 * t] * x;
+                ac += gt[t] * x;
             }
         }
-        __syncthreads();
-    }
-    const size_t sl = slot(a, bh, c);
-    float *RG = a.RG + sl * D * DV, *RC = a.RC + sl * D * DV;
-#pragma unroll
-    for (int i = 0; i < MR; ++i)
-#pragma unroll
-        for (int j = 0; j < MC; ++j) {
-            const int o = (ty + 16 * i) * DV + tx + 16 * j;
-            RG[o] = aG[i][j];
-            if (ridge) RC[o] = aC[i][j];
-        }
-    if (tid < D) {
         a.rg[sl * D + tid] = ag;
         if (ridge) a.rc[sl * D + tid] = ac;
     }
@@ -187,7 +169,19 @@ __global__ __launch_bounds__(kThreads) void k_rprefix(BwdArgs a, RScan s0, RScan
     const float rf = gpow(g, power * a.w), rl = gpow(g, power * Llast);
     float *p = sg.base + static_cast<size_t>(bh) * (a.nc + 1) * sg.E + e;
     float run = p[static_cast<size_t>(a.nc) * sg.E];
-    for (int c = a.nc - 1; c >= 0; --c) {
+    // eight slot loads in flight per step (the scan itself is serial)
+    int c = a.nc - 1;
+    for (; c >= 7; c -= 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p[static_cast<size_t>(c - u) * sg.E];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            run = (c - u == a.nc - 1 ? rl : rf) * run + x[u];
+            p[static_cast<size_t>(c - u) * sg.E] = run;
+        }
+    }
+    for (; c >= 0; --c) {
         float *sl = p + static_cast<size_t>(c) * sg.E;
         run = (c == a.nc - 1 ? rl : rf) * run + *sl;
         *sl = run;

@@ -117,10 +117,15 @@ __global__ __launch_bounds__(kThreads) void k_init_slot(GenArgs a) {
     s_times_c_minus<D, DV>(iS, iC, iG, X, im, ih, y);
 }
 
+// K^T diag(f) K, Q^T diag(f) V and Q^T f of chunk c -> slot c+1 (products from
+// LDS, tile_fp32.h).  The key moment is formed from sqrt(f_s) k_s on both
+// sides: fma(x_a, x_b, acc) is the same operation for (a, b) and (b, a), so
+// the moment (and every prefix of it) is exactly symmetric.
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_chunk_sums(GenArgs a) {
-    constexpr int TB = 32, MR = D / 16, MC = DV / 16;
-    __shared__ float ks[TB][D], qs[TB][D], vs[TB][DV], fs[TB];
+    constexpr int MR = D / 16, MC = DV / 16;
+    __shared__ float fs[kMaxW], hs[kMaxW];  // f_s = g^(L-1-s) and sqrt(f_s)
+    __shared__ tile::Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -128,52 +133,30 @@ __global__ __launch_bounds__(kThreads) void k_chunk_sums(GenArgs a) {
     const T *q = static_cast<const T *>(a.q) + tok * D;
     const T *k = static_cast<const T *>(a.k) + tok * D;
     const T *v = static_cast<const T *>(a.v) + tok * DV;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    float aS[MR][MR] = {}, aC[MR][MC] = {}, am = 0.0f;
-    for (int b0 = 0; b0 < L; b0 += TB) {
-        const int nb = min(TB, L - b0);
-        for (int i = tid; i < nb * D; i += kThreads) {
-            ks[i / D][i % D] = Elem<T>::get(k, static_cast<size_t>(b0) * D + i);
-            qs[i / D][i % D] = Elem<T>::get(q, static_cast<size_t>(b0) * D + i);
-        }
-        for (int i = tid; i < nb * DV; i += kThreads)
-            vs[i / DV][i % DV] = Elem<T>::get(v, static_cast<size_t>(b0) * DV + i);
-        if (tid < nb) fs[tid] = gpow(g, L - 1 - (b0 + tid));
-        __syncthreads();
-        for (int s = 0; s < nb; ++s) {
-            const float f = fs[s];
-            float kr[MR], kc[MR], qr[MR], vc[MC];
-#pragma unroll
-            for (int i = 0; i < MR; ++i) kr[i] = ks[s][ty + 16 * i], qr[i] = qs[s][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < MR; ++j) kc[j] = ks[s][tx + 16 * j];
-#pragma unroll
-            for (int j = 0; j < MC; ++j) vc[j] = vs[s][tx + 16 * j];
-            // f * (k_a k_b): the product k_a k_b is symmetric in (a, b), so S stays
-            // exactly symmetric.
-#pragma unroll
-            for (int i = 0; i < MR; ++i)
-#pragma unroll
-                for (int j = 0; j < MR; ++j) aS[i][j] += f * (kr[i] * kc[j]);
-#pragma unroll
-            for (int i = 0; i < MR; ++i)
-#pragma unroll
-                for (int j = 0; j < MC; ++j) aC[i][j] += f * (qr[i] * vc[j]);
-            if (tid < D) am += f * qs[s][tid];
-        }
-        __syncthreads();
+    const int tid = threadIdx.x;
+    for (int i = tid; i < L; i += kThreads) {
+        fs[i] = gpow(g, L - 1 - i);
+        hs[i] = sqrtf(fs[i]);
     }
+    __syncthreads();
+    auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
+    auto ke = [&](int t, int l) { return Elem<T>::get(k, static_cast<size_t>(t) * D + l); };
+    auto ve = [&](int t, int l) { return Elem<T>::get(v, static_cast<size_t>(t) * DV + l); };
     const size_t sl = slot_index(a, bh, c + 1);
-    float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
-#pragma unroll
-    for (int i = 0; i < MR; ++i)
-#pragma unroll
-        for (int j = 0; j < MR; ++j) S[(ty + 16 * i) * D + tx + 16 * j] = aS[i][j];
-#pragma unroll
-    for (int i = 0; i < MR; ++i)
-#pragma unroll
-        for (int j = 0; j < MC; ++j) C[(ty + 16 * i) * DV + tx + 16 * j] = aC[i][j];
-    if (tid < D) m[tid] = am;
+    {
+        float aS[MR][MR] = {};
+        tile::mm<MR, MR, true>(aS, D, L, st, [&](int r, int t) { return hs[t] * ke(t, r); },
+                               [&](int t, int col) { return hs[t] * ke(t, col); });
+        tile::store_tile<MR, MR>(a.ws.S + sl * D * D, D, D, aS);
+    }
+    float aC[MR][MC] = {};
+    tile::mm<MR, MC, true>(aC, D, L, st, [&](int r, int t) { return fs[t] * qe(t, r); }, ve);
+    tile::store_tile<MR, MC>(a.ws.C + sl * D * DV, D, DV, aC);
+    if (tid < D) {
+        float am = 0.0f;
+        for (int t = 0; t < L; ++t) am += fs[t] * qe(t, tid);
+        a.ws.m[sl * D + tid] = am;
+    }
 }
 
 // Exclusive-to-inclusive decayed prefix over the chunk slots, elementwise:
@@ -204,7 +187,19 @@ __global__ __launch_bounds__(kThreads) void k_prefix(GenArgs a, ScanSeg s0, Scan
     const float rf = gpow(g, power * a.w), rl = gpow(g, power * Llast);
     float *p = seg.base + static_cast<size_t>(bh) * (a.nc + 1) * seg.E + e;
     float run = p[0];
-    for (int c = 0; c < a.nc; ++c) {
+    // eight slot loads in flight per step (the scan itself is serial)
+    int c = 0;
+    for (; c + 8 <= a.nc; c += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p[static_cast<size_t>(c + 1 + u) * seg.E];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            run = (c + u == a.nc - 1 ? rl : rf) * run + x[u];
+            p[static_cast<size_t>(c + 1 + u) * seg.E] = run;
+        }
+    }
+    for (; c < a.nc; ++c) {
         const float r = (c == a.nc - 1) ? rl : rf;
         float *slot = p + static_cast<size_t>(c + 1) * seg.E;
         run = r * run + *slot;
