@@ -488,6 +488,7 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t st) {
     fw.den = reinterpret_cast<float *>(base + L.den);
     fw.init = hla_state{};
     fw.fin = hla_state{};
+    fw.carries_only = f.normalize ? 0 : 1;  // out and den only enter the ratio's gradient
     hipError_t e = generic_forward(fw, st);
     if (e != hipSuccess) return e;
     const GenericSlots sl = generic_slots(fw);

@@ -50,6 +50,7 @@ struct GenArgs {
     int H, n, d, dv, w, nc;
     float ridge;
     int normalize;
+    int carries_only;
     const void *q, *k, *v;
     float *out, *den;
     hla_state init, fin;
@@ -363,6 +364,7 @@ hipError_t launch_all(const GenArgs &a, int BH, hipStream_t st) {
         const int e2 = D * DV + D;
         hipLaunchKernelGGL(k_prefix, dim3((e2 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sX, sy,
                            none, 2);
+        if (a.carries_only) return hipGetLastError();
         if (a.w > 64)
             hipLaunchKernelGGL((k_chunk_out<T, D, DV, 8>), dim3(a.nc, BH), blk, 0, st, a);
         else
@@ -435,7 +437,7 @@ hipError_t generic_forward(const FwdProblem &p, hipStream_t st) {
     char *base = static_cast<char *>(p.ws);
     GenArgs a{};
     a.H = p.H; a.n = p.n; a.d = p.d; a.dv = p.dv; a.w = p.w; a.nc = p.nc;
-    a.ridge = p.ridge; a.normalize = p.normalize;
+    a.ridge = p.ridge; a.normalize = p.normalize; a.carries_only = p.carries_only;
     a.q = p.q; a.k = p.k; a.v = p.v; a.out = p.out; a.den = p.den;
     a.init = p.init; a.fin = p.fin; a.gam = p.gam;
     a.ws.S = reinterpret_cast<float *>(base + L.S);

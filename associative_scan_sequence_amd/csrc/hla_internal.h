@@ -35,6 +35,7 @@ struct FwdProblem {
     GammaTab gam;
     void *ws;
     size_t ws_bytes;
+    int carries_only;  // generic path: stop after the carries and U (no out, den or final state)
 };
 
 // Every forward workspace starts with a control block of kCtrlBytes: words

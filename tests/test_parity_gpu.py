@@ -246,6 +246,19 @@ def test_split_point_continuation_on_gpu():
     check_state(s2, rf, tol)
 
 
+@pytest.mark.parametrize("dtype,d,w", [(torch.float32, 32, 16), (torch.bfloat16, 64, 64), (torch.bfloat16, 128, 128)])
+def test_final_key_moment_is_exactly_symmetric(dtype, d, w):
+    """The decode step reads only S's upper tiles, so the forward must hand
+    over an exactly symmetric S (every chunk sum and prefix keeps it so)."""
+    q, k, v = inputs.qkv(2, 3, 301, d, d, dtype, seed=43)
+    qg, kg, vg = on_gpu(q, k, v)
+    g = inputs.gamma_list_fp32([0.97, 0.999, 1.0])
+    _, _, st = hla.forward_chunked(qg, kg, vg, gamma=g, chunk=w, return_state=True)
+    torch.cuda.synchronize()
+    S = st.S.cpu()
+    assert torch.equal(S, S.transpose(1, 2))
+
+
 def test_forward_last_row_equals_decode_on_gpu():
     B, H, n, d, dv = 1, 4, 200, 64, 64
     q, k, v = inputs.qkv(B, H, n + 1, d, dv, torch.bfloat16, seed=42)
