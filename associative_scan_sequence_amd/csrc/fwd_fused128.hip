@@ -234,8 +234,9 @@ __device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
     ib = static_cast<int>((kIb >> (2 * idx)) & 3u);
 }
 
-// LOOP = false: one segment per workgroup (segs <= grid); true: workgroup b
-// takes segments b, b + grid, ... (grid = CU count < segs).
+// LOOP = false: one segment per workgroup (grid = segs: at most the CU count,
+// or any count when each head is one segment); true: workgroup b takes
+// segments b, b + grid, ... (grid = CU count < segs).
 template <bool DECAY, bool LOOP>
 __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     __shared__ Smem128 sm;
@@ -624,12 +625,15 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
-    // one workgroup per CU at most (its LDS fills the CU), so the whole grid is resident
+    // when segments of a head wait on each other the grid is at most one
+    // workgroup per CU (its LDS fills the CU), so the whole grid is resident
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const bool loop = a.segs > cus;
+    // with one segment per head no workgroup waits on another, so the grid need
+    // not be resident: one workgroup per segment, without the looped body
+    const bool loop = a.segs > cus && a.P > 1;
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
     if (decay) {
         if (loop) hipLaunchKernelGGL((k_fused128<true, true>), grid, dim3(kThreads), 0, st, a);

@@ -104,8 +104,9 @@ typedef struct {
  * afterwards.  The rest holds per-chunk or per-segment partial summaries.
  *
  * The one-launch kernels (bf16, d = dv = 64 or 128, no init or final state)
- * hand partial sums between workgroups of one launch and rely on all of
- * them being resident at once (at most one per CU).  Kernels that other
+ * hand partial sums between workgroups of one launch when a head is cut into
+ * several segments, and then rely on all of them being resident at once (at
+ * most one per CU).  Kernels that other
  * streams run at the same time can delay that; a wait that exceeds a fixed
  * spin limit (about 4M polls) gives up, adds one to word 3 and the outputs
  * of that call are then not reliable.  A caller that shares the device

@@ -380,6 +380,7 @@ def ctrl_words(ws):
     (1, 2, 8192, None),            # more than eight earlier segments to sum, no decay
     (1, 1, 16384, "decay"),        # one head, long
     (4, 64, 256, None),            # 256 heads: the tail of q_0 . k_0 near zero at t = 0
+    (5, 64, 200, "decay"),         # 320 one-segment heads: a grid larger than the CU count
 ])
 def test_fused_forward(B, H, n, gk):
     q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=900 + n + H)
