@@ -486,7 +486,7 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t st) {
     fw.ws_bytes = generic_workspace_bytes(BH, f.n, f.d, f.dv, f.w);
     fw.out = reinterpret_cast<float *>(base + L.out);
     fw.den = reinterpret_cast<float *>(base + L.den);
-    fw.init = hla_state{};
+    fw.init = f.init;  // the left carries start from it (held constant)
     fw.fin = hla_state{};
     fw.carries_only = f.normalize ? 0 : 1;  // out and den only enter the ratio's gradient
     hipError_t e = generic_forward(fw, st);

@@ -276,8 +276,8 @@ size_t hla_backward_workspace_size(const hla_params *p) {
 }
 
 hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
-                                const float *dout, float *dq, float *dk, float *dv, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                const hla_state *init, const float *dout, float *dq, float *dk, float *dv,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
     Geometry geo{};
     hla_status s = forward_geometry(p, &geo);
     if (s != HLA_OK) return s;
@@ -294,6 +294,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
         if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
         if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
     }
+    if (init && (s = check_state(init, "init")) != HLA_OK) return s;
     const size_t need = hla::generic_backward_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
     if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
@@ -309,6 +310,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     ins.push_back(span("k", k, BH * n * p->d * esz));
     ins.push_back(span("v", v, BH * n * p->dv * esz));
     ins.push_back(span("dout", dout, BH * n * p->dv * 4));
+    if (init) state_spans(init, "init", BH, p->d, p->dv, &ins);
     std::string detail;
     if (first_overlap(outs, ins, &detail))
         return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
@@ -316,6 +318,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     fp.w = geo.w; fp.nc = geo.nc;
     fp.dtype = p->dtype; fp.ridge = p->ridge; fp.normalize = p->normalize;
     fp.q = q; fp.k = k; fp.v = v;
+    if (init) fp.init = *init;
     fp.ws = workspace; fp.ws_bytes = workspace_bytes;
     bp.dout = dout; bp.dq = dq; bp.dk = dk; bp.dv = dv;
     const hipError_t e = hla::generic_backward(bp, stream);

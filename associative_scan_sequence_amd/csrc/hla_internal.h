@@ -59,10 +59,11 @@ struct GenericSlots {
 };
 GenericSlots generic_slots(const FwdProblem &p);
 
-// Chunked backward: gradients of sum(out * dout) with respect to q, k, v for
-// the zero initial state, any d, dv, w in {16,32,64,128}, fp32 or bf16.
+// Chunked backward: gradients of sum(out * dout) with respect to q, k, v, from
+// the zero state or a given initial state held constant; any d, dv, w in
+// {16,32,64,128}, fp32 or bf16.
 struct BwdProblem {
-    FwdProblem f;        // the forward call (init, fin, den unused); f.ws = backward data area
+    FwdProblem f;        // the forward call (fin and den unused); f.ws = backward data area
     const float *dout;   // [B,H,n,dv]
     float *dq, *dk, *dv; // [B,H,n,d], [B,H,n,d], [B,H,n,dv]
 };

@@ -140,9 +140,10 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
  * contents need no initialisation and are overwritten by every call. */
 size_t hla_backward_workspace_size(const hla_params *p);
 
-/* Gradients of the chunked forward from the zero initial state: with
- * L = sum_t <out_t, dout_t>, writes dq = dL/dq, dk = dL/dk, dv = dL/dv for
- * every option of p (decay per head, ridge, normalize).  [SUM] sec. 4 and 5
+/* Gradients of the chunked forward: with L = sum_t <out_t, dout_t>, writes
+ * dq = dL/dq, dk = dL/dk, dv = dL/dv for every option of p (decay per head,
+ * ridge, normalize), from the zero state or from `init` held constant (no
+ * gradient with respect to the initial state is formed).  [SUM] sec. 4 and 5
  * (the scan trains chunk-parallel).  The gradient is itself a masked
  * second-order scan, run from the last token to the first: with
  * Gb_j = sum_{t>=j} g^(2(t-j)) q_t dnum_t^T (and its den column),
@@ -153,6 +154,8 @@ size_t hla_backward_workspace_size(const hla_params *p);
  * dnum = dout/den and the den column carries -(dout . out)/den.  The forward
  * is recomputed inside the call (its out and den are not inputs).
  *   q, k  [B,H,n,d], v [B,H,n,dv] in p->dtype       (inputs, not modified)
+ *   init  NULL = zero state, else the state at position -1 (all of S, C, m,
+ *         G, h set; as for hla_forward_chunked)
  *   dout  [B,H,n,dv] fp32                            (input)
  *   dq, dk [B,H,n,d], dv [B,H,n,dv] fp32             (outputs)
  *   workspace  device memory of at least hla_backward_workspace_size(p)
@@ -160,9 +163,9 @@ size_t hla_backward_workspace_size(const hla_params *p);
  * Outputs must not overlap each other, the inputs or the workspace.  With the
  * ratio, a zero denominator gives IEEE inf/NaN gradients. */
 hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k,
-                                const void *v, const float *dout, float *dq, float *dk,
-                                float *dv, void *workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                const void *v, const hla_state *init, const float *dout,
+                                float *dq, float *dk, float *dv, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* One streaming decode step ([SUM] sec. 1 and 2: constant-size state,
  * O(d^2 + d dv) work per token): applies token (q, k, v) to `state` in place

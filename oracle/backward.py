@@ -18,7 +18,8 @@ gist.science page "Methodik" item 1 for the read-out q^T(S C - G)):
     den_t = q_t^T ((S_t + lam I) m_t - h_t)
     out_t = num_t, or num_t / den_t with normalize
 
-starting from the zero state.  The pages' training claim is that this scan
+starting from the zero state or from a given state (S, C, m, G, h) at
+position -1, held constant.  The pages' training claim is that this scan
 is differentiated like any other layer; here the gradient of the scalar
 sum_t <out_t, dout_t> with respect to q, k and v is taken by torch's
 autograd through exactly these updates, written with plain tensor ops in
@@ -46,10 +47,12 @@ def _t64(a) -> torch.Tensor:
 
 def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        gamma: Optional[Sequence[float]] = None, lam: float = 0.0,
-                       normalize: bool = False):
+                       normalize: bool = False, init=None):
     """The serial recurrence in float64 torch ops (differentiable).
 
-    q, k: [B,H,n,d]; v: [B,H,n,dv].  Returns (out [B,H,n,dv], den [B,H,n])."""
+    q, k: [B,H,n,d]; v: [B,H,n,dv]; init: None or an object with S [N,d,d],
+    C [N,d,dv], m [N,d], G [N,d,dv], h [N,d] (N = B*H), the state before
+    token 0.  Returns (out [B,H,n,dv], den [B,H,n])."""
     B, H, n, d = q.shape
     dv = v.shape[-1]
     N = B * H
@@ -58,11 +61,15 @@ def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         torch.as_tensor(np.asarray(gamma, dtype=np.float64)).repeat(B)
     g1, g2 = g.view(N, 1, 1), (g * g).view(N, 1, 1)
     gv1, gv2 = g.view(N, 1), (g * g).view(N, 1)
-    S = torch.zeros(N, d, d, dtype=torch.float64)
-    C = torch.zeros(N, d, dv, dtype=torch.float64)
-    G = torch.zeros(N, d, dv, dtype=torch.float64)
-    m = torch.zeros(N, d, dtype=torch.float64)
-    h = torch.zeros(N, d, dtype=torch.float64)
+    if init is None:
+        S = torch.zeros(N, d, d, dtype=torch.float64)
+        C = torch.zeros(N, d, dv, dtype=torch.float64)
+        G = torch.zeros(N, d, dv, dtype=torch.float64)
+        m = torch.zeros(N, d, dtype=torch.float64)
+        h = torch.zeros(N, d, dtype=torch.float64)
+    else:
+        S, C, G = (_t64(x).reshape(N, d, w) for x, w in ((init.S, d), (init.C, dv), (init.G, dv)))
+        m, h = (_t64(x).reshape(N, d) for x in (init.m, init.h))
     outs, dens = [], []
     for t in range(n):
         qt, kt, vt = qf[:, t], kf[:, t], vf[:, t]
@@ -88,14 +95,15 @@ def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def backward(q, k, v, dout, gamma: Optional[Sequence[float]] = None, lam: float = 0.0,
-             normalize: bool = False):
-    """Gradients (dq, dk, dv) of sum(out * dout) for the zero initial state.
+             normalize: bool = False, init=None):
+    """Gradients (dq, dk, dv) of sum(out * dout), from the zero state or from
+    ``init`` (held constant; see :func:`forward_recurrence`).
 
     q, k: [B,H,n,d]; v, dout: [B,H,n,dv]; any real dtype (converted exactly to
     float64).  Returns float64 numpy arrays shaped like q, k, v."""
     q, k, v, dout = (_t64(x).clone().requires_grad_(i < 3) for i, x in enumerate((q, k, v, dout)))
     if q.shape[2] == 0:
         return (np.zeros(tuple(q.shape)), np.zeros(tuple(k.shape)), np.zeros(tuple(v.shape)))
-    out, _ = forward_recurrence(q, k, v, gamma, lam, normalize)
+    out, _ = forward_recurrence(q, k, v, gamma, lam, normalize, init)
     (out * dout).sum().backward()
     return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()

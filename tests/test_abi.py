@@ -166,13 +166,14 @@ def test_forward_empty_sequence_without_state_is_a_no_op(lib):
 
 
 def bwd(lib, p, q=addr(1), k=addr(2), v=addr(3), dout=addr(4), dq=addr(5), dk=addr(6), dv=addr(7),
-        ws=None, ws_bytes=None):
+        ws=None, ws_bytes=None, init=None):
     need = lib.hla_backward_workspace_size(ctypes.byref(p))
     if ws is None:
         ws = addr(8)
     if ws_bytes is None:
         ws_bytes = need
-    return lib.hla_backward_chunked(ctypes.byref(p), q, k, v, dout, dq, dk, dv, ws, ws_bytes, None)
+    return lib.hla_backward_chunked(ctypes.byref(p), q, k, v, ctypes.byref(init) if init is not None else None,
+                                    dout, dq, dk, dv, ws, ws_bytes, None)
 
 
 def test_backward_workspace_size(lib):
@@ -205,7 +206,7 @@ def test_backward_rejects_bad_pointers_and_workspace(lib):
     need = lib.hla_backward_workspace_size(ctypes.byref(p))
     assert bwd(lib, p, ws_bytes=need - 1) == WORKSPACE
     assert bwd(lib, p, ws=addr(8) + 16) == ALIGN and "256-byte" in last(lib)
-    assert lib.hla_backward_chunked(ctypes.byref(p), addr(1), addr(2), addr(3), addr(4), addr(5),
+    assert lib.hla_backward_chunked(ctypes.byref(p), addr(1), addr(2), addr(3), None, addr(4), addr(5),
                                     addr(6), addr(7), None, need, None) == WORKSPACE
 
 
@@ -215,11 +216,15 @@ def test_backward_rejects_aliasing(lib):
     assert bwd(lib, p, dk=addr(5) + 512) == INVALID and "overlaps" in last(lib)
     assert bwd(lib, p, dv=addr(4)) == INVALID and "dv overlaps dout" in last(lib)
     assert bwd(lib, p, ws=addr(2)) == INVALID and "workspace overlaps k" in last(lib)
+    st = CState(addr(9), addr(10), addr(11), addr(12), addr(13), None)
+    assert bwd(lib, p, dq=addr(10), init=st) == INVALID and "dq overlaps init.C" in last(lib)
+    assert bwd(lib, p, init=CState(addr(9), None, addr(11), addr(12), addr(13), None)) == INVALID
+    assert "init->C is NULL" in last(lib)
 
 
 def test_backward_empty_sequence_is_a_no_op(lib):
     p = params(n=0)
-    assert lib.hla_backward_chunked(ctypes.byref(p), None, None, None, None, None, None, None, None,
+    assert lib.hla_backward_chunked(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
                                     0, None) == OK
 
 

@@ -146,3 +146,29 @@ def test_backward_agrees_with_forward_difference():
     fd = (16 * R1(h / 2) - R1(h)) / 15
     an = sum(float((gr.double() * du.double()).sum()) for gr, du in zip(grads, u))
     assert abs(fd - an) <= 2e-4 * abs(an), (fd, an)
+
+
+@pytest.mark.parametrize("dtype,d,chunk,norm", [(torch.bfloat16, 64, 64, False), (torch.float32, 32, 16, True)])
+def test_backward_from_a_state(dtype, d, chunk, norm):
+    """Continuing from the state of a prefix (its fp64 oracle state rounded to
+    fp32, given to both sides), held constant."""
+    import types
+
+    import oracle
+    from oracle import backward as ob
+    B, H, n0, n = 1, 2, 100, 150
+    q, k, v = inputs.qkv(B, H, n0 + n, d, d, dtype, seed=61 + d)
+    if norm:
+        q, k = (x.float().abs().add(0.1).to(dtype) for x in (q, k))
+    g = inputs.gamma_list_fp32([0.97, 0.995])
+    lam = inputs.ridge_fp32(0.1)
+    _, _, st = oracle.forward(q[:, :, :n0], k[:, :, :n0], v[:, :, :n0], gamma=g, lam=lam)
+    f32 = {name: torch.tensor(getattr(st, name), dtype=torch.float32) for name in ("S", "C", "m", "G", "h")}
+    init = hla.State(*(f32[x].to(DEV) for x in ("S", "C", "m", "G", "h")))
+    qs, ks, vs = (x[:, :, n0:].contiguous() for x in (q, k, v))
+    dout = inputs.upstream(B, H, n, d, seed=71)
+    qg, kg, vg, dg = (x.to(DEV) for x in (qs, ks, vs, dout))
+    got = hla.backward_chunked(qg, kg, vg, dg, gamma=g, ridge=lam, normalize=norm, chunk=chunk, init=init)
+    torch.cuda.synchronize()
+    ref = ob.backward(qs, ks, vs, dout, g, lam, norm, types.SimpleNamespace(**f32))
+    check([x.cpu() for x in got], ref)

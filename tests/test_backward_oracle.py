@@ -113,3 +113,31 @@ def test_causality_of_gradients():
     for gr in grads:
         assert np.all(gr[0, 0, t + 1:] == 0.0)
         assert np.any(gr[0, 0, :t + 1] != 0.0)
+
+
+def test_forward_recurrence_from_a_state_matches_c_oracle(oracle_mod):
+    """With an init state (a method-produced state of a prefix, from the C
+    oracle), the torch recurrence continues exactly like the C oracle."""
+    q, k, v = rnd(81, (1, 2, 30, 4), (1, 2, 30, 4), (1, 2, 30, 3))
+    g = [0.9, 0.8]
+    _, _, st = oracle_mod.forward(q[:, :, :12], k[:, :, :12], v[:, :, :12], gamma=g, lam=0.2)
+    ro, rd, _ = oracle_mod.forward(q[:, :, 12:], k[:, :, 12:], v[:, :, 12:], gamma=g, lam=0.2, init=st,
+                                   want_state=False)
+    out, den = ob.forward_recurrence(*(torch.tensor(x[:, :, 12:]) for x in (q, k, v)), g, 0.2, False, st)
+    assert np.abs(out.numpy() - ro).max() <= 1e-12 * max(1.0, np.abs(ro).max())
+    assert np.abs(den.numpy() - rd).max() <= 1e-12 * max(1.0, np.abs(rd).max())
+
+
+def test_gradients_from_a_state_are_those_of_the_whole_sequence(oracle_mod):
+    """Splitting a sequence and continuing from the (detached) prefix state
+    leaves the gradients of the suffix inputs that only suffix outputs reach
+    unchanged: with dout zero on the prefix, the whole-sequence gradients of
+    the suffix tokens equal the split ones."""
+    q, k, v, dout = rnd(91, (1, 2, 26, 4), (1, 2, 26, 4), (1, 2, 26, 3), (1, 2, 26, 3))
+    g, p = [0.95, 0.85], 10
+    dout[:, :, :p] = 0.0
+    whole = ob.backward(q, k, v, dout, g, 0.3, False)
+    _, _, st = oracle_mod.forward(q[:, :, :p], k[:, :, :p], v[:, :, :p], gamma=g, lam=0.3)
+    part = ob.backward(q[:, :, p:], k[:, :, p:], v[:, :, p:], dout[:, :, p:], g, 0.3, False, st)
+    for a, b in zip(whole, part):
+        np.testing.assert_allclose(a[:, :, p:], b, rtol=1e-11, atol=1e-13)
