@@ -17,6 +17,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int W = 64;          // chunk width = d = dv
 constexpr int kTileElems = W * W;  // one LDS tile: 64 rows of 64 bf16, see tile_off
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kSpinWord = 4;   // control word: spin limit of the bounded waits (0: kSpinLimit)
 constexpr int kLine = 64;      // words per 256-byte control line
 constexpr int kTabWord = 2 * kLine;  // XCD table: one 64-bit entry per workgroup from this word
 constexpr int kTabCap = static_cast<int>(kCtrlBytes / 8) - kTabWord / 2;
@@ -102,8 +103,16 @@ __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u
 // of coherence and the flag is read where it lives, by an atomic (always
 // executed in L2, never served by a CU's L1).  Otherwise the flag is read
 // device-coherently.
-__device__ bool wait_flag(uint32_t *f, uint32_t want, bool local) {
-    for (int it = 0; it < kSpinLimit; ++it) {
+// The spin limit is kSpinLimit polls, or the control word *spin_word when it
+// is nonzero; the word is read only once the first poll has failed.
+__device__ __forceinline__ int spin_limit(const uint32_t *spin_word) {
+    const int s = static_cast<int>(__hip_atomic_load(spin_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return s > 0 ? s : kSpinLimit;
+}
+
+__device__ bool wait_flag(uint32_t *f, uint32_t want, bool local, const uint32_t *spin_word) {
+    int spin = kSpinLimit;
+    for (int it = 0; it < spin; ++it) {
         uint32_t v;
         if (local) {
             v = want;
@@ -113,6 +122,7 @@ __device__ bool wait_flag(uint32_t *f, uint32_t want, bool local) {
             v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (v == want) return true;
+        if (it == 0) spin = spin_limit(spin_word);
         __builtin_amdgcn_s_sleep(1);
     }
     return false;
@@ -144,14 +154,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
 // the caller (any value if lane >= P).  Every segment of the head reads the
 // same entries, so all of them reach the same answer.
 __device__ bool head_on_one_xcd(uint64_t *xtab, bool tab_ok, int P, int BH, int bh, uint32_t ep_now,
-                                uint64_t tabv) {
+                                uint64_t tabv, const uint32_t *spin_word) {
     const int lane = static_cast<int>(threadIdx.x & 63);
     const uint32_t me = 0x100u | xcd_id();
     bool ok = tab_ok;
     for (int i = lane; ok && i < P; i += 64) {
         uint64_t *ent = xtab + (i * BH + bh) % static_cast<int>(gridDim.x);
         uint64_t v = i == lane ? tabv : __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int it = 0; static_cast<uint32_t>(v >> 32) != ep_now && it < kSpinLimit; ++it) {
+        int spin = kSpinLimit;
+        for (int it = 0; static_cast<uint32_t>(v >> 32) != ep_now && it < spin; ++it) {
+            if (it == 0) spin = spin_limit(spin_word);
             __builtin_amdgcn_s_sleep(1);
             v = __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

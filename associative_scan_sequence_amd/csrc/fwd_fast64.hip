@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         }
         // the exchange goes through the XCD's L2 when every workgroup holding
         // a segment of this head runs on this XCD (every wave decides alike)
-        const bool local = head_on_one_xcd(xtab, tab_ok, a.P, a.BH, bh, epoch, tabv);
+        const bool local = head_on_one_xcd(xtab, tab_ok, a.P, a.BH, bh, epoch, tabv, a.ctrl + kSpinWord);
         auto flag_of = [&](size_t sl, int round) { return &a.flags[((sl * 2 + round) * kWaves + wave) * kFlagStride]; };
         if (publish) {
             put_tiles(a.aggS + slot * 4096, wave, l, srun, local);
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         const int seg_tokens = a.L * W;
         auto wait_round = [&](int round) {
             for (int pp = l; pp < p; pp += 64)
-                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local))
+                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local, a.ctrl + kSpinWord))
                     __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
         auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int pw) {

@@ -63,6 +63,7 @@ constexpr int kBlk128 = 2432;  // elements per 16-row block of a 128-wide tile
 constexpr int kTile128 = 4 * kBlk128;  // a 64-row 128-wide tile
 constexpr int kThreads = 512;  // eight waves
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kSpinWord = 4;   // control word: spin limit of the bounded waits (0: kSpinLimit)
 constexpr int kLine = 64;
 constexpr int kSlot = 16384;   // floats per published 128 x 128 aggregate
 constexpr float kMinGamma = 0.75f;
@@ -158,8 +159,8 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F7
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u + 1013904223u; }
 
-__device__ bool wait_flag(const uint32_t *f, uint32_t want) {
-    for (int it = 0; it < kSpinLimit; ++it) {
+__device__ bool wait_flag(const uint32_t *f, uint32_t want, int spin) {
+    for (int it = 0; it < spin; ++it) {
         if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
         __builtin_amdgcn_s_sleep(1);
     }
@@ -495,8 +496,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         wait_stores();
         __syncthreads();
         if (tid == 0) __hip_atomic_store(&a.flags[2 * (slot0 + p)], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int spin_set = static_cast<int>(__hip_atomic_load(&a.ctrl[kSpinWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        const int spin = spin_set > 0 ? spin_set : kSpinLimit;
         for (int pp = tid; pp < p; pp += kThreads)
-            if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch))
+            if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch, spin))
                 __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         sum_slots(sacc, a.aggS, static_cast<int>(slot0), p, tid,
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         if (tid == 0)
             __hip_atomic_store(&a.flags[2 * (slot0 + p) + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int pp = tid; pp < p; pp += kThreads)
-            if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch))
+            if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch, spin))
                 __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         sum_slots(xacc, a.aggZ, static_cast<int>(slot0), p, tid,

@@ -98,10 +98,12 @@ typedef struct {
 /* Bytes of device workspace hla_forward_chunked needs for these params
  * (0 for an invalid p).  Its first 8192 bytes are a control block that the
  * library keeps valid from call to call (32-bit words: 2 = launches of the
- * one-launch kernels, 3 = waits that hit the spin limit, 64 = finished-
- * workgroup counter, 65 = launch epoch, then a table of XCD ids):
- * zero-fill the workspace once before its first use and do not write it
- * afterwards.  The rest holds per-chunk or per-segment partial summaries.
+ * one-launch kernels, 3 = waits that hit the spin limit, 4 = that limit in
+ * polls (0 = the built-in 4M; the only word a caller may set, e.g. to test
+ * the give-up path), 64 = finished-workgroup counter, 65 = launch epoch,
+ * then a table of XCD ids): zero-fill the workspace once before its first
+ * use and write nothing else in it afterwards.  The rest holds per-chunk or
+ * per-segment partial summaries.
  *
  * The one-launch kernels (bf16, d = dv = 64 or 128, no init or final state)
  * hand partial sums between workgroups of one launch when a head is cut into

@@ -554,3 +554,28 @@ def test_fused128_causality_bitwise():
             x[:, :, t + 1:] = -x[:, :, t + 1:]
         o2, _, _ = hla.forward_chunked(q2, k2, v2)
         assert torch.equal(o2[:, :, : t + 1], out[:, :, : t + 1]), t
+
+
+@pytest.mark.parametrize("d,B,H,n", [(64, 4, 8, 2048), (128, 1, 16, 4096)])
+def test_bounded_waits_give_up_and_are_counted(d, B, H, n):
+    """Failure handling of the one-launch kernels, forced from the host: with
+    the spin limit (control word 4) set to one poll, the cross-workgroup waits
+    give up at once.  The launch must still end normally and count the
+    give-ups in word 3; with the limit restored, the next call on the same
+    workspace is again bit-identical to one on a fresh workspace."""
+    q, k, v = on_gpu(*inputs.qkv(B, H, n, d, d, torch.bfloat16, seed=47))
+    ws = torch.zeros(hla.workspace_size(B, H, n, d, d), dtype=torch.uint8, device=DEV)
+    words = ws[:64].view(torch.int32)
+    words[4] = 1
+    hla.forward_chunked(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    w = ctrl_words(ws)
+    assert w[2] == 1, w          # the one-launch path ran, and ran to its end
+    assert w[3] > 0, w           # some wait gave up (multi-segment heads)
+    words[4] = 0
+    words[3] = 0
+    out, _, _ = hla.forward_chunked(q, k, v, workspace=ws)
+    ref, _, _ = hla.forward_chunked(q, k, v)
+    torch.cuda.synchronize()
+    assert ctrl_words(ws)[3] == 0
+    assert torch.equal(out, ref)
