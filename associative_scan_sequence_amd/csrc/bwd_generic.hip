@@ -122,18 +122,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_sums(BwdArgs a) {
         mm<MR, MC, true>(aC, D, L, st, [&](int r, int t) { return gt[t] * qe(t, r); }, gne);
         store_tile<MR, MC>(a.RC + sl * D * DV, D, DV, aC);
     }
-    if (tid < D) {
-        float ag = 0.0f, ac = 0.0f;
-        if (gd) {
-            for (int t = 0; t < L; ++t) {
-                const float x = qe(t, tid) * gd[t];
-                ag += gt[2 * t] * x;
-                ac += gt[t] * x;
-            }
-        }
-        a.rg[sl * D + tid] = ag;
-        if (ridge) a.rc[sl * D + tid] = ac;
-    }
+    tile::row_sums(D, gd ? L : 0, [&](int r, int t) { return gt[2 * t] * qe(t, r) * gd[t]; },
+                   [&](int r, float x) { a.rg[sl * D + r] = x; });
+    if (ridge)
+        tile::row_sums(D, gd ? L : 0, [&](int r, int t) { return gt[t] * qe(t, r) * gd[t]; },
+                       [&](int r, float x) { a.rc[sl * D + r] = x; });
     if (c == a.nc - 1) {  // slot nc: nothing to the right of the last token
         const size_t se = slot(a, bh, a.nc);
         for (int i = tid; i < D * DV; i += kThreads) {

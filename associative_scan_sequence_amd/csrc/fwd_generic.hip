@@ -65,37 +65,26 @@ __device__ __forceinline__ size_t slot_index(const GenArgs &a, int bh, int slot)
 // Out = S*C - In and outv = S*m - inv for one head; S [D][D], C/In/Out [D][DV].
 template <int D, int DV>
 __device__ void s_times_c_minus(const float *S, const float *C, const float *In, float *Out,
-                                const float *m, const float *inv, float *outv) {
+                                const float *m, const float *inv, float *outv, tile::Stage &st) {
     constexpr int MR = D / 16, MC = DV / 16;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     float acc[MR][MC] = {};
-    for (int l = 0; l < D; ++l) {
-        float sr[MR], cc[MC];
-#pragma unroll
-        for (int i = 0; i < MR; ++i) sr[i] = S[(ty + 16 * i) * D + l];
-#pragma unroll
-        for (int j = 0; j < MC; ++j) cc[j] = C[l * DV + tx + 16 * j];
-#pragma unroll
-        for (int i = 0; i < MR; ++i)
-#pragma unroll
-            for (int j = 0; j < MC; ++j) acc[i][j] += sr[i] * cc[j];
-    }
+    tile::mm<MR, MC, false>(acc, D, D, st, [&](int r, int l) { return S[r * D + l]; },
+                            [&](int l, int col) { return C[l * DV + col]; });
 #pragma unroll
     for (int i = 0; i < MR; ++i)
 #pragma unroll
         for (int j = 0; j < MC; ++j) {
-            const int o = (ty + 16 * i) * DV + tx + 16 * j;
+            const int o = (MR * ty + i) * DV + MC * tx + j;
             Out[o] = acc[i][j] - In[o];
         }
-    if (tid < D) {
-        float s = 0.0f;
-        for (int l = 0; l < D; ++l) s += S[tid * D + l] * m[l];
-        outv[tid] = s - inv[tid];
-    }
+    tile::row_sums(D, D, [&](int r, int l) { return S[r * D + l] * m[l]; },
+                   [&](int r, float s) { outv[r] = s - inv[r]; });
 }
 
 template <int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_init_slot(GenArgs a) {
+    __shared__ tile::Stage st;
     const int bh = blockIdx.x;
     const size_t sl = slot_index(a, bh, 0);
     float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
@@ -115,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void k_init_slot(GenArgs a) {
     for (int i = tid; i < D * D; i += kThreads) S[i] = iS[i];
     for (int i = tid; i < D * DV; i += kThreads) C[i] = iC[i];
     if (tid < D) m[tid] = im[tid];
-    s_times_c_minus<D, DV>(iS, iC, iG, X, im, ih, y);
+    s_times_c_minus<D, DV>(iS, iC, iG, X, im, ih, y, st);
 }
 
 // K^T diag(f) K, Q^T diag(f) V and Q^T f of chunk c -> slot c+1 (products from
@@ -153,11 +142,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_sums(GenArgs a) {
     float aC[MR][MC] = {};
     tile::mm<MR, MC, true>(aC, D, L, st, [&](int r, int t) { return fs[t] * qe(t, r); }, ve);
     tile::store_tile<MR, MC>(a.ws.C + sl * D * DV, D, DV, aC);
-    if (tid < D) {
-        float am = 0.0f;
-        for (int t = 0; t < L; ++t) am += fs[t] * qe(t, tid);
-        a.ws.m[sl * D + tid] = am;
-    }
+    tile::row_sums(D, L, [&](int r, int t) { return fs[t] * qe(t, r); },
+                   [&](int r, float x) { a.ws.m[sl * D + r] = x; });
 }
 
 // Exclusive-to-inclusive decayed prefix over the chunk slots, elementwise:
@@ -247,11 +233,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_uz(GenArgs a) {
     tile::mm<MC, MZ, true>(z, D, L, st, [&](int r, int s) { return gt[2 * (L - 1 - s)] * buf[s * D + r]; }, ve);
     const size_t sl = slot_index(a, bh, c + 1);
     tile::store_tile<MC, MZ>(a.ws.X + sl * D * DV, D, DV, z);
-    if (tid < D) {
-        float acc = 0.0f;
-        for (int s = 0; s < L; ++s) acc += gt[2 * (L - 1 - s)] * buf[s * D + tid];
-        a.ws.y[sl * D + tid] = acc;
-    }
+    tile::row_sums(D, L, [&](int r, int s) { return gt[2 * (L - 1 - s)] * buf[s * D + r]; },
+                   [&](int r, float x) { a.ws.y[sl * D + r] = x; });
 }
 
 // P, num, den and the ratio of chunk c (products from LDS, tile_fp32.h)
@@ -287,20 +270,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
     }
     __syncthreads();
     // den_t = sum_s P[t][s] + e_t^2 (q_t . y0) + lambda e_t (q_t . m0)
-    if (tid < L) {
-        const int t = tid;
-        float ps = 0.0f, qy = 0.0f, qm = 0.0f;
-        for (int s = 0; s <= t; ++s) ps += P[t * PS + s];
-        for (int l = 0; l < D; ++l) {
-            const float ql = qe(t, l);
-            qy += ql * y0[l];
-            qm += ql * m0[l];
-        }
-        const float e = gt[t + 1];
-        const float dn = ps + e * e * qy + lam * e * qm;
-        dens[t] = dn;
-        if (a.den) a.den[tok + t] = dn;
-    }
+    tile::row_sums(L, L, [&](int t, int s) { return s <= t ? P[t * PS + s] : 0.0f; },
+                   [&](int t, float ps) { dens[t] = ps; });
+    // (each row's fin runs on the lane that wrote its dens entry above)
+    tile::row_sums(L, D,
+                   [&](int t, int l) {
+                       const float e = gt[t + 1];
+                       return qe(t, l) * (e * e * y0[l] + lam * e * m0[l]);
+                   },
+                   [&](int t, float x) {
+                       const float dn = dens[t] + x;
+                       dens[t] = dn;
+                       if (a.den) a.den[tok + t] = dn;
+                   });
     __syncthreads();
     // num = P V + diag(e^2) Q X0 + lambda diag(e) Q C0
     float acc[RT][MC] = {};
@@ -326,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
 
 template <int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
+    __shared__ tile::Stage st;
     const int bh = blockIdx.x;
     const size_t sl = slot_index(a, bh, a.nc);
     const float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
@@ -338,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
     for (int i = tid; i < D * DV; i += kThreads) fC[i] = C[i];
     if (tid < D) fm[tid] = m[tid];
     s_times_c_minus<D, DV>(S, C, X, a.fin.G + static_cast<size_t>(bh) * D * DV, m, y,
-                           a.fin.h + static_cast<size_t>(bh) * D);
+                           a.fin.h + static_cast<size_t>(bh) * D, st);
     if (tid == 0 && a.fin.rho) {
         const float g = head_gamma(a.gam, bh % a.H);
         const float r0 = (a.init.S && a.init.rho) ? a.init.rho[bh] : 1.0f;

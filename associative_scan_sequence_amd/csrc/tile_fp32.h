@@ -128,5 +128,22 @@ __device__ __forceinline__ void store_tile(float *dst, int nrows, int width, con
     }
 }
 
+// fin(r, sum_{i<N} f(r, i)) for rows r < R, by all threads of the workgroup:
+// four lanes per row, each summing every fourth term, then two shuffles (a
+// fixed order, so the result is deterministic).  fin runs on one lane per row.
+template <typename F, typename FIN>
+__device__ __forceinline__ void row_sums(int R, int N, F f, FIN fin) {
+    const int tid = threadIdx.x, part = tid & 3;
+    for (int r0 = 0; r0 < R; r0 += kThreads / 4) {
+        const int r = r0 + (tid >> 2);
+        float s = 0.0f;
+        if (r < R)
+            for (int i = part; i < N; i += 4) s += f(r, i);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (r < R && part == 0) fin(r, s);
+    }
+}
+
 }  // namespace tile
 }  // namespace hla

@@ -19,7 +19,9 @@ against 8 TB/s), and the fp64 CPU oracle timed on the host on a bounded
 sample of the same workload.  The line also carries ``workloads``: the
 other parts of the hot path (the ratio-normalised forward with decay and
 ridge, the long d=128 forward, the streaming decode step, state composition,
-the small fp32 forward) and the backward at the headline shape, each timed with HIP events on its launch stream and
+the small fp32 forward), and at the headline shape the forward that also
+returns its final state (the generic path a sequence shard runs) and the
+backward, each timed with HIP events on its launch stream and
 set against its own HBM roofline (``--headline-only`` skips them).
 """
 import argparse
@@ -36,7 +38,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
-SECONDARY = ("ratio", "long", "decode", "compose", "small", "backward")
+SECONDARY = ("ratio", "long", "decode", "compose", "small", "state", "backward")
 
 
 def parse():
@@ -202,7 +204,7 @@ def secondary_states(dev, stream, only):
     import hla_inputs as inputs
 
     res = []
-    if only in ("small", "backward"):
+    if only in ("small", "state", "backward"):
         return res + secondary_small(dev, stream, only)
     # streaming decode: 4096 states seeded from a 512-token prefix
     w = inputs.DECODE_D128
@@ -240,9 +242,54 @@ def secondary_small(dev, stream, only):
     res = []
     if only in (None, "small"):
         res += small_forward(dev, stream)
+    if only in (None, "state"):
+        res += forward_with_state(dev, stream)
     if only in (None, "backward"):
         res += backward_headline_shape(dev, stream)
     return res
+
+
+def forward_with_state(dev, stream):
+    """hla_forward_chunked at B4 H8 n2048 d64 bf16 returning the final state
+    (the per-head summary a sequence shard hands on); the one-launch kernel
+    does not form it, so this is the generic chunked path.  Algorithmic bytes:
+    q, k, v in and out per head-token, plus the final state per head."""
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    w = inputs.FWD_D64
+    tok = w.B * w.H * w.n
+    per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv
+    state_b = 4 * (w.d * w.d + 2 * w.d * w.dv + 2 * w.d + 1)
+    need = hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, chunk=w.chunk)
+    copies = max(2, math.ceil(2 * MALL_BYTES / (tok * per_tok + need)))
+    sets = []
+    for c in range(copies):
+        q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5600 + c, dev)
+        out = torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        sets.append((q, k, v, out, ws))
+    fin = hla.State.empty(w.B * w.H, w.d, w.dv, dev)
+    lib = hla.load()
+
+    # the binding allocates a new state per call when asked for one; pass a
+    # preallocated state through the C ABI instead
+    import ctypes
+    p, _keep = hla._binding._params(w.B, w.H, w.n, w.d, w.dv, w.chunk, w.dtype, None, 0.0, False)
+    fin_c = fin.c()
+
+    def call_state(i):
+        q, k, v, out, ws = sets[i % copies]
+        hla._binding._check(lib.hla_forward_chunked(
+            ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, None,
+            ctypes.byref(fin_c), ws.data_ptr(), need, hla._binding._stream(dev)))
+    us = time_calls(call_state, stream, 20)
+    return [{"workload": "masked_hla_fwd_final_state_B4_H8_n2048_d64_bf16_w64",
+             "entry": "hla_forward_chunked (out + final state, generic path)", "us_per_call": us,
+             "tokens_per_s": w.B * w.n / (us * 1e-6),
+             "roofline": roof(tok * per_tok + w.B * w.H * state_b, us)}]
 
 
 def backward_headline_shape(dev, stream):
