@@ -300,3 +300,33 @@ def state_compose(earlier: State, later: State, result: Optional[State] = None) 
                                _stream(earlier.C.device))
     _check(st)
     return result
+
+
+class _HLAFunction(torch.autograd.Function):
+    """Forward through ``hla_forward_chunked``, backward through
+    ``hla_backward_chunked`` (both C ABI calls; nothing is computed here)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gamma, ridge, normalize, chunk):
+        out, _, _ = forward_chunked(q, k, v, gamma=gamma, ridge=ridge, normalize=normalize, chunk=chunk)
+        ctx.save_for_backward(q, k, v)
+        ctx.opts = (gamma, ridge, normalize, chunk)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v = ctx.saved_tensors
+        gamma, ridge, normalize, chunk = ctx.opts
+        dq, dk, dv = backward_chunked(q, k, v, dout.float().contiguous(), gamma=gamma, ridge=ridge,
+                                      normalize=normalize, chunk=chunk)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=None, ridge: float = 0.0,
+              normalize: bool = False, chunk: int = 0) -> torch.Tensor:
+    """Masked second-order HLA as a differentiable op (zero initial state):
+    out [B,H,n,dv] fp32 from q, k [B,H,n,d] and v [B,H,n,dv] (bf16 or fp32);
+    gradients flow to q, k, v through ``hla_backward_chunked`` and are
+    returned in the inputs' dtype."""
+    return _HLAFunction.apply(q, k, v, gamma, ridge, normalize, chunk)
+

@@ -172,3 +172,25 @@ def test_backward_from_a_state(dtype, d, chunk, norm):
     torch.cuda.synchronize()
     ref = ob.backward(qs, ks, vs, dout, g, lam, norm, types.SimpleNamespace(**f32))
     check([x.cpu() for x in got], ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_autograd_op(dtype):
+    """hla.attention as a torch autograd op: loss.backward() through the C ABI
+    gives the oracle's gradients (returned in the inputs' dtype)."""
+    from oracle import backward as ob
+    B, H, n, d, dv = 1, 2, 130, 64, 32
+    q, k, v, dout, g = make(B, H, n, d, dv, dtype, "per_head", False, seed=99)
+    qg, kg, vg = (x.to(DEV).requires_grad_(True) for x in (q, k, v))
+    out = hla.attention(qg, kg, vg, gamma=g, ridge=0.1, chunk=64)
+    (out * dout.to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    ref = ob.backward(q, k, v, dout, g, inputs.ridge_fp32(0.1), False)
+    got = [x.grad.float().cpu() for x in (qg, kg, vg)]
+    assert all(x.grad.dtype == dtype for x in (qg, kg, vg))
+    if dtype == torch.float32:
+        check(got, ref)
+    else:  # gradients rounded to bf16 on return: within bf16's half-ulp of the fp32 result
+        for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+            e = slab_err(x, r, lead=2)
+            assert e <= 2 ** -8, f"{name}: {e:.3e}"
