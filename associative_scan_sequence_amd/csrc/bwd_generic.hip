@@ -185,7 +185,8 @@ __global__ __launch_bounds__(kThreads) void k_rprefix(BwdArgs a, RScan s0, RScan
 template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kThreads) void k_bwd_w(BwdArgs a) {
     constexpr int MA = D / 16, BW = 16 * RT;
-    __shared__ float buf[BW * kMaxW];  // Gam2 (stride BW), then W rows (stride D)
+    constexpr int BUF = BW * kMaxW > D * D ? BW * kMaxW : D * D;
+    __shared__ float buf[BUF];  // Gam2 (stride BW), then W rows (stride D), then A (D x D)
     __shared__ float gt[2 * kMaxW + 1];
     __shared__ Stage st;
     const int c = blockIdx.x, bh = blockIdx.y;
@@ -222,12 +223,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_w(BwdArgs a) {
     store_tile<RT, MA>(Wg, L, D, wacc);
     store_tile<RT, MA>(buf, L, D, wacc);  // W rows, stride D (Gam2 reads ended in mm)
     __syncthreads();
-    // T increment: sum_t g^t (w_t q_t^T + q_t w_t^T), d x d
+    // T increment: A + A^T with A = sum_t g^t w_t q_t^T (d x d), so it is exactly symmetric
     float tacc[MA][MA] = {};
     mm<MA, MA, true>(tacc, D, L, st, [&](int r, int t) { return gt[t] * buf[t * D + r]; }, qe);
-    mm<MA, MA, true>(tacc, D, L, st, [&](int r, int t) { return gt[t] * qe(t, r); },
-                     [&](int t, int col) { return buf[t * D + col]; });
-    store_tile<MA, MA>(a.T + slot(a, bh, c) * D * D, D, D, tacc);
+    store_tile<MA, MA>(buf, D, D, tacc);  // the W reads ended inside mm
+    __syncthreads();
+    {
+        const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+        float *Tc = a.T + slot(a, bh, c) * D * D;
+#pragma unroll
+        for (int i = 0; i < MA; ++i)
+#pragma unroll
+            for (int j = 0; j < MA; ++j) {
+                const int r = MA * ty + i, col = MA * tx + j;
+                Tc[r * D + col] = tacc[i][j] + buf[col * D + r];
+            }
+    }
 }
 
 // ---- dQ
