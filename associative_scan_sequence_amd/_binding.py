@@ -170,10 +170,13 @@ def forward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=
                     init: Optional[State] = None, return_state: bool = False,
                     return_den: bool = False, out: Optional[torch.Tensor] = None,
                     den: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None,
+                    final_state: Optional[State] = None):
     """Masked second-order HLA forward through ``hla_forward_chunked``.
 
     q, k: [B,H,n,d]; v: [B,H,n,dv] (bf16 or fp32, same dtype, on one device).
+    ``final_state``: a State to write the final state into (implies
+    return_state; otherwise one is allocated when return_state is set).
     Returns (out [B,H,n,dv] fp32, den [B,H,n] fp32 or None, final State or None).
     """
     lib = load()
@@ -198,7 +201,7 @@ def forward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=
         den = torch.empty(B, H, n, dtype=torch.float32, device=dev)
     if den is not None:
         _need(den, "den", (torch.float32,))
-    fin = State.empty(B * H, d, dv, dev) if return_state else None
+    fin = final_state if final_state is not None else (State.empty(B * H, d, dv, dev) if return_state else None)
     ini_c = init.c() if init is not None else None
     fin_c = fin.c() if fin is not None else None
     ws_ptr = workspace.data_ptr() if workspace is not None else None

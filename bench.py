@@ -272,19 +272,10 @@ def forward_with_state(dev, stream):
         ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         sets.append((q, k, v, out, ws))
     fin = hla.State.empty(w.B * w.H, w.d, w.dv, dev)
-    lib = hla.load()
-
-    # the binding allocates a new state per call when asked for one; pass a
-    # preallocated state through the C ABI instead
-    import ctypes
-    p, _keep = hla._binding._params(w.B, w.H, w.n, w.d, w.dv, w.chunk, w.dtype, None, 0.0, False)
-    fin_c = fin.c()
 
     def call_state(i):
         q, k, v, out, ws = sets[i % copies]
-        hla._binding._check(lib.hla_forward_chunked(
-            ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, None,
-            ctypes.byref(fin_c), ws.data_ptr(), need, hla._binding._stream(dev)))
+        hla.forward_chunked(q, k, v, chunk=w.chunk, out=out, workspace=ws, final_state=fin)
     us = time_calls(call_state, stream, 20)
     return [{"workload": "masked_hla_fwd_final_state_B4_H8_n2048_d64_bf16_w64",
              "entry": "hla_forward_chunked (out + final state, generic path)", "us_per_call": us,

@@ -579,3 +579,17 @@ def test_bounded_waits_give_up_and_are_counted(d, B, H, n):
     torch.cuda.synchronize()
     assert ctrl_words(ws)[3] == 0
     assert torch.equal(out, ref)
+
+
+def test_final_state_into_a_given_state():
+    """forward_chunked(final_state=...) writes the same state that
+    return_state=True returns, into the caller's tensors."""
+    q, k, v = on_gpu(*inputs.qkv(2, 3, 150, 32, 32, torch.float32, seed=48))
+    g = inputs.gamma_list_fp32([0.95, 0.99, 1.0])
+    _, _, ref = hla.forward_chunked(q, k, v, gamma=g, return_state=True)
+    fin = hla.State.empty(6, 32, 32, DEV)
+    _, _, got = hla.forward_chunked(q, k, v, gamma=g, final_state=fin)
+    torch.cuda.synchronize()
+    assert got is fin
+    for a, b in zip(ref.tensors(), fin.tensors()):
+        assert torch.equal(a, b)
