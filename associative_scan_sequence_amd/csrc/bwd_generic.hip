@@ -45,6 +45,7 @@ namespace {
 constexpr int kThreads = tile::kThreads;
 constexpr int kMaxW = tile::kMaxW;
 using tile::gram;
+using tile::max3;
 using tile::mm;
 using tile::Stage;
 using tile::store_tile;
@@ -98,7 +99,7 @@ template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_bwd_sums(BwdArgs a) {
     constexpr int MR = D / 16, MC = DV / 16;
     __shared__ float gt[2 * kMaxW + 1];
-    __shared__ Stage st;
+    __shared__ Stage<max3(D, DV, 16)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_w(BwdArgs a) {
     constexpr int BUF = BW * kMaxW > D * D ? BW * kMaxW : D * D;
     __shared__ float buf[BUF];  // Gam2 (stride BW), then W rows (stride D), then A (D x D)
     __shared__ float gt[2 * kMaxW + 1];
-    __shared__ Stage st;
+    __shared__ Stage<max3(BW, D, DV)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
     constexpr int MA = D / 16, BW = 16 * RT;
     __shared__ float buf[BW * BW];
     __shared__ float gt[2 * kMaxW + 1];
-    __shared__ Stage st;
+    __shared__ Stage<max3(BW, D, DV)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dk(BwdArgs a) {
     constexpr int MA = D / 16, BW = 16 * RT;
     __shared__ float buf[BW * BW];
     __shared__ float gt[2 * kMaxW + 1];
-    __shared__ Stage st;
+    __shared__ Stage<max3(BW, D, DV)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
     constexpr int MC = DV / 16, BW = 16 * RT;
     __shared__ float buf[BW * BW];
     __shared__ float gt[2 * kMaxW + 1];
-    __shared__ Stage st;
+    __shared__ Stage<max3(BW, D, DV)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);

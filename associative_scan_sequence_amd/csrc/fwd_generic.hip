@@ -63,9 +63,9 @@ __device__ __forceinline__ size_t slot_index(const GenArgs &a, int bh, int slot)
 }
 
 // Out = S*C - In and outv = S*m - inv for one head; S [D][D], C/In/Out [D][DV].
-template <int D, int DV>
+template <int D, int DV, int SR>
 __device__ void s_times_c_minus(const float *S, const float *C, const float *In, float *Out,
-                                const float *m, const float *inv, float *outv, tile::Stage &st) {
+                                const float *m, const float *inv, float *outv, tile::Stage<SR> &st) {
     constexpr int MR = D / 16, MC = DV / 16;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     float acc[MR][MC] = {};
@@ -84,7 +84,7 @@ __device__ void s_times_c_minus(const float *S, const float *C, const float *In,
 
 template <int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_init_slot(GenArgs a) {
-    __shared__ tile::Stage st;
+    __shared__ tile::Stage<tile::max3(D, DV, 16)> st;
     const int bh = blockIdx.x;
     const size_t sl = slot_index(a, bh, 0);
     float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
@@ -115,7 +115,7 @@ template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_chunk_sums(GenArgs a) {
     constexpr int MR = D / 16, MC = DV / 16;
     __shared__ float fs[kMaxW], hs[kMaxW];  // f_s = g^(L-1-s) and sqrt(f_s)
-    __shared__ tile::Stage st;
+    __shared__ tile::Stage<tile::max3(D, DV, 16)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_uz(GenArgs a) {
     constexpr int MC = D / 16, MZ = DV / 16, BW = 16 * RT;
     __shared__ float buf[BW * kMaxW];  // A (L x L, stride BW), then U rows (stride D)
     __shared__ float gt[2 * kMaxW + 1];
-    __shared__ tile::Stage st;
+    __shared__ tile::Stage<tile::max3(BW, D, DV)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
     constexpr int MC = DV / 16, BW = 16 * RT, PS = BW + 1;  // odd stride: row walks hit distinct banks
     __shared__ float P[BW * PS];
     __shared__ float gt[2 * kMaxW + 1], dens[kMaxW];
-    __shared__ tile::Stage st;
+    __shared__ tile::Stage<tile::max3(BW, D, DV)> st;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int s0 = c * a.w, L = min(a.w, a.n - s0);
     const float g = head_gamma(a.gam, bh % a.H);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
 
 template <int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
-    __shared__ tile::Stage st;
+    __shared__ tile::Stage<tile::max3(D, DV, 16)> st;
     const int bh = blockIdx.x;
     const size_t sl = slot_index(a, bh, a.nc);
     const float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;

@@ -2,7 +2,7 @@
 // kernels, formed from LDS by a workgroup of 256 threads.
 //
 // Operands are staged in k-blocks of KB, transposed ([k][row], rows padded
-// by 4 floats); every thread owns a contiguous block of output rows (RM per
+// by 4 floats, sized to the largest row count the kernel stages); every thread owns a contiguous block of output rows (RM per
 // thread, rows RM*ty ..) and columns (NC per thread, columns NC*tx ..), with
 // ty = tid / 16 and tx = tid % 16, so its operand reads are 16-byte vectors.
 // Operands are given as element functions (row, k) -> float; masks, decay
@@ -16,13 +16,16 @@ namespace tile {
 
 constexpr int kThreads = 256;
 constexpr int kMaxW = 128;  // largest row count of a staged operand
-constexpr int KB = 16;
-constexpr int kStageW = kMaxW + 4;
+constexpr int KB = 32;
 
+// ROWS: the largest row (or column) count a kernel stages
+template <int ROWS>
 struct alignas(16) Stage {
-    float a[KB][kStageW];
-    float b[KB][kStageW];
+    float a[KB][ROWS + 4];
+    float b[KB][ROWS + 4];
 };
+
+constexpr int max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
 
 template <int N>
 __device__ __forceinline__ void read_vec(const float *p, float (&v)[N]) {
@@ -40,15 +43,16 @@ __device__ __forceinline__ void read_vec(const float *p, float (&v)[N]) {
 
 // buf[t][s] (row stride BW) = fin(t, s, sum_{l<K} A(t, l) B(s, l)) for t, s < L;
 // thread (ty, tx) forms rows RT*ty .. and columns RT*tx .. (RT*16 >= L).
-template <int RT, int K, typename FA, typename FB, typename FF>
-__device__ __forceinline__ void gram(float *buf, int BW, int L, Stage &st, FA A, FB B, FF fin) {
+template <int RT, int K, int SR, typename FA, typename FB, typename FF>
+__device__ __forceinline__ void gram(float *buf, int BW, int L, Stage<SR> &st, FA A, FB B, FF fin) {
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     float acc[RT][RT] = {};
     for (int l0 = 0; l0 < K; l0 += KB) {
         for (int idx = tid; idx < L * KB; idx += kThreads) {  // k fastest: row-major operands
             const int row = idx / KB, kk = idx % KB;
-            st.a[kk][row] = A(row, l0 + kk);
-            st.b[kk][row] = B(row, l0 + kk);
+            const bool in = l0 + kk < K;
+            st.a[kk][row] = in ? A(row, l0 + kk) : 0.0f;
+            st.b[kk][row] = in ? B(row, l0 + kk) : 0.0f;
         }
         __syncthreads();
         if (RT * ty < L && RT * tx < L) {
@@ -77,8 +81,8 @@ __device__ __forceinline__ void gram(float *buf, int BW, int L, Stage &st, FA A,
 // acc[i][j] += sum_{k<K} M(r_i, k) X(k, c_j) for rows r_i = RM*ty + i < nrows and
 // columns c_j = NC*tx + j (16*NC columns).  ROWFAST stages M with the row index
 // fastest (for M read as a transpose, M(r, k) = P[k][r]); else k fastest.
-template <int RM, int NC, bool ROWFAST, typename FM, typename FX>
-__device__ __forceinline__ void mm(float (&acc)[RM][NC], int nrows, int K, Stage &st, FM M, FX X) {
+template <int RM, int NC, bool ROWFAST, int SR, typename FM, typename FX>
+__device__ __forceinline__ void mm(float (&acc)[RM][NC], int nrows, int K, Stage<SR> &st, FM M, FX X) {
     constexpr int NCOL = 16 * NC;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     for (int k0 = 0; k0 < K; k0 += KB) {
