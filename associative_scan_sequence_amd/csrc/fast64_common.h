@@ -107,7 +107,7 @@ __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u
 // is nonzero; the word is read only once the first poll has failed.
 __device__ __forceinline__ int spin_limit(const uint32_t *spin_word) {
     const int s = static_cast<int>(__hip_atomic_load(spin_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    return s > 0 ? s : kSpinLimit;
+    return s > 0 ? s : (s < 0 ? 1 : kSpinLimit);  // -1: give up after the first poll
 }
 
 __device__ bool wait_flag(uint32_t *f, uint32_t want, bool local, const uint32_t *spin_word) {

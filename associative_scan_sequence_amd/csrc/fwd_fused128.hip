@@ -497,7 +497,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         __syncthreads();
         if (tid == 0) __hip_atomic_store(&a.flags[2 * (slot0 + p)], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int spin_set = static_cast<int>(__hip_atomic_load(&a.ctrl[kSpinWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        const int spin = spin_set > 0 ? spin_set : kSpinLimit;
+        // -1: give up without polling (a host-forced failure); n > 0: n polls
+        const int spin = spin_set < 0 ? 0 : (spin_set > 0 ? spin_set : kSpinLimit);
         for (int pp = tid; pp < p; pp += kThreads)
             if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch, spin))
                 __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

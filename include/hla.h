@@ -99,8 +99,9 @@ typedef struct {
  * (0 for an invalid p).  Its first 8192 bytes are a control block that the
  * library keeps valid from call to call (32-bit words: 2 = launches of the
  * one-launch kernels, 3 = waits that hit the spin limit, 4 = that limit in
- * polls (0 = the built-in 4M; the only word a caller may set, e.g. to test
- * the give-up path), 64 = finished-workgroup counter, 65 = launch epoch,
+ * polls (0 = the built-in 4M; -1 = give up at once in the d = 128 kernel and
+ * after one poll in the d = 64 kernel; the only word a caller may set, e.g.
+ * to test the give-up path), 64 = finished-workgroup counter, 65 = launch epoch,
  * then a table of XCD ids): zero-fill the workspace once before its first
  * use and write nothing else in it afterwards.  The rest holds per-chunk or
  * per-segment partial summaries.
