@@ -36,7 +36,7 @@ def lib():
     return hla.load()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("hla_forward_chunked", "hla_backward_chunked", "hla_decode_step", "hla_state_compose"):
         assert name in fns
