@@ -41,6 +41,8 @@ def make(B, H, n, d, dv, dtype, gk, norm, seed):
         g = inputs.gamma_list_fp32([0.97] * H)
     elif gk == "per_head":
         g = inputs.gamma_list_fp32([1 - 2.0 ** -(3 + h % 6) for h in range(H)])
+    elif gk == "strong":  # g^k underflows fp32 inside a 128-token chunk (0.3^80 < 1e-38)
+        g = inputs.gamma_list_fp32([0.3, 0.6][:H])
     dout = inputs.upstream(B, H, n, dv, seed=seed + 7)
     return q, k, v, dout, g
 
@@ -74,6 +76,7 @@ CASES = [
     (2, 2, 1, 64, 64, 64, torch.bfloat16, None, 0.0, False),
     (1, 1, 64, 16, 16, 16, torch.float32, "decay", 0.0, True),
     (1, 3, 200, 64, 16, 128, torch.bfloat16, "per_head", 0.5, False),
+    (1, 2, 300, 32, 32, 128, torch.float32, "strong", 0.2, False),
 ]
 
 
