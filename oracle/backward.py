@@ -19,7 +19,7 @@ gist.science page "Methodik" item 1 for the read-out q^T(S C - G)):
     out_t = num_t, or num_t / den_t with normalize
 
 starting from the zero state or from a given state (S, C, m, G, h) at
-position -1, held constant.  The pages' training claim is that this scan
+position -1 (held constant, or, on request, differentiated as well).  The pages' training claim is that this scan
 is differentiated like any other layer; here the gradient of the scalar
 sum_t <out_t, dout_t> with respect to q, k and v is taken by torch's
 autograd through exactly these updates, written with plain tensor ops in
@@ -45,6 +45,14 @@ def _t64(a) -> torch.Tensor:
     return torch.as_tensor(np.asarray(a, dtype=np.float64))
 
 
+def _part(a) -> torch.Tensor:
+    """A state part: kept as is when it is a float64 tensor that requires a
+    gradient (so autograd reaches it), else converted like any input."""
+    if isinstance(a, torch.Tensor) and a.requires_grad:
+        return a
+    return _t64(a)
+
+
 def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        gamma: Optional[Sequence[float]] = None, lam: float = 0.0,
                        normalize: bool = False, init=None):
@@ -68,8 +76,8 @@ def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         m = torch.zeros(N, d, dtype=torch.float64)
         h = torch.zeros(N, d, dtype=torch.float64)
     else:
-        S, C, G = (_t64(x).reshape(N, d, w) for x, w in ((init.S, d), (init.C, dv), (init.G, dv)))
-        m, h = (_t64(x).reshape(N, d) for x in (init.m, init.h))
+        S, C, G = (_part(x).reshape(N, d, w) for x, w in ((init.S, d), (init.C, dv), (init.G, dv)))
+        m, h = (_part(x).reshape(N, d) for x in (init.m, init.h))
     outs, dens = [], []
     for t in range(n):
         qt, kt, vt = qf[:, t], kf[:, t], vf[:, t]
@@ -94,16 +102,49 @@ def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, den
 
 
+class _Init:
+    def __init__(self, S, C, m, G, h):
+        self.S, self.C, self.m, self.G, self.h = S, C, m, G, h
+
+
 def backward(q, k, v, dout, gamma: Optional[Sequence[float]] = None, lam: float = 0.0,
-             normalize: bool = False, init=None):
+             normalize: bool = False, init=None, init_grad: bool = False):
     """Gradients (dq, dk, dv) of sum(out * dout), from the zero state or from
-    ``init`` (held constant; see :func:`forward_recurrence`).
+    ``init`` (see :func:`forward_recurrence`).
 
     q, k: [B,H,n,d]; v, dout: [B,H,n,dv]; any real dtype (converted exactly to
-    float64).  Returns float64 numpy arrays shaped like q, k, v."""
+    float64).  Returns float64 numpy arrays shaped like q, k, v.  With
+    ``init_grad`` a fourth item is returned: a dict of the gradients with
+    respect to the initial state's parts, S [N,d,d], C [N,d,dv], m [N,d],
+    G [N,d,dv], h [N,d] (N = B*H; a zero initial state when ``init`` is None).
+    Every entry of S counts as its own variable, with the read-out written as
+    (S_t q_t)^T C_t."""
     q, k, v, dout = (_t64(x).clone().requires_grad_(i < 3) for i, x in enumerate((q, k, v, dout)))
-    if q.shape[2] == 0:
-        return (np.zeros(tuple(q.shape)), np.zeros(tuple(k.shape)), np.zeros(tuple(v.shape)))
-    out, _ = forward_recurrence(q, k, v, gamma, lam, normalize, init)
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    N = B * H
+    ini = init
+    if init_grad:
+        if init is None:
+            parts = [torch.zeros(N, d, d), torch.zeros(N, d, dv), torch.zeros(N, d),
+                     torch.zeros(N, d, dv), torch.zeros(N, d)]
+            parts = [x.to(torch.float64) for x in parts]
+        else:
+            parts = [_t64(x).reshape(shape) for x, shape in
+                     ((init.S, (N, d, d)), (init.C, (N, d, dv)), (init.m, (N, d)),
+                      (init.G, (N, d, dv)), (init.h, (N, d)))]
+        parts = [x.clone().requires_grad_(True) for x in parts]
+        ini = _Init(*parts)
+    if n == 0:
+        grads = (np.zeros(tuple(q.shape)), np.zeros(tuple(k.shape)), np.zeros(tuple(v.shape)))
+        if init_grad:
+            return grads + ({key: np.zeros(tuple(x.shape)) for key, x in
+                             zip(("S", "C", "m", "G", "h"), parts)},)
+        return grads
+    out, _ = forward_recurrence(q, k, v, gamma, lam, normalize, ini)
     (out * dout).sum().backward()
-    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+    grads = (q.grad.numpy(), k.grad.numpy(), v.grad.numpy())
+    if init_grad:
+        return grads + ({key: x.grad.numpy() if x.grad is not None else np.zeros(tuple(x.shape))
+                         for key, x in zip(("S", "C", "m", "G", "h"), parts)},)
+    return grads

@@ -141,3 +141,81 @@ def test_gradients_from_a_state_are_those_of_the_whole_sequence(oracle_mod):
     part = ob.backward(q[:, :, p:], k[:, :, p:], v[:, :, p:], dout[:, :, p:], g, 0.3, False, st)
     for a, b in zip(whole, part):
         np.testing.assert_allclose(a[:, :, p:], b, rtol=1e-11, atol=1e-13)
+
+
+def _prefix_state(oracle_mod, seed, B, H, p, d, dv, g, lam):
+    """A method-produced state (symmetric S) from a random prefix of p tokens,
+    with C, m, G, h then moved off the method's manifold by random offsets so
+    every part of the initial state is an independent variable."""
+    q, k, v = rnd(seed, (B, H, p, d), (B, H, p, d), (B, H, p, dv))
+    _, _, st = oracle_mod.forward(q, k, v, gamma=g, lam=lam)
+    N = B * H
+    oC, om, oG, oh = rnd(seed + 1, (N, d, dv), (N, d), (N, d, dv), (N, d), scale=0.3)
+    st.C = st.C + oC; st.m = st.m + om; st.G = st.G + oG; st.h = st.h + oh
+    return st
+
+
+@pytest.mark.parametrize("g,lam,norm", CASES)
+@pytest.mark.parametrize("part", ["S", "C", "m", "G", "h"])
+def test_init_gradients_match_finite_differences(oracle_mod, g, lam, norm, part):
+    """Directional derivative of the C oracle's loss along a random direction
+    of one part of the initial state (symmetric for S, the form the method's
+    states take) against <dinit, u>."""
+    B, H, n, d, dv = 1, 2, 9, 4, 3
+    q, k, v, dout = rnd(41, (B, H, n, d), (B, H, n, d), (B, H, n, dv), (B, H, n, dv))
+    if norm:
+        q, k = np.abs(q) + 0.3, np.abs(k) + 0.3
+    st = _prefix_state(oracle_mod, 43, B, H, 5, d, dv, g, lam)
+    if norm:  # positive-leaning prefix: denominators stay away from zero
+        st.m = np.abs(st.m) + 0.5; st.h = 0.1 * st.h
+    *_, dini = ob.backward(q, k, v, dout, g, lam, norm, st, init_grad=True)
+    base = getattr(st, part)
+    u = rnd(47, base.shape, scale=1.0)[0]
+    if part == "S":
+        u = u + np.swapaxes(u, -1, -2)
+    eps = 1e-5
+
+    def moved(sign):
+        s2 = st.__class__(st.S.copy(), st.C.copy(), st.m.copy(), st.G.copy(), st.h.copy(), st.rho.copy())
+        setattr(s2, part, base + sign * eps * u)
+        out, _, _ = oracle_mod.forward(q, k, v, gamma=g, lam=lam, normalize=norm, init=s2, want_state=False)
+        return float((out * dout).sum())
+
+    fd = (moved(1) - moved(-1)) / (2 * eps)
+    an = float((dini[part] * u).sum())
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+
+
+def test_init_gradient_of_a_zero_state_is_the_prefix_chain_rule(oracle_mod):
+    """Gradients with respect to a zero initial state, checked against the
+    whole sequence: with the read-out of token t equal to q_t^T X_t where
+    X_t = g^2 X_{t-1} + S_t q_t v_t^T (X = S C - G), the gradient of G_{-1}
+    is -sum_t g^(2(t+1)) q_t dout_t^T, which a prepended token with k = 0
+    cannot change.  Also: with no ridge and no ratio, dC_{-1} and dm_{-1}
+    vanish at S_{-1} = 0, and dh_{-1} is zero without the ratio."""
+    B, H, n, d, dv = 1, 2, 10, 4, 3
+    q, k, v, dout = rnd(51, (B, H, n, d), (B, H, n, d), (B, H, n, dv), (B, H, n, dv))
+    g = [0.9, 0.7]
+    *_, dini = ob.backward(q, k, v, dout, g, 0.0, False, None, init_grad=True)
+    gg = np.asarray(g)
+    pw = gg[:, None] ** (2 * (np.arange(n)[None, :] + 1))          # [H, n]
+    want_G = -np.einsum("hn,hna,hnj->haj", pw, q[0], dout[0])
+    np.testing.assert_allclose(dini["G"], want_G, rtol=1e-12, atol=1e-14)
+    # the S_t C_t and G_t paths cancel exactly in the algebra, to rounding here
+    assert np.abs(dini["C"]).max() <= 1e-13 and np.abs(dini["m"]).max() <= 1e-13
+    assert np.all(dini["h"] == 0.0)
+    # dS at S_{-1} = 0, C_{-1} = 0: sum_j g^(j+1) q_j w_j^T with w_j = Gb_j v_j,
+    # Gb_j = sum_{t>=j} g^(2(t-j)) q_t dout_t^T -- written out per token here
+    want_S = np.zeros((H, d, d))
+    for hh in range(H):
+        for j in range(n):
+            Gb = sum(gg[hh] ** (2 * (t - j)) * np.outer(q[0, hh, t], dout[0, hh, t]) for t in range(j, n))
+            want_S[hh] += gg[hh] ** (j + 1) * np.outer(q[0, hh, j], Gb @ v[0, hh, j])
+    np.testing.assert_allclose(dini["S"], want_S, rtol=1e-11, atol=1e-13)
+
+
+def test_init_gradient_empty_sequence():
+    *_, dini = ob.backward(np.zeros((1, 2, 0, 4)), np.zeros((1, 2, 0, 4)), np.zeros((1, 2, 0, 3)),
+                           np.zeros((1, 2, 0, 3)), init_grad=True)
+    assert dini["S"].shape == (2, 4, 4) and dini["C"].shape == (2, 4, 3)
+    assert all(np.all(x == 0.0) for x in dini.values())
