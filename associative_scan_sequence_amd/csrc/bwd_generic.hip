@@ -64,6 +64,8 @@ struct BwdArgs {
     float *RG, *rg, *RC, *rc, *T;        // right slots [BH][nc+1][..]; slot c = state at chunk c's start
     float *W;                            // [BH][nc][w][d]
     GammaTab gam;
+    hla_state ini;                       // initial state (ini.S null: zero state)
+    hla_state dini;                      // its gradient (dini.S null: not formed)
 };
 
 __device__ __forceinline__ size_t slot(const BwdArgs &a, int bh, int c) {
@@ -393,6 +395,78 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
     store_tile<RT, MC>(a.gv + tok * DV, L, DV, acc);
 }
 
+// ---- gradient of the initial state (the state at position -1), one
+// workgroup per row r of the d rows of every head.  With C' = [C | m] of the
+// initial state (zero when none is given), Gb0' = [Gb_0 | gb_0] and
+// Cb0' = [Cb_0 | cb_0] the right slots at token 0, and w_j the kept W rows:
+//   dS[r][b]  = g^2 sum_c C'[r][c] Gb0'[b][c] + sum_j g^(j+1) q_j[r] w_j[b]
+//   dC'[r][c] = g^2 (S Gb0')[r][c] + lambda g Cb0'[r][c]
+//   dG'[r][c] = -g^2 Gb0'[r][c]              (G' = [G | h])
+// The first two come from the read-out (S_t q_t)^T C_t of every token and the
+// carry X = S C - G with X_{-1} scaled by g^(2(t+1)); S's entries count as
+// independent variables.
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_init(BwdArgs a, hla_state ini, hla_state dini) {
+    constexpr int NG = kThreads / D;  // token groups of the dS sum
+    __shared__ float red[NG][D];
+    const int r = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const float g = head_gamma(a.gam, bh % a.H), g2 = g * g;
+    const size_t s0 = slot(a, bh, 0);
+    const float *Gb = a.RG + s0 * D * DV, *gb = a.rg + s0 * D;
+    const bool ridge = a.ridge != 0.0f;
+    {
+        const int b = tid % D, grp = tid / D;
+        const T *q = static_cast<const T *>(a.q) + static_cast<size_t>(bh) * a.n * D;
+        const float *W = a.W + static_cast<size_t>(bh) * a.nc * a.w * D;
+        float acc = 0.0f;
+        for (int j = grp; j < a.n; j += NG) {
+            const int c = j / a.w, s = j - c * a.w;
+            acc += gpow(g, j + 1) * Elem<T>::get(q, static_cast<size_t>(j) * D + r) *
+                   W[(static_cast<size_t>(c) * a.w + s) * D + b];
+        }
+        red[grp][b] = acc;
+    }
+    __syncthreads();
+    const size_t so = static_cast<size_t>(bh);
+    if (tid < D) {
+        const int b = tid;
+        float x = 0.0f;
+        for (int k = 0; k < NG; ++k) x += red[k][b];
+        if (ini.S) {
+            const float *Cr = ini.C + (so * D + r) * DV;
+            float y = ini.m[so * D + r] * gb[b];
+            for (int c = 0; c < DV; ++c) y += Cr[c] * Gb[static_cast<size_t>(b) * DV + c];
+            x += g2 * y;
+        }
+        dini.S[(so * D + r) * D + b] = x;
+    }
+    for (int c = tid; c <= DV; c += kThreads) {  // column DV is the m / h column
+        const float *gcol = c < DV ? Gb + c : gb;
+        const int ld = c < DV ? DV : 1;
+        float y = 0.0f;
+        if (ini.S) {
+            const float *Sr = ini.S + (so * D + r) * D;
+            for (int b = 0; b < D; ++b) y += Sr[b] * gcol[static_cast<size_t>(b) * ld];
+        }
+        float x = g2 * y;
+        if (ridge) x += a.ridge * g * (c < DV ? a.RC[(s0 * D + r) * DV + c] : a.rc[s0 * D + r]);
+        const float gr = -g2 * gcol[static_cast<size_t>(r) * ld];
+        if (c < DV) {
+            dini.C[(so * D + r) * DV + c] = x;
+            dini.G[(so * D + r) * DV + c] = gr;
+        } else {
+            dini.m[so * D + r] = x;
+            dini.h[so * D + r] = gr;
+        }
+    }
+    if (dini.rho && r == 0 && tid == 0) dini.rho[bh] = 0.0f;  // rho does not reach any output
+}
+
+__global__ __launch_bounds__(kThreads) void k_fill_zero(float *p, size_t count) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < count) p[i] = 0.0f;
+}
+
 template <typename T, int D, int DV>
 hipError_t launch_bwd(const BwdArgs &a, int BH, hipStream_t st) {
     const dim3 blk(kThreads), grid(a.nc, BH);
@@ -422,6 +496,7 @@ hipError_t launch_bwd(const BwdArgs &a, int BH, hipStream_t st) {
         hipLaunchKernelGGL((k_bwd_dk<T, D, DV, 4>), grid, blk, 0, st, a);
         hipLaunchKernelGGL((k_bwd_dv<T, D, DV, 4>), grid, blk, 0, st, a);
     }
+    if (a.dini.S) hipLaunchKernelGGL((k_bwd_init<T, D, DV>), dim3(D, BH), blk, 0, st, a, a.ini, a.dini);
     return hipGetLastError();
 }
 
@@ -514,8 +589,21 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t st) {
     a.T = reinterpret_cast<float *>(base + L.T);
     a.W = reinterpret_cast<float *>(base + L.W);
     a.gam = f.gam;
+    a.ini = f.init;
+    a.dini = p.dinit;
     if (f.dtype == HLA_BF16) return pick_d<uint16_t>(a, BH, st);
     return pick_d<float>(a, BH, st);
+}
+
+hipError_t zero_state_grad(const hla_state &s, int BH, int d, int dv, hipStream_t st) {
+    const size_t N = static_cast<size_t>(BH);
+    float *parts[6] = {s.S, s.C, s.m, s.G, s.h, s.rho};
+    const size_t sizes[6] = {N * d * d, N * d * dv, N * d, N * d * dv, N * d, N};
+    for (int i = 0; i < 6; ++i)
+        if (parts[i] && sizes[i])
+            hipLaunchKernelGGL(k_fill_zero, dim3((sizes[i] + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
+                               parts[i], sizes[i]);
+    return hipGetLastError();
 }
 
 }  // namespace hla

@@ -277,7 +277,8 @@ size_t hla_backward_workspace_size(const hla_params *p) {
 
 hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
                                 const hla_state *init, const float *dout, float *dq, float *dk, float *dv,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                hla_state *dinit, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
     Geometry geo{};
     hla_status s = forward_geometry(p, &geo);
     if (s != HLA_OK) return s;
@@ -286,7 +287,22 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &fp.gam);
     if (s != HLA_OK) return s;
     const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
-    if (n == 0) return ok();
+    if (init && (s = check_state(init, "init")) != HLA_OK) return s;
+    if (dinit && (s = check_state(dinit, "dinit")) != HLA_OK) return s;
+    if (dinit) {  // disjoint from each other and from the initial state
+        std::vector<Span> douts, dins;
+        state_spans(dinit, "dinit", BH, p->d, p->dv, &douts);
+        if (init) state_spans(init, "init", BH, p->d, p->dv, &dins);
+        std::string detail;
+        if (first_overlap(douts, dins, &detail))
+            return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    }
+    if (n == 0) {  // the gradient of an empty sum
+        if (!dinit) return ok();
+        const hipError_t e = hla::zero_state_grad(*dinit, int(BH), p->d, p->dv, stream);
+        if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
+        return ok();
+    }
     const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
     const void *req[7] = {q, k, v, dout, dq, dk, dv};
     const char *nm[7] = {"q", "k", "v", "dout", "dq", "dk", "dv"};
@@ -294,7 +310,6 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
         if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
         if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
     }
-    if (init && (s = check_state(init, "init")) != HLA_OK) return s;
     const size_t need = hla::generic_backward_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
     if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
@@ -311,6 +326,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     ins.push_back(span("v", v, BH * n * p->dv * esz));
     ins.push_back(span("dout", dout, BH * n * p->dv * 4));
     if (init) state_spans(init, "init", BH, p->d, p->dv, &ins);
+    if (dinit) state_spans(dinit, "dinit", BH, p->d, p->dv, &outs);
     std::string detail;
     if (first_overlap(outs, ins, &detail))
         return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
@@ -321,6 +337,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     if (init) fp.init = *init;
     fp.ws = workspace; fp.ws_bytes = workspace_bytes;
     bp.dout = dout; bp.dq = dq; bp.dk = dk; bp.dv = dv;
+    if (dinit) bp.dinit = *dinit;
     const hipError_t e = hla::generic_backward(bp, stream);
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
     return ok();

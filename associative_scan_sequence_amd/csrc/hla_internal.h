@@ -66,9 +66,13 @@ struct BwdProblem {
     FwdProblem f;        // the forward call (fin and den unused); f.ws = backward data area
     const float *dout;   // [B,H,n,dv]
     float *dq, *dk, *dv; // [B,H,n,d], [B,H,n,d], [B,H,n,dv]
+    hla_state dinit;     // gradient with respect to the initial state; dinit.S null: not formed
 };
 size_t generic_backward_workspace_bytes(int BH, int n, int d, int dv, int w);
 hipError_t generic_backward(const BwdProblem &p, hipStream_t s);
+// Writes zeros into every part of s that is set (the initial-state gradient
+// of an empty sequence).
+hipError_t zero_state_grad(const hla_state &s, int BH, int d, int dv, hipStream_t st);
 
 // One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
 // ridge, denominator and normalisation (no init or final state).

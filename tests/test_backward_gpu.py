@@ -197,3 +197,89 @@ def test_autograd_op(dtype):
         for name, x, r in zip(("dq", "dk", "dv"), got, ref):
             e = slab_err(x, r, lead=2)
             assert e <= 2 ** -8, f"{name}: {e:.3e}"
+
+
+def _dinit_check(got, ref):
+    """Each part's max abs error over the heads' largest gradient entry in
+    that part, floored at 1e-3 of the largest entry over all parts (parts
+    that vanish in the algebra are only zero to rounding in the oracle)."""
+    top = max(float(np.abs(ref[p]).max()) for p in ref)
+    for part in ("S", "C", "m", "G", "h"):
+        x = getattr(got, part).double().cpu().numpy()
+        r = np.asarray(ref[part]).reshape(x.shape)
+        scale = max(float(np.abs(r).max()), 1e-3 * top, 1e-30)
+        e = float(np.abs(x - r).max()) / scale
+        print(f"dinit.{part}: {e:.3e}")
+        assert e <= GTOL, f"dinit.{part}: error {e:.3e} > {GTOL:.0e}"
+
+
+DINIT_CASES = [
+    # dtype, d, dv, chunk, n, gamma, ridge, normalize, with init
+    (torch.float32, 32, 32, 16, 150, "per_head", 0.1, False, True),
+    (torch.bfloat16, 64, 64, 64, 150, "decay", 0.0, False, True),
+    (torch.float32, 32, 16, 32, 97, "per_head", 0.2, True, True),
+    (torch.bfloat16, 128, 128, 128, 300, "decay", 1e-3, True, True),
+    (torch.float32, 16, 64, 16, 70, None, 0.0, False, False),
+    (torch.float32, 64, 32, 64, 130, "per_head", 0.3, False, False),
+]
+
+
+@pytest.mark.parametrize("case", DINIT_CASES, ids=lambda c: f"{'bf16' if c[0] == torch.bfloat16 else 'f32'}"
+                         f"-d{c[1]}dv{c[2]}w{c[3]}n{c[4]}-{c[5]}-l{c[6]}-r{int(c[7])}-init{int(c[8])}")
+def test_backward_initial_state_gradient(case):
+    """dL/d(init) through hla_backward_chunked against the fp64 autograd
+    oracle, from a prefix state (rounded to fp32 and given to both sides) or
+    from the zero state; dq, dk, dv are the same bits with and without it."""
+    import types
+
+    import oracle
+    from oracle import backward as ob
+    dtype, d, dv, chunk, n, gk, lam, norm, with_init = case
+    B, H, n0 = 1, 2, 60
+    q, k, v = inputs.qkv(B, H, n0 + n, d, dv, dtype, seed=91 + d + n)
+    if norm:
+        q, k = (x.float().abs().add(0.1).to(dtype) for x in (q, k))
+    g = None
+    if gk == "decay":
+        g = inputs.gamma_list_fp32([0.97] * H)
+    elif gk == "per_head":
+        g = inputs.gamma_list_fp32([0.95, 0.99])
+    lam = inputs.ridge_fp32(lam)
+    init = ref_init = None
+    if with_init:
+        _, _, st = oracle.forward(q[:, :, :n0], k[:, :, :n0], v[:, :, :n0], gamma=g, lam=lam)
+        f32 = {name: torch.tensor(getattr(st, name), dtype=torch.float32) for name in ("S", "C", "m", "G", "h")}
+        if not norm:  # off the method's states: C, G moved independently of S
+            f32["C"] = f32["C"] + 0.3 * inputs.upstream(1, 1, B * H * d, dv, seed=93).reshape(B * H, d, dv)
+            f32["G"] = f32["G"] - 0.2 * inputs.upstream(1, 1, B * H * d, dv, seed=94).reshape(B * H, d, dv)
+        init = hla.State(*(f32[x].to(DEV) for x in ("S", "C", "m", "G", "h")))
+        ref_init = types.SimpleNamespace(**f32)
+    qs, ks, vs = (x[:, :, n0:].contiguous() for x in (q, k, v))
+    dout = inputs.upstream(B, H, n, dv, seed=97)
+    qg, kg, vg, dg = (x.to(DEV) for x in (qs, ks, vs, dout))
+    dini = hla.State.empty(B * H, d, dv, DEV)
+    for t in dini.tensors():
+        t.fill_(float("nan"))
+    got = hla.backward_chunked(qg, kg, vg, dg, gamma=g, ridge=lam, normalize=norm, chunk=chunk, init=init,
+                               dinit=dini)
+    plain = hla.backward_chunked(qg, kg, vg, dg, gamma=g, ridge=lam, normalize=norm, chunk=chunk, init=init)
+    torch.cuda.synchronize()
+    for a, b in zip(got, plain):
+        assert torch.equal(a, b)
+    assert torch.all(dini.rho == 0.0)
+    *ref, rdini = ob.backward(qs, ks, vs, dout, g, lam, norm, ref_init, init_grad=True)
+    check([x.cpu() for x in got], ref)
+    _dinit_check(dini, rdini)
+
+
+def test_backward_initial_state_gradient_empty_sequence():
+    """n = 0: the gradient of an empty sum is zero in every part set."""
+    q = torch.zeros(1, 2, 0, 32, dtype=torch.float32, device=DEV)
+    v = torch.zeros(1, 2, 0, 16, dtype=torch.float32, device=DEV)
+    dini = hla.State.empty(2, 32, 16, DEV)
+    for t in dini.tensors():
+        t.fill_(float("nan"))
+    hla.backward_chunked(q, q, v, v.clone(), dinit=dini)
+    torch.cuda.synchronize()
+    for t in dini.tensors():
+        assert torch.all(t == 0.0)
