@@ -55,12 +55,13 @@ def _part(a) -> torch.Tensor:
 
 def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        gamma: Optional[Sequence[float]] = None, lam: float = 0.0,
-                       normalize: bool = False, init=None):
+                       normalize: bool = False, init=None, return_state: bool = False):
     """The serial recurrence in float64 torch ops (differentiable).
 
     q, k: [B,H,n,d]; v: [B,H,n,dv]; init: None or an object with S [N,d,d],
     C [N,d,dv], m [N,d], G [N,d,dv], h [N,d] (N = B*H), the state before
-    token 0.  Returns (out [B,H,n,dv], den [B,H,n])."""
+    token 0.  Returns (out [B,H,n,dv], den [B,H,n]), and with ``return_state``
+    also the final state as a tuple (S, C, m, G, h) shaped as ``init``'s parts."""
     B, H, n, d = q.shape
     dv = v.shape[-1]
     N = B * H
@@ -95,10 +96,13 @@ def forward_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         outs.append(num / den.unsqueeze(-1) if normalize else num)
         dens.append(den)
     if n == 0:
-        return (torch.zeros(B, H, 0, dv, dtype=torch.float64),
-                torch.zeros(B, H, 0, dtype=torch.float64))
-    out = torch.stack(outs, 1).reshape(B, H, n, dv)
-    den = torch.stack(dens, 1).reshape(B, H, n)
+        out = torch.zeros(B, H, 0, dv, dtype=torch.float64)
+        den = torch.zeros(B, H, 0, dtype=torch.float64)
+    else:
+        out = torch.stack(outs, 1).reshape(B, H, n, dv)
+        den = torch.stack(dens, 1).reshape(B, H, n)
+    if return_state:
+        return out, den, (S, C, m, G, h)
     return out, den
 
 
@@ -108,7 +112,7 @@ class _Init:
 
 
 def backward(q, k, v, dout, gamma: Optional[Sequence[float]] = None, lam: float = 0.0,
-             normalize: bool = False, init=None, init_grad: bool = False):
+             normalize: bool = False, init=None, init_grad: bool = False, dfinal=None):
     """Gradients (dq, dk, dv) of sum(out * dout), from the zero state or from
     ``init`` (see :func:`forward_recurrence`).
 
@@ -118,7 +122,9 @@ def backward(q, k, v, dout, gamma: Optional[Sequence[float]] = None, lam: float 
     respect to the initial state's parts, S [N,d,d], C [N,d,dv], m [N,d],
     G [N,d,dv], h [N,d] (N = B*H; a zero initial state when ``init`` is None).
     Every entry of S counts as its own variable, with the read-out written as
-    (S_t q_t)^T C_t."""
+    (S_t q_t)^T C_t.  ``dfinal``, an object with S, C, m, G, h shaped as a
+    state, adds sum over the parts of <final part, dfinal part> to the loss:
+    the gradient a later segment hands back for the final state."""
     q, k, v, dout = (_t64(x).clone().requires_grad_(i < 3) for i, x in enumerate((q, k, v, dout)))
     B, H, n, d = q.shape
     dv = v.shape[-1]
@@ -135,15 +141,20 @@ def backward(q, k, v, dout, gamma: Optional[Sequence[float]] = None, lam: float 
                       (init.G, (N, d, dv)), (init.h, (N, d)))]
         parts = [x.clone().requires_grad_(True) for x in parts]
         ini = _Init(*parts)
-    if n == 0:
+    if n == 0 and dfinal is None:
         grads = (np.zeros(tuple(q.shape)), np.zeros(tuple(k.shape)), np.zeros(tuple(v.shape)))
         if init_grad:
             return grads + ({key: np.zeros(tuple(x.shape)) for key, x in
                              zip(("S", "C", "m", "G", "h"), parts)},)
         return grads
-    out, _ = forward_recurrence(q, k, v, gamma, lam, normalize, ini)
-    (out * dout).sum().backward()
-    grads = (q.grad.numpy(), k.grad.numpy(), v.grad.numpy())
+    out, _, fin = forward_recurrence(q, k, v, gamma, lam, normalize, ini, return_state=True)
+    loss = (out * dout).sum()
+    if dfinal is not None:
+        for x, name in zip(fin, ("S", "C", "m", "G", "h")):
+            loss = loss + (x * _t64(getattr(dfinal, name)).reshape(x.shape)).sum()
+    if loss.requires_grad:
+        loss.backward()
+    grads = tuple(x.grad.numpy() if x.grad is not None else np.zeros(tuple(x.shape)) for x in (q, k, v))
     if init_grad:
         return grads + ({key: x.grad.numpy() if x.grad is not None else np.zeros(tuple(x.shape))
                          for key, x in zip(("S", "C", "m", "G", "h"), parts)},)

@@ -219,3 +219,67 @@ def test_init_gradient_empty_sequence():
                            np.zeros((1, 2, 0, 3)), init_grad=True)
     assert dini["S"].shape == (2, 4, 4) and dini["C"].shape == (2, 4, 3)
     assert all(np.all(x == 0.0) for x in dini.values())
+
+
+def _fin_loss(oracle_mod, q, k, v, dout, g, lam, norm, st, dfin):
+    out, _, fin = oracle_mod.forward(q, k, v, gamma=g, lam=lam, normalize=norm, init=st)
+    tot = float((out * dout).sum())
+    for name in ("S", "C", "m", "G", "h"):
+        tot += float((getattr(fin, name) * dfin[name]).sum())
+    return tot
+
+
+@pytest.mark.parametrize("g,lam,norm", CASES)
+@pytest.mark.parametrize("which", ["q", "k", "v", "S", "C", "G"])
+def test_final_state_gradients_match_finite_differences(oracle_mod, g, lam, norm, which):
+    """With a gradient flowing into the final state, <grad, u> for a random
+    direction of an input or of a part of the initial state against central
+    differences of the C oracle's loss sum <out, dout> + sum <fin, dfin>."""
+    B, H, n, d, dv = 1, 2, 9, 4, 3
+    q, k, v, dout = rnd(61, (B, H, n, d), (B, H, n, d), (B, H, n, dv), (B, H, n, dv))
+    if norm:
+        q, k = np.abs(q) + 0.3, np.abs(k) + 0.3
+    st = _prefix_state(oracle_mod, 63, B, H, 4, d, dv, g, lam)
+    if norm:
+        st.m = np.abs(st.m) + 0.5; st.h = 0.1 * st.h
+    N = B * H
+    dfin = dict(zip(("S", "C", "m", "G", "h"),
+                    rnd(65, (N, d, d), (N, d, dv), (N, d), (N, d, dv), (N, d), scale=0.7)))
+    import types
+    dq, dk, dv_, dini = ob.backward(q, k, v, dout, g, lam, norm, st, init_grad=True,
+                                    dfinal=types.SimpleNamespace(**dfin))
+    eps = 1e-5
+    xs = {"q": q, "k": k, "v": v}
+    if which in xs:
+        base, an_grad = xs[which], {"q": dq, "k": dk, "v": dv_}[which]
+    else:
+        base, an_grad = getattr(st, which), dini[which]
+    u = rnd(67, base.shape, scale=1.0)[0]
+    if which == "S":
+        u = u + np.swapaxes(u, -1, -2)
+
+    def moved(sign):
+        s2 = st.__class__(st.S.copy(), st.C.copy(), st.m.copy(), st.G.copy(), st.h.copy(), st.rho.copy())
+        x2 = {kk: vv.copy() for kk, vv in xs.items()}
+        if which in x2:
+            x2[which] = base + sign * eps * u
+        else:
+            setattr(s2, which, base + sign * eps * u)
+        return _fin_loss(oracle_mod, x2["q"], x2["k"], x2["v"], dout, g, lam, norm, s2, dfin)
+
+    fd = (moved(1) - moved(-1)) / (2 * eps)
+    an = float((an_grad * u).sum())
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+
+
+def test_final_state_gradient_of_an_empty_sequence_is_passed_through(oracle_mod):
+    """n = 0: the final state is the initial one, so dinit = dfinal."""
+    import types
+    d, dv = 4, 3
+    st = _prefix_state(oracle_mod, 69, 1, 2, 5, d, dv, [0.9, 0.8], 0.0)
+    dfin = dict(zip(("S", "C", "m", "G", "h"), rnd(70, (2, d, d), (2, d, dv), (2, d), (2, d, dv), (2, d))))
+    *_, dini = ob.backward(np.zeros((1, 2, 0, d)), np.zeros((1, 2, 0, d)), np.zeros((1, 2, 0, dv)),
+                           np.zeros((1, 2, 0, dv)), [0.9, 0.8], 0.0, False, st, init_grad=True,
+                           dfinal=types.SimpleNamespace(**dfin))
+    for name in dfin:
+        np.testing.assert_array_equal(dini[name], dfin[name])
