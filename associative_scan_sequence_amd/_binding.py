@@ -64,7 +64,7 @@ def load(path: str = LIB_PATH):
     lib.hla_forward_chunked.restype = ctypes.c_int
     lib.hla_backward_workspace_size.argtypes = [pp]
     lib.hla_backward_workspace_size.restype = sz
-    lib.hla_backward_chunked.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, vp, ps, vp, sz, vp]
+    lib.hla_backward_chunked.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, vp, ps, ps, vp, sz, vp]
     lib.hla_backward_chunked.restype = ctypes.c_int
     lib.hla_decode_step.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
     lib.hla_decode_step.restype = ctypes.c_int
@@ -225,12 +225,14 @@ def backward_workspace_size(B, H, n, d, dv, *, chunk=0, dtype=torch.bfloat16, ga
 def backward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *,
                      gamma=None, ridge: float = 0.0, normalize: bool = False, chunk: int = 0,
                      init: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
-                     grads=None, dinit: Optional[State] = None):
+                     grads=None, dinit: Optional[State] = None, dfinal: Optional[State] = None):
     """Gradients of sum(out * dout) through ``hla_backward_chunked``, from the
     zero state or from ``init``.  q, k: [B,H,n,d]; v, dout: [B,H,n,dv] (dout
     fp32).  Returns (dq, dk, dv), fp32, shaped like q, k, v; ``grads`` may
     supply them.  ``dinit``, if given, receives the gradient with respect to
-    the initial state (``init``, or the zero state)."""
+    the initial state (``init``, or the zero state); ``dfinal``, if given, is
+    a gradient flowing into the final state (added to the loss as
+    sum <final part, dfinal part>)."""
     lib = load()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, (torch.bfloat16, torch.float32))
@@ -258,9 +260,11 @@ def backward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: to
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ini_c = init.c() if init is not None else None
     dini_c = dinit.c() if dinit is not None else None
+    dfin_c = dfinal.c() if dfinal is not None else None
     st = lib.hla_backward_chunked(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   ctypes.byref(ini_c) if ini_c is not None else None, dout.data_ptr(),
                                   grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                                  ctypes.byref(dfin_c) if dfin_c is not None else None,
                                   ctypes.byref(dini_c) if dini_c is not None else None,
                                   ws_ptr, ws_bytes, _stream(dev))
     _check(st)

@@ -12,6 +12,7 @@
 //
 //   u_j  = S_j q_j                                     (forward, kept per chunk)
 //   Gb_j = sum_{t>=j} g^(2(t-j)) q_t g^_t^T            Cb_j: the same with g^(t-j)
+//   (the Cb slots hold lambda Cb, plus the seed of a final-state gradient)
 //   w_j  = Gb_j v^_j        T_i = sum_{j>=i} g^(j-i) (w_j q_j^T + q_j w_j^T)
 //   dq_t = X^_t g^_t + S_t w_t + lambda (C^_t g^_t + Cb_t v^_t)
 //   dk_i = T_i k_i          dv_j = Gb_j^T u_j + lambda Cb_j^T q_j   (first dv columns)
@@ -66,6 +67,8 @@ struct BwdArgs {
     GammaTab gam;
     hla_state ini;                       // initial state (ini.S null: zero state)
     hla_state dini;                      // its gradient (dini.S null: not formed)
+    hla_state dfin;                      // gradient flowing into the final state (dfin.S null: none)
+    int cbar;                            // the C-bar slots are live (ridge, or dfin given)
 };
 
 __device__ __forceinline__ size_t slot(const BwdArgs &a, int bh, int c) {
@@ -109,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_sums(BwdArgs a) {
     const T *q = static_cast<const T *>(a.q) + tok * D;
     const float *gn = a.Gn + tok * DV;
     const float *gd = a.gd ? a.gd + tok : nullptr;
-    const bool ridge = a.ridge != 0.0f;
+    const bool cbar = a.cbar != 0;
+    const float lam = a.ridge;
     const int tid = threadIdx.x;
     pow_table(gt, g, a.w);
     auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
@@ -120,26 +124,26 @@ __global__ __launch_bounds__(kThreads) void k_bwd_sums(BwdArgs a) {
         mm<MR, MC, true>(aG, D, L, st, [&](int r, int t) { return gt[2 * t] * qe(t, r); }, gne);
         store_tile<MR, MC>(a.RG + sl * D * DV, D, DV, aG);
     }
-    if (ridge) {
+    if (cbar) {  // lambda is folded into the C-bar increments
         float aC[MR][MC] = {};
-        mm<MR, MC, true>(aC, D, L, st, [&](int r, int t) { return gt[t] * qe(t, r); }, gne);
+        mm<MR, MC, true>(aC, D, L, st, [&](int r, int t) { return lam * gt[t] * qe(t, r); }, gne);
         store_tile<MR, MC>(a.RC + sl * D * DV, D, DV, aC);
     }
     tile::row_sums(D, gd ? L : 0, [&](int r, int t) { return gt[2 * t] * qe(t, r) * gd[t]; },
                    [&](int r, float x) { a.rg[sl * D + r] = x; });
-    if (ridge)
-        tile::row_sums(D, gd ? L : 0, [&](int r, int t) { return gt[t] * qe(t, r) * gd[t]; },
+    if (cbar)
+        tile::row_sums(D, gd ? L : 0, [&](int r, int t) { return lam * gt[t] * qe(t, r) * gd[t]; },
                        [&](int r, float x) { a.rc[sl * D + r] = x; });
     if (c == a.nc - 1) {  // slot nc: nothing to the right of the last token
         const size_t se = slot(a, bh, a.nc);
         for (int i = tid; i < D * DV; i += kThreads) {
             a.RG[se * D * DV + i] = 0.0f;
-            if (ridge) a.RC[se * D * DV + i] = 0.0f;
+            if (cbar) a.RC[se * D * DV + i] = 0.0f;
         }
         for (int i = tid; i < D * D; i += kThreads) a.T[se * D * D + i] = 0.0f;
         if (tid < D) {
             a.rg[se * D + tid] = 0.0f;
-            if (ridge) a.rc[se * D + tid] = 0.0f;
+            if (cbar) a.rc[se * D + tid] = 0.0f;
         }
     }
 }
@@ -301,12 +305,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
                       [&](int l, int col) { return X0[col * DV + l]; });
     mm<RT, MA, false>(acc, L, D, st, [&](int t, int b) { return gt[t + 1] * Wc[t * D + b]; },
                       [&](int b, int col) { return S0[b * D + col]; });
-    if (lam != 0.0f) {
+    if (lam != 0.0f)
         mm<RT, MA, false>(acc, L, DV, st, [&](int t, int l) { return lam * gt[t + 1] * gne(t, l); },
                           [&](int l, int col) { return C0[col * DV + l]; });
-        mm<RT, MA, false>(acc, L, DV, st, [&](int t, int l) { return lam * gt[L - t] * ve(t, l); },
+    if (a.cbar)  // the C-bar slots already carry lambda
+        mm<RT, MA, false>(acc, L, DV, st, [&](int t, int l) { return gt[L - t] * ve(t, l); },
                           [&](int l, int col) { return RCn[col * DV + l]; });
-    }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         const int t = RT * ty + i;
@@ -316,7 +320,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
         for (int j = 0; j < MA; ++j) {
             const int col = MA * tx + j;
             float x = e * e * gdt * y0[col];
-            if (lam != 0.0f) x += lam * (e * gdt * m0[col] + eh * rcd[col]);
+            if (lam != 0.0f) x += lam * e * gdt * m0[col];
+            if (a.cbar) x += eh * rcd[col];
             acc[i][j] += x;
         }
     }
@@ -389,10 +394,54 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
                      [&](int t, int col) { return gn[static_cast<size_t>(t) * DV + col]; });
     mm<RT, MC, false>(acc, L, D, st, [&](int s, int l) { return gt[2 * (L - s)] * U[s * D + l]; },
                       [&](int l, int col) { return RGn[l * DV + col]; });
-    if (lam != 0.0f)
-        mm<RT, MC, false>(acc, L, D, st, [&](int s, int l) { return lam * gt[L - s] * qe(s, l); },
+    if (a.cbar)
+        mm<RT, MC, false>(acc, L, D, st, [&](int s, int l) { return gt[L - s] * qe(s, l); },
                           [&](int l, int col) { return RCn[l * DV + col]; });
     store_tile<RT, MC>(a.gv + tok * DV, L, DV, acc);
+}
+
+// D[r][b] = dS_f[r][b] + sum_c C_n[r][c] dG_f[b][c] + m_n[r] dh_f[b]: the gradient
+// reaching the final key moment S_n, directly and through G_n = S_n^T C_n - X_n
+// (with C and G widened by their m and h columns).
+template <int D, int DV>
+__device__ __forceinline__ float fin_moment(const BwdArgs &a, int bh, int r, int b) {
+    const size_t sn = slot(a, bh, a.nc), so = static_cast<size_t>(bh);
+    const float *Cn = a.C + (sn * D + r) * DV, *dG = a.dfin.G + (so * D + b) * DV;
+    float x = a.dfin.S[(so * D + r) * D + b] + a.m[sn * D + r] * a.dfin.h[so * D + b];
+    for (int c = 0; c < DV; ++c) x += Cn[c] * dG[c];
+    return x;
+}
+
+// ---- seeds of the right slots at position n from a gradient flowing into the
+// final state, one workgroup per row r of every head (after k_bwd_sums has
+// cleared slot nc, before the reverse prefixes).  The final state reaches the
+// loss through X_n (G_n = S_n^T C_n - X_n), S_n and C_n, each a right carry
+// read one token past the last one, hence the g^-1 and g^-2:
+//   Gb slot nc   = -g^-2 dG_f          (widened by -g^-2 dh_f)
+//   T slot nc    = g^-1 (D + D^T)      (D above)
+//   Cb slot nc   = g^-1 (dC_f + S_n dG_f)   (widened by dm_f + S_n dh_f)
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_seed(BwdArgs a) {
+    const int r = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const float g = head_gamma(a.gam, bh % a.H), gi = 1.0f / g, gi2 = gi * gi;
+    const size_t sn = slot(a, bh, a.nc), so = static_cast<size_t>(bh);
+    for (int b = tid; b < D; b += kThreads)
+        a.T[(sn * D + r) * D + b] = gi * (fin_moment<D, DV>(a, bh, r, b) + fin_moment<D, DV>(a, bh, b, r));
+    const float *Sr = a.S + (sn * D + r) * D;
+    for (int c = tid; c <= DV; c += kThreads) {  // column DV: the m / h column
+        const float *dgc = c < DV ? a.dfin.G + so * D * DV + c : a.dfin.h + so * D;
+        const int ld = c < DV ? DV : 1;
+        float y = c < DV ? a.dfin.C[(so * D + r) * DV + c] : a.dfin.m[so * D + r];
+        for (int b = 0; b < D; ++b) y += Sr[b] * dgc[static_cast<size_t>(b) * ld];
+        const float gs = -gi2 * dgc[static_cast<size_t>(r) * ld];
+        if (c < DV) {
+            a.RG[(sn * D + r) * DV + c] = gs;
+            a.RC[(sn * D + r) * DV + c] = gi * y;
+        } else {
+            a.rg[sn * D + r] = gs;
+            a.rc[sn * D + r] = gi * y;
+        }
+    }
 }
 
 // ---- gradient of the initial state (the state at position -1), one
@@ -401,6 +450,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(BwdArgs a) {
 // Cb0' = [Cb_0 | cb_0] the right slots at token 0, and w_j the kept W rows:
 //   dS[r][b]  = g^2 sum_c C'[r][c] Gb0'[b][c] + sum_j g^(j+1) q_j[r] w_j[b]
 //   dC'[r][c] = g^2 (S Gb0')[r][c] + lambda g Cb0'[r][c]
+//   (+ g^n D[r][b] in dS with a final-state gradient; its C' part arrives
+//   through the seeded Cb slots, which also carry lambda)
 //   dG'[r][c] = -g^2 Gb0'[r][c]              (G' = [G | h])
 // The first two come from the read-out (S_t q_t)^T C_t of every token and the
 // carry X = S C - G with X_{-1} scaled by g^(2(t+1)); S's entries count as
@@ -413,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_init(BwdArgs a, hla_state ini,
     const float g = head_gamma(a.gam, bh % a.H), g2 = g * g;
     const size_t s0 = slot(a, bh, 0);
     const float *Gb = a.RG + s0 * D * DV, *gb = a.rg + s0 * D;
-    const bool ridge = a.ridge != 0.0f;
+    const bool cbar = a.cbar != 0;
     {
         const int b = tid % D, grp = tid / D;
         const T *q = static_cast<const T *>(a.q) + static_cast<size_t>(bh) * a.n * D;
@@ -438,6 +489,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_init(BwdArgs a, hla_state ini,
             for (int c = 0; c < DV; ++c) y += Cr[c] * Gb[static_cast<size_t>(b) * DV + c];
             x += g2 * y;
         }
+        if (a.dfin.S) x += gpow(g, a.n) * fin_moment<D, DV>(a, bh, r, b);
         dini.S[(so * D + r) * D + b] = x;
     }
     for (int c = tid; c <= DV; c += kThreads) {  // column DV is the m / h column
@@ -449,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_init(BwdArgs a, hla_state ini,
             for (int b = 0; b < D; ++b) y += Sr[b] * gcol[static_cast<size_t>(b) * ld];
         }
         float x = g2 * y;
-        if (ridge) x += a.ridge * g * (c < DV ? a.RC[(s0 * D + r) * DV + c] : a.rc[s0 * D + r]);
+        if (cbar) x += g * (c < DV ? a.RC[(s0 * D + r) * DV + c] : a.rc[s0 * D + r]);
         const float gr = -g2 * gcol[static_cast<size_t>(r) * ld];
         if (c < DV) {
             dini.C[(so * D + r) * DV + c] = x;
@@ -475,10 +527,11 @@ hipError_t launch_bwd(const BwdArgs &a, int BH, hipStream_t st) {
         hipLaunchKernelGGL((k_bwd_prep<DV>), dim3((tokens + kThreads - 1) / kThreads), blk, 0, st, a, tokens);
     }
     hipLaunchKernelGGL((k_bwd_sums<T, D, DV>), grid, blk, 0, st, a);
+    if (a.dfin.S) hipLaunchKernelGGL((k_bwd_seed<D, DV>), dim3(D, BH), blk, 0, st, a);
     const RScan sG{a.RG, D * DV}, sg{a.rg, D}, sC{a.RC, D * DV}, sc{a.rc, D}, sT{a.T, D * D}, none{nullptr, 0};
     const int e1 = D * DV + D;
     hipLaunchKernelGGL(k_rprefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sG, sg, 2);
-    if (a.ridge != 0.0f)
+    if (a.cbar)
         hipLaunchKernelGGL(k_rprefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sC, sc, 1);
     // register tile: 4 x 4 per thread for chunks up to 64 tokens, 8 x 8 for 128
     if (a.w > 64) {
@@ -591,6 +644,8 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t st) {
     a.gam = f.gam;
     a.ini = f.init;
     a.dini = p.dinit;
+    a.dfin = p.dfinal;
+    a.cbar = (f.ridge != 0.0f || p.dfinal.S) ? 1 : 0;
     if (f.dtype == HLA_BF16) return pick_d<uint16_t>(a, BH, st);
     return pick_d<float>(a, BH, st);
 }

@@ -277,8 +277,8 @@ size_t hla_backward_workspace_size(const hla_params *p) {
 
 hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
                                 const hla_state *init, const float *dout, float *dq, float *dk, float *dv,
-                                hla_state *dinit, void *workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                const hla_state *dfinal, hla_state *dinit, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
     Geometry geo{};
     hla_status s = forward_geometry(p, &geo);
     if (s != HLA_OK) return s;
@@ -289,17 +289,32 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
     if (init && (s = check_state(init, "init")) != HLA_OK) return s;
     if (dinit && (s = check_state(dinit, "dinit")) != HLA_OK) return s;
-    if (dinit) {  // disjoint from each other and from the initial state
+    if (dfinal && (s = check_state(dfinal, "dfinal")) != HLA_OK) return s;
+    if (dfinal && p->gamma) {  // the seeds at position n divide by g^2
+        for (int h = 0; h < p->H; ++h)
+            if (!(p->gamma[h] >= 1e-6f))
+                return fail(HLA_ERR_UNSUPPORTED, "gamma[%d]=%g: a final-state gradient needs gamma >= 1e-6", h,
+                            double(p->gamma[h]));
+    }
+    if (dinit) {  // disjoint from each other and from the initial state and dfinal
         std::vector<Span> douts, dins;
         state_spans(dinit, "dinit", BH, p->d, p->dv, &douts);
         if (init) state_spans(init, "init", BH, p->d, p->dv, &dins);
+        if (dfinal) state_spans(dfinal, "dfinal", BH, p->d, p->dv, &dins);
         std::string detail;
         if (first_overlap(douts, dins, &detail))
             return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
     }
-    if (n == 0) {  // the gradient of an empty sum
+    if (n == 0) {  // the final state is the initial one: dinit = dfinal (zero without it)
         if (!dinit) return ok();
-        const hipError_t e = hla::zero_state_grad(*dinit, int(BH), p->d, p->dv, stream);
+        hipError_t e = hla::zero_state_grad(*dinit, int(BH), p->d, p->dv, stream);
+        if (e == hipSuccess && dfinal) {
+            const float *src[5] = {dfinal->S, dfinal->C, dfinal->m, dfinal->G, dfinal->h};
+            float *dst[5] = {dinit->S, dinit->C, dinit->m, dinit->G, dinit->h};
+            const size_t cnt[5] = {BH * p->d * p->d, BH * p->d * p->dv, BH * p->d, BH * p->d * p->dv, BH * p->d};
+            for (int i = 0; i < 5 && e == hipSuccess; ++i)
+                e = hipMemcpyAsync(dst[i], src[i], cnt[i] * sizeof(float), hipMemcpyDeviceToDevice, stream);
+        }
         if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
         return ok();
     }
@@ -327,6 +342,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     ins.push_back(span("dout", dout, BH * n * p->dv * 4));
     if (init) state_spans(init, "init", BH, p->d, p->dv, &ins);
     if (dinit) state_spans(dinit, "dinit", BH, p->d, p->dv, &outs);
+    if (dfinal) state_spans(dfinal, "dfinal", BH, p->d, p->dv, &ins);
     std::string detail;
     if (first_overlap(outs, ins, &detail))
         return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
@@ -338,6 +354,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     fp.ws = workspace; fp.ws_bytes = workspace_bytes;
     bp.dout = dout; bp.dq = dq; bp.dk = dk; bp.dv = dv;
     if (dinit) bp.dinit = *dinit;
+    if (dfinal) bp.dfinal = *dfinal;
     const hipError_t e = hla::generic_backward(bp, stream);
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
     return ok();

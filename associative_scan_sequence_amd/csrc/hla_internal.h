@@ -67,6 +67,7 @@ struct BwdProblem {
     const float *dout;   // [B,H,n,dv]
     float *dq, *dk, *dv; // [B,H,n,d], [B,H,n,d], [B,H,n,dv]
     hla_state dinit;     // gradient with respect to the initial state; dinit.S null: not formed
+    hla_state dfinal;    // gradient flowing into the final state; dfinal.S null: none
 };
 size_t generic_backward_workspace_bytes(int BH, int n, int d, int dv, int w);
 hipError_t generic_backward(const BwdProblem &p, hipStream_t s);

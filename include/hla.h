@@ -146,7 +146,8 @@ size_t hla_backward_workspace_size(const hla_params *p);
 /* Gradients of the chunked forward: with L = sum_t <out_t, dout_t>, writes
  * dq = dL/dq, dk = dL/dk, dv = dL/dv for every option of p (decay per head,
  * ridge, normalize), from the zero state or from `init`, and on request the
- * gradient with respect to that initial state.  [SUM] sec. 4 and 5 (the scan
+ * gradient with respect to that initial state; a gradient flowing into the
+ * final state (`dfinal`) may be added to L.  [SUM] sec. 4 and 5 (the scan
  * trains chunk-parallel; the state at a segment boundary is what sequence
  * shards hand on, so its gradient is what they hand back).  The gradient is
  * itself a masked second-order scan, run from the last token to the first:
@@ -162,6 +163,12 @@ size_t hla_backward_workspace_size(const hla_params *p);
  *         G, h set; as for hla_forward_chunked)
  *   dout  [B,H,n,dv] fp32                            (input)
  *   dq, dk [B,H,n,d], dv [B,H,n,dv] fp32             (outputs)
+ *   dfinal NULL = none, else all of S, C, m, G, h set (fp32, shaped as a
+ *         state; rho not read): L gains sum over the parts of <final part,
+ *         dfinal part>, the gradient a later segment hands back.  It enters
+ *         the reverse scan as its carries one token past the last, so every
+ *         decay must be >= 1e-6 (HLA_ERR_UNSUPPORTED otherwise).  With n = 0
+ *         it passes straight to dinit.
  *   dinit NULL = not formed, else all of S, C, m, G, h set (fp32, shaped as
  *         a state): receives dL/d(init) (of the zero state when init is
  *         NULL); its rho, if set, receives 0 (rho reaches no output).  Each
@@ -169,16 +176,19 @@ size_t hla_backward_workspace_size(const hla_params *p);
  *         being (S_t q_t)^T C_t; with Gb_0 and Cb_0 (Cb: powers g^(t-j)) at
  *         token 0 and [C | m], [G | h] of init widened by the den column,
  *           dS = g^2 [C|m] Gb_0^T + sum_j g^(j+1) q_j w_j^T,
- *           d[C|m] = g^2 S Gb_0 + lambda g Cb_0,   d[G|h] = -g^2 Gb_0.
- *         For n = 0 it is zero.
+ *           d[C|m] = g^2 S Gb_0 + lambda g Cb_0,   d[G|h] = -g^2 Gb_0,
+ *         plus, with dfinal, g^n (dS_f + [C|m]_n d[G|h]_f^T) in dS and
+ *         g^n (d[C|m]_f + S_n d[G|h]_f) in d[C|m] (Gb_0 already holds the
+ *         g^(2n) X_n part).  For n = 0 it is dfinal, or zero.
  *   workspace  device memory of at least hla_backward_workspace_size(p)
  *         bytes, 256-byte aligned (may be NULL when n = 0).
  * Outputs must not overlap each other, the inputs or the workspace.  With the
  * ratio, a zero denominator gives IEEE inf/NaN gradients. */
 hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k,
                                 const void *v, const hla_state *init, const float *dout,
-                                float *dq, float *dk, float *dv, hla_state *dinit,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                float *dq, float *dk, float *dv, const hla_state *dfinal,
+                                hla_state *dinit, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* One streaming decode step ([SUM] sec. 1 and 2: constant-size state,
  * O(d^2 + d dv) work per token): applies token (q, k, v) to `state` in place

@@ -166,14 +166,15 @@ def test_forward_empty_sequence_without_state_is_a_no_op(lib):
 
 
 def bwd(lib, p, q=addr(1), k=addr(2), v=addr(3), dout=addr(4), dq=addr(5), dk=addr(6), dv=addr(7),
-        ws=None, ws_bytes=None, init=None, dinit=None):
+        ws=None, ws_bytes=None, init=None, dinit=None, dfinal=None):
     need = lib.hla_backward_workspace_size(ctypes.byref(p))
     if ws is None:
         ws = addr(8)
     if ws_bytes is None:
         ws_bytes = need
     return lib.hla_backward_chunked(ctypes.byref(p), q, k, v, ctypes.byref(init) if init is not None else None,
-                                    dout, dq, dk, dv, ctypes.byref(dinit) if dinit is not None else None,
+                                    dout, dq, dk, dv, ctypes.byref(dfinal) if dfinal is not None else None,
+                                    ctypes.byref(dinit) if dinit is not None else None,
                                     ws, ws_bytes, None)
 
 
@@ -208,7 +209,7 @@ def test_backward_rejects_bad_pointers_and_workspace(lib):
     assert bwd(lib, p, ws_bytes=need - 1) == WORKSPACE
     assert bwd(lib, p, ws=addr(8) + 16) == ALIGN and "256-byte" in last(lib)
     assert lib.hla_backward_chunked(ctypes.byref(p), addr(1), addr(2), addr(3), None, addr(4), addr(5),
-                                    addr(6), addr(7), None, None, need, None) == WORKSPACE
+                                    addr(6), addr(7), None, None, None, need, None) == WORKSPACE
     bad = CState(addr(9), addr(10), None, addr(12), addr(13), None)
     assert bwd(lib, p, dinit=bad) == INVALID and "dinit->m is NULL" in last(lib)
     bad = CState(addr(9) + 4, addr(10), addr(11), addr(12), addr(13), None)
@@ -231,12 +232,21 @@ def test_backward_rejects_aliasing(lib):
     assert bwd(lib, p, dinit=CState(addr(14), addr(15), addr(16), addr(17), addr(18), addr(5))) \
         == INVALID and "overlaps" in last(lib)
     assert bwd(lib, p, dq=addr(14), dinit=dst) == INVALID and "overlaps" in last(lib)
+    fst = CState(addr(19), addr(20), addr(21), addr(22), addr(23), None)
+    assert bwd(lib, p, dfinal=CState(addr(19), None, addr(21), addr(22), addr(23), None)) == INVALID
+    assert "dfinal->C is NULL" in last(lib)
+    assert bwd(lib, p, dfinal=fst, dinit=CState(addr(14), addr(20), addr(16), addr(17), addr(18), None)) \
+        == INVALID and "dinit.C overlaps dfinal.C" in last(lib)
+    assert bwd(lib, p, dfinal=fst, dk=addr(21)) == INVALID and "dk overlaps dfinal.m" in last(lib)
+    g = (ctypes.c_float * 2)(0.9, 1e-7)
+    pg = params(H=2, gamma=ctypes.cast(g, ctypes.POINTER(ctypes.c_float)))
+    assert bwd(lib, pg, dfinal=fst) == UNSUPPORTED and "gamma[1]" in last(lib)
 
 
 def test_backward_empty_sequence_is_a_no_op(lib):
     p = params(n=0)
     assert lib.hla_backward_chunked(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
-                                    None, 0, None) == OK
+                                    None, None, 0, None) == OK
 
 
 def dec(lib, p, state, q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None):

@@ -283,3 +283,92 @@ def test_backward_initial_state_gradient_empty_sequence():
     torch.cuda.synchronize()
     for t in dini.tensors():
         assert torch.all(t == 0.0)
+
+
+DFIN_CASES = [
+    # dtype, d, dv, chunk, n, gamma, ridge, normalize, with init
+    (torch.float32, 32, 32, 16, 150, "per_head", 0.0, False, True),
+    (torch.float32, 32, 16, 32, 97, "per_head", 0.2, False, True),
+    (torch.bfloat16, 64, 64, 64, 150, "decay", 0.0, False, False),
+    (torch.float32, 32, 32, 32, 120, "decay", 0.1, True, True),
+    (torch.bfloat16, 128, 128, 128, 300, "decay", 1e-3, True, True),
+    (torch.float32, 16, 64, 16, 70, None, 0.0, False, True),
+    (torch.float32, 64, 32, 64, 45, "strong", 0.0, False, False),
+]
+
+
+@pytest.mark.parametrize("case", DFIN_CASES, ids=lambda c: f"{'bf16' if c[0] == torch.bfloat16 else 'f32'}"
+                         f"-d{c[1]}dv{c[2]}w{c[3]}n{c[4]}-{c[5]}-l{c[6]}-r{int(c[7])}-init{int(c[8])}")
+def test_backward_final_state_gradient(case):
+    """A gradient flowing into the final state (dfinal): dq, dk, dv and dinit
+    through hla_backward_chunked against the fp64 autograd oracle of
+    sum <out, dout> + sum <final part, dfinal part>."""
+    import types
+
+    import oracle
+    from oracle import backward as ob
+    dtype, d, dv, chunk, n, gk, lam, norm, with_init = case
+    B, H, n0 = 1, 2, 40
+    q, k, v = inputs.qkv(B, H, n0 + n, d, dv, dtype, seed=101 + d + n)
+    if norm:
+        q, k = (x.float().abs().add(0.1).to(dtype) for x in (q, k))
+    g = None
+    if gk == "decay":
+        g = inputs.gamma_list_fp32([0.97] * H)
+    elif gk == "per_head":
+        g = inputs.gamma_list_fp32([0.95, 0.99])
+    elif gk == "strong":
+        g = inputs.gamma_list_fp32([0.3, 0.6])
+    lam = inputs.ridge_fp32(lam)
+    init = ref_init = None
+    if with_init:
+        _, _, st = oracle.forward(q[:, :, :n0], k[:, :, :n0], v[:, :, :n0], gamma=g, lam=lam)
+        f32 = {name: torch.tensor(getattr(st, name), dtype=torch.float32) for name in ("S", "C", "m", "G", "h")}
+        init = hla.State(*(f32[x].to(DEV) for x in ("S", "C", "m", "G", "h")))
+        ref_init = types.SimpleNamespace(**f32)
+    N = B * H
+    shapes = {"S": (N, d, d), "C": (N, d, dv), "m": (N, d), "G": (N, d, dv), "h": (N, d)}
+    dfin = {name: 0.1 * inputs.upstream(1, 1, 1, int(np.prod(shp)), seed=103 + i).reshape(shp)
+            for i, (name, shp) in enumerate(shapes.items())}
+    qs, ks, vs = (x[:, :, n0:].contiguous() for x in (q, k, v))
+    dout = inputs.upstream(B, H, n, dv, seed=107)
+    qg, kg, vg, dg = (x.to(DEV) for x in (qs, ks, vs, dout))
+    dini = hla.State.empty(N, d, dv, DEV)
+    dfin_dev = hla.State(*(dfin[x].to(DEV) for x in ("S", "C", "m", "G", "h")))
+    got = hla.backward_chunked(qg, kg, vg, dg, gamma=g, ridge=lam, normalize=norm, chunk=chunk, init=init,
+                               dinit=dini, dfinal=dfin_dev)
+    torch.cuda.synchronize()
+    *ref, rdini = ob.backward(qs, ks, vs, dout, g, lam, norm, ref_init, init_grad=True,
+                              dfinal=types.SimpleNamespace(**dfin))
+    check([x.cpu() for x in got], ref)
+    _dinit_check(dini, rdini)
+
+
+@pytest.mark.parametrize("dtype,norm,lam", [(torch.float32, False, 0.0), (torch.bfloat16, True, 0.05)])
+def test_backward_segments_chain_to_the_whole_sequence(dtype, norm, lam):
+    """Sequence-sharded training on one GPU: segment A's final state (GPU
+    forward) starts segment B; B's backward returns dinit, which A's backward
+    takes as dfinal.  Together they give the whole sequence's gradients (fp64
+    oracle over all tokens)."""
+    from oracle import backward as ob
+    B, H, na, nb, d, dv = 1, 2, 130, 90, 32, 32
+    q, k, v = inputs.qkv(B, H, na + nb, d, dv, dtype, seed=111)
+    if norm:
+        q, k = (x.float().abs().add(0.1).to(dtype) for x in (q, k))
+    g = inputs.gamma_list_fp32([0.98, 0.995])
+    lam = inputs.ridge_fp32(lam)
+    dout = inputs.upstream(B, H, na + nb, dv, seed=113)
+    qg, kg, vg, dg = (x.to(DEV) for x in (q, k, v, dout))
+    sa = lambda x: x[:, :, :na].contiguous()
+    sb = lambda x: x[:, :, na:].contiguous()
+    _, _, stA = hla.forward_chunked(sa(qg), sa(kg), sa(vg), gamma=g, ridge=lam, normalize=norm, chunk=32,
+                                    return_state=True)
+    dB = hla.State.empty(B * H, d, dv, DEV)
+    gB = hla.backward_chunked(sb(qg), sb(kg), sb(vg), sb(dg), gamma=g, ridge=lam, normalize=norm, chunk=32,
+                              init=stA, dinit=dB)
+    gA = hla.backward_chunked(sa(qg), sa(kg), sa(vg), sa(dg), gamma=g, ridge=lam, normalize=norm, chunk=32,
+                              dfinal=dB)
+    torch.cuda.synchronize()
+    got = [torch.cat([a.cpu(), b.cpu()], dim=2) for a, b in zip(gA, gB)]
+    ref = ob.backward(q, k, v, dout, g, lam, norm)
+    check(got, ref)
