@@ -444,8 +444,36 @@ __global__ __launch_bounds__(kThreads) void k_bwd_seed(BwdArgs a) {
     }
 }
 
+// ---- per-chunk parts of sum_j g^(j+1) q_j w_j^T (the one-sided key-moment
+// term of the initial-state gradient) into T slot c.  Runs after k_bwd_dk, the
+// last reader of T; the last chunk clears slot nc, so an undecayed suffix sum
+// over the slots leaves the total in slot 0.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_bwd_qw(BwdArgs a) {
+    constexpr int MR = D / 16;
+    __shared__ float gt[2 * kMaxW + 1];
+    __shared__ Stage<max3(D, D, 16)> st;
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int s0 = c * a.w, L = min(a.w, a.n - s0);
+    const float g = head_gamma(a.gam, bh % a.H), base = gpow(g, s0);
+    const size_t tok = static_cast<size_t>(bh) * a.n + s0;
+    const T *q = static_cast<const T *>(a.q) + tok * D;
+    const float *Wc = a.W + (static_cast<size_t>(bh) * a.nc + c) * a.w * D;
+    pow_table(gt, g, a.w);
+    float acc[MR][MR] = {};
+    mm<MR, MR, true>(acc, D, L, st,
+                     [&](int r, int t) { return base * gt[t + 1] * Elem<T>::get(q, static_cast<size_t>(t) * D + r); },
+                     [&](int t, int b) { return Wc[t * D + b]; });
+    store_tile<MR, MR>(a.T + slot(a, bh, c) * D * D, D, D, acc);
+    if (c == a.nc - 1) {
+        float *z = a.T + slot(a, bh, a.nc) * D * D;
+        for (int i = threadIdx.x; i < D * D; i += kThreads) z[i] = 0.0f;
+    }
+}
+
 // ---- gradient of the initial state (the state at position -1), one
-// workgroup per row r of the d rows of every head.  With C' = [C | m] of the
+// workgroup per row r of the d rows of every head (the token sum of dS is
+// already in T slot 0).  With C' = [C | m] of the
 // initial state (zero when none is given), Gb0' = [Gb_0 | gb_0] and
 // Cb0' = [Cb_0 | cb_0] the right slots at token 0, and w_j the kept W rows:
 //   dS[r][b]  = g^2 sum_c C'[r][c] Gb0'[b][c] + sum_j g^(j+1) q_j[r] w_j[b]
@@ -458,31 +486,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_seed(BwdArgs a) {
 // independent variables.
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads) void k_bwd_init(BwdArgs a, hla_state ini, hla_state dini) {
-    constexpr int NG = kThreads / D;  // token groups of the dS sum
-    __shared__ float red[NG][D];
     const int r = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const float g = head_gamma(a.gam, bh % a.H), g2 = g * g;
     const size_t s0 = slot(a, bh, 0);
     const float *Gb = a.RG + s0 * D * DV, *gb = a.rg + s0 * D;
     const bool cbar = a.cbar != 0;
-    {
-        const int b = tid % D, grp = tid / D;
-        const T *q = static_cast<const T *>(a.q) + static_cast<size_t>(bh) * a.n * D;
-        const float *W = a.W + static_cast<size_t>(bh) * a.nc * a.w * D;
-        float acc = 0.0f;
-        for (int j = grp; j < a.n; j += NG) {
-            const int c = j / a.w, s = j - c * a.w;
-            acc += gpow(g, j + 1) * Elem<T>::get(q, static_cast<size_t>(j) * D + r) *
-                   W[(static_cast<size_t>(c) * a.w + s) * D + b];
-        }
-        red[grp][b] = acc;
-    }
-    __syncthreads();
     const size_t so = static_cast<size_t>(bh);
     if (tid < D) {
         const int b = tid;
-        float x = 0.0f;
-        for (int k = 0; k < NG; ++k) x += red[k][b];
+        float x = a.T[(s0 * D + r) * D + b];  // sum_j g^(j+1) q_j w_j^T, from k_bwd_qw
         if (ini.S) {
             const float *Cr = ini.C + (so * D + r) * DV;
             float y = ini.m[so * D + r] * gb[b];
@@ -549,7 +561,12 @@ hipError_t launch_bwd(const BwdArgs &a, int BH, hipStream_t st) {
         hipLaunchKernelGGL((k_bwd_dk<T, D, DV, 4>), grid, blk, 0, st, a);
         hipLaunchKernelGGL((k_bwd_dv<T, D, DV, 4>), grid, blk, 0, st, a);
     }
-    if (a.dini.S) hipLaunchKernelGGL((k_bwd_init<T, D, DV>), dim3(D, BH), blk, 0, st, a, a.ini, a.dini);
+    if (a.dini.S) {
+        hipLaunchKernelGGL((k_bwd_qw<T, D>), grid, blk, 0, st, a);
+        const RScan sQ{a.T, D * D};
+        hipLaunchKernelGGL(k_rprefix, dim3((D * D + kThreads - 1) / kThreads, BH), blk, 0, st, a, sQ, none, 0);
+        hipLaunchKernelGGL((k_bwd_init<T, D, DV>), dim3(D, BH), blk, 0, st, a, a.ini, a.dini);
+    }
     return hipGetLastError();
 }
 

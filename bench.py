@@ -21,7 +21,9 @@ other parts of the hot path (the ratio-normalised forward with decay and
 ridge, the long d=128 forward, the streaming decode step, state composition,
 the small fp32 forward), and at the headline shape the forward that also
 returns its final state (the generic path a sequence shard runs) and the
-backward, each timed with HIP events on its launch stream and
+backward (plain, and as a sequence shard runs it: from an initial state, with a
+final-state gradient in and the initial-state gradient out), each timed with
+HIP events on its launch stream and
 set against its own HBM roofline (``--headline-only`` skips them).
 """
 import argparse
@@ -312,9 +314,33 @@ def backward_headline_shape(dev, stream):
         q, k, v, dout, grads, ws = sets[i % copies]
         hla.backward_chunked(q, k, v, dout, chunk=w.chunk, workspace=ws, grads=grads)
     us = time_calls(call, stream, 10, warmup=2)
-    return [{"workload": "masked_hla_bwd_B4_H8_n2048_d64_bf16_w64", "entry": "hla_backward_chunked",
-             "us_per_call": us, "tokens_per_s": w.B * w.n / (us * 1e-6),
-             "roofline": roof(tok * per_tok, us)}]
+    res = [{"workload": "masked_hla_bwd_B4_H8_n2048_d64_bf16_w64", "entry": "hla_backward_chunked",
+            "us_per_call": us, "tokens_per_s": w.B * w.n / (us * 1e-6),
+            "roofline": roof(tok * per_tok, us)}]
+
+    # the backward of a sequence shard: from an initial state (the previous
+    # shard's final state), with a gradient flowing into its own final state,
+    # returning the gradient of its initial state; three states more per head
+    N = w.B * w.H
+    state_b = 4 * (w.d * w.d + 2 * w.d * w.dv + 2 * w.d)
+    q0, k0, v0 = sets[0][:3]
+    _, _, ini = hla.forward_chunked(q0, k0, v0, chunk=w.chunk, return_state=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5590)
+    dfin = hla.State(*(0.1 * torch.randn(t.shape, generator=gen, dtype=torch.float32, device=dev)
+                       for t in ini.tensors()[:5]))
+    dini = hla.State.empty(N, w.d, w.dv, dev)
+
+    def call_shard(i):
+        q, k, v, dout, grads, ws = sets[i % copies]
+        hla.backward_chunked(q, k, v, dout, chunk=w.chunk, workspace=ws, grads=grads, init=ini,
+                             dfinal=dfin, dinit=dini)
+    us = time_calls(call_shard, stream, 10, warmup=2)
+    res.append({"workload": "masked_hla_bwd_shard_B4_H8_n2048_d64_bf16_w64",
+                "entry": "hla_backward_chunked (init, dfinal in; dinit out)",
+                "us_per_call": us, "tokens_per_s": w.B * w.n / (us * 1e-6),
+                "roofline": roof(tok * per_tok + 3 * N * state_b, us)})
+    return res
 
 
 def small_forward(dev, stream):
