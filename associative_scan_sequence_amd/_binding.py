@@ -333,11 +333,47 @@ class _HLAFunction(torch.autograd.Function):
         return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
 
 
+class _HLAStateFunction(torch.autograd.Function):
+    """The forward from an initial state, returning out and the final state's
+    five parts; the backward takes the final state's gradient as dfinal and
+    returns the initial state's as dinit (both C ABI calls)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, S, C, m, G, h, gamma, ridge, normalize, chunk):
+        out, _, fin = forward_chunked(q, k, v, gamma=gamma, ridge=ridge, normalize=normalize, chunk=chunk,
+                                      init=State(S, C, m, G, h), return_state=True)
+        ctx.save_for_backward(q, k, v, S, C, m, G, h)
+        ctx.opts = (gamma, ridge, normalize, chunk)
+        return out, fin.S, fin.C, fin.m, fin.G, fin.h
+
+    @staticmethod
+    def backward(ctx, dout, dS, dC, dm, dG, dh):
+        q, k, v, S, C, m, G, h = ctx.saved_tensors
+        gamma, ridge, normalize, chunk = ctx.opts
+        dfinal = State(*(x.float().contiguous() for x in (dS, dC, dm, dG, dh)))
+        dini = State.empty(S.shape[0], q.shape[-1], v.shape[-1], q.device, with_rho=False)
+        dq, dk, dv = backward_chunked(q, k, v, dout.float().contiguous(), gamma=gamma, ridge=ridge,
+                                      normalize=normalize, chunk=chunk, init=State(S, C, m, G, h),
+                                      dinit=dini, dfinal=dfinal)
+        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dini.S, dini.C, dini.m, dini.G, dini.h,
+                None, None, None, None)
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=None, ridge: float = 0.0,
-              normalize: bool = False, chunk: int = 0) -> torch.Tensor:
-    """Masked second-order HLA as a differentiable op (zero initial state):
-    out [B,H,n,dv] fp32 from q, k [B,H,n,d] and v [B,H,n,dv] (bf16 or fp32);
-    gradients flow to q, k, v through ``hla_backward_chunked`` and are
-    returned in the inputs' dtype."""
-    return _HLAFunction.apply(q, k, v, gamma, ridge, normalize, chunk)
+              normalize: bool = False, chunk: int = 0, init: Optional[State] = None):
+    """Masked second-order HLA as a differentiable op: out [B,H,n,dv] fp32 from
+    q, k [B,H,n,d] and v [B,H,n,dv] (bf16 or fp32); gradients flow to q, k, v
+    through ``hla_backward_chunked`` and are returned in the inputs' dtype.
+
+    Without ``init`` the sequence starts from the zero state and only out is
+    returned.  With ``init`` (a State of fp32 tensors, which may require
+    grad) it returns (out, final State): gradients reach the initial state's
+    parts and flow back from the final state's, so sequence segments chain
+    (``attention(..., init=final_of_previous)``) and train as one sequence.
+    That path needs every decay >= 1e-6."""
+    if init is None:
+        return _HLAFunction.apply(q, k, v, gamma, ridge, normalize, chunk)
+    out, *fin = _HLAStateFunction.apply(q, k, v, init.S, init.C, init.m, init.G, init.h, gamma, ridge,
+                                        normalize, chunk)
+    return out, State(*fin)
 

@@ -372,3 +372,37 @@ def test_backward_segments_chain_to_the_whole_sequence(dtype, norm, lam):
     got = [torch.cat([a.cpu(), b.cpu()], dim=2) for a, b in zip(gA, gB)]
     ref = ob.backward(q, k, v, dout, g, lam, norm)
     check(got, ref)
+
+
+@pytest.mark.parametrize("norm,lam", [(False, 0.0), (True, 0.05)])
+def test_autograd_op_chains_segments(norm, lam):
+    """hla.attention with a state: three segments chained through their
+    states under one loss.backward() give the whole sequence's gradients
+    (fp64 oracle), and a leaf initial state receives the oracle's dinit."""
+    import types
+
+    from oracle import backward as ob
+    B, H, d, dv, cuts = 1, 2, 32, 32, (0, 70, 160, 230)
+    n = cuts[-1]
+    q, k, v = inputs.qkv(B, H, n, d, dv, torch.float32, seed=121)
+    if norm:
+        q, k = (x.abs().add(0.1) for x in (q, k))
+    g = inputs.gamma_list_fp32([0.97, 0.99])
+    lam = inputs.ridge_fp32(lam)
+    dout = inputs.upstream(B, H, n, dv, seed=123)
+    N = B * H
+    ini = {"S": 0.05 * torch.eye(d).repeat(N, 1, 1), "C": 0.1 * inputs.upstream(1, 1, N * d, dv, seed=125).reshape(N, d, dv),
+           "m": torch.full((N, d), 0.5), "G": torch.zeros(N, d, dv), "h": torch.zeros(N, d)}
+    qg, kg, vg = (x.to(DEV).requires_grad_(True) for x in (q, k, v))
+    st = hla.State(*(ini[x].to(DEV).requires_grad_(True) for x in ("S", "C", "m", "G", "h")))
+    leaf = st
+    loss = 0.0
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = lambda x: x[:, :, a:b].contiguous()
+        out, st = hla.attention(sl(qg), sl(kg), sl(vg), gamma=g, ridge=lam, normalize=norm, chunk=32, init=st)
+        loss = loss + (out * sl(dout.to(DEV))).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    *ref, rdini = ob.backward(q, k, v, dout, g, lam, norm, types.SimpleNamespace(**ini), init_grad=True)
+    check([x.grad.cpu() for x in (qg, kg, vg)], ref)
+    _dinit_check(types.SimpleNamespace(**{x: getattr(leaf, x).grad for x in ("S", "C", "m", "G", "h")}), rdini)
