@@ -10,9 +10,9 @@ C ABI in include/hla.h); this package is its thin Python binding:
 * :func:`state_compose` -- masked semidirect-product composition (``hla_state_compose``)
 """
 from ._binding import (EXPORTED, LIB_PATH, HlaError, State, attention, backward_chunked,
-                       backward_workspace_size, decode_step, forward_chunked, load, state_compose,
-                       workspace_size)
+                       backward_workspace_size, decode_step, forward_chunked, give_ups, load,
+                       state_compose, workspace_size)
 
 __all__ = ["EXPORTED", "LIB_PATH", "HlaError", "State", "attention", "backward_chunked",
-           "backward_workspace_size", "decode_step", "forward_chunked", "load", "state_compose",
-           "workspace_size"]
+           "backward_workspace_size", "decode_step", "forward_chunked", "give_ups", "load",
+           "state_compose", "workspace_size"]

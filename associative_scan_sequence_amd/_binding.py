@@ -158,6 +158,14 @@ def _params(B, H, n, d, dv, chunk, dtype, gamma, ridge, normalize):
     return p, keep
 
 
+def give_ups(workspace: torch.Tensor) -> int:
+    """Waits that gave up in the one-launch kernels that ran on this
+    forward workspace (control word 3; synchronises with the device).  A
+    give-up makes the outputs that depend on it NaN; zero is the normal
+    value."""
+    return int(workspace[12:16].view(torch.int32).item())
+
+
 def workspace_size(B, H, n, d, dv, *, chunk=0, dtype=torch.bfloat16, gamma=None, ridge=0.0,
                    normalize=False) -> int:
     """Bytes of forward workspace; allocate it zero-filled (``torch.zeros``)."""
@@ -344,19 +352,29 @@ class _HLAStateFunction(torch.autograd.Function):
                                       init=State(S, C, m, G, h), return_state=True)
         ctx.save_for_backward(q, k, v, S, C, m, G, h)
         ctx.opts = (gamma, ridge, normalize, chunk)
+        ctx.set_materialize_grads(False)  # unused outputs arrive as None, not zeros
         return out, fin.S, fin.C, fin.m, fin.G, fin.h
 
     @staticmethod
     def backward(ctx, dout, dS, dC, dm, dG, dh):
         q, k, v, S, C, m, G, h = ctx.saved_tensors
         gamma, ridge, normalize, chunk = ctx.opts
-        dfinal = State(*(x.float().contiguous() for x in (dS, dC, dm, dG, dh)))
-        dini = State.empty(S.shape[0], q.shape[-1], v.shape[-1], q.device, with_rho=False)
+        parts = (dS, dC, dm, dG, dh)
+        dfinal = None
+        if any(x is not None for x in parts):  # the final state is used downstream
+            like = (S, C, m, G, h)
+            dfinal = State(*(torch.zeros_like(t, dtype=torch.float32) if x is None else x.float().contiguous()
+                             for x, t in zip(parts, like)))
+        if dout is None:
+            dout = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
+        dini = None
+        if any(ctx.needs_input_grad[3:8]):  # some part of the initial state wants its gradient
+            dini = State.empty(S.shape[0], q.shape[-1], v.shape[-1], q.device, with_rho=False)
         dq, dk, dv = backward_chunked(q, k, v, dout.float().contiguous(), gamma=gamma, ridge=ridge,
                                       normalize=normalize, chunk=chunk, init=State(S, C, m, G, h),
                                       dinit=dini, dfinal=dfinal)
-        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dini.S, dini.C, dini.m, dini.G, dini.h,
-                None, None, None, None)
+        dst = (None,) * 5 if dini is None else (dini.S, dini.C, dini.m, dini.G, dini.h)
+        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), *dst, None, None, None, None)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=None, ridge: float = 0.0,
@@ -370,10 +388,17 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=None, 
     grad) it returns (out, final State): gradients reach the initial state's
     parts and flow back from the final state's, so sequence segments chain
     (``attention(..., init=final_of_previous)``) and train as one sequence.
-    That path needs every decay >= 1e-6."""
+    That path needs every decay >= 1e-6.
+
+    The key moment S of a state is symmetric (a sum of k k^T), and the
+    library reads it as such.  The op therefore uses the symmetric part
+    (S + S^T)/2 of the given S, so a learnable initial S that an optimizer
+    step has moved off the symmetric matrices still gives the function the
+    gradient describes, and the gradient it receives is itself symmetric."""
     if init is None:
         return _HLAFunction.apply(q, k, v, gamma, ridge, normalize, chunk)
-    out, *fin = _HLAStateFunction.apply(q, k, v, init.S, init.C, init.m, init.G, init.h, gamma, ridge,
-                                        normalize, chunk)
+    S = 0.5 * (init.S + init.S.transpose(-1, -2))
+    out, *fin = _HLAStateFunction.apply(q, k, v, S.contiguous(), init.C, init.m, init.G, init.h, gamma,
+                                        ridge, normalize, chunk)
     return out, State(*fin)
 

@@ -78,6 +78,7 @@ struct FastArgs {
     const uint16_t *q, *k, *v;
     float *out, *den;  // den may be null
     float ridge;
+    int force_device;  // 1: device-coherent exchange even when a head's segments share an XCD
     uint32_t *ctrl;   // control block (epoch, done counter, XCD table)
     uint32_t *flags;  // [BH * P][2 rounds][8 waves] at kFlagStride words: publication epoch
     float *aggS, *aggX, *aggC;  // [BH * P][16 tiles][64 lanes][4]
@@ -326,7 +327,8 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         }
         // the exchange goes through the XCD's L2 when every workgroup holding
         // a segment of this head runs on this XCD (every wave decides alike)
-        const bool local = head_on_one_xcd(xtab, tab_ok, a.P, a.BH, bh, epoch, tabv, a.ctrl + kSpinWord);
+        const bool local =
+            !a.force_device && head_on_one_xcd(xtab, tab_ok, a.P, a.BH, bh, epoch, tabv, a.ctrl + kSpinWord);
         auto flag_of = [&](size_t sl, int round) { return &a.flags[((sl * 2 + round) * kWaves + wave) * kFlagStride]; };
         if (publish) {
             put_tiles(a.aggS + slot * 4096, wave, l, srun, local);
@@ -424,10 +426,21 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // ---- carry = sum over earlier segments pp of g^(pw * gap) * (wave's
         // tiles of agg[pp]), gap = tokens between; waits on this wave's flags only
         const int seg_tokens = a.L * W;
-        auto wait_round = [&](int round) {
+        // true when a wait of this wave gave up: the carry it sums is then
+        // made NaN, so every output built on it is NaN (never a silently
+        // wrong number), here and in the later segments that read it
+        auto wait_round = [&](int round) -> bool {
+            bool failed = false;
             for (int pp = l; pp < p; pp += 64)
-                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local, a.ctrl + kSpinWord))
+                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local, a.ctrl + kSpinWord)) {
                     __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    failed = true;
+                }
+            return __builtin_amdgcn_ballot_w64(failed) != 0;
+        };
+        auto poison = [&](f32x4 (&acc)[2]) {
+            const float nan = __builtin_nanf("");
+            acc[0] = acc[1] = f32x4{nan, nan, nan, nan};
         };
         auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int pw) {
             constexpr int NB = 8;
@@ -471,8 +484,9 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // ================= round 1: S0 of every chunk -> LDS ========================
         {
             f32x4 s0seg[2];
-            wait_round(0);
+            const bool bad = wait_round(0);
             carry_tiles(s0seg, a.aggS, 1);
+            if (bad) poison(s0seg);
             // With the denominator, S0 takes a third term (in the key tile: no
             // key is read after the carry-free stage).  The ratio amplifies the
             // absolute error of den where |den| is small, and a two-term S0 in U
@@ -738,10 +752,15 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // at vec[c * kVecSlot], the m0 half at +64)
         f32x4 x0seg[2], c0seg[2];
         float v0seg[2];
-        wait_round(1);
+        const bool bad2 = wait_round(1);
         carry_tiles(x0seg, a.aggX, 2);
         if constexpr (RIDGE) carry_tiles(c0seg, a.aggC, 1);
         if (yw || mw) carry_vec(v0seg, voff, yw ? 2 : 1);
+        if (bad2) {
+            poison(x0seg);
+            if constexpr (RIDGE) poison(c0seg);
+            v0seg[0] = v0seg[1] = __builtin_nanf("");
+        }
         float *const vec = reinterpret_cast<float *>(sm.T[RIDGE ? 16 : 0]);
         __syncthreads();  // every Us, value and query read done: the tiles take X0 (C0, vectors)
 #pragma unroll
@@ -953,6 +972,7 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     a.out = p.out;
     a.den = p.den;
     a.ridge = p.ridge;
+    a.force_device = exchange_forced_device() ? 1 : 0;
     a.ctrl = ctrl;
     const FastLayout L = fast_layout(a.BH, a.P);
     char *base = static_cast<char *>(data);

@@ -24,9 +24,9 @@
 // Z = S0 Ct + Lz is formed (one fp32 product) and published (round 2), and
 // the X carry is summed likewise.  Pass 2 walks again from the true carries
 // and writes the outputs.  With P = 1 (many heads, or short sequences) pass
-// 1 and both rounds are skipped.  Rounds, segment order and epochs work as
-// in fwd_fast64.hip (a resident grid walking segments in increasing order,
-// device-coherent aggregates, a launch epoch on the flags).
+// 1 and both rounds are skipped.  Aggregates and flags are device-coherent
+// (sc1) accesses and carry a launch epoch; segments are taken from a ticket
+// counter in increasing order (see k_fused128).
 //
 // Layout.  512 threads = 8 waves; wave w owns feature block w (16 of 128):
 // the columns b = 16w.. of S (= its rows, S being symmetric), the columns
@@ -65,6 +65,7 @@ constexpr int kThreads = 512;  // eight waves
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kSpinWord = 4;   // control word: spin limit of the bounded waits (0: kSpinLimit)
 constexpr int kLine = 64;
+constexpr int kTicketWord = kLine + 2;  // control word: next segment ticket (P > 1)
 constexpr int kSlot = 16384;   // floats per published 128 x 128 aggregate
 constexpr float kMinGamma = 0.75f;
 static_assert(kCtrlBytes >= 2 * kLine * 4, "control block too small");
@@ -167,6 +168,13 @@ __device__ bool wait_flag(const uint32_t *f, uint32_t want, int spin) {
     return false;
 }
 
+// a carry whose inputs could not be waited for: NaN, so every output built on it is NaN
+__device__ __forceinline__ void poison(f32x4 (&acc)[8]) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = f32x4{nan, nan, nan, nan};
+}
+
 constexpr int kSc1 = 16;  // buffer cache policy: sc1 (device scope)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
@@ -220,6 +228,8 @@ struct Smem128 {
     __bf16 Ah[W * LDN];  // masked scores A[t][i], then P[t][s], hi and lo
     __bf16 Al[W * LDN];
     uint32_t epoch;
+    int ticket;    // the segment this workgroup holds (ticketed launches)
+    uint32_t bad;  // nonzero: a wait of this segment gave up
 };
 // the S0 tiles of the Z product (128 rows, hi and lo) overlay K .. Uh
 static_assert(4 * kTile128 >= 2 * (2 * kTile128), "S0 overlay does not fit");
@@ -236,8 +246,19 @@ __device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
 }
 
 // LOOP = false: one segment per workgroup (grid = segs: at most the CU count,
-// or any count when each head is one segment); true: workgroup b takes
-// segments b, b + grid, ... (grid = CU count < segs).
+// or any count when each head is one segment); true: workgroups take
+// segments until none is left (grid = CU count < segs).
+// When the segments of a head wait on each other (P > 1), a workgroup takes
+// its segments from a ticket counter (control word kTicketWord), so segment
+// s is only ever held by a workgroup that is already running, and every
+// earlier segment of its head was taken before it by a running workgroup
+// that waits only on segments earlier still: the waits always end, whatever
+// other streams keep resident on the device.  With P = 1 nothing waits and
+// segment = workgroup index.
+// A wait that still gives up (spin limit, or forced from the host through
+// control word 4) makes the carry it was waiting for NaN: every output of
+// the segment and of the later segments of its head that read the carry is
+// then NaN, never a silently wrong number.
 template <bool DECAY, bool LOOP>
 __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     __shared__ Smem128 sm;
@@ -490,6 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     };
 
     if (a.P > 1) {
+        if (tid == 0) sm.bad = 0u;  // read only after the barriers below
         walk(std::integral_constant<bool, false>{});
         // ---- round 1: publish the segment's key moment; S carry from the earlier segments
         put32(a.aggS + (slot0 + p) * kSlot, tid, sacc);
@@ -500,11 +522,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         // -1: give up without polling (a host-forced failure); n > 0: n polls
         const int spin = spin_set < 0 ? 0 : (spin_set > 0 ? spin_set : kSpinLimit);
         for (int pp = tid; pp < p; pp += kThreads)
-            if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch, spin))
+            if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch, spin)) {
                 __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.bad = 1u;
+            }
         __syncthreads();
         sum_slots(sacc, a.aggS, static_cast<int>(slot0), p, tid,
                   [&](int pp) { return gp(static_cast<float>((p - 1 - pp) * seg_tokens)); });
+        if (sm.bad) poison(sacc);
         // ---- Z = S0 Ct + Lz: S0 -> LDS rows (hi/lo); lane holds S0[a][b = 16w+r] = S0[b][a]
         __bf16 *S0h = sm.K, *S0l = sm.K + 2 * kTile128;  // 128-row tiles over K, V and Q, Uh
 #pragma unroll
@@ -536,11 +561,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         if (tid == 0)
             __hip_atomic_store(&a.flags[2 * (slot0 + p) + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int pp = tid; pp < p; pp += kThreads)
-            if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch, spin))
+            if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch, spin)) {
                 __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.bad = 1u;
+            }
         __syncthreads();
         sum_slots(xacc, a.aggZ, static_cast<int>(slot0), p, tid,
                   [&](int pp) { return gp(static_cast<float>(2 * (p - 1 - pp) * seg_tokens)); });
+        if (sm.bad) poison(xacc);
     }
     walk(std::integral_constant<bool, true>{});
 
@@ -548,17 +576,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     };
     // (a loop around the body costs registers even when it runs once, so the
     // one-segment-per-workgroup launch calls it straight)
+    // the next segment: a ticket when segments wait on each other
+    auto take = [&]() -> int {
+        if (tid == 0)
+            sm.ticket = static_cast<int>(
+                __hip_atomic_fetch_add(&a.ctrl[kTicketWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __syncthreads();
+        const int t = __builtin_amdgcn_readfirstlane(sm.ticket);
+        __syncthreads();  // every wave has read it before it is overwritten
+        return t;
+    };
     if constexpr (LOOP) {
-        for (int seg = static_cast<int>(blockIdx.x); seg < a.segs; seg += static_cast<int>(gridDim.x)) seg_body(seg);
+        for (int seg = take(); seg < a.segs; seg = take()) seg_body(seg);
     } else {
-        seg_body(static_cast<int>(blockIdx.x));
+        seg_body(a.P > 1 ? take() : static_cast<int>(blockIdx.x));
     }
 
-    // ---- the last workgroup to finish resets the counter and advances the epoch
+    // ---- the last workgroup to finish resets the counters and advances the epoch
     if (tid == 0) {
         const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(&a.ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kTicketWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -629,8 +668,8 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
-    // when segments of a head wait on each other the grid is at most one
-    // workgroup per CU (its LDS fills the CU), so the whole grid is resident
+    // when segments of a head wait on each other, workgroups take them by
+    // ticket, at most one workgroup per CU (its LDS fills the CU)
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -7,10 +7,21 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 #include <vector>
 
 #include "hla_internal.h"
+
+namespace hla {
+
+bool exchange_forced_device() {
+    const char *e = std::getenv("HLA_EXCHANGE");
+    return e != nullptr && std::strcmp(e, "device") == 0;
+}
+
+}  // namespace hla
 
 namespace {
 

@@ -75,6 +75,12 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t s);
 // of an empty sequence).
 hipError_t zero_state_grad(const hla_state &s, int BH, int d, int dv, hipStream_t st);
 
+// True when the environment sets HLA_EXCHANGE=device: the one-launch d = 64
+// forward then hands aggregates between workgroups device-coherently even
+// when every segment of a head runs on one XCD (a diagnostic switch, read on
+// every call; the results are the same bits either way).
+bool exchange_forced_device();
+
 // One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
 // ridge, denominator and normalisation (no init or final state).
 bool fast64_supported(const FwdProblem &p);

@@ -57,6 +57,10 @@ def parse():
                     help="only run plain device copies of 256 MiB (for scaling HBM counters)")
     ap.add_argument("--only", choices=SECONDARY,
                     help="only time this secondary workload and print its record (for profiling)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="only time plain device copies of the headline's size and of 1 GiB")
+    ap.add_argument("--calls", type=int, default=100,
+                    help="event-timed single calls per mode for the p10/p50/p90 figures")
     return ap.parse_args()
 
 
@@ -104,14 +108,87 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "copies": 5}))
 
 
+def copy_ceiling(dev):
+    """What a plain device copy sustains at the headline's byte count
+    (25.2 MB read + 16.8 MB written -> one 21 MB copy each way, 42 MB moved)
+    and at 1 GiB: p50 of HIP-event-timed copies, cold (a 1 GiB scratch write
+    between copies) and warm."""
+    import torch
+
+    out = []
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    for nbytes in (41943040 // 2, 1 << 30):
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        rec = {"bytes_moved": 2 * nbytes}
+        for mode in ("cold", "warm"):
+            ts = event_times(lambda i: b.copy_(a), stream, 30, scratch if mode == "cold" else None)
+            p50 = percentiles(ts)["p50"]
+            rec[mode] = {"p50_us": p50, "GB_per_s": 2 * nbytes / (p50 * 1e-6) / 1e9}
+        out.append(rec)
+        del a, b
+    return {"copy_ceiling": out}
+
+
+def event_times(fn, stream, calls, flush=None, warmup=3):
+    """Microseconds of each of ``calls`` calls fn(i), each bracketed by its
+    own pair of HIP events on ``stream``.  flush: a buffer written in full
+    before every call, outside the events (cold mode: evicts the caches);
+    without it the calls run back to back (warm mode).  The device is held
+    busy first (torch.cuda._sleep) so the host enqueues ahead of it and no
+    launch gap falls inside a pair of events."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(50_000_000)  # ~20 ms of device time for the host to run ahead
+        for i in range(calls):
+            if flush is not None:
+                flush.fill_(i & 0xFF)
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def percentiles(ts):
+    import numpy as np
+
+    a = np.asarray(ts, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def algorithmic_bytes(w) -> int:
     # q, k (d each) and v (dv) in bf16 read once, out (dv) in fp32 written once
     per_token = 2 * (2 * w.d + w.dv) + 4 * w.dv
     return w.B * w.H * w.n * per_token
 
 
+_LAST_PCT = {}
+
+
 def time_calls(fn, stream, reps, warmup=3):
-    """Mean microseconds per call of fn(i), HIP events on ``stream``."""
+    """Mean microseconds per call of fn(i) over ``reps`` calls bracketed by
+    one pair of HIP events on ``stream``; the p10/p50/p90 of the same calls
+    timed one by one (each between its own events, see event_times) are kept
+    for the record that follows (``single_call_us``)."""
     import torch
 
     with torch.cuda.stream(stream):
@@ -125,6 +202,8 @@ def time_calls(fn, stream, reps, warmup=3):
             fn(i)
         e1.record(stream)
     e1.synchronize()
+    _LAST_PCT.clear()
+    _LAST_PCT.update(percentiles(event_times(fn, stream, reps, warmup=0)))
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
@@ -164,7 +243,7 @@ def secondary_workloads(dev, stream, only=None):
                             out=out, den=den, workspace=ws)
     us = time_calls(ratio_call, stream, 20)
     tok = w.B * w.H * w.n
-    res.append({"workload": w.name, "entry": "hla_forward_chunked (out + den)", "us_per_call": us,
+    res.append({"workload": w.name, "entry": "hla_forward_chunked (out + den)", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
                 "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
     del sets
     if only is not None:
@@ -191,7 +270,7 @@ def secondary_rest(dev, stream, only):
     us = time_calls(lambda i: hla.forward_chunked(q, k, v, gamma=w.gamma, chunk=w.chunk, out=out,
                                                   workspace=ws), stream, 5, warmup=2)
     tok = w.B * w.H * w.n
-    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us,
+    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
                 "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
     del q, k, v, out, ws
     if only is not None:
@@ -221,7 +300,7 @@ def secondary_states(dev, stream, only):
     if only in (None, "decode"):
         us = time_calls(lambda i: hla.decode_step(q1, k1, v1, st, out=o1), stream, 30)
         per_state = 2 * state_b + 2 * (2 * w.d + w.dv) + 4 * w.dv
-        res.append({"workload": w.name, "entry": "hla_decode_step", "us_per_call": us,
+        res.append({"workload": w.name, "entry": "hla_decode_step", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
                     "states_per_s": N / (us * 1e-6), "roofline": roof(N * per_state, us)})
     if only == "decode":
         return res
@@ -233,7 +312,7 @@ def secondary_states(dev, stream, only):
     us = time_calls(lambda i: hla.state_compose(st, b, r), stream, 30)
     per_pair = 3 * (state_b + 4)
     res.append({"workload": "masked_hla_compose_4096_pairs_d128", "entry": "hla_state_compose",
-                "us_per_call": us, "pairs_per_s": N / (us * 1e-6), "roofline": roof(N * per_pair, us)})
+                "us_per_call": us, "single_call_us": dict(_LAST_PCT), "pairs_per_s": N / (us * 1e-6), "roofline": roof(N * per_pair, us)})
     del st, b, r
     if only is not None:
         return res
@@ -280,7 +359,7 @@ def forward_with_state(dev, stream):
         hla.forward_chunked(q, k, v, chunk=w.chunk, out=out, workspace=ws, final_state=fin)
     us = time_calls(call_state, stream, 20)
     return [{"workload": "masked_hla_fwd_final_state_B4_H8_n2048_d64_bf16_w64",
-             "entry": "hla_forward_chunked (out + final state, generic path)", "us_per_call": us,
+             "entry": "hla_forward_chunked (out + final state, generic path)", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
              "tokens_per_s": w.B * w.n / (us * 1e-6),
              "roofline": roof(tok * per_tok + w.B * w.H * state_b, us)}]
 
@@ -315,7 +394,7 @@ def backward_headline_shape(dev, stream):
         hla.backward_chunked(q, k, v, dout, chunk=w.chunk, workspace=ws, grads=grads)
     us = time_calls(call, stream, 10, warmup=2)
     res = [{"workload": "masked_hla_bwd_B4_H8_n2048_d64_bf16_w64", "entry": "hla_backward_chunked",
-            "us_per_call": us, "tokens_per_s": w.B * w.n / (us * 1e-6),
+            "us_per_call": us, "single_call_us": dict(_LAST_PCT), "tokens_per_s": w.B * w.n / (us * 1e-6),
             "roofline": roof(tok * per_tok, us)}]
 
     # the backward of a sequence shard: from an initial state (the previous
@@ -338,7 +417,7 @@ def backward_headline_shape(dev, stream):
     us = time_calls(call_shard, stream, 10, warmup=2)
     res.append({"workload": "masked_hla_bwd_shard_B4_H8_n2048_d64_bf16_w64",
                 "entry": "hla_backward_chunked (init, dfinal in; dinit out)",
-                "us_per_call": us, "tokens_per_s": w.B * w.n / (us * 1e-6),
+                "us_per_call": us, "single_call_us": dict(_LAST_PCT), "tokens_per_s": w.B * w.n / (us * 1e-6),
                 "roofline": roof(tok * per_tok + 3 * N * state_b, us)})
     return res
 
@@ -358,16 +437,25 @@ def small_forward(dev, stream):
                      device=dev)
     us = time_calls(lambda i: hla.forward_chunked(q, k, v, out=out, workspace=ws), stream, 50)
     per_tok = 4 * (2 * w.d + 2 * w.dv)
-    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us,
+    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
                 "tokens_per_s": w.B * w.n / (us * 1e-6),
                 "roofline": roof(w.B * w.H * w.n * per_tok, us)})
     return res
 
 
 def cpu_baseline(w, q, k, v):
+    """The fp64 oracle on the host: one head per thread, as many threads as
+    the process may use, at most the heads (B*H) and at most the CPU share
+    of one GPU on these hosts (16 threads, the limit the hosts set through
+    OMP_NUM_THREADS)."""
     import oracle
 
-    threads = oracle.default_threads()
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(nproc, w.B * w.H, share))
     oracle.forward(q[:, :1, :64], k[:, :1, :64], v[:, :1, :64], want_state=False)  # load/build
     reps, t_total = 0, 0.0
     while t_total < 10.0 and reps < 2000:
@@ -376,10 +464,11 @@ def cpu_baseline(w, q, k, v):
         t_total += time.perf_counter() - t0
         reps += 1
     tokens = w.B * w.n * reps
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": min(threads, w.B * w.H),
-            "kind": "oracle",
-            "sample": f"the full {w.name} workload, {reps} repetition(s), {t_total:.1f} s; "
-                      f"fp64 serial recurrence, one head per thread"}
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(), "nproc": nproc, "thread_cap": share,
+            "sample": f"the full {w.name} workload ({w.B * w.H} heads), {reps} repetition(s), "
+                      f"{t_total:.1f} s; fp64 serial recurrence, one head per thread, "
+                      f"{threads} threads = min(nproc {nproc}, heads {w.B * w.H}, CPU share {share})"}
 
 
 def main():
@@ -399,6 +488,9 @@ def main():
         copy_calibration()
         return
     dev = torch.device("cuda:0")
+    if args.copy_ceiling:
+        print(json.dumps(copy_ceiling(dev)))
+        return
     if args.only:
         for rec in secondary_workloads(dev, torch.cuda.Stream(device=dev), only=args.only):
             print(json.dumps(rec))
@@ -473,6 +565,14 @@ def main():
     if args.eager:
         ms_total = eager_ms * K
     torch.cuda.synchronize()
+    # single calls, each between its own events: cold (caches evicted before
+    # every call by a 1 GiB write) and warm (one input set, back to back)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = percentiles(event_times(step, stream, args.calls, flush=scratch))
+    warm = percentiles(event_times(lambda i: step(0), stream, args.calls))
+    del scratch
+    for s in sets:
+        assert hla.give_ups(s[4]) == 0, "a cross-workgroup wait gave up"
 
     ms = ms_total / K
     tokens = w.B * w.n
@@ -500,6 +600,12 @@ def main():
                      "kernel": "k_fast64 (the whole hla_forward_chunked call is one launch)",
                      "algorithmic_bytes_per_step": alg},
         "eager_ms_per_step": eager_ms,
+        "single_call_us": {"cold": cold, "warm": warm,
+                           "how": "HIP events around each eager call on the launch stream; cold: a 1 GiB "
+                                  "scratch write before every call (outside the events) evicts L2 and "
+                                  "the 256 MB Infinity Cache; warm: one input set, calls back to back"},
+        "roofline_single_call_p50_cold": {"frac": alg / (cold["p50"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                          "achieved_GBps": alg / (cold["p50"] * 1e-6) / 1e9},
         "parity_guard_row_error": err,
     }
     if not args.headline_only:

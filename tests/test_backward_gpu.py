@@ -405,4 +405,51 @@ def test_autograd_op_chains_segments(norm, lam):
     torch.cuda.synchronize()
     *ref, rdini = ob.backward(q, k, v, dout, g, lam, norm, types.SimpleNamespace(**ini), init_grad=True)
     check([x.grad.cpu() for x in (qg, kg, vg)], ref)
+    # the op reads S through its symmetric part, so the leaf S receives the
+    # symmetric part of the oracle's gradient (which counts every entry of S
+    # as its own variable)
+    rS = np.asarray(rdini["S"])
+    rdini = dict(rdini, S=0.5 * (rS + rS.transpose(0, 2, 1)))
     _dinit_check(types.SimpleNamespace(**{x: getattr(leaf, x).grad for x in ("S", "C", "m", "G", "h")}), rdini)
+
+
+def test_autograd_op_symmetrises_the_initial_key_moment():
+    """A leaf initial S that is not symmetric (as after an optimizer step)
+    enters through its symmetric part: the op's output equals the forward
+    from (S + S^T)/2, the gradient S receives has no antisymmetric part, it
+    equals the oracle's dinit symmetrised, and one SGD step from a symmetric
+    S keeps S symmetric."""
+    import types
+
+    from oracle import backward as ob
+    B, H, n, d, dv = 1, 2, 90, 32, 32
+    q, k, v = inputs.qkv(B, H, n, d, dv, torch.float32, seed=131)
+    g = inputs.gamma_list_fp32([0.97, 0.99])
+    dout = inputs.upstream(B, H, n, dv, seed=133)
+    N = B * H
+    gen = torch.Generator().manual_seed(135)
+    a = 0.05 * torch.randn(N, d, d, generator=gen)
+    ini = {"S": a + 0.01 * torch.eye(d),  # not symmetric
+           "C": 0.1 * torch.randn(N, d, dv, generator=gen), "m": 0.1 * torch.randn(N, d, generator=gen),
+           "G": torch.zeros(N, d, dv), "h": torch.zeros(N, d)}
+    Ssym = 0.5 * (ini["S"] + ini["S"].transpose(1, 2))  # the same fp32 operations as the op's
+    qg, kg, vg = (x.to(DEV) for x in (q, k, v))
+    st = hla.State(*(ini[x].to(DEV).requires_grad_(True) for x in ("S", "C", "m", "G", "h")))
+    out, _ = hla.attention(qg, kg, vg, gamma=g, chunk=32, init=st)
+    (out * dout.to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    ref_out, _, _ = hla.forward_chunked(qg, kg, vg, gamma=g, chunk=32,
+                                        init=hla.State(Ssym.to(DEV), *(ini[x].to(DEV) for x in ("C", "m", "G", "h"))))
+    assert torch.equal(out.detach(), ref_out)
+    dS = st.S.grad.cpu().double()
+    assert float((dS - dS.transpose(1, 2)).abs().max()) == 0.0
+    sym = dict(ini, S=Ssym)
+    *_, rdini = ob.backward(q, k, v, dout, g, 0.0, False, types.SimpleNamespace(**sym), init_grad=True)
+    rS = np.asarray(rdini["S"], dtype=np.float64)
+    rS = 0.5 * (rS + rS.transpose(0, 2, 1))
+    e = slab_err(dS, rS)
+    print(f"symmetrised dS slab error {e:.3e}")
+    assert e <= GTOL
+    # one SGD step from the symmetric S: S stays exactly symmetric
+    S1 = (Ssym.to(DEV) - 0.1 * st.S.grad).cpu()
+    assert torch.equal(S1, S1.transpose(1, 2))
