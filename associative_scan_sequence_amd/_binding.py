@@ -21,9 +21,10 @@ LIB_PATH = os.path.join(_PKG, "libhla.so")
 HLA_F32, HLA_BF16 = 0, 1
 STATUS = {0: "HLA_OK", 1: "HLA_ERR_INVALID_ARGUMENT", 2: "HLA_ERR_UNSUPPORTED",
           3: "HLA_ERR_ALIGNMENT", 4: "HLA_ERR_WORKSPACE", 5: "HLA_ERR_DEVICE"}
-EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_backward_workspace_size",
-            "hla_backward_chunked", "hla_decode_step", "hla_state_compose", "hla_status_string",
-            "hla_last_error")
+EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_forward_chunked_noalloc",
+            "hla_backward_workspace_size", "hla_backward_chunked", "hla_decode_step", "hla_state_compose",
+            "hla_status_string", "hla_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HLA_NOALLOC_SCRATCH_BYTES
 
 
 class CState(ctypes.Structure):
@@ -62,6 +63,8 @@ def load(path: str = LIB_PATH):
     lib.hla_forward_workspace_size.restype = sz
     lib.hla_forward_chunked.argtypes = [pp, vp, vp, vp, vp, vp, ps, ps, vp, sz, vp]
     lib.hla_forward_chunked.restype = ctypes.c_int
+    lib.hla_forward_chunked_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, ps, ps, vp]
+    lib.hla_forward_chunked_noalloc.restype = ctypes.c_int
     lib.hla_backward_workspace_size.argtypes = [pp]
     lib.hla_backward_workspace_size.restype = sz
     lib.hla_backward_chunked.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, vp, ps, ps, vp, sz, vp]
@@ -221,6 +224,41 @@ def forward_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=
                                  ws_ptr, ws_bytes, _stream(dev))
     _check(st)
     return out, den, fin
+
+
+def forward_chunked_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, gamma=None,
+                            ridge: float = 0.0, normalize: bool = False, chunk: int = 0,
+                            init: Optional[State] = None, out: Optional[torch.Tensor] = None,
+                            den: Optional[torch.Tensor] = None, final_state: Optional[State] = None):
+    """The forward through ``hla_forward_chunked_noalloc``: no workspace, the
+    library's static scratch instead (calls on one GPU must not overlap in
+    time).  With ``out``, ``den`` and ``final_state`` given nothing is
+    allocated here either.  Returns (out, den or None, final_state or None)."""
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (torch.bfloat16, torch.float32))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}: "
+                         "expected q,k [B,H,n,d] and v [B,H,n,dv]")
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    p, _keep = _params(B, H, n, d, dv, chunk, q.dtype, gamma, ridge, normalize)
+    if out is None:
+        out = torch.empty(B, H, n, dv, dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,))
+    if den is not None:
+        _need(den, "den", (torch.float32,))
+    ini_c = init.c() if init is not None else None
+    fin_c = final_state.c() if final_state is not None else None
+    st = lib.hla_forward_chunked_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         out.data_ptr(), den.data_ptr() if den is not None else None,
+                                         ctypes.byref(ini_c) if ini_c is not None else None,
+                                         ctypes.byref(fin_c) if fin_c is not None else None,
+                                         _stream(q.device))
+    _check(st)
+    return out, den, final_state
 
 
 def backward_workspace_size(B, H, n, d, dv, *, chunk=0, dtype=torch.bfloat16, gamma=None,

@@ -182,6 +182,16 @@ size_t workspace_need(const hla_params *p, const Geometry &geo, const hla_state 
     return hla::kCtrlBytes + (gen > fused ? gen : fused);
 }
 
+// Workspace bytes of the one path a call takes (the control block included).
+size_t path_need(const hla_params *p, const Geometry &geo, FwdPath path) {
+    const int BH = p->B * p->H;
+    size_t data = 0;
+    if (path == FwdPath::Fast64) data = hla::fast64_workspace_bytes(BH, p->n);
+    else if (path == FwdPath::Fused128) data = hla::fused128_workspace_bytes(BH, p->n);
+    else data = hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w);
+    return hla::kCtrlBytes + data;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,6 +221,24 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
                                float *out, float *den, const hla_state *init,
                                hla_state *final_state, void *workspace, size_t workspace_bytes,
                                hipStream_t stream) {
+    return hla::forward_impl(p, q, k, v, out, den, init, final_state, workspace, workspace_bytes, stream,
+                             nullptr);
+}
+
+}  // extern "C"
+
+namespace hla {
+
+hla_status set_error(hla_status s, const char *msg) { return fail(s, "%s", msg); }
+
+// The forward entry points' common body.  scratch_name == nullptr: the
+// caller's workspace, which must hold hla_forward_workspace_size(p) bytes
+// (the largest path's need).  Otherwise a fixed buffer of workspace_bytes
+// (so named in errors) that must hold only what the path this call takes
+// needs.
+hla_status forward_impl(const hla_params *p, const void *q, const void *k, const void *v, float *out,
+                        float *den, const hla_state *init, hla_state *final_state, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream, const char *scratch_name) {
     Geometry geo{};
     hla_status s = forward_geometry(p, &geo);
     if (s != HLA_OK) return s;
@@ -230,8 +258,12 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     }
     if (init && (s = check_state(init, "init")) != HLA_OK) return s;
     if (final_state && (s = check_state(final_state, "final_state")) != HLA_OK) return s;
-    const size_t need = workspace_need(p, geo, init, final_state, den);
-    if (need > 0) {
+    const size_t need = scratch_name ? path_need(p, geo, choose_path(p, geo, init, final_state, den, fp.gam))
+                                     : workspace_need(p, geo, init, final_state, den);
+    if (scratch_name && need > workspace_bytes)
+        return fail(HLA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; %s holds %zu", need, scratch_name,
+                    workspace_bytes);
+    if (!scratch_name && need > 0) {
         if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (workspace_bytes < need)
             return fail(HLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -262,6 +294,11 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     if (final_state) fp.fin = *final_state;
     fp.ws = workspace; fp.ws_bytes = workspace_bytes;
     if (n == 0 && !final_state) return ok();
+    if (scratch_name) {  // the static scratch: its address, once every argument has passed
+        const hla_status ss = noalloc_scratch(&workspace);
+        if (ss != HLA_OK) return ss;
+        fp.ws = workspace;
+    }
     char *ws = static_cast<char *>(workspace);
     hipError_t e;
     const FwdPath path = choose_path(p, geo, init, final_state, den, fp.gam);
@@ -277,6 +314,10 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "forward launch: %s", hipGetErrorString(e));
     return ok();
 }
+
+}  // namespace hla
+
+extern "C" {
 
 size_t hla_backward_workspace_size(const hla_params *p) {
     Geometry geo{};

@@ -75,6 +75,24 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t s);
 // of an empty sequence).
 hipError_t zero_state_grad(const hla_state &s, int BH, int d, int dv, hipStream_t st);
 
+// The body of the forward entry points (hla_api.cpp): validation, then the
+// kernels.  scratch_name == nullptr: `workspace` is the caller's and must
+// hold hla_forward_workspace_size(p) bytes.  Otherwise `workspace` is
+// ignored: the static scratch (workspace_bytes of it, named scratch_name in
+// errors) must hold what the path of this call needs, and its address is
+// looked up only once every argument has passed validation.
+hla_status forward_impl(const hla_params *p, const void *q, const void *k, const void *v, float *out,
+                        float *den, const hla_state *init, hla_state *final_state, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream, const char *scratch_name);
+
+// The current device's address of the static scratch behind
+// hla_forward_chunked_noalloc (noalloc.hip; looked up once per device).
+hla_status noalloc_scratch(void **ptr);
+constexpr size_t kNoallocBytes = HLA_NOALLOC_SCRATCH_BYTES;
+
+// Records msg as this thread's last error (hla_last_error) and returns s.
+hla_status set_error(hla_status s, const char *msg);
+
 // True when the environment sets HLA_EXCHANGE=device: the one-launch d = 64
 // forward then hands aggregates between workgroups device-coherently even
 // when every segment of a head runs on one XCD (a diagnostic switch, read on

@@ -36,7 +36,8 @@
  *     Tensors are contiguous, row-major.  The state index of batch b,
  *     head h is b*H + h.
  *   - The caller owns all memory.  The library allocates and frees nothing
- *     and keeps no state between calls beyond its loaded code.
+ *     and keeps no state between calls beyond its loaded code and the
+ *     static scratch of hla_forward_chunked_noalloc.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never
  *     synchronise.  Validation is host-only and happens before anything is
  *     enqueued; on any error nothing is enqueued and no output is touched.
@@ -108,12 +109,16 @@ typedef struct {
  *
  * The one-launch kernels (bf16, d = dv = 64 or 128, no init or final state)
  * hand partial sums between workgroups of one launch when a head is cut into
- * several segments, and then rely on all of them being resident at once (at
- * most one per CU).  Kernels that other
- * streams run at the same time can delay that; a wait that exceeds a fixed
- * spin limit (about 4M polls) gives up, adds one to word 3 and the outputs
- * of that call are then not reliable.  A caller that shares the device
- * can check word 3. */
+ * several segments: a segment waits for the sums of the earlier segments of
+ * its head.  The d = 128 kernel hands segments out by ticket, so a segment
+ * only ever waits on segments that running workgroups hold, whatever other
+ * streams run.  The d = 64 kernel assigns segment s to workgroup s mod grid
+ * (grid <= CU count, one workgroup per CU), so its waits rely on the earlier
+ * workgroups being dispatched; kernels that other streams run at the same
+ * time can delay that.  A wait that exceeds a fixed spin limit (about 4M
+ * polls, seconds) gives up and adds one to word 3, and the carry it waited
+ * for is made NaN: every output that depends on it (that segment's and the
+ * later segments' of the head) is then NaN, never a wrong number. */
 size_t hla_forward_workspace_size(const hla_params *p);
 
 /* Chunk-parallel masked forward ([SUM] sec. 4 and 5: token deltas feed an
@@ -137,6 +142,31 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
                                const hla_state *init, hla_state *final_state,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/* Bytes of the static scratch behind hla_forward_chunked_noalloc. */
+#define HLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* hla_forward_chunked without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, computation, outputs and
+ * errors as hla_forward_chunked, minus workspace and workspace_bytes: the
+ * workspace is a static device array of HLA_NOALLOC_SCRATCH_BYTES owned by
+ * the library, one per GPU it runs on, held until the process ends.  The
+ * call allocates nothing; its first call on a device looks up that device's
+ * copy of the array.  A call whose kernel path needs more scratch than that
+ * (the one-launch paths need about 13 MB at B4 H8 n2048 d64 and 50 MB at
+ * B8 H8 n4096 d64; the generic path with an initial or final state needs
+ * about 2.2 KB per head-token at d = dv = 64) fails with HLA_ERR_WORKSPACE
+ * before anything is enqueued.  Every call on a GPU shares that GPU's array,
+ * which keeps the previous call's contents (a control block that each call
+ * leaves valid for the next; nothing needs clearing): calls that overlap in
+ * time on one GPU (two streams or two host threads) race and must not be
+ * made; calls ordered on one stream are fine, captured into a HIP graph
+ * too. */
+hla_status hla_forward_chunked_noalloc(const hla_params *p, const void *q, const void *k,
+                                       const void *v, float *out, float *den,
+                                       const hla_state *init, hla_state *final_state,
+                                       hipStream_t stream);
 
 /* Bytes of device workspace hla_backward_chunked needs for these params (0
  * for an invalid p).  Unlike the forward's, it holds no control block: its

@@ -294,3 +294,22 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 16, 16)
     with pytest.raises(ValueError, match="HIP device"):
         hla.forward_chunked(q, q, q)
+
+
+def test_noalloc_validates_before_any_device_call(lib):
+    """hla_forward_chunked_noalloc takes the forward's arguments without a
+    workspace; bad arguments and calls whose path needs more than the static
+    scratch fail on the host, before the scratch is looked up on a device."""
+    def call(p, **kw):
+        a = dict(q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None, init=None, fin=None)
+        a.update(kw)
+        return lib.hla_forward_chunked_noalloc(ctypes.byref(p), a["q"], a["k"], a["v"], a["out"], a["den"],
+                                               ctypes.byref(a["init"]) if a["init"] is not None else None,
+                                               ctypes.byref(a["fin"]) if a["fin"] is not None else None, None)
+    assert call(params(d=48)) == UNSUPPORTED
+    assert call(params(), q=None) == INVALID and "q is NULL" in last(lib)
+    # the generic path (a final state) at B4 H8 n2048 d64 needs more than 64 MiB
+    fin = CState(*[addr(10 + i) for i in range(6)])
+    p = params(B=4, H=8, n=2048, d=64, dv=64, chunk=64)
+    assert call(p, fin=fin) == WORKSPACE
+    assert "static scratch" in last(lib) and str(hla._binding.NOALLOC_SCRATCH_BYTES) in last(lib)
