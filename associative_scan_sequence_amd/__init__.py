@@ -8,14 +8,19 @@ C ABI in include/hla.h); this package is its thin Python binding:
 * :func:`backward_chunked` -- gradients with respect to q, k, v (``hla_backward_chunked``)
 * :func:`attention` -- the two as one differentiable ``torch.autograd`` op
 * :func:`decode_step` -- one streaming token per state (``hla_decode_step``)
+* :func:`decode_step_mq` -- the same with the key moment packed and shared by
+  groups of query heads (``hla_decode_step_mq``; :func:`key_moment_pack` and
+  :func:`key_moment_unpack` convert full and packed key moments)
 * :func:`state_compose` -- masked semidirect-product composition (``hla_state_compose``)
 """
-from ._binding import (EXPORTED, LIB_PATH, HlaError, State, attention, backward_chunked,
-                       backward_workspace_size, decode_step, forward_chunked, forward_chunked_noalloc,
-                       give_ups, load,
+from ._binding import (EXPORTED, LIB_PATH, HlaError, MqState, State, attention, backward_chunked,
+                       backward_workspace_size, decode_step, decode_step_mq, forward_chunked,
+                       forward_chunked_noalloc, give_ups, key_moment_pack, key_moment_unpack, load,
+                       packed_size,
                        state_compose, workspace_size)
 
-__all__ = ["EXPORTED", "LIB_PATH", "HlaError", "State", "attention", "backward_chunked",
-           "backward_workspace_size", "decode_step", "forward_chunked", "forward_chunked_noalloc",
-           "give_ups", "load",
+__all__ = ["EXPORTED", "LIB_PATH", "HlaError", "MqState", "State", "attention", "backward_chunked",
+           "backward_workspace_size", "decode_step", "decode_step_mq", "forward_chunked",
+           "forward_chunked_noalloc", "give_ups", "key_moment_pack", "key_moment_unpack", "load",
+           "packed_size",
            "state_compose", "workspace_size"]

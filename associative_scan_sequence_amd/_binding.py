@@ -22,8 +22,9 @@ HLA_F32, HLA_BF16 = 0, 1
 STATUS = {0: "HLA_OK", 1: "HLA_ERR_INVALID_ARGUMENT", 2: "HLA_ERR_UNSUPPORTED",
           3: "HLA_ERR_ALIGNMENT", 4: "HLA_ERR_WORKSPACE", 5: "HLA_ERR_DEVICE"}
 EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_forward_chunked_noalloc",
-            "hla_backward_workspace_size", "hla_backward_chunked", "hla_decode_step", "hla_state_compose",
-            "hla_status_string", "hla_last_error")
+            "hla_backward_workspace_size", "hla_backward_chunked", "hla_decode_step", "hla_decode_step_mq",
+            "hla_key_moment_pack", "hla_key_moment_unpack", "hla_state_compose", "hla_status_string",
+            "hla_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -71,6 +72,11 @@ def load(path: str = LIB_PATH):
     lib.hla_backward_chunked.restype = ctypes.c_int
     lib.hla_decode_step.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
     lib.hla_decode_step.restype = ctypes.c_int
+    lib.hla_decode_step_mq.argtypes = [pp, ctypes.c_int32, vp, vp, vp, ps, vp, vp, vp]
+    lib.hla_decode_step_mq.restype = ctypes.c_int
+    for fn in (lib.hla_key_moment_pack, lib.hla_key_moment_unpack):
+        fn.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+        fn.restype = ctypes.c_int
     lib.hla_state_compose.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ps, ps, ps, vp]
     lib.hla_state_compose.restype = ctypes.c_int
     lib.hla_status_string.argtypes = [ctypes.c_int]
@@ -342,6 +348,83 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: State,
     st = lib.hla_decode_step(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              ctypes.byref(sc), out.data_ptr(),
                              den.data_ptr() if den is not None else None, _stream(dev))
+    _check(st)
+    return out, den
+
+
+@dataclass
+class MqState:
+    """Decode state with the key moment shared by groups of query heads and
+    stored packed (hla_mq_state): S [B*kv_heads, d*(d+1)/2]; C, G
+    [B*H, d, dv]; m, h [B*H, d]; rho [B*kv_heads] or None (fp32, device)."""
+    S: torch.Tensor
+    C: torch.Tensor
+    m: torch.Tensor
+    G: torch.Tensor
+    h: torch.Tensor
+    rho: Optional[torch.Tensor] = None
+
+    def tensors(self):
+        return (self.S, self.C, self.m, self.G, self.h, self.rho)
+
+    def c(self) -> CState:
+        for t in self.tensors():
+            if t is not None:
+                _need(t, "state", (torch.float32,))
+        return CState(*[t.data_ptr() if t is not None else None for t in self.tensors()])
+
+
+def packed_size(d: int) -> int:
+    return d * (d + 1) // 2
+
+
+def key_moment_pack(S: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Full symmetric key moments [N,d,d] -> packed [N, d(d+1)/2] (``hla_key_moment_pack``)."""
+    _need(S, "S", (torch.float32,))
+    N, d, _ = S.shape
+    if out is None:
+        out = torch.empty(N, packed_size(d), dtype=torch.float32, device=S.device)
+    _need(out, "out", (torch.float32,))
+    _check(load().hla_key_moment_pack(N, d, S.data_ptr(), out.data_ptr(), _stream(S.device)))
+    return out
+
+
+def key_moment_unpack(P: torch.Tensor, d: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed key moments [N, d(d+1)/2] -> full symmetric [N,d,d] (``hla_key_moment_unpack``)."""
+    _need(P, "P", (torch.float32,))
+    N = P.shape[0]
+    if out is None:
+        out = torch.empty(N, d, d, dtype=torch.float32, device=P.device)
+    _need(out, "out", (torch.float32,))
+    _check(load().hla_key_moment_unpack(N, d, P.data_ptr(), out.data_ptr(), _stream(P.device)))
+    return out
+
+
+def decode_step_mq(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: MqState, *, gamma=None,
+                   ridge: float = 0.0, normalize: bool = False, return_den: bool = False,
+                   out: Optional[torch.Tensor] = None, den: Optional[torch.Tensor] = None):
+    """One token per query head through ``hla_decode_step_mq``: q [B,H,d];
+    k [B,G,d] and v [B,G,dv] for G groups of query heads (G divides H);
+    ``state`` (an MqState) is updated in place.  Returns (out [B,H,dv], den [B,H] or None)."""
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (torch.bfloat16, torch.float32))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape[0] != q.shape[0] or v.shape[:2] != k.shape[:2] \
+            or k.shape[2] != q.shape[2]:
+        raise ValueError("expected q [B,H,d], k [B,G,d] and v [B,G,dv]")
+    B, H, d = q.shape
+    G, dv = k.shape[1], v.shape[-1]
+    p, _keep = _params(B, H, 1, d, dv, 0, q.dtype, gamma, ridge, normalize)
+    if out is None:
+        out = torch.empty(B, H, dv, dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,))
+    if den is None and return_den:
+        den = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    sc = state.c()
+    st = lib.hla_decode_step_mq(ctypes.byref(p), G, q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sc),
+                                out.data_ptr(), den.data_ptr() if den is not None else None, _stream(q.device))
     _check(st)
     return out, den
 

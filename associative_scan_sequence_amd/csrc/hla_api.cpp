@@ -451,6 +451,93 @@ hla_status hla_decode_step(const hla_params *p, const void *q, const void *k, co
     return ok();
 }
 
+hla_status hla_decode_step_mq(const hla_params *p, int32_t kv_heads, const void *q, const void *k,
+                              const void *v, hla_mq_state *state, float *out, float *den,
+                              hipStream_t stream) {
+    if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (p->B < 1 || p->H < 1) return fail(HLA_ERR_INVALID_ARGUMENT, "B=%d, H=%d must be >= 1", p->B, p->H);
+    if (p->n != 1) return fail(HLA_ERR_INVALID_ARGUMENT, "decode needs n = 1 (got %d)", p->n);
+    if (kv_heads < 1 || p->H % kv_heads != 0)
+        return fail(HLA_ERR_INVALID_ARGUMENT, "kv_heads=%d must be >= 1 and divide H=%d", kv_heads, p->H);
+    if (p->d != 32 && p->d != 64 && p->d != 128)
+        return fail(HLA_ERR_UNSUPPORTED, "d=%d: the packed key moment needs d = 32, 64 or 128", p->d);
+    hla::DecodeMqProblem dp{};
+    hla_status s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &dp.gam);
+    if (s != HLA_OK) return s;
+    const int R = p->H / kv_heads;
+    if (p->gamma) {  // one decay per group: the group's S is decayed once
+        for (int h = 0; h < p->H; ++h)
+            if (p->gamma[h] != p->gamma[(h / R) * R])
+                return fail(HLA_ERR_INVALID_ARGUMENT, "gamma[%d] differs from the first decay of its group", h);
+    }
+    const uint64_t N = static_cast<uint64_t>(p->B) * p->H, NG = static_cast<uint64_t>(p->B) * kv_heads;
+    if (N > 0x7fffffffull / (128ull * 128ull))
+        return fail(HLA_ERR_UNSUPPORTED, "B*H=%llu too large", (unsigned long long)N);
+    const void *req[4] = {q, k, v, out};
+    const char *nm[4] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i) {
+        if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
+        if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
+    }
+    if (den && !aligned16(den)) return fail(HLA_ERR_ALIGNMENT, "den is not 16-byte aligned");
+    if (!state) return fail(HLA_ERR_INVALID_ARGUMENT, "state is NULL");
+    {
+        const hla_state as{state->S, state->C, state->m, state->G, state->h, state->rho};
+        if ((s = check_state(&as, "state")) != HLA_OK) return s;
+    }
+    const size_t esz = p->dtype == HLA_BF16 ? 2 : 4, d = p->d, dv = p->dv;
+    std::vector<Span> outs, ins;
+    outs.push_back(span("out", out, N * dv * 4));
+    if (den) outs.push_back(span("den", den, N * 4));
+    outs.push_back(span("state.S", state->S, NG * (d * (d + 1) / 2) * 4));
+    outs.push_back(span("state.C", state->C, N * d * dv * 4));
+    outs.push_back(span("state.m", state->m, N * d * 4));
+    outs.push_back(span("state.G", state->G, N * d * dv * 4));
+    outs.push_back(span("state.h", state->h, N * d * 4));
+    if (state->rho) outs.push_back(span("state.rho", state->rho, NG * 4));
+    ins.push_back(span("q", q, N * d * esz));
+    ins.push_back(span("k", k, NG * d * esz));
+    ins.push_back(span("v", v, NG * dv * esz));
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    dp.B = p->B; dp.H = p->H; dp.kv_heads = kv_heads; dp.d = p->d; dp.dv = p->dv; dp.dtype = p->dtype;
+    dp.ridge = p->ridge; dp.normalize = p->normalize;
+    dp.q = q; dp.k = k; dp.v = v; dp.st = *state; dp.out = out; dp.den = den;
+    const hipError_t e = hla::decode_step_mq(dp, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+static hla_status pack_common(int32_t count, int32_t d, const float *src, float *dst, bool pack,
+                              hipStream_t stream) {
+    if (count < 0) return fail(HLA_ERR_INVALID_ARGUMENT, "count=%d must be >= 0", count);
+    if (d != 32 && d != 64 && d != 128)
+        return fail(HLA_ERR_UNSUPPORTED, "d=%d: the packed key moment needs d = 32, 64 or 128", d);
+    if (count == 0) return ok();
+    if (static_cast<uint64_t>(count) * 128ull * 128ull > 0x7fffffffull)
+        return fail(HLA_ERR_UNSUPPORTED, "count=%d too large", count);
+    if (!src || !dst) return fail(HLA_ERR_INVALID_ARGUMENT, "a pointer is NULL");
+    if (!aligned16(src) || !aligned16(dst)) return fail(HLA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t full = static_cast<size_t>(count) * d * d * 4, packed = static_cast<size_t>(count) * (d * (d + 1) / 2) * 4;
+    std::string detail;
+    if (first_overlap({span("dst", dst, pack ? packed : full)}, {span("src", src, pack ? full : packed)}, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    const hipError_t e = hla::key_moment_pack(count, d, src, dst, pack, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "pack launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+hla_status hla_key_moment_pack(int32_t count, int32_t d, const float *S_full, float *S_packed,
+                               hipStream_t stream) {
+    return pack_common(count, d, S_full, S_packed, true, stream);
+}
+
+hla_status hla_key_moment_unpack(int32_t count, int32_t d, const float *S_packed, float *S_full,
+                                 hipStream_t stream) {
+    return pack_common(count, d, S_packed, S_full, false, stream);
+}
+
 hla_status hla_state_compose(int32_t count, int32_t d, int32_t dv, const hla_state *earlier,
                              const hla_state *later, hla_state *result, hipStream_t stream) {
     if (count < 0) return fail(HLA_ERR_INVALID_ARGUMENT, "count=%d must be >= 0", count);

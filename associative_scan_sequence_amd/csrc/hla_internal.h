@@ -124,6 +124,22 @@ struct DecodeProblem {
 };
 hipError_t decode_step(const DecodeProblem &p, hipStream_t s);
 
+// Decode with the key moment packed and shared by the query heads of a group
+// (decode_mq.hip); H query heads, kv_heads groups, H % kv_heads == 0.
+struct DecodeMqProblem {
+    int B, H, kv_heads, d, dv;
+    hla_dtype dtype;
+    float ridge;
+    int normalize;
+    const void *q, *k, *v;
+    hla_mq_state st;
+    float *out, *den;
+    GammaTab gam;
+};
+hipError_t decode_step_mq(const DecodeMqProblem &p, hipStream_t s);
+// count symmetric d x d matrices: full -> packed (pack) or packed -> full
+hipError_t key_moment_pack(int count, int d, const float *src, float *dst, bool pack, hipStream_t s);
+
 hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,
                          const hla_state &r, hipStream_t s);
 

@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
-SECONDARY = ("ratio", "long", "decode", "compose", "small", "state", "backward")
+SECONDARY = ("ratio", "long", "decode", "decode_mq", "compose", "small", "state", "backward")
 
 
 def parse():
@@ -302,7 +302,9 @@ def secondary_states(dev, stream, only):
         per_state = 2 * state_b + 2 * (2 * w.d + w.dv) + 4 * w.dv
         res.append({"workload": w.name, "entry": "hla_decode_step", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
                     "states_per_s": N / (us * 1e-6), "roofline": roof(N * per_state, us)})
-    if only == "decode":
+    if only in (None, "decode_mq"):
+        res += decode_mq_workloads(st, q1, k1, v1, w, stream)
+    if only in ("decode", "decode_mq"):
         return res
     # state composition of 4096 segment pairs at d = dv = 128
     b = hla.State.empty(N, w.d, w.dv, dev)
@@ -317,6 +319,38 @@ def secondary_states(dev, stream, only):
     if only is not None:
         return res
     return res + secondary_small(dev, stream, None)
+
+
+def decode_mq_workloads(st, q1, k1, v1, w, stream):
+    """The decode step with the key moment packed (hla_decode_step_mq): the
+    4096 states unshared (each of S packed, C, G read once and written once),
+    then as multi-query attention, the 16 query heads of each batch row
+    sharing k, v and one packed S."""
+    import torch
+
+    import associative_scan_sequence_amd as hla
+
+    res = []
+    d, dv, B, H = w.d, w.dv, w.B, w.H
+    N = B * H
+    o1 = torch.empty(B, H, dv, dtype=torch.float32, device=q1.device)
+    sp = 4 * hla.packed_size(d)                  # packed S bytes
+    per_head = 4 * (2 * d * dv + 2 * d)          # C, G, m, h bytes
+    mq = hla.MqState(hla.key_moment_pack(st.S), st.C, st.m, st.G, st.h, st.rho)
+    us = time_calls(lambda i: hla.decode_step_mq(q1, k1, v1, mq, out=o1), stream, 30)
+    per_state = 2 * (sp + per_head) + 2 * (2 * d + dv) + 4 * dv
+    res.append({"workload": "masked_hla_decode_packed_S_4096_states_d128", "entry": "hla_decode_step_mq (kv_heads = H)",
+                "us_per_call": us, "single_call_us": dict(_LAST_PCT), "states_per_s": N / (us * 1e-6), "bytes_per_state": per_state,
+                "roofline": roof(N * per_state, us)})
+    k1g, v1g = k1[:, :1].contiguous(), v1[:, :1].contiguous()
+    Sg = mq.S.view(B, H, -1)[:, 0].contiguous()
+    mqa = hla.MqState(Sg, st.C, st.m, st.G, st.h, st.rho.view(B, H)[:, 0].contiguous())
+    us = time_calls(lambda i: hla.decode_step_mq(q1, k1g, v1g, mqa, out=o1), stream, 30)
+    total = B * (2 * sp + H * (2 * per_head + 2 * d + 4 * dv) + 2 * (d + dv))
+    res.append({"workload": "masked_hla_decode_multi_query_B256_H16_kv1_d128", "entry": "hla_decode_step_mq (kv_heads = 1)",
+                "us_per_call": us, "single_call_us": dict(_LAST_PCT), "states_per_s": N / (us * 1e-6), "bytes_per_call": total,
+                "roofline": roof(total, us)})
+    return res
 
 
 def secondary_small(dev, stream, only):

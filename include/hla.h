@@ -232,6 +232,54 @@ hla_status hla_decode_step(const hla_params *p, const void *q, const void *k,
                            const void *v, hla_state *state, float *out, float *den,
                            hipStream_t stream);
 
+/* The decode state with the key moment shared by groups of query heads and
+ * stored packed ([SUM] sec. 5.2: multi-query sharing reduces the state from
+ * O(h d^2) to O(d^2 + h d dv); packed symmetric storage of S cuts
+ * bandwidth).  For B batches, H query heads and kv_heads groups (H a
+ * multiple of kv_heads; group j holds query heads j*R .. j*R + R - 1,
+ * R = H / kv_heads), fp32 device arrays:
+ *   S   [B*kv_heads, d*(d+1)/2]  the group's key moment, packed: the 32 x 32
+ *       tiles (I, J), I <= J, in row-major tile order, an off-diagonal tile
+ *       whole (1024 floats, row-major), a diagonal tile as its upper
+ *       triangle (528 floats, row r holding columns r..31);
+ *   C, G [B*H, d, dv], m, h [B*H, d]  per query head, as in hla_state;
+ *   rho [B*kv_heads] or NULL. */
+typedef struct {
+    float *S;
+    float *C;
+    float *m;
+    float *G;
+    float *h;
+    float *rho;
+} hla_mq_state;
+
+/* One decode step ([SUM] sec. 1, 2 and 5.2) for query heads that share keys
+ * and values in groups (grouped / multi-query attention): the update and
+ * output of hla_decode_step for every query head, with one key moment S per
+ * group, read from and written to packed storage.
+ *   p          B, H (query heads), d in {32, 64, 128}, dv, dtype, gamma
+ *              (per query head, equal within a group), ridge, normalize;
+ *              n must be 1
+ *   q          [B,H,d];  k [B,kv_heads,d];  v [B,kv_heads,dv]  (p->dtype)
+ *   state      in/out, updated in place (hla_mq_state)
+ *   out        [B,H,dv] fp32;  den [B,H] fp32 or NULL
+ * With one query head per group (kv_heads = H) this is the unshared step on
+ * packed storage: each of S (packed), C, G read once and written once.
+ * With groups of several heads the group's S is read by each of its heads
+ * and then updated once. */
+hla_status hla_decode_step_mq(const hla_params *p, int32_t kv_heads, const void *q, const void *k,
+                              const void *v, hla_mq_state *state, float *out, float *den,
+                              hipStream_t stream);
+
+/* Converts `count` symmetric d x d key moments (d in {32, 64, 128}) between
+ * full storage ([count,d,d], as in hla_state) and the packed storage of
+ * hla_mq_state ([count, d*(d+1)/2]): pack reads the upper triangle of each
+ * full matrix; unpack writes both triangles.  src and dst must not overlap. */
+hla_status hla_key_moment_pack(int32_t count, int32_t d, const float *S_full, float *S_packed,
+                               hipStream_t stream);
+hla_status hla_key_moment_unpack(int32_t count, int32_t d, const float *S_packed, float *S_full,
+                                 hipStream_t stream);
+
 /* Masked semidirect-product composition of `count` segment pairs, earlier
  * segment a then later segment b ([SUM] sec. 4.2; [EXP] "Assoziative
  * Operatoren", cross term S_B C_A):

@@ -13,6 +13,8 @@ Functions (each follows the pages' identities; see ``hla_oracle.c``):
   optional ratio), Higher-order Linear Attention, paperlayer.ai page
   sec. 3.1 / 5.1 and gist.science page "Methodik" item 1.
 * :func:`decode` -- the same update for one new token per state.
+* :func:`decode_mq` -- the decode step when groups of query heads share keys
+  and values (and so the key moment): the per-head step with the group's k, v.
 * :func:`compose` -- the masked semidirect product of two segment summaries,
   paperlayer.ai page sec. 4.2 and gist.science page "Assoziative Operatoren".
 * :func:`oracle.backward.backward` (module ``backward.py``) -- gradients of
@@ -182,6 +184,29 @@ def decode(state: State, q, k, v, gamma=None, lam: float = 0.0,
                                int(threads))
     if rc != 0:
         raise ValueError("hla_oracle_decode: bad sizes")
+    return out, den, st
+
+
+def decode_mq(state: State, q, k, v, gamma=None, lam: float = 0.0, normalize: bool = False,
+              threads: Optional[int] = None):
+    """One token per query head when groups of query heads share keys and
+    values (paperlayer.ai summary sec. 5.2, multi-query sharing).  The key
+    moment S depends on the keys alone, so heads that share keys share it,
+    and each head's step is the ordinary one (:func:`decode`) with its
+    group's k and v.  q: [B,H,d]; k: [B,G,d]; v: [B,G,dv] with G dividing H
+    (group j = query heads j*R .. j*R+R-1, R = H/G); ``state`` holds one
+    full state per query head (S equal within a group).  Returns (out
+    [B,H,dv], den [B,H], new per-head State); S stays equal within a group."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, d = q.shape
+    G = k.shape[1]
+    assert H % G == 0 and k.shape == (B, G, d) and v.shape[:2] == (B, G)
+    R = H // G
+    kk = np.ascontiguousarray(np.repeat(k, R, axis=1))
+    vv = np.ascontiguousarray(np.repeat(v, R, axis=1))
+    out, den, st = decode(state, q, kk, vv, gamma=gamma, lam=lam, normalize=normalize, threads=threads)
+    S = st.S.reshape(B, G, R, d, d)
+    assert np.array_equal(S, np.broadcast_to(S[:, :, :1], S.shape)), "S differs within a group"
     return out, den, st
 
 
