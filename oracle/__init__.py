@@ -15,6 +15,8 @@ Functions (each follows the pages' identities; see ``hla_oracle.c``):
 * :func:`decode` -- the same update for one new token per state.
 * :func:`decode_mq` -- the decode step when groups of query heads share keys
   and values (and so the key moment): the per-head step with the group's k, v.
+* :mod:`oracle.higher` -- the asymmetric variant (AHLA) and third-order HLA
+  (``higher_oracle.c``): serial recurrences, one decode step, composition.
 * :func:`compose` -- the masked semidirect product of two segment summaries,
   paperlayer.ai page sec. 4.2 and gist.science page "Assoziative Operatoren".
 * :func:`oracle.backward.backward` (module ``backward.py``) -- gradients of
@@ -36,24 +38,29 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hla_oracle.c")
+_SRC_HIGHER = os.path.join(_HERE, "higher_oracle.c")
 _LIB = os.path.join(_HERE, "libhla_oracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (plain -O2, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < _src_mtime():
         tmp = _LIB + ".tmp"
         subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                        "-Wall", "-Wextra", "-o", tmp, _SRC], check=True)
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_HIGHER], check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def _src_mtime() -> float:
+    return max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_HIGHER))
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < _src_mtime():
             build(force=True)
         _lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)
@@ -67,6 +74,14 @@ def _load():
         _lib.hla_oracle_decode.restype = i
         _lib.hla_oracle_compose.argtypes = [i, i, i] + [dp] * 18
         _lib.hla_oracle_compose.restype = i
+        _lib.hla_oracle_ahla_forward.argtypes = [i, i, i, i, i, dp, dp, dp, dp, i] + [dp] * 5 + [dp, dp] + [dp] * 6 + [i]
+        _lib.hla_oracle_ahla_forward.restype = i
+        _lib.hla_oracle_ahla_compose.argtypes = [i, i, i] + [dp] * 18
+        _lib.hla_oracle_ahla_compose.restype = i
+        _lib.hla_oracle_ho3_forward.argtypes = [i, i, i, i, i, dp, dp, dp, i] + [dp] * 5 + [dp, dp] + [dp] * 9 + [i]
+        _lib.hla_oracle_ho3_forward.restype = i
+        _lib.hla_oracle_ho3_compose.argtypes = [i, i, i] + [dp] * 27
+        _lib.hla_oracle_ho3_compose.restype = i
     return _lib
 
 

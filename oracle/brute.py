@@ -113,3 +113,96 @@ def future_pairs(q, k, v, t: int, gamma: float = 1.0):
             G += c * np.outer(k[i], v[j])
             h += c * k[i]
     return G, h
+
+
+# ---------------------------------------------------------------------------
+# the asymmetric variant (AHLA) and third order, by their definitions
+#
+# AHLA (paperlayer.ai page sec. 6 and 6.1; gist.science page "Methodik" item
+# 2): the left-cascaded product Q (K^T Q)(K^T V) with the causal mask on
+# both factors, decay g per token of distance:
+#   num_t = sum_{j<=t} sum_{i<=j} g^(t-i) (q_t.k_j)(q_j.k_i) v_i
+# Third order (paperlayer.ai page sec. 7 and 7.1; gist.science page
+# "Methodik" item 3): A A^T A V with A = Q K^T, masked at every factor, no
+# decay:
+#   num_t = sum_{j<=t} sum_{i<=j} sum_{l<=j} (q_t.k_i)(k_i.q_j)(q_j.k_l) v_l
+# den_t: the same with every value equal to one.
+
+def ahla_exact(q, k, v, gamma=Fraction(1)):
+    """Exact-rational AHLA definition for one head (lists of Fractions/ints)."""
+    n, dv = len(q), len(v[0])
+    g = Fraction(gamma)
+
+    def dot(a, b):
+        return sum((Fraction(x) * Fraction(y) for x, y in zip(a, b)), Fraction(0))
+
+    num, den = [], []
+    for t in range(n):
+        row = [Fraction(0)] * dv
+        dn = Fraction(0)
+        for j in range(t + 1):
+            for i in range(j + 1):
+                w = _pow(g, t - i) * dot(q[t], k[j]) * dot(q[j], k[i])
+                for c in range(dv):
+                    row[c] += w * Fraction(v[i][c])
+                dn += w
+        num.append(row)
+        den.append(dn)
+    return num, den
+
+
+def ahla(q, k, v, gamma: float = 1.0):
+    """fp64 AHLA definition for one head: explicit loops over t, j, i."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    n = q.shape[0]
+    num = np.zeros((n, v.shape[1]))
+    den = np.zeros(n)
+    for t in range(n):
+        for j in range(t + 1):
+            a = float(q[t] @ k[j])
+            for i in range(j + 1):
+                w = _pow(gamma, t - i) * a * float(q[j] @ k[i])
+                num[t] += w * v[i]
+                den[t] += w
+    return num, den
+
+
+def third_exact(q, k, v):
+    """Exact-rational third-order definition for one head."""
+    n, dv = len(q), len(v[0])
+
+    def dot(a, b):
+        return sum((Fraction(x) * Fraction(y) for x, y in zip(a, b)), Fraction(0))
+
+    num, den = [], []
+    for t in range(n):
+        row = [Fraction(0)] * dv
+        dn = Fraction(0)
+        for j in range(t + 1):
+            for i in range(j + 1):
+                a = dot(q[t], k[i]) * dot(k[i], q[j])
+                for l in range(j + 1):
+                    w = a * dot(q[j], k[l])
+                    for c in range(dv):
+                        row[c] += w * Fraction(v[l][c])
+                    dn += w
+        num.append(row)
+        den.append(dn)
+    return num, den
+
+
+def third(q, k, v):
+    """fp64 third-order definition for one head: explicit loops over t, j, i, l."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    n = q.shape[0]
+    num = np.zeros((n, v.shape[1]))
+    den = np.zeros(n)
+    for t in range(n):
+        for j in range(t + 1):
+            for i in range(j + 1):
+                a = float(q[t] @ k[i]) * float(k[i] @ q[j])
+                for l in range(j + 1):
+                    w = a * float(q[j] @ k[l])
+                    num[t] += w * v[l]
+                    den[t] += w
+    return num, den
