@@ -77,7 +77,7 @@ def pristine_src():
 def _run_variant(tmp_path, src):
     pkg = tmp_path / "oracle"
     pkg.mkdir()
-    for name in ("__init__.py", "brute.py"):
+    for name in ("__init__.py", "brute.py", "higher.py", "higher_oracle.c"):
         shutil.copy(os.path.join(ROOT, "oracle", name), pkg / name)
     (pkg / "hla_oracle.c").write_text(src)
     (tmp_path / "checks.py").write_text(CHECKS)
