@@ -24,12 +24,17 @@ STATUS = {0: "HLA_OK", 1: "HLA_ERR_INVALID_ARGUMENT", 2: "HLA_ERR_UNSUPPORTED",
 EXPORTED = ("hla_forward_workspace_size", "hla_forward_chunked", "hla_forward_chunked_noalloc",
             "hla_backward_workspace_size", "hla_backward_chunked", "hla_decode_step", "hla_decode_step_mq",
             "hla_key_moment_pack", "hla_key_moment_unpack", "hla_state_compose", "hla_status_string",
-            "hla_last_error")
+            "hla_last_error", "hla_ahla_workspace_size", "hla_third_workspace_size", "hla_ahla_forward",
+            "hla_third_forward", "hla_ahla_decode_step", "hla_third_decode_step")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HLA_NOALLOC_SCRATCH_BYTES
 
 
 class CState(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in ("S", "C", "m", "G", "h", "rho")]
+
+
+class CHiState(ctypes.Structure):  # hla_ahla_state (P, m, E, n, rho) / hla_third_state (S, P, m, F, Fd)
+    _fields_ = [(name, ctypes.c_void_p) for name in ("a", "b", "c", "d", "e")]
 
 
 class CParams(ctypes.Structure):
@@ -79,6 +84,16 @@ def load(path: str = LIB_PATH):
         fn.restype = ctypes.c_int
     lib.hla_state_compose.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ps, ps, ps, vp]
     lib.hla_state_compose.restype = ctypes.c_int
+    for fn in (lib.hla_ahla_workspace_size, lib.hla_third_workspace_size):
+        fn.argtypes = [pp]
+        fn.restype = sz
+    p5 = ctypes.POINTER(CHiState)
+    for fn in (lib.hla_ahla_forward, lib.hla_third_forward):
+        fn.argtypes = [pp, vp, vp, vp, vp, vp, p5, p5, vp, sz, vp]
+        fn.restype = ctypes.c_int
+    for fn in (lib.hla_ahla_decode_step, lib.hla_third_decode_step):
+        fn.argtypes = [pp, vp, vp, vp, p5, vp, vp, vp]
+        fn.restype = ctypes.c_int
     lib.hla_status_string.argtypes = [ctypes.c_int]
     lib.hla_status_string.restype = ctypes.c_char_p
     lib.hla_last_error.argtypes = []
@@ -427,6 +442,143 @@ def decode_step_mq(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: MqS
                                 out.data_ptr(), den.data_ptr() if den is not None else None, _stream(q.device))
     _check(st)
     return out, den
+
+
+@dataclass
+class AhlaState:
+    """AHLA streaming summaries for B*H heads (fp32, device): P [N,d,dv],
+    m [N,d], E [N,d,dv], n [N,d], rho [N] or None."""
+    P: torch.Tensor
+    m: torch.Tensor
+    E: torch.Tensor
+    n: torch.Tensor
+    rho: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def empty(N, d, dv, device):
+        f = dict(dtype=torch.float32, device=device)
+        return AhlaState(torch.empty(N, d, dv, **f), torch.empty(N, d, **f), torch.empty(N, d, dv, **f),
+                         torch.empty(N, d, **f), torch.empty(N, **f))
+
+    def tensors(self):
+        return (self.P, self.m, self.E, self.n, self.rho)
+
+
+@dataclass
+class ThirdState:
+    """Third-order streaming state for B*H heads (fp32, device): S [N,d,d],
+    P [N,d,dv], m [N,d], F [N,d,dv], Fd [N,d]."""
+    S: torch.Tensor
+    P: torch.Tensor
+    m: torch.Tensor
+    F: torch.Tensor
+    Fd: torch.Tensor
+
+    @staticmethod
+    def empty(N, d, dv, device):
+        f = dict(dtype=torch.float32, device=device)
+        return ThirdState(torch.empty(N, d, d, **f), torch.empty(N, d, dv, **f), torch.empty(N, d, **f),
+                          torch.empty(N, d, dv, **f), torch.empty(N, d, **f))
+
+    def tensors(self):
+        return (self.S, self.P, self.m, self.F, self.Fd)
+
+
+def _hi_c(st):
+    if st is None:
+        return None
+    for t in st.tensors():
+        if t is not None:
+            _need(t, "state", (torch.float32,))
+    return CHiState(*[t.data_ptr() if t is not None else None for t in st.tensors()])
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (torch.bfloat16, torch.float32))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+
+
+def _higher_forward(third, q, k, v, gamma, normalize, chunk, init, return_state, return_den, out, den,
+                    workspace, final_state):
+    lib = load()
+    _check_qkv(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q,k [B,H,n,d] and v [B,H,n,dv]")
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    p, _keep = _params(B, H, n, d, dv, chunk, q.dtype, gamma, 0.0, normalize)
+    size_fn = lib.hla_third_workspace_size if third else lib.hla_ahla_workspace_size
+    need = int(size_fn(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty(B, H, n, dv, dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,))
+    if den is None and return_den:
+        den = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    if den is not None:
+        _need(den, "den", (torch.float32,))
+    cls = ThirdState if third else AhlaState
+    fin = final_state if final_state is not None else (cls.empty(B * H, d, dv, dev) if return_state else None)
+    ic, fc = _hi_c(init), _hi_c(fin)
+    fn = lib.hla_third_forward if third else lib.hla_ahla_forward
+    st = fn(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            den.data_ptr() if den is not None else None, ctypes.byref(ic) if ic is not None else None,
+            ctypes.byref(fc) if fc is not None else None, workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _stream(dev))
+    _check(st)
+    return out, den, fin
+
+
+def ahla_forward(q, k, v, *, gamma=None, normalize=False, chunk=0, init: Optional[AhlaState] = None,
+                 return_state=False, return_den=False, out=None, den=None, workspace=None,
+                 final_state: Optional[AhlaState] = None):
+    """The asymmetric variant (AHLA) through ``hla_ahla_forward``: q, k [B,H,n,d],
+    v [B,H,n,dv].  Returns (out, den or None, final AhlaState or None)."""
+    return _higher_forward(False, q, k, v, gamma, normalize, chunk, init, return_state, return_den, out, den,
+                           workspace, final_state)
+
+
+def third_forward(q, k, v, *, normalize=False, chunk=0, init: Optional[ThirdState] = None, return_state=False,
+                  return_den=False, out=None, den=None, workspace=None, final_state: Optional[ThirdState] = None):
+    """Masked third-order HLA through ``hla_third_forward`` (no decay).
+    Returns (out, den or None, final ThirdState or None)."""
+    return _higher_forward(True, q, k, v, None, normalize, chunk, init, return_state, return_den, out, den,
+                           workspace, final_state)
+
+
+def _higher_decode(third, q, k, v, state, gamma, normalize, return_den, out, den):
+    lib = load()
+    _check_qkv(q, k, v)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q,k [B,H,d] and v [B,H,dv]")
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    p, _keep = _params(B, H, 1, d, dv, 0, q.dtype, gamma, 0.0, normalize)
+    if out is None:
+        out = torch.empty(B, H, dv, dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,))
+    if den is None and return_den:
+        den = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    sc = _hi_c(state)
+    fn = lib.hla_third_decode_step if third else lib.hla_ahla_decode_step
+    _check(fn(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sc), out.data_ptr(),
+              den.data_ptr() if den is not None else None, _stream(q.device)))
+    return out, den
+
+
+def ahla_decode_step(q, k, v, state: AhlaState, *, gamma=None, normalize=False, return_den=False, out=None,
+                     den=None):
+    """One AHLA token per state (``hla_ahla_decode_step``); ``state`` updated in place."""
+    return _higher_decode(False, q, k, v, state, gamma, normalize, return_den, out, den)
+
+
+def third_decode_step(q, k, v, state: ThirdState, *, normalize=False, return_den=False, out=None, den=None):
+    """One third-order token per state (``hla_third_decode_step``); ``state`` updated in place."""
+    return _higher_decode(True, q, k, v, state, None, normalize, return_den, out, den)
 
 
 def state_compose(earlier: State, later: State, result: Optional[State] = None) -> State:

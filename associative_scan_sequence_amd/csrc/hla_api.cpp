@@ -538,6 +538,188 @@ hla_status hla_key_moment_unpack(int32_t count, int32_t d, const float *S_packed
     return pack_common(count, d, S_packed, S_full, false, stream);
 }
 
+// ---- AHLA and third order: shared validation and dispatch
+
+static hla_status higher_common(const hla_params *p, bool third, hla::GammaTab *gam) {
+    hla_status s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, gam);
+    if (s != HLA_OK) return s;
+    if (p->ridge != 0.0f) return fail(HLA_ERR_UNSUPPORTED, "ridge must be 0 for this operator");
+    if (third && p->gamma)
+        for (int h = 0; h < p->H; ++h)
+            if (p->gamma[h] != 1.0f)
+                return fail(HLA_ERR_UNSUPPORTED, "third order takes no decay (gamma[%d] = %g)", h, double(p->gamma[h]));
+    return HLA_OK;
+}
+
+static hla_status check_hi_state(const hla::HiState &st, bool third, const char *what) {
+    const float *ptrs[5] = {st.X1, st.v1, st.X2, st.v2, st.S};
+    const char *names[2][5] = {{"P", "m", "E", "n", "S"}, {"P", "m", "F", "Fd", "S"}};
+    for (int i = 0; i < (third ? 5 : 4); ++i) {
+        if (!ptrs[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s->%s is NULL", what, names[third][i]);
+        if (!aligned16(ptrs[i]))
+            return fail(HLA_ERR_ALIGNMENT, "%s->%s is not 16-byte aligned", what, names[third][i]);
+    }
+    if (st.rho && (reinterpret_cast<uintptr_t>(st.rho) & 3u))
+        return fail(HLA_ERR_ALIGNMENT, "%s->rho is not 4-byte aligned", what);
+    return HLA_OK;
+}
+
+static void hi_spans(const hla::HiState &st, bool third, const char *prefix, size_t N, int d, int dv,
+                     std::vector<Span> *out) {
+    const char *tags[6] = {"X1", "v1", "X2", "v2", "S", "rho"};
+    const float *ptrs[6] = {st.X1, st.v1, st.X2, st.v2, third ? st.S : nullptr, third ? nullptr : st.rho};
+    const size_t sizes[6] = {N * d * dv, N * d, N * d * dv, N * d, N * d * d, N};
+    for (int i = 0; i < 6; ++i)
+        if (ptrs[i]) out->push_back(span(std::string(prefix) + "." + tags[i], ptrs[i], sizes[i] * sizeof(float)));
+}
+
+static size_t higher_need(const hla_params *p, bool third) {
+    Geometry geo{};
+    if (forward_geometry(p, &geo) != HLA_OK || !width_ok(p->d) || !width_ok(p->dv)) return 0;
+    return hla::higher_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w, third);
+}
+
+static hla_status higher_forward_impl(const hla_params *p, bool third, const void *q, const void *k,
+                                      const void *v, float *out, float *den, const hla::HiState *init,
+                                      hla::HiState *fin, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    Geometry geo{};
+    hla_status s = forward_geometry(p, &geo);
+    if (s != HLA_OK) return s;
+    hla::HiProblem hp{};
+    if ((s = higher_common(p, third, &hp.gam)) != HLA_OK) return s;
+    const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
+    const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
+    if (n > 0) {
+        const void *req[4] = {q, k, v, out};
+        const char *nm[4] = {"q", "k", "v", "out"};
+        for (int i = 0; i < 4; ++i) {
+            if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
+            if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
+        }
+        if (den && !aligned16(den)) return fail(HLA_ERR_ALIGNMENT, "den is not 16-byte aligned");
+    }
+    if (init && (s = check_hi_state(*init, third, "init")) != HLA_OK) return s;
+    if (fin && (s = check_hi_state(*fin, third, "final_state")) != HLA_OK) return s;
+    const size_t need = hla::higher_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w, third);
+    if (need > 0) {
+        if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(HLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(HLA_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+    }
+    std::vector<Span> outs, ins;
+    if (n > 0) {
+        outs.push_back(span("out", out, BH * n * p->dv * 4));
+        if (den) outs.push_back(span("den", den, BH * n * 4));
+        ins.push_back(span("q", q, BH * n * p->d * esz));
+        ins.push_back(span("k", k, BH * n * p->d * esz));
+        ins.push_back(span("v", v, BH * n * p->dv * esz));
+    }
+    if (need > 0) outs.push_back(span("workspace", workspace, need));
+    if (fin) hi_spans(*fin, third, "final_state", BH, p->d, p->dv, &outs);
+    if (init) hi_spans(*init, third, "init", BH, p->d, p->dv, &ins);
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    if (n == 0 && !fin) return ok();
+    hp.B = p->B; hp.H = p->H; hp.n = p->n; hp.d = p->d; hp.dv = p->dv; hp.w = geo.w;
+    hp.dtype = p->dtype; hp.normalize = p->normalize; hp.third = third;
+    hp.q = q; hp.k = k; hp.v = v; hp.out = out; hp.den = den;
+    if (init) hp.init = *init;
+    if (fin) hp.fin = *fin;
+    hp.ws = workspace;
+    const hipError_t e = hla::higher_forward(hp, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "forward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+static hla_status higher_decode_impl(const hla_params *p, bool third, const void *q, const void *k,
+                                     const void *v, hla::HiState *state, float *out, float *den,
+                                     hipStream_t stream) {
+    if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (p->B < 1 || p->H < 1) return fail(HLA_ERR_INVALID_ARGUMENT, "B=%d, H=%d must be >= 1", p->B, p->H);
+    if (p->n != 1) return fail(HLA_ERR_INVALID_ARGUMENT, "decode needs n = 1 (got %d)", p->n);
+    hla::HiDecodeProblem dp{};
+    hla_status s = higher_common(p, third, &dp.gam);
+    if (s != HLA_OK) return s;
+    const uint64_t N = static_cast<uint64_t>(p->B) * p->H;
+    if (N > 0x7fffffffull / (128ull * 128ull))
+        return fail(HLA_ERR_UNSUPPORTED, "B*H=%llu too large", (unsigned long long)N);
+    const void *req[4] = {q, k, v, out};
+    const char *nm[4] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i) {
+        if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
+        if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
+    }
+    if (den && !aligned16(den)) return fail(HLA_ERR_ALIGNMENT, "den is not 16-byte aligned");
+    if ((s = check_hi_state(*state, third, "state")) != HLA_OK) return s;
+    const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
+    std::vector<Span> outs, ins;
+    outs.push_back(span("out", out, N * p->dv * 4));
+    if (den) outs.push_back(span("den", den, N * 4));
+    hi_spans(*state, third, "state", N, p->d, p->dv, &outs);
+    ins.push_back(span("q", q, N * p->d * esz));
+    ins.push_back(span("k", k, N * p->d * esz));
+    ins.push_back(span("v", v, N * p->dv * esz));
+    std::string detail;
+    if (first_overlap(outs, ins, &detail))
+        return fail(HLA_ERR_INVALID_ARGUMENT, "aliasing: %s", detail.c_str());
+    dp.B = p->B; dp.H = p->H; dp.d = p->d; dp.dv = p->dv; dp.dtype = p->dtype; dp.normalize = p->normalize;
+    dp.third = third; dp.q = q; dp.k = k; dp.v = v; dp.st = *state; dp.out = out; dp.den = den;
+    const hipError_t e = hla::higher_decode(dp, stream);
+    if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+static hla::HiState from_ahla(const hla_ahla_state *s) {
+    hla::HiState h{};
+    if (s) h = hla::HiState{nullptr, s->P, s->m, s->E, s->n, s->rho};
+    return h;
+}
+
+static hla::HiState from_third(const hla_third_state *s) {
+    hla::HiState h{};
+    if (s) h = hla::HiState{s->S, s->P, s->m, s->F, s->Fd, nullptr};
+    return h;
+}
+
+size_t hla_ahla_workspace_size(const hla_params *p) { return p ? higher_need(p, false) : 0; }
+size_t hla_third_workspace_size(const hla_params *p) { return p ? higher_need(p, true) : 0; }
+
+hla_status hla_ahla_forward(const hla_params *p, const void *q, const void *k, const void *v, float *out,
+                            float *den, const hla_ahla_state *init, hla_ahla_state *final_state,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");
+    hla::HiState i = from_ahla(init), f = from_ahla(final_state);
+    return higher_forward_impl(p, false, q, k, v, out, den, init ? &i : nullptr, final_state ? &f : nullptr,
+                               workspace, workspace_bytes, stream);
+}
+
+hla_status hla_third_forward(const hla_params *p, const void *q, const void *k, const void *v, float *out,
+                             float *den, const hla_third_state *init, hla_third_state *final_state,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!p) return fail(HLA_ERR_INVALID_ARGUMENT, "params is NULL");
+    hla::HiState i = from_third(init), f = from_third(final_state);
+    return higher_forward_impl(p, true, q, k, v, out, den, init ? &i : nullptr, final_state ? &f : nullptr,
+                               workspace, workspace_bytes, stream);
+}
+
+hla_status hla_ahla_decode_step(const hla_params *p, const void *q, const void *k, const void *v,
+                                hla_ahla_state *state, float *out, float *den, hipStream_t stream) {
+    if (!state) return fail(HLA_ERR_INVALID_ARGUMENT, "state is NULL");
+    hla::HiState s = from_ahla(state);
+    return higher_decode_impl(p, false, q, k, v, &s, out, den, stream);
+}
+
+hla_status hla_third_decode_step(const hla_params *p, const void *q, const void *k, const void *v,
+                                 hla_third_state *state, float *out, float *den, hipStream_t stream) {
+    if (!state) return fail(HLA_ERR_INVALID_ARGUMENT, "state is NULL");
+    hla::HiState s = from_third(state);
+    return higher_decode_impl(p, true, q, k, v, &s, out, den, stream);
+}
+
 hla_status hla_state_compose(int32_t count, int32_t d, int32_t dv, const hla_state *earlier,
                              const hla_state *later, hla_state *result, hipStream_t stream) {
     if (count < 0) return fail(HLA_ERR_INVALID_ARGUMENT, "count=%d must be >= 0", count);

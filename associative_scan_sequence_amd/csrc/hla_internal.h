@@ -140,6 +140,37 @@ hipError_t decode_step_mq(const DecodeMqProblem &p, hipStream_t s);
 // count symmetric d x d matrices: full -> packed (pack) or packed -> full
 hipError_t key_moment_pack(int count, int d, const float *src, float *dst, bool pack, hipStream_t s);
 
+// The asymmetric variant (AHLA) and third order (fwd_higher.hip,
+// decode_higher.hip).  A state: AHLA (X1, v1, X2, v2) = (P, m, E, n) and rho;
+// third order S and (X1, v1, X2, v2) = (P, m, F, Fd).
+struct HiState {
+    float *S, *X1, *v1, *X2, *v2, *rho;
+};
+struct HiProblem {
+    int B, H, n, d, dv, w;
+    hla_dtype dtype;
+    int normalize;
+    bool third;
+    const void *q, *k, *v;
+    float *out, *den;
+    HiState init, fin;  // init.X1 == nullptr: zero state; fin.X1 == nullptr: not returned
+    GammaTab gam;
+    void *ws;
+};
+size_t higher_workspace_bytes(int BH, int n, int d, int dv, int w, bool third);
+hipError_t higher_forward(const HiProblem &p, hipStream_t s);
+struct HiDecodeProblem {
+    int B, H, d, dv;
+    hla_dtype dtype;
+    int normalize;
+    bool third;
+    const void *q, *k, *v;
+    HiState st;
+    float *out, *den;
+    GammaTab gam;
+};
+hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
+
 hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,
                          const hla_state &r, hipStream_t s);
 

@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
-SECONDARY = ("ratio", "long", "decode", "decode_mq", "compose", "small", "state", "backward")
+SECONDARY = ("ratio", "long", "decode", "decode_mq", "compose", "small", "state", "backward", "ahla", "third")
 
 
 def parse():
@@ -285,7 +285,7 @@ def secondary_states(dev, stream, only):
     import hla_inputs as inputs
 
     res = []
-    if only in ("small", "state", "backward"):
+    if only in ("small", "state", "backward", "ahla", "third"):
         return res + secondary_small(dev, stream, only)
     # streaming decode: 4096 states seeded from a 512-token prefix
     w = inputs.DECODE_D128
@@ -353,8 +353,52 @@ def decode_mq_workloads(st, q1, k1, v1, w, stream):
     return res
 
 
+def higher_workloads(dev, stream, which):
+    """The asymmetric variant (AHLA, per-head decay g_h = 1 - 2^-(5+h)) and
+    masked third order at B4 H8 n2048 d = dv = 64 bf16, chunk 64: q, k, v in
+    and out, 640 algorithmic bytes per head-token; inputs rotated over copies
+    that exceed the Infinity Cache twice."""
+    import torch
+
+    import associative_scan_sequence_amd as hla
+    import hla_inputs as inputs
+
+    w = inputs.FWD_D64
+    tok = w.B * w.H * w.n
+    per_tok = 2 * (2 * w.d + w.dv) + 4 * w.dv
+    res = []
+    for name in which:
+        third = name == "third"
+        g = None if third else inputs.gamma_list_fp32([1 - 2.0 ** -(5 + h) for h in range(w.H)])
+        size_fn = hla._binding.load().hla_third_workspace_size if third else hla._binding.load().hla_ahla_workspace_size
+        p, _keep = hla._binding._params(w.B, w.H, w.n, w.d, w.dv, w.chunk, w.dtype, g, 0.0, False)
+        need = int(size_fn(hla._binding.ctypes.byref(p)))
+        copies = max(2, math.ceil(2 * MALL_BYTES / (tok * per_tok + need)))
+        sets = []
+        for c in range(copies):
+            q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5700 + c, dev)
+            sets.append((q, k, v, torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev),
+                         torch.empty(need, dtype=torch.uint8, device=dev)))
+
+        def call(i, third=third, g=g, sets=sets):
+            q, k, v, out, ws = sets[i % len(sets)]
+            if third:
+                hla.third_forward(q, k, v, chunk=w.chunk, out=out, workspace=ws)
+            else:
+                hla.ahla_forward(q, k, v, gamma=g, chunk=w.chunk, out=out, workspace=ws)
+        us = time_calls(call, stream, 20)
+        res.append({"workload": ("masked_third_order_fwd" if third else "ahla_fwd_decay") + "_B4_H8_n2048_d64_bf16_w64",
+                    "entry": "hla_third_forward" if third else "hla_ahla_forward", "us_per_call": us,
+                    "single_call_us": dict(_LAST_PCT), "tokens_per_s": w.B * w.n / (us * 1e-6),
+                    "roofline": roof(tok * per_tok, us)})
+        del sets
+    return res
+
+
 def secondary_small(dev, stream, only):
     res = []
+    if only in (None, "ahla", "third"):
+        res += higher_workloads(dev, stream, ("ahla", "third") if only is None else (only,))
     if only in (None, "small"):
         res += small_forward(dev, stream)
     if only in (None, "state"):

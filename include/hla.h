@@ -280,6 +280,72 @@ hla_status hla_key_moment_pack(int32_t count, int32_t d, const float *S_full, fl
 hla_status hla_key_moment_unpack(int32_t count, int32_t d, const float *S_packed, float *S_full,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * The asymmetric variant (AHLA) and third order.
+ *
+ * AHLA ([SUM] sec. 6, 6.1-6.3; [EXP] "Methodik" item 2): the masked
+ * left-cascaded product Q (K^T Q)(K^T V), per head with decay g:
+ *   num_t = sum_{j<=t} sum_{i<=j} g^(t-i) (q_t . k_j)(q_j . k_i) v_i
+ *   den_t = the same with every v_i = 1;   out_t = num_t or num_t / den_t
+ * Streaming summaries, each decayed by g per token:
+ *   P_t = g P + k v^T,  m_t = g m + k,  E_t = g E + k (P_t^T q)^T,
+ *   n_t = g n + (q . m_t) k;   num_t = E_t^T q_t,  den_t = q_t . n_t.
+ *
+ * Third order ([SUM] sec. 7, 7.1-7.3; [EXP] "Methodik" item 3): A A^T A V
+ * with A = Q K^T, masked at every factor, no decay (the pages state its scan
+ * for g = 1):
+ *   num_t = sum_{j<=t} sum_{i<=j} sum_{l<=j} (q_t . k_i)(k_i . q_j)(q_j . k_l) v_l
+ * Streaming state: S_t = S + k k^T, P_t = P + k v^T, m_t = m + k,
+ *   F_t = F + (S_t q)(P_t^T q)^T,  Fd_t = Fd + (q . m_t)(S_t q);
+ *   num_t = F_t^T q_t,  den_t = q_t . Fd_t.
+ *
+ * Both take hla_params with ridge = 0 (the pages define no ridge for them;
+ * HLA_ERR_UNSUPPORTED otherwise); third order takes gamma NULL or all 1.
+ * Arguments, layouts, aliasing rules and errors are those of
+ * hla_forward_chunked and hla_decode_step, with these states (fp32 device
+ * arrays, BH = B*H entries): */
+typedef struct {
+    float *P;    /* [BH,d,dv] */
+    float *m;    /* [BH,d]    */
+    float *E;    /* [BH,d,dv] */
+    float *n;    /* [BH,d]    */
+    float *rho;  /* [BH] or NULL: g^len of the covered segment (NULL read as 1) */
+} hla_ahla_state;
+
+typedef struct {
+    float *S;    /* [BH,d,d] (symmetric) */
+    float *P;    /* [BH,d,dv] */
+    float *m;    /* [BH,d]    */
+    float *F;    /* [BH,d,dv] */
+    float *Fd;   /* [BH,d]    */
+} hla_third_state;
+
+/* Workspace bytes of the AHLA / third-order forward (no initialisation
+ * needed; every call overwrites it); 0 for an invalid p. */
+size_t hla_ahla_workspace_size(const hla_params *p);
+size_t hla_third_workspace_size(const hla_params *p);
+
+/* Chunk-parallel forward (sec. 6.2 / 7.3: an exclusive scan of chunk
+ * summaries gives each chunk its carry-in, the result equals the serial
+ * recurrence up to fp32 rounding order).  init NULL = zero state;
+ * final_state NULL = not returned (AHLA rho = (init rho or 1) * g^n). */
+hla_status hla_ahla_forward(const hla_params *p, const void *q, const void *k, const void *v,
+                            float *out, float *den, const hla_ahla_state *init,
+                            hla_ahla_state *final_state, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+hla_status hla_third_forward(const hla_params *p, const void *q, const void *k, const void *v,
+                             float *out, float *den, const hla_third_state *init,
+                             hla_third_state *final_state, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* One streaming step per state (sec. 6.3 / 7.2), state updated in place;
+ * q, k [B,H,d], v [B,H,dv]; out [B,H,dv]; den [B,H] or NULL.  Each state
+ * matrix is read once and written once. */
+hla_status hla_ahla_decode_step(const hla_params *p, const void *q, const void *k, const void *v,
+                                hla_ahla_state *state, float *out, float *den, hipStream_t stream);
+hla_status hla_third_decode_step(const hla_params *p, const void *q, const void *k, const void *v,
+                                 hla_third_state *state, float *out, float *den, hipStream_t stream);
+
 /* Masked semidirect-product composition of `count` segment pairs, earlier
  * segment a then later segment b ([SUM] sec. 4.2; [EXP] "Assoziative
  * Operatoren", cross term S_B C_A):
