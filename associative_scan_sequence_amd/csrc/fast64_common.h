@@ -19,11 +19,13 @@ constexpr int kTileElems = W * W;  // one LDS tile: 64 rows of 64 bf16, see tile
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kSpinWord = 4;   // control word: spin limit of the bounded waits (0: kSpinLimit)
 constexpr int kLine = 64;      // words per 256-byte control line
-constexpr int kTabWord = 2 * kLine;  // XCD table: one 64-bit entry per workgroup from this word
-constexpr int kTabCap = static_cast<int>(kCtrlBytes / 8) - kTabWord / 2;
+constexpr int kTicketWord = kLine + 2;  // control word: next segment ticket (looped grids)
+constexpr int kHeadTicketWord = 2 * kLine;  // per-head segment tickets, 8 words apart (one-pass grids)
+constexpr int kHeadTicketStride = 8;
+constexpr int kMaxTicketHeads = (static_cast<int>(kCtrlBytes / 4) - kHeadTicketWord) / kHeadTicketStride;
 constexpr int kFlagStride = 32;  // words between flags (one 128-byte line each)
 constexpr float kMinGamma = 0.75f;
-static_assert(kCtrlBytes >= 2 * kLine * 4 + 256 * 8, "control block too small");
+static_assert(kCtrlBytes >= 2 * kLine * 4, "control block too small");
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -93,16 +95,12 @@ __device__ __forceinline__ float row_sum16(float v) {
 // Cross-workgroup hand-off without cache maintenance: aggregates and flags
 // are written and read as device-coherent (sc1) accesses, so no L2
 // write-back or invalidate is needed.  The writer waits for its stores to
-// complete (vmcnt 0) before the workgroup barrier that precedes the flag
-// store; readers poll the flag and only then load the aggregate.
+// complete (vmcnt 0) before the flag store; readers poll the flag and only
+// then load the aggregate.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e * 1664525u + 1013904223u; }
 
-// local: the writer and every reader run on one XCD, so its L2 is the point
-// of coherence and the flag is read where it lives, by an atomic (always
-// executed in L2, never served by a CU's L1).  Otherwise the flag is read
-// device-coherently.
 // The spin limit is kSpinLimit polls, or the control word *spin_word when it
 // is nonzero; the word is read only once the first poll has failed.
 __device__ __forceinline__ int spin_limit(const uint32_t *spin_word) {
@@ -110,31 +108,19 @@ __device__ __forceinline__ int spin_limit(const uint32_t *spin_word) {
     return s > 0 ? s : (s < 0 ? 1 : kSpinLimit);  // -1: give up after the first poll
 }
 
-__device__ bool wait_flag(uint32_t *f, uint32_t want, bool local, const uint32_t *spin_word) {
+__device__ bool wait_flag(uint32_t *f, uint32_t want, const uint32_t *spin_word) {
     int spin = kSpinLimit;
     for (int it = 0; it < spin; ++it) {
-        uint32_t v;
-        if (local) {
-            v = want;
-            __hip_atomic_compare_exchange_strong(f, &v, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-        } else {
-            v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (v == want) return true;
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
         if (it == 0) spin = spin_limit(spin_word);
         __builtin_amdgcn_s_sleep(1);
     }
     return false;
 }
 
-__device__ __forceinline__ void set_flag(uint32_t *f, uint32_t v, bool local) {
-    if (local) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    else __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void set_flag(uint32_t *f, uint32_t v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
-__device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu; }
 
 constexpr int kSc1 = 16;  // buffer cache policy: sc1 (device scope)
 
@@ -145,31 +131,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot) {
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(addr >> 32)));
     float *base = reinterpret_cast<float *>((static_cast<uint64_t>(hi) << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, 16384, 0x00020000);
-}
-
-// Decides, in wave 0, whether every workgroup that holds a segment of head
-// bh runs on this workgroup's XCD.  Segment s = i * BH + bh runs on
-// workgroup s mod grid; each workgroup wrote (epoch << 32) | 0x100 | XCD id
-// to xtab at its start.  tabv is the entry for i = lane, loaded earlier by
-// the caller (any value if lane >= P).  Every segment of the head reads the
-// same entries, so all of them reach the same answer.
-__device__ bool head_on_one_xcd(uint64_t *xtab, bool tab_ok, int P, int BH, int bh, uint32_t ep_now,
-                                uint64_t tabv, const uint32_t *spin_word) {
-    const int lane = static_cast<int>(threadIdx.x & 63);
-    const uint32_t me = 0x100u | xcd_id();
-    bool ok = tab_ok;
-    for (int i = lane; ok && i < P; i += 64) {
-        uint64_t *ent = xtab + (i * BH + bh) % static_cast<int>(gridDim.x);
-        uint64_t v = i == lane ? tabv : __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int spin = kSpinLimit;
-        for (int it = 0; static_cast<uint32_t>(v >> 32) != ep_now && it < spin; ++it) {
-            if (it == 0) spin = spin_limit(spin_word);
-            __builtin_amdgcn_s_sleep(1);
-            v = __hip_atomic_load(ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        ok = static_cast<uint32_t>(v >> 32) == ep_now && static_cast<uint32_t>(v) == me;
-    }
-    return __builtin_amdgcn_ballot_w64(!ok) == 0;
 }
 
 }  // namespace

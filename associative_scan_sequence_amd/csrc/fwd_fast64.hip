@@ -51,12 +51,14 @@
 //   round 2: X0 of every chunk -> T[8+2c], T[9+2c] (C0 -> T[c], T[4+c],
 //   y0 and m0 -> a vector area); out = num + e^2 Q X0 (+ the ridge and
 //   denominator terms)
-// Segment s = p * BH + head runs on workgroup s mod grid; the grid never
-// exceeds the CU count and a workgroup fills a CU, so every workgroup is
-// resident and waits only on smaller segments of its head, which are running
-// or done.  When every workgroup holding a segment of a head runs on one XCD
-// (checked at run time from the XCD table in the control block), aggregates
-// and flags go through that XCD's L2; otherwise they are device-coherent.
+// Segment s = p * BH + head.  When a head has several segments, workgroups
+// take segments from a ticket counter in increasing order, so a segment is
+// only ever held by a running workgroup and waits only on smaller segments of
+// its head, which were taken earlier by running workgroups that wait on
+// smaller ones still: every wait ends, whatever other streams keep resident.
+// Aggregates and flags are device-coherent (sc1) accesses.  A wait that still
+// gives up (spin limit, or forced from the host) makes the carry it waited
+// for NaN, so no output is ever a silently wrong number.
 #include "fast64_common.h"
 
 namespace hla {
@@ -78,8 +80,7 @@ struct FastArgs {
     const uint16_t *q, *k, *v;
     float *out, *den;  // den may be null
     float ridge;
-    int force_device;  // 1: device-coherent exchange even when a head's segments share an XCD
-    uint32_t *ctrl;   // control block (epoch, done counter, XCD table)
+    uint32_t *ctrl;   // control block (epoch, done counter, ticket, counters)
     uint32_t *flags;  // [BH * P][2 rounds][8 waves] at kFlagStride words: publication epoch
     float *aggS, *aggX, *aggC;  // [BH * P][16 tiles][64 lanes][4]
     float *aggV;                // [BH * P][kVecSlot]: y increment, then m increment
@@ -92,21 +93,16 @@ struct FastSmem {
 };
 
 // wave v's two tiles <-> a 16 KB slot: tile i at tile index 2v+i, lane l's
-// 16 bytes at byte ((2v+i) * 64 + l) * 16
-__device__ __forceinline__ void put_tiles(const float *slot, int v, int l, const f32x4 (&x)[2], bool local) {
+// 16 bytes at byte ((2v+i) * 64 + l) * 16 (device-coherent stores)
+__device__ __forceinline__ void put_tiles(const float *slot, int v, int l, const f32x4 (&x)[2]) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
-    if (local) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, 0);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
-    }
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
 }
 
 // acc += sum over n slots of scale[s] * (wave v's tiles of slot s); all
-// loads are issued before the first add
-template <int NB, int POL>
+// loads (device-coherent) are issued before the first add
+template <int NB>
 __device__ __forceinline__ void add_tiles(f32x4 (&acc)[2], const float *const (&slots)[NB],
                                           const float (&scale)[NB], int n, int v, int l) {
     f32x4 x[NB][2];
@@ -115,7 +111,7 @@ __device__ __forceinline__ void add_tiles(f32x4 (&acc)[2], const float *const (&
         if (s < n) {
             const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slots[s]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) x[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((2 * v + i) * 64 + l) * 16, 0, POL);
+            for (int i = 0; i < 2; ++i) x[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
         }
 #pragma unroll
     for (int s = 0; s < NB; ++s)
@@ -125,19 +121,15 @@ __device__ __forceinline__ void add_tiles(f32x4 (&acc)[2], const float *const (&
         }
 }
 
-// stores one float per lane into a published slot
-__device__ __forceinline__ void put_float(const float *slot, int idx, float x, bool local) {
+// one float per lane into / out of a published slot (device-coherent)
+__device__ __forceinline__ void put_float(const float *slot, int idx, float x) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
-    const uint32_t u = __float_as_uint(x);
-    if (local) __builtin_amdgcn_raw_buffer_store_b32(u, rs, 4 * idx, 0, 0);
-    else __builtin_amdgcn_raw_buffer_store_b32(u, rs, 4 * idx, 0, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, 4 * idx, 0, kSc1);
 }
 
-__device__ __forceinline__ float get_float(const float *slot, int idx, bool local) {
+__device__ __forceinline__ float get_float(const float *slot, int idx) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
-    const uint32_t u = local ? __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * idx, 0, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * idx, 0, kSc1);
-    return __uint_as_float(u);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * idx, 0, kSc1));
 }
 
 // RIDGE: lambda terms; DEN: the denominator (written to den when it is
@@ -158,8 +150,6 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     float lg = 0.0f;
     auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
     auto gpl = [&](float el) { return DECAY ? __builtin_amdgcn_exp2f(el) : 1.0f; };   // g^e from e log2(g)
-    uint64_t *const xtab = reinterpret_cast<uint64_t *>(a.ctrl + kTabWord);
-    const bool tab_ok = static_cast<int>(gridDim.x) <= kTabCap;
 
     auto seg_body = [&](const int seg) __attribute__((always_inline)) {
         // lane indices, laundered per pass in the looped launch so that the
@@ -237,10 +227,6 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         };
         issue_k(seg);
         if constexpr (RIDGE) issue_q(seg);
-        const bool first = seg == static_cast<int>(blockIdx.x);
-        if (tid == 0 && first && tab_ok)  // this workgroup's XCD, tagged with the launch epoch
-            __hip_atomic_store(xtab + blockIdx.x, (static_cast<uint64_t>(next_epoch(ep_raw)) << 32) | 0x100u | xcd_id(),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int bh = seg % a.BH, p = seg / a.BH;
         lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
         // Per-element decay exponents are formed as fma(constant, log2 g, lane base):
@@ -276,12 +262,6 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
             }
         __syncthreads();
-        if (first) epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))));
-        // XCD entries of the workgroups holding this head's segments (checked after phase A)
-        uint64_t tabv = 0;
-        if (l < a.P && tab_ok)
-            tabv = __hip_atomic_load(xtab + (l * a.BH + bh) % static_cast<int>(gridDim.x), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
 
         // ================= phase A (tiles): key moments ===========================
         // spre[c] = moment of chunks 0..c-1 at chunk c's start; srun ends as S_seg.
@@ -325,15 +305,11 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) srun[i] = rho * srun[i] + acc[i];
         }
-        // the exchange goes through the XCD's L2 when every workgroup holding
-        // a segment of this head runs on this XCD (every wave decides alike)
-        const bool local =
-            !a.force_device && head_on_one_xcd(xtab, tab_ok, a.P, a.BH, bh, epoch, tabv, a.ctrl + kSpinWord);
         auto flag_of = [&](size_t sl, int round) { return &a.flags[((sl * 2 + round) * kWaves + wave) * kFlagStride]; };
         if (publish) {
-            put_tiles(a.aggS + slot * 4096, wave, l, srun, local);
+            put_tiles(a.aggS + slot * 4096, wave, l, srun);
             wait_stores();
-            if (l == 0) set_flag(flag_of(slot, 0), epoch, local);
+            if (l == 0) set_flag(flag_of(slot, 0), epoch);
         }
         if constexpr (RIDGE) issue_v(seg);
         else issue_q(seg);
@@ -432,7 +408,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         auto wait_round = [&](int round) -> bool {
             bool failed = false;
             for (int pp = l; pp < p; pp += 64)
-                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, local, a.ctrl + kSpinWord)) {
+                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp, round), epoch, a.ctrl + kSpinWord)) {
                     __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     failed = true;
                 }
@@ -455,8 +431,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                     scale[s2] = gp(static_cast<float>(pw * (p - 1 - pp) * seg_tokens));
                 }
                 const int cnt = min(NB, p - p0);
-                if (local) add_tiles<NB, 0>(acc, slots, scale, cnt, wave, l);
-                else add_tiles<NB, kSc1>(acc, slots, scale, cnt, wave, l);
+                add_tiles<NB>(acc, slots, scale, cnt, wave, l);
             }
         };
         // the same for entries off + 16(cb+i) + r of the published vectors
@@ -469,7 +444,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 for (int s2 = 0; s2 < NB; ++s2) {
                     const float *vs = a.aggV + (static_cast<size_t>(bh) * a.P + min(p0 + s2, p - 1)) * kVecSlot;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) x[s2][i] = get_float(vs, off + 16 * (cb + i) + r, local);
+                    for (int i = 0; i < 2; ++i) x[s2][i] = get_float(vs, off + 16 * (cb + i) + r);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < NB; ++s2)
@@ -654,14 +629,14 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             }
         }
         if (publish) {
-            put_tiles(a.aggX + slot * 4096, wave, l, xrun, local);
-            if constexpr (RIDGE) put_tiles(a.aggC + slot * 4096, wave, l, crun, local);
+            put_tiles(a.aggX + slot * 4096, wave, l, xrun);
+            if constexpr (RIDGE) put_tiles(a.aggC + slot * 4096, wave, l, crun);
             if ((yw || mw) && l < 16) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) put_float(a.aggV + slot * kVecSlot, voff + 16 * (cb + i) + r, vrun[i][0], local);
+                for (int i = 0; i < 2; ++i) put_float(a.aggV + slot * kVecSlot, voff + 16 * (cb + i) + r, vrun[i][0]);
             }
             wait_stores();
-            if (l == 0) set_flag(flag_of(slot, 1), epoch, local);
+            if (l == 0) set_flag(flag_of(slot, 1), epoch);
         }
 
         // ================= P and the local numerator (slice) ======================
@@ -884,10 +859,40 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     };
     // A loop around the body costs registers even when it runs once, so the
     // one-segment launch calls the body straight.
-    if constexpr (LOOP) {
-        for (int seg = static_cast<int>(blockIdx.x); seg < a.segs; seg += static_cast<int>(gridDim.x)) seg_body(seg);
+    // The next segment: a ticket when segments wait on each other.  Thread 0
+    // takes it and hands it to the other waves through the last key tile,
+    // which is free at the start of every segment.  One-pass grid (one
+    // segment per workgroup): head b mod BH, its segment index p from that
+    // head's own counter (P workgroups per head contend for it; the one that
+    // takes the last index resets it).  Looped grid: one counter over all
+    // segments.  Either way a head's segments are taken in increasing order.
+    auto take = [&]() -> int {
+        int *slot = reinterpret_cast<int *>(sm.T[3]);
+        if (tid == 0) {
+            int t;
+            if constexpr (LOOP) {
+                t = static_cast<int>(
+                    __hip_atomic_fetch_add(&a.ctrl[kTicketWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            } else {
+                const int head = static_cast<int>(blockIdx.x) % a.BH;
+                uint32_t *cnt = &a.ctrl[kHeadTicketWord + kHeadTicketStride * head];
+                const int pp = static_cast<int>(__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                if (pp == a.P - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                t = pp * a.BH + head;
+            }
+            *slot = t;
+        }
+        __syncthreads();
+        const int t = __builtin_amdgcn_readfirstlane(*slot);
+        __syncthreads();  // every wave has read it before the tile is staged
+        return t;
+    };
+    const int seg0 = a.P > 1 ? take() : static_cast<int>(blockIdx.x);
+    epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))));
+    if constexpr (LOOP) {  // (with one segment per head nothing waits: a plain stride)
+        for (int seg = seg0; seg < a.segs; seg = a.P > 1 ? take() : seg + static_cast<int>(gridDim.x)) seg_body(seg);
     } else {
-        seg_body(static_cast<int>(blockIdx.x));
+        seg_body(seg0);
     }
 
     // ---- the last workgroup to finish resets the counter and advances the epoch
@@ -895,6 +900,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(&a.ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kTicketWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -972,7 +978,6 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     a.out = p.out;
     a.den = p.den;
     a.ridge = p.ridge;
-    a.force_device = exchange_forced_device() ? 1 : 0;
     a.ctrl = ctrl;
     const FastLayout L = fast_layout(a.BH, a.P);
     char *base = static_cast<char *>(data);
@@ -985,12 +990,12 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
-    // one workgroup per CU at most (its LDS fills the CU), so the whole grid is resident
+    // one workgroup per CU at most (its LDS fills the CU); segments by ticket when they wait on each other
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const bool loop = a.segs > cus;
+    const bool loop = a.segs > cus || (a.P > 1 && a.BH > kMaxTicketHeads);
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
     const bool ridge = p.ridge != 0.0f, norm = p.normalize != 0, den = norm || p.den != nullptr;
     if (decay) {

@@ -14,15 +14,6 @@
 
 #include "hla_internal.h"
 
-namespace hla {
-
-bool exchange_forced_device() {
-    const char *e = std::getenv("HLA_EXCHANGE");
-    return e != nullptr && std::strcmp(e, "device") == 0;
-}
-
-}  // namespace hla
-
 namespace {
 
 thread_local std::string g_last_error;

@@ -93,12 +93,6 @@ constexpr size_t kNoallocBytes = HLA_NOALLOC_SCRATCH_BYTES;
 // Records msg as this thread's last error (hla_last_error) and returns s.
 hla_status set_error(hla_status s, const char *msg);
 
-// True when the environment sets HLA_EXCHANGE=device: the one-launch d = 64
-// forward then hands aggregates between workgroups device-coherently even
-// when every segment of a head runs on one XCD (a diagnostic switch, read on
-// every call; the results are the same bits either way).
-bool exchange_forced_device();
-
 // One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
 // ridge, denominator and normalisation (no init or final state).
 bool fast64_supported(const FwdProblem &p);

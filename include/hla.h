@@ -102,23 +102,22 @@ typedef struct {
  * one-launch kernels, 3 = waits that hit the spin limit, 4 = that limit in
  * polls (0 = the built-in 4M; -1 = give up at once in the d = 128 kernel and
  * after one poll in the d = 64 kernel; the only word a caller may set, e.g.
- * to test the give-up path), 64 = finished-workgroup counter, 65 = launch epoch,
- * then a table of XCD ids): zero-fill the workspace once before its first
+ * to test the give-up path), 64 = finished-workgroup counter, 65 = launch
+ * epoch, 66 = segment ticket): zero-fill the workspace once before its first
  * use and write nothing else in it afterwards.  The rest holds per-chunk or
  * per-segment partial summaries.
  *
  * The one-launch kernels (bf16, d = dv = 64 or 128, no init or final state)
  * hand partial sums between workgroups of one launch when a head is cut into
  * several segments: a segment waits for the sums of the earlier segments of
- * its head.  The d = 128 kernel hands segments out by ticket, so a segment
- * only ever waits on segments that running workgroups hold, whatever other
- * streams run.  The d = 64 kernel assigns segment s to workgroup s mod grid
- * (grid <= CU count, one workgroup per CU), so its waits rely on the earlier
- * workgroups being dispatched; kernels that other streams run at the same
- * time can delay that.  A wait that exceeds a fixed spin limit (about 4M
- * polls, seconds) gives up and adds one to word 3, and the carry it waited
- * for is made NaN: every output that depends on it (that segment's and the
- * later segments' of the head) is then NaN, never a wrong number. */
+ * its head.  Both kernels then hand segments out by ticket, in increasing
+ * order, so a segment only ever waits on segments that running workgroups
+ * hold, whatever other streams run: every wait ends.  The sums travel as
+ * device-coherent accesses.  A wait that still exceeds a fixed spin limit
+ * (about 4M polls, seconds) gives up and adds one to word 3, and the carry
+ * it waited for is made NaN: every output that depends on it (that
+ * segment's and the later segments' of the head) is then NaN, never a wrong
+ * number. */
 size_t hla_forward_workspace_size(const hla_params *p);
 
 /* Chunk-parallel masked forward ([SUM] sec. 4 and 5: token deltas feed an
