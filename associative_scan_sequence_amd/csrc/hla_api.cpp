@@ -92,11 +92,22 @@ void state_spans(const hla_state *s, const char *prefix, size_t N, int d, int dv
         if (ptrs[i]) out->push_back(span(std::string(prefix) + "." + tags[i], ptrs[i], sizes[i] * sizeof(float)));
 }
 
-hla_status check_common(int H, int d, int dv, hla_dtype dtype, const float *gamma, float ridge,
+// The dtype field as the integer the caller stored: an out-of-range value is
+// read without ever holding it in the enum type.
+static_assert(sizeof(hla_dtype) == sizeof(int32_t), "hla_dtype is a 32-bit int in the C ABI");
+int dtype_code(const hla_params *p) {
+    int32_t x;
+    std::memcpy(&x, &p->dtype, sizeof(x));
+    return x;
+}
+
+bool dtype_ok(const hla_params *p) { return dtype_code(p) == HLA_F32 || dtype_code(p) == HLA_BF16; }
+
+hla_status check_common(int H, int d, int dv, int dtype, const float *gamma, float ridge,
                         int normalize, hla::GammaTab *tab) {
     if (!width_ok(d) || !width_ok(dv))
         return fail(HLA_ERR_UNSUPPORTED, "d=%d, dv=%d: each must be 16, 32, 64 or 128", d, dv);
-    if (dtype != HLA_F32 && dtype != HLA_BF16) return fail(HLA_ERR_INVALID_ARGUMENT, "bad dtype %d", int(dtype));
+    if (dtype != HLA_F32 && dtype != HLA_BF16) return fail(HLA_ERR_INVALID_ARGUMENT, "bad dtype %d", dtype);
     if (!std::isfinite(ridge) || ridge < 0.0f)
         return fail(HLA_ERR_INVALID_ARGUMENT, "ridge must be finite and >= 0");
     if (normalize != 0 && normalize != 1) return fail(HLA_ERR_INVALID_ARGUMENT, "normalize must be 0 or 1");
@@ -204,7 +215,7 @@ const char *hla_last_error(void) { return g_last_error.c_str(); }
 size_t hla_forward_workspace_size(const hla_params *p) {
     Geometry geo{};
     if (forward_geometry(p, &geo) != HLA_OK) return 0;
-    if (!width_ok(p->d) || !width_ok(p->dv)) return 0;
+    if (!width_ok(p->d) || !width_ok(p->dv) || !dtype_ok(p)) return 0;
     return workspace_need(p, geo, nullptr, nullptr, nullptr);
 }
 
@@ -214,6 +225,14 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
                                hipStream_t stream) {
     return hla::forward_impl(p, q, k, v, out, den, init, final_state, workspace, workspace_bytes, stream,
                              nullptr);
+}
+
+hla_status hla_forward_chunked_noalloc(const hla_params *p, const void *q, const void *k, const void *v,
+                                       float *out, float *den, const hla_state *init, hla_state *final_state,
+                                       hipStream_t stream) {
+    // validation first (host only); the static scratch (noalloc.hip) is looked up after it
+    return hla::forward_impl(p, q, k, v, out, den, init, final_state, nullptr, hla::kNoallocBytes, stream,
+                             "the library's static scratch");
 }
 
 }  // extern "C"
@@ -234,7 +253,7 @@ hla_status forward_impl(const hla_params *p, const void *q, const void *k, const
     hla_status s = forward_geometry(p, &geo);
     if (s != HLA_OK) return s;
     hla::FwdProblem fp{};
-    s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &fp.gam);
+    s = check_common(p->H, p->d, p->dv, dtype_code(p), p->gamma, p->ridge, p->normalize, &fp.gam);
     if (s != HLA_OK) return s;
     const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
     const size_t esz = p->dtype == HLA_BF16 ? 2 : 4;
@@ -313,7 +332,7 @@ extern "C" {
 size_t hla_backward_workspace_size(const hla_params *p) {
     Geometry geo{};
     if (forward_geometry(p, &geo) != HLA_OK) return 0;
-    if (!width_ok(p->d) || !width_ok(p->dv)) return 0;
+    if (!width_ok(p->d) || !width_ok(p->dv) || !dtype_ok(p)) return 0;
     if (p->n == 0) return 0;
     return hla::generic_backward_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w);
 }
@@ -327,7 +346,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     if (s != HLA_OK) return s;
     hla::BwdProblem bp{};
     hla::FwdProblem &fp = bp.f;
-    s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &fp.gam);
+    s = check_common(p->H, p->d, p->dv, dtype_code(p), p->gamma, p->ridge, p->normalize, &fp.gam);
     if (s != HLA_OK) return s;
     const size_t BH = static_cast<size_t>(p->B) * p->H, n = static_cast<size_t>(p->n);
     if (init && (s = check_state(init, "init")) != HLA_OK) return s;
@@ -409,7 +428,7 @@ hla_status hla_decode_step(const hla_params *p, const void *q, const void *k, co
     if (p->B < 1 || p->H < 1) return fail(HLA_ERR_INVALID_ARGUMENT, "B=%d, H=%d must be >= 1", p->B, p->H);
     if (p->n != 1) return fail(HLA_ERR_INVALID_ARGUMENT, "decode needs n = 1 (got %d)", p->n);
     hla::DecodeProblem dp{};
-    hla_status s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &dp.gam);
+    hla_status s = check_common(p->H, p->d, p->dv, dtype_code(p), p->gamma, p->ridge, p->normalize, &dp.gam);
     if (s != HLA_OK) return s;
     const uint64_t N = static_cast<uint64_t>(p->B) * p->H;
     if (N > 0x7fffffffull / (128ull * 128ull))
@@ -453,7 +472,7 @@ hla_status hla_decode_step_mq(const hla_params *p, int32_t kv_heads, const void 
     if (p->d != 32 && p->d != 64 && p->d != 128)
         return fail(HLA_ERR_UNSUPPORTED, "d=%d: the packed key moment needs d = 32, 64 or 128", p->d);
     hla::DecodeMqProblem dp{};
-    hla_status s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, &dp.gam);
+    hla_status s = check_common(p->H, p->d, p->dv, dtype_code(p), p->gamma, p->ridge, p->normalize, &dp.gam);
     if (s != HLA_OK) return s;
     const int R = p->H / kv_heads;
     if (p->gamma) {  // one decay per group: the group's S is decayed once
@@ -532,7 +551,7 @@ hla_status hla_key_moment_unpack(int32_t count, int32_t d, const float *S_packed
 // ---- AHLA and third order: shared validation and dispatch
 
 static hla_status higher_common(const hla_params *p, bool third, hla::GammaTab *gam) {
-    hla_status s = check_common(p->H, p->d, p->dv, p->dtype, p->gamma, p->ridge, p->normalize, gam);
+    hla_status s = check_common(p->H, p->d, p->dv, dtype_code(p), p->gamma, p->ridge, p->normalize, gam);
     if (s != HLA_OK) return s;
     if (p->ridge != 0.0f) return fail(HLA_ERR_UNSUPPORTED, "ridge must be 0 for this operator");
     if (third && p->gamma)
@@ -557,7 +576,7 @@ static hla_status check_hi_state(const hla::HiState &st, bool third, const char 
 
 static void hi_spans(const hla::HiState &st, bool third, const char *prefix, size_t N, int d, int dv,
                      std::vector<Span> *out) {
-    const char *tags[6] = {"X1", "v1", "X2", "v2", "S", "rho"};
+    const char *tags[6] = {"P", "m", third ? "F" : "E", third ? "Fd" : "n", "S", "rho"};  // the header's names
     const float *ptrs[6] = {st.X1, st.v1, st.X2, st.v2, third ? st.S : nullptr, third ? nullptr : st.rho};
     const size_t sizes[6] = {N * d * dv, N * d, N * d * dv, N * d, N * d * d, N};
     for (int i = 0; i < 6; ++i)
@@ -566,7 +585,7 @@ static void hi_spans(const hla::HiState &st, bool third, const char *prefix, siz
 
 static size_t higher_need(const hla_params *p, bool third) {
     Geometry geo{};
-    if (forward_geometry(p, &geo) != HLA_OK || !width_ok(p->d) || !width_ok(p->dv)) return 0;
+    if (forward_geometry(p, &geo) != HLA_OK || !width_ok(p->d) || !width_ok(p->dv) || !dtype_ok(p)) return 0;
     return hla::higher_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w, third);
 }
 

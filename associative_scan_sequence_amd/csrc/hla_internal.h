@@ -40,8 +40,8 @@ struct FwdProblem {
 
 // Every forward workspace starts with a control block of kCtrlBytes: words
 // that the one-launch kernels keep valid across calls (a finished-workgroup
-// counter and the launch epoch, a launch count and a wait-timeout count, and
-// a table of epoch-tagged XCD ids, one per workgroup of the last launch).
+// counter and the launch epoch, a launch count, a wait give-up count and the
+// spin limit, and the segment tickets: one over all segments, one per head).
 // It must be zero before the first call; no kernel writes it except through
 // those words.  Path data follows it.
 constexpr size_t kCtrlBytes = 8192;

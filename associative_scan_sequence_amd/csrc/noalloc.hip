@@ -1,7 +1,8 @@
-// noalloc.hip -- hla_forward_chunked_noalloc: the chunked forward with its
-// workspace in a static device array instead of a caller's buffer, for
-// callers that cannot allocate device memory (code under HIP graph capture,
-// tight serving loops, harnesses that forbid hipMalloc).
+// noalloc.hip -- the static device array behind hla_forward_chunked_noalloc
+// (hla_api.cpp): the chunked forward with its workspace in this array instead
+// of a caller's buffer, for callers that cannot allocate device memory (code
+// under HIP graph capture, tight serving loops, harnesses that forbid
+// hipMalloc).
 //
 // The array `scratch` below is file-scope device storage: each GPU the
 // library runs on holds its own copy, at its own address, from the first
@@ -11,8 +12,8 @@
 // and is the only form in which the array reaches the kernels.
 //
 // Contents.  The first kCtrlBytes are the forward's control block (a
-// finished-workgroup counter, the launch epoch, a segment ticket, counters
-// and the XCD table of the one-launch kernels).  It must be zero before the
+// finished-workgroup counter, the launch epoch, segment tickets and counters
+// of the one-launch kernels).  It must be zero before the
 // first launch; static storage is zero-initialised when the code object is
 // loaded, and every launch leaves the block valid for the next, so nothing is
 // cleared here (clearing it again would restart the launch epochs, and a
@@ -56,12 +57,3 @@ hla_status noalloc_scratch(void **out) {
 }
 
 }  // namespace hla
-
-extern "C" hla_status hla_forward_chunked_noalloc(const hla_params *p, const void *q, const void *k,
-                                                  const void *v, float *out, float *den,
-                                                  const hla_state *init, hla_state *final_state,
-                                                  hipStream_t stream) {
-    // validation first (host only); the scratch address is looked up after it
-    return hla::forward_impl(p, q, k, v, out, den, init, final_state, nullptr, hla::kNoallocBytes, stream,
-                             "the library's static scratch");
-}

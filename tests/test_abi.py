@@ -9,7 +9,7 @@ import subprocess
 import pytest
 
 import associative_scan_sequence_amd as hla
-from associative_scan_sequence_amd._binding import CParams, CState
+from associative_scan_sequence_amd._binding import CHiState, CParams, CState
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hla.h")
@@ -313,3 +313,106 @@ def test_noalloc_validates_before_any_device_call(lib):
     p = params(B=4, H=8, n=2048, d=64, dv=64, chunk=64)
     assert call(p, fin=fin) == WORKSPACE
     assert "static scratch" in last(lib) and str(hla._binding.NOALLOC_SCRATCH_BYTES) in last(lib)
+
+
+def mq(lib, p, kv_heads, state, q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None):
+    return lib.hla_decode_step_mq(ctypes.byref(p), kv_heads, q, k, v,
+                                  ctypes.byref(state) if state is not None else None, out, den, None)
+
+
+def test_decode_mq_rejects_bad_arguments(lib):
+    st = CState(addr(7), addr(8), addr(9), addr(10), addr(11), addr(12))
+    p = params(B=2, H=4, n=1, d=64, dv=64)
+    assert mq(lib, p, 3, st) == INVALID and "divide H=4" in last(lib)
+    assert mq(lib, p, 0, st) == INVALID and "kv_heads=0" in last(lib)
+    assert mq(lib, params(B=2, H=4, n=1, d=16, dv=64), 2, st) == UNSUPPORTED and "packed" in last(lib)
+    assert mq(lib, params(B=2, H=4, n=2, d=64, dv=64), 2, st) == INVALID and "n = 1" in last(lib)
+    # one decay per group of heads that share a key moment
+    g = (ctypes.c_float * 4)(0.9, 0.8, 0.7, 0.7)
+    pg = params(B=2, H=4, n=1, d=64, dv=64, gamma=ctypes.cast(g, ctypes.POINTER(ctypes.c_float)))
+    assert mq(lib, pg, 2, st) == INVALID and "gamma[1]" in last(lib)
+    assert mq(lib, p, 2, None) == INVALID and "state is NULL" in last(lib)
+    assert mq(lib, p, 2, st, q=None) == INVALID and "q is NULL" in last(lib)
+    assert mq(lib, p, 2, st, k=addr(2) + 4) == ALIGN and "k is not" in last(lib)
+    assert mq(lib, p, 2, CState(addr(7), addr(8), None, addr(10), addr(11), None)) == INVALID
+    # out written over the (packed, per-group) key moment
+    assert mq(lib, p, 2, st, out=addr(7) + 1024) == INVALID and "overlaps" in last(lib)
+
+
+def test_key_moment_pack_rejects_bad_arguments(lib):
+    for fn in (lib.hla_key_moment_pack, lib.hla_key_moment_unpack):
+        assert fn(-1, 64, addr(1), addr(2), None) == INVALID
+        assert fn(4, 48, addr(1), addr(2), None) == UNSUPPORTED and "d=48" in last(lib)
+        assert fn(0, 64, None, None, None) == OK  # nothing to do
+        assert fn(4, 64, None, addr(2), None) == INVALID and "NULL" in last(lib)
+        assert fn(4, 64, addr(1) + 8, addr(2), None) == ALIGN
+        assert fn(4, 64, addr(1), addr(1) + 4096, None) == INVALID and "aliasing" in last(lib)
+        assert fn(1 << 20, 128, addr(1), addr(2), None) == UNSUPPORTED and "too large" in last(lib)
+
+
+def hi_fwd(lib, fn, size_fn, p, q=addr(1), k=addr(2), v=addr(3), out=addr(4), den=None, init=None,
+           fin=None, ws=None, ws_bytes=None):
+    need = size_fn(ctypes.byref(p))
+    return fn(ctypes.byref(p), q, k, v, out, den, ctypes.byref(init) if init is not None else None,
+              ctypes.byref(fin) if fin is not None else None, addr(5) if ws is None else ws,
+              need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("third", [False, True])
+def test_ahla_and_third_forward_reject_bad_arguments(lib, third):
+    fn = lib.hla_third_forward if third else lib.hla_ahla_forward
+    size_fn = lib.hla_third_workspace_size if third else lib.hla_ahla_workspace_size
+    call = lambda p, **kw: hi_fwd(lib, fn, size_fn, p, **kw)  # noqa: E731
+    p = params(n=200, d=64, dv=64)
+    assert size_fn(ctypes.byref(p)) > 0
+    assert size_fn(None) == 0 and size_fn(ctypes.byref(params(d=48))) == 0
+    assert size_fn(ctypes.byref(params(dtype=7))) == 0
+    assert fn(None, addr(1), addr(2), addr(3), addr(4), None, None, None, addr(5), 1 << 30, None) == INVALID
+    assert call(params(B=0)) == INVALID and "B=" in last(lib)
+    assert call(params(dtype=7)) == INVALID and "dtype" in last(lib)
+    assert call(params(d=48)) == UNSUPPORTED
+    # neither operator has a ridge term
+    assert call(params(ridge=0.5)) == UNSUPPORTED and "ridge" in last(lib)
+    g = (ctypes.c_float * 3)(1.0, 0.9, 1.0)
+    pg = params(gamma=ctypes.cast(g, ctypes.POINTER(ctypes.c_float)))
+    if third:  # masked third order here is the undecayed operator
+        assert call(pg) == UNSUPPORTED and "gamma[1]" in last(lib)
+    else:
+        assert call(pg, ws_bytes=0) == WORKSPACE  # a decay is fine for AHLA: the next check fires
+    assert call(p, q=None) == INVALID and "q is NULL" in last(lib)
+    assert call(p, v=addr(3) + 4) == ALIGN and "v is not" in last(lib)
+    need = size_fn(ctypes.byref(p))
+    assert call(p, ws_bytes=need - 1) == WORKSPACE
+    assert call(p, ws=addr(5) + 16) == ALIGN and "workspace" in last(lib)
+    assert call(p, out=addr(2) + 256) == INVALID and "out overlaps k" in last(lib)
+    # field order: hla_third_state (S, P, m, F, Fd), hla_ahla_state (P, m, E, n, rho)
+    names = ("S", "P", "m", "F", "Fd") if third else ("P", "m", "E", "n", "rho")
+    full = CHiState(addr(7), addr(8), addr(9), addr(10), addr(11))
+    gap = CHiState(addr(7), None, addr(9), addr(10), addr(11))
+    assert call(p, init=gap) == INVALID and f"init->{names[1]} is NULL" in last(lib)
+    mis = CHiState(addr(7), addr(8), addr(9) + 4, addr(10), addr(11))
+    assert call(p, fin=mis) == ALIGN and f"final_state->{names[2]}" in last(lib)
+    # a final-state array written over an init array; the message uses the header's names
+    fin = CHiState(addr(12), addr(13), addr(14), addr(10), addr(15))
+    assert call(p, init=full, fin=fin) == INVALID
+    assert f"final_state.{names[3]} overlaps init.{names[3]}" in last(lib)
+    # nothing to do: no tokens and no final state
+    assert call(params(n=0), q=None, k=None, v=None, out=None, ws=None) == OK
+
+
+@pytest.mark.parametrize("third", [False, True])
+def test_ahla_and_third_decode_reject_bad_arguments(lib, third):
+    fn = lib.hla_third_decode_step if third else lib.hla_ahla_decode_step
+    st = CHiState(addr(7), addr(8), addr(9), addr(10), addr(11))
+    call = lambda p, state=st, q=addr(1), out=addr(4): fn(  # noqa: E731
+        ctypes.byref(p) if p is not None else None, q, addr(2), addr(3),
+        ctypes.byref(state) if state is not None else None, out, None, None)
+    assert call(params(n=1), state=None) == INVALID and "state is NULL" in last(lib)
+    assert call(None) == INVALID and "params is NULL" in last(lib)
+    assert call(params(n=2)) == INVALID and "n = 1" in last(lib)
+    assert call(params(n=1, ridge=1.0)) == UNSUPPORTED
+    assert call(params(n=1), q=None) == INVALID and "q is NULL" in last(lib)
+    assert call(params(n=1), q=addr(1) + 2) == ALIGN
+    hole = CHiState(addr(7), addr(8), addr(9), None, addr(11))
+    assert call(params(n=1), state=hole) == INVALID and "is NULL" in last(lib)
+    assert call(params(n=1), out=addr(8)) == INVALID and "overlaps" in last(lib)
