@@ -85,6 +85,12 @@ struct FastArgs {
     float *aggS, *aggX, *aggC;  // [BH * P][16 tiles][64 lanes][4]
     float *aggV;                // [BH * P][kVecSlot]: y increment, then m increment
     GammaTab gam;
+    // STATE variants only:
+    const float *iagg;   // [BH][3][4096] the initial state's S, X = S C - G and C in the slot
+                         // layout of the aggregates, or null (zero initial state)
+    const float *iaggV;  // [BH][kVecSlot] its y = S m - h, then m
+    const float *irho;   // initial rho [BH] or null (read as 1)
+    hla_state fin;       // final state; fin.S null: not requested
 };
 
 template <int NT>
@@ -133,10 +139,15 @@ __device__ __forceinline__ float get_float(const float *slot, int idx) {
 }
 
 // RIDGE: lambda terms; DEN: the denominator (written to den when it is
-// given); NORM: out = num / den.
-template <bool DECAY, bool LOOP, bool RIDGE, bool DEN, bool NORM>
+// given); NORM: out = num / den.  STATE: an initial state enters every carry
+// (a.iagg, prepared by k_fast64_init), and a final state is formed when
+// a.fin.S is set.  A state has all of S, C, m, G, h, so the STATE variants
+// carry C, m and y as the ridge and denominator variants do (with lambda = 0
+// when no ridge is asked for).
+template <bool DECAY, bool LOOP, bool RIDGE, bool DEN, bool NORM, bool STATE>
 __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     static_assert(!NORM || DEN, "the ratio needs the denominator");
+    static_assert(!STATE || (RIDGE && DEN), "a state carries C, m and y");
     constexpr bool MV = RIDGE && DEN;  // the query mass m only enters the ridge part of den
     __shared__ FastSmem<RIDGE ? 20 : 16> sm;
     const int tid = threadIdx.x;
@@ -251,7 +262,10 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
         for (int c = 0; c < kFMaxL; ++c) lcc[c] = c < Lseg ? chunk_len(c) : 0;
         const size_t slot = static_cast<size_t>(bh) * a.P + p;
-        const bool publish = p + 1 < a.P;  // the last segment of a head has no readers
+        // the last segment of a head has no readers, unless a final state is formed from it
+        const bool want_fin = STATE && a.fin.S != nullptr;
+        const bool publish = p + 1 < a.P || want_fin;
+        const bool fin_seg = want_fin && p + 1 == a.P;  // this workgroup writes the head's final state
 
         // ---- stage key rows
 #pragma unroll
@@ -418,7 +432,9 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             const float nan = __builtin_nanf("");
             acc[0] = acc[1] = f32x4{nan, nan, nan, nan};
         };
-        auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int pw) {
+        // (STATE: plus the initial state's part `kind` (0 S, 1 X, 2 C), decayed
+        // over the p * seg_tokens tokens before the segment)
+        auto carry_tiles = [&](f32x4 (&acc)[2], const float *agg, int pw, int kind) {
             constexpr int NB = 8;
             acc[0] = acc[1] = zero4;
             for (int p0 = 0; p0 < p; p0 += NB) {
@@ -433,6 +449,14 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 const int cnt = min(NB, p - p0);
                 add_tiles<NB>(acc, slots, scale, cnt, wave, l);
             }
+            if constexpr (STATE) {
+                if (a.iagg != nullptr) {
+                    const float *slots[1] = {a.iagg + (static_cast<size_t>(bh) * 3 + kind) * 4096};
+                    const float scale[1] = {gp(static_cast<float>(pw * p * seg_tokens))};
+                    add_tiles<1>(acc, slots, scale, 1, wave, l);
+                }
+            }
+            (void)kind;
         };
         // the same for entries off + 16(cb+i) + r of the published vectors
         auto carry_vec = [&](float (&acc)[2], int off, int pw) {
@@ -454,14 +478,44 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                         for (int i = 0; i < 2; ++i) acc[i] += sc2 * x[s2][i];
                     }
             }
+            if constexpr (STATE) {
+                if (a.iaggV != nullptr) {
+                    const float *vs = a.iaggV + static_cast<size_t>(bh) * kVecSlot;
+                    const float sc2 = gp(static_cast<float>(pw * p * seg_tokens));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) acc[i] += sc2 * get_float(vs, off + 16 * (cb + i) + r);
+                }
+            }
+        };
+        // STATE, the head's last segment: the state at the end of the sequence,
+        // g^(pw len) * carry + this segment's own published aggregate (len = the
+        // segment's tokens), in this wave's tile layout
+        auto fin_tiles = [&](f32x4 (&x)[2], const f32x4 (&carry)[2], const float *agg, int pw) {
+            const float *slots[1] = {agg + slot * 4096};
+            const float scale[1] = {1.0f};
+            const float dl = gp(static_cast<float>(pw * (a.n - p * seg_tokens)));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) x[i] = dl * carry[i];
+            add_tiles<1>(x, slots, scale, 1, wave, l);
         };
 
         // ================= round 1: S0 of every chunk -> LDS ========================
         {
             f32x4 s0seg[2];
             const bool bad = wait_round(0);
-            carry_tiles(s0seg, a.aggS, 1);
+            carry_tiles(s0seg, a.aggS, 1, 0);
             if (bad) poison(s0seg);
+            if constexpr (STATE) {
+                if (fin_seg) {  // final S[a = 16tb+4g+e][b = 16(cb+i)+r]
+                    f32x4 sf[2];
+                    fin_tiles(sf, s0seg, a.aggS, 1);
+                    float *S = a.fin.S + static_cast<size_t>(bh) * W * W;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[(16 * tb + 4 * g + e) * W + 16 * (cb + i) + r] = sf[i][e];
+                }
+            }
             // With the denominator, S0 takes a third term (in the key tile: no
             // key is read after the carry-free stage).  The ratio amplifies the
             // absolute error of den where |den| is small, and a two-term S0 in U
@@ -728,13 +782,40 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         f32x4 x0seg[2], c0seg[2];
         float v0seg[2];
         const bool bad2 = wait_round(1);
-        carry_tiles(x0seg, a.aggX, 2);
-        if constexpr (RIDGE) carry_tiles(c0seg, a.aggC, 1);
+        carry_tiles(x0seg, a.aggX, 2, 1);
+        if constexpr (RIDGE) carry_tiles(c0seg, a.aggC, 1, 2);
         if (yw || mw) carry_vec(v0seg, voff, yw ? 2 : 1);
         if (bad2) {
             poison(x0seg);
             if constexpr (RIDGE) poison(c0seg);
             v0seg[0] = v0seg[1] = __builtin_nanf("");
+        }
+        if constexpr (STATE) {
+            // final X (into fin.G, which the finish step below turns into G =
+            // S C - X) and C at [a = 16(cb+i)+r][j = 16tb+4g+e]; final y (into
+            // fin.h, likewise) and m
+            if (fin_seg) {
+                f32x4 xf[2], cf[2];
+                fin_tiles(xf, x0seg, a.aggX, 2);
+                fin_tiles(cf, c0seg, a.aggC, 1);
+                const size_t mo = static_cast<size_t>(bh) * W * W;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const size_t at = mo + static_cast<size_t>(16 * (cb + i) + r) * W + 16 * tb + 4 * g + e;
+                        a.fin.G[at] = xf[i][e];
+                        a.fin.C[at] = cf[i][e];
+                    }
+                if ((yw || mw) && l < 16) {
+                    const float *own = a.aggV + slot * kVecSlot;
+                    const float dl = gp(static_cast<float>((yw ? 2 : 1) * (a.n - p * seg_tokens)));
+                    float *dst = (yw ? a.fin.h : a.fin.m) + static_cast<size_t>(bh) * W;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        dst[16 * (cb + i) + r] = dl * v0seg[i] + get_float(own, voff + 16 * (cb + i) + r);
+                }
+            }
         }
         float *const vec = reinterpret_cast<float *>(sm.T[RIDGE ? 16 : 0]);
         __syncthreads();  // every Us, value and query read done: the tiles take X0 (C0, vectors)
@@ -856,6 +937,64 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             }
         }
         __syncthreads();  // this segment's LDS reads are done before the next one is staged
+        if constexpr (STATE) {
+            if (fin_seg) {
+                // finish the final state: S made exactly symmetric (the mean of
+                // the two triangles: the MFMA sums of the two triangles round
+                // differently), then G = S C - X and h = S m - y (X and y were
+                // left in G and h above), in fp32 from S and C staged in LDS
+                float *Ss = reinterpret_cast<float *>(sm.T[0]);
+                float *Cs = Ss + W * W;
+                float *ms = Cs + W * W;
+                const size_t mo = static_cast<size_t>(bh) * W * W;
+                for (int idx = tid_l; idx < W * W; idx += kFThreads) {
+                    Ss[idx] = a.fin.S[mo + idx];
+                    Cs[idx] = a.fin.C[mo + idx];
+                }
+                if (tid_l < W) ms[tid_l] = a.fin.m[static_cast<size_t>(bh) * W + tid_l];
+                __syncthreads();
+                {
+                    constexpr int PER = W * W / kFThreads;
+                    float sym[PER];
+#pragma unroll
+                    for (int u = 0; u < PER; ++u) {
+                        const int idx = tid_l + u * kFThreads, ra = idx / W, cj = idx % W;
+                        sym[u] = 0.5f * (Ss[idx] + Ss[cj * W + ra]);
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int u = 0; u < PER; ++u) {
+                        const int idx = tid_l + u * kFThreads;
+                        Ss[idx] = sym[u];
+                        a.fin.S[mo + idx] = sym[u];
+                    }
+                }
+                __syncthreads();
+                {  // eight entries of one row per thread
+                    const int ra = tid_l >> 3, j0 = (tid_l & 7) * 8;
+                    float acc[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+                    for (int b = 0; b < W; ++b) {
+                        const float sab = Ss[ra * W + b];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[j] = fmaf(sab, Cs[b * W + j0 + j], acc[j]);
+                    }
+                    float *G = a.fin.G + mo + ra * W + j0;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) G[j] = acc[j] - G[j];
+                }
+                if (tid_l < W) {
+                    float acc = 0.0f;
+                    for (int b = 0; b < W; ++b) acc = fmaf(Ss[tid_l * W + b], ms[b], acc);
+                    float *h = a.fin.h + static_cast<size_t>(bh) * W + tid_l;
+                    *h = acc - *h;
+                }
+                if (tid_l == 0 && a.fin.rho != nullptr)
+                    a.fin.rho[bh] = (a.irho != nullptr ? a.irho[bh] : 1.0f) * gp(static_cast<float>(a.n));
+                __syncthreads();  // LDS reads done before the next segment is staged
+            }
+        }
     };
     // A loop around the body costs registers even when it runs once, so the
     // one-segment launch calls the body straight.
@@ -907,10 +1046,48 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     }
 }
 
+// The initial state in the slot layout of the aggregates (put_tiles): S, X =
+// S C - G and C as sixteen tiles of 64 lanes x 4 floats each, where tile 2v+i,
+// lane 16g+r, entry e holds element (16tb+4g+e, 16(cb+i)+r), tb = v/2, cb =
+// 2(v%2), of S, of X^T and of C^T; then y = S m - h and m as one vector pair.
+// One workgroup per head, fp32.
+__global__ __launch_bounds__(256) void k_fast64_init(hla_state in, float *iagg, float *iaggV) {
+    __shared__ float Ss[W * W], Cs[W * W], ms[W];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const size_t mo = static_cast<size_t>(bh) * W * W;
+    for (int i = tid; i < W * W; i += 256) {
+        Ss[i] = in.S[mo + i];
+        Cs[i] = in.C[mo + i];
+    }
+    if (tid < W) ms[tid] = in.m[static_cast<size_t>(bh) * W + tid];
+    __syncthreads();
+    // slot index of element (u, w): u the row index 16tb+4g+e, w the column index 16(cb+i)+r
+    auto sidx = [](int u, int w) {
+        const int tb = u >> 4, g = (u >> 2) & 3, e = u & 3, ci = w >> 4, r = w & 15;
+        const int v = 2 * tb + (ci >> 1), i = ci & 1;
+        return ((2 * v + i) * 64 + 16 * g + r) * 4 + e;
+    };
+    float *dst = iagg + static_cast<size_t>(bh) * 3 * 4096;
+    for (int idx = tid; idx < W * W; idx += 256) {
+        const int ra = idx / W, cj = idx % W;
+        float x = 0.0f;
+        for (int b = 0; b < W; ++b) x = fmaf(Ss[ra * W + b], Cs[b * W + cj], x);
+        dst[sidx(ra, cj)] = Ss[idx];                             // S[ra][cj]
+        dst[4096 + sidx(cj, ra)] = x - in.G[mo + idx];           // X[ra][cj], transposed
+        dst[2 * 4096 + sidx(cj, ra)] = Cs[idx];                  // C[ra][cj], transposed
+    }
+    if (tid < W) {
+        float y = 0.0f;
+        for (int b = 0; b < W; ++b) y = fmaf(Ss[tid * W + b], ms[b], y);
+        iaggV[static_cast<size_t>(bh) * kVecSlot + tid] = y - in.h[static_cast<size_t>(bh) * W + tid];
+        iaggV[static_cast<size_t>(bh) * kVecSlot + 64 + tid] = ms[tid];
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct FastLayout {
-    size_t flags, aggS, aggX, aggC, aggV, total;
+    size_t flags, aggS, aggX, aggC, aggV, iagg, iaggV, total;
 };
 
 FastLayout fast_layout(int BH, int P) {
@@ -921,21 +1098,26 @@ FastLayout fast_layout(int BH, int P) {
     L.aggX = L.aggS + slots * 4096 * sizeof(float);
     L.aggC = L.aggX + slots * 4096 * sizeof(float);
     L.aggV = L.aggC + slots * 4096 * sizeof(float);
-    L.total = L.aggV + slots * kVecSlot * sizeof(float);
+    L.iagg = L.aggV + align256(slots * kVecSlot * sizeof(float));
+    L.iaggV = L.iagg + static_cast<size_t>(BH) * 3 * 4096 * sizeof(float);
+    L.total = L.iaggV + static_cast<size_t>(BH) * kVecSlot * sizeof(float);
     return L;
 }
 
 template <bool DECAY, bool LOOP>
-void launch_fast(const FastArgs &a, dim3 grid, hipStream_t st, bool ridge, bool den, bool norm) {
+void launch_fast(const FastArgs &a, dim3 grid, hipStream_t st, bool ridge, bool den, bool norm, bool state) {
     const dim3 block(kFThreads);
-    if (ridge) {
-        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true>), grid, block, 0, st, a);
-        else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, false, false>), grid, block, 0, st, a);
+    if (state) {  // the ridge and denominator variants' carries, with an initial and a final state
+        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false, true>), grid, block, 0, st, a);
+    } else if (ridge) {
+        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true, false>), grid, block, 0, st, a);
+        else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, false, false, false>), grid, block, 0, st, a);
     } else {
-        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, true, true>), grid, block, 0, st, a);
-        else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, true, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, false, false>), grid, block, 0, st, a);
+        if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, true, true, false>), grid, block, 0, st, a);
+        else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, true, false, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, false, false, false>), grid, block, 0, st, a);
     }
 }
 
@@ -951,9 +1133,7 @@ void fast64_geometry(int BH, int nc, int *P, int *L) {
 }  // namespace
 
 bool fast64_supported(const FwdProblem &p) {
-    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.init.S == nullptr &&
-          p.fin.S == nullptr && p.n > 0))
-        return false;
+    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.n > 0)) return false;
     const int nh = p.gam.per_head ? p.H : 1;
     for (int h = 0; h < nh; ++h)
         if (p.gam.g[h] < kMinGamma) return false;
@@ -987,6 +1167,17 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     a.aggC = reinterpret_cast<float *>(base + L.aggC);
     a.aggV = reinterpret_cast<float *>(base + L.aggV);
     a.gam = p.gam;
+    const bool state = p.init.S != nullptr || p.fin.S != nullptr;
+    if (p.init.S != nullptr) {
+        a.iagg = reinterpret_cast<float *>(base + L.iagg);
+        a.iaggV = reinterpret_cast<float *>(base + L.iaggV);
+        a.irho = p.init.rho;
+        hipLaunchKernelGGL(k_fast64_init, dim3(a.BH), dim3(256), 0, st, p.init, const_cast<float *>(a.iagg),
+                           const_cast<float *>(a.iaggV));
+        const hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
+    a.fin = p.fin;
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
@@ -999,11 +1190,11 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
     const bool ridge = p.ridge != 0.0f, norm = p.normalize != 0, den = norm || p.den != nullptr;
     if (decay) {
-        if (loop) launch_fast<true, true>(a, grid, st, ridge, den, norm);
-        else launch_fast<true, false>(a, grid, st, ridge, den, norm);
+        if (loop) launch_fast<true, true>(a, grid, st, ridge, den, norm, state);
+        else launch_fast<true, false>(a, grid, st, ridge, den, norm, state);
     } else {
-        if (loop) launch_fast<false, true>(a, grid, st, ridge, den, norm);
-        else launch_fast<false, false>(a, grid, st, ridge, den, norm);
+        if (loop) launch_fast<false, true>(a, grid, st, ridge, den, norm, state);
+        else launch_fast<false, false>(a, grid, st, ridge, den, norm, state);
     }
     return hipGetLastError();
 }

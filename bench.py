@@ -410,9 +410,10 @@ def secondary_small(dev, stream, only):
 
 def forward_with_state(dev, stream):
     """hla_forward_chunked at B4 H8 n2048 d64 bf16 returning the final state
-    (the per-head summary a sequence shard hands on); the one-launch kernel
-    does not form it, so this is the generic chunked path.  Algorithmic bytes:
-    q, k, v in and out per head-token, plus the final state per head."""
+    (the per-head summary a sequence shard hands on), and the same call that
+    also starts from an initial state (a shard in the middle of a sequence):
+    the one-launch kernel's state variant.  Algorithmic bytes: q, k, v in and
+    out per head-token, plus each state read or written per head."""
     import torch
 
     import associative_scan_sequence_amd as hla
@@ -431,15 +432,19 @@ def forward_with_state(dev, stream):
         ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         sets.append((q, k, v, out, ws))
     fin = hla.State.empty(w.B * w.H, w.d, w.dv, dev)
-
-    def call_state(i):
-        q, k, v, out, ws = sets[i % copies]
-        hla.forward_chunked(q, k, v, chunk=w.chunk, out=out, workspace=ws, final_state=fin)
-    us = time_calls(call_state, stream, 20)
-    return [{"workload": "masked_hla_fwd_final_state_B4_H8_n2048_d64_bf16_w64",
-             "entry": "hla_forward_chunked (out + final state, generic path)", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
-             "tokens_per_s": w.B * w.n / (us * 1e-6),
-             "roofline": roof(tok * per_tok + w.B * w.H * state_b, us)}]
+    init = hla.State(*(t.to(dev) for t in inputs.random_state_fp32(w.B * w.H, w.d, w.dv, 5700, scale=0.1)))
+    res = []
+    for tag, ini, nstates in (("final_state", None, 1), ("init_and_final_state", init, 2)):
+        def call_state(i, ini=ini):
+            q, k, v, out, ws = sets[i % copies]
+            hla.forward_chunked(q, k, v, chunk=w.chunk, out=out, workspace=ws, init=ini, final_state=fin)
+        us = time_calls(call_state, stream, 20)
+        res.append({"workload": f"masked_hla_fwd_{tag}_B4_H8_n2048_d64_bf16_w64",
+                    "entry": f"hla_forward_chunked (out + {tag.replace('_', ' ')}, one-launch kernel)",
+                    "us_per_call": us, "single_call_us": dict(_LAST_PCT),
+                    "tokens_per_s": w.B * w.n / (us * 1e-6),
+                    "roofline": roof(tok * per_tok + nstates * w.B * w.H * state_b, us)})
+    return res
 
 
 def backward_headline_shape(dev, stream):

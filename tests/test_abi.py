@@ -308,9 +308,9 @@ def test_noalloc_validates_before_any_device_call(lib):
                                                ctypes.byref(a["fin"]) if a["fin"] is not None else None, None)
     assert call(params(d=48)) == UNSUPPORTED
     assert call(params(), q=None) == INVALID and "q is NULL" in last(lib)
-    # the generic path (a final state) at B4 H8 n2048 d64 needs more than 64 MiB
+    # the generic path (fp32, a final state) at B4 H8 n2048 d64 needs more than 64 MiB
     fin = CState(*[addr(10 + i) for i in range(6)])
-    p = params(B=4, H=8, n=2048, d=64, dv=64, chunk=64)
+    p = params(B=4, H=8, n=2048, d=64, dv=64, chunk=64, dtype=0)
     assert call(p, fin=fin) == WORKSPACE
     assert "static scratch" in last(lib) and str(hla._binding.NOALLOC_SCRATCH_BYTES) in last(lib)
 

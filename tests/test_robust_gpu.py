@@ -77,9 +77,10 @@ def test_fused128_writes_every_output():
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("d,dtype,norm", [(64, torch.bfloat16, True), (32, torch.float32, False),
-                                          (128, torch.bfloat16, False)])
-def test_generic_with_state_writes_every_output(d, dtype, norm):
+@pytest.mark.parametrize("d,dtype,norm", [(64, torch.bfloat16, True), (64, torch.float32, True),
+                                          (32, torch.float32, False), (128, torch.bfloat16, False)])
+def test_forward_with_state_writes_every_output(d, dtype, norm):
+    """bf16 d = 64: the one-launch kernel's state variant; otherwise the generic kernels."""
     B, H, n = 2, 3, 301
     q, k, v = (x.to(DEV) for x in inputs.qkv(B, H, n, d, d, dtype, seed=62 + d))
     if norm:

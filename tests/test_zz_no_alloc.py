@@ -2,8 +2,8 @@
 on the same inputs: the same kernels run on the library's static scratch
 instead of a caller's workspace, so the outputs must be the same bits.  Two
 calls in a row, the second with a smaller input, on every kernel path (the
-one-launch d = 64 and d = 128 forwards and the generic path with a final
-state), then a call too large for the scratch, which must fail before
+one-launch d = 64 and d = 128 forwards, the d = 64 kernel with initial and
+final states, and the generic path with a final state), then a call too large for the scratch, which must fail before
 anything is enqueued."""
 import sys
 
@@ -57,6 +57,17 @@ def test_noalloc_two_calls_second_smaller():
     both(q2, k2, v2, chunk=64, gamma=g, ridge=1e-3, normalize=True, return_den=True)
 
 
+def test_noalloc_d64_with_states():
+    """The one-launch d = 64 kernel's state variant: a final state, then a
+    smaller call that continues from it."""
+    q, k, v = (x.to(DEV) for x in inputs.qkv(2, 4, 1000, 64, 64, torch.bfloat16, seed=97))
+    g = inputs.gamma_list_fp32([0.99, 0.9, 1.0, 0.97])
+    both(q, k, v, chunk=64, gamma=g, ridge=1e-3, return_den=True, return_state=True)
+    _, _, st = hla.forward_chunked(q, k, v, chunk=64, gamma=g, return_state=True)
+    q2, k2, v2 = (x.to(DEV) for x in inputs.qkv(2, 4, 300, 64, 64, torch.bfloat16, seed=98))
+    both(q2, k2, v2, chunk=64, gamma=g, init=st, return_state=True)
+
+
 def test_noalloc_d128_then_generic_with_state():
     q, k, v = (x.to(DEV) for x in inputs.qkv(1, 16, 4096, 128, 128, torch.bfloat16, seed=93))
     both(q, k, v, gamma=inputs.gamma_list_fp32([0.999] * 16))
@@ -89,10 +100,10 @@ def test_noalloc_in_a_graph():
 
 
 def test_noalloc_rejects_a_call_beyond_the_scratch():
-    """The generic path (a final state) at B4 H8 n2048 d64 needs more than the
-    64 MiB scratch: HLA_ERR_WORKSPACE before anything is enqueued, outputs
-    untouched."""
-    q, k, v = (x.to(DEV) for x in inputs.qkv(4, 8, 2048, 64, 64, torch.bfloat16, seed=96))
+    """The generic path (fp32 inputs, a final state) at B4 H8 n2048 d64 needs
+    more than the 64 MiB scratch: HLA_ERR_WORKSPACE before anything is
+    enqueued, outputs untouched."""
+    q, k, v = (x.to(DEV) for x in inputs.qkv(4, 8, 2048, 64, 64, torch.float32, seed=96))
     out = torch.full((4, 8, 2048, 64), 7.0, device=DEV)
     fin = hla.State.empty(32, 64, 64, DEV)
     with pytest.raises(hla.HlaError, match="WORKSPACE.*static scratch"):
