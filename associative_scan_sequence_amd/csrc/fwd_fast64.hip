@@ -142,14 +142,15 @@ __device__ __forceinline__ float get_float(const float *slot, int idx) {
 // given); NORM: out = num / den.  STATE: an initial state enters every carry
 // (a.iagg, prepared by k_fast64_init), and a final state is formed when
 // a.fin.S is set.  A state has all of S, C, m, G, h, so the STATE variants
-// carry C, m and y as the ridge and denominator variants do (with lambda = 0
-// when no ridge is asked for).
+// carry C, m and y as the ridge and denominator variants do, whether or not
+// the ridge and denominator themselves are asked for.
 template <bool DECAY, bool LOOP, bool RIDGE, bool DEN, bool NORM, bool STATE>
 __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     static_assert(!NORM || DEN, "the ratio needs the denominator");
-    static_assert(!STATE || (RIDGE && DEN), "a state carries C, m and y");
+    // the moments C and m (as the ridge needs them), and y (as the denominator does)
+    constexpr bool CM = RIDGE || STATE, YV = DEN || STATE;
     constexpr bool MV = RIDGE && DEN;  // the query mass m only enters the ridge part of den
-    __shared__ FastSmem<RIDGE ? 20 : 16> sm;
+    __shared__ FastSmem<CM ? 20 : 16> sm;
     const int tid = threadIdx.x;
     // launch epoch, read by every wave: read now, first needed when the
     // segment sum is published
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             asm volatile("" : "+v"(qn[0][0]), "+v"(qn[1][1])::"memory");
             issue_v(seg);
         }
-        if constexpr (RIDGE) {  // query rows of the slice chunk (zero past its end), read after round 1
+        if constexpr (CM) {  // query rows of the slice chunk (zero past its end), read after round 1
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -487,33 +488,38 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 }
             }
         };
-        // STATE, the head's last segment: the state at the end of the sequence,
+        // STATE, the head's last segment: the state at the end of the sequence is
         // g^(pw len) * carry + this segment's own published aggregate (len = the
-        // segment's tokens), in this wave's tile layout
-        auto fin_tiles = [&](f32x4 (&x)[2], const f32x4 (&carry)[2], const float *agg, int pw) {
-            const float *slots[1] = {agg + slot * 4096};
-            const float scale[1] = {1.0f};
-            const float dl = gp(static_cast<float>(pw * (a.n - p * seg_tokens)));
+        // segment's tokens).  The own aggregate is loaded before the wait for the
+        // carries, so that its latency overlaps theirs (after them in the ridge
+        // variants, where the registers held across the wait would spill).
+        constexpr bool kEarlyOwn = !RIDGE;
+        auto own_tiles = [&](f32x4 (&x)[2], const float *agg) {
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(agg + slot * 4096);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) x[i] = dl * carry[i];
-            add_tiles<1>(x, slots, scale, 1, wave, l);
+            for (int i = 0; i < 2; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((2 * wave + i) * 64 + l) * 16, 0, kSc1);
         };
+        const float dl1 = gp(static_cast<float>(a.n - p * seg_tokens));
 
         // ================= round 1: S0 of every chunk -> LDS ========================
         {
-            f32x4 s0seg[2];
+            f32x4 s0seg[2], own_s[2];
+            if constexpr (STATE && kEarlyOwn) {
+                if (fin_seg) own_tiles(own_s, a.aggS);
+            }
             const bool bad = wait_round(0);
             carry_tiles(s0seg, a.aggS, 1, 0);
             if (bad) poison(s0seg);
             if constexpr (STATE) {
                 if (fin_seg) {  // final S[a = 16tb+4g+e][b = 16(cb+i)+r]
-                    f32x4 sf[2];
-                    fin_tiles(sf, s0seg, a.aggS, 1);
+                    if constexpr (!kEarlyOwn) own_tiles(own_s, a.aggS);
                     float *S = a.fin.S + static_cast<size_t>(bh) * W * W;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < 2; ++i) {
+                        const f32x4 sf = dl1 * s0seg[i] + own_s[i];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) S[(16 * tb + 4 * g + e) * W + 16 * (cb + i) + r] = sf[i][e];
+                        for (int e = 0; e < 4; ++e) S[(16 * tb + 4 * g + e) * W + 16 * (cb + i) + r] = sf[e];
+                    }
                 }
             }
             // With the denominator, S0 takes a third term (in the key tile: no
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // 0-1 y[a] = sum_s Us[s][a] (the three-term Us, lo in T[c]), waves 2-3
         // m[a] = sum_s f_s Q[s][a].
         const int tbu = __builtin_amdgcn_readfirstlane(tb);
-        const bool yw = DEN && tbu == 0, mw = MV && tbu == 1;
+        const bool yw = YV && tbu == 0, mw = (MV || STATE) && tbu == 1;
         const int voff = tbu == 0 ? 0 : 64;  // the vector's place in a published pair
         bf16x8 ones;
 #pragma unroll
@@ -624,14 +630,14 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             const float rho = gp(static_cast<float>(lcc[c])), rho2 = gp(static_cast<float>(2 * lcc[c]));
 #pragma unroll
             for (int i = 0; i < 2; ++i) xrun[i] *= rho2;
-            if constexpr (RIDGE) {
+            if constexpr (CM) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     cpre[c][i] = crun[i];
                     crun[i] *= rho;
                 }
             }
-            if constexpr (DEN) {
+            if constexpr (YV) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     vpre[c][i] = vrun[i][0];
@@ -654,7 +660,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                         vrun[i] = mfma(ones, tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r), vrun[i]);
                     }
                 }
-                if constexpr (RIDGE) {
+                if constexpr (CM) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const bf16x8 qt = tr8(sm.T[16 + c], rb, rb + 4, 16 * (cb + i), r);
@@ -684,7 +690,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         }
         if (publish) {
             put_tiles(a.aggX + slot * 4096, wave, l, xrun);
-            if constexpr (RIDGE) put_tiles(a.aggC + slot * 4096, wave, l, crun);
+            if constexpr (CM) put_tiles(a.aggC + slot * 4096, wave, l, crun);
             if ((yw || mw) && l < 16) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) put_float(a.aggV + slot * kVecSlot, voff + 16 * (cb + i) + r, vrun[i][0]);
@@ -781,13 +787,26 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // at vec[c * kVecSlot], the m0 half at +64)
         f32x4 x0seg[2], c0seg[2];
         float v0seg[2];
+        f32x4 own_x[2], own_c[2];
+        float own_v[2];
+        auto own_round2 = [&]() {
+            own_tiles(own_x, a.aggX);
+            own_tiles(own_c, a.aggC);
+            if (yw || mw) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) own_v[i] = get_float(a.aggV + slot * kVecSlot, voff + 16 * (cb + i) + r);
+            }
+        };
+        if constexpr (STATE && kEarlyOwn) {
+            if (fin_seg) own_round2();
+        }
         const bool bad2 = wait_round(1);
         carry_tiles(x0seg, a.aggX, 2, 1);
-        if constexpr (RIDGE) carry_tiles(c0seg, a.aggC, 1, 2);
+        if constexpr (CM) carry_tiles(c0seg, a.aggC, 1, 2);
         if (yw || mw) carry_vec(v0seg, voff, yw ? 2 : 1);
         if (bad2) {
             poison(x0seg);
-            if constexpr (RIDGE) poison(c0seg);
+            if constexpr (CM) poison(c0seg);
             v0seg[0] = v0seg[1] = __builtin_nanf("");
         }
         if constexpr (STATE) {
@@ -795,25 +814,23 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             // S C - X) and C at [a = 16(cb+i)+r][j = 16tb+4g+e]; final y (into
             // fin.h, likewise) and m
             if (fin_seg) {
-                f32x4 xf[2], cf[2];
-                fin_tiles(xf, x0seg, a.aggX, 2);
-                fin_tiles(cf, c0seg, a.aggC, 1);
+                if constexpr (!kEarlyOwn) own_round2();
                 const size_t mo = static_cast<size_t>(bh) * W * W;
+                const float dl2 = dl1 * dl1;
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i) {
+                    const f32x4 xf = dl2 * x0seg[i] + own_x[i], cf = dl1 * c0seg[i] + own_c[i];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const size_t at = mo + static_cast<size_t>(16 * (cb + i) + r) * W + 16 * tb + 4 * g + e;
-                        a.fin.G[at] = xf[i][e];
-                        a.fin.C[at] = cf[i][e];
+                        a.fin.G[at] = xf[e];
+                        a.fin.C[at] = cf[e];
                     }
+                }
                 if ((yw || mw) && l < 16) {
-                    const float *own = a.aggV + slot * kVecSlot;
-                    const float dl = gp(static_cast<float>((yw ? 2 : 1) * (a.n - p * seg_tokens)));
                     float *dst = (yw ? a.fin.h : a.fin.m) + static_cast<size_t>(bh) * W;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        dst[16 * (cb + i) + r] = dl * v0seg[i] + get_float(own, voff + 16 * (cb + i) + r);
+                    for (int i = 0; i < 2; ++i) dst[16 * (cb + i) + r] = (yw ? dl2 : dl1) * v0seg[i] + own_v[i];
                 }
             }
         }
@@ -841,7 +858,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                         st4(sm.T[4 + c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
                     }
                 }
-                if ((yw || mw) && l < 16) {
+                if (DEN && (yw || mw) && l < 16) {
                     const float dv = gp(static_cast<float>((yw ? 2 : 1) * W * c));
 #pragma unroll
                     for (int i = 0; i < 2; ++i) vec[c * kVecSlot + voff + 16 * (cb + i) + r] = dv * v0seg[i] + vpre[c][i];
@@ -942,14 +959,16 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                 // finish the final state: S made exactly symmetric (the mean of
                 // the two triangles: the MFMA sums of the two triangles round
                 // differently), then G = S C - X and h = S m - y (X and y were
-                // left in G and h above), in fp32 from S and C staged in LDS
+                // left in G and h above), in fp32 (fp32 MFMA) from S and C staged
+                // in LDS with padded rows (conflict-light operand reads)
+                constexpr int SP = W + 4, CP = W + 16;
                 float *Ss = reinterpret_cast<float *>(sm.T[0]);
-                float *Cs = Ss + W * W;
-                float *ms = Cs + W * W;
+                float *Cs = Ss + W * SP;
+                float *ms = Cs + W * CP;
                 const size_t mo = static_cast<size_t>(bh) * W * W;
                 for (int idx = tid_l; idx < W * W; idx += kFThreads) {
-                    Ss[idx] = a.fin.S[mo + idx];
-                    Cs[idx] = a.fin.C[mo + idx];
+                    Ss[(idx / W) * SP + idx % W] = a.fin.S[mo + idx];
+                    Cs[(idx / W) * CP + idx % W] = a.fin.C[mo + idx];
                 }
                 if (tid_l < W) ms[tid_l] = a.fin.m[static_cast<size_t>(bh) * W + tid_l];
                 __syncthreads();
@@ -959,34 +978,37 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
                     for (int u = 0; u < PER; ++u) {
                         const int idx = tid_l + u * kFThreads, ra = idx / W, cj = idx % W;
-                        sym[u] = 0.5f * (Ss[idx] + Ss[cj * W + ra]);
+                        sym[u] = 0.5f * (Ss[ra * SP + cj] + Ss[cj * SP + ra]);
                     }
                     __syncthreads();
 #pragma unroll
                     for (int u = 0; u < PER; ++u) {
                         const int idx = tid_l + u * kFThreads;
-                        Ss[idx] = sym[u];
+                        Ss[(idx / W) * SP + idx % W] = sym[u];
                         a.fin.S[mo + idx] = sym[u];
                     }
                 }
                 __syncthreads();
-                {  // eight entries of one row per thread
-                    const int ra = tid_l >> 3, j0 = (tid_l & 7) * 8;
-                    float acc[8];
+                // wave v forms the 16 x 16 output tiles 2v and 2v+1 (row block t/4,
+                // column block t%4): lane (g, r) takes S[m0 + r][k0 + g] and
+                // C[k0 + g][n0 + r], and receives G[m0 + 4g + e][n0 + r]
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-                    for (int b = 0; b < W; ++b) {
-                        const float sab = Ss[ra * W + b];
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int t = 2 * wave + tt, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+                    f32x4 acc = zero4;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[j] = fmaf(sab, Cs[b * W + j0 + j], acc[j]);
+                    for (int k0 = 0; k0 < W; k0 += 4)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ss[(m0 + r) * SP + k0 + g], Cs[(k0 + g) * CP + n0 + r],
+                                                                   acc, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float *G = a.fin.G + mo + static_cast<size_t>(m0 + 4 * g + e) * W + n0 + r;
+                        *G = acc[e] - *G;
                     }
-                    float *G = a.fin.G + mo + ra * W + j0;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) G[j] = acc[j] - G[j];
                 }
                 if (tid_l < W) {
                     float acc = 0.0f;
-                    for (int b = 0; b < W; ++b) acc = fmaf(Ss[tid_l * W + b], ms[b], acc);
+                    for (int b = 0; b < W; ++b) acc = fmaf(Ss[tid_l * SP + b], ms[b], acc);
                     float *h = a.fin.h + static_cast<size_t>(bh) * W + tid_l;
                     *h = acc - *h;
                 }
@@ -1050,15 +1072,15 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 // S C - G and C as sixteen tiles of 64 lanes x 4 floats each, where tile 2v+i,
 // lane 16g+r, entry e holds element (16tb+4g+e, 16(cb+i)+r), tb = v/2, cb =
 // 2(v%2), of S, of X^T and of C^T; then y = S m - h and m as one vector pair.
-// One workgroup per head, fp32.
+// Grid (BH, 4): workgroup (bh, y) forms rows 16y..16y+15 of X, S, C, y; each
+// thread a 1 x 4 block of X (fp32, all of C staged in LDS).
 __global__ __launch_bounds__(256) void k_fast64_init(hla_state in, float *iagg, float *iaggV) {
-    __shared__ float Ss[W * W], Cs[W * W], ms[W];
-    const int bh = blockIdx.x, tid = threadIdx.x;
+    __shared__ float Cs[W * W], Ss[16 * W], ms[W];
+    const int bh = blockIdx.x, r0 = 16 * blockIdx.y, tid = threadIdx.x;
     const size_t mo = static_cast<size_t>(bh) * W * W;
-    for (int i = tid; i < W * W; i += 256) {
-        Ss[i] = in.S[mo + i];
-        Cs[i] = in.C[mo + i];
-    }
+    for (int i = tid; i < W * W / 4; i += 256)
+        reinterpret_cast<float4 *>(Cs)[i] = reinterpret_cast<const float4 *>(in.C + mo)[i];
+    reinterpret_cast<float4 *>(Ss)[tid] = reinterpret_cast<const float4 *>(in.S + mo + r0 * W)[tid];
     if (tid < W) ms[tid] = in.m[static_cast<size_t>(bh) * W + tid];
     __syncthreads();
     // slot index of element (u, w): u the row index 16tb+4g+e, w the column index 16(cb+i)+r
@@ -1068,19 +1090,30 @@ __global__ __launch_bounds__(256) void k_fast64_init(hla_state in, float *iagg, 
         return ((2 * v + i) * 64 + 16 * g + r) * 4 + e;
     };
     float *dst = iagg + static_cast<size_t>(bh) * 3 * 4096;
-    for (int idx = tid; idx < W * W; idx += 256) {
-        const int ra = idx / W, cj = idx % W;
-        float x = 0.0f;
-        for (int b = 0; b < W; ++b) x = fmaf(Ss[ra * W + b], Cs[b * W + cj], x);
-        dst[sidx(ra, cj)] = Ss[idx];                             // S[ra][cj]
-        dst[4096 + sidx(cj, ra)] = x - in.G[mo + idx];           // X[ra][cj], transposed
-        dst[2 * 4096 + sidx(cj, ra)] = Cs[idx];                  // C[ra][cj], transposed
+    const int lr = tid >> 4, c0 = 4 * (tid & 15), ra = r0 + lr;
+    float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < W; ++b) {
+        const float s = Ss[lr * W + b];
+        const float4 c = *reinterpret_cast<const float4 *>(Cs + b * W + c0);
+        x[0] = fmaf(s, c.x, x[0]);
+        x[1] = fmaf(s, c.y, x[1]);
+        x[2] = fmaf(s, c.z, x[2]);
+        x[3] = fmaf(s, c.w, x[3]);
     }
-    if (tid < W) {
+    const float4 gv = *reinterpret_cast<const float4 *>(in.G + mo + ra * W + c0);
+    const float gg[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int cj = c0 + u;
+        dst[sidx(ra, cj)] = Ss[lr * W + cj];                    // S[ra][cj]
+        dst[4096 + sidx(cj, ra)] = x[u] - gg[u];                // X[ra][cj], transposed
+        dst[2 * 4096 + sidx(cj, ra)] = Cs[ra * W + cj];         // C[ra][cj], transposed
+    }
+    if (tid < 16) {
         float y = 0.0f;
         for (int b = 0; b < W; ++b) y = fmaf(Ss[tid * W + b], ms[b], y);
-        iaggV[static_cast<size_t>(bh) * kVecSlot + tid] = y - in.h[static_cast<size_t>(bh) * W + tid];
-        iaggV[static_cast<size_t>(bh) * kVecSlot + 64 + tid] = ms[tid];
+        iaggV[static_cast<size_t>(bh) * kVecSlot + r0 + tid] = y - in.h[static_cast<size_t>(bh) * W + r0 + tid];
+        iaggV[static_cast<size_t>(bh) * kVecSlot + 64 + r0 + tid] = ms[r0 + tid];
     }
 }
 
@@ -1107,9 +1140,10 @@ FastLayout fast_layout(int BH, int P) {
 template <bool DECAY, bool LOOP>
 void launch_fast(const FastArgs &a, dim3 grid, hipStream_t st, bool ridge, bool den, bool norm, bool state) {
     const dim3 block(kFThreads);
-    if (state) {  // the ridge and denominator variants' carries, with an initial and a final state
+    if (state) {  // with an initial and/or a final state: the plain numerator, or every option
         if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false, true>), grid, block, 0, st, a);
+        else if (ridge || den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, false, false, true>), grid, block, 0, st, a);
     } else if (ridge) {
         if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true, false>), grid, block, 0, st, a);
         else if (den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false, false>), grid, block, 0, st, a);
@@ -1172,7 +1206,7 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
         a.iagg = reinterpret_cast<float *>(base + L.iagg);
         a.iaggV = reinterpret_cast<float *>(base + L.iaggV);
         a.irho = p.init.rho;
-        hipLaunchKernelGGL(k_fast64_init, dim3(a.BH), dim3(256), 0, st, p.init, const_cast<float *>(a.iagg),
+        hipLaunchKernelGGL(k_fast64_init, dim3(a.BH, 4), dim3(256), 0, st, p.init, const_cast<float *>(a.iagg),
                            const_cast<float *>(a.iaggV));
         const hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return e0;
