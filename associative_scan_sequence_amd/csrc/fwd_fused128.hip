@@ -68,6 +68,7 @@ constexpr int kLine = 64;
 constexpr int kTicketWord = kLine + 2;  // control word: next segment ticket (P > 1)
 constexpr int kSlot = 16384;   // floats per published 128 x 128 aggregate
 constexpr float kMinGamma = 0.75f;
+constexpr int kStateMaxSegs = 256;  // state calls: at most one segment per CU of MI355X
 static_assert(kCtrlBytes >= 2 * kLine * 4, "control block too small");
 
 struct Args128 {
@@ -78,6 +79,13 @@ struct Args128 {
     uint32_t *flags;    // [BH * P][2]
     float *aggS, *aggZ; // [BH * P][kSlot]
     GammaTab gam;
+    // STATE variants only:
+    float *aggC;         // [BH * P][kSlot] the segments' value moments C_seg
+    float *aggV;         // [BH * P][2 * D] their y increments, then their query sums m_seg
+    const float *iagg;   // [BH][3][kSlot] the initial S, X = S C - G and C in the slot layout, or null
+    const float *iaggV;  // [BH][2 * D] its y = S m - h, then m
+    const float *irho;   // initial rho [BH] or null (read as 1)
+    hla_state fin;       // final state; fin.S null: not requested
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -192,12 +200,10 @@ __device__ __forceinline__ void put32(const float *slot, int tid, const f32x4 (&
     for (int b = 0; b < 8; ++b) __builtin_amdgcn_raw_buffer_store_b128(x[b], rs, 128 * tid + 16 * b, 0, kSc1);
 }
 
-// acc = sum over earlier segments pp < p of scale(pp) * slot(pp)
+// acc += sum over earlier segments pp < p of scale(pp) * slot(pp)
 template <typename F>
-__device__ void sum_slots(f32x4 (&acc)[8], const float *agg, int first, int p, int tid, F scale) {
+__device__ void add_slots(f32x4 (&acc)[8], const float *agg, int first, int p, int tid, F scale) {
     constexpr int NB = 4;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int p0 = 0; p0 < p; p0 += NB) {
         f32x4 v[NB][8];
 #pragma unroll
@@ -218,6 +224,22 @@ __device__ void sum_slots(f32x4 (&acc)[8], const float *agg, int first, int p, i
     }
 }
 
+// acc = sum over earlier segments pp < p of scale(pp) * slot(pp)
+template <typename F>
+__device__ void sum_slots(f32x4 (&acc)[8], const float *agg, int first, int p, int tid, F scale) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    add_slots(acc, agg, first, p, tid, scale);
+}
+
+// one float of a published vector slot (device-coherent)
+__device__ __forceinline__ void put_vec(const float *slot, int idx, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), slot_rsrc(slot), 4 * idx, 0, kSc1);
+}
+__device__ __forceinline__ float get_vec(const float *slot, int idx) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(slot_rsrc(slot), 4 * idx, 0, kSc1));
+}
+
 struct Smem128 {
     __bf16 K[kTile128];   // chunk rows [s][a]
     __bf16 V[kTile128];   // [s][j]
@@ -227,6 +249,7 @@ struct Smem128 {
     __bf16 Ux[kTile128];
     __bf16 Ah[W * LDN];  // masked scores A[t][i], then P[t][s], hi and lo
     __bf16 Al[W * LDN];
+    float vec[2 * D];    // STATE: vectors exchanged between the waves
     uint32_t epoch;
     int ticket;    // the segment this workgroup holds (ticketed launches)
     uint32_t bad;  // nonzero: a wait of this segment gave up
@@ -259,7 +282,16 @@ __device__ __forceinline__ void tri_tile(int idx, int &tb, int &ib) {
 // control word 4) makes the carry it was waiting for NaN: every output of
 // the segment and of the later segments of its head that read the carry is
 // then NaN, never a silently wrong number.
-template <bool DECAY, bool LOOP>
+// STATE: an initial state enters the carries (a.iagg, prepared by
+// k_fused128_init) and the last segment of each head forms the final state
+// when a.fin.S is set.  For the final state every segment also sums, in pass
+// 1, its value moment C_seg (whence Ct = g^T C_seg, T its token count), its
+// query sum m_seg and its zero-carry y increment ly (column sums of Us); its
+// y increment from the true carry is y_seg = S0 g^T m_seg + ly, by the same
+// affine argument as Z.  C_seg, y_seg and m_seg are published with Z.  The
+// last segment then has S and X at the sequence end in its registers after
+// pass 2, and forms G = S C - X and h = S m - y from the summed C, m and y.
+template <bool DECAY, bool LOOP, bool STATE>
 __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     __shared__ Smem128 sm;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
@@ -280,6 +312,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     const int Lseg = min(a.L, a.nc - c0);
     const int seg_tokens = a.L * W;
     const size_t slot0 = static_cast<size_t>(bh) * a.P;
+    const bool want_fin = STATE && a.fin.S != nullptr;
+    const bool fin_seg = want_fin && p + 1 == a.P;  // this workgroup writes the head's final state
+    const int T = min(a.n - c0 * W, a.L * W);       // tokens of this segment
 
     // ---- chunk inputs: each thread fetches two 16-byte pieces of q, k and v
     u32x4 pre[3][2];
@@ -309,9 +344,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
         }
     };
 
-    f32x4 sacc[8], xacc[8], cacc[8];  // S[a][b = 16w+r], X[a][j = 16w+r], Ct[a][j]
+    f32x4 sacc[8], xacc[8], cacc[8];  // S[a][b = 16w+r], X[a][j = 16w+r], Ct[a][j] (STATE: C_seg[a][j])
 #pragma unroll
     for (int b = 0; b < 8; ++b) sacc[b] = xacc[b] = cacc[b] = zero4;
+    // STATE, pass 1: m_seg and ly, entry 16w+r in row 0 (lanes 0-15) of a ones-operand product
+    f32x4 macc = zero4, lyacc = zero4;
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(r == 0 ? 1.0f : 0.0f);
 
     // One walk over the segment.  OUT: pass 2 (outputs); else pass 1 (Ct too).
     auto walk = [&](auto out_tag) {
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
                     }
                 }
             }
-            if constexpr (!OUT) {
+            if constexpr (!OUT && !STATE) {
                 // -- Ct <- g^2L Ct + Q^T diag(g^(pos + 2L - 1 - s)) V   (columns j = 16w..)
                 const float rho2 = gp(static_cast<float>(2 * Lc));
 #pragma unroll
@@ -506,73 +546,259 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
                     }
                 }
             }
+            if constexpr (!OUT && STATE) {
+                // -- C_seg <- g^L C_seg + Q^T diag(g^(L - 1 - s)) V, m_seg <- g^L m_seg +
+                // Q^T g^(L - 1 - s), ly <- g^2L ly + Us^T 1   (columns j, entries 16w..)
+                const float rho = gp(static_cast<float>(Lc)), rho2 = rho * rho;
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab) cacc[ab] *= rho;
+                macc *= rho;
+                lyacc *= rho2;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    auto wdec = [&](int s) { return gp(static_cast<float>(Lc - 1 - s)); };
+                    const bf16x8 vt = tr8<LDW>(sm.V, rb, rb + 4, 16 * w, r);
+                    bf16x8 vh = vt, vl;
+                    if (DECAY) scaled_split(vt, rb, wdec, vh, vl);
+#pragma unroll
+                    for (int ab = 0; ab < 8; ++ab) {
+                        const bf16x8 qa = tr8<LDW>(sm.Q, rb, rb + 4, 16 * ab, r);
+                        cacc[ab] = mfma(qa, vh, cacc[ab]);
+                        if (DECAY) cacc[ab] = mfma(qa, vl, cacc[ab]);
+                    }
+                    const bf16x8 qw = tr8<LDW>(sm.Q, rb, rb + 4, 16 * w, r);
+                    bf16x8 qh = qw, ql;
+                    if (DECAY) scaled_split(qw, rb, wdec, qh, ql);
+                    macc = mfma(ones, qh, macc);
+                    if (DECAY) macc = mfma(ones, ql, macc);
+                    lyacc = mfma(ones, tr8<LDW>(sm.Uh, rb, rb + 4, 16 * w, r), lyacc);
+                    lyacc = mfma(ones, tr8<LDW>(sm.Ul, rb, rb + 4, 16 * w, r), lyacc);
+                    lyacc = mfma(ones, tr8<LDW>(sm.Ux, rb, rb + 4, 16 * w, r), lyacc);
+                }
+            }
             pos += Lc;
         }
     };
 
-    if (a.P > 1) {
+    // the initial state's part `kind` (0 S, 1 X, 2 C), scaled, added to acc
+    auto add_init = [&](f32x4 (&acc)[8], int kind, float sc) {
+        if constexpr (STATE) {
+            if (a.iagg != nullptr)
+                add_slots(acc, a.iagg, 3 * bh + kind, 1, tid, [&](int) { return sc; });
+        }
+    };
+    if (a.P > 1 || fin_seg) {  // (one segment with a final state: pass 1 for C, m and y)
         if (tid == 0) sm.bad = 0u;  // read only after the barriers below
         walk(std::integral_constant<bool, false>{});
-        // ---- round 1: publish the segment's key moment; S carry from the earlier segments
-        put32(a.aggS + (slot0 + p) * kSlot, tid, sacc);
-        wait_stores();
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(&a.flags[2 * (slot0 + p)], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int spin_set = static_cast<int>(__hip_atomic_load(&a.ctrl[kSpinWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         // -1: give up without polling (a host-forced failure); n > 0: n polls
         const int spin = spin_set < 0 ? 0 : (spin_set > 0 ? spin_set : kSpinLimit);
-        for (int pp = tid; pp < p; pp += kThreads)
-            if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch, spin)) {
-                __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sm.bad = 1u;
-            }
-        __syncthreads();
-        sum_slots(sacc, a.aggS, static_cast<int>(slot0), p, tid,
-                  [&](int pp) { return gp(static_cast<float>((p - 1 - pp) * seg_tokens)); });
-        if (sm.bad) poison(sacc);
-        // ---- Z = S0 Ct + Lz: S0 -> LDS rows (hi/lo); lane holds S0[a][b = 16w+r] = S0[b][a]
-        __bf16 *S0h = sm.K, *S0l = sm.K + 2 * kTile128;  // 128-row tiles over K, V and Q, Uh
+        if (a.P > 1) {
+            // ---- round 1: publish the segment's key moment; S carry from the earlier segments
+            put32(a.aggS + (slot0 + p) * kSlot, tid, sacc);
+            wait_stores();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(&a.flags[2 * (slot0 + p)], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int pp = tid; pp < p; pp += kThreads)
+                if (!wait_flag(&a.flags[2 * (slot0 + pp)], epoch, spin)) {
+                    __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sm.bad = 1u;
+                }
+            __syncthreads();
+            sum_slots(sacc, a.aggS, static_cast<int>(slot0), p, tid,
+                      [&](int pp) { return gp(static_cast<float>((p - 1 - pp) * seg_tokens)); });
+        } else {
 #pragma unroll
-        for (int ab = 0; ab < 8; ++ab) {
-            bf16x4 h, lo;
-            split4(sacc[ab], h, lo);
-            st4<LDW>(S0h, 16 * w + r, 16 * ab + 4 * g, h);
-            st4<LDW>(S0l, 16 * w + r, 16 * ab + 4 * g, lo);
+            for (int b = 0; b < 8; ++b) sacc[b] = zero4;
         }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 ch, cl2;
-            pair_operand(cacc[2 * kk], cacc[2 * kk + 1], ch, cl2);
+        add_init(sacc, 0, gp(static_cast<float>(p * seg_tokens)));
+        if (sm.bad) poison(sacc);
+        if (a.P > 1) {
+            // ---- Z = S0 Ct + Lz: S0 -> LDS rows (hi/lo); lane holds S0[a][b = 16w+r] = S0[b][a]
+            __bf16 *S0h = sm.K, *S0l = sm.K + 2 * kTile128;  // 128-row tiles over K, V and Q, Uh
 #pragma unroll
             for (int ab = 0; ab < 8; ++ab) {
-                const int row = 16 * ab + r;
-                const bf16x8 s0h = ld44<LDW>(S0h, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
-                const bf16x8 s0l = ld44<LDW>(S0l, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
-                xacc[ab] = mfma(s0h, ch, xacc[ab]);
-                xacc[ab] = mfma(s0h, cl2, xacc[ab]);
-                xacc[ab] = mfma(s0l, ch, xacc[ab]);
+                bf16x4 h, lo;
+                split4(sacc[ab], h, lo);
+                st4<LDW>(S0h, 16 * w + r, 16 * ab + 4 * g, h);
+                st4<LDW>(S0l, 16 * w + r, 16 * ab + 4 * g, lo);
+            }
+            __syncthreads();
+            const float gT = STATE ? gp(static_cast<float>(T)) : 1.0f;  // STATE: Ct = g^T C_seg
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 ch, cl2;
+                if constexpr (STATE) pair_operand(gT * cacc[2 * kk], gT * cacc[2 * kk + 1], ch, cl2);
+                else pair_operand(cacc[2 * kk], cacc[2 * kk + 1], ch, cl2);
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab) {
+                    const int row = 16 * ab + r;
+                    const bf16x8 s0h = ld44<LDW>(S0h, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                    const bf16x8 s0l = ld44<LDW>(S0l, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                    xacc[ab] = mfma(s0h, ch, xacc[ab]);
+                    xacc[ab] = mfma(s0h, cl2, xacc[ab]);
+                    xacc[ab] = mfma(s0l, ch, xacc[ab]);
+                }
             }
         }
-        // ---- round 2: publish Z; X carry from the earlier segments
-        put32(a.aggZ + (slot0 + p) * kSlot, tid, xacc);
-        wait_stores();
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_store(&a.flags[2 * (slot0 + p) + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int pp = tid; pp < p; pp += kThreads)
-            if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch, spin)) {
-                __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sm.bad = 1u;
+        // STATE: y_seg = S0 (g^T m_seg) + ly, entry b = 16w+r in lanes 0-15 (S0 symmetric)
+        float yseg = 0.0f;
+        if constexpr (STATE) {
+            __syncthreads();  // (S0 tile reads done; sm.vec free)
+            if (g == 0) sm.vec[16 * w + r] = macc[0];
+            __syncthreads();
+            float part = 0.0f;
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) part += sacc[ab][e] * sm.vec[16 * ab + 4 * g + e];
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            yseg = gp(static_cast<float>(T)) * part + lyacc[0];
+            __syncthreads();  // sm.vec reads done
+        }
+        if (a.P > 1) {
+            // ---- round 2: publish Z (STATE: and C_seg, y_seg, m_seg); X carry from the earlier segments
+            put32(a.aggZ + (slot0 + p) * kSlot, tid, xacc);
+            if constexpr (STATE) {
+                if (want_fin) {
+                    put32(a.aggC + (slot0 + p) * kSlot, tid, cacc);
+                    if (g == 0) {
+                        put_vec(a.aggV + (slot0 + p) * 2 * D, 16 * w + r, yseg);
+                        put_vec(a.aggV + (slot0 + p) * 2 * D, D + 16 * w + r, macc[0]);
+                    }
+                }
             }
-        __syncthreads();
-        sum_slots(xacc, a.aggZ, static_cast<int>(slot0), p, tid,
-                  [&](int pp) { return gp(static_cast<float>(2 * (p - 1 - pp) * seg_tokens)); });
+            wait_stores();
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(&a.flags[2 * (slot0 + p) + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int pp = tid; pp < p; pp += kThreads)
+                if (!wait_flag(&a.flags[2 * (slot0 + pp) + 1], epoch, spin)) {
+                    __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sm.bad = 1u;
+                }
+            __syncthreads();
+            sum_slots(xacc, a.aggZ, static_cast<int>(slot0), p, tid,
+                      [&](int pp) { return gp(static_cast<float>(2 * (p - 1 - pp) * seg_tokens)); });
+        } else {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) xacc[b] = zero4;
+        }
+        add_init(xacc, 1, gp(static_cast<float>(2 * p * seg_tokens)));
         if (sm.bad) poison(xacc);
+        if constexpr (STATE) {
+            if (fin_seg) {
+                // C, m and y at the sequence end: this segment's own sums plus the
+                // earlier segments' (decayed over the tokens after each) and the
+                // initial state's; C to fin.C, m to fin.m and sm.vec, y to sm.vec
+                auto after = [&](int pp) { return static_cast<float>(a.n - (pp + 1) * seg_tokens); };
+                add_slots(cacc, a.aggC, static_cast<int>(slot0), p, tid, [&](int pp) { return gp(after(pp)); });
+                add_init(cacc, 2, gp(static_cast<float>(a.n)));
+                if (sm.bad) poison(cacc);
+                float *C = a.fin.C + static_cast<size_t>(bh) * D * D;
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) C[(16 * ab + 4 * g + e) * D + 16 * w + r] = cacc[ab][e];
+                if (g == 0) {
+                    float mv = macc[0], yv = yseg;
+                    for (int pp = 0; pp < p; ++pp) {
+                        const float *vs = a.aggV + (slot0 + pp) * 2 * D;
+                        const float d1 = gp(after(pp));
+                        yv += d1 * d1 * get_vec(vs, 16 * w + r);
+                        mv += d1 * get_vec(vs, D + 16 * w + r);
+                    }
+                    if (a.iaggV != nullptr) {
+                        const float dn = gp(static_cast<float>(a.n));
+                        yv += dn * dn * a.iaggV[static_cast<size_t>(bh) * 2 * D + 16 * w + r];
+                        mv += dn * a.iaggV[static_cast<size_t>(bh) * 2 * D + D + 16 * w + r];
+                    }
+                    if (sm.bad) mv = yv = __builtin_nanf("");
+                    a.fin.m[static_cast<size_t>(bh) * D + 16 * w + r] = mv;
+                    sm.vec[16 * w + r] = mv;
+                    sm.vec[D + 16 * w + r] = yv;
+                }
+            }
+        }
+    } else if constexpr (STATE) {  // one segment, no final state: the carries are the initial state
+        add_init(sacc, 0, 1.0f);
+        add_init(xacc, 1, 1.0f);
     }
     walk(std::integral_constant<bool, true>{});
 
     __syncthreads();  // this segment's LDS reads are done before the next one is staged
+    if constexpr (STATE) {
+        if (fin_seg) {
+            // ---- the final state: sacc, xacc hold S and X at the sequence end.
+            // S is made exactly symmetric (the mean of the two triangles, through
+            // fin.S), then h = S m - y, and G = S C - X with C reloaded from fin.C
+            // (the product as for Z: S tiles in LDS, C from registers)
+            float *S = a.fin.S + static_cast<size_t>(bh) * D * D;
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[(16 * ab + 4 * g + e) * D + 16 * w + r] = sacc[ab][e];
+            __syncthreads();
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sacc[ab][e] = 0.5f * (sacc[ab][e] + S[(16 * w + r) * D + 16 * ab + 4 * g + e]);
+            __syncthreads();
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[(16 * ab + 4 * g + e) * D + 16 * w + r] = sacc[ab][e];
+            float part = 0.0f;
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) part += sacc[ab][e] * sm.vec[16 * ab + 4 * g + e];
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (g == 0) a.fin.h[static_cast<size_t>(bh) * D + 16 * w + r] = part - sm.vec[D + 16 * w + r];
+            const float *C = a.fin.C + static_cast<size_t>(bh) * D * D;
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab) {
+                xacc[ab] = -xacc[ab];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cacc[ab][e] = C[(16 * ab + 4 * g + e) * D + 16 * w + r];
+            }
+            __bf16 *S0h = sm.K, *S0l = sm.K + 2 * kTile128;
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab) {
+                bf16x4 h, lo;
+                split4(sacc[ab], h, lo);
+                st4<LDW>(S0h, 16 * w + r, 16 * ab + 4 * g, h);
+                st4<LDW>(S0l, 16 * w + r, 16 * ab + 4 * g, lo);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 ch, cl2;
+                pair_operand(cacc[2 * kk], cacc[2 * kk + 1], ch, cl2);
+#pragma unroll
+                for (int ab = 0; ab < 8; ++ab) {
+                    const int row = 16 * ab + r;
+                    const bf16x8 s0h = ld44<LDW>(S0h, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                    const bf16x8 s0l = ld44<LDW>(S0l, row, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g);
+                    xacc[ab] = mfma(s0h, ch, xacc[ab]);
+                    xacc[ab] = mfma(s0h, cl2, xacc[ab]);
+                    xacc[ab] = mfma(s0l, ch, xacc[ab]);
+                }
+            }
+            float *G = a.fin.G + static_cast<size_t>(bh) * D * D;
+#pragma unroll
+            for (int ab = 0; ab < 8; ++ab)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G[(16 * ab + 4 * g + e) * D + 16 * w + r] = xacc[ab][e];
+            if (tid == 0 && a.fin.rho != nullptr)
+                a.fin.rho[bh] = (a.irho != nullptr ? a.irho[bh] : 1.0f) * gp(static_cast<float>(a.n));
+            __syncthreads();  // LDS reads done before the next segment is staged
+        }
+    }
     };
     // (a loop around the body costs registers even when it runs once, so the
     // one-segment-per-workgroup launch calls it straight)
@@ -604,6 +830,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     }
 }
 
+// The initial state in the slot layout of the kernel's registers: thread tid
+// = 64 w + 16 g + r holds, at floats 32 tid + 4 ab + e of a slot, element
+// (16 ab + 4 g + e, 16 w + r) of S, of X = S C - G and of C; then y = S m - h
+// and m as one vector pair.  Grid (BH, 8): workgroup (bh, y) forms rows
+// 16y..16y+15; each thread a 1 x 8 block of X (fp32, all of C staged in LDS).
+__global__ __launch_bounds__(256) void k_fused128_init(hla_state in, float *iagg, float *iaggV) {
+    __shared__ float Cs[D * D], Ss[16 * D], ms[D];
+    const int bh = blockIdx.x, r0 = 16 * blockIdx.y, tid = threadIdx.x;
+    const size_t mo = static_cast<size_t>(bh) * D * D;
+    for (int i = tid; i < D * D / 4; i += 256)
+        reinterpret_cast<float4 *>(Cs)[i] = reinterpret_cast<const float4 *>(in.C + mo)[i];
+    for (int i = tid; i < 16 * D / 4; i += 256)
+        reinterpret_cast<float4 *>(Ss)[i] = reinterpret_cast<const float4 *>(in.S + mo + r0 * D)[i];
+    if (tid < D / 2) {
+        ms[2 * tid] = in.m[static_cast<size_t>(bh) * D + 2 * tid];
+        ms[2 * tid + 1] = in.m[static_cast<size_t>(bh) * D + 2 * tid + 1];
+    }
+    __syncthreads();
+    auto sidx = [](int ra, int c) {
+        const int ab = ra >> 4, g = (ra >> 2) & 3, e = ra & 3, w = c >> 4, r = c & 15;
+        return 32 * (64 * w + 16 * g + r) + 4 * ab + e;
+    };
+    float *dst = iagg + static_cast<size_t>(bh) * 3 * kSlot;
+    const int lr = tid >> 4, c0 = 8 * (tid & 15), ra = r0 + lr;
+    float x[8] = {};
+    for (int b = 0; b < D; ++b) {
+        const float sv = Ss[lr * D + b];
+        const float4 u = *reinterpret_cast<const float4 *>(Cs + b * D + c0);
+        const float4 v = *reinterpret_cast<const float4 *>(Cs + b * D + c0 + 4);
+        x[0] = fmaf(sv, u.x, x[0]); x[1] = fmaf(sv, u.y, x[1]); x[2] = fmaf(sv, u.z, x[2]); x[3] = fmaf(sv, u.w, x[3]);
+        x[4] = fmaf(sv, v.x, x[4]); x[5] = fmaf(sv, v.y, x[5]); x[6] = fmaf(sv, v.z, x[6]); x[7] = fmaf(sv, v.w, x[7]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int cj = c0 + u;
+        const int at = sidx(ra, cj);
+        dst[at] = Ss[lr * D + cj];                           // S[ra][cj]
+        dst[kSlot + at] = x[u] - in.G[mo + ra * D + cj];     // X[ra][cj]
+        dst[2 * kSlot + at] = Cs[ra * D + cj];               // C[ra][cj]
+    }
+    if (tid < 16) {
+        float y = 0.0f;
+        for (int b = 0; b < D; ++b) y = fmaf(Ss[tid * D + b], ms[b], y);
+        iaggV[static_cast<size_t>(bh) * 2 * D + r0 + tid] = y - in.h[static_cast<size_t>(bh) * D + r0 + tid];
+        iaggV[static_cast<size_t>(bh) * 2 * D + D + r0 + tid] = ms[r0 + tid];
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 void geometry(int BH, int nc, int *P, int *L) {
@@ -616,16 +890,21 @@ void geometry(int BH, int nc, int *P, int *L) {
 }
 
 struct Layout128 {
-    size_t flags, aggS, aggZ, total;
+    size_t flags, aggS, aggZ, aggC, aggV, iagg, iaggV, total;
 };
 
 Layout128 layout(int BH, int P) {
     Layout128 L{};
     const size_t slots = static_cast<size_t>(BH) * P;
+    const size_t pub = P > 1 ? slots * kSlot * sizeof(float) : 0;  // one published 128 x 128 slot per segment
     L.flags = 0;
     L.aggS = align256(2 * slots * sizeof(uint32_t));
-    L.aggZ = L.aggS + (P > 1 ? slots * kSlot * sizeof(float) : 0);
-    L.total = L.aggZ + (P > 1 ? slots * kSlot * sizeof(float) : 0);
+    L.aggZ = L.aggS + pub;
+    L.aggC = L.aggZ + pub;
+    L.aggV = L.aggC + pub;
+    L.iagg = L.aggV + align256(P > 1 ? slots * 2 * D * sizeof(float) : 0);
+    L.iaggV = L.iagg + static_cast<size_t>(BH) * 3 * kSlot * sizeof(float);
+    L.total = L.iaggV + static_cast<size_t>(BH) * 2 * D * sizeof(float);
     return L;
 }
 
@@ -633,8 +912,16 @@ Layout128 layout(int BH, int P) {
 
 bool fused128_supported(const FwdProblem &p) {
     if (!(p.dtype == HLA_BF16 && p.d == 128 && p.dv == 128 && p.ridge == 0.0f && !p.normalize &&
-          p.den == nullptr && p.init.S == nullptr && p.fin.S == nullptr && p.n > 0))
+          p.den == nullptr && p.n > 0))
         return false;
+    if (p.init.S != nullptr || p.fin.S != nullptr) {
+        // with a state, the looped body (segments beyond one per CU) spills
+        // heavily: those calls take the generic path
+        if (p.B < 1 || p.H < 1) return false;
+        int P, L;
+        geometry(p.B * p.H, (p.n + W - 1) / W, &P, &L);
+        if (P > 1 && static_cast<long>(p.B) * p.H * P > kStateMaxSegs) return false;
+    }
     const int nh = p.gam.per_head ? p.H : 1;
     for (int h = 0; h < nh; ++h)
         if (p.gam.g[h] < kMinGamma) return false;
@@ -664,7 +951,20 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
     a.aggS = reinterpret_cast<float *>(base + L.aggS);
     a.aggZ = reinterpret_cast<float *>(base + L.aggZ);
+    a.aggC = reinterpret_cast<float *>(base + L.aggC);
+    a.aggV = reinterpret_cast<float *>(base + L.aggV);
     a.gam = p.gam;
+    const bool state = p.init.S != nullptr || p.fin.S != nullptr;
+    if (p.init.S != nullptr) {
+        float *iagg = reinterpret_cast<float *>(base + L.iagg), *iaggV = reinterpret_cast<float *>(base + L.iaggV);
+        a.iagg = iagg;
+        a.iaggV = iaggV;
+        a.irho = p.init.rho;
+        hipLaunchKernelGGL(k_fused128_init, dim3(a.BH, 8), dim3(256), 0, st, p.init, iagg, iaggV);
+        const hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
+    a.fin = p.fin;
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
@@ -678,12 +978,21 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     // not be resident: one workgroup per segment, without the looped body
     const bool loop = a.segs > cus && a.P > 1;
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
-    if (decay) {
-        if (loop) hipLaunchKernelGGL((k_fused128<true, true>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_fused128<true, false>), grid, dim3(kThreads), 0, st, a);
+    const dim3 block(kThreads);
+    if (state) {
+        if (decay) {
+            if (loop) hipLaunchKernelGGL((k_fused128<true, true, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fused128<true, false, true>), grid, block, 0, st, a);
+        } else {
+            if (loop) hipLaunchKernelGGL((k_fused128<false, true, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fused128<false, false, true>), grid, block, 0, st, a);
+        }
+    } else if (decay) {
+        if (loop) hipLaunchKernelGGL((k_fused128<true, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fused128<true, false, false>), grid, block, 0, st, a);
     } else {
-        if (loop) hipLaunchKernelGGL((k_fused128<false, true>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_fused128<false, false>), grid, dim3(kThreads), 0, st, a);
+        if (loop) hipLaunchKernelGGL((k_fused128<false, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fused128<false, false, false>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }

@@ -157,7 +157,7 @@ hla_status forward_geometry(const hla_params *p, Geometry *geo) {
 FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *init,
                     const hla_state *fin, const float *den, const hla::GammaTab &gam) {
     hla::FwdProblem fp{};
-    fp.dtype = p->dtype; fp.d = p->d; fp.dv = p->dv; fp.w = geo.w; fp.n = p->n; fp.H = p->H;
+    fp.dtype = p->dtype; fp.d = p->d; fp.dv = p->dv; fp.w = geo.w; fp.n = p->n; fp.B = p->B; fp.H = p->H;
     fp.gam = gam;
     fp.ridge = p->ridge; fp.normalize = p->normalize; fp.den = const_cast<float *>(den);
     if (init) fp.init = *init;

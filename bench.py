@@ -272,7 +272,21 @@ def secondary_rest(dev, stream, only):
     tok = w.B * w.H * w.n
     res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
                 "tokens_per_s": w.B * w.n / (us * 1e-6), "roofline": roof(tok * per_tok, us)})
-    del q, k, v, out, ws
+    # the same call returning its final state, and starting from an initial one
+    # (a long-context shard): the one-launch kernel's state variant
+    fin = hla.State.empty(w.B * w.H, w.d, w.dv, dev)
+    init = hla.State(*(t.to(dev) for t in inputs.random_state_fp32(w.B * w.H, w.d, w.dv, 5101, scale=0.05)))
+    state_b = 4 * (w.d * w.d + 2 * w.d * w.dv + 2 * w.d + 1)
+    for tag, ini, nstates in (("final_state", None, 1), ("init_and_final_state", init, 2)):
+        us = time_calls(lambda i, ini=ini: hla.forward_chunked(q, k, v, gamma=w.gamma, chunk=w.chunk, out=out,
+                                                               workspace=ws, init=ini, final_state=fin),
+                        stream, 5, warmup=2)
+        res.append({"workload": w.name.replace("masked_hla_fwd", f"masked_hla_fwd_{tag}"),
+                    "entry": f"hla_forward_chunked (out + {tag.replace('_', ' ')}, one-launch kernel)",
+                    "us_per_call": us, "single_call_us": dict(_LAST_PCT),
+                    "tokens_per_s": w.B * w.n / (us * 1e-6),
+                    "roofline": roof(tok * per_tok + nstates * w.B * w.H * state_b, us)})
+    del q, k, v, out, ws, fin, init
     if only is not None:
         return res
     return res + secondary_states(dev, stream, None)

@@ -416,3 +416,23 @@ def test_ahla_and_third_decode_reject_bad_arguments(lib, third):
     hole = CHiState(addr(7), addr(8), addr(9), None, addr(11))
     assert call(params(n=1), state=hole) == INVALID and "is NULL" in last(lib)
     assert call(params(n=1), out=addr(8)) == INVALID and "overlaps" in last(lib)
+
+
+def test_path_choice_with_a_state_at_every_width(lib):
+    """Choosing the kernel path for a call with a state reads the batch size
+    (the d = 128 one-launch kernel checks its segment count): every width,
+    both dtypes, through the no-alloc entry point, whose validation chooses
+    the path before anything touches a device.  A call either fits the static
+    scratch (and then fails here, without a GPU, looking up its address) or is
+    rejected for its size; it never reaches a kernel."""
+    init = CState(*[addr(10 + i) for i in range(6)])
+    fin = CState(*[addr(20 + i) for i in range(6)])
+    for d in (16, 32, 64, 128):
+        for dtype in (0, 1):
+            for n in (1, 300, 4096):
+                for ini in (None, init):
+                    p = params(B=1, H=16, n=n, d=d, dv=d, dtype=dtype)
+                    st = lib.hla_forward_chunked_noalloc(
+                        ctypes.byref(p), addr(1), addr(2), addr(3), addr(4), None,
+                        ctypes.byref(ini) if ini is not None else None, ctypes.byref(fin), None)
+                    assert st in (WORKSPACE, 5), (d, dtype, n, st, last(lib))
