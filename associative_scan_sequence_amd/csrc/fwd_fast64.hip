@@ -1052,8 +1052,10 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))));
     if constexpr (LOOP) {  // (with one segment per head nothing waits: a plain stride)
         for (int seg = seg0; seg < a.segs; seg = a.P > 1 ? take() : seg + static_cast<int>(gridDim.x)) seg_body(seg);
-    } else {
+    } else if (seg0 < a.segs) {
         seg_body(seg0);
+    } else if (tid == 0) {  // a ticket out of range: the control block was not zero before first use
+        __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- the last workgroup to finish resets the counter and advances the epoch

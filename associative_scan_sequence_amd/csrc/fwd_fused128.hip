@@ -815,7 +815,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused128(Args128 a) {
     if constexpr (LOOP) {
         for (int seg = take(); seg < a.segs; seg = take()) seg_body(seg);
     } else {
-        seg_body(a.P > 1 ? take() : static_cast<int>(blockIdx.x));
+        const int seg = a.P > 1 ? take() : static_cast<int>(blockIdx.x);
+        if (seg < a.segs) seg_body(seg);
+        else if (tid == 0)  // a ticket out of range: the control block was not zero before first use
+            __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- the last workgroup to finish resets the counters and advances the epoch

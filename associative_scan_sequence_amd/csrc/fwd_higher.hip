@@ -366,11 +366,13 @@ struct HiLayout {
     size_t S, P, m, E, n, U, Y, yd, total;
 };
 
+// (the first kCtrlBytes are the control block of the one-launch path below,
+// which this path never touches)
 HiLayout layout(int BH, int n, int d, int dv, int w, bool third) {
     const size_t nc = (static_cast<size_t>(n) + w - 1) / w;
     const size_t slots = static_cast<size_t>(BH) * (nc + 1), chunks = static_cast<size_t>(BH) * nc;
     HiLayout L{};
-    size_t off = 0;
+    size_t off = kCtrlBytes;
     L.S = off; off = align256(off + (third ? slots * d * d * sizeof(float) : 0));
     L.P = off; off = align256(off + slots * d * dv * sizeof(float));
     L.m = off; off = align256(off + slots * d * sizeof(float));
@@ -383,13 +385,84 @@ HiLayout layout(int BH, int n, int d, int dv, int w, bool third) {
     return L;
 }
 
+// ---- one-launch path (bf16, d = dv = 64, chunk 64, numerator only, no states):
+// AHLA = LA(Q, K, LA(Q, K, V)) and third order = HLA2(Q, K, LA(Q, K, V)) with
+// LA the masked first-order map (fwd_la64.hip, decay g; g = 1 for third
+// order) and HLA2 the second-order forward (k_fast64).  The intermediate
+// values Y = LA(Q, K, V) are kept as bf16 hi + lo, and both maps are linear in
+// their values, so the second map runs once on each half (AHLA: the second
+// half is added in place; third order: into a buffer added afterwards).
+// Workspace: control block, the one-launch kernels' data (shared: every
+// launch leaves the control block valid for the next), Y hi, Y lo, and for
+// third order the fp32 buffer.
+struct FastHiLayout {
+    size_t data, yh, yl, tmp, total;
+};
+
+FastHiLayout fast_layout(int BH, int n, bool third) {
+    const size_t tok = static_cast<size_t>(BH) * n;
+    const size_t la = la64_workspace_bytes(BH, n), f64 = third ? fast64_workspace_bytes(BH, n) : 0;
+    FastHiLayout L{};
+    L.data = kCtrlBytes;
+    L.yh = align256(L.data + (la > f64 ? la : f64));
+    L.yl = align256(L.yh + tok * 64 * sizeof(uint16_t));
+    L.tmp = align256(L.yl + tok * 64 * sizeof(uint16_t));
+    L.total = L.tmp + (third ? tok * 64 * sizeof(float) : 0);
+    return L;
+}
+
+bool fast_eligible(const HiProblem &p) {
+    if (!(p.dtype == HLA_BF16 && p.d == 64 && p.dv == 64 && p.w == 64 && p.n > 0 && !p.normalize &&
+          p.den == nullptr && p.init.X1 == nullptr && p.fin.X1 == nullptr))
+        return false;
+    const int nh = p.gam.per_head ? p.H : 1;
+    for (int h = 0; h < nh; ++h)
+        if (p.gam.g[h] < 0.75f) return false;
+    return true;
+}
+
+hipError_t fast_higher(const HiProblem &p, hipStream_t st) {
+    const int BH = p.B * p.H;
+    const FastHiLayout L = fast_layout(BH, p.n, p.third);
+    char *base = static_cast<char *>(p.ws);
+    uint32_t *ctrl = reinterpret_cast<uint32_t *>(base);
+    void *data = base + L.data;
+    uint16_t *yh = reinterpret_cast<uint16_t *>(base + L.yh), *yl = reinterpret_cast<uint16_t *>(base + L.yl);
+    LaProblem la{};
+    la.B = p.B; la.H = p.H; la.n = p.n; la.q = p.q; la.k = p.k; la.gam = p.gam;
+    // Y = LA(Q, K, V) as bf16 hi + lo
+    la.v = p.v; la.oh = yh; la.ol = yl; la.mode = 2;
+    hipError_t e = la64_forward(la, ctrl, data, st);
+    if (e != hipSuccess) return e;
+    if (!p.third) {
+        la.oh = la.ol = nullptr; la.out = p.out;
+        la.v = yh; la.mode = 0;
+        if ((e = la64_forward(la, ctrl, data, st)) != hipSuccess) return e;
+        la.v = yl; la.mode = 1;
+        return la64_forward(la, ctrl, data, st);
+    }
+    FwdProblem f{};
+    f.B = p.B; f.H = p.H; f.n = p.n; f.d = 64; f.dv = 64; f.w = 64; f.nc = (p.n + 63) / 64;
+    f.dtype = HLA_BF16; f.q = p.q; f.k = p.k; f.gam = p.gam;
+    f.v = yh; f.out = p.out;
+    if ((e = fast64_forward(f, ctrl, data, st)) != hipSuccess) return e;
+    float *tmp = reinterpret_cast<float *>(base + L.tmp);
+    f.v = yl; f.out = tmp;
+    if ((e = fast64_forward(f, ctrl, data, st)) != hipSuccess) return e;
+    return add_into(p.out, tmp, static_cast<size_t>(BH) * p.n * 64, st);
+}
+
 }  // namespace
 
 size_t higher_workspace_bytes(int BH, int n, int d, int dv, int w, bool third) {
-    return layout(BH, n, d, dv, w, third).total;
+    const size_t gen = layout(BH, n, d, dv, w, third).total;
+    if (!(d == 64 && dv == 64 && w == 64 && n > 0)) return gen;
+    const size_t fast = fast_layout(BH, n, third).total;
+    return gen > fast ? gen : fast;
 }
 
 hipError_t higher_forward(const HiProblem &p, hipStream_t st) {
+    if (fast_eligible(p)) return fast_higher(p, st);
     const int BH = p.B * p.H;
     const HiLayout L = layout(BH, p.n, p.d, p.dv, p.w, p.third);
     char *base = static_cast<char *>(p.ws);

@@ -1,0 +1,475 @@
+// fwd_la64.hip -- one-launch masked first-order (causal) linear attention
+// for d = dv = 64, chunk 64, bf16 q/k/v on gfx950 MFMA:
+//   y_t = sum_{s <= t} g^(t - s) (q_t . k_s) v_s.
+// The asymmetric variant (AHLA) is this map applied twice, and masked third
+// order is second-order HLA over values that this map has mixed (Higher-order
+// Linear Attention, paperlayer.ai summary sec. 6 and 7; the decompositions
+// are pinned on the CPU in tests/test_higher_oracle.py), so both are built
+// from it where their inputs allow.
+//
+// Per chunk (local t, s; L tokens; e_t = g^(t+1), f_s = g^(L-1-s)), with the
+// carry C0 = sum over earlier tokens of g^(distance to the chunk start - 1) k v^T:
+//   A = (Q K^T) o D_g o L,   y = A V + diag(e) Q C0,   C0 <- g^L C0 + K^T diag(f) V.
+// The layout, segments, tickets and the device-coherent hand-off of the C
+// aggregates are those of the second-order kernel (fwd_fast64.hip), with one
+// exchange round instead of two:
+//  * tile role: wave v sums tiles 2v, 2v+1 of the segment's C^T (rows j =
+//    16tb+4g+e, columns a = 16(cb+i)+r) over its chunks, publishes them, and
+//    sums the carry from the earlier segments' aggregates;
+//  * slice role: wave v forms the masked A^T tiles of 32 tokens of chunk v/2
+//    and the local part A V, then adds e_t C0^T q_t once the carry is in LDS.
+// Output: fp32 (stored, or added to what out holds), or the result split into
+// bf16 hi = bf16(y) and lo = bf16(y - hi), ready to be values of a later pass.
+// Precision: A is split into bf16 hi + lo (its entries are fp32 sums), as are
+// the decayed key operand of the C sums and the carry C0.
+#include "fast64_common.h"
+
+namespace hla {
+namespace {
+
+template <int V>
+struct IC {  // an int as a type, to instantiate a lambda for each half
+    static constexpr int value = V;
+};
+
+constexpr int kLThreads = 512;
+constexpr int kLMaxL = 4;  // chunks per segment
+constexpr int kLWaves = 8;
+
+constexpr int kStore = 0, kAccumulate = 1, kSplit = 2;  // output modes (LaProblem::mode)
+
+struct LaArgs {
+    int H, n, nc, P, L, BH, segs;
+    const uint16_t *q, *k, *v;
+    float *out;             // kStore, kAccumulate
+    uint16_t *oh, *ol;      // kSplit: bf16 hi and lo of the result
+    uint32_t *ctrl;         // control block, as for the second-order kernel
+    uint32_t *flags;        // [BH * P][8 waves] at kFlagStride words
+    float *aggC;            // [BH * P][16 tiles][64 lanes][4]
+    GammaTab gam;
+};
+
+struct LaSmem {
+    __bf16 T[16][kTileElems];  // K_c in T[c], V_c in T[4+c], C0 of chunk c in T[8+2c] (hi), T[9+2c] (lo)
+};
+
+__device__ __forceinline__ void put_tiles2(const float *slot, int v, int l, const f32x4 (&x)[2]) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
+}
+
+template <bool DECAY, bool LOOP, int OUT>
+__global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
+    __shared__ LaSmem sm;
+    const int tid = threadIdx.x;
+    uint32_t ep_raw = 0;
+    if ((tid & 63) == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t epoch = 0;
+    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lg = 0.0f;
+    auto gp = [&](float e) { return DECAY ? __builtin_amdgcn_exp2f(e * lg) : 1.0f; };  // g^e
+    auto gpl = [&](float el) { return DECAY ? __builtin_amdgcn_exp2f(el) : 1.0f; };   // g^e from e log2(g)
+
+    auto seg_body = [&](const int seg) __attribute__((always_inline)) {
+        int tid_l = static_cast<int>(threadIdx.x);
+        if constexpr (LOOP) asm volatile("" : "+v"(tid_l));
+        const int wave = tid_l >> 6, l = tid_l & 63, r = l & 15, g = l >> 4;
+        const int grp = wave >> 2, wt = tid_l & 255;
+        const int sc = wave >> 1, hh = (wave ^ (wave >> 2)) & 1;
+        const int t0 = 32 * hh + r;
+        const int tb = wave >> 1, cb = 2 * (wave & 1);
+        const int bh = seg % a.BH, p = seg / a.BH;
+        lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
+        const size_t head = static_cast<size_t>(bh) * a.n;
+        const int c0 = p * a.L;
+        const int Lseg = min(a.L, a.nc - c0);
+        auto chunk_len = [&](int j) { return min(W, a.n - (c0 + j) * W); };
+        int lc_of[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) lc_of[jj] = 2 * grp + jj < Lseg ? chunk_len(2 * grp + jj) : 0;
+        const int Lcs = sc < Lseg ? chunk_len(sc) : 0;
+        int lcc[kLMaxL];
+#pragma unroll
+        for (int c = 0; c < kLMaxL; ++c) lcc[c] = c < Lseg ? chunk_len(c) : 0;
+        const size_t slot = static_cast<size_t>(bh) * a.P + p;
+        const bool publish = p + 1 < a.P;
+
+        // ---- loads: keys and values of the segment's chunks (rows past a chunk
+        // read the head's first row and are zeroed when staged), queries of the slice
+        u32x4 kx[2][2], vx[2][2], qx[2][2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * grp + jj;
+            const size_t tok0 = head + static_cast<size_t>(c0 + j) * W;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
+                const size_t src = row < lc_of[jj] ? tok0 + row : head;
+                kx[jj][u] = *reinterpret_cast<const u32x4 *>(a.k + src * W + cg * 8);
+                vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
+            }
+        }
+        {
+            const size_t tok0 = head + static_cast<size_t>(c0 + sc) * W;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int tt = t0 + 16 * i;
+                    const size_t src = tt < Lcs ? tok0 + tt : head;
+                    qx[i][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
+                }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
+                st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
+                st16(sm.T[4 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
+            }
+        bf16x8 qn[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
+        __syncthreads();
+
+        auto lane_base = [&](int off) __attribute__((always_inline)) {
+            if (!DECAY) return 0.0f;
+            asm volatile("" : "+v"(off));
+            return static_cast<float>(off) * lg;
+        };
+
+        // ================= tiles: the segment's C^T ================================
+        // cpre[c] = sum of chunks 0..c-1 at chunk c's start; crun ends as C_seg.
+        // Tile (j = 16tb+4g+e, a = 16(cb+i)+r) = sum_s V[s][j] f_s K[s][a].
+        f32x4 cpre[kLMaxL][2], crun[2] = {zero4, zero4};
+#pragma unroll
+        for (int c = 0; c < kLMaxL; ++c) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) cpre[c][i] = crun[i];
+            const int Lc = lcc[c];
+            const float rho = gp(static_cast<float>(Lc));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) crun[i] *= rho;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rb = 32 * ks + 8 * g;
+                const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const bf16x8 kt = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
+                    if (!DECAY) {
+                        crun[i] = mfma(vt, kt, crun[i]);
+                    } else {
+                        // f_s = g^(Lc - 1 - s) for the tokens s = 32ks + 8g + e (+4)
+                        const float base = fmaf(static_cast<float>(Lc - 1), lg, lane_base(-8 * g));
+                        f32x4 x0, x1;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x0[e] = gpl(fmaf(static_cast<float>(-(32 * ks + e)), lg, base)) * static_cast<float>(kt[e]);
+                            x1[e] = gpl(fmaf(static_cast<float>(-(32 * ks + 4 + e)), lg, base)) * static_cast<float>(kt[4 + e]);
+                        }
+                        bf16x8 h, lo;
+                        pair_operand(x0, x1, h, lo);
+                        crun[i] = mfma(vt, h, crun[i]);
+                        crun[i] = mfma(vt, lo, crun[i]);
+                    }
+                }
+            }
+        }
+        auto flag_of = [&](size_t sl) { return &a.flags[(sl * kLWaves + wave) * kFlagStride]; };
+        if (publish) {
+            put_tiles2(a.aggC + slot * 4096, wave, l, crun);
+            wait_stores();
+            if (l == 0) set_flag(flag_of(slot), epoch);
+        }
+
+        // ================= slice: A^T and the local part A V =========================
+        f32x4 num[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
+        auto local = [&](auto hc) __attribute__((always_inline)) {
+            constexpr int HH = decltype(hc)::value;
+            const float lg_rg = lane_base(r - 4 * g);
+            f32x4 at[2][4];
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                at[0][ib] = at[1][ib] = zero4;
+                if (ib <= 2 * HH + 1) {
+                    const bf16x8 k0 = ld8(sm.T[sc], 16 * ib + r, 8 * g), k1 = ld8(sm.T[sc], 16 * ib + r, 32 + 8 * g);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        if (ib <= 2 * HH + i) {
+                            at[i][ib] = mfma(k1, qn[i][1], mfma(k0, qn[i][0], zero4));
+                            // g^(t - s), t = 32HH + 16i + r, s = 16ib + 4g + e; s > t only in the diagonal tile
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float dec = gpl(fmaf(static_cast<float>(32 * HH + 16 * i - 16 * ib - e), lg, lg_rg));
+                                if (ib == 2 * HH + i) at[i][ib][e] = 4 * g + e <= r ? dec * at[i][ib][e] : 0.0f;
+                                else at[i][ib][e] *= dec;
+                            }
+                        }
+                    }
+                }
+            }
+            // num^T[j][t] = sum_s V[s][j] A[t][s]
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks <= 2 * HH + 1) {
+                    bf16x8 vt[4];
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        if (2 * ks <= 2 * HH + i) {
+                            bf16x8 ah, al;
+                            pair_operand(at[i][2 * ks], at[i][2 * ks + 1], ah, al);
+#pragma unroll
+                            for (int jb = 0; jb < 4; ++jb) {
+                                num[i][jb] = mfma(vt[jb], ah, num[i][jb]);
+                                num[i][jb] = mfma(vt[jb], al, num[i][jb]);
+                            }
+                        }
+                    }
+                }
+            }
+        };
+        if (Lcs > 0) {
+            if (hh) local(IC<1>{});
+            else local(IC<0>{});
+        }
+
+        // ================= the carry: C0 of every chunk -> LDS =======================
+        const int seg_tokens = a.L * W;
+        f32x4 c0seg[2] = {zero4, zero4};
+        {
+            bool failed = false;
+            for (int pp = l; pp < p; pp += 64)
+                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp), epoch, a.ctrl + kSpinWord)) {
+                    __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    failed = true;
+                }
+            const bool bad = __builtin_amdgcn_ballot_w64(failed) != 0;
+            constexpr int NB = 8;
+            for (int p0 = 0; p0 < p; p0 += NB) {
+                f32x4 x[NB][2];
+#pragma unroll
+                for (int s2 = 0; s2 < NB; ++s2)
+                    if (p0 + s2 < p) {
+                        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.aggC + (static_cast<size_t>(bh) * a.P + p0 + s2) * 4096);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+                            x[s2][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((2 * wave + i) * 64 + l) * 16, 0, kSc1);
+                    }
+#pragma unroll
+                for (int s2 = 0; s2 < NB; ++s2)
+                    if (p0 + s2 < p) {
+                        const float scl = gp(static_cast<float>((p - 1 - (p0 + s2)) * seg_tokens));
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) c0seg[i] += scl * x[s2][i];
+                    }
+            }
+            if (bad) {  // a carry that could not be waited for: NaN, never a silently wrong number
+                const float nan = __builtin_nanf("");
+                c0seg[0] = c0seg[1] = f32x4{nan, nan, nan, nan};
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kLMaxL; ++c) {
+            if (c < Lseg) {
+                const float d1 = gp(static_cast<float>(W * c));
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    bf16x4 h, lo;
+                    split4(d1 * c0seg[i] + cpre[c][i], h, lo);
+                    // lane holds C0^T[j = 16tb+4g+e][a = 16(cb+i)+r]; tile rows a
+                    st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                    st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= output: num + e_t C0^T q_t ==============================
+        if (Lcs > 0) {
+            f32x4 acc[2][4];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                acc[0][jb] = acc[1][jb] = zero4;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 32 * ks + 8 * g;
+                    const bf16x8 ch = tr8(sm.T[8 + 2 * sc], rb, rb + 4, 16 * jb, r);
+                    const bf16x8 cl = tr8(sm.T[9 + 2 * sc], rb, rb + 4, 16 * jb, r);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        acc[i][jb] = mfma(ch, qn[i][ks], acc[i][jb]);
+                        acc[i][jb] = mfma(cl, qn[i][ks], acc[i][jb]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = t0 + 16 * i;
+                if (tt < Lcs) {
+                    const float e = gp(static_cast<float>(tt + 1));
+                    const size_t tok = head + static_cast<size_t>(c0 + sc) * W + tt;
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) {
+                        f32x4 o = num[i][jb] + e * acc[i][jb];
+                        const size_t at = tok * W + 16 * jb + 4 * g;
+                        if constexpr (OUT == kSplit) {
+                            bf16x4 h, lo;
+                            split4(o, h, lo);
+                            *reinterpret_cast<bf16x4 *>(a.oh + at) = h;
+                            *reinterpret_cast<bf16x4 *>(a.ol + at) = lo;
+                        } else {
+                            f32x4 *dst = reinterpret_cast<f32x4 *>(a.out + at);
+                            if constexpr (OUT == kAccumulate) o += *dst;
+                            __builtin_nontemporal_store(o, dst);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();  // this segment's LDS reads are done before the next one is staged
+    };
+    // segments by ticket when they wait on each other (see fwd_fast64.hip)
+    auto take = [&]() -> int {
+        int *sl = reinterpret_cast<int *>(sm.T[3]);
+        if (tid == 0) {
+            int t;
+            if constexpr (LOOP) {
+                t = static_cast<int>(
+                    __hip_atomic_fetch_add(&a.ctrl[kTicketWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            } else {
+                const int head = static_cast<int>(blockIdx.x) % a.BH;
+                uint32_t *cnt = &a.ctrl[kHeadTicketWord + kHeadTicketStride * head];
+                const int pp = static_cast<int>(__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                if (pp == a.P - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                t = pp * a.BH + head;
+            }
+            *sl = t;
+        }
+        __syncthreads();
+        const int t = __builtin_amdgcn_readfirstlane(*sl);
+        __syncthreads();
+        return t;
+    };
+    const int seg0 = a.P > 1 ? take() : static_cast<int>(blockIdx.x);
+    epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))));
+    if constexpr (LOOP) {
+        for (int seg = seg0; seg < a.segs; seg = a.P > 1 ? take() : seg + static_cast<int>(gridDim.x)) seg_body(seg);
+    } else if (seg0 < a.segs) {
+        seg_body(seg0);
+    } else if (tid == 0) {  // a ticket out of range: the control block was not zero before first use
+        __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kTicketWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// out += x, elementwise (count a multiple of 4, 16-byte aligned)
+__global__ __launch_bounds__(256) void k_add_into(float *out, const float *x, size_t n4) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    float4 o = reinterpret_cast<float4 *>(out)[i];
+    const float4 y = reinterpret_cast<const float4 *>(x)[i];
+    o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
+    reinterpret_cast<float4 *>(out)[i] = o;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct LaLayout {
+    size_t flags, aggC, total;
+};
+
+LaLayout la_layout(int BH, int P) {
+    LaLayout L{};
+    const size_t slots = static_cast<size_t>(BH) * P;
+    L.flags = 0;
+    L.aggC = align256(slots * kLWaves * kFlagStride * sizeof(uint32_t));
+    L.total = L.aggC + slots * 4096 * sizeof(float);
+    return L;
+}
+
+void la_geometry(int BH, int nc, int *P, int *L) {
+    const int target = (256 + BH - 1) / BH;
+    int l = (nc + target - 1) / target;
+    l = l < 1 ? 1 : (l > kLMaxL ? kLMaxL : l);
+    *L = l;
+    *P = (nc + l - 1) / l;
+}
+
+template <bool DECAY, bool LOOP>
+void launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode) {
+    const dim3 block(kLThreads);
+    if (mode == kSplit) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit>), grid, block, 0, st, a);
+    else if (mode == kAccumulate) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kAccumulate>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore>), grid, block, 0, st, a);
+}
+
+}  // namespace
+
+size_t la64_workspace_bytes(int BH, int n) {
+    int P, L;
+    la_geometry(BH, (n + W - 1) / W, &P, &L);
+    return la_layout(BH, P).total;
+}
+
+hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+    LaArgs a{};
+    a.H = p.H; a.n = p.n; a.nc = (p.n + W - 1) / W; a.BH = p.B * p.H;
+    la_geometry(a.BH, a.nc, &a.P, &a.L);
+    a.segs = a.BH * a.P;
+    a.q = static_cast<const uint16_t *>(p.q);
+    a.k = static_cast<const uint16_t *>(p.k);
+    a.v = static_cast<const uint16_t *>(p.v);
+    a.out = p.out; a.oh = p.oh; a.ol = p.ol;
+    a.ctrl = ctrl;
+    const LaLayout L = la_layout(a.BH, a.P);
+    char *base = static_cast<char *>(data);
+    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    a.aggC = reinterpret_cast<float *>(base + L.aggC);
+    a.gam = p.gam;
+    const int nh = p.gam.per_head ? p.H : 1;
+    bool decay = false;
+    for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const bool loop = a.segs > cus || (a.P > 1 && a.BH > kMaxTicketHeads);
+    const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
+    if (decay) {
+        if (loop) launch_la<true, true>(a, grid, st, p.mode);
+        else launch_la<true, false>(a, grid, st, p.mode);
+    } else {
+        if (loop) launch_la<false, true>(a, grid, st, p.mode);
+        else launch_la<false, false>(a, grid, st, p.mode);
+    }
+    return hipGetLastError();
+}
+
+hipError_t add_into(float *out, const float *x, size_t count, hipStream_t st) {
+    const size_t n4 = count / 4;
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_add_into, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, out, x, n4);
+    return hipGetLastError();
+}
+
+}  // namespace hla

@@ -165,6 +165,22 @@ struct HiDecodeProblem {
 };
 hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
 
+// One-launch masked first-order linear attention, bf16 q, k, v with d = dv =
+// 64 (chunk 64, every decay >= 0.75): y_t = sum_{s<=t} g^(t-s) (q_t.k_s) v_s.
+// mode 0: out = y; 1: out += y; 2: oh, ol = bf16 hi and lo of y.  The
+// workspace is a forward workspace: control block, then la64_workspace_bytes.
+struct LaProblem {
+    int B, H, n;
+    const void *q, *k, *v;
+    float *out;
+    uint16_t *oh, *ol;
+    int mode;
+    GammaTab gam;
+};
+size_t la64_workspace_bytes(int BH, int n);
+hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
+hipError_t add_into(float *out, const float *x, size_t count, hipStream_t s);
+
 hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,
                          const hla_state &r, hipStream_t s);
 

@@ -392,7 +392,7 @@ def higher_workloads(dev, stream, which):
         for c in range(copies):
             q, k, v = inputs.qkv_on_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, 5700 + c, dev)
             sets.append((q, k, v, torch.empty(w.B, w.H, w.n, w.dv, dtype=torch.float32, device=dev),
-                         torch.empty(need, dtype=torch.uint8, device=dev)))
+                         torch.zeros(need, dtype=torch.uint8, device=dev)))
 
         def call(i, third=third, g=g, sets=sets):
             q, k, v, out, ws = sets[i % len(sets)]

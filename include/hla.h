@@ -319,8 +319,14 @@ typedef struct {
     float *Fd;   /* [BH,d]    */
 } hla_third_state;
 
-/* Workspace bytes of the AHLA / third-order forward (no initialisation
- * needed; every call overwrites it); 0 for an invalid p. */
+/* Workspace bytes of the AHLA / third-order forward; 0 for an invalid p.
+ * As for hla_forward_chunked, the first 8 KB are a control block that must
+ * be zero before the workspace's first use (the one-launch kernels keep it
+ * valid from call to call; a call never clears it); the rest needs no
+ * initialisation.  bf16 calls with d = dv = 64, chunk 64, every decay >= 0.75,
+ * no denominator, ratio or state run one-launch kernels (AHLA as first-order
+ * attention applied twice, third order as second-order HLA over first-order
+ * attention values); every other call runs the chunked fp32 kernels. */
 size_t hla_ahla_workspace_size(const hla_params *p);
 size_t hla_third_workspace_size(const hla_params *p);
 

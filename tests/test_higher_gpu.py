@@ -205,11 +205,18 @@ def test_causality_nan_poison_and_errors(third):
     B, H, n, d, dv = 1, 2, 256, 64, 64
     q, k, v = on_gpu(*inputs.qkv(B, H, n, d, dv, torch.bfloat16, seed=840))
     fwd = hla.third_forward if third else hla.ahla_forward
+    # every output and denominator is written (the chunked fp32 kernels: a
+    # denominator is asked for)
     out = torch.full((B, H, n, dv), float("nan"), device=DEV)
     den = torch.full((B, H, n), float("nan"), device=DEV)
     fwd(q, k, v, out=out, den=den)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and torch.isfinite(den).all()
+    # causality, bitwise, on the numerator-only one-launch path
+    out = torch.full((B, H, n, dv), float("nan"), device=DEV)
+    fwd(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
     for t in (0, 63, 64, 200):
         q2, k2, v2 = q.clone(), k.clone(), v.clone()
         for x in (q2, k2, v2):
@@ -225,3 +232,39 @@ def test_causality_nan_poison_and_errors(third):
         out2, _, _ = hla.ahla_forward(q, k, v, **p_ridge)  # decay is fine for AHLA
         torch.cuda.synchronize()
         assert torch.isfinite(out2).all()
+
+
+ONE_LAUNCH = [  # B, H, n: the bench shape (one segment of four chunks per workgroup), ragged
+    (4, 8, 2048), (2, 3, 64 * 13 + 37),  # (14 one-chunk segments per head), a looped grid (288 segments),
+    (4, 8, 64 * 32 + 37), (1, 2, 50), (2, 1, 1)]  # one segment, one token
+
+
+@pytest.mark.parametrize("third", [False, True])
+@pytest.mark.parametrize("B,H,n", ONE_LAUNCH)
+def test_one_launch_path(third, B, H, n):
+    """bf16, d = dv = 64, chunk 64, numerator only: AHLA runs first-order
+    attention three times (the second application once on each bf16 half of
+    the intermediate values), third order runs it once and the second-order
+    kernel twice; the control block counts the launches and shows that no
+    wait gave up.  AHLA with a decay per head down to 0.75."""
+    q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=1700 + n + H + int(third))
+    g = None if third else inputs.gamma_list_fp32([(0.75, 0.9, 0.97, 1.0, 0.999, 0.8, 0.95, 0.99)[h % 8]
+                                                   for h in range(H)])
+    size_fn = hla._binding.load().hla_third_workspace_size if third else hla._binding.load().hla_ahla_workspace_size
+    p, _keep = hla._binding._params(B, H, n, 64, 64, 64, torch.bfloat16, g, 0.0, False)
+    ws = torch.zeros(int(size_fn(hla._binding.ctypes.byref(p))), dtype=torch.uint8, device=DEV)
+    fwd = hla.third_forward if third else hla.ahla_forward
+    kw = {} if third else {"gamma": g}
+    out, _, _ = fwd(*on_gpu(q, k, v), chunk=64, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    words = ws[:16].view(torch.int32).cpu().tolist()
+    assert words[2] == 3 and words[3] == 0, words
+    ro, _, _ = (higher.third_forward(q, k, v, want_state=False) if third
+                else higher.ahla_forward(q, k, v, gamma=g, want_state=False))
+    e = row_err(out.cpu(), ro)
+    print(f"row error {e:.3e}")
+    assert e <= TOL[torch.bfloat16]
+    out2, _, _ = fwd(*on_gpu(q, k, v), chunk=64, workspace=ws, **kw)  # the same workspace again
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    assert ws[:16].view(torch.int32).cpu().tolist()[2] == 6
