@@ -78,6 +78,7 @@ constexpr int kVecSlot = 128;  // floats per published vector pair (y, m)
 struct FastArgs {
     int H, n, nc, P, L, BH, segs;  // segs = BH * P
     const uint16_t *q, *k, *v;
+    const uint16_t *vl;  // VS: the values' lo half (values = v + vl)
     float *out, *den;  // den may be null
     float ridge;
     uint32_t *ctrl;   // control block (epoch, done counter, ticket, counters)
@@ -143,14 +144,18 @@ __device__ __forceinline__ float get_float(const float *slot, int idx) {
 // (a.iagg, prepared by k_fast64_init), and a final state is formed when
 // a.fin.S is set.  A state has all of S, C, m, G, h, so the STATE variants
 // carry C, m and y as the ridge and denominator variants do, whether or not
-// the ridge and denominator themselves are asked for.
-template <bool DECAY, bool LOOP, bool RIDGE, bool DEN, bool NORM, bool STATE>
+// the ridge and denominator themselves are asked for.  VS (plain numerator
+// only): the values come as a bf16 pair v + vl (an fp32 intermediate split in
+// two); products with the values take hi * x + lo * x_hi, the lo half staged
+// in T[16+c].
+template <bool DECAY, bool LOOP, bool RIDGE, bool DEN, bool NORM, bool STATE, bool VS = false>
 __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
     static_assert(!NORM || DEN, "the ratio needs the denominator");
     // the moments C and m (as the ridge needs them), and y (as the denominator does)
     constexpr bool CM = RIDGE || STATE, YV = DEN || STATE;
+    static_assert(!VS || !(CM || YV), "value pairs only for the plain numerator");
     constexpr bool MV = RIDGE && DEN;  // the query mass m only enters the ridge part of den
-    __shared__ FastSmem<CM ? 20 : 16> sm;
+    __shared__ FastSmem<(CM || VS) ? 20 : 16> sm;
     const int tid = threadIdx.x;
     // launch epoch, read by every wave: read now, first needed when the
     // segment sum is published
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
         // values follow the flag: later query loads made those variants spill.)
         // Unconditional (rows past the chunk read the head's first row), masked
         // where used.
-        u32x4 kx[2][2], qx[2][2], vx[2][2];
+        u32x4 kx[2][2], qx[2][2], vx[2][2], vlx[2][2];
         auto chunk_rows = [&](int sg_, int jj, int &Lc_, size_t &tok0_, size_t &head_) {
             const int bh_ = sg_ % a.BH, p_ = sg_ / a.BH;
             head_ = static_cast<size_t>(bh_) * a.n;
@@ -234,6 +239,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                     const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
                     const size_t src = row < Lc_ ? tok0_ + row : head_;
                     vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
+                    if constexpr (VS) vlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.vl + src * W + cg * 8);
                 }
             }
         };
@@ -412,6 +418,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             for (int u = 0; u < 2; ++u) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
                 st16(sm.T[4 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
+                if constexpr (VS) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vlx[jj][u] : z4);
             }
 
         // ---- carry = sum over earlier segments pp of g^(pw * gap) * (wave's
@@ -648,12 +655,15 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
             for (int ks = 0; ks < 2; ++ks) {
                 const int rb = 32 * ks + 8 * g;
                 const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
+                bf16x8 vtl;
+                if constexpr (VS) vtl = tr8(sm.T[16 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const bf16x8 uh = tr8(sm.T[8 + 2 * c], rb, rb + 4, 16 * (cb + i), r);
                     const bf16x8 um = tr8(sm.T[9 + 2 * c], rb, rb + 4, 16 * (cb + i), r);
                     xrun[i] = mfma(vt, uh, xrun[i]);
                     xrun[i] = mfma(vt, um, xrun[i]);
+                    if constexpr (VS) xrun[i] = mfma(vtl, uh, xrun[i]);
                     if (yw) {  // all three terms: den cancels more than num near small values
                         vrun[i] = mfma(ones, uh, vrun[i]);
                         vrun[i] = mfma(ones, um, vrun[i]);
@@ -759,9 +769,12 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (2 * ks <= 2 * HH + 1) {
-                    bf16x8 vt[4];
+                    bf16x8 vt[4], vtl[4];
 #pragma unroll
-                    for (int jb = 0; jb < 4; ++jb) vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                    for (int jb = 0; jb < 4; ++jb) {
+                        vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        if constexpr (VS) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                    }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         if (2 * ks <= 2 * HH + i) {
@@ -771,6 +784,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k_fast64(FastArgs a) {
                             for (int jb = 0; jb < 4; ++jb) {
                                 num[i][jb] = mfma(vt[jb], ph, num[i][jb]);
                                 num[i][jb] = mfma(vt[jb], pl, num[i][jb]);
+                                if constexpr (VS) num[i][jb] = mfma(vtl[jb], ph, num[i][jb]);
                             }
                         }
                     }
@@ -1142,6 +1156,10 @@ FastLayout fast_layout(int BH, int P) {
 template <bool DECAY, bool LOOP>
 void launch_fast(const FastArgs &a, dim3 grid, hipStream_t st, bool ridge, bool den, bool norm, bool state) {
     const dim3 block(kFThreads);
+    if (a.vl != nullptr) {  // values as a bf16 pair: the plain numerator only
+        hipLaunchKernelGGL((k_fast64<DECAY, LOOP, false, false, false, false, true>), grid, block, 0, st, a);
+        return;
+    }
     if (state) {  // with an initial and/or a final state: the plain numerator, or every option
         if (norm) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, true, true>), grid, block, 0, st, a);
         else if (ridge || den) hipLaunchKernelGGL((k_fast64<DECAY, LOOP, true, true, false, true>), grid, block, 0, st, a);
@@ -1191,6 +1209,7 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     a.q = static_cast<const uint16_t *>(p.q);
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
+    a.vl = static_cast<const uint16_t *>(p.vl);
     a.out = p.out;
     a.den = p.den;
     a.ridge = p.ridge;

@@ -390,13 +390,12 @@ HiLayout layout(int BH, int n, int d, int dv, int w, bool third) {
 // LA the masked first-order map (fwd_la64.hip, decay g; g = 1 for third
 // order) and HLA2 the second-order forward (k_fast64).  The intermediate
 // values Y = LA(Q, K, V) are kept as bf16 hi + lo, and both maps are linear in
-// their values, so the second map runs once on each half (AHLA: the second
-// half is added in place; third order: into a buffer added afterwards).
+// their values: the second map (first order for AHLA, second order for third
+// order) takes the pair as its values, in one launch.
 // Workspace: control block, the one-launch kernels' data (shared: every
-// launch leaves the control block valid for the next), Y hi, Y lo, and for
-// third order the fp32 buffer.
+// launch leaves the control block valid for the next), Y hi, Y lo.
 struct FastHiLayout {
-    size_t data, yh, yl, tmp, total;
+    size_t data, yh, yl, total;
 };
 
 FastHiLayout fast_layout(int BH, int n, bool third) {
@@ -406,8 +405,7 @@ FastHiLayout fast_layout(int BH, int n, bool third) {
     L.data = kCtrlBytes;
     L.yh = align256(L.data + (la > f64 ? la : f64));
     L.yl = align256(L.yh + tok * 64 * sizeof(uint16_t));
-    L.tmp = align256(L.yl + tok * 64 * sizeof(uint16_t));
-    L.total = L.tmp + (third ? tok * 64 * sizeof(float) : 0);
+    L.total = L.yl + tok * 64 * sizeof(uint16_t);
     return L;
 }
 
@@ -434,22 +432,16 @@ hipError_t fast_higher(const HiProblem &p, hipStream_t st) {
     la.v = p.v; la.oh = yh; la.ol = yl; la.mode = 2;
     hipError_t e = la64_forward(la, ctrl, data, st);
     if (e != hipSuccess) return e;
-    if (!p.third) {
+    if (!p.third) {  // the second application on the pair (hi, lo) at once
         la.oh = la.ol = nullptr; la.out = p.out;
-        la.v = yh; la.mode = 0;
-        if ((e = la64_forward(la, ctrl, data, st)) != hipSuccess) return e;
-        la.v = yl; la.mode = 1;
+        la.v = yh; la.vl = yl; la.mode = 0;
         return la64_forward(la, ctrl, data, st);
     }
-    FwdProblem f{};
+    FwdProblem f{};  // the second-order map on the pair (hi, lo) at once
     f.B = p.B; f.H = p.H; f.n = p.n; f.d = 64; f.dv = 64; f.w = 64; f.nc = (p.n + 63) / 64;
     f.dtype = HLA_BF16; f.q = p.q; f.k = p.k; f.gam = p.gam;
-    f.v = yh; f.out = p.out;
-    if ((e = fast64_forward(f, ctrl, data, st)) != hipSuccess) return e;
-    float *tmp = reinterpret_cast<float *>(base + L.tmp);
-    f.v = yl; f.out = tmp;
-    if ((e = fast64_forward(f, ctrl, data, st)) != hipSuccess) return e;
-    return add_into(p.out, tmp, static_cast<size_t>(BH) * p.n * 64, st);
+    f.v = yh; f.vl = yl; f.out = p.out;
+    return fast64_forward(f, ctrl, data, st);
 }
 
 }  // namespace

@@ -18,8 +18,11 @@
 //    sums the carry from the earlier segments' aggregates;
 //  * slice role: wave v forms the masked A^T tiles of 32 tokens of chunk v/2
 //    and the local part A V, then adds e_t C0^T q_t once the carry is in LDS.
-// Output: fp32 (stored, or added to what out holds), or the result split into
+// Output: fp32, or the result split into
 // bf16 hi = bf16(y) and lo = bf16(y - hi), ready to be values of a later pass.
+// VS: the values come as such a pair (v = hi + lo, two bf16 arrays); the
+// products with the values take hi * x + lo * x_hi (the lo * x_lo term is
+// below 2^-24 of the product).
 // Precision: A is split into bf16 hi + lo (its entries are fp32 sums), as are
 // the decayed key operand of the C sums and the carry C0.
 #include "fast64_common.h"
@@ -36,12 +39,12 @@ constexpr int kLThreads = 512;
 constexpr int kLMaxL = 4;  // chunks per segment
 constexpr int kLWaves = 8;
 
-constexpr int kStore = 0, kAccumulate = 1, kSplit = 2;  // output modes (LaProblem::mode)
+constexpr int kStore = 0, kSplit = 2;  // output modes (LaProblem::mode)
 
 struct LaArgs {
     int H, n, nc, P, L, BH, segs;
-    const uint16_t *q, *k, *v;
-    float *out;             // kStore, kAccumulate
+    const uint16_t *q, *k, *v, *vl;  // vl: the values' lo half (VS)
+    float *out;             // kStore
     uint16_t *oh, *ol;      // kSplit: bf16 hi and lo of the result
     uint32_t *ctrl;         // control block, as for the second-order kernel
     uint32_t *flags;        // [BH * P][8 waves] at kFlagStride words
@@ -49,8 +52,11 @@ struct LaArgs {
     GammaTab gam;
 };
 
+template <int NT>
 struct LaSmem {
-    __bf16 T[16][kTileElems];  // K_c in T[c], V_c in T[4+c], C0 of chunk c in T[8+2c] (hi), T[9+2c] (lo)
+    // K_c in T[c], V_c in T[4+c], C0 of chunk c in T[8+2c] (hi), T[9+2c] (lo);
+    // VS: the values' lo half in T[16+c]
+    __bf16 T[NT][kTileElems];
 };
 
 __device__ __forceinline__ void put_tiles2(const float *slot, int v, int l, const f32x4 (&x)[2]) {
@@ -59,9 +65,9 @@ __device__ __forceinline__ void put_tiles2(const float *slot, int v, int l, cons
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
 }
 
-template <bool DECAY, bool LOOP, int OUT>
+template <bool DECAY, bool LOOP, int OUT, bool VS>
 __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
-    __shared__ LaSmem sm;
+    __shared__ LaSmem<VS ? 20 : 16> sm;
     const int tid = threadIdx.x;
     uint32_t ep_raw = 0;
     if ((tid & 63) == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 
         // ---- loads: keys and values of the segment's chunks (rows past a chunk
         // read the head's first row and are zeroed when staged), queries of the slice
-        u32x4 kx[2][2], vx[2][2], qx[2][2];
+        u32x4 kx[2][2], vx[2][2], qx[2][2], vlx[2][2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * grp + jj;
@@ -109,6 +115,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 const size_t src = row < lc_of[jj] ? tok0 + row : head;
                 kx[jj][u] = *reinterpret_cast<const u32x4 *>(a.k + src * W + cg * 8);
                 vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
+                if constexpr (VS) vlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.vl + src * W + cg * 8);
             }
         }
         {
@@ -129,6 +136,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
                 st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
                 st16(sm.T[4 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
+                if constexpr (VS) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vlx[jj][u] : z4);
             }
         bf16x8 qn[2][2];
 #pragma unroll
@@ -159,11 +167,14 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
             for (int ks = 0; ks < 2; ++ks) {
                 const int rb = 32 * ks + 8 * g;
                 const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
+                bf16x8 vtl;
+                if constexpr (VS) vtl = tr8(sm.T[16 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const bf16x8 kt = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
                     if (!DECAY) {
                         crun[i] = mfma(vt, kt, crun[i]);
+                        if constexpr (VS) crun[i] = mfma(vtl, kt, crun[i]);
                     } else {
                         // f_s = g^(Lc - 1 - s) for the tokens s = 32ks + 8g + e (+4)
                         const float base = fmaf(static_cast<float>(Lc - 1), lg, lane_base(-8 * g));
@@ -177,6 +188,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                         pair_operand(x0, x1, h, lo);
                         crun[i] = mfma(vt, h, crun[i]);
                         crun[i] = mfma(vt, lo, crun[i]);
+                        if constexpr (VS) crun[i] = mfma(vtl, h, crun[i]);
                     }
                 }
             }
@@ -222,9 +234,12 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (2 * ks <= 2 * HH + 1) {
-                    bf16x8 vt[4];
+                    bf16x8 vt[4], vtl[4];
 #pragma unroll
-                    for (int jb = 0; jb < 4; ++jb) vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                    for (int jb = 0; jb < 4; ++jb) {
+                        vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        if constexpr (VS) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                    }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         if (2 * ks <= 2 * HH + i) {
@@ -234,6 +249,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                             for (int jb = 0; jb < 4; ++jb) {
                                 num[i][jb] = mfma(vt[jb], ah, num[i][jb]);
                                 num[i][jb] = mfma(vt[jb], al, num[i][jb]);
+                                if constexpr (VS) num[i][jb] = mfma(vtl[jb], ah, num[i][jb]);
                             }
                         }
                     }
@@ -330,9 +346,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                             *reinterpret_cast<bf16x4 *>(a.oh + at) = h;
                             *reinterpret_cast<bf16x4 *>(a.ol + at) = lo;
                         } else {
-                            f32x4 *dst = reinterpret_cast<f32x4 *>(a.out + at);
-                            if constexpr (OUT == kAccumulate) o += *dst;
-                            __builtin_nontemporal_store(o, dst);
+                            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(a.out + at));
                         }
                     }
                 }
@@ -382,16 +396,6 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
     }
 }
 
-// out += x, elementwise (count a multiple of 4, 16-byte aligned)
-__global__ __launch_bounds__(256) void k_add_into(float *out, const float *x, size_t n4) {
-    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= n4) return;
-    float4 o = reinterpret_cast<float4 *>(out)[i];
-    const float4 y = reinterpret_cast<const float4 *>(x)[i];
-    o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
-    reinterpret_cast<float4 *>(out)[i] = o;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct LaLayout {
@@ -418,9 +422,9 @@ void la_geometry(int BH, int nc, int *P, int *L) {
 template <bool DECAY, bool LOOP>
 void launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode) {
     const dim3 block(kLThreads);
-    if (mode == kSplit) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit>), grid, block, 0, st, a);
-    else if (mode == kAccumulate) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kAccumulate>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore>), grid, block, 0, st, a);
+    if (a.vl != nullptr) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, true>), grid, block, 0, st, a);
+    else if (mode == kSplit) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false>), grid, block, 0, st, a);
 }
 
 }  // namespace
@@ -439,6 +443,7 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     a.q = static_cast<const uint16_t *>(p.q);
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
+    a.vl = static_cast<const uint16_t *>(p.vl);
     a.out = p.out; a.oh = p.oh; a.ol = p.ol;
     a.ctrl = ctrl;
     const LaLayout L = la_layout(a.BH, a.P);
@@ -462,13 +467,6 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
         if (loop) launch_la<false, true>(a, grid, st, p.mode);
         else launch_la<false, false>(a, grid, st, p.mode);
     }
-    return hipGetLastError();
-}
-
-hipError_t add_into(float *out, const float *x, size_t count, hipStream_t st) {
-    const size_t n4 = count / 4;
-    if (n4 == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_add_into, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, out, x, n4);
     return hipGetLastError();
 }
 

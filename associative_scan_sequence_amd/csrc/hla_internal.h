@@ -29,6 +29,7 @@ struct FwdProblem {
     float ridge;
     int normalize;
     const void *q, *k, *v;
+    const void *vl;    // one-launch d = 64 kernel, plain numerator only: the values are v + vl (a bf16 pair)
     float *out, *den;  // den may be null
     hla_state init;    // init.S == nullptr: zero state
     hla_state fin;     // fin.S == nullptr: not requested
@@ -167,11 +168,12 @@ hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
 
 // One-launch masked first-order linear attention, bf16 q, k, v with d = dv =
 // 64 (chunk 64, every decay >= 0.75): y_t = sum_{s<=t} g^(t-s) (q_t.k_s) v_s.
-// mode 0: out = y; 1: out += y; 2: oh, ol = bf16 hi and lo of y.  The
-// workspace is a forward workspace: control block, then la64_workspace_bytes.
+// mode 0: out = y; 2: oh, ol = bf16 hi and lo of y.  vl set:
+// the values are v + vl (a hi/lo pair) and mode must be 0.  The workspace is a
+// forward workspace: control block, then la64_workspace_bytes.
 struct LaProblem {
     int B, H, n;
-    const void *q, *k, *v;
+    const void *q, *k, *v, *vl;
     float *out;
     uint16_t *oh, *ol;
     int mode;
@@ -179,7 +181,6 @@ struct LaProblem {
 };
 size_t la64_workspace_bytes(int BH, int n);
 hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
-hipError_t add_into(float *out, const float *x, size_t count, hipStream_t s);
 
 hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,
                          const hla_state &r, hipStream_t s);
