@@ -1,11 +1,14 @@
 // fwd_la64.hip -- one-launch masked first-order (causal) linear attention
-// for d = dv = 64, chunk 64, bf16 q/k/v on gfx950 MFMA:
-//   y_t = sum_{s <= t} g^(t - s) (q_t . k_s) v_s.
+// for d = dv = 64, chunk 64, bf16 operands on gfx950 MFMA:
+//   y_t = sum_{s <= t} g^(t - s) (q_t . k_s) v_s          (REV: s >= t, g^(s - t)).
 // The asymmetric variant (AHLA) is this map applied twice, and masked third
 // order is second-order HLA over values that this map has mixed (Higher-order
 // Linear Attention, paperlayer.ai summary sec. 6 and 7; the decompositions
 // are pinned on the CPU in tests/test_higher_oracle.py), so both are built
-// from it where their inputs allow.
+// from it where their inputs allow.  The gradient of the second-order
+// numerator is a sum of such maps, forward and reverse in time (sec. 4: the
+// reverse-mode scan; the identity is pinned in tests/test_backward_algebra.py),
+// so the backward is built from it too (bwd_la64.hip).
 //
 // Per chunk (local t, s; L tokens; e_t = g^(t+1), f_s = g^(L-1-s)), with the
 // carry C0 = sum over earlier tokens of g^(distance to the chunk start - 1) k v^T:
@@ -18,11 +21,13 @@
 //    sums the carry from the earlier segments' aggregates;
 //  * slice role: wave v forms the masked A^T tiles of 32 tokens of chunk v/2
 //    and the local part A V, then adds e_t C0^T q_t once the carry is in LDS.
-// Output: fp32, or the result split into
-// bf16 hi = bf16(y) and lo = bf16(y - hi), ready to be values of a later pass.
-// VS: the values come as such a pair (v = hi + lo, two bf16 arrays); the
-// products with the values take hi * x + lo * x_hi (the lo * x_lo term is
-// below 2^-24 of the product).
+// Output: fp32 (stored, or added to what out holds), or the result split into
+// bf16 hi = bf16(y) and lo = bf16(y - hi), ready to be an operand of a later
+// map.  QP, KP, VP: the queries, keys or values come as such a pair (x = hi +
+// lo, two bf16 arrays; not keys and values both); a product with a pair takes
+// hi * y + lo * y_hi (the dropped lo * y_lo is about 2^-16 of the product).
+// REV: the map runs on the reversed sequence (token t read and written at
+// n - 1 - t), which is the reverse-time map.
 // Precision: A is split into bf16 hi + lo (its entries are fp32 sums), as are
 // the decayed key operand of the C sums and the carry C0.
 #include "fast64_common.h"
@@ -39,23 +44,25 @@ constexpr int kLThreads = 512;
 constexpr int kLMaxL = 4;  // chunks per segment
 constexpr int kLWaves = 8;
 
-constexpr int kStore = 0, kSplit = 2;  // output modes (LaProblem::mode)
+constexpr int kStore = 0, kAccumulate = 1, kSplit = 2;  // output modes (LaProblem::mode)
 
 struct LaArgs {
     int H, n, nc, P, L, BH, segs;
-    const uint16_t *q, *k, *v, *vl;  // vl: the values' lo half (VS)
-    float *out;             // kStore
+    const uint16_t *q, *k, *v;
+    const uint16_t *ql, *kl, *vl;  // the lo halves of paired operands (QP, KP, VP)
+    float *out;             // kStore, kAccumulate
     uint16_t *oh, *ol;      // kSplit: bf16 hi and lo of the result
     uint32_t *ctrl;         // control block, as for the second-order kernel
     uint32_t *flags;        // [BH * P][8 waves] at kFlagStride words
     float *aggC;            // [BH * P][16 tiles][64 lanes][4]
     GammaTab gam;
+    float gexp;             // the decay per token is g^gexp (1, or 2 for the squared decay)
 };
 
 template <int NT>
 struct LaSmem {
     // K_c in T[c], V_c in T[4+c], C0 of chunk c in T[8+2c] (hi), T[9+2c] (lo);
-    // VS: the values' lo half in T[16+c]
+    // KP or VP: the keys' or values' lo half in T[16+c]
     __bf16 T[NT][kTileElems];
 };
 
@@ -65,9 +72,10 @@ __device__ __forceinline__ void put_tiles2(const float *slot, int v, int l, cons
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
 }
 
-template <bool DECAY, bool LOOP, int OUT, bool VS>
+template <bool DECAY, bool LOOP, int OUT, bool QP, bool KP, bool VP, bool REV>
 __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
-    __shared__ LaSmem<VS ? 20 : 16> sm;
+    static_assert(!(KP && VP), "the lo halves of keys and values share four tiles");
+    __shared__ LaSmem<(KP || VP) ? 20 : 16> sm;
     const int tid = threadIdx.x;
     uint32_t ep_raw = 0;
     if ((tid & 63) == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -87,8 +95,10 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
         const int t0 = 32 * hh + r;
         const int tb = wave >> 1, cb = 2 * (wave & 1);
         const int bh = seg % a.BH, p = seg / a.BH;
-        lg = DECAY ? log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
+        lg = DECAY ? a.gexp * log2f(head_gamma(a.gam, bh % a.H)) : 0.0f;
         const size_t head = static_cast<size_t>(bh) * a.n;
+        // the head's token at position pos of the (possibly reversed) sequence
+        auto at_pos = [&](int pos) { return head + static_cast<size_t>(REV ? a.n - 1 - pos : pos); };
         const int c0 = p * a.L;
         const int Lseg = min(a.L, a.nc - c0);
         auto chunk_len = [&](int j) { return min(W, a.n - (c0 + j) * W); };
@@ -104,31 +114,29 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 
         // ---- loads: keys and values of the segment's chunks (rows past a chunk
         // read the head's first row and are zeroed when staged), queries of the slice
-        u32x4 kx[2][2], vx[2][2], qx[2][2], vlx[2][2];
+        u32x4 kx[2][2], vx[2][2], qx[2][2], xlx[2][2], qlx[2][2];  // xlx: lo half of keys or values
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * grp + jj;
-            const size_t tok0 = head + static_cast<size_t>(c0 + j) * W;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
-                const size_t src = row < lc_of[jj] ? tok0 + row : head;
+                const size_t src = row < lc_of[jj] ? at_pos((c0 + j) * W + row) : head;
                 kx[jj][u] = *reinterpret_cast<const u32x4 *>(a.k + src * W + cg * 8);
                 vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
-                if constexpr (VS) vlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.vl + src * W + cg * 8);
+                if constexpr (KP) xlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.kl + src * W + cg * 8);
+                if constexpr (VP) xlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.vl + src * W + cg * 8);
             }
         }
-        {
-            const size_t tok0 = head + static_cast<size_t>(c0 + sc) * W;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int tt = t0 + 16 * i;
-                    const size_t src = tt < Lcs ? tok0 + tt : head;
-                    qx[i][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
-                }
-        }
+            for (int ks = 0; ks < 2; ++ks) {
+                const int tt = t0 + 16 * i;
+                const size_t src = tt < Lcs ? at_pos((c0 + sc) * W + tt) : head;
+                qx[i][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
+                if constexpr (QP) qlx[i][ks] = *reinterpret_cast<const u32x4 *>(a.ql + src * W + 32 * ks + 8 * g);
+            }
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -136,13 +144,16 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
                 st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
                 st16(sm.T[4 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
-                if constexpr (VS) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vlx[jj][u] : z4);
+                if constexpr (KP || VP) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? xlx[jj][u] : z4);
             }
-        bf16x8 qn[2][2];
+        bf16x8 qn[2][2], qnl[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
+            for (int ks = 0; ks < 2; ++ks) {
+                qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
+                if constexpr (QP) qnl[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qlx[i][ks] : z4);
+            }
         __syncthreads();
 
         auto lane_base = [&](int off) __attribute__((always_inline)) {
@@ -168,13 +179,16 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 const int rb = 32 * ks + 8 * g;
                 const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
                 bf16x8 vtl;
-                if constexpr (VS) vtl = tr8(sm.T[16 + c], rb, rb + 4, 16 * tb, r);
+                if constexpr (VP) vtl = tr8(sm.T[16 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const bf16x8 kt = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
+                    bf16x8 ktl;
+                    if constexpr (KP) ktl = tr8(sm.T[16 + c], rb, rb + 4, 16 * (cb + i), r);
                     if (!DECAY) {
                         crun[i] = mfma(vt, kt, crun[i]);
-                        if constexpr (VS) crun[i] = mfma(vtl, kt, crun[i]);
+                        if constexpr (VP) crun[i] = mfma(vtl, kt, crun[i]);
+                        if constexpr (KP) crun[i] = mfma(vt, ktl, crun[i]);
                     } else {
                         // f_s = g^(Lc - 1 - s) for the tokens s = 32ks + 8g + e (+4)
                         const float base = fmaf(static_cast<float>(Lc - 1), lg, lane_base(-8 * g));
@@ -188,7 +202,18 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                         pair_operand(x0, x1, h, lo);
                         crun[i] = mfma(vt, h, crun[i]);
                         crun[i] = mfma(vt, lo, crun[i]);
-                        if constexpr (VS) crun[i] = mfma(vtl, h, crun[i]);
+                        if constexpr (VP) crun[i] = mfma(vtl, h, crun[i]);
+                        if constexpr (KP) {  // the decayed lo half, rounded once: its own lo is ~2^-16 of the product
+                            f32x4 y0, y1;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                y0[e] = gpl(fmaf(static_cast<float>(-(32 * ks + e)), lg, base)) * static_cast<float>(ktl[e]);
+                                y1[e] = gpl(fmaf(static_cast<float>(-(32 * ks + 4 + e)), lg, base)) * static_cast<float>(ktl[4 + e]);
+                            }
+                            bf16x8 hl, ll;
+                            pair_operand(y0, y1, hl, ll);
+                            crun[i] = mfma(vt, hl, crun[i]);
+                        }
                     }
                 }
             }
@@ -215,10 +240,17 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 at[0][ib] = at[1][ib] = zero4;
                 if (ib <= 2 * HH + 1) {
                     const bf16x8 k0 = ld8(sm.T[sc], 16 * ib + r, 8 * g), k1 = ld8(sm.T[sc], 16 * ib + r, 32 + 8 * g);
+                    bf16x8 k0l, k1l;
+                    if constexpr (KP) {
+                        k0l = ld8(sm.T[16 + sc], 16 * ib + r, 8 * g);
+                        k1l = ld8(sm.T[16 + sc], 16 * ib + r, 32 + 8 * g);
+                    }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         if (ib <= 2 * HH + i) {
                             at[i][ib] = mfma(k1, qn[i][1], mfma(k0, qn[i][0], zero4));
+                            if constexpr (QP) at[i][ib] = mfma(k1, qnl[i][1], mfma(k0, qnl[i][0], at[i][ib]));
+                            if constexpr (KP) at[i][ib] = mfma(k1l, qn[i][1], mfma(k0l, qn[i][0], at[i][ib]));
                             // g^(t - s), t = 32HH + 16i + r, s = 16ib + 4g + e; s > t only in the diagonal tile
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -238,7 +270,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
                         vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
-                        if constexpr (VS) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        if constexpr (VP) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
                     }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -249,7 +281,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                             for (int jb = 0; jb < 4; ++jb) {
                                 num[i][jb] = mfma(vt[jb], ah, num[i][jb]);
                                 num[i][jb] = mfma(vt[jb], al, num[i][jb]);
-                                if constexpr (VS) num[i][jb] = mfma(vtl[jb], ah, num[i][jb]);
+                                if constexpr (VP) num[i][jb] = mfma(vtl[jb], ah, num[i][jb]);
                             }
                         }
                     }
@@ -327,6 +359,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                     for (int i = 0; i < 2; ++i) {
                         acc[i][jb] = mfma(ch, qn[i][ks], acc[i][jb]);
                         acc[i][jb] = mfma(cl, qn[i][ks], acc[i][jb]);
+                        if constexpr (QP) acc[i][jb] = mfma(ch, qnl[i][ks], acc[i][jb]);
                     }
                 }
             }
@@ -335,7 +368,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 const int tt = t0 + 16 * i;
                 if (tt < Lcs) {
                     const float e = gp(static_cast<float>(tt + 1));
-                    const size_t tok = head + static_cast<size_t>(c0 + sc) * W + tt;
+                    const size_t tok = at_pos((c0 + sc) * W + tt);
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
                         f32x4 o = num[i][jb] + e * acc[i][jb];
@@ -346,7 +379,9 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                             *reinterpret_cast<bf16x4 *>(a.oh + at) = h;
                             *reinterpret_cast<bf16x4 *>(a.ol + at) = lo;
                         } else {
-                            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(a.out + at));
+                            f32x4 *dst = reinterpret_cast<f32x4 *>(a.out + at);
+                            if constexpr (OUT == kAccumulate) o += *dst;
+                            __builtin_nontemporal_store(o, dst);
                         }
                     }
                 }
@@ -419,12 +454,31 @@ void la_geometry(int BH, int nc, int *P, int *L) {
     *P = (nc + l - 1) / l;
 }
 
+// the operand/direction/output combinations the library uses
 template <bool DECAY, bool LOOP>
-void launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode) {
+hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode, bool rev) {
     const dim3 block(kLThreads);
-    if (a.vl != nullptr) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, true>), grid, block, 0, st, a);
-    else if (mode == kSplit) hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false>), grid, block, 0, st, a);
+    const bool qp = a.ql != nullptr, kp = a.kl != nullptr, vp = a.vl != nullptr;
+    const int key = (qp ? 1 : 0) | (kp ? 2 : 0) | (vp ? 4 : 0) | (rev ? 8 : 0) | (mode << 4);
+    switch (key) {
+        // forward, plain operands: split output (AHLA, third order, backward U) or fp32
+        case (kSplit << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit, false, false, false, false>), grid, block, 0, st, a); break;
+        case (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false, false, false, false>), grid, block, 0, st, a); break;
+        // forward, paired values, fp32 (AHLA's second map)
+        case 4 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false, false, true, false>), grid, block, 0, st, a); break;
+        // backward: W = reverse, paired keys, split output
+        case 2 | 8 | (kSplit << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit, false, true, false, true>), grid, block, 0, st, a); break;
+        // dQ: forward, paired queries and values (store); forward, paired queries (accumulate)
+        case 1 | 4 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, true, false, true, false>), grid, block, 0, st, a); break;
+        case 1 | (kAccumulate << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kAccumulate, true, false, false, false>), grid, block, 0, st, a); break;
+        // dK: reverse, paired values (store); reverse, paired keys (accumulate)
+        case 4 | 8 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false, false, true, true>), grid, block, 0, st, a); break;
+        case 2 | 8 | (kAccumulate << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kAccumulate, false, true, false, true>), grid, block, 0, st, a); break;
+        // dV: reverse, paired queries and values (store)
+        case 1 | 4 | 8 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, true, false, true, true>), grid, block, 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -435,6 +489,12 @@ size_t la64_workspace_bytes(int BH, int n) {
     return la_layout(BH, P).total;
 }
 
+size_t la64_flag_bytes(int BH, int n) {
+    int P, L;
+    la_geometry(BH, (n + W - 1) / W, &P, &L);
+    return la_layout(BH, P).aggC;
+}
+
 hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
     LaArgs a{};
     a.H = p.H; a.n = p.n; a.nc = (p.n + W - 1) / W; a.BH = p.B * p.H;
@@ -443,6 +503,8 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     a.q = static_cast<const uint16_t *>(p.q);
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
+    a.ql = static_cast<const uint16_t *>(p.ql);
+    a.kl = static_cast<const uint16_t *>(p.kl);
     a.vl = static_cast<const uint16_t *>(p.vl);
     a.out = p.out; a.oh = p.oh; a.ol = p.ol;
     a.ctrl = ctrl;
@@ -451,6 +513,7 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
     a.aggC = reinterpret_cast<float *>(base + L.aggC);
     a.gam = p.gam;
+    a.gexp = p.gsq ? 2.0f : 1.0f;
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
@@ -460,14 +523,8 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     if (e != hipSuccess) return e;
     const bool loop = a.segs > cus || (a.P > 1 && a.BH > kMaxTicketHeads);
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
-    if (decay) {
-        if (loop) launch_la<true, true>(a, grid, st, p.mode);
-        else launch_la<true, false>(a, grid, st, p.mode);
-    } else {
-        if (loop) launch_la<false, true>(a, grid, st, p.mode);
-        else launch_la<false, false>(a, grid, st, p.mode);
-    }
-    return hipGetLastError();
+    if (decay) return loop ? launch_la<true, true>(a, grid, st, p.mode, p.rev) : launch_la<true, false>(a, grid, st, p.mode, p.rev);
+    return loop ? launch_la<false, true>(a, grid, st, p.mode, p.rev) : launch_la<false, false>(a, grid, st, p.mode, p.rev);
 }
 
 }  // namespace hla

@@ -334,7 +334,7 @@ size_t hla_backward_workspace_size(const hla_params *p) {
     if (forward_geometry(p, &geo) != HLA_OK) return 0;
     if (!width_ok(p->d) || !width_ok(p->dv) || !dtype_ok(p)) return 0;
     if (p->n == 0) return 0;
-    return hla::generic_backward_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w);
+    return hla::backward_workspace_bytes(p->B * p->H, p->n, p->d, p->dv, geo.w);
 }
 
 hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
@@ -387,7 +387,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
         if (!req[i]) return fail(HLA_ERR_INVALID_ARGUMENT, "%s is NULL", nm[i]);
         if (!aligned16(req[i])) return fail(HLA_ERR_ALIGNMENT, "%s is not 16-byte aligned", nm[i]);
     }
-    const size_t need = hla::generic_backward_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
+    const size_t need = hla::backward_workspace_bytes(int(BH), p->n, p->d, p->dv, geo.w);
     if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
         return fail(HLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -417,7 +417,7 @@ hla_status hla_backward_chunked(const hla_params *p, const void *q, const void *
     bp.dout = dout; bp.dq = dq; bp.dk = dk; bp.dv = dv;
     if (dinit) bp.dinit = *dinit;
     if (dfinal) bp.dfinal = *dfinal;
-    const hipError_t e = hla::generic_backward(bp, stream);
+    const hipError_t e = hla::la_backward_eligible(bp) ? hla::la_backward(bp, stream) : hla::generic_backward(bp, stream);
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -72,6 +72,14 @@ struct BwdProblem {
 };
 size_t generic_backward_workspace_bytes(int BH, int n, int d, int dv, int w);
 hipError_t generic_backward(const BwdProblem &p, hipStream_t s);
+// The plain-numerator backward as first-order maps (bwd_la64.hip): bf16,
+// d = dv = w = 64, no ridge, ratio or states, every decay >= 0.75.
+bool la_backward_eligible(const BwdProblem &p);
+size_t la_backward_workspace_bytes(int BH, int n);
+hipError_t la_backward(const BwdProblem &p, hipStream_t s);
+// Workspace bytes of hla_backward_chunked: the larger of the two paths' needs
+// when both can serve these widths.
+size_t backward_workspace_bytes(int BH, int n, int d, int dv, int w);
 // Writes zeros into every part of s that is set (the initial-state gradient
 // of an empty sequence).
 hipError_t zero_state_grad(const hla_state &s, int BH, int d, int dv, hipStream_t st);
@@ -167,19 +175,25 @@ struct HiDecodeProblem {
 hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
 
 // One-launch masked first-order linear attention, bf16 q, k, v with d = dv =
-// 64 (chunk 64, every decay >= 0.75): y_t = sum_{s<=t} g^(t-s) (q_t.k_s) v_s.
-// mode 0: out = y; 2: oh, ol = bf16 hi and lo of y.  vl set:
-// the values are v + vl (a hi/lo pair) and mode must be 0.  The workspace is a
-// forward workspace: control block, then la64_workspace_bytes.
+// 64 (chunk 64, every decay >= 0.75): y_t = sum_{s<=t} g^(t-s) (q_t.k_s) v_s,
+// or with rev the reverse-time map (s >= t, g^(s-t)).  mode 0: out = y; 1:
+// out += y; 2: oh, ol = bf16 hi and lo of y.  ql, kl, vl set: that operand is
+// the bf16 pair (x, xl).  Only the combinations listed in la64_forward are
+// built (hipErrorInvalidValue otherwise).  The workspace is a forward
+// workspace: control block, then la64_workspace_bytes.
 struct LaProblem {
     int B, H, n;
-    const void *q, *k, *v, *vl;
+    const void *q, *k, *v;
+    const void *ql, *kl, *vl;
     float *out;
     uint16_t *oh, *ol;
     int mode;
+    bool rev;
+    bool gsq;      // the decay per token is g^2 (g from gam)
     GammaTab gam;
 };
 size_t la64_workspace_bytes(int BH, int n);
+size_t la64_flag_bytes(int BH, int n);  // the leading part of that data holding the flags
 hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
 
 hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,

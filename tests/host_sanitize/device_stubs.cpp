@@ -30,6 +30,10 @@ hipError_t generic_forward(const FwdProblem &, hipStream_t) { reached("generic_f
 size_t generic_backward_workspace_bytes(int BH, int n, int d, int dv, int) { return 2 * fixed_size(BH, n, d, dv); }
 hipError_t generic_backward(const BwdProblem &, hipStream_t) { reached("generic_backward"); }
 hipError_t zero_state_grad(const hla_state &, int, int, int, hipStream_t) { reached("zero_state_grad"); }
+bool la_backward_eligible(const BwdProblem &) { return false; }
+size_t la_backward_workspace_bytes(int BH, int n) { return fixed_size(BH, n, 64, 64); }
+hipError_t la_backward(const BwdProblem &, hipStream_t) { reached("la_backward"); }
+size_t backward_workspace_bytes(int BH, int n, int d, int dv, int w) { return generic_backward_workspace_bytes(BH, n, d, dv, w); }
 hla_status noalloc_scratch(void **) { reached("noalloc_scratch"); }
 bool fast64_supported(const FwdProblem &) { return false; }
 size_t fast64_workspace_bytes(int BH, int n) { return fixed_size(BH, n, 64, 64); }

@@ -133,3 +133,39 @@ def test_chunked_backward_matches_oracle(n, w, g, lam, norm):
     for x, y in zip(got, ref):
         y = y[0, 0]
         assert np.abs(x - y).max() <= 1e-11 * max(1.0, np.abs(y).max())
+
+
+# ------------------------------------------------------------------------------
+# The plain-numerator gradient as masked first-order maps, the form the
+# one-launch backward runs: with LA(A, B, C; r)_t = sum_{s<=t} r^(t-s) (a_t.b_s) c_s
+# and LA^rev the same over s >= t with r^(s-t),
+#   U = LA(Q, K, K; g),  W = LA^rev(V, dO, Q; g^2)
+#   dq = LA(dO, V, U; g^2) + LA(W, K, K; g)
+#   dk = LA^rev(K, Q, W; g) + LA^rev(K, W, Q; g)
+#   dv = LA^rev(U, Q, dO; g^2)
+# (each a rearrangement of the sums above for lam = 0 and dnum = dout).
+
+def _la(a, b, c, r):
+    n = a.shape[0]
+    t = np.arange(n)
+    D = np.where(t[:, None] >= t[None, :], float(r) ** np.clip(t[:, None] - t[None, :], 0, None), 0.0)
+    return ((a @ b.T) * D) @ c
+
+
+def _la_rev(a, b, c, r):
+    return _la(a[::-1], b[::-1], c[::-1], r)[::-1]
+
+
+@pytest.mark.parametrize("n,d,dv,g", [(37, 5, 4, 1.0), (50, 6, 6, 0.9), (23, 3, 7, 0.75)])
+def test_plain_gradient_is_first_order_maps(n, d, dv, g):
+    r = np.random.default_rng(n + d)
+    q, k, v = r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, dv))
+    dout = r.standard_normal((n, dv))
+    dq, dk, dvv = (np.asarray(x)[0, 0] for x in
+                   ob.backward(q[None, None], k[None, None], v[None, None], dout[None, None], gamma=[g])[:3])
+    U = _la(q, k, k, g)
+    Wm = _la_rev(v, dout, q, g * g)
+    rel = lambda a, b: np.max(np.abs(a - b)) / np.max(np.abs(b))  # noqa: E731
+    assert rel(_la(dout, v, U, g * g) + _la(Wm, k, k, g), dq) < 1e-12
+    assert rel(_la_rev(k, q, Wm, g) + _la_rev(k, Wm, q, g), dk) < 1e-12
+    assert rel(_la_rev(U, q, dout, g * g), dvv) < 1e-12

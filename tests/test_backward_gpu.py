@@ -1,10 +1,14 @@
 """GPU parity of the backward (hla_backward_chunked through the C ABI) against
 the fp64 autograd oracle (oracle/backward.py) on identical seeded inputs.
 
-The backward computes in fp32 from exactly widened inputs, so bf16 and fp32
-inputs share one gate: slab error (per (b, h), max |x - ref| / max |ref|)
-of each gradient at most 1e-5 (fp32 accumulation over a few hundred terms
-of mixed sign; see the tolerance reading in the design notes).  With the
+The chunked backward computes in fp32 from exactly widened inputs, so bf16
+and fp32 inputs share one gate: slab error (per (b, h), max |x - ref| /
+max |ref|) of each gradient at most 1e-5 (fp32 accumulation over a few
+hundred terms of mixed sign; see the tolerance reading in the design notes).
+bf16 calls with d = dv = 64, chunk 64, no ridge, ratio or states and every
+decay >= 0.75 take the one-launch backward instead (first-order maps on bf16
+MFMA, fp32 intermediates carried as bf16 pairs); its gate is FTOL
+(tests/test_backward_fast_gpu.py).  With the
 ratio, q and k are drawn positive (|x| + 0.1 of the seeded draws) so that
 every denominator is bounded away from zero.
 """
@@ -21,6 +25,12 @@ from parity import row_err, slab_err
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 GTOL = 1e-5
+FTOL = 1e-4  # the one-launch backward (bf16 pairs: products to about 2^-16)
+
+
+def fast_path(dtype, d, dv, chunk, gk, lam, norm):
+    return (dtype == torch.bfloat16 and d == dv == 64 and chunk == 64 and lam == 0.0 and not norm
+            and gk in (None, "decay", "per_head"))
 
 
 @pytest.fixture(autouse=True)
@@ -54,14 +64,14 @@ def run_gpu(q, k, v, dout, g, lam, norm, chunk):
     return [x.cpu() for x in out]
 
 
-def check(got, ref, names=("dq", "dk", "dv")):
+def check(got, ref, names=("dq", "dk", "dv"), tol=GTOL):
     errs = {}
     for name, x, r in zip(names, got, ref):
         e = slab_err(x, r, lead=2)
         errs[name] = e
         print(f"{name}: slab {e:.3e} row {row_err(x, r):.3e}")
     for name, e in errs.items():
-        assert e <= GTOL, f"{name}: slab error {e:.3e} > {GTOL:.0e}"
+        assert e <= tol, f"{name}: slab error {e:.3e} > {tol:.0e}"
 
 
 CASES = [
@@ -89,7 +99,7 @@ def test_backward_matches_oracle(case):
     got = run_gpu(q, k, v, dout, g, lam, norm, chunk)
     from oracle import backward as ob
     ref = ob.backward(q, k, v, dout, g, lam, norm)
-    check(got, ref)
+    check(got, ref, tol=FTOL if fast_path(dtype, d, dv, chunk, gk, lam, norm) else GTOL)
 
 
 def test_backward_headline_shape_sampled_heads():
@@ -103,7 +113,7 @@ def test_backward_headline_shape_sampled_heads():
     for b, h in ((0, 0), (3, 7)):
         sl = lambda x: x[b:b + 1, h:h + 1]  # noqa: E731
         ref = ob.backward(sl(q), sl(k), sl(v), sl(dout))
-        check([sl(x) for x in got], ref)
+        check([sl(x) for x in got], ref, tol=FTOL)  # the one-launch backward
 
 
 def test_backward_deterministic_and_causal():
