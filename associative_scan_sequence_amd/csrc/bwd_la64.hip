@@ -13,13 +13,16 @@
 //   dv  = LA^rev (U, Q, dO; g^2)
 // where LA (A, B, C; r)_t = sum_{s<=t} r^(t-s) (a_t . b_s) c_s and LA^rev the
 // same over s >= t with r^(s-t).  dO, U and W are fp32; they enter the maps
-// as bf16 pairs (hi = bf16(x), lo = bf16(x - hi)).
+// as bf16 pairs (hi = bf16(x), lo = bf16(x - hi)): dO split as it is staged,
+// U and W written as pairs by the maps that form them.  U and the second part
+// of dq share their keys, values and decay, so they are one launch with two
+// sets of queries, and the two maps of dk are one launch whose carry is
+// symmetric: five launches in all.
 //
 // Workspace: the first kCtrlBytes are the one-launch kernels' control block,
-// then their flags and aggregates, then the pairs of dO, U and W.  The call
-// clears the control block and the flags itself (a fill kernel), so the
-// backward workspace needs no initialisation, as for the chunked path.
-#include "bf16_split.h"
+// then their flags and aggregates, then the pairs of U and W.  The call clears
+// the control block and the flags itself (a fill kernel), so the backward
+// workspace needs no initialisation, as for the chunked path.
 #include "device_common.h"
 #include "hla_internal.h"
 
@@ -33,30 +36,17 @@ __global__ __launch_bounds__(256) void k_zero_words(uint32_t *p, size_t n) {
         p[i] = 0u;
 }
 
-// x (fp32) -> the bf16 pair (hi, lo), four values per thread
-__global__ __launch_bounds__(256) void k_split_pair(const float *x, uint16_t *hi, uint16_t *lo, size_t n4) {
-    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= n4) return;
-    const float4 v = reinterpret_cast<const float4 *>(x)[i];
-    bf16x4 h, l;
-    split4(f32x4{v.x, v.y, v.z, v.w}, h, l);
-    reinterpret_cast<bf16x4 *>(hi)[i] = h;
-    reinterpret_cast<bf16x4 *>(lo)[i] = l;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLaLayout {
-    size_t data, doh, dol, uh, ul, wh, wl, total;
+    size_t data, uh, ul, wh, wl, total;
 };
 
 BwdLaLayout bwd_la_layout(int BH, int n) {
     const size_t pair = static_cast<size_t>(BH) * n * kBw * sizeof(uint16_t);
     BwdLaLayout L{};
     L.data = kCtrlBytes;
-    L.doh = align256(L.data + la64_workspace_bytes(BH, n));
-    L.dol = align256(L.doh + pair);
-    L.uh = align256(L.dol + pair);
+    L.uh = align256(L.data + la64_workspace_bytes(BH, n));
     L.ul = align256(L.uh + pair);
     L.wh = align256(L.ul + pair);
     L.wl = align256(L.wh + pair);
@@ -94,8 +84,7 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
     uint32_t *ctrl = reinterpret_cast<uint32_t *>(base);
     void *data = base + L.data;
     auto pair = [&](size_t off) { return reinterpret_cast<uint16_t *>(base + off); };
-    uint16_t *doh = pair(L.doh), *dol = pair(L.dol), *uh = pair(L.uh), *ul = pair(L.ul), *wh = pair(L.wh),
-             *wl = pair(L.wl);
+    uint16_t *uh = pair(L.uh), *ul = pair(L.ul), *wh = pair(L.wh), *wl = pair(L.wl);
     // the control block and the flags start clear (every launch below then
     // leaves them valid for the next)
     const size_t words = (kCtrlBytes + la64_flag_bytes(BH, f.n)) / sizeof(uint32_t);
@@ -103,29 +92,28 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
                        dim3(256), 0, st, ctrl, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t n4 = static_cast<size_t>(BH) * f.n * kBw / 4;
-    hipLaunchKernelGGL(k_split_pair, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, p.dout, doh, dol,
-                       n4);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    auto la = [&](const void *q, const void *ql, const void *k, const void *kl, const void *v, const void *vl,
-                  bool rev, bool gsq, int mode, float *out, uint16_t *oh, uint16_t *ol) {
-        LaProblem m{};
+    auto map = [&](LaProblem m, bool rev, bool gsq) {
         m.B = f.B; m.H = f.H; m.n = f.n; m.gam = f.gam;
-        m.q = q; m.ql = ql; m.k = k; m.kl = kl; m.v = v; m.vl = vl;
-        m.rev = rev; m.gsq = gsq; m.mode = mode; m.out = out; m.oh = oh; m.ol = ol;
+        m.rev = rev; m.gsq = gsq;
         return la64_forward(m, ctrl, data, st);
     };
-    // U = LA (Q, K, K; g), W = LA^rev (V, dO, Q; g^2), both as pairs
-    if ((e = la(f.q, nullptr, f.k, nullptr, f.k, nullptr, false, false, 2, nullptr, uh, ul)) != hipSuccess) return e;
-    if ((e = la(f.v, nullptr, doh, dol, f.q, nullptr, true, true, 2, nullptr, wh, wl)) != hipSuccess) return e;
-    // dq = LA (dO, V, U; g^2) + LA (W, K, K; g)
-    if ((e = la(doh, dol, f.v, nullptr, uh, ul, false, true, 0, p.dq, nullptr, nullptr)) != hipSuccess) return e;
-    if ((e = la(wh, wl, f.k, nullptr, f.k, nullptr, false, false, 1, p.dq, nullptr, nullptr)) != hipSuccess) return e;
-    // dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g)
-    if ((e = la(f.k, nullptr, f.q, nullptr, wh, wl, true, false, 0, p.dk, nullptr, nullptr)) != hipSuccess) return e;
-    if ((e = la(f.k, nullptr, wh, wl, f.q, nullptr, true, false, 1, p.dk, nullptr, nullptr)) != hipSuccess) return e;
+    LaProblem m{};
+    // W = LA^rev (V, dO, Q; g^2), as a pair
+    m = LaProblem{}; m.q = f.v; m.kf = p.dout; m.v = f.q; m.mode = 2; m.oh = wh; m.ol = wl;
+    if ((e = map(m, true, true)) != hipSuccess) return e;
+    // U = LA (Q, K, K; g), as a pair, and dq = LA (W, K, K; g): one launch, two sets of queries
+    m = LaProblem{}; m.q = f.q; m.k = f.k; m.v = f.k; m.mode = 2; m.oh = uh; m.ol = ul;
+    m.q2 = wh; m.q2l = wl; m.mode2 = 0; m.out2 = p.dq;
+    if ((e = map(m, false, false)) != hipSuccess) return e;
+    // dq += LA (dO, V, U; g^2)
+    m = LaProblem{}; m.qf = p.dout; m.k = f.v; m.v = uh; m.vl = ul; m.mode = 1; m.out = p.dq;
+    if ((e = map(m, false, true)) != hipSuccess) return e;
+    // dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g): one launch, the symmetric carry
+    m = LaProblem{}; m.q = f.k; m.k = f.q; m.v = wh; m.vl = wl; m.mode = 0; m.sym = true; m.out = p.dk;
+    if ((e = map(m, true, false)) != hipSuccess) return e;
     // dv = LA^rev (U, Q, dO; g^2)
-    return la(uh, ul, f.q, nullptr, doh, dol, true, true, 0, p.dv, nullptr, nullptr);
+    m = LaProblem{}; m.q = uh; m.ql = ul; m.k = f.q; m.vf = p.dout; m.mode = 0; m.out = p.dv;
+    return map(m, true, true);
 }
 
 }  // namespace hla

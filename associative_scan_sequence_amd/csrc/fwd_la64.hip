@@ -23,11 +23,20 @@
 //    and the local part A V, then adds e_t C0^T q_t once the carry is in LDS.
 // Output: fp32 (stored, or added to what out holds), or the result split into
 // bf16 hi = bf16(y) and lo = bf16(y - hi), ready to be an operand of a later
-// map.  QP, KP, VP: the queries, keys or values come as such a pair (x = hi +
-// lo, two bf16 arrays; not keys and values both); a product with a pair takes
-// hi * y + lo * y_hi (the dropped lo * y_lo is about 2^-16 of the product).
+// map.  Operand modes QM, KM, VM: 0 bf16; 1 such a pair (x = hi + lo, two
+// bf16 arrays); 2 fp32, split into such a pair as it is staged.  Not keys and
+// values both in pairs.  A product with a pair takes hi * y + lo * y_hi (the
+// dropped lo * y_lo is about 2^-16 of the product).
+// OUT2 >= 0: a second set of queries (mode Q2M) against the same keys, values
+// and carries, with its own output (mode OUT2): its local part and output are
+// formed after the first set's, while the carry tiles are still in LDS.
 // REV: the map runs on the reversed sequence (token t read and written at
 // n - 1 - t), which is the reverse-time map.
+// SYM: the sum of the map and the map with keys and values exchanged,
+//   y_t = sum g^|t-s| [(q_t . k_s) v_s + (q_t . v_s) k_s]   (d = dv),
+// whose carry is C0 + C0^T: the C sums run as for the map alone, the output
+// reads the carry tiles both ways, and the local part is formed twice with
+// the key and value tiles exchanged.
 // Precision: A is split into bf16 hi + lo (its entries are fp32 sums), as are
 // the decayed key operand of the C sums and the carry C0.
 #include "fast64_common.h"
@@ -49,9 +58,14 @@ constexpr int kStore = 0, kAccumulate = 1, kSplit = 2;  // output modes (LaProbl
 struct LaArgs {
     int H, n, nc, P, L, BH, segs;
     const uint16_t *q, *k, *v;
-    const uint16_t *ql, *kl, *vl;  // the lo halves of paired operands (QP, KP, VP)
+    const uint16_t *ql, *kl, *vl;  // the lo halves of paired operands (mode 1)
+    const float *qf, *kf, *vf;     // fp32 operands (mode 2)
+    const uint16_t *q2, *q2l;      // the second queries (OUT2 >= 0), bf16 or pair
+    const float *q2f;              // or fp32
     float *out;             // kStore, kAccumulate
     uint16_t *oh, *ol;      // kSplit: bf16 hi and lo of the result
+    float *out2;            // the second queries' output
+    uint16_t *oh2, *ol2;
     uint32_t *ctrl;         // control block, as for the second-order kernel
     uint32_t *flags;        // [BH * P][8 waves] at kFlagStride words
     float *aggC;            // [BH * P][16 tiles][64 lanes][4]
@@ -72,8 +86,38 @@ __device__ __forceinline__ void put_tiles2(const float *slot, int v, int l, cons
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(x[i], rs, ((2 * v + i) * 64 + l) * 16, 0, kSc1);
 }
 
-template <bool DECAY, bool LOOP, int OUT, bool QP, bool KP, bool VP, bool REV>
+// 8 consecutive values of a row (element e of the array) as raw registers:
+// mode 0 raw[0] = 8 bf16; mode 1 raw[0], raw[1] = hi, lo; mode 2 raw[0],
+// raw[1] = the 8 fp32 values (split later, so the load is not waited for here)
+template <int M>
+__device__ __forceinline__ void ld_op(const uint16_t *h, const uint16_t *lo, const float *f, size_t e,
+                                      u32x4 (&raw)[2]) {
+    if constexpr (M == 2) {
+        raw[0] = *reinterpret_cast<const u32x4 *>(f + e);
+        raw[1] = *reinterpret_cast<const u32x4 *>(f + e + 4);
+    } else {
+        raw[0] = *reinterpret_cast<const u32x4 *>(h + e);
+        if constexpr (M == 1) raw[1] = *reinterpret_cast<const u32x4 *>(lo + e);
+    }
+}
+
+// raw registers -> (hi, lo) bf16 (lo only for modes 1 and 2)
+template <int M>
+__device__ __forceinline__ void to_pair(const u32x4 (&raw)[2], u32x4 &hi, u32x4 &lo) {
+    if constexpr (M == 2) {
+        bf16x8 h, l;
+        pair_operand(__builtin_bit_cast(f32x4, raw[0]), __builtin_bit_cast(f32x4, raw[1]), h, l);
+        hi = __builtin_bit_cast(u32x4, h);
+        lo = __builtin_bit_cast(u32x4, l);
+    } else {
+        hi = raw[0];
+        if constexpr (M == 1) lo = raw[1];
+    }
+}
+
+template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2 = -1, int Q2M = 0, bool SYM = false>
 __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
+    constexpr bool KP = KM != 0, VP = VM != 0, Q2 = OUT2 >= 0;
     static_assert(!(KP && VP), "the lo halves of keys and values share four tiles");
     __shared__ LaSmem<(KP || VP) ? 20 : 16> sm;
     const int tid = threadIdx.x;
@@ -114,7 +158,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 
         // ---- loads: keys and values of the segment's chunks (rows past a chunk
         // read the head's first row and are zeroed when staged), queries of the slice
-        u32x4 kx[2][2], vx[2][2], qx[2][2], xlx[2][2], qlx[2][2];  // xlx: lo half of keys or values
+        u32x4 kr[2][2][2], vr[2][2][2], qr[2][2][2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * grp + jj;
@@ -122,38 +166,52 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
             for (int u = 0; u < 2; ++u) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
                 const size_t src = row < lc_of[jj] ? at_pos((c0 + j) * W + row) : head;
-                kx[jj][u] = *reinterpret_cast<const u32x4 *>(a.k + src * W + cg * 8);
-                vx[jj][u] = *reinterpret_cast<const u32x4 *>(a.v + src * W + cg * 8);
-                if constexpr (KP) xlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.kl + src * W + cg * 8);
-                if constexpr (VP) xlx[jj][u] = *reinterpret_cast<const u32x4 *>(a.vl + src * W + cg * 8);
+                ld_op<KM>(a.k, a.kl, a.kf, src * W + cg * 8, kr[jj][u]);
+                ld_op<VM>(a.v, a.vl, a.vf, src * W + cg * 8, vr[jj][u]);
             }
         }
+        // queries of the slice: token t0 + 16i, features 32ks + 8g ..
+        auto load_q = [&](auto mode, const uint16_t *h, const uint16_t *lo, const float *f, u32x4 (&raw)[2][2][2])
+            __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int tt = t0 + 16 * i;
-                const size_t src = tt < Lcs ? at_pos((c0 + sc) * W + tt) : head;
-                qx[i][ks] = *reinterpret_cast<const u32x4 *>(a.q + src * W + 32 * ks + 8 * g);
-                if constexpr (QP) qlx[i][ks] = *reinterpret_cast<const u32x4 *>(a.ql + src * W + 32 * ks + 8 * g);
-            }
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int tt = t0 + 16 * i;
+                    const size_t src = tt < Lcs ? at_pos((c0 + sc) * W + tt) : head;
+                    ld_op<decltype(mode)::value>(h, lo, f, src * W + 32 * ks + 8 * g, raw[i][ks]);
+                }
+        };
+        auto to_q = [&](auto mode, const u32x4 (&raw)[2][2][2], bf16x8 (&qh)[2][2], bf16x8 (&ql)[2][2])
+            __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    u32x4 h, lo;
+                    to_pair<decltype(mode)::value>(raw[i][ks], h, lo);
+                    const bool in = t0 + 16 * i < Lcs;
+                    qh[i][ks] = __builtin_bit_cast(bf16x8, in ? h : z4);
+                    if constexpr (decltype(mode)::value != 0) ql[i][ks] = __builtin_bit_cast(bf16x8, in ? lo : z4);
+                }
+        };
+        load_q(IC<QM>{}, a.q, a.ql, a.qf, qr);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = (wt + 256 * u) >> 3, cg = (wt + 256 * u) & 7;
-                st16(sm.T[2 * grp + jj], row, cg * 8, row < lc_of[jj] ? kx[jj][u] : z4);
-                st16(sm.T[4 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? vx[jj][u] : z4);
-                if constexpr (KP || VP) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, row < lc_of[jj] ? xlx[jj][u] : z4);
+                const bool in = row < lc_of[jj];
+                u32x4 kh, kl_, vh, vl_;
+                to_pair<KM>(kr[jj][u], kh, kl_);
+                to_pair<VM>(vr[jj][u], vh, vl_);
+                st16(sm.T[2 * grp + jj], row, cg * 8, in ? kh : z4);
+                st16(sm.T[4 + 2 * grp + jj], row, cg * 8, in ? vh : z4);
+                if constexpr (KP) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, in ? kl_ : z4);
+                if constexpr (VP) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, in ? vl_ : z4);
             }
         bf16x8 qn[2][2], qnl[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                qn[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qx[i][ks] : z4);
-                if constexpr (QP) qnl[i][ks] = __builtin_bit_cast(bf16x8, t0 + 16 * i < Lcs ? qlx[i][ks] : z4);
-            }
+        to_q(IC<QM>{}, qr, qn, qnl);
         __syncthreads();
 
         auto lane_base = [&](int off) __attribute__((always_inline)) {
@@ -227,21 +285,23 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 
         // ================= slice: A^T and the local part A V =========================
         f32x4 num[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
-        auto local = [&](auto hc) __attribute__((always_inline)) {
+        auto local = [&](auto hc, auto qpair, auto swap, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2])
+            __attribute__((always_inline)) {
             constexpr int HH = decltype(hc)::value;
+            constexpr bool QP = decltype(qpair)::value != 0;
+            // swap: the keys are read from the value tiles and the values from the key tiles
+            constexpr bool SW = decltype(swap)::value != 0;
+            constexpr int KB = SW ? 4 : 0, VB = SW ? 0 : 4;
+            constexpr bool LKP = SW ? VP : KP, LVP = SW ? KP : VP;
             const float lg_rg = lane_base(r - 4 * g);
             f32x4 at[2][4];
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 at[0][ib] = at[1][ib] = zero4;
                 if (ib <= 2 * HH + 1) {
-                    const bf16x8 k0 = ld8(sm.T[sc], 16 * ib + r, 8 * g), k1 = ld8(sm.T[sc], 16 * ib + r, 32 + 8 * g);
+                    const bf16x8 k0 = ld8(sm.T[KB + sc], 16 * ib + r, 8 * g), k1 = ld8(sm.T[KB + sc], 16 * ib + r, 32 + 8 * g);
                     bf16x8 k0l, k1l;
-                    if constexpr (KP) {
+                    if constexpr (LKP) {
                         k0l = ld8(sm.T[16 + sc], 16 * ib + r, 8 * g);
                         k1l = ld8(sm.T[16 + sc], 16 * ib + r, 32 + 8 * g);
                     }
@@ -250,7 +310,7 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                         if (ib <= 2 * HH + i) {
                             at[i][ib] = mfma(k1, qn[i][1], mfma(k0, qn[i][0], zero4));
                             if constexpr (QP) at[i][ib] = mfma(k1, qnl[i][1], mfma(k0, qnl[i][0], at[i][ib]));
-                            if constexpr (KP) at[i][ib] = mfma(k1l, qn[i][1], mfma(k0l, qn[i][0], at[i][ib]));
+                            if constexpr (LKP) at[i][ib] = mfma(k1l, qn[i][1], mfma(k0l, qn[i][0], at[i][ib]));
                             // g^(t - s), t = 32HH + 16i + r, s = 16ib + 4g + e; s > t only in the diagonal tile
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -269,8 +329,8 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                     bf16x8 vt[4], vtl[4];
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
-                        vt[jb] = tr8(sm.T[4 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
-                        if constexpr (VP) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        vt[jb] = tr8(sm.T[VB + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        if constexpr (LVP) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
                     }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -281,17 +341,29 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                             for (int jb = 0; jb < 4; ++jb) {
                                 num[i][jb] = mfma(vt[jb], ah, num[i][jb]);
                                 num[i][jb] = mfma(vt[jb], al, num[i][jb]);
-                                if constexpr (VP) num[i][jb] = mfma(vtl[jb], ah, num[i][jb]);
+                                if constexpr (LVP) num[i][jb] = mfma(vtl[jb], ah, num[i][jb]);
                             }
                         }
                     }
                 }
             }
         };
-        if (Lcs > 0) {
-            if (hh) local(IC<1>{});
-            else local(IC<0>{});
-        }
+        auto local_part = [&](auto qpair, const bf16x8 (&qh)[2][2], const bf16x8 (&ql)[2][2])
+            __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
+            if (Lcs > 0) {
+                if (hh) local(IC<1>{}, qpair, IC<0>{}, qh, ql);
+                else local(IC<0>{}, qpair, IC<0>{}, qh, ql);
+                if constexpr (SYM) {
+                    if (hh) local(IC<1>{}, qpair, IC<1>{}, qh, ql);
+                    else local(IC<0>{}, qpair, IC<1>{}, qh, ql);
+                }
+            }
+        };
+        local_part(IC<QM>{}, qn, qnl);
 
         // ================= the carry: C0 of every chunk -> LDS =======================
         const int seg_tokens = a.L * W;
@@ -345,7 +417,11 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
         __syncthreads();
 
         // ================= output: num + e_t C0^T q_t ==============================
-        if (Lcs > 0) {
+        auto output = [&](auto omode, auto qpair, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2], float *out,
+                          uint16_t *oh, uint16_t *ol) __attribute__((always_inline)) {
+            constexpr int OM = decltype(omode)::value;
+            constexpr bool QP = decltype(qpair)::value != 0;
+            if (Lcs == 0) return;
             f32x4 acc[2][4];
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
@@ -361,6 +437,16 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                         acc[i][jb] = mfma(cl, qn[i][ks], acc[i][jb]);
                         if constexpr (QP) acc[i][jb] = mfma(ch, qnl[i][ks], acc[i][jb]);
                     }
+                    if constexpr (SYM) {  // C0 read the other way: the same lanes and k slots, rows for columns
+                        const bf16x8 th = ld8(sm.T[8 + 2 * sc], 16 * jb + r, rb);
+                        const bf16x8 tl = ld8(sm.T[9 + 2 * sc], 16 * jb + r, rb);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            acc[i][jb] = mfma(th, qn[i][ks], acc[i][jb]);
+                            acc[i][jb] = mfma(tl, qn[i][ks], acc[i][jb]);
+                            if constexpr (QP) acc[i][jb] = mfma(th, qnl[i][ks], acc[i][jb]);
+                        }
+                    }
                 }
             }
 #pragma unroll
@@ -373,19 +459,30 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                     for (int jb = 0; jb < 4; ++jb) {
                         f32x4 o = num[i][jb] + e * acc[i][jb];
                         const size_t at = tok * W + 16 * jb + 4 * g;
-                        if constexpr (OUT == kSplit) {
+                        if constexpr (OM == kSplit) {
                             bf16x4 h, lo;
                             split4(o, h, lo);
-                            *reinterpret_cast<bf16x4 *>(a.oh + at) = h;
-                            *reinterpret_cast<bf16x4 *>(a.ol + at) = lo;
+                            *reinterpret_cast<bf16x4 *>(oh + at) = h;
+                            *reinterpret_cast<bf16x4 *>(ol + at) = lo;
                         } else {
-                            f32x4 *dst = reinterpret_cast<f32x4 *>(a.out + at);
-                            if constexpr (OUT == kAccumulate) o += *dst;
+                            f32x4 *dst = reinterpret_cast<f32x4 *>(out + at);
+                            if constexpr (OM == kAccumulate) o += *dst;
                             __builtin_nontemporal_store(o, dst);
                         }
                     }
                 }
             }
+        };
+        if constexpr (Q2) {  // the second queries' loads go out now, used after the first output
+            u32x4 q2r[2][2][2];
+            load_q(IC<Q2M>{}, a.q2, a.q2l, a.q2f, q2r);
+            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol);
+            bf16x8 qn2[2][2], qnl2[2][2];
+            to_q(IC<Q2M>{}, q2r, qn2, qnl2);
+            local_part(IC<Q2M>{}, qn2, qnl2);
+            output(IC<OUT2>{}, IC<Q2M>{}, qn2, qnl2, a.out2, a.oh2, a.ol2);
+        } else {
+            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol);
         }
         __syncthreads();  // this segment's LDS reads are done before the next one is staged
     };
@@ -456,29 +553,33 @@ void la_geometry(int BH, int nc, int *P, int *L) {
 
 // the operand/direction/output combinations the library uses
 template <bool DECAY, bool LOOP>
-hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode, bool rev) {
+hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode, bool rev, int mode2, bool sym) {
     const dim3 block(kLThreads);
-    const bool qp = a.ql != nullptr, kp = a.kl != nullptr, vp = a.vl != nullptr;
-    const int key = (qp ? 1 : 0) | (kp ? 2 : 0) | (vp ? 4 : 0) | (rev ? 8 : 0) | (mode << 4);
-    switch (key) {
-        // forward, plain operands: split output (AHLA, third order, backward U) or fp32
-        case (kSplit << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit, false, false, false, false>), grid, block, 0, st, a); break;
-        case (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false, false, false, false>), grid, block, 0, st, a); break;
-        // forward, paired values, fp32 (AHLA's second map)
-        case 4 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false, false, true, false>), grid, block, 0, st, a); break;
-        // backward: W = reverse, paired keys, split output
-        case 2 | 8 | (kSplit << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kSplit, false, true, false, true>), grid, block, 0, st, a); break;
-        // dQ: forward, paired queries and values (store); forward, paired queries (accumulate)
-        case 1 | 4 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, true, false, true, false>), grid, block, 0, st, a); break;
-        case 1 | (kAccumulate << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kAccumulate, true, false, false, false>), grid, block, 0, st, a); break;
-        // dK: reverse, paired values (store); reverse, paired keys (accumulate)
-        case 4 | 8 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, false, false, true, true>), grid, block, 0, st, a); break;
-        case 2 | 8 | (kAccumulate << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kAccumulate, false, true, false, true>), grid, block, 0, st, a); break;
-        // dV: reverse, paired queries and values (store)
-        case 1 | 4 | 8 | (kStore << 4): hipLaunchKernelGGL((k_la64<DECAY, LOOP, kStore, true, false, true, true>), grid, block, 0, st, a); break;
-        default: return hipErrorInvalidValue;
+    const int qm = a.qf ? 2 : (a.ql ? 1 : 0), km = a.kf ? 2 : (a.kl ? 1 : 0), vm = a.vf ? 2 : (a.vl ? 1 : 0);
+    const int q2m = a.q2f ? 2 : (a.q2l ? 1 : 0);
+    const bool two = a.q2 != nullptr || a.q2f != nullptr;
+    // key: operand modes, direction, output mode(s), symmetric sum
+    const int key = qm | (km << 2) | (vm << 4) | (rev ? 64 : 0) | (mode << 7) |
+                    (two ? ((1 + mode2) << 9) | (q2m << 11) : 0) | (sym ? 1 << 13 : 0);
+    auto K = [](int q, int k, int v, bool r, int m, int m2 = -1, int q2 = 0, bool sy = false) {
+        return q | (k << 2) | (v << 4) | (r ? 64 : 0) | (m << 7) | (m2 >= 0 ? ((1 + m2) << 9) | (q2 << 11) : 0) |
+               (sy ? 1 << 13 : 0);
+    };
+#define HLA_LA(QM_, KM_, VM_, REV_, OUT_, ...) \
+    if (key == K(QM_, KM_, VM_, REV_, OUT_, ##__VA_ARGS__)) { \
+        hipLaunchKernelGGL((k_la64<DECAY, LOOP, OUT_, QM_, KM_, VM_, REV_, ##__VA_ARGS__>), grid, block, 0, st, a); \
+        return hipGetLastError(); \
     }
-    return hipGetLastError();
+    HLA_LA(0, 0, 0, false, kSplit)                // first maps of AHLA and third order
+    HLA_LA(0, 0, 0, false, kStore)                // a plain map
+    HLA_LA(0, 0, 1, false, kStore)                // AHLA's second map (values as a pair)
+    HLA_LA(0, 2, 0, true, kSplit)                 // backward: W = LA^rev (V, dO, Q; g^2)
+    HLA_LA(0, 0, 0, false, kSplit, kStore, 1)     // backward: U = LA (Q, K, K; g) and LA (W, K, K; g)
+    HLA_LA(2, 0, 1, false, kAccumulate)           // backward: + LA (dO, V, U; g^2)
+    HLA_LA(0, 0, 1, true, kStore, -1, 0, true)    // backward: LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g)
+    HLA_LA(1, 0, 2, true, kStore)                 // backward: LA^rev (U, Q, dO; g^2)
+#undef HLA_LA
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -506,6 +607,11 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     a.ql = static_cast<const uint16_t *>(p.ql);
     a.kl = static_cast<const uint16_t *>(p.kl);
     a.vl = static_cast<const uint16_t *>(p.vl);
+    a.qf = p.qf; a.kf = p.kf; a.vf = p.vf;
+    a.q2 = static_cast<const uint16_t *>(p.q2);
+    a.q2l = static_cast<const uint16_t *>(p.q2l);
+    a.q2f = p.q2f;
+    a.out2 = p.out2; a.oh2 = p.oh2; a.ol2 = p.ol2;
     a.out = p.out; a.oh = p.oh; a.ol = p.ol;
     a.ctrl = ctrl;
     const LaLayout L = la_layout(a.BH, a.P);
@@ -523,8 +629,11 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     if (e != hipSuccess) return e;
     const bool loop = a.segs > cus || (a.P > 1 && a.BH > kMaxTicketHeads);
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
-    if (decay) return loop ? launch_la<true, true>(a, grid, st, p.mode, p.rev) : launch_la<true, false>(a, grid, st, p.mode, p.rev);
-    return loop ? launch_la<false, true>(a, grid, st, p.mode, p.rev) : launch_la<false, false>(a, grid, st, p.mode, p.rev);
+    if (decay)
+        return loop ? launch_la<true, true>(a, grid, st, p.mode, p.rev, p.mode2, p.sym)
+                    : launch_la<true, false>(a, grid, st, p.mode, p.rev, p.mode2, p.sym);
+    return loop ? launch_la<false, true>(a, grid, st, p.mode, p.rev, p.mode2, p.sym)
+                : launch_la<false, false>(a, grid, st, p.mode, p.rev, p.mode2, p.sym);
 }
 
 }  // namespace hla

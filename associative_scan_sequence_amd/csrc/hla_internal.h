@@ -178,18 +178,27 @@ hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
 // 64 (chunk 64, every decay >= 0.75): y_t = sum_{s<=t} g^(t-s) (q_t.k_s) v_s,
 // or with rev the reverse-time map (s >= t, g^(s-t)).  mode 0: out = y; 1:
 // out += y; 2: oh, ol = bf16 hi and lo of y.  ql, kl, vl set: that operand is
-// the bf16 pair (x, xl).  Only the combinations listed in la64_forward are
-// built (hipErrorInvalidValue otherwise).  The workspace is a forward
-// workspace: control block, then la64_workspace_bytes.
+// the bf16 pair (x, xl); qf, kf, vf set: it is fp32 (and q, k, v unused).
+// q2 (or q2 + q2l, or q2f) set: a second set of queries against the same
+// keys and values, written to out2 (or oh2, ol2) with mode2.  Only the
+// combinations listed in la64_forward are built (hipErrorInvalidValue
+// otherwise).  The workspace is a forward workspace: control block, then
+// la64_workspace_bytes.
 struct LaProblem {
     int B, H, n;
     const void *q, *k, *v;
     const void *ql, *kl, *vl;
+    const float *qf, *kf, *vf;
+    const void *q2, *q2l;
+    const float *q2f;
     float *out;
     uint16_t *oh, *ol;
-    int mode;
+    float *out2;
+    uint16_t *oh2, *ol2;
+    int mode, mode2;
     bool rev;
     bool gsq;      // the decay per token is g^2 (g from gam)
+    bool sym;      // plus the map with keys and values exchanged (d = dv; values bf16 or a pair, keys bf16)
     GammaTab gam;
 };
 size_t la64_workspace_bytes(int BH, int n);

@@ -464,8 +464,9 @@ def forward_with_state(dev, stream):
 def backward_headline_shape(dev, stream):
     """hla_backward_chunked at B4 H8 n2048 d64 bf16: read q, k, v (bf16) and
     dout (fp32), write dq, dk, dv (fp32): 1408 B per head-token.  The plain
-    call takes the one-launch backward (seven first-order maps); the shard's
-    call (initial state, final-state gradient) the chunked fp32 backward."""
+    call takes the one-launch backward (seven first-order maps in five
+    launches); the shard's call (initial state, final-state gradient) the
+    chunked fp32 backward."""
     import torch
 
     import associative_scan_sequence_amd as hla
@@ -493,7 +494,7 @@ def backward_headline_shape(dev, stream):
         hla.backward_chunked(q, k, v, dout, chunk=w.chunk, workspace=ws, grads=grads)
     us = time_calls(call, stream, 10, warmup=2)
     res = [{"workload": "masked_hla_bwd_B4_H8_n2048_d64_bf16_w64",
-            "entry": "hla_backward_chunked (one-launch: seven first-order maps)",
+            "entry": "hla_backward_chunked (seven first-order maps in five launches)",
             "us_per_call": us, "single_call_us": dict(_LAST_PCT), "tokens_per_s": w.B * w.n / (us * 1e-6),
             "roofline": roof(tok * per_tok, us)}]
 
