@@ -17,10 +17,11 @@
 // U and W written as pairs by the maps that form them.  U and the second part
 // of dq share their keys, values and decay, so they are one launch with two
 // sets of queries, and the two maps of dk are one launch whose carry is
-// symmetric: five launches in all.
+// symmetric.  After W, the maps fall into two pairs that do not depend on
+// each other, each pair one grid: three launches in all.
 //
 // Workspace: the first kCtrlBytes are the one-launch kernels' control block,
-// then their flags and aggregates, then the pairs of U and W.  The call clears
+// then the flags of two maps, their aggregates, and the pairs of U and W.  The call clears
 // the control block and the flags itself (a fill kernel), so the backward
 // workspace needs no initialisation, as for the chunked path.
 #include "device_common.h"
@@ -39,14 +40,15 @@ __global__ __launch_bounds__(256) void k_zero_words(uint32_t *p, size_t n) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLaLayout {
-    size_t data, uh, ul, wh, wl, total;
+    size_t flags, agg, uh, ul, wh, wl, total;
 };
 
 BwdLaLayout bwd_la_layout(int BH, int n) {
     const size_t pair = static_cast<size_t>(BH) * n * kBw * sizeof(uint16_t);
     BwdLaLayout L{};
-    L.data = kCtrlBytes;
-    L.uh = align256(L.data + la64_workspace_bytes(BH, n));
+    L.flags = kCtrlBytes;  // two maps' flags, then their aggregates
+    L.agg = L.flags + 2 * la64_flag_bytes(BH, n);
+    L.uh = align256(L.agg + 2 * la64_agg_bytes(BH, n));
     L.ul = align256(L.uh + pair);
     L.wh = align256(L.ul + pair);
     L.wl = align256(L.wh + pair);
@@ -82,38 +84,40 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
     const BwdLaLayout L = bwd_la_layout(BH, f.n);
     char *base = static_cast<char *>(f.ws);
     uint32_t *ctrl = reinterpret_cast<uint32_t *>(base);
-    void *data = base + L.data;
+    const size_t fb = la64_flag_bytes(BH, f.n), ab = la64_agg_bytes(BH, f.n);
+    const LaSpace sa{reinterpret_cast<uint32_t *>(base + L.flags), reinterpret_cast<float *>(base + L.agg)};
+    const LaSpace sb{reinterpret_cast<uint32_t *>(base + L.flags + fb), reinterpret_cast<float *>(base + L.agg + ab)};
     auto pair = [&](size_t off) { return reinterpret_cast<uint16_t *>(base + off); };
     uint16_t *uh = pair(L.uh), *ul = pair(L.ul), *wh = pair(L.wh), *wl = pair(L.wl);
-    // the control block and the flags start clear (every launch below then
-    // leaves them valid for the next)
-    const size_t words = (kCtrlBytes + la64_flag_bytes(BH, f.n)) / sizeof(uint32_t);
+    // the control block and both maps' flags start clear (every launch below
+    // then leaves them valid for the next)
+    const size_t words = (kCtrlBytes + 2 * fb) / sizeof(uint32_t);
     hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
                        dim3(256), 0, st, ctrl, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto map = [&](LaProblem m, bool rev, bool gsq) {
+    auto map = [&](bool rev, bool gsq) {
+        LaProblem m{};
         m.B = f.B; m.H = f.H; m.n = f.n; m.gam = f.gam;
         m.rev = rev; m.gsq = gsq;
-        return la64_forward(m, ctrl, data, st);
+        return m;
     };
-    LaProblem m{};
     // W = LA^rev (V, dO, Q; g^2), as a pair
-    m = LaProblem{}; m.q = f.v; m.kf = p.dout; m.v = f.q; m.mode = 2; m.oh = wh; m.ol = wl;
-    if ((e = map(m, true, true)) != hipSuccess) return e;
-    // U = LA (Q, K, K; g), as a pair, and dq = LA (W, K, K; g): one launch, two sets of queries
-    m = LaProblem{}; m.q = f.q; m.k = f.k; m.v = f.k; m.mode = 2; m.oh = uh; m.ol = ul;
-    m.q2 = wh; m.q2l = wl; m.mode2 = 0; m.out2 = p.dq;
-    if ((e = map(m, false, false)) != hipSuccess) return e;
-    // dq += LA (dO, V, U; g^2)
-    m = LaProblem{}; m.qf = p.dout; m.k = f.v; m.v = uh; m.vl = ul; m.mode = 1; m.out = p.dq;
-    if ((e = map(m, false, true)) != hipSuccess) return e;
-    // dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g): one launch, the symmetric carry
-    m = LaProblem{}; m.q = f.k; m.k = f.q; m.v = wh; m.vl = wl; m.mode = 0; m.sym = true; m.out = p.dk;
-    if ((e = map(m, true, false)) != hipSuccess) return e;
-    // dv = LA^rev (U, Q, dO; g^2)
-    m = LaProblem{}; m.q = uh; m.ql = ul; m.k = f.q; m.vf = p.dout; m.mode = 0; m.out = p.dv;
-    return map(m, true, true);
+    LaProblem w = map(true, true);
+    w.q = f.v; w.kf = p.dout; w.v = f.q; w.mode = 2; w.oh = wh; w.ol = wl;
+    if ((e = la64_forward_in(w, ctrl, sa, st)) != hipSuccess) return e;
+    // U = LA (Q, K, K; g), as a pair, and dq = LA (W, K, K; g): two sets of queries;
+    // with dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g), the symmetric carry
+    LaProblem u = map(false, false), dk = map(true, false);
+    u.q = f.q; u.k = f.k; u.v = f.k; u.mode = 2; u.oh = uh; u.ol = ul;
+    u.q2 = wh; u.q2l = wl; u.mode2 = 0; u.out2 = p.dq;
+    dk.q = f.k; dk.k = f.q; dk.v = wh; dk.vl = wl; dk.mode = 0; dk.sym = true; dk.out = p.dk;
+    if ((e = la64_forward_pair(u, sa, dk, sb, ctrl, st)) != hipSuccess) return e;
+    // dq += LA (dO, V, U; g^2), with dv = LA^rev (U, Q, dO; g^2)
+    LaProblem dq = map(false, true), dv = map(true, true);
+    dq.qf = p.dout; dq.k = f.v; dq.v = uh; dq.vl = ul; dq.mode = 1; dq.out = p.dq;
+    dv.q = uh; dv.ql = ul; dv.k = f.q; dv.vf = p.dout; dv.mode = 0; dv.out = p.dv;
+    return la64_forward_pair(dq, sa, dv, sb, ctrl, st);
 }
 
 }  // namespace hla

@@ -39,6 +39,8 @@
 // the key and value tiles exchanged.
 // Precision: A is split into bf16 hi + lo (its entries are fp32 sums), as are
 // the decayed key operand of the C sums and the carry C0.
+// k_la64 runs one map; k_la64_pair two maps that do not depend on each other
+// in one grid, so that their launches do not wait on each other's tails.
 #include "fast64_common.h"
 
 namespace hla {
@@ -115,11 +117,21 @@ __device__ __forceinline__ void to_pair(const u32x4 (&raw)[2], u32x4 &hi, u32x4 
     }
 }
 
+// One map: its segments are taken by nblocks workgroups, of which this is
+// number block; its per-head ticket counters start at counter head_base.
+// Returns the launch's epoch.
 template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2 = -1, int Q2M = 0, bool SYM = false>
-__global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
+struct LaMap {
+    static constexpr int kTiles = (KM != 0 || VM != 0) ? 20 : 16;
+    __device__ __forceinline__ static uint32_t run(const LaArgs &a, __bf16 (*T)[kTileElems], int block, int nblocks,
+                                                   int head_base);
+};
+
+template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2, int Q2M, bool SYM>
+__device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT2, Q2M, SYM>::run(
+    const LaArgs &a, __bf16 (*T)[kTileElems], int block, int nblocks, int head_base) {
     constexpr bool KP = KM != 0, VP = VM != 0, Q2 = OUT2 >= 0;
     static_assert(!(KP && VP), "the lo halves of keys and values share four tiles");
-    __shared__ LaSmem<(KP || VP) ? 20 : 16> sm;
     const int tid = threadIdx.x;
     uint32_t ep_raw = 0;
     if ((tid & 63) == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -205,10 +217,10 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                 u32x4 kh, kl_, vh, vl_;
                 to_pair<KM>(kr[jj][u], kh, kl_);
                 to_pair<VM>(vr[jj][u], vh, vl_);
-                st16(sm.T[2 * grp + jj], row, cg * 8, in ? kh : z4);
-                st16(sm.T[4 + 2 * grp + jj], row, cg * 8, in ? vh : z4);
-                if constexpr (KP) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, in ? kl_ : z4);
-                if constexpr (VP) st16(sm.T[16 + 2 * grp + jj], row, cg * 8, in ? vl_ : z4);
+                st16(T[2 * grp + jj], row, cg * 8, in ? kh : z4);
+                st16(T[4 + 2 * grp + jj], row, cg * 8, in ? vh : z4);
+                if constexpr (KP) st16(T[16 + 2 * grp + jj], row, cg * 8, in ? kl_ : z4);
+                if constexpr (VP) st16(T[16 + 2 * grp + jj], row, cg * 8, in ? vl_ : z4);
             }
         bf16x8 qn[2][2], qnl[2][2];
         to_q(IC<QM>{}, qr, qn, qnl);
@@ -235,14 +247,14 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int rb = 32 * ks + 8 * g;
-                const bf16x8 vt = tr8(sm.T[4 + c], rb, rb + 4, 16 * tb, r);
+                const bf16x8 vt = tr8(T[4 + c], rb, rb + 4, 16 * tb, r);
                 bf16x8 vtl;
-                if constexpr (VP) vtl = tr8(sm.T[16 + c], rb, rb + 4, 16 * tb, r);
+                if constexpr (VP) vtl = tr8(T[16 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const bf16x8 kt = tr8(sm.T[c], rb, rb + 4, 16 * (cb + i), r);
+                    const bf16x8 kt = tr8(T[c], rb, rb + 4, 16 * (cb + i), r);
                     bf16x8 ktl;
-                    if constexpr (KP) ktl = tr8(sm.T[16 + c], rb, rb + 4, 16 * (cb + i), r);
+                    if constexpr (KP) ktl = tr8(T[16 + c], rb, rb + 4, 16 * (cb + i), r);
                     if (!DECAY) {
                         crun[i] = mfma(vt, kt, crun[i]);
                         if constexpr (VP) crun[i] = mfma(vtl, kt, crun[i]);
@@ -299,11 +311,11 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
             for (int ib = 0; ib < 4; ++ib) {
                 at[0][ib] = at[1][ib] = zero4;
                 if (ib <= 2 * HH + 1) {
-                    const bf16x8 k0 = ld8(sm.T[KB + sc], 16 * ib + r, 8 * g), k1 = ld8(sm.T[KB + sc], 16 * ib + r, 32 + 8 * g);
+                    const bf16x8 k0 = ld8(T[KB + sc], 16 * ib + r, 8 * g), k1 = ld8(T[KB + sc], 16 * ib + r, 32 + 8 * g);
                     bf16x8 k0l, k1l;
                     if constexpr (LKP) {
-                        k0l = ld8(sm.T[16 + sc], 16 * ib + r, 8 * g);
-                        k1l = ld8(sm.T[16 + sc], 16 * ib + r, 32 + 8 * g);
+                        k0l = ld8(T[16 + sc], 16 * ib + r, 8 * g);
+                        k1l = ld8(T[16 + sc], 16 * ib + r, 32 + 8 * g);
                     }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -329,8 +341,8 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                     bf16x8 vt[4], vtl[4];
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
-                        vt[jb] = tr8(sm.T[VB + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
-                        if constexpr (LVP) vtl[jb] = tr8(sm.T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        vt[jb] = tr8(T[VB + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
+                        if constexpr (LVP) vtl[jb] = tr8(T[16 + sc], 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * jb, r);
                     }
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -409,8 +421,8 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                     bf16x4 h, lo;
                     split4(d1 * c0seg[i] + cpre[c][i], h, lo);
                     // lane holds C0^T[j = 16tb+4g+e][a = 16(cb+i)+r]; tile rows a
-                    st4(sm.T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
-                    st4(sm.T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                    st4(T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                    st4(T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
                 }
             }
         }
@@ -429,8 +441,8 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int rb = 32 * ks + 8 * g;
-                    const bf16x8 ch = tr8(sm.T[8 + 2 * sc], rb, rb + 4, 16 * jb, r);
-                    const bf16x8 cl = tr8(sm.T[9 + 2 * sc], rb, rb + 4, 16 * jb, r);
+                    const bf16x8 ch = tr8(T[8 + 2 * sc], rb, rb + 4, 16 * jb, r);
+                    const bf16x8 cl = tr8(T[9 + 2 * sc], rb, rb + 4, 16 * jb, r);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         acc[i][jb] = mfma(ch, qn[i][ks], acc[i][jb]);
@@ -438,8 +450,8 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
                         if constexpr (QP) acc[i][jb] = mfma(ch, qnl[i][ks], acc[i][jb]);
                     }
                     if constexpr (SYM) {  // C0 read the other way: the same lanes and k slots, rows for columns
-                        const bf16x8 th = ld8(sm.T[8 + 2 * sc], 16 * jb + r, rb);
-                        const bf16x8 tl = ld8(sm.T[9 + 2 * sc], 16 * jb + r, rb);
+                        const bf16x8 th = ld8(T[8 + 2 * sc], 16 * jb + r, rb);
+                        const bf16x8 tl = ld8(T[9 + 2 * sc], 16 * jb + r, rb);
 #pragma unroll
                         for (int i = 0; i < 2; ++i) {
                             acc[i][jb] = mfma(th, qn[i][ks], acc[i][jb]);
@@ -488,15 +500,15 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
     };
     // segments by ticket when they wait on each other (see fwd_fast64.hip)
     auto take = [&]() -> int {
-        int *sl = reinterpret_cast<int *>(sm.T[3]);
+        int *sl = reinterpret_cast<int *>(T[3]);
         if (tid == 0) {
             int t;
             if constexpr (LOOP) {
                 t = static_cast<int>(
                     __hip_atomic_fetch_add(&a.ctrl[kTicketWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
             } else {
-                const int head = static_cast<int>(blockIdx.x) % a.BH;
-                uint32_t *cnt = &a.ctrl[kHeadTicketWord + kHeadTicketStride * head];
+                const int head = block % a.BH;
+                uint32_t *cnt = &a.ctrl[kHeadTicketWord + kHeadTicketStride * (head_base + head)];
                 const int pp = static_cast<int>(__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                 if (pp == a.P - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 t = pp * a.BH + head;
@@ -508,24 +520,48 @@ __global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
         __syncthreads();
         return t;
     };
-    const int seg0 = a.P > 1 ? take() : static_cast<int>(blockIdx.x);
+    const int seg0 = a.P > 1 ? take() : block;
     epoch = next_epoch(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ep_raw))));
     if constexpr (LOOP) {
-        for (int seg = seg0; seg < a.segs; seg = a.P > 1 ? take() : seg + static_cast<int>(gridDim.x)) seg_body(seg);
+        for (int seg = seg0; seg < a.segs; seg = a.P > 1 ? take() : seg + nblocks) seg_body(seg);
     } else if (seg0 < a.segs) {
         seg_body(seg0);
     } else if (tid == 0) {  // a ticket out of range: the control block was not zero before first use
         __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return epoch;
+}
+
+// The last workgroup of a launch to finish resets the looped grid's ticket
+// and advances the epoch for the next launch.
+__device__ __forceinline__ void la_done(uint32_t *ctrl, uint32_t epoch) {
+    if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&ctrl[kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
-            __hip_atomic_store(&a.ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[kTicketWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&a.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctrl[kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctrl[kTicketWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctrl[kLine + 1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+template <class M>
+__global__ __launch_bounds__(kLThreads, 1) void k_la64(LaArgs a) {
+    __shared__ LaSmem<M::kTiles> sm;
+    const uint32_t epoch = M::run(a, sm.T, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), 0);
+    la_done(a.ctrl, epoch);
+}
+
+// Two independent maps in one grid (one-pass): workgroups below a.segs take
+// the first map's segments, the rest the second's, each by its own per-head
+// tickets, flags and aggregates.  No wait crosses the maps.
+template <class MA, class MB>
+__global__ __launch_bounds__(kLThreads, 1) void k_la64_pair(LaArgs a, LaArgs b) {
+    __shared__ LaSmem<(MA::kTiles > MB::kTiles ? MA::kTiles : MB::kTiles)> sm;
+    const int blk = static_cast<int>(blockIdx.x);
+    const uint32_t epoch = blk < a.segs ? MA::run(a, sm.T, blk, a.segs, 0) : MB::run(b, sm.T, blk - a.segs, b.segs, a.BH);
+    la_done(a.ctrl, epoch);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -551,23 +587,26 @@ void la_geometry(int BH, int nc, int *P, int *L) {
     *P = (nc + l - 1) / l;
 }
 
-// the operand/direction/output combinations the library uses
-template <bool DECAY, bool LOOP>
-hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode, bool rev, int mode2, bool sym) {
-    const dim3 block(kLThreads);
+// key of an operand/direction/output combination
+constexpr int la_key(int qm, int km, int vm, bool rev, int mode, int mode2 = -1, int q2m = 0, bool sym = false) {
+    return qm | (km << 2) | (vm << 4) | (rev ? 64 : 0) | (mode << 7) | (mode2 >= 0 ? ((1 + mode2) << 9) | (q2m << 11) : 0) |
+           (sym ? 1 << 13 : 0);
+}
+
+int la_key_of(const LaArgs &a, const LaProblem &p) {
     const int qm = a.qf ? 2 : (a.ql ? 1 : 0), km = a.kf ? 2 : (a.kl ? 1 : 0), vm = a.vf ? 2 : (a.vl ? 1 : 0);
     const int q2m = a.q2f ? 2 : (a.q2l ? 1 : 0);
     const bool two = a.q2 != nullptr || a.q2f != nullptr;
-    // key: operand modes, direction, output mode(s), symmetric sum
-    const int key = qm | (km << 2) | (vm << 4) | (rev ? 64 : 0) | (mode << 7) |
-                    (two ? ((1 + mode2) << 9) | (q2m << 11) : 0) | (sym ? 1 << 13 : 0);
-    auto K = [](int q, int k, int v, bool r, int m, int m2 = -1, int q2 = 0, bool sy = false) {
-        return q | (k << 2) | (v << 4) | (r ? 64 : 0) | (m << 7) | (m2 >= 0 ? ((1 + m2) << 9) | (q2 << 11) : 0) |
-               (sy ? 1 << 13 : 0);
-    };
+    return la_key(qm, km, vm, p.rev, p.mode, two ? p.mode2 : -1, two ? q2m : 0, p.sym);
+}
+
+// the operand/direction/output combinations the library uses
+template <bool DECAY, bool LOOP>
+hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int key) {
+    const dim3 block(kLThreads);
 #define HLA_LA(QM_, KM_, VM_, REV_, OUT_, ...) \
-    if (key == K(QM_, KM_, VM_, REV_, OUT_, ##__VA_ARGS__)) { \
-        hipLaunchKernelGGL((k_la64<DECAY, LOOP, OUT_, QM_, KM_, VM_, REV_, ##__VA_ARGS__>), grid, block, 0, st, a); \
+    if (key == la_key(QM_, KM_, VM_, REV_, OUT_, ##__VA_ARGS__)) { \
+        hipLaunchKernelGGL((k_la64<LaMap<DECAY, LOOP, OUT_, QM_, KM_, VM_, REV_, ##__VA_ARGS__>>), grid, block, 0, st, a); \
         return hipGetLastError(); \
     }
     HLA_LA(0, 0, 0, false, kSplit)                // first maps of AHLA and third order
@@ -582,21 +621,27 @@ hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int mode, bool 
     return hipErrorInvalidValue;
 }
 
-}  // namespace
+// the pairs of independent maps the backward launches together
+template <bool D> using MapUdq = LaMap<D, false, kSplit, 0, 0, 0, false, kStore, 1>;
+template <bool D> using MapDk = LaMap<D, false, kStore, 0, 0, 1, true, -1, 0, true>;
+template <bool D> using MapDq2 = LaMap<D, false, kAccumulate, 2, 0, 1, false>;
+template <bool D> using MapDv = LaMap<D, false, kStore, 1, 0, 2, true>;
 
-size_t la64_workspace_bytes(int BH, int n) {
-    int P, L;
-    la_geometry(BH, (n + W - 1) / W, &P, &L);
-    return la_layout(BH, P).total;
+template <bool DECAY>
+hipError_t launch_la_pair(const LaArgs &a, const LaArgs &b, hipStream_t st, int ka, int kb) {
+    const dim3 block(kLThreads), grid(static_cast<unsigned>(a.segs + b.segs));
+    if (ka == la_key(0, 0, 0, false, kSplit, kStore, 1) && kb == la_key(0, 0, 1, true, kStore, -1, 0, true)) {
+        hipLaunchKernelGGL((k_la64_pair<MapUdq<DECAY>, MapDk<DECAY>>), grid, block, 0, st, a, b);
+        return hipGetLastError();
+    }
+    if (ka == la_key(2, 0, 1, false, kAccumulate) && kb == la_key(1, 0, 2, true, kStore)) {
+        hipLaunchKernelGGL((k_la64_pair<MapDq2<DECAY>, MapDv<DECAY>>), grid, block, 0, st, a, b);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
 }
 
-size_t la64_flag_bytes(int BH, int n) {
-    int P, L;
-    la_geometry(BH, (n + W - 1) / W, &P, &L);
-    return la_layout(BH, P).aggC;
-}
-
-hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+LaArgs la_args(const LaProblem &p, uint32_t *ctrl, LaSpace sp) {
     LaArgs a{};
     a.H = p.H; a.n = p.n; a.nc = (p.n + W - 1) / W; a.BH = p.B * p.H;
     la_geometry(a.BH, a.nc, &a.P, &a.L);
@@ -614,26 +659,80 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     a.out2 = p.out2; a.oh2 = p.oh2; a.ol2 = p.ol2;
     a.out = p.out; a.oh = p.oh; a.ol = p.ol;
     a.ctrl = ctrl;
-    const LaLayout L = la_layout(a.BH, a.P);
-    char *base = static_cast<char *>(data);
-    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
-    a.aggC = reinterpret_cast<float *>(base + L.aggC);
+    a.flags = sp.flags;
+    a.aggC = sp.aggC;
     a.gam = p.gam;
     a.gexp = p.gsq ? 2.0f : 1.0f;
+    return a;
+}
+
+bool la_decay(const LaProblem &p) {
     const int nh = p.gam.per_head ? p.H : 1;
     bool decay = false;
     for (int h = 0; h < nh; ++h) decay = decay || p.gam.g[h] != 1.0f;
-    int dev = 0, cus = 0;
+    return decay;
+}
+
+hipError_t cu_count(int *cus) {
+    int dev = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
+}
+
+}  // namespace
+
+size_t la64_flag_bytes(int BH, int n) {
+    int P, L;
+    la_geometry(BH, (n + W - 1) / W, &P, &L);
+    return la_layout(BH, P).aggC;
+}
+
+size_t la64_agg_bytes(int BH, int n) {
+    int P, L;
+    la_geometry(BH, (n + W - 1) / W, &P, &L);
+    const LaLayout l = la_layout(BH, P);
+    return l.total - l.aggC;
+}
+
+size_t la64_workspace_bytes(int BH, int n) { return la64_flag_bytes(BH, n) + la64_agg_bytes(BH, n); }
+
+hipError_t la64_forward_in(const LaProblem &p, uint32_t *ctrl, LaSpace sp, hipStream_t st) {
+    const LaArgs a = la_args(p, ctrl, sp);
+    int cus = 0;
+    const hipError_t e = cu_count(&cus);
     if (e != hipSuccess) return e;
     const bool loop = a.segs > cus || (a.P > 1 && a.BH > kMaxTicketHeads);
     const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
-    if (decay)
-        return loop ? launch_la<true, true>(a, grid, st, p.mode, p.rev, p.mode2, p.sym)
-                    : launch_la<true, false>(a, grid, st, p.mode, p.rev, p.mode2, p.sym);
-    return loop ? launch_la<false, true>(a, grid, st, p.mode, p.rev, p.mode2, p.sym)
-                : launch_la<false, false>(a, grid, st, p.mode, p.rev, p.mode2, p.sym);
+    const int key = la_key_of(a, p);
+    if (la_decay(p)) return loop ? launch_la<true, true>(a, grid, st, key) : launch_la<true, false>(a, grid, st, key);
+    return loop ? launch_la<false, true>(a, grid, st, key) : launch_la<false, false>(a, grid, st, key);
+}
+
+hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+    const int BH = p.B * p.H;
+    char *base = static_cast<char *>(data);
+    const LaSpace sp{reinterpret_cast<uint32_t *>(base), reinterpret_cast<float *>(base + la64_flag_bytes(BH, p.n))};
+    return la64_forward_in(p, ctrl, sp, st);
+}
+
+hipError_t la64_forward_pair(const LaProblem &pa, LaSpace sa, const LaProblem &pb, LaSpace sb, uint32_t *ctrl,
+                             hipStream_t st) {
+    const LaArgs a = la_args(pa, ctrl, sa), b = la_args(pb, ctrl, sb);
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    // one grid when each map alone would take the one-pass grid and the
+    // per-head ticket counters of both fit the control block
+    const bool one = a.segs <= cus && b.segs <= cus && a.BH + b.BH <= kMaxTicketHeads && la_decay(pa) == la_decay(pb);
+    if (one) {
+        const int ka = la_key_of(a, pa), kb = la_key_of(b, pb);
+        e = la_decay(pa) ? launch_la_pair<true>(a, b, st, ka, kb) : launch_la_pair<false>(a, b, st, ka, kb);
+        if (e != hipErrorInvalidValue) return e;
+        (void)hipGetLastError();
+    }
+    if ((e = la64_forward_in(pa, ctrl, sa, st)) != hipSuccess) return e;
+    return la64_forward_in(pb, ctrl, sb, st);
 }
 
 }  // namespace hla

@@ -180,10 +180,10 @@ hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
 // out += y; 2: oh, ol = bf16 hi and lo of y.  ql, kl, vl set: that operand is
 // the bf16 pair (x, xl); qf, kf, vf set: it is fp32 (and q, k, v unused).
 // q2 (or q2 + q2l, or q2f) set: a second set of queries against the same
-// keys and values, written to out2 (or oh2, ol2) with mode2.  Only the
-// combinations listed in la64_forward are built (hipErrorInvalidValue
-// otherwise).  The workspace is a forward workspace: control block, then
-// la64_workspace_bytes.
+// keys and values, written to out2 (or oh2, ol2) with mode2.  sym: plus the
+// map with keys and values exchanged.  Only the combinations listed in
+// fwd_la64.hip are built (hipErrorInvalidValue otherwise).  ctrl is the
+// one-launch kernels' control block (zero before first use).
 struct LaProblem {
     int B, H, n;
     const void *q, *k, *v;
@@ -201,9 +201,20 @@ struct LaProblem {
     bool sym;      // plus the map with keys and values exchanged (d = dv; values bf16 or a pair, keys bf16)
     GammaTab gam;
 };
-size_t la64_workspace_bytes(int BH, int n);
-size_t la64_flag_bytes(int BH, int n);  // the leading part of that data holding the flags
+// A map's flags (zero before their first use) and its segment aggregates.
+struct LaSpace {
+    uint32_t *flags;
+    float *aggC;
+};
+size_t la64_flag_bytes(int BH, int n);
+size_t la64_agg_bytes(int BH, int n);
+size_t la64_workspace_bytes(int BH, int n);  // la64_forward's data: the flags, then the aggregates
 hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
+hipError_t la64_forward_in(const LaProblem &p, uint32_t *ctrl, LaSpace sp, hipStream_t s);
+// Two maps that do not depend on each other, in one grid where the
+// combination is built and both fit a one-pass grid, else one after the other.
+hipError_t la64_forward_pair(const LaProblem &a, LaSpace sa, const LaProblem &b, LaSpace sb, uint32_t *ctrl,
+                             hipStream_t s);
 
 hipError_t state_compose(int count, int d, int dv, const hla_state &a, const hla_state &b,
                          const hla_state &r, hipStream_t s);

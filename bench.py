@@ -464,7 +464,7 @@ def forward_with_state(dev, stream):
 def backward_headline_shape(dev, stream):
     """hla_backward_chunked at B4 H8 n2048 d64 bf16: read q, k, v (bf16) and
     dout (fp32), write dq, dk, dv (fp32): 1408 B per head-token.  The plain
-    call takes the one-launch backward (seven first-order maps in five
+    call takes the one-launch backward (seven first-order maps in three
     launches); the shard's call (initial state, final-state gradient) the
     chunked fp32 backward."""
     import torch
@@ -494,7 +494,7 @@ def backward_headline_shape(dev, stream):
         hla.backward_chunked(q, k, v, dout, chunk=w.chunk, workspace=ws, grads=grads)
     us = time_calls(call, stream, 10, warmup=2)
     res = [{"workload": "masked_hla_bwd_B4_H8_n2048_d64_bf16_w64",
-            "entry": "hla_backward_chunked (seven first-order maps in five launches)",
+            "entry": "hla_backward_chunked (seven first-order maps in three launches)",
             "us_per_call": us, "single_call_us": dict(_LAST_PCT), "tokens_per_s": w.B * w.n / (us * 1e-6),
             "roofline": roof(tok * per_tok, us)}]
 
