@@ -20,10 +20,35 @@
 // symmetric.  After W, the maps fall into two pairs that do not depend on
 // each other, each pair one grid: three launches in all.
 //
+// With an initial state (S, C, m, G, h at position -1) and a gradient dF
+// flowing into the final state, the same maps carry the states' terms.  With
+// X' = S^T C - G and Y' = S^T m - h (the read-out of token t is (S_t q_t)^T
+// C_t, every entry of S its own variable), p = n - 1 - t, and the final
+// state's gradient folded into
+//   D_S = dS_F + C_n dG_F^T + m_n dh_F^T,  D_C = dC_F + S_n dG_F,
+//   D_m = dm_F + S_n dh_F,                 dX' = -dG_F,  dY' = -dh_F,
+// the maps take carries at position -1 of their own direction:
+//   U  = LA (Q, K, K; g)  from S_init               (final carry: S_n)
+//   W  = LA^rev (V, dO, Q; g^2) from g^-2 dX'^T, plus g^(2p) dY'
+//                                                   (final carry M_W)
+//   dq = LA (W, K, K; g) from S_init^T + LA (dO, V, U; g^2) from X'_init^T
+//        + g^p (D_C v_t + D_m)
+//   dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g) from g^-1 D_S, whose
+//        carry is symmetric                         (final carry M_K)
+//   dv = LA^rev (U, Q, dO; g^2) from g^-2 dX' + g^p D_C^T q_t
+// and the initial state's gradient is
+//   dX'_0 = g^2 M_W^T,  dY'_0 = g^(2n) dY',  dS = g M_K + C dX'_0^T + m dY'_0^T,
+//   dC = g^n D_C + S dX'_0,  dm = g^n D_m + S dY'_0,  dG = -dX'_0,  dh = -dY'_0
+// (pinned against the oracle on the CPU, tests/test_backward_algebra.py).
+// C_n comes from a map with keys Q and values V that forms no output, only
+// its final carry, and m_n from a reduction of the decayed queries.
+//
 // Workspace: the first kCtrlBytes are the one-launch kernels' control block,
-// then the flags of two maps, their aggregates, and the pairs of U and W.  The call clears
-// the control block and the flags itself (a fill kernel), so the backward
-// workspace needs no initialisation, as for the chunked path.
+// then the flags of two maps, their aggregates, the pairs of U and W, and
+// per head the states' matrices.  The call clears the control block and the
+// flags itself (a fill kernel), so the backward workspace needs no
+// initialisation, as for the chunked path.
+#include "bf16_split.h"
 #include "device_common.h"
 #include "hla_internal.h"
 
@@ -31,6 +56,14 @@ namespace hla {
 namespace {
 
 constexpr int kBw = 64;  // d = dv = chunk
+constexpr int kMSplits = 8;  // token ranges of the decayed query sums
+constexpr int kMat = kBw * kBw;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __global__ __launch_bounds__(256) void k_zero_words(uint32_t *p, size_t n) {
     for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
@@ -40,8 +73,291 @@ __global__ __launch_bounds__(256) void k_zero_words(uint32_t *p, size_t n) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLaLayout {
-    size_t flags, agg, uh, ul, wh, wl, total;
+    size_t flags, agg, uh, ul, wh, wl, state, total;
 };
+
+// the states' per-head matrices ([BH][64][64] fp32) and vectors ([BH][64])
+struct ShardBufs {
+    float *sinT, *xinT, *wc, *kc, *vc, *dc, *dcT, *sfin, *cfin, *mw, *mk;
+    float *wb, *dm, *mfin, *mpart;  // mpart: [BH][kMSplits][64]
+};
+constexpr int kShardMats = 11, kShardVecs = 3 + kMSplits;
+
+ShardBufs shard_bufs(char *base, int BH) {
+    float *f = reinterpret_cast<float *>(base);
+    const size_t M = static_cast<size_t>(BH) * kMat, V = static_cast<size_t>(BH) * kBw;
+    ShardBufs b{};
+    float **mats[kShardMats] = {&b.sinT, &b.xinT, &b.wc, &b.kc, &b.vc, &b.dc, &b.dcT, &b.sfin, &b.cfin, &b.mw, &b.mk};
+    for (int i = 0; i < kShardMats; ++i) *mats[i] = f + i * M;
+    f += kShardMats * M;
+    b.wb = f; b.dm = f + V; b.mfin = f + 2 * V; b.mpart = f + 3 * V;
+    return b;
+}
+
+struct ShardArgs {
+    int H, n;
+    GammaTab gam;
+    hla_state init;   // init.S null: the zero state
+    hla_state dfin;   // dfin.S null: no gradient into the final state
+    ShardBufs b;
+};
+
+__device__ __forceinline__ float bf16_word(const u32x4 &w, int e) {  // element e of 8 packed bf16
+    const uint32_t x = w[e >> 1];
+    return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+}
+
+// partial sums over token ranges of g^(n-1-t) q_t (for m_n): thread (rows
+// tid/8 + 32i, columns 8 (tid % 8) ..), its loads issued together
+__global__ __launch_bounds__(256) void k_msum(const uint16_t *q, int n, int H, GammaTab gam, float *mpart) {
+    __shared__ float red[32][kBw + 1];
+    const int bh = blockIdx.x, sp = blockIdx.y, cg = threadIdx.x & 7, tr = threadIdx.x >> 3;
+    const float lg = log2f(head_gamma(gam, bh % H));
+    const int per = (n + kMSplits - 1) / kMSplits, t0 = sp * per, t1 = min(n, t0 + per);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int tb = t0; tb < t1; tb += 256) {
+        u32x4 raw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = tb + tr + 32 * i;
+            raw[i] = t < t1 ? *reinterpret_cast<const u32x4 *>(q + (static_cast<size_t>(bh) * n + t) * kBw + 8 * cg)
+                            : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = tb + tr + 32 * i;
+            const float w = t < t1 ? exp2f(static_cast<float>(n - 1 - t) * lg) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, bf16_word(raw[i], e), acc[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tr][8 * cg + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < kBw) {
+        float sum = 0.0f;
+        for (int i = 0; i < 32; ++i) sum += red[i][threadIdx.x];
+        mpart[(static_cast<size_t>(bh) * kMSplits + sp) * kBw + threadIdx.x] = sum;
+    }
+}
+
+typedef float Lmat[kBw][kBw + 1];  // a 64 x 64 matrix in LDS, rows padded (conflict-free transposed writes)
+
+// row r, columns c0 .. c0 + 15 of a [64][64] matrix, 16 bytes at a time
+__device__ __forceinline__ void ld_row16(const float *m, int r, int c0, float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(m + r * kBw + c0 + 4 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
+    }
+}
+
+__device__ __forceinline__ void st_row16(float *m, int r, int c0, const float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4 *>(m + r * kBw + c0 + 4 * i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+}
+
+// stage a matrix into LDS, as it is or transposed (thread: row r, columns c0..)
+__device__ __forceinline__ void stage(Lmat &L, const float *m, int r, int c0, bool transpose) {
+    float x[16];
+    ld_row16(m, r, c0, x);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        if (transpose) L[c0 + c][r] = x[c];
+        else L[r][c0 + c] = x[c];
+    }
+}
+
+// thread (r, c0): out[c] = sum_l A[l][r] B[l][c0 + c]
+__device__ __forceinline__ void atb16(const Lmat &A, const Lmat &B, int r, int c0, float (&o)[16]) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] = 0.0f;
+    for (int l = 0; l < kBw; ++l) {
+        const float x = A[l][r];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[c] = fmaf(x, B[l][c0 + c], o[c]);
+    }
+}
+
+// Per head: the maps' carries and bias and the final state's folded terms
+// (see the header).  Needs S_n (sfin), C_n (cfin) and the query partials
+// when dfin is set.  Thread (r = tid / 4, c0 = 16 (tid % 4)) forms row r,
+// columns c0.. of every output.
+__global__ __launch_bounds__(256) void k_shard_prep(ShardArgs a) {
+    __shared__ Lmat L[8];  // S_0, C_0, G_0^T, C_n^T, dG_F^T, S_n^T, dG_F, dC_F^T
+    __shared__ float mnv[kBw], dhv[kBw];
+    const int bh = blockIdx.x, tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+    const float g = head_gamma(a.gam, bh % a.H), lg = log2f(g);
+    const bool ini = a.init.S != nullptr, fin = a.dfin.S != nullptr;
+    const size_t mo = static_cast<size_t>(bh) * kMat, vo = static_cast<size_t>(bh) * kBw;
+    if (ini) {
+        stage(L[0], a.init.S + mo, r, c0, false);
+        stage(L[1], a.init.C + mo, r, c0, false);
+        stage(L[2], a.init.G + mo, r, c0, true);
+    }
+    if (fin) {
+        stage(L[3], a.b.cfin + mo, r, c0, true);
+        stage(L[4], a.dfin.G + mo, r, c0, true);
+        stage(L[5], a.b.sfin + mo, r, c0, true);
+        stage(L[6], a.dfin.G + mo, r, c0, false);
+        stage(L[7], a.dfin.C + mo, r, c0, true);
+        if (tid < kBw) {  // m_n and dh_F
+            float part[kMSplits];
+#pragma unroll
+            for (int sp = 0; sp < kMSplits; ++sp) part[sp] = a.b.mpart[vo * kMSplits + sp * kBw + tid];
+            float mn = ini ? exp2f(static_cast<float>(a.n) * lg) * a.init.m[vo + tid] : 0.0f;
+#pragma unroll
+            for (int sp = 0; sp < kMSplits; ++sp) mn += part[sp];
+            mnv[tid] = mn;
+            dhv[tid] = a.dfin.h[vo + tid];
+        }
+    }
+    __syncthreads();
+    float x[16], y[16];
+    if (ini) {  // S_0^T (dq's first map) and X'_0^T, X'_0 = S_0^T C_0 - G_0 (its second)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = L[0][c0 + c][r];
+        st_row16(a.b.sinT + mo, r, c0, x);
+        atb16(L[1], L[0], r, c0, y);  // (C_0^T S_0)[r][c] = X'_0[c][r] + G_0[c][r]
+#pragma unroll
+        for (int c = 0; c < 16; ++c) y[c] -= L[2][r][c0 + c];
+        st_row16(a.b.xinT + mo, r, c0, y);
+    }
+    if (fin) {
+        const float ig = 1.0f / g, ig2 = ig * ig;
+        float d[16];
+        atb16(L[3], L[4], r, c0, y);  // (C_n dG_F^T)[r][c]
+        ld_row16(a.dfin.S + mo, r, c0, d);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = ig * (d[c] + y[c] + mnv[r] * dhv[c0 + c]);
+        st_row16(a.b.kc + mo, r, c0, x);  // g^-1 D_S
+        atb16(L[5], L[6], r, c0, y);  // (S_n dG_F)[r][c]
+        ld_row16(a.dfin.C + mo, r, c0, d);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = d[c] + y[c];
+        st_row16(a.b.dc + mo, r, c0, x);  // D_C
+        atb16(L[6], L[5], r, c0, y);  // (dG_F^T S_n^T)[r][c] = (S_n dG_F)[c][r]
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = L[7][r][c0 + c] + y[c];
+        st_row16(a.b.dcT + mo, r, c0, x);  // D_C^T
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            x[c] = -ig2 * L[4][r][c0 + c];  // W's carry: -g^-2 dG_F^T
+            y[c] = -ig2 * L[6][r][c0 + c];  // dv's carry: -g^-2 dG_F
+        }
+        st_row16(a.b.wc + mo, r, c0, x);
+        st_row16(a.b.vc + mo, r, c0, y);
+        if ((tid & 3) == 0) {
+            float sh = 0.0f;
+            for (int b2 = 0; b2 < kBw; ++b2) sh = fmaf(L[5][b2][r], dhv[b2], sh);
+            a.b.dm[vo + r] = a.dfin.m[vo + r] + sh;  // D_m
+            a.b.wb[vo + r] = -ig2 * dhv[r];        // W's bias: -g^-2 dh_F
+            a.b.mfin[vo + r] = mnv[r];
+        }
+    }
+}
+
+// dq_t += g^p (D_C v_t + D_m) and dv_t += g^p D_C^T q_t, p = n - 1 - t: per
+// 64-token block, wave w forms features 16w.. on the MFMA as (M x^T)^T, so
+// that a lane holds four consecutive features of one token (v and q are
+// exact bf16, D_C enters as a bf16 pair).
+__global__ __launch_bounds__(256) void k_shard_corr(const uint16_t *q, const uint16_t *v, int n, int H, GammaTab gam,
+                                                    const float *dc, const float *dcT, const float *dm, float *dq,
+                                                    float *dv) {
+    const int bh = blockIdx.x, tb0 = blockIdx.y * kBw, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int r = l & 15, g4 = l >> 4, c0 = 16 * wave;
+    const float lg = log2f(head_gamma(gam, bh % H));
+    const size_t mo = static_cast<size_t>(bh) * kMat, head = static_cast<size_t>(bh) * n;
+    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int prod = 0; prod < 2; ++prod) {
+        const uint16_t *x = prod == 0 ? v : q;  // out[t][c] = sum_k M[c][k] x_t[k]
+        const float *M = prod == 0 ? dc : dcT;
+        float *out = prod == 0 ? dq : dv;
+        bf16x8 mh[2], ml[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {  // A operand: lane (g4, r) holds M[c0 + r][32 ks + 8 g4 ..]
+            const float *row = M + mo + (c0 + r) * kBw + 32 * ks + 8 * g4;
+            pair_operand(*reinterpret_cast<const f32x4 *>(row), *reinterpret_cast<const f32x4 *>(row + 4), mh[ks], ml[ks]);
+        }
+        const f32x4 add = prod == 0 ? *reinterpret_cast<const f32x4 *>(dm + static_cast<size_t>(bh) * kBw + c0 + 4 * g4)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int t = tb0 + 16 * tb + r;  // this lane's token (B operand column and output row)
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 raw = t < n ? *reinterpret_cast<const u32x4 *>(x + (head + t) * kBw + 32 * ks + 8 * g4) : z4;
+                const bf16x8 xb = __builtin_bit_cast(bf16x8, raw);
+                acc = mfma(mh[ks], xb, acc);
+                acc = mfma(ml[ks], xb, acc);
+            }
+            if (t < n) {  // acc[e] = out[t][c0 + 4 g4 + e]
+                f32x4 *o = reinterpret_cast<f32x4 *>(out + (head + t) * kBw + c0 + 4 * g4);
+                *o += exp2f(static_cast<float>(n - 1 - t) * lg) * (acc + add);
+            }
+        }
+    }
+}
+
+// The initial state's gradient (see the header) from M_W, M_K and the folded
+// terms; thread (r, c0) forms row r, columns c0.. of each matrix part.
+__global__ __launch_bounds__(256) void k_shard_finish(ShardArgs a, hla_state dinit) {
+    __shared__ Lmat L[4];  // C_0^T, M_W, S_0^T, M_W^T
+    __shared__ float dyv[kBw];
+    const int bh = blockIdx.x, tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+    const float g = head_gamma(a.gam, bh % a.H), lg = log2f(g);
+    const float g2 = g * g, gn = exp2f(static_cast<float>(a.n) * lg), g2n = gn * gn;
+    const bool ini = a.init.S != nullptr, fin = a.dfin.S != nullptr;
+    const size_t mo = static_cast<size_t>(bh) * kMat, vo = static_cast<size_t>(bh) * kBw;
+    stage(L[1], a.b.mw + mo, r, c0, false);
+    stage(L[3], a.b.mw + mo, r, c0, true);
+    if (ini) {
+        stage(L[0], a.init.C + mo, r, c0, true);
+        stage(L[2], a.init.S + mo, r, c0, true);
+    }
+    if (tid < kBw) dyv[tid] = fin ? -g2n * a.dfin.h[vo + tid] : 0.0f;  // dY'_0
+    __syncthreads();
+    float x[16], y[16], m[16];
+    ld_row16(a.b.mk + mo, r, c0, m);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) x[c] = g * m[c];  // dS = g M_K + g^2 C_0 M_W + m_0 dY'_0^T
+    if (ini) {
+        atb16(L[0], L[1], r, c0, y);
+        const float m0 = a.init.m[vo + r];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] += g2 * y[c] + m0 * dyv[c0 + c];
+    }
+    st_row16(dinit.S + mo, r, c0, x);
+    if (fin) {  // dC = g^n D_C + g^2 S_0 M_W^T
+        ld_row16(a.b.dc + mo, r, c0, m);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = gn * m[c];
+    } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = 0.0f;
+    }
+    if (ini) {
+        atb16(L[2], L[3], r, c0, y);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] += g2 * y[c];
+    }
+    st_row16(dinit.C + mo, r, c0, x);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) x[c] = -g2 * L[3][r][c0 + c];  // dG = -dX'_0 = -g^2 M_W^T
+    st_row16(dinit.G + mo, r, c0, x);
+    if ((tid & 3) == 0) {  // dm = g^n D_m + S_0 dY'_0, dh = -dY'_0
+        float dmv = fin ? gn * a.b.dm[vo + r] : 0.0f;
+        if (ini && fin)
+            for (int b2 = 0; b2 < kBw; ++b2) dmv = fmaf(L[2][b2][r], dyv[b2], dmv);
+        dinit.m[vo + r] = dmv;
+        dinit.h[vo + r] = -dyv[r];
+        if (dinit.rho != nullptr && r == 0) dinit.rho[bh] = 0.0f;
+    }
+}
 
 BwdLaLayout bwd_la_layout(int BH, int n) {
     const size_t pair = static_cast<size_t>(BH) * n * kBw * sizeof(uint16_t);
@@ -52,7 +368,9 @@ BwdLaLayout bwd_la_layout(int BH, int n) {
     L.ul = align256(L.uh + pair);
     L.wh = align256(L.ul + pair);
     L.wl = align256(L.wh + pair);
-    L.total = L.wl + pair;
+    L.state = align256(L.wl + pair);
+    L.total = L.state + (static_cast<size_t>(kShardMats) * kMat + static_cast<size_t>(kShardVecs) * kBw) *
+                            static_cast<size_t>(BH) * sizeof(float);
     return L;
 }
 
@@ -61,8 +379,14 @@ BwdLaLayout bwd_la_layout(int BH, int n) {
 bool la_backward_eligible(const BwdProblem &p) {
     const FwdProblem &f = p.f;
     if (!(f.dtype == HLA_BF16 && f.d == kBw && f.dv == kBw && f.w == kBw && f.n > 0 && f.ridge == 0.0f &&
-          !f.normalize && f.init.S == nullptr && p.dinit.S == nullptr && p.dfinal.S == nullptr))
+          !f.normalize))
         return false;
+    // the states' matrices are read and written 16 bytes at a time
+    auto a16 = [](const hla_state &x) {
+        auto al = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; };
+        return x.S == nullptr || (al(x.S) && al(x.C) && al(x.G));
+    };
+    if (!(a16(f.init) && a16(p.dfinal) && a16(p.dinit))) return false;
     const int nh = f.gam.per_head ? f.H : 1;
     for (int h = 0; h < nh; ++h)
         if (f.gam.g[h] < 0.75f) return false;
@@ -102,22 +426,84 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
         m.rev = rev; m.gsq = gsq;
         return m;
     };
-    // W = LA^rev (V, dO, Q; g^2), as a pair
+    const bool states = f.init.S != nullptr || p.dfinal.S != nullptr || p.dinit.S != nullptr;
+    if (!states) {
+        // W = LA^rev (V, dO, Q; g^2), as a pair
+        LaProblem w = map(true, true);
+        w.q = f.v; w.kf = p.dout; w.v = f.q; w.mode = 2; w.oh = wh; w.ol = wl;
+        if ((e = la64_forward_in(w, ctrl, sa, st)) != hipSuccess) return e;
+        // U = LA (Q, K, K; g), as a pair, and dq = LA (W, K, K; g): two sets of queries;
+        // with dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g), the symmetric carry
+        LaProblem u = map(false, false), dk = map(true, false);
+        u.q = f.q; u.k = f.k; u.v = f.k; u.mode = 2; u.oh = uh; u.ol = ul;
+        u.q2 = wh; u.q2l = wl; u.mode2 = 0; u.out2 = p.dq;
+        dk.q = f.k; dk.k = f.q; dk.v = wh; dk.vl = wl; dk.mode = 0; dk.sym = true; dk.out = p.dk;
+        if ((e = la64_forward_pair(u, sa, dk, sb, ctrl, st)) != hipSuccess) return e;
+        // dq += LA (dO, V, U; g^2), with dv = LA^rev (U, Q, dO; g^2)
+        LaProblem dq = map(false, true), dv = map(true, true);
+        dq.qf = p.dout; dq.k = f.v; dq.v = uh; dq.vl = ul; dq.mode = 1; dq.out = p.dq;
+        dv.q = uh; dv.ql = ul; dv.k = f.q; dv.vf = p.dout; dv.mode = 0; dv.out = p.dv;
+        return la64_forward_pair(dq, sa, dv, sb, ctrl, st);
+    }
+
+    // ---- with states (the header's second identity) ----
+    const bool ini = f.init.S != nullptr, fin = p.dfinal.S != nullptr, dini = p.dinit.S != nullptr;
+    ShardArgs sh{};
+    sh.H = f.H; sh.n = f.n; sh.gam = f.gam;
+    if (ini) sh.init = f.init;
+    if (fin) sh.dfin = p.dfinal;
+    sh.b = shard_bufs(base + L.state, BH);
+    const uint16_t *q16 = static_cast<const uint16_t *>(f.q), *v16 = static_cast<const uint16_t *>(f.v);
+    // U from S_0 (its final carry S_n), and C_n from a map that forms no output
+    LaProblem u = map(false, false);
+    u.q = f.q; u.k = f.k; u.v = f.k; u.mode = 2; u.oh = uh; u.ol = ul;
+    u.init = ini ? f.init.S : nullptr;
+    if (fin) {
+        hipLaunchKernelGGL(k_msum, dim3(static_cast<unsigned>(BH), kMSplits), dim3(256), 0, st, q16, f.n, f.H, f.gam,
+                           sh.b.mpart);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        u.fin = sh.b.sfin;
+        LaProblem cn = map(false, false);
+        cn.q = f.q; cn.k = f.q; cn.v = f.v; cn.mode = 3; cn.init = ini ? f.init.C : nullptr; cn.fin = sh.b.cfin;
+        if ((e = la64_forward_pair(u, sa, cn, sb, ctrl, st)) != hipSuccess) return e;
+    } else if ((e = la64_forward_in(u, ctrl, sa, st)) != hipSuccess) {
+        return e;
+    }
+    if (ini || fin) {
+        hipLaunchKernelGGL(k_shard_prep, dim3(static_cast<unsigned>(BH)), dim3(256), 0, st, sh);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // W from g^-2 dX'^T with the bias g^(2p) dY' (its final carry M_W)
     LaProblem w = map(true, true);
     w.q = f.v; w.kf = p.dout; w.v = f.q; w.mode = 2; w.oh = wh; w.ol = wl;
+    if (fin) { w.init = sh.b.wc; w.bias = sh.b.wb; }
+    if (dini) w.fin = sh.b.mw;
     if ((e = la64_forward_in(w, ctrl, sa, st)) != hipSuccess) return e;
-    // U = LA (Q, K, K; g), as a pair, and dq = LA (W, K, K; g): two sets of queries;
-    // with dk = LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g), the symmetric carry
-    LaProblem u = map(false, false), dk = map(true, false);
-    u.q = f.q; u.k = f.k; u.v = f.k; u.mode = 2; u.oh = uh; u.ol = ul;
-    u.q2 = wh; u.q2l = wl; u.mode2 = 0; u.out2 = p.dq;
+    // dq = LA (W, K, K; g) from S_0^T, with dk from g^-1 D_S (its final carry M_K)
+    LaProblem dq1 = map(false, false), dk = map(true, false);
+    dq1.q = wh; dq1.ql = wl; dq1.k = f.k; dq1.v = f.k; dq1.mode = 0; dq1.out = p.dq;
+    if (ini) dq1.init = sh.b.sinT;
     dk.q = f.k; dk.k = f.q; dk.v = wh; dk.vl = wl; dk.mode = 0; dk.sym = true; dk.out = p.dk;
-    if ((e = la64_forward_pair(u, sa, dk, sb, ctrl, st)) != hipSuccess) return e;
-    // dq += LA (dO, V, U; g^2), with dv = LA^rev (U, Q, dO; g^2)
+    if (fin) dk.init = sh.b.kc;
+    if (dini) dk.fin = sh.b.mk;
+    if ((e = la64_forward_pair(dq1, sa, dk, sb, ctrl, st)) != hipSuccess) return e;
+    // dq += LA (dO, V, U; g^2) from X'_0^T, with dv from g^-2 dX'
     LaProblem dq = map(false, true), dv = map(true, true);
     dq.qf = p.dout; dq.k = f.v; dq.v = uh; dq.vl = ul; dq.mode = 1; dq.out = p.dq;
+    if (ini) dq.init = sh.b.xinT;
     dv.q = uh; dv.ql = ul; dv.k = f.q; dv.vf = p.dout; dv.mode = 0; dv.out = p.dv;
-    return la64_forward_pair(dq, sa, dv, sb, ctrl, st);
+    if (fin) dv.init = sh.b.vc;
+    if ((e = la64_forward_pair(dq, sa, dv, sb, ctrl, st)) != hipSuccess) return e;
+    if (fin) {  // the final state's C and m terms
+        hipLaunchKernelGGL(k_shard_corr, dim3(static_cast<unsigned>(BH), static_cast<unsigned>((f.n + kBw - 1) / kBw)),
+                           dim3(256), 0, st, q16, v16, f.n, f.H, f.gam, sh.b.dc, sh.b.dcT, sh.b.dm, p.dq, p.dv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (dini) {
+        hipLaunchKernelGGL(k_shard_finish, dim3(static_cast<unsigned>(BH)), dim3(256), 0, st, sh, p.dinit);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace hla

@@ -39,6 +39,11 @@
 // the key and value tiles exchanged.
 // Precision: A is split into bf16 hi + lo (its entries are fp32 sums), as are
 // the decayed key operand of the C sums and the carry C0.
+// Carries: an initial carry M_in at position -1 adds r^(p+1) M_in^T q_p to
+// the output at position p (its aggregate enters every segment's carry as a
+// segment before the first), and the last segment can write the carry after
+// the last token; a bias b adds r^(p+1) b.  Output mode kNone forms no
+// output, only that final carry.
 // k_la64 runs one map; k_la64_pair two maps that do not depend on each other
 // in one grid, so that their launches do not wait on each other's tails.
 #include "fast64_common.h"
@@ -55,7 +60,7 @@ constexpr int kLThreads = 512;
 constexpr int kLMaxL = 4;  // chunks per segment
 constexpr int kLWaves = 8;
 
-constexpr int kStore = 0, kAccumulate = 1, kSplit = 2;  // output modes (LaProblem::mode)
+constexpr int kStore = 0, kAccumulate = 1, kSplit = 2, kNone = 3;  // output modes (LaProblem::mode)
 
 struct LaArgs {
     int H, n, nc, P, L, BH, segs;
@@ -68,6 +73,9 @@ struct LaArgs {
     uint16_t *oh, *ol;      // kSplit: bf16 hi and lo of the result
     float *out2;            // the second queries' output
     uint16_t *oh2, *ol2;
+    const float *init;      // [BH][64 keys][64 values]: the carry at position -1 (null: zero)
+    float *fin;             // [BH][64][64]: receives the carry after the last token (null: not formed)
+    const float *bias;      // [BH][64]: y_t += r^(p+1) bias, p the position (null: none)
     uint32_t *ctrl;         // control block, as for the second-order kernel
     uint32_t *flags;        // [BH * P][8 waves] at kFlagStride words
     float *aggC;            // [BH * P][16 tiles][64 lanes][4]
@@ -207,7 +215,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                     if constexpr (decltype(mode)::value != 0) ql[i][ks] = __builtin_bit_cast(bf16x8, in ? lo : z4);
                 }
         };
-        load_q(IC<QM>{}, a.q, a.ql, a.qf, qr);
+        if constexpr (OUT != kNone) load_q(IC<QM>{}, a.q, a.ql, a.qf, qr);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -223,7 +231,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 if constexpr (VP) st16(T[16 + 2 * grp + jj], row, cg * 8, in ? vl_ : z4);
             }
         bf16x8 qn[2][2], qnl[2][2];
-        to_q(IC<QM>{}, qr, qn, qnl);
+        if constexpr (OUT != kNone) to_q(IC<QM>{}, qr, qn, qnl);
         __syncthreads();
 
         auto lane_base = [&](int off) __attribute__((always_inline)) {
@@ -375,12 +383,13 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 }
             }
         };
-        local_part(IC<QM>{}, qn, qnl);
+        if constexpr (OUT != kNone) local_part(IC<QM>{}, qn, qnl);
 
         // ================= the carry: C0 of every chunk -> LDS =======================
         const int seg_tokens = a.L * W;
         f32x4 c0seg[2] = {zero4, zero4};
-        {
+        const bool last = p == a.P - 1;
+        if (OUT != kNone || (a.fin != nullptr && last)) {
             bool failed = false;
             for (int pp = l; pp < p; pp += 64)
                 if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp), epoch, a.ctrl + kSpinWord)) {
@@ -407,11 +416,28 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                         for (int i = 0; i < 2; ++i) c0seg[i] += scl * x[s2][i];
                     }
             }
+            // this lane's elements of a [key a][value j] matrix of the head
+            auto mat_at = [&](int i) {
+                return static_cast<size_t>(bh) * 4096 + (16 * (cb + i) + r) * 64 + 16 * tb + 4 * g;
+            };
+            if (a.init != nullptr) {  // the carry at position -1, decayed to this segment's start
+                const float scl = gp(static_cast<float>(p * seg_tokens));
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    c0seg[i] += scl * *reinterpret_cast<const f32x4 *>(a.init + mat_at(i));
+            }
             if (bad) {  // a carry that could not be waited for: NaN, never a silently wrong number
                 const float nan = __builtin_nanf("");
                 c0seg[0] = c0seg[1] = f32x4{nan, nan, nan, nan};
             }
+            if (a.fin != nullptr && last) {  // the carry after the last token
+                const float scl = gp(static_cast<float>(a.n - c0 * W));
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    *reinterpret_cast<f32x4 *>(a.fin + mat_at(i)) = scl * c0seg[i] + crun[i];
+            }
         }
+        if constexpr (OUT != kNone) {
 #pragma unroll
         for (int c = 0; c < kLMaxL; ++c) {
             if (c < Lseg) {
@@ -430,7 +456,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
 
         // ================= output: num + e_t C0^T q_t ==============================
         auto output = [&](auto omode, auto qpair, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2], float *out,
-                          uint16_t *oh, uint16_t *ol) __attribute__((always_inline)) {
+                          uint16_t *oh, uint16_t *ol, const float *bias) __attribute__((always_inline)) {
             constexpr int OM = decltype(omode)::value;
             constexpr bool QP = decltype(qpair)::value != 0;
             if (Lcs == 0) return;
@@ -466,10 +492,14 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 const int tt = t0 + 16 * i;
                 if (tt < Lcs) {
                     const float e = gp(static_cast<float>(tt + 1));
-                    const size_t tok = at_pos((c0 + sc) * W + tt);
+                    const int pos = (c0 + sc) * W + tt;
+                    const size_t tok = at_pos(pos);
+                    const float eb = bias != nullptr ? gp(static_cast<float>(pos + 1)) : 0.0f;
 #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) {
                         f32x4 o = num[i][jb] + e * acc[i][jb];
+                        if (bias != nullptr)
+                            o += eb * *reinterpret_cast<const f32x4 *>(bias + static_cast<size_t>(bh) * W + 16 * jb + 4 * g);
                         const size_t at = tok * W + 16 * jb + 4 * g;
                         if constexpr (OM == kSplit) {
                             bf16x4 h, lo;
@@ -488,14 +518,15 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
         if constexpr (Q2) {  // the second queries' loads go out now, used after the first output
             u32x4 q2r[2][2][2];
             load_q(IC<Q2M>{}, a.q2, a.q2l, a.q2f, q2r);
-            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol);
+            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol, a.bias);
             bf16x8 qn2[2][2], qnl2[2][2];
             to_q(IC<Q2M>{}, q2r, qn2, qnl2);
             local_part(IC<Q2M>{}, qn2, qnl2);
-            output(IC<OUT2>{}, IC<Q2M>{}, qn2, qnl2, a.out2, a.oh2, a.ol2);
+            output(IC<OUT2>{}, IC<Q2M>{}, qn2, qnl2, a.out2, a.oh2, a.ol2, nullptr);
         } else {
-            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol);
+            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol, a.bias);
         }
+        }  // OUT != kNone
         __syncthreads();  // this segment's LDS reads are done before the next one is staged
     };
     // segments by ticket when they wait on each other (see fwd_fast64.hip)
@@ -617,6 +648,8 @@ hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int key) {
     HLA_LA(2, 0, 1, false, kAccumulate)           // backward: + LA (dO, V, U; g^2)
     HLA_LA(0, 0, 1, true, kStore, -1, 0, true)    // backward: LA^rev (K, Q, W; g) + LA^rev (K, W, Q; g)
     HLA_LA(1, 0, 2, true, kStore)                 // backward: LA^rev (U, Q, dO; g^2)
+    HLA_LA(1, 0, 0, false, kStore)                // backward with states: LA (W, K, K; g)
+    HLA_LA(0, 0, 0, false, kNone)                 // backward with states: the final carry of (Q, V; g)
 #undef HLA_LA
     return hipErrorInvalidValue;
 }
@@ -626,6 +659,9 @@ template <bool D> using MapUdq = LaMap<D, false, kSplit, 0, 0, 0, false, kStore,
 template <bool D> using MapDk = LaMap<D, false, kStore, 0, 0, 1, true, -1, 0, true>;
 template <bool D> using MapDq2 = LaMap<D, false, kAccumulate, 2, 0, 1, false>;
 template <bool D> using MapDv = LaMap<D, false, kStore, 1, 0, 2, true>;
+template <bool D> using MapU = LaMap<D, false, kSplit, 0, 0, 0, false>;
+template <bool D> using MapCfin = LaMap<D, false, kNone, 0, 0, 0, false>;
+template <bool D> using MapDq1 = LaMap<D, false, kStore, 1, 0, 0, false>;
 
 template <bool DECAY>
 hipError_t launch_la_pair(const LaArgs &a, const LaArgs &b, hipStream_t st, int ka, int kb) {
@@ -636,6 +672,14 @@ hipError_t launch_la_pair(const LaArgs &a, const LaArgs &b, hipStream_t st, int 
     }
     if (ka == la_key(2, 0, 1, false, kAccumulate) && kb == la_key(1, 0, 2, true, kStore)) {
         hipLaunchKernelGGL((k_la64_pair<MapDq2<DECAY>, MapDv<DECAY>>), grid, block, 0, st, a, b);
+        return hipGetLastError();
+    }
+    if (ka == la_key(0, 0, 0, false, kSplit) && kb == la_key(0, 0, 0, false, kNone)) {
+        hipLaunchKernelGGL((k_la64_pair<MapU<DECAY>, MapCfin<DECAY>>), grid, block, 0, st, a, b);
+        return hipGetLastError();
+    }
+    if (ka == la_key(1, 0, 0, false, kStore) && kb == la_key(0, 0, 1, true, kStore, -1, 0, true)) {
+        hipLaunchKernelGGL((k_la64_pair<MapDq1<DECAY>, MapDk<DECAY>>), grid, block, 0, st, a, b);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;
@@ -658,6 +702,7 @@ LaArgs la_args(const LaProblem &p, uint32_t *ctrl, LaSpace sp) {
     a.q2f = p.q2f;
     a.out2 = p.out2; a.oh2 = p.oh2; a.ol2 = p.ol2;
     a.out = p.out; a.oh = p.oh; a.ol = p.ol;
+    a.init = p.init; a.fin = p.fin; a.bias = p.bias;
     a.ctrl = ctrl;
     a.flags = sp.flags;
     a.aggC = sp.aggC;

@@ -181,7 +181,9 @@ hipError_t higher_decode(const HiDecodeProblem &p, hipStream_t s);
 // the bf16 pair (x, xl); qf, kf, vf set: it is fp32 (and q, k, v unused).
 // q2 (or q2 + q2l, or q2f) set: a second set of queries against the same
 // keys and values, written to out2 (or oh2, ol2) with mode2.  sym: plus the
-// map with keys and values exchanged.  Only the combinations listed in
+// map with keys and values exchanged.  mode 3: no output (only fin).  r is
+// the decay per token (g, or g^2 with gsq); p the position in the direction
+// of the map.  Only the combinations listed in
 // fwd_la64.hip are built (hipErrorInvalidValue otherwise).  ctrl is the
 // one-launch kernels' control block (zero before first use).
 struct LaProblem {
@@ -199,6 +201,9 @@ struct LaProblem {
     bool rev;
     bool gsq;      // the decay per token is g^2 (g from gam)
     bool sym;      // plus the map with keys and values exchanged (d = dv; values bf16 or a pair, keys bf16)
+    const float *init;  // [BH][64 keys][64 values] fp32: the carry at position -1 (null: zero)
+    float *fin;         // [BH][64][64]: receives the carry after the last token (null: not formed)
+    const float *bias;  // [BH][64]: out_p += r^(p+1) bias (null: none; first output only)
     GammaTab gam;
 };
 // A map's flags (zero before their first use) and its segment aggregates.

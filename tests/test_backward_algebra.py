@@ -169,3 +169,65 @@ def test_plain_gradient_is_first_order_maps(n, d, dv, g):
     assert rel(_la(dout, v, U, g * g) + _la(Wm, k, k, g), dq) < 1e-12
     assert rel(_la_rev(k, q, Wm, g) + _la_rev(k, Wm, q, g), dk) < 1e-12
     assert rel(_la_rev(U, q, dout, g * g), dvv) < 1e-12
+
+
+def _la_c(a, b, c, r, M):
+    """LA with a carry M at position -1: y_t = M_t^T a_t, M_t = r M_{t-1} + b_t c_t^T.
+    Returns y and the carry after the last token."""
+    y = np.zeros((a.shape[0], c.shape[1]))
+    for t in range(a.shape[0]):
+        M = r * M + np.outer(b[t], c[t])
+        y[t] = M.T @ a[t]
+    return y, M
+
+
+def _la_rev_c(a, b, c, r, M):
+    y, M = _la_c(a[::-1], b[::-1], c[::-1], r, M)
+    return y[::-1], M
+
+
+class _St:
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+@pytest.mark.parametrize("n,d,g", [(17, 4, 1.0), (23, 5, 0.9), (9, 3, 0.75), (1, 4, 0.8)])
+def test_state_gradients_are_first_order_maps_with_carries(n, d, g):
+    """With an initial state (S not symmetric) and a gradient flowing into the
+    final state: the maps above from carries at position -1 (their own
+    direction), two decayed terms, and the initial state's gradient from the
+    final carries of W and of dk's map (the identity written out in
+    bwd_la64.hip), against the oracle's autograd gradients."""
+    r = np.random.default_rng(100 + n + d)
+    q, k, v, dout = (0.5 * r.standard_normal((n, d)) for _ in range(4))
+    S0, C0, G0 = (r.standard_normal((d, d)) for _ in range(3))
+    m0, h0 = r.standard_normal(d), r.standard_normal(d)
+    dS, dC, dG = (r.standard_normal((d, d)) for _ in range(3))
+    dm, dh = r.standard_normal(d), r.standard_normal(d)
+    init = _St(S=S0[None], C=C0[None], m=m0[None], G=G0[None], h=h0[None])
+    dfin = _St(S=dS[None], C=dC[None], m=dm[None], G=dG[None], h=dh[None])
+    dq_r, dk_r, dv_r, di = ob.backward(q[None, None], k[None, None], v[None, None], dout[None, None], gamma=[g],
+                                       init=init, init_grad=True, dfinal=dfin)
+    g2, p = g * g, np.arange(n)[::-1].astype(float)  # p = n - 1 - t
+    U, Sn = _la_c(q, k, k, g, S0)
+    Cn = g ** n * C0 + sum(g ** (n - 1 - s) * np.outer(q[s], v[s]) for s in range(n))
+    mn = g ** n * m0 + sum(g ** (n - 1 - s) * q[s] for s in range(n))
+    DS, DC, Dm = dS + Cn @ dG.T + np.outer(mn, dh), dC + Sn @ dG, dm + Sn @ dh
+    dX, dY, X0 = -dG, -dh, S0.T @ C0 - G0
+    W, MW = _la_rev_c(v, dout, q, g2, dX.T / g2)
+    W = W + (g2 ** p)[:, None] * dY[None]
+    dq = (_la_c(W, k, k, g, S0.T)[0] + _la_c(dout, v, U, g2, X0.T)[0]
+          + (g ** p)[:, None] * (v @ DC.T + Dm[None]))
+    y1, MK = _la_rev_c(k, q, W, g, DS / g)
+    y2, MK2 = _la_rev_c(k, W, q, g, DS.T / g)
+    assert np.allclose(MK2, MK.T)  # one symmetric carry serves both maps of dk
+    dvv = _la_rev_c(U, q, dout, g2, dX / g2)[0] + (g ** p)[:, None] * (q @ DC)
+    dX0, dY0 = g2 * MW.T, g2 ** n * dY
+    parts = {"S": g * MK + C0 @ dX0.T + np.outer(m0, dY0), "C": g ** n * DC + S0 @ dX0,
+             "m": g ** n * Dm + S0 @ dY0, "G": -dX0, "h": -dY0}
+    rel = lambda a, b: np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)  # noqa: E731
+    assert rel(dq, dq_r[0, 0]) < 1e-12
+    assert rel(y1 + y2, dk_r[0, 0]) < 1e-12
+    assert rel(dvv, dv_r[0, 0]) < 1e-12
+    for name, x in parts.items():
+        assert rel(x, np.asarray(di[name])[0]) < 1e-12, name
