@@ -79,9 +79,9 @@ struct BwdLaLayout {
 // the states' per-head matrices ([BH][64][64] fp32) and vectors ([BH][64])
 struct ShardBufs {
     float *sinT, *xinT, *wc, *kc, *vc, *dc, *dcT, *sfin, *cfin, *mw, *mk;
-    float *wb, *dm, *mfin, *mpart;  // mpart: [BH][kMSplits][64]
+    float *wb, *dm, *mpart;  // mpart: [BH][kMSplits][64]
 };
-constexpr int kShardMats = 11, kShardVecs = 3 + kMSplits;
+constexpr int kShardMats = 11, kShardVecs = 2 + kMSplits;
 
 ShardBufs shard_bufs(char *base, int BH) {
     float *f = reinterpret_cast<float *>(base);
@@ -90,7 +90,7 @@ ShardBufs shard_bufs(char *base, int BH) {
     float **mats[kShardMats] = {&b.sinT, &b.xinT, &b.wc, &b.kc, &b.vc, &b.dc, &b.dcT, &b.sfin, &b.cfin, &b.mw, &b.mk};
     for (int i = 0; i < kShardMats; ++i) *mats[i] = f + i * M;
     f += kShardMats * M;
-    b.wb = f; b.dm = f + V; b.mfin = f + 2 * V; b.mpart = f + 3 * V;
+    b.wb = f; b.dm = f + V; b.mpart = f + 2 * V;
     return b;
 }
 
@@ -141,121 +141,159 @@ __global__ __launch_bounds__(256) void k_msum(const uint16_t *q, int n, int H, G
     }
 }
 
-typedef float Lmat[kBw][kBw + 1];  // a 64 x 64 matrix in LDS, rows padded (conflict-free transposed writes)
+typedef float Lmat[kBw][kBw];  // a 64 x 64 matrix in LDS
 
-// row r, columns c0 .. c0 + 15 of a [64][64] matrix, 16 bytes at a time
-__device__ __forceinline__ void ld_row16(const float *m, int r, int c0, float (&x)[16]) {
+// Thread tid of 256 owns the 4 x 4 block at rows r0 = 4 (tid / 16), columns
+// c0 = 4 (tid % 16) of every 64 x 64 matrix it stages or forms.
+struct Blk {
+    int r0, c0;
+};
+__device__ __forceinline__ Blk blk_of(int tid) { return Blk{4 * (tid >> 4), 4 * (tid & 15)}; }
+
+typedef f32x4 B4[4];  // a 4 x 4 block, by rows
+
+__device__ __forceinline__ void ld_blk(const float *m, Blk b, B4 &x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const f32x4 *>(m + (b.r0 + i) * kBw + b.c0);
+}
+
+__device__ __forceinline__ void st_blk(float *m, Blk b, const B4 &x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(m + (b.r0 + i) * kBw + b.c0) = x[i];
+}
+
+// the block of A^T B over LDS matrices: o[i][e] = sum_l A[l][r0 + i] B[l][c0 + e]
+__device__ __forceinline__ void atb(const Lmat &A, const Lmat &B, Blk b, B4 &o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int l = 0; l < kBw; ++l) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(&A[l][b.r0]);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(&B[l][b.c0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] += a[i] * x;
+    }
+}
+
+// a block read from LDS, transposed or not
+__device__ __forceinline__ void lds_blk(const Lmat &L, Blk b, bool transpose, B4 &x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(m + r * kBw + c0 + 4 * i);
+        if (transpose) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
+            for (int e = 0; e < 4; ++e) x[i][e] = L[b.c0 + e][b.r0 + i];
+        } else {
+            x[i] = *reinterpret_cast<const f32x4 *>(&L[b.r0 + i][b.c0]);
+        }
     }
 }
 
-__device__ __forceinline__ void st_row16(float *m, int r, int c0, const float (&x)[16]) {
+// put a block into LDS, as it is or transposed
+__device__ __forceinline__ void put_blk(Lmat &L, Blk b, const B4 &x, bool transpose) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<f32x4 *>(m + r * kBw + c0 + 4 * i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-}
-
-// stage a matrix into LDS, as it is or transposed (thread: row r, columns c0..)
-__device__ __forceinline__ void stage(Lmat &L, const float *m, int r, int c0, bool transpose) {
-    float x[16];
-    ld_row16(m, r, c0, x);
+    for (int i = 0; i < 4; ++i) {
+        if (transpose) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        if (transpose) L[c0 + c][r] = x[c];
-        else L[r][c0 + c] = x[c];
+            for (int e = 0; e < 4; ++e) L[b.c0 + e][b.r0 + i] = x[i][e];
+        } else {
+            *reinterpret_cast<f32x4 *>(&L[b.r0 + i][b.c0]) = x[i];
+        }
     }
 }
 
-// thread (r, c0): out[c] = sum_l A[l][r] B[l][c0 + c]
-__device__ __forceinline__ void atb16(const Lmat &A, const Lmat &B, int r, int c0, float (&o)[16]) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) o[c] = 0.0f;
-    for (int l = 0; l < kBw; ++l) {
-        const float x = A[l][r];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) o[c] = fmaf(x, B[l][c0 + c], o[c]);
-    }
-}
+constexpr int kPrepJobs = 3, kFinishJobs = 2;
 
-// Per head: the maps' carries and bias and the final state's folded terms
-// (see the header).  Needs S_n (sfin), C_n (cfin) and the query partials
-// when dfin is set.  Thread (r = tid / 4, c0 = 16 (tid % 4)) forms row r,
-// columns c0.. of every output.
+// Per head (blockIdx.x) and job (blockIdx.y), the maps' carries and bias
+// and the final state's folded terms (see the header); every load of a job
+// is issued before its first use.
+//   job 0: S_0^T (dq's first map), X'_0^T (its second), X'_0 = S_0^T C_0 - G_0
+//   job 1: g^-1 D_S (dk), D_S = dS_F + C_n dG_F^T + m_n dh_F^T
+//   job 2: D_C, D_C^T, D_m, W's and dv's carries -g^-2 dG_F^T, -g^-2 dG_F, W's bias -g^-2 dh_F
+// Jobs 1 and 2 need S_n (sfin), C_n (cfin) and the query partials.
 __global__ __launch_bounds__(256) void k_shard_prep(ShardArgs a) {
-    __shared__ Lmat L[8];  // S_0, C_0, G_0^T, C_n^T, dG_F^T, S_n^T, dG_F, dC_F^T
+    __shared__ Lmat L[3];
     __shared__ float mnv[kBw], dhv[kBw];
-    const int bh = blockIdx.x, tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+    const int bh = blockIdx.x, job = blockIdx.y, tid = threadIdx.x;
+    const Blk b = blk_of(tid);
     const float g = head_gamma(a.gam, bh % a.H), lg = log2f(g);
+    const float ig2 = 1.0f / (g * g);
     const bool ini = a.init.S != nullptr, fin = a.dfin.S != nullptr;
     const size_t mo = static_cast<size_t>(bh) * kMat, vo = static_cast<size_t>(bh) * kBw;
-    if (ini) {
-        stage(L[0], a.init.S + mo, r, c0, false);
-        stage(L[1], a.init.C + mo, r, c0, false);
-        stage(L[2], a.init.G + mo, r, c0, true);
+    B4 x, y, z, d;
+    if (job == 0) {
+        if (!ini) return;
+        ld_blk(a.init.S + mo, b, x);
+        ld_blk(a.init.C + mo, b, y);
+        ld_blk(a.init.G + mo, b, z);
+        put_blk(L[0], b, x, false);  // S_0
+        put_blk(L[1], b, y, false);  // C_0
+        put_blk(L[2], b, z, true);   // G_0^T
+        __syncthreads();
+        lds_blk(L[0], b, true, x);
+        st_blk(a.b.sinT + mo, b, x);
+        atb(L[1], L[0], b, y);  // (C_0^T S_0)[r][c] = X'_0[c][r] + G_0[c][r]
+        lds_blk(L[2], b, false, z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] -= z[i];
+        st_blk(a.b.xinT + mo, b, y);
+        return;
     }
-    if (fin) {
-        stage(L[3], a.b.cfin + mo, r, c0, true);
-        stage(L[4], a.dfin.G + mo, r, c0, true);
-        stage(L[5], a.b.sfin + mo, r, c0, true);
-        stage(L[6], a.dfin.G + mo, r, c0, false);
-        stage(L[7], a.dfin.C + mo, r, c0, true);
+    if (!fin) return;
+    if (job == 1) {
+        ld_blk(a.b.cfin + mo, b, x);
+        ld_blk(a.dfin.G + mo, b, y);
+        ld_blk(a.dfin.S + mo, b, d);
         if (tid < kBw) {  // m_n and dh_F
             float part[kMSplits];
 #pragma unroll
             for (int sp = 0; sp < kMSplits; ++sp) part[sp] = a.b.mpart[vo * kMSplits + sp * kBw + tid];
-            float mn = ini ? exp2f(static_cast<float>(a.n) * lg) * a.init.m[vo + tid] : 0.0f;
+            const float m0 = ini ? a.init.m[vo + tid] : 0.0f, dh = a.dfin.h[vo + tid];
+            float mn = exp2f(static_cast<float>(a.n) * lg) * m0;
 #pragma unroll
             for (int sp = 0; sp < kMSplits; ++sp) mn += part[sp];
             mnv[tid] = mn;
-            dhv[tid] = a.dfin.h[vo + tid];
+            dhv[tid] = dh;
         }
+        put_blk(L[0], b, x, true);  // C_n^T
+        put_blk(L[1], b, y, true);  // dG_F^T
+        __syncthreads();
+        atb(L[0], L[1], b, z);  // (C_n dG_F^T)[r][c]
+        const f32x4 dh4 = *reinterpret_cast<const f32x4 *>(&dhv[b.c0]);
+        const float ig = 1.0f / g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = ig * (d[i] + z[i] + mnv[b.r0 + i] * dh4);
+        st_blk(a.b.kc + mo, b, x);
+        return;
     }
+    ld_blk(a.b.sfin + mo, b, x);
+    ld_blk(a.dfin.G + mo, b, y);
+    ld_blk(a.dfin.C + mo, b, d);
+    if (tid < kBw) dhv[tid] = a.dfin.h[vo + tid];
+    put_blk(L[0], b, x, true);   // S_n^T
+    put_blk(L[1], b, y, false);  // dG_F
+    put_blk(L[2], b, d, false);  // dC_F
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] *= -ig2;
+    st_blk(a.b.vc + mo, b, y);   // dv's carry: -g^-2 dG_F
     __syncthreads();
-    float x[16], y[16];
-    if (ini) {  // S_0^T (dq's first map) and X'_0^T, X'_0 = S_0^T C_0 - G_0 (its second)
+    atb(L[0], L[1], b, z);  // (S_n dG_F)[r][c]
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] = L[0][c0 + c][r];
-        st_row16(a.b.sinT + mo, r, c0, x);
-        atb16(L[1], L[0], r, c0, y);  // (C_0^T S_0)[r][c] = X'_0[c][r] + G_0[c][r]
+    for (int i = 0; i < 4; ++i) x[i] = d[i] + z[i];
+    st_blk(a.b.dc + mo, b, x);   // D_C
+    atb(L[1], L[0], b, z);  // (dG_F^T S_n^T)[r][c] = (S_n dG_F)[c][r]
+    lds_blk(L[2], b, true, d);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) y[c] -= L[2][r][c0 + c];
-        st_row16(a.b.xinT + mo, r, c0, y);
-    }
-    if (fin) {
-        const float ig = 1.0f / g, ig2 = ig * ig;
-        float d[16];
-        atb16(L[3], L[4], r, c0, y);  // (C_n dG_F^T)[r][c]
-        ld_row16(a.dfin.S + mo, r, c0, d);
+    for (int i = 0; i < 4; ++i) x[i] = d[i] + z[i];
+    st_blk(a.b.dcT + mo, b, x);  // D_C^T
+    lds_blk(L[1], b, true, x);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] = ig * (d[c] + y[c] + mnv[r] * dhv[c0 + c]);
-        st_row16(a.b.kc + mo, r, c0, x);  // g^-1 D_S
-        atb16(L[5], L[6], r, c0, y);  // (S_n dG_F)[r][c]
-        ld_row16(a.dfin.C + mo, r, c0, d);
-#pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] = d[c] + y[c];
-        st_row16(a.b.dc + mo, r, c0, x);  // D_C
-        atb16(L[6], L[5], r, c0, y);  // (dG_F^T S_n^T)[r][c] = (S_n dG_F)[c][r]
-#pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] = L[7][r][c0 + c] + y[c];
-        st_row16(a.b.dcT + mo, r, c0, x);  // D_C^T
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            x[c] = -ig2 * L[4][r][c0 + c];  // W's carry: -g^-2 dG_F^T
-            y[c] = -ig2 * L[6][r][c0 + c];  // dv's carry: -g^-2 dG_F
-        }
-        st_row16(a.b.wc + mo, r, c0, x);
-        st_row16(a.b.vc + mo, r, c0, y);
-        if ((tid & 3) == 0) {
-            float sh = 0.0f;
-            for (int b2 = 0; b2 < kBw; ++b2) sh = fmaf(L[5][b2][r], dhv[b2], sh);
-            a.b.dm[vo + r] = a.dfin.m[vo + r] + sh;  // D_m
-            a.b.wb[vo + r] = -ig2 * dhv[r];        // W's bias: -g^-2 dh_F
-            a.b.mfin[vo + r] = mnv[r];
-        }
+    for (int i = 0; i < 4; ++i) x[i] *= -ig2;
+    st_blk(a.b.wc + mo, b, x);   // W's carry: -g^-2 dG_F^T
+    if (tid < kBw) {
+        float sh = 0.0f;
+        for (int b2 = 0; b2 < kBw; ++b2) sh = fmaf(L[0][b2][tid], dhv[b2], sh);
+        a.b.dm[vo + tid] = a.dfin.m[vo + tid] + sh;  // D_m
+        a.b.wb[vo + tid] = -ig2 * dhv[tid];         // W's bias
     }
 }
 
@@ -304,58 +342,67 @@ __global__ __launch_bounds__(256) void k_shard_corr(const uint16_t *q, const uin
 }
 
 // The initial state's gradient (see the header) from M_W, M_K and the folded
-// terms; thread (r, c0) forms row r, columns c0.. of each matrix part.
+// terms, per head (blockIdx.x) and job (blockIdx.y):
+//   job 0: dS = g M_K + g^2 C_0 M_W + m_0 dY'_0^T
+//   job 1: dC = g^n D_C + g^2 S_0 M_W^T, dG = -g^2 M_W^T, dm = g^n D_m + S_0 dY'_0, dh = -dY'_0
 __global__ __launch_bounds__(256) void k_shard_finish(ShardArgs a, hla_state dinit) {
-    __shared__ Lmat L[4];  // C_0^T, M_W, S_0^T, M_W^T
+    __shared__ Lmat L[2];
     __shared__ float dyv[kBw];
-    const int bh = blockIdx.x, tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+    const int bh = blockIdx.x, job = blockIdx.y, tid = threadIdx.x;
+    const Blk b = blk_of(tid);
     const float g = head_gamma(a.gam, bh % a.H), lg = log2f(g);
     const float g2 = g * g, gn = exp2f(static_cast<float>(a.n) * lg), g2n = gn * gn;
     const bool ini = a.init.S != nullptr, fin = a.dfin.S != nullptr;
     const size_t mo = static_cast<size_t>(bh) * kMat, vo = static_cast<size_t>(bh) * kBw;
-    stage(L[1], a.b.mw + mo, r, c0, false);
-    stage(L[3], a.b.mw + mo, r, c0, true);
-    if (ini) {
-        stage(L[0], a.init.C + mo, r, c0, true);
-        stage(L[2], a.init.S + mo, r, c0, true);
-    }
+    B4 x, y, w, m = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                     f32x4{0.f, 0.f, 0.f, 0.f}};
     if (tid < kBw) dyv[tid] = fin ? -g2n * a.dfin.h[vo + tid] : 0.0f;  // dY'_0
+    ld_blk(a.b.mw + mo, b, w);
+    if (job == 0) {
+        ld_blk(a.b.mk + mo, b, m);
+        if (ini) {
+            ld_blk(a.init.C + mo, b, x);
+            put_blk(L[0], b, x, true);   // C_0^T
+            put_blk(L[1], b, w, false);  // M_W
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = g * m[i];
+        if (ini) {
+            atb(L[0], L[1], b, y);
+            const f32x4 dy4 = *reinterpret_cast<const f32x4 *>(&dyv[b.c0]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] += g2 * y[i] + a.init.m[vo + b.r0 + i] * dy4;
+        }
+        st_blk(dinit.S + mo, b, x);
+        return;
+    }
+    if (fin) ld_blk(a.b.dc + mo, b, m);
+    if (ini) {
+        ld_blk(a.init.S + mo, b, x);
+        put_blk(L[0], b, x, true);  // S_0^T
+    }
+    put_blk(L[1], b, w, true);  // M_W^T
     __syncthreads();
-    float x[16], y[16], m[16];
-    ld_row16(a.b.mk + mo, r, c0, m);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) x[c] = g * m[c];  // dS = g M_K + g^2 C_0 M_W + m_0 dY'_0^T
+    for (int i = 0; i < 4; ++i) x[i] = gn * m[i];  // zero without dF
     if (ini) {
-        atb16(L[0], L[1], r, c0, y);
-        const float m0 = a.init.m[vo + r];
+        atb(L[0], L[1], b, y);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] += g2 * y[c] + m0 * dyv[c0 + c];
+        for (int i = 0; i < 4; ++i) x[i] += g2 * y[i];
     }
-    st_row16(dinit.S + mo, r, c0, x);
-    if (fin) {  // dC = g^n D_C + g^2 S_0 M_W^T
-        ld_row16(a.b.dc + mo, r, c0, m);
+    st_blk(dinit.C + mo, b, x);
+    lds_blk(L[1], b, false, x);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] = gn * m[c];
-    } else {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] = 0.0f;
-    }
-    if (ini) {
-        atb16(L[2], L[3], r, c0, y);
-#pragma unroll
-        for (int c = 0; c < 16; ++c) x[c] += g2 * y[c];
-    }
-    st_row16(dinit.C + mo, r, c0, x);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) x[c] = -g2 * L[3][r][c0 + c];  // dG = -dX'_0 = -g^2 M_W^T
-    st_row16(dinit.G + mo, r, c0, x);
-    if ((tid & 3) == 0) {  // dm = g^n D_m + S_0 dY'_0, dh = -dY'_0
-        float dmv = fin ? gn * a.b.dm[vo + r] : 0.0f;
+    for (int i = 0; i < 4; ++i) x[i] *= -g2;
+    st_blk(dinit.G + mo, b, x);
+    if (tid < kBw) {
+        float dmv = fin ? gn * a.b.dm[vo + tid] : 0.0f;
         if (ini && fin)
-            for (int b2 = 0; b2 < kBw; ++b2) dmv = fmaf(L[2][b2][r], dyv[b2], dmv);
-        dinit.m[vo + r] = dmv;
-        dinit.h[vo + r] = -dyv[r];
-        if (dinit.rho != nullptr && r == 0) dinit.rho[bh] = 0.0f;
+            for (int b2 = 0; b2 < kBw; ++b2) dmv = fmaf(L[0][b2][tid], dyv[b2], dmv);
+        dinit.m[vo + tid] = dmv;
+        dinit.h[vo + tid] = -dyv[tid];
+        if (dinit.rho != nullptr && tid == 0) dinit.rho[bh] = 0.0f;
     }
 }
 
@@ -470,7 +517,7 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
         return e;
     }
     if (ini || fin) {
-        hipLaunchKernelGGL(k_shard_prep, dim3(static_cast<unsigned>(BH)), dim3(256), 0, st, sh);
+        hipLaunchKernelGGL(k_shard_prep, dim3(static_cast<unsigned>(BH), kPrepJobs), dim3(256), 0, st, sh);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // W from g^-2 dX'^T with the bias g^(2p) dY' (its final carry M_W)
@@ -500,7 +547,7 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (dini) {
-        hipLaunchKernelGGL(k_shard_finish, dim3(static_cast<unsigned>(BH)), dim3(256), 0, st, sh, p.dinit);
+        hipLaunchKernelGGL(k_shard_finish, dim3(static_cast<unsigned>(BH), kFinishJobs), dim3(256), 0, st, sh, p.dinit);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
