@@ -537,9 +537,29 @@ def small_forward(dev, stream):
     ws = torch.zeros(hla.workspace_size(w.B, w.H, w.n, w.d, w.dv, dtype=w.dtype), dtype=torch.uint8,
                      device=dev)
     us = time_calls(lambda i: hla.forward_chunked(q, k, v, out=out, workspace=ws), stream, 50)
+    pct = dict(_LAST_PCT)
+    # the same calls replayed from a HIP graph: the launch cost without the host's
+    reps = 50
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            hla.forward_chunked(q, k, v, out=out, workspace=ws)
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "graph replay differs from the eager result"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / reps
     per_tok = 4 * (2 * w.d + 2 * w.dv)
-    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us, "single_call_us": dict(_LAST_PCT),
-                "tokens_per_s": w.B * w.n / (us * 1e-6),
+    res.append({"workload": w.name, "entry": "hla_forward_chunked", "us_per_call": us, "single_call_us": pct,
+                "graph_us_per_call": graph_us, "tokens_per_s": w.B * w.n / (us * 1e-6),
                 "roofline": roof(w.B * w.H * w.n * per_tok, us)})
     return res
 
