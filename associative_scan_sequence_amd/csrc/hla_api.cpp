@@ -128,7 +128,8 @@ hla_status check_common(int H, int d, int dv, int dtype, const float *gamma, flo
     return HLA_OK;
 }
 
-int default_chunk(int d) { return d > 64 ? 128 : 64; }
+// the chunk algebra costs O(w^2 d + w d^2) per chunk of w tokens, O(w d + d^2) per token: w = d
+int default_chunk(int d) { return d <= 16 ? 16 : (d <= 32 ? 32 : (d <= 64 ? 64 : 128)); }
 
 // Kernel path for a forward call.  init/fin/den only matter for the choice.
 enum class FwdPath { Generic, Fast64, Fused128 };

@@ -88,8 +88,7 @@ typedef struct {
     int32_t B, H;        /* batch and heads, >= 1                                 */
     int32_t n;           /* tokens per head, >= 0 (decode: must be 1)             */
     int32_t d, dv;       /* key/query width and value width, each 16, 32, 64, 128 */
-    int32_t chunk;       /* chunk width w: 16, 32, 64 or 128; 0 = default: 64,    */
-                         /* or 128 when d = 128                                   */
+    int32_t chunk;       /* chunk width w: 16, 32, 64 or 128; 0 = default: w = d  */
     hla_dtype dtype;     /* element type of q, k, v                               */
     const float *gamma;  /* HOST array [H] of decays in (0, 1]; NULL = no decay   */
     float ridge;         /* lambda >= 0                                           */
