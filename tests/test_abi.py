@@ -92,6 +92,16 @@ def test_workspace_size(lib):
     assert b > a
 
 
+@pytest.mark.parametrize("d,w", [(16, 16), (32, 32), (64, 64), (128, 128)])
+def test_default_chunk_is_d(lib, d, w):
+    """chunk = 0 takes w = d (the chunk algebra costs O(w d + d^2) per token):
+    the default call asks for the same workspace as the explicit chunk."""
+    for dtype in (0, 1):
+        size = lambda c: lib.hla_forward_workspace_size(  # noqa: E731
+            ctypes.byref(params(d=d, dv=d, n=1000, chunk=c, dtype=dtype)))
+        assert size(0) == size(w) > 0
+
+
 @pytest.mark.parametrize("kw,code,frag", [
     (dict(B=0), INVALID, "B="),
     (dict(H=0), INVALID, "H="),
