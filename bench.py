@@ -18,13 +18,14 @@ path (algorithmic q/k/v/out bytes per step over the measured step time,
 against 8 TB/s), and the fp64 CPU oracle timed on the host on a bounded
 sample of the same workload.  The line also carries ``workloads``: the
 other parts of the hot path (the ratio-normalised forward with decay and
-ridge, the long d=128 forward, the streaming decode step, state composition,
+ridge, the long d=128 forward with and without states, the streaming decode
+step, packed and multi-query decode, state composition, AHLA and third order,
 the small fp32 forward), and at the headline shape the forward that also
-returns its final state (the generic path a sequence shard runs) and the
-backward (plain, and as a sequence shard runs it: from an initial state, with a
-final-state gradient in and the initial-state gradient out), each timed with
-HIP events on its launch stream and
-set against its own HBM roofline (``--headline-only`` skips them).
+returns its final state or also starts from an initial state (the calls a
+sequence shard makes) and the backward (plain, and as a sequence shard runs
+it: from an initial state, with a final-state gradient in and the
+initial-state gradient out), each timed with HIP events on its launch stream
+and set against its own HBM roofline (``--headline-only`` skips them).
 """
 import argparse
 import json
@@ -465,8 +466,8 @@ def backward_headline_shape(dev, stream):
     """hla_backward_chunked at B4 H8 n2048 d64 bf16: read q, k, v (bf16) and
     dout (fp32), write dq, dk, dv (fp32): 1408 B per head-token.  The plain
     call takes the one-launch backward (seven first-order maps in three
-    launches); the shard's call (initial state, final-state gradient) the
-    chunked fp32 backward."""
+    launches); the shard's call (initial state, final-state gradient,
+    initial-state gradient) the same maps with carries in and out."""
     import torch
 
     import associative_scan_sequence_amd as hla
@@ -517,7 +518,7 @@ def backward_headline_shape(dev, stream):
                              dfinal=dfin, dinit=dini)
     us = time_calls(call_shard, stream, 10, warmup=2)
     res.append({"workload": "masked_hla_bwd_shard_B4_H8_n2048_d64_bf16_w64",
-                "entry": "hla_backward_chunked (init, dfinal in; dinit out)",
+                "entry": "hla_backward_chunked (init, dfinal in; dinit out; first-order maps with carries)",
                 "us_per_call": us, "single_call_us": dict(_LAST_PCT), "tokens_per_s": w.B * w.n / (us * 1e-6),
                 "roofline": roof(tok * per_tok + 3 * N * state_b, us)})
     return res
