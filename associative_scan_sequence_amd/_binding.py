@@ -513,7 +513,7 @@ def _higher_forward(third, q, k, v, gamma, normalize, chunk, init, return_state,
     size_fn = lib.hla_third_workspace_size if third else lib.hla_ahla_workspace_size
     need = int(size_fn(ctypes.byref(p)))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)  # control block zero before first use
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)  # zero-filled before first use
     if out is None:
         out = torch.empty(B, H, n, dv, dtype=torch.float32, device=dev)
     _need(out, "out", (torch.float32,))

@@ -319,10 +319,10 @@ typedef struct {
 } hla_third_state;
 
 /* Workspace bytes of the AHLA / third-order forward; 0 for an invalid p.
- * As for hla_forward_chunked, the first 8 KB are a control block that must
- * be zero before the workspace's first use (the one-launch kernels keep it
- * valid from call to call; a call never clears it); the rest needs no
- * initialisation.  bf16 calls with d = dv = 64, chunk 64, every decay >= 0.75,
+ * As for hla_forward_chunked, zero-fill the workspace once before its first
+ * use and write nothing in it afterwards: its first 8 KB are a control block
+ * and the flags that follow it are tagged with the launch epoch kept there,
+ * both kept valid from call to call (a call never clears them).  bf16 calls with d = dv = 64, chunk 64, every decay >= 0.75,
  * no denominator, ratio or state run one-launch kernels (AHLA as first-order
  * attention applied twice, third order as second-order HLA over first-order
  * attention values); every other call runs the chunked fp32 kernels. */
