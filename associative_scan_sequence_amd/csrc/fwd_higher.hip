@@ -398,11 +398,19 @@ struct FastHiLayout {
     size_t data, yh, yl, total;
 };
 
+// AHLA: the chained map's two spaces ([flags 1][flags 2][sums 1][sums 2]);
+// third order: the first map's space (or the second-order kernel's data,
+// whichever is larger), then its output as a bf16 pair
 FastHiLayout fast_layout(int BH, int n, bool third) {
     const size_t tok = static_cast<size_t>(BH) * n;
-    const size_t la = la64_workspace_bytes(BH, n), f64 = third ? fast64_workspace_bytes(BH, n) : 0;
     FastHiLayout L{};
     L.data = kCtrlBytes;
+    if (!third) {
+        L.yh = L.yl = 0;
+        L.total = L.data + 2 * (la64_flag_bytes(BH, n) + la64_agg_bytes(BH, n));
+        return L;
+    }
+    const size_t la = la64_workspace_bytes(BH, n), f64 = fast64_workspace_bytes(BH, n);
     L.yh = align256(L.data + (la > f64 ? la : f64));
     L.yl = align256(L.yh + tok * 64 * sizeof(uint16_t));
     L.total = L.yl + tok * 64 * sizeof(uint16_t);
@@ -425,18 +433,21 @@ hipError_t fast_higher(const HiProblem &p, hipStream_t st) {
     char *base = static_cast<char *>(p.ws);
     uint32_t *ctrl = reinterpret_cast<uint32_t *>(base);
     void *data = base + L.data;
-    uint16_t *yh = reinterpret_cast<uint16_t *>(base + L.yh), *yl = reinterpret_cast<uint16_t *>(base + L.yl);
     LaProblem la{};
     la.B = p.B; la.H = p.H; la.n = p.n; la.q = p.q; la.k = p.k; la.gam = p.gam;
+    if (!p.third) {  // out = LA (Q, K, LA (Q, K, V)) in one launch
+        const size_t fb = la64_flag_bytes(BH, p.n), ab = la64_agg_bytes(BH, p.n);
+        char *d = static_cast<char *>(data);
+        const LaSpace s1{reinterpret_cast<uint32_t *>(d), reinterpret_cast<float *>(d + 2 * fb)};
+        const LaSpace s2{reinterpret_cast<uint32_t *>(d + fb), reinterpret_cast<float *>(d + 2 * fb + ab)};
+        la.v = p.v; la.out = p.out; la.mode = 0;
+        return la64_chain(la, ctrl, s1, s2, st);
+    }
+    uint16_t *yh = reinterpret_cast<uint16_t *>(base + L.yh), *yl = reinterpret_cast<uint16_t *>(base + L.yl);
     // Y = LA(Q, K, V) as bf16 hi + lo
     la.v = p.v; la.oh = yh; la.ol = yl; la.mode = 2;
     hipError_t e = la64_forward(la, ctrl, data, st);
     if (e != hipSuccess) return e;
-    if (!p.third) {  // the second application on the pair (hi, lo) at once
-        la.oh = la.ol = nullptr; la.out = p.out;
-        la.v = yh; la.vl = yl; la.mode = 0;
-        return la64_forward(la, ctrl, data, st);
-    }
     FwdProblem f{};  // the second-order map on the pair (hi, lo) at once
     f.B = p.B; f.H = p.H; f.n = p.n; f.d = 64; f.dv = 64; f.w = 64; f.nc = (p.n + 63) / 64;
     f.dtype = HLA_BF16; f.q = p.q; f.k = p.k; f.gam = p.gam;

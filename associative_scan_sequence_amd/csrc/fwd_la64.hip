@@ -79,6 +79,8 @@ struct LaArgs {
     uint32_t *ctrl;         // control block, as for the second-order kernel
     uint32_t *flags;        // [BH * P][8 waves] at kFlagStride words
     float *aggC;            // [BH * P][16 tiles][64 lanes][4]
+    uint32_t *flags2;       // the chained map's second hand-off, laid out as flags and aggC
+    float *aggC2;
     GammaTab gam;
     float gexp;             // the decay per token is g^gexp (1, or 2 for the squared decay)
 };
@@ -128,18 +130,20 @@ __device__ __forceinline__ void to_pair(const u32x4 (&raw)[2], u32x4 &hi, u32x4 
 // One map: its segments are taken by nblocks workgroups, of which this is
 // number block; its per-head ticket counters start at counter head_base.
 // Returns the launch's epoch.
-template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2 = -1, int Q2M = 0, bool SYM = false>
+template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2 = -1, int Q2M = 0, bool SYM = false,
+          bool CH = false>
 struct LaMap {
-    static constexpr int kTiles = (KM != 0 || VM != 0) ? 20 : 16;
+    static constexpr int kTiles = (KM != 0 || VM != 0 || CH) ? 20 : 16;
     __device__ __forceinline__ static uint32_t run(const LaArgs &a, __bf16 (*T)[kTileElems], int block, int nblocks,
                                                    int head_base);
 };
 
-template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2, int Q2M, bool SYM>
-__device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT2, Q2M, SYM>::run(
+template <bool DECAY, bool LOOP, int OUT, int QM, int KM, int VM, bool REV, int OUT2, int Q2M, bool SYM, bool CH>
+__device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT2, Q2M, SYM, CH>::run(
     const LaArgs &a, __bf16 (*T)[kTileElems], int block, int nblocks, int head_base) {
     constexpr bool KP = KM != 0, VP = VM != 0, Q2 = OUT2 >= 0;
     static_assert(!(KP && VP), "the lo halves of keys and values share four tiles");
+    static_assert(!CH || (!KP && !VP && !SYM && !Q2 && OUT != kNone), "the chained map takes plain operands");
     const int tid = threadIdx.x;
     uint32_t ep_raw = 0;
     if ((tid & 63) == 0) ep_raw = __hip_atomic_load(&a.ctrl[kLine + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -243,7 +247,11 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
         // ================= tiles: the segment's C^T ================================
         // cpre[c] = sum of chunks 0..c-1 at chunk c's start; crun ends as C_seg.
         // Tile (j = 16tb+4g+e, a = 16(cb+i)+r) = sum_s V[s][j] f_s K[s][a].
-        f32x4 cpre[kLMaxL][2], crun[2] = {zero4, zero4};
+        // vpair: the values are a bf16 pair, hi in the value tiles and lo in T[16 + c]
+        f32x4 cpre[kLMaxL][2], crun[2];
+        auto csums = [&](auto vpair) __attribute__((always_inline)) {
+        constexpr bool VPX = VP || decltype(vpair)::value != 0;
+        crun[0] = crun[1] = zero4;
 #pragma unroll
         for (int c = 0; c < kLMaxL; ++c) {
 #pragma unroll
@@ -257,7 +265,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 const int rb = 32 * ks + 8 * g;
                 const bf16x8 vt = tr8(T[4 + c], rb, rb + 4, 16 * tb, r);
                 bf16x8 vtl;
-                if constexpr (VP) vtl = tr8(T[16 + c], rb, rb + 4, 16 * tb, r);
+                if constexpr (VPX) vtl = tr8(T[16 + c], rb, rb + 4, 16 * tb, r);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const bf16x8 kt = tr8(T[c], rb, rb + 4, 16 * (cb + i), r);
@@ -265,7 +273,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                     if constexpr (KP) ktl = tr8(T[16 + c], rb, rb + 4, 16 * (cb + i), r);
                     if (!DECAY) {
                         crun[i] = mfma(vt, kt, crun[i]);
-                        if constexpr (VP) crun[i] = mfma(vtl, kt, crun[i]);
+                        if constexpr (VPX) crun[i] = mfma(vtl, kt, crun[i]);
                         if constexpr (KP) crun[i] = mfma(vt, ktl, crun[i]);
                     } else {
                         // f_s = g^(Lc - 1 - s) for the tokens s = 32ks + 8g + e (+4)
@@ -280,7 +288,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                         pair_operand(x0, x1, h, lo);
                         crun[i] = mfma(vt, h, crun[i]);
                         crun[i] = mfma(vt, lo, crun[i]);
-                        if constexpr (VP) crun[i] = mfma(vtl, h, crun[i]);
+                        if constexpr (VPX) crun[i] = mfma(vtl, h, crun[i]);
                         if constexpr (KP) {  // the decayed lo half, rounded once: its own lo is ~2^-16 of the product
                             f32x4 y0, y1;
 #pragma unroll
@@ -296,23 +304,27 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 }
             }
         }
-        auto flag_of = [&](size_t sl) { return &a.flags[(sl * kLWaves + wave) * kFlagStride]; };
-        if (publish) {
-            put_tiles2(a.aggC + slot * 4096, wave, l, crun);
-            wait_stores();
-            if (l == 0) set_flag(flag_of(slot), epoch);
-        }
+        };
+        auto flag_of = [&](uint32_t *flags, size_t sl) { return &flags[(sl * kLWaves + wave) * kFlagStride]; };
+        auto publish_sums = [&](uint32_t *flags, float *aggC) __attribute__((always_inline)) {
+            if (publish) {
+                put_tiles2(aggC + slot * 4096, wave, l, crun);
+                wait_stores();
+                if (l == 0) set_flag(flag_of(flags, slot), epoch);
+            }
+        };
 
         // ================= slice: A^T and the local part A V =========================
         f32x4 num[2][4];
-        auto local = [&](auto hc, auto qpair, auto swap, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2])
-            __attribute__((always_inline)) {
+        auto local = [&](auto hc, auto qpair, auto swap, auto vpair, const bf16x8 (&qn)[2][2],
+                         const bf16x8 (&qnl)[2][2]) __attribute__((always_inline)) {
             constexpr int HH = decltype(hc)::value;
             constexpr bool QP = decltype(qpair)::value != 0;
             // swap: the keys are read from the value tiles and the values from the key tiles
             constexpr bool SW = decltype(swap)::value != 0;
+            constexpr bool VPX = VP || decltype(vpair)::value != 0;
             constexpr int KB = SW ? 4 : 0, VB = SW ? 0 : 4;
-            constexpr bool LKP = SW ? VP : KP, LVP = SW ? KP : VP;
+            constexpr bool LKP = SW ? VPX : KP, LVP = SW ? KP : VPX;
             const float lg_rg = lane_base(r - 4 * g);
             f32x4 at[2][4];
 #pragma unroll
@@ -368,31 +380,32 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 }
             }
         };
-        auto local_part = [&](auto qpair, const bf16x8 (&qh)[2][2], const bf16x8 (&ql)[2][2])
+        auto local_part = [&](auto qpair, auto vpair, const bf16x8 (&qh)[2][2], const bf16x8 (&ql)[2][2])
             __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) num[i][jb] = zero4;
             if (Lcs > 0) {
-                if (hh) local(IC<1>{}, qpair, IC<0>{}, qh, ql);
-                else local(IC<0>{}, qpair, IC<0>{}, qh, ql);
+                if (hh) local(IC<1>{}, qpair, IC<0>{}, vpair, qh, ql);
+                else local(IC<0>{}, qpair, IC<0>{}, vpair, qh, ql);
                 if constexpr (SYM) {
-                    if (hh) local(IC<1>{}, qpair, IC<1>{}, qh, ql);
-                    else local(IC<0>{}, qpair, IC<1>{}, qh, ql);
+                    if (hh) local(IC<1>{}, qpair, IC<1>{}, vpair, qh, ql);
+                    else local(IC<0>{}, qpair, IC<1>{}, vpair, qh, ql);
                 }
             }
         };
-        if constexpr (OUT != kNone) local_part(IC<QM>{}, qn, qnl);
-
         // ================= the carry: C0 of every chunk -> LDS =======================
+        // from the earlier segments' sums behind flags / aggC (with the initial
+        // carry and the final carry when states), then C0 of every chunk into
+        // T[8 + 2c] (hi), T[9 + 2c] (lo) when tiles
         const int seg_tokens = a.L * W;
-        f32x4 c0seg[2] = {zero4, zero4};
         const bool last = p == a.P - 1;
-        if (OUT != kNone || (a.fin != nullptr && last)) {
+        auto carry = [&](uint32_t *flags, const float *aggC, bool states, bool tiles) __attribute__((always_inline)) {
+            f32x4 c0seg[2] = {zero4, zero4};
             bool failed = false;
             for (int pp = l; pp < p; pp += 64)
-                if (!wait_flag(flag_of(static_cast<size_t>(bh) * a.P + pp), epoch, a.ctrl + kSpinWord)) {
+                if (!wait_flag(flag_of(flags, static_cast<size_t>(bh) * a.P + pp), epoch, a.ctrl + kSpinWord)) {
                     __hip_atomic_fetch_add(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     failed = true;
                 }
@@ -403,7 +416,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
 #pragma unroll
                 for (int s2 = 0; s2 < NB; ++s2)
                     if (p0 + s2 < p) {
-                        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.aggC + (static_cast<size_t>(bh) * a.P + p0 + s2) * 4096);
+                        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(aggC + (static_cast<size_t>(bh) * a.P + p0 + s2) * 4096);
 #pragma unroll
                         for (int i = 0; i < 2; ++i)
                             x[s2][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((2 * wave + i) * 64 + l) * 16, 0, kSc1);
@@ -420,7 +433,7 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
             auto mat_at = [&](int i) {
                 return static_cast<size_t>(bh) * 4096 + (16 * (cb + i) + r) * 64 + 16 * tb + 4 * g;
             };
-            if (a.init != nullptr) {  // the carry at position -1, decayed to this segment's start
+            if (states && a.init != nullptr) {  // the carry at position -1, decayed to this segment's start
                 const float scl = gp(static_cast<float>(p * seg_tokens));
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
@@ -430,37 +443,35 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 const float nan = __builtin_nanf("");
                 c0seg[0] = c0seg[1] = f32x4{nan, nan, nan, nan};
             }
-            if (a.fin != nullptr && last) {  // the carry after the last token
+            if (states && a.fin != nullptr && last) {  // the carry after the last token
                 const float scl = gp(static_cast<float>(a.n - c0 * W));
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
                     *reinterpret_cast<f32x4 *>(a.fin + mat_at(i)) = scl * c0seg[i] + crun[i];
             }
-        }
-        if constexpr (OUT != kNone) {
+            if (!tiles) return;
 #pragma unroll
-        for (int c = 0; c < kLMaxL; ++c) {
-            if (c < Lseg) {
-                const float d1 = gp(static_cast<float>(W * c));
+            for (int c = 0; c < kLMaxL; ++c) {
+                if (c < Lseg) {
+                    const float d1 = gp(static_cast<float>(W * c));
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    bf16x4 h, lo;
-                    split4(d1 * c0seg[i] + cpre[c][i], h, lo);
-                    // lane holds C0^T[j = 16tb+4g+e][a = 16(cb+i)+r]; tile rows a
-                    st4(T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
-                    st4(T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                    for (int i = 0; i < 2; ++i) {
+                        bf16x4 h, lo;
+                        split4(d1 * c0seg[i] + cpre[c][i], h, lo);
+                        // lane holds C0^T[j = 16tb+4g+e][a = 16(cb+i)+r]; tile rows a
+                        st4(T[8 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, h);
+                        st4(T[9 + 2 * c], 16 * (cb + i) + r, 16 * tb + 4 * g, lo);
+                    }
                 }
             }
-        }
-        __syncthreads();
+            __syncthreads();
+        };
 
         // ================= output: num + e_t C0^T q_t ==============================
-        auto output = [&](auto omode, auto qpair, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2], float *out,
-                          uint16_t *oh, uint16_t *ol, const float *bias) __attribute__((always_inline)) {
-            constexpr int OM = decltype(omode)::value;
+        // acc[i][jb]: lane (g, r) holds (C0^T q_t)[16 jb + 4g + e] for t = t0 + 16 i
+        auto carry_term = [&](auto qpair, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2], f32x4 (&acc)[2][4])
+            __attribute__((always_inline)) {
             constexpr bool QP = decltype(qpair)::value != 0;
-            if (Lcs == 0) return;
-            f32x4 acc[2][4];
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
                 acc[0][jb] = acc[1][jb] = zero4;
@@ -487,6 +498,13 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                     }
                 }
             }
+        };
+        auto output = [&](auto omode, auto qpair, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2], float *out,
+                          uint16_t *oh, uint16_t *ol, const float *bias) __attribute__((always_inline)) {
+            constexpr int OM = decltype(omode)::value;
+            if (Lcs == 0) return;
+            f32x4 acc[2][4];
+            carry_term(qpair, qn, qnl, acc);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int tt = t0 + 16 * i;
@@ -515,18 +533,63 @@ __device__ __forceinline__ uint32_t LaMap<DECAY, LOOP, OUT, QM, KM, VM, REV, OUT
                 }
             }
         };
-        if constexpr (Q2) {  // the second queries' loads go out now, used after the first output
-            u32x4 q2r[2][2][2];
-            load_q(IC<Q2M>{}, a.q2, a.q2l, a.q2f, q2r);
+        // the chained map's first output, as the second one's values: the bf16
+        // pair of every row of this slice (zero past the chunk) into the value
+        // tiles, hi in T[4 + sc] and lo in T[16 + sc]
+        auto output_values = [&](auto qpair, const bf16x8 (&qn)[2][2], const bf16x8 (&qnl)[2][2])
+            __attribute__((always_inline)) {
+            f32x4 acc[2][4];
+            if (Lcs > 0) carry_term(qpair, qn, qnl, acc);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = t0 + 16 * i;
+                const float e = gp(static_cast<float>(tt + 1));
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const f32x4 o = tt < Lcs ? num[i][jb] + e * acc[i][jb] : zero4;
+                    bf16x4 h, lo;
+                    split4(o, h, lo);
+                    st4(T[4 + sc], tt, 16 * jb + 4 * g, h);
+                    st4(T[16 + sc], tt, 16 * jb + 4 * g, lo);
+                }
+            }
+        };
+
+        if constexpr (CH) {
+            // the first map: its output stays in LDS as the second map's values
+            csums(IC<0>{});
+            publish_sums(a.flags, a.aggC);
+            local_part(IC<QM>{}, IC<0>{}, qn, qnl);
+            carry(a.flags, a.aggC, false, true);
+            output_values(IC<QM>{}, qn, qnl);
+            __syncthreads();
+            // the second map over those values (a pair), with its own hand-off
+            csums(IC<1>{});
+            publish_sums(a.flags2, a.aggC2);
+            local_part(IC<QM>{}, IC<1>{}, qn, qnl);
+            carry(a.flags2, a.aggC2, true, true);
             output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol, a.bias);
-            bf16x8 qn2[2][2], qnl2[2][2];
-            to_q(IC<Q2M>{}, q2r, qn2, qnl2);
-            local_part(IC<Q2M>{}, qn2, qnl2);
-            output(IC<OUT2>{}, IC<Q2M>{}, qn2, qnl2, a.out2, a.oh2, a.ol2, nullptr);
         } else {
-            output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol, a.bias);
+            csums(IC<0>{});
+            publish_sums(a.flags, a.aggC);
+            if constexpr (OUT != kNone) {
+                local_part(IC<QM>{}, IC<0>{}, qn, qnl);
+                carry(a.flags, a.aggC, true, true);
+                if constexpr (Q2) {  // the second queries' loads go out now, used after the first output
+                    u32x4 q2r[2][2][2];
+                    load_q(IC<Q2M>{}, a.q2, a.q2l, a.q2f, q2r);
+                    output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol, a.bias);
+                    bf16x8 qn2[2][2], qnl2[2][2];
+                    to_q(IC<Q2M>{}, q2r, qn2, qnl2);
+                    local_part(IC<Q2M>{}, IC<0>{}, qn2, qnl2);
+                    output(IC<OUT2>{}, IC<Q2M>{}, qn2, qnl2, a.out2, a.oh2, a.ol2, nullptr);
+                } else {
+                    output(IC<OUT>{}, IC<QM>{}, qn, qnl, a.out, a.oh, a.ol, a.bias);
+                }
+            } else if (a.fin != nullptr && last) {  // only the final carry
+                carry(a.flags, a.aggC, true, false);
+            }
         }
-        }  // OUT != kNone
         __syncthreads();  // this segment's LDS reads are done before the next one is staged
     };
     // segments by ticket when they wait on each other (see fwd_fast64.hip)
@@ -619,16 +682,17 @@ void la_geometry(int BH, int nc, int *P, int *L) {
 }
 
 // key of an operand/direction/output combination
-constexpr int la_key(int qm, int km, int vm, bool rev, int mode, int mode2 = -1, int q2m = 0, bool sym = false) {
+constexpr int la_key(int qm, int km, int vm, bool rev, int mode, int mode2 = -1, int q2m = 0, bool sym = false,
+                     bool ch = false) {
     return qm | (km << 2) | (vm << 4) | (rev ? 64 : 0) | (mode << 7) | (mode2 >= 0 ? ((1 + mode2) << 9) | (q2m << 11) : 0) |
-           (sym ? 1 << 13 : 0);
+           (sym ? 1 << 13 : 0) | (ch ? 1 << 14 : 0);
 }
 
 int la_key_of(const LaArgs &a, const LaProblem &p) {
     const int qm = a.qf ? 2 : (a.ql ? 1 : 0), km = a.kf ? 2 : (a.kl ? 1 : 0), vm = a.vf ? 2 : (a.vl ? 1 : 0);
     const int q2m = a.q2f ? 2 : (a.q2l ? 1 : 0);
     const bool two = a.q2 != nullptr || a.q2f != nullptr;
-    return la_key(qm, km, vm, p.rev, p.mode, two ? p.mode2 : -1, two ? q2m : 0, p.sym);
+    return la_key(qm, km, vm, p.rev, p.mode, two ? p.mode2 : -1, two ? q2m : 0, p.sym, p.chain);
 }
 
 // the operand/direction/output combinations the library uses
@@ -650,6 +714,7 @@ hipError_t launch_la(const LaArgs &a, dim3 grid, hipStream_t st, int key) {
     HLA_LA(1, 0, 2, true, kStore)                 // backward: LA^rev (U, Q, dO; g^2)
     HLA_LA(1, 0, 0, false, kStore)                // backward with states: LA (W, K, K; g)
     HLA_LA(0, 0, 0, false, kNone)                 // backward with states: the final carry of (Q, V; g)
+    HLA_LA(0, 0, 0, false, kStore, -1, 0, false, true)  // AHLA: LA (Q, K, LA (Q, K, V)) chained
 #undef HLA_LA
     return hipErrorInvalidValue;
 }
@@ -759,6 +824,22 @@ hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStrea
     char *base = static_cast<char *>(data);
     const LaSpace sp{reinterpret_cast<uint32_t *>(base), reinterpret_cast<float *>(base + la64_flag_bytes(BH, p.n))};
     return la64_forward_in(p, ctrl, sp, st);
+}
+
+hipError_t la64_chain(const LaProblem &p, uint32_t *ctrl, LaSpace s1, LaSpace s2, hipStream_t st) {
+    LaProblem q = p;
+    q.chain = true;
+    LaArgs a = la_args(q, ctrl, s1);
+    a.flags2 = s2.flags;
+    a.aggC2 = s2.aggC;
+    int cus = 0;
+    const hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const bool loop = a.segs > cus || (a.P > 1 && a.BH > kMaxTicketHeads);
+    const dim3 grid(static_cast<unsigned>(loop ? cus : a.segs));
+    const int key = la_key_of(a, q);
+    if (la_decay(q)) return loop ? launch_la<true, true>(a, grid, st, key) : launch_la<true, false>(a, grid, st, key);
+    return loop ? launch_la<false, true>(a, grid, st, key) : launch_la<false, false>(a, grid, st, key);
 }
 
 hipError_t la64_forward_pair(const LaProblem &pa, LaSpace sa, const LaProblem &pb, LaSpace sb, uint32_t *ctrl,

@@ -204,6 +204,7 @@ struct LaProblem {
     const float *init;  // [BH][64 keys][64 values] fp32: the carry at position -1 (null: zero)
     float *fin;         // [BH][64][64]: receives the carry after the last token (null: not formed)
     const float *bias;  // [BH][64]: out_p += r^(p+1) bias (null: none; first output only)
+    bool chain;         // set by la64_chain
     GammaTab gam;
 };
 // A map's flags (zero before their first use) and its segment aggregates.
@@ -216,6 +217,11 @@ size_t la64_agg_bytes(int BH, int n);
 size_t la64_workspace_bytes(int BH, int n);  // la64_forward's data: the flags, then the aggregates
 hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
 hipError_t la64_forward_in(const LaProblem &p, uint32_t *ctrl, LaSpace sp, hipStream_t s);
+// The map applied twice in one launch, out = LA (Q, K, LA (Q, K, V)): the
+// first map's output stays in LDS as the second's values (a bf16 pair); each
+// map hands its segment sums over through its own space.  q, k, v bf16;
+// mode store.
+hipError_t la64_chain(const LaProblem &p, uint32_t *ctrl, LaSpace s1, LaSpace s2, hipStream_t s);
 // Two maps that do not depend on each other, in one grid where the
 // combination is built and both fit a one-pass grid, else one after the other.
 hipError_t la64_forward_pair(const LaProblem &a, LaSpace sa, const LaProblem &b, LaSpace sb, uint32_t *ctrl,

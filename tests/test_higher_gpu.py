@@ -242,11 +242,13 @@ ONE_LAUNCH = [  # B, H, n: the bench shape (one segment of four chunks per workg
 @pytest.mark.parametrize("third", [False, True])
 @pytest.mark.parametrize("B,H,n", ONE_LAUNCH)
 def test_one_launch_path(third, B, H, n):
-    """bf16, d = dv = 64, chunk 64, numerator only: two one-launch kernels
-    each.  The first-order map gives the intermediate values as a bf16 pair;
-    the second map (first order for AHLA, second order for third order) takes
-    that pair as its values.  The control block counts the launches and shows
-    that no wait gave up.  AHLA with a decay per head down to 0.75."""
+    """bf16, d = dv = 64, chunk 64, numerator only.  The first-order map
+    gives the intermediate values as a bf16 pair, and the second map (first
+    order for AHLA, second order for third order) takes that pair as its
+    values: for AHLA both maps in one launch, the pair kept in LDS (two
+    hand-offs); for third order two launches, the pair through HBM.  The
+    control block counts the launches and shows that no wait gave up.  AHLA
+    with a decay per head down to 0.75."""
     q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=1700 + n + H + int(third))
     g = None if third else inputs.gamma_list_fp32([(0.75, 0.9, 0.97, 1.0, 0.999, 0.8, 0.95, 0.99)[h % 8]
                                                    for h in range(H)])
@@ -258,7 +260,7 @@ def test_one_launch_path(third, B, H, n):
     out, _, _ = fwd(*on_gpu(q, k, v), chunk=64, workspace=ws, **kw)
     torch.cuda.synchronize()
     words = ws[:16].view(torch.int32).cpu().tolist()
-    assert words[2] == 2 and words[3] == 0, words
+    assert words[2] == (2 if third else 1) and words[3] == 0, words
     ro, _, _ = (higher.third_forward(q, k, v, want_state=False) if third
                 else higher.ahla_forward(q, k, v, gamma=g, want_state=False))
     e = row_err(out.cpu(), ro)
@@ -267,4 +269,4 @@ def test_one_launch_path(third, B, H, n):
     out2, _, _ = fwd(*on_gpu(q, k, v), chunk=64, workspace=ws, **kw)  # the same workspace again
     torch.cuda.synchronize()
     assert torch.equal(out2, out)
-    assert ws[:16].view(torch.int32).cpu().tolist()[2] == 4
+    assert ws[:16].view(torch.int32).cpu().tolist()[2] == (4 if third else 2)
