@@ -270,3 +270,35 @@ def test_one_launch_path(third, B, H, n):
     torch.cuda.synchronize()
     assert torch.equal(out2, out)
     assert ws[:16].view(torch.int32).cpu().tolist()[2] == (4 if third else 2)
+
+
+def test_one_launch_ahla_give_up_poisons_and_recovers():
+    """With control word 4 = -1 the chained AHLA launch's waits give up after
+    one unsuccessful poll (both hand-offs).  Every output row is then the
+    normal bits or holds a NaN, the first chunk of each head (its segment
+    waits on nothing) is exact, and NaN rows appear exactly when a wait gave
+    up.  With word 4 back to 0 the next call on the same workspace gives the
+    normal bits again."""
+    B, H, n = 4, 8, 2048
+    q, k, v = inputs.qkv(B, H, n, 64, 64, torch.bfloat16, seed=1750)
+    g = inputs.gamma_list_fp32([(0.75, 0.9, 0.97, 1.0, 0.999, 0.8, 0.95, 0.99)[h % 8] for h in range(H)])
+    p, _keep = hla._binding._params(B, H, n, 64, 64, 64, torch.bfloat16, g, 0.0, False)
+    ws = torch.zeros(int(hla._binding.load().hla_ahla_workspace_size(hla._binding.ctypes.byref(p))),
+                     dtype=torch.uint8, device=DEV)
+    qg, kg, vg = on_gpu(q, k, v)
+    ref, _, _ = hla.ahla_forward(qg, kg, vg, gamma=g, chunk=64, workspace=ws)
+    words = ws[:64].view(torch.int32)
+    words[4] = -1
+    out, _, _ = hla.ahla_forward(qg, kg, vg, gamma=g, chunk=64, workspace=ws)
+    torch.cuda.synchronize()
+    w = words.cpu().tolist()
+    assert w[2] == 2, w
+    rows_nan = torch.isnan(out).any(dim=-1)
+    rows_same = (out == ref).all(dim=-1)
+    assert bool((rows_nan | rows_same).all()), "a row is neither NaN nor the normal result"
+    assert bool(rows_same[:, :, :64].all()), "the first chunk of a head waits on nothing"
+    assert bool(rows_nan.any()) == (w[3] > 0)
+    words[4] = 0
+    again, _, _ = hla.ahla_forward(qg, kg, vg, gamma=g, chunk=64, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref)
