@@ -79,7 +79,8 @@ def check(got, ref):
 
 CASES = [  # B, H, n, gamma: one segment of four chunks per workgroup at the headline
     (4, 8, 2048, None), (2, 3, 64 * 13 + 37, "per_head"),  # shape; ragged one-chunk segments;
-    (4, 8, 64 * 32 + 37, "decay"), (1, 2, 50, "per_head"), (2, 1, 1, None)]  # a looped grid; one segment; one token
+    (4, 8, 64 * 32 + 37, "decay"), (1, 2, 50, "per_head"), (2, 1, 1, None),  # a looped grid; one segment; one token
+    (2, 64, 100, "per_head")]  # more heads than two maps' ticket counters: the pairs launch one after the other
 
 
 @pytest.mark.parametrize("B,H,n,gk", CASES)

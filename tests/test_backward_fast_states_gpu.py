@@ -148,6 +148,7 @@ CASES = [  # B, H, n, gamma, init, dfinal, dinit, S symmetric
     (1, 2, 150, None, True, False, False, True),            # an initial state only
     (1, 2, 150, "decay", False, True, False, True),         # a final-state gradient only
     (1, 2, 150, "per_head", False, False, True, True),      # the zero state's gradient only
+    (2, 64, 100, "decay", True, True, True, False),         # more heads than two maps' ticket counters
 ]
 
 
