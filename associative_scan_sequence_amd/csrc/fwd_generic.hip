@@ -24,7 +24,8 @@
 //           y0' = rho^2 y0 + U^T f^2
 //
 // Kernels (one workgroup of 256 threads per chunk unless stated):
-//   k_init_slot   per head: slot 0 = init (X = S C - G) or zeros
+//   k_init_slot   per head: slot 0 = init (X = S C - G); without init (and
+//                 n > 0) the scans write slot 0's zeros themselves
 //   k_chunk_sums  K^T diag(f) K, Q^T diag(f) V, Q^T f     -> slot c+1
 //   k_prefix      per head, elementwise: slot c+1 = rho^p slot c + slot c+1
 //   k_chunk_uz    A, U (kept for the output pass), U^T diag(f^2) V, U^T f^2
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_prefix(GenArgs a, ScanSeg s0, Scan
     const int Llast = a.n - (a.nc - 1) * a.w;
     const float rf = gpow(g, power * a.w), rl = gpow(g, power * Llast);
     float *p = seg.base + static_cast<size_t>(bh) * (a.nc + 1) * seg.E + e;
+    if (a.init.S == nullptr) p[0] = 0.0f;  // the zero state before chunk 0
     float run = p[0];
     // eight slot loads in flight per step (the scan itself is serial)
     int c = 0;
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
 template <typename T, int D, int DV>
 hipError_t launch_all(const GenArgs &a, int BH, hipStream_t st) {
     const dim3 blk(kThreads);
-    hipLaunchKernelGGL((k_init_slot<D, DV>), dim3(BH), blk, 0, st, a);
+    if (a.init.S != nullptr || a.nc == 0) hipLaunchKernelGGL((k_init_slot<D, DV>), dim3(BH), blk, 0, st, a);
     if (a.nc > 0) {
         hipLaunchKernelGGL((k_chunk_sums<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
         const ScanSeg sS{a.ws.S, D * D}, sC{a.ws.C, D * DV}, sm{a.ws.m, D};
