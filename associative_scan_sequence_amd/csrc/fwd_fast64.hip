@@ -1135,15 +1135,20 @@ __global__ __launch_bounds__(256) void k_fast64_init(hla_state in, float *iagg, 
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// The data region (the flags live in a region of their own, which holds
+// nothing but launch epochs: flag_bytes)
 struct FastLayout {
-    size_t flags, aggS, aggX, aggC, aggV, iagg, iaggV, total;
+    size_t aggS, aggX, aggC, aggV, iagg, iaggV, total;
 };
+
+size_t flag_bytes(int BH, int P) {
+    return align256(static_cast<size_t>(BH) * P * 2 * kWaves * kFlagStride * sizeof(uint32_t));
+}
 
 FastLayout fast_layout(int BH, int P) {
     FastLayout L{};
     const size_t slots = static_cast<size_t>(BH) * P;
-    L.flags = 0;
-    L.aggS = L.flags + align256(slots * 2 * kWaves * kFlagStride * sizeof(uint32_t));
+    L.aggS = 0;
     L.aggX = L.aggS + slots * 4096 * sizeof(float);
     L.aggC = L.aggX + slots * 4096 * sizeof(float);
     L.aggV = L.aggC + slots * 4096 * sizeof(float);
@@ -1194,14 +1199,21 @@ bool fast64_supported(const FwdProblem &p) {
     return true;
 }
 
-size_t fast64_workspace_bytes(int BH, int n) {
+size_t fast64_flag_bytes(int BH, int n) {
+    const int nc = (n + W - 1) / W;
+    int P, L;
+    fast64_geometry(BH, nc, &P, &L);
+    return flag_bytes(BH, P);
+}
+
+size_t fast64_data_bytes(int BH, int n) {
     const int nc = (n + W - 1) / W;
     int P, L;
     fast64_geometry(BH, nc, &P, &L);
     return fast_layout(BH, P).total;
 }
 
-hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, uint32_t *flags, void *data, hipStream_t st) {
     FastArgs a{};
     a.H = p.H; a.n = p.n; a.nc = p.nc; a.BH = p.B * p.H;
     fast64_geometry(a.BH, a.nc, &a.P, &a.L);
@@ -1216,7 +1228,7 @@ hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipSt
     a.ctrl = ctrl;
     const FastLayout L = fast_layout(a.BH, a.P);
     char *base = static_cast<char *>(data);
-    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    a.flags = flags;
     a.aggS = reinterpret_cast<float *>(base + L.aggS);
     a.aggX = reinterpret_cast<float *>(base + L.aggX);
     a.aggC = reinterpret_cast<float *>(base + L.aggC);

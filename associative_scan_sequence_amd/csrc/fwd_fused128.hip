@@ -892,16 +892,19 @@ void geometry(int BH, int nc, int *P, int *L) {
     *P = (nc + *L - 1) / *L;
 }
 
+// The data region (the flags live in a region of their own, which holds
+// nothing but launch epochs: flag_bytes)
 struct Layout128 {
-    size_t flags, aggS, aggZ, aggC, aggV, iagg, iaggV, total;
+    size_t aggS, aggZ, aggC, aggV, iagg, iaggV, total;
 };
+
+size_t flag_bytes(int BH, int P) { return align256(2 * static_cast<size_t>(BH) * P * sizeof(uint32_t)); }
 
 Layout128 layout(int BH, int P) {
     Layout128 L{};
     const size_t slots = static_cast<size_t>(BH) * P;
     const size_t pub = P > 1 ? slots * kSlot * sizeof(float) : 0;  // one published 128 x 128 slot per segment
-    L.flags = 0;
-    L.aggS = align256(2 * slots * sizeof(uint32_t));
+    L.aggS = 0;
     L.aggZ = L.aggS + pub;
     L.aggC = L.aggZ + pub;
     L.aggV = L.aggC + pub;
@@ -931,14 +934,21 @@ bool fused128_supported(const FwdProblem &p) {
     return true;
 }
 
-size_t fused128_workspace_bytes(int BH, int n) {
+size_t fused128_flag_bytes(int BH, int n) {
+    const int nc = (n + W - 1) / W;
+    int P, L;
+    geometry(BH, nc, &P, &L);
+    return flag_bytes(BH, P);
+}
+
+size_t fused128_data_bytes(int BH, int n) {
     const int nc = (n + W - 1) / W;
     int P, L;
     geometry(BH, nc, &P, &L);
     return layout(BH, P).total;
 }
 
-hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
+hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, uint32_t *flags, void *data, hipStream_t st) {
     Args128 a{};
     a.H = p.H; a.n = p.n; a.BH = p.B * p.H;
     a.nc = (p.n + W - 1) / W;
@@ -951,7 +961,7 @@ hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hip
     a.ctrl = ctrl;
     const Layout128 L = layout(a.BH, a.P);
     char *base = static_cast<char *>(data);
-    a.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    a.flags = flags;
     a.aggS = reinterpret_cast<float *>(base + L.aggS);
     a.aggZ = reinterpret_cast<float *>(base + L.aggZ);
     a.aggC = reinterpret_cast<float *>(base + L.aggC);

@@ -366,13 +366,27 @@ struct HiLayout {
     size_t S, P, m, E, n, U, Y, yd, total;
 };
 
-// (the first kCtrlBytes are the control block of the one-launch path below,
-// which this path never touches)
+// Bytes of the flag region that follows the control block: the one-launch
+// path's flags (none where that path cannot run), which no data overlaps.
+// AHLA: the chained map's two flag sets side by side (one launch, so one
+// epoch: they must not overlap); third order: the first-order map's flags
+// and the second-order kernel's, which launch one after the other and share
+// the region.
+size_t flag_area(int BH, int n, int d, int dv, int w, bool third) {
+    if (!(d == 64 && dv == 64 && w == 64 && n > 0)) return 0;
+    const size_t fb = la64_flag_bytes(BH, n);
+    if (!third) return align256(2 * fb);
+    const size_t f2 = fast64_flag_bytes(BH, n);
+    return align256(fb > f2 ? fb : f2);
+}
+
+// (the control block and the flag region of the one-launch path below come
+// first; this path touches neither)
 HiLayout layout(int BH, int n, int d, int dv, int w, bool third) {
     const size_t nc = (static_cast<size_t>(n) + w - 1) / w;
     const size_t slots = static_cast<size_t>(BH) * (nc + 1), chunks = static_cast<size_t>(BH) * nc;
     HiLayout L{};
-    size_t off = kCtrlBytes;
+    size_t off = kCtrlBytes + flag_area(BH, n, d, dv, w, third);
     L.S = off; off = align256(off + (third ? slots * d * d * sizeof(float) : 0));
     L.P = off; off = align256(off + slots * d * dv * sizeof(float));
     L.m = off; off = align256(off + slots * d * sizeof(float));
@@ -392,25 +406,27 @@ HiLayout layout(int BH, int n, int d, int dv, int w, bool third) {
 // values Y = LA(Q, K, V) are kept as bf16 hi + lo, and both maps are linear in
 // their values: the second map (first order for AHLA, second order for third
 // order) takes the pair as its values, in one launch.
-// Workspace: control block, the one-launch kernels' data (shared: every
-// launch leaves the control block valid for the next), Y hi, Y lo.
+// Workspace: control block, flag region, the one-launch kernels' data
+// (shared: every launch leaves the control block valid for the next), Y hi,
+// Y lo.
 struct FastHiLayout {
-    size_t data, yh, yl, total;
+    size_t flags, data, yh, yl, total;
 };
 
-// AHLA: the chained map's two spaces ([flags 1][flags 2][sums 1][sums 2]);
-// third order: the first map's space (or the second-order kernel's data,
-// whichever is larger), then its output as a bf16 pair
+// AHLA: the chained map's two sets of sums; third order: the first map's
+// sums (or the second-order kernel's data, whichever is larger), then its
+// output as a bf16 pair
 FastHiLayout fast_layout(int BH, int n, bool third) {
     const size_t tok = static_cast<size_t>(BH) * n;
     FastHiLayout L{};
-    L.data = kCtrlBytes;
+    L.flags = kCtrlBytes;
+    L.data = L.flags + flag_area(BH, n, 64, 64, 64, third);
     if (!third) {
         L.yh = L.yl = 0;
-        L.total = L.data + 2 * (la64_flag_bytes(BH, n) + la64_agg_bytes(BH, n));
+        L.total = L.data + 2 * la64_agg_bytes(BH, n);
         return L;
     }
-    const size_t la = la64_workspace_bytes(BH, n), f64 = fast64_workspace_bytes(BH, n);
+    const size_t la = la64_agg_bytes(BH, n), f64 = fast64_data_bytes(BH, n);
     L.yh = align256(L.data + (la > f64 ? la : f64));
     L.yl = align256(L.yh + tok * 64 * sizeof(uint16_t));
     L.total = L.yl + tok * 64 * sizeof(uint16_t);
@@ -432,27 +448,26 @@ hipError_t fast_higher(const HiProblem &p, hipStream_t st) {
     const FastHiLayout L = fast_layout(BH, p.n, p.third);
     char *base = static_cast<char *>(p.ws);
     uint32_t *ctrl = reinterpret_cast<uint32_t *>(base);
-    void *data = base + L.data;
+    char *flags = base + L.flags, *data = base + L.data;
     LaProblem la{};
     la.B = p.B; la.H = p.H; la.n = p.n; la.q = p.q; la.k = p.k; la.gam = p.gam;
     if (!p.third) {  // out = LA (Q, K, LA (Q, K, V)) in one launch
         const size_t fb = la64_flag_bytes(BH, p.n), ab = la64_agg_bytes(BH, p.n);
-        char *d = static_cast<char *>(data);
-        const LaSpace s1{reinterpret_cast<uint32_t *>(d), reinterpret_cast<float *>(d + 2 * fb)};
-        const LaSpace s2{reinterpret_cast<uint32_t *>(d + fb), reinterpret_cast<float *>(d + 2 * fb + ab)};
+        const LaSpace s1{reinterpret_cast<uint32_t *>(flags), reinterpret_cast<float *>(data)};
+        const LaSpace s2{reinterpret_cast<uint32_t *>(flags + fb), reinterpret_cast<float *>(data + ab)};
         la.v = p.v; la.out = p.out; la.mode = 0;
         return la64_chain(la, ctrl, s1, s2, st);
     }
     uint16_t *yh = reinterpret_cast<uint16_t *>(base + L.yh), *yl = reinterpret_cast<uint16_t *>(base + L.yl);
     // Y = LA(Q, K, V) as bf16 hi + lo
     la.v = p.v; la.oh = yh; la.ol = yl; la.mode = 2;
-    hipError_t e = la64_forward(la, ctrl, data, st);
+    hipError_t e = la64_forward_in(la, ctrl, LaSpace{reinterpret_cast<uint32_t *>(flags), reinterpret_cast<float *>(data)}, st);
     if (e != hipSuccess) return e;
     FwdProblem f{};  // the second-order map on the pair (hi, lo) at once
     f.B = p.B; f.H = p.H; f.n = p.n; f.d = 64; f.dv = 64; f.w = 64; f.nc = (p.n + 63) / 64;
     f.dtype = HLA_BF16; f.q = p.q; f.k = p.k; f.gam = p.gam;
     f.v = yh; f.vl = yl; f.out = p.out;
-    return fast64_forward(f, ctrl, data, st);
+    return fast64_forward(f, ctrl, reinterpret_cast<uint32_t *>(flags), data, st);
 }
 
 }  // namespace

@@ -805,8 +805,6 @@ size_t la64_agg_bytes(int BH, int n) {
     return l.total - l.aggC;
 }
 
-size_t la64_workspace_bytes(int BH, int n) { return la64_flag_bytes(BH, n) + la64_agg_bytes(BH, n); }
-
 hipError_t la64_forward_in(const LaProblem &p, uint32_t *ctrl, LaSpace sp, hipStream_t st) {
     const LaArgs a = la_args(p, ctrl, sp);
     int cus = 0;
@@ -817,13 +815,6 @@ hipError_t la64_forward_in(const LaProblem &p, uint32_t *ctrl, LaSpace sp, hipSt
     const int key = la_key_of(a, p);
     if (la_decay(p)) return loop ? launch_la<true, true>(a, grid, st, key) : launch_la<true, false>(a, grid, st, key);
     return loop ? launch_la<false, true>(a, grid, st, key) : launch_la<false, false>(a, grid, st, key);
-}
-
-hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t st) {
-    const int BH = p.B * p.H;
-    char *base = static_cast<char *>(data);
-    const LaSpace sp{reinterpret_cast<uint32_t *>(base), reinterpret_cast<float *>(base + la64_flag_bytes(BH, p.n))};
-    return la64_forward_in(p, ctrl, sp, st);
 }
 
 hipError_t la64_chain(const LaProblem &p, uint32_t *ctrl, LaSpace s1, LaSpace s2, hipStream_t st) {

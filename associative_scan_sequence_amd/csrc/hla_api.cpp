@@ -168,31 +168,43 @@ FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *i
     return FwdPath::Generic;
 }
 
-// Workspace bytes for the call: the control block, then the path's data.
-// With state/den unknown (the size query), the largest of the candidate
-// paths is returned.
-size_t workspace_need(const hla_params *p, const Geometry &geo, const hla_state *init,
-                      const hla_state *fin, const float *den) {
+// A caller's workspace is the control block, a flag region, then the data
+// of whichever path a call takes.  The flag region holds the flags of the
+// one-launch kernel that calls with these params may take (none where no such
+// kernel applies) and nothing else; its size depends on the params alone, so
+// calls with the same params, whatever their states and den, find every flag
+// outside every path's data.
+size_t flag_area(const hla_params *p, const Geometry &geo) {
+    const int BH = p->B * p->H;
+    if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0)
+        return hla::fast64_flag_bytes(BH, p->n);
+    if (p->dtype == HLA_BF16 && p->d == 128 && p->dv == 128 && p->n > 0) return hla::fused128_flag_bytes(BH, p->n);
+    return 0;
+}
+
+// Workspace bytes for any call with these params: the largest of the
+// candidate paths' data (states and den are not known to the size query).
+size_t workspace_need(const hla_params *p, const Geometry &geo) {
     const int BH = p->B * p->H;
     const size_t gen = hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w);
     size_t fused = 0;
-    if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0) {
-        fused = hla::fast64_workspace_bytes(BH, p->n);
-    }
-    if (p->dtype == HLA_BF16 && p->d == 128 && p->dv == 128 && p->n > 0)
-        fused = hla::fused128_workspace_bytes(BH, p->n);
-    (void)init; (void)fin; (void)den;
-    return hla::kCtrlBytes + (gen > fused ? gen : fused);
+    if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0)
+        fused = hla::fast64_data_bytes(BH, p->n);
+    if (p->dtype == HLA_BF16 && p->d == 128 && p->dv == 128 && p->n > 0) fused = hla::fused128_data_bytes(BH, p->n);
+    return hla::kCtrlBytes + flag_area(p, geo) + (gen > fused ? gen : fused);
 }
 
-// Workspace bytes of the one path a call takes (the control block included).
-size_t path_need(const hla_params *p, const Geometry &geo, FwdPath path) {
+// Flag and data bytes of the one path a call takes.
+struct PathNeed {
+    size_t flags, data;
+};
+
+PathNeed path_need(const hla_params *p, const Geometry &geo, FwdPath path) {
     const int BH = p->B * p->H;
-    size_t data = 0;
-    if (path == FwdPath::Fast64) data = hla::fast64_workspace_bytes(BH, p->n);
-    else if (path == FwdPath::Fused128) data = hla::fused128_workspace_bytes(BH, p->n);
-    else data = hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w);
-    return hla::kCtrlBytes + data;
+    if (path == FwdPath::Fast64) return PathNeed{hla::fast64_flag_bytes(BH, p->n), hla::fast64_data_bytes(BH, p->n)};
+    if (path == FwdPath::Fused128)
+        return PathNeed{hla::fused128_flag_bytes(BH, p->n), hla::fused128_data_bytes(BH, p->n)};
+    return PathNeed{0, hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w)};
 }
 
 }  // namespace
@@ -217,7 +229,7 @@ size_t hla_forward_workspace_size(const hla_params *p) {
     Geometry geo{};
     if (forward_geometry(p, &geo) != HLA_OK) return 0;
     if (!width_ok(p->d) || !width_ok(p->dv) || !dtype_ok(p)) return 0;
-    return workspace_need(p, geo, nullptr, nullptr, nullptr);
+    return workspace_need(p, geo);
 }
 
 hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k, const void *v,
@@ -269,11 +281,15 @@ hla_status forward_impl(const hla_params *p, const void *q, const void *k, const
     }
     if (init && (s = check_state(init, "init")) != HLA_OK) return s;
     if (final_state && (s = check_state(final_state, "final_state")) != HLA_OK) return s;
-    const size_t need = scratch_name ? path_need(p, geo, choose_path(p, geo, init, final_state, den, fp.gam))
-                                     : workspace_need(p, geo, init, final_state, den);
-    if (scratch_name && need > workspace_bytes)
-        return fail(HLA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; %s holds %zu", need, scratch_name,
-                    workspace_bytes);
+    // the static scratch keeps a flag region of fixed size, so that calls with
+    // any params find every flag outside every other call's data
+    const PathNeed pn = path_need(p, geo, choose_path(p, geo, init, final_state, den, fp.gam));
+    const size_t area = scratch_name ? hla::kNoallocFlagBytes : flag_area(p, geo);
+    const size_t need = scratch_name ? hla::kCtrlBytes + area + pn.data : workspace_need(p, geo);
+    if (scratch_name && (pn.flags > area || need > workspace_bytes))
+        return fail(HLA_ERR_WORKSPACE,
+                    "this call needs %zu bytes of flags and %zu of data; %s holds %zu bytes: %zu for flags, %zu for data",
+                    pn.flags, pn.data, scratch_name, workspace_bytes, area, workspace_bytes - hla::kCtrlBytes - area);
     if (!scratch_name && need > 0) {
         if (!workspace) return fail(HLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (workspace_bytes < need)
@@ -311,15 +327,17 @@ hla_status forward_impl(const hla_params *p, const void *q, const void *k, const
         fp.ws = workspace;
     }
     char *ws = static_cast<char *>(workspace);
+    uint32_t *ctrl = reinterpret_cast<uint32_t *>(ws), *flags = reinterpret_cast<uint32_t *>(ws + hla::kCtrlBytes);
+    char *data = ws + hla::kCtrlBytes + area;
     hipError_t e;
     const FwdPath path = choose_path(p, geo, init, final_state, den, fp.gam);
     if (path == FwdPath::Fast64) {
-        e = hla::fast64_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
+        e = hla::fast64_forward(fp, ctrl, flags, data, stream);
     } else if (path == FwdPath::Fused128) {
-        e = hla::fused128_forward(fp, reinterpret_cast<uint32_t *>(ws), ws + hla::kCtrlBytes, stream);
+        e = hla::fused128_forward(fp, ctrl, flags, data, stream);
     } else {
-        fp.ws = ws + hla::kCtrlBytes;
-        fp.ws_bytes = workspace_bytes - hla::kCtrlBytes;
+        fp.ws = data;
+        fp.ws_bytes = workspace_bytes - hla::kCtrlBytes - area;
         e = hla::generic_forward(fp, stream);
     }
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "forward launch: %s", hipGetErrorString(e));

@@ -98,22 +98,37 @@ hla_status forward_impl(const hla_params *p, const void *q, const void *k, const
 // hla_forward_chunked_noalloc (noalloc.hip; looked up once per device).
 hla_status noalloc_scratch(void **ptr);
 constexpr size_t kNoallocBytes = HLA_NOALLOC_SCRATCH_BYTES;
+// The scratch's flag region, fixed so that calls with any params find every
+// flag outside every other call's data: the largest one-launch call whose data
+// fits the rest of the scratch needs about 2.6 MB of flags.
+constexpr size_t kNoallocFlagBytes = static_cast<size_t>(4) << 20;
 
 // Records msg as this thread's last error (hla_last_error) and returns s.
 hla_status set_error(hla_status s, const char *msg);
 
+// The one-launch forwards take three regions: the control block, their
+// flags and their data.  A flag holds the epoch of the launch that last set
+// it, and a wait compares it with the running launch's epoch; so a flag
+// region must hold nothing but epochs (or the zeros it started as): every
+// workspace keeps the flags in a region of their own, after the control
+// block, that no path's data overlaps.  Flags of different one-launch kernels
+// may share that region, as every epoch comes from the one sequence in the
+// control block.
+
 // One-launch MFMA forward for bf16, d = dv = w = 64, decays >= 0.75, any
-// ridge, denominator and normalisation (no init or final state).
+// ridge, denominator, normalisation, initial and final state.
 bool fast64_supported(const FwdProblem &p);
-size_t fast64_workspace_bytes(int BH, int n);
-hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
+size_t fast64_flag_bytes(int BH, int n);
+size_t fast64_data_bytes(int BH, int n);
+hipError_t fast64_forward(const FwdProblem &p, uint32_t *ctrl, uint32_t *flags, void *data, hipStream_t s);
 
 // One-launch MFMA forward for bf16, d = dv = 128 (any chunk setting; the
-// kernel works in 64-token chunks), decays >= 0.75, no ridge, denominator,
-// normalisation, init or final state.
+// kernel works in 64-token chunks), decays >= 0.75, no ridge, denominator or
+// normalisation; an initial or final state while the segments fit one pass.
 bool fused128_supported(const FwdProblem &p);
-size_t fused128_workspace_bytes(int BH, int n);
-hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
+size_t fused128_flag_bytes(int BH, int n);
+size_t fused128_data_bytes(int BH, int n);
+hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, uint32_t *flags, void *data, hipStream_t s);
 
 struct DecodeProblem {
     int B, H, d, dv;
@@ -214,8 +229,6 @@ struct LaSpace {
 };
 size_t la64_flag_bytes(int BH, int n);
 size_t la64_agg_bytes(int BH, int n);
-size_t la64_workspace_bytes(int BH, int n);  // la64_forward's data: the flags, then the aggregates
-hipError_t la64_forward(const LaProblem &p, uint32_t *ctrl, void *data, hipStream_t s);
 hipError_t la64_forward_in(const LaProblem &p, uint32_t *ctrl, LaSpace sp, hipStream_t s);
 // The map applied twice in one launch, out = LA (Q, K, LA (Q, K, V)): the
 // first map's output stays in LDS as the second's values (a bf16 pair); each

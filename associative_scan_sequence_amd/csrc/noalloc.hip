@@ -18,9 +18,13 @@
 // loaded, and every launch leaves the block valid for the next, so nothing is
 // cleared here (clearing it again would restart the launch epochs, and a
 // wait could then take a flag left by an earlier call for a fresh one).  The
-// rest holds per-call partial sums that every call writes before it reads
-// them.  Calls on one GPU share the array: calls that overlap in time on that
-// GPU (two streams, two threads) race and must not be made.
+// next kNoallocFlagBytes hold the one-launch kernels' flags and nothing
+// else, whatever the params of each call, so a flag only ever holds the epoch
+// of an earlier launch (never a partial sum that happens to equal the running
+// launch's epoch).  The rest holds per-call partial sums that every call
+// writes before it reads them.  Calls on one GPU share the array: calls that
+// overlap in time on that GPU (two streams, two threads) race and must not be
+// made.
 #include <hip/hip_runtime.h>
 
 #include <mutex>

@@ -102,9 +102,15 @@ typedef struct {
  * polls (0 = the built-in 4M; -1 = give up at once in the d = 128 kernel and
  * after one poll in the d = 64 kernel; the only word a caller may set, e.g.
  * to test the give-up path), 64 = finished-workgroup counter, 65 = launch
- * epoch, 66 = segment ticket): zero-fill the workspace once before its first
- * use and write nothing else in it afterwards.  The rest holds per-chunk or
- * per-segment partial summaries.
+ * epoch, 66 = segment ticket).  Then come the flags of the one-launch
+ * kernels, each tagged with the epoch of the launch that set it, in a region
+ * of their own whose place and size depend on p alone, and then the data of
+ * whichever path a call takes (per-chunk or per-segment partial summaries),
+ * which never reaches the flags.  Zero-fill the workspace once before its
+ * first use and write nothing else in it afterwards; it then serves any
+ * number of calls with the same params (with or without states and den, in
+ * any order).  Zero-fill it again before calls with other params: their data
+ * may cover where this call's flags were.
  *
  * The one-launch kernels (bf16, d = dv = 64 or 128, no init or final state)
  * hand partial sums between workgroups of one launch when a head is cut into
@@ -151,13 +157,17 @@ hla_status hla_forward_chunked(const hla_params *p, const void *q, const void *k
  * workspace is a static device array of HLA_NOALLOC_SCRATCH_BYTES owned by
  * the library, one per GPU it runs on, held until the process ends.  The
  * call allocates nothing; its first call on a device looks up that device's
- * copy of the array.  A call whose kernel path needs more scratch than that
- * (the one-launch paths need about 13 MB at B4 H8 n2048 d64 and 50 MB at
- * B8 H8 n4096 d64; the generic path with an initial or final state needs
- * about 2.2 KB per head-token at d = dv = 64) fails with HLA_ERR_WORKSPACE
- * before anything is enqueued.  Every call on a GPU shares that GPU's array,
- * which keeps the previous call's contents (a control block that each call
- * leaves valid for the next; nothing needs clearing): calls that overlap in
+ * copy of the array.  The array keeps 4 MiB for the one-launch kernels'
+ * flags at a fixed place, so calls with any params, in any order, find their
+ * flags outside every other call's data.  A call whose kernel path needs
+ * more than that (the one-launch paths need 0.5 MB of flags and 14 MB of
+ * data at B4 H8 n2048 d64, 2.1 MB and 54 MB at B8 H8 n4096 d64; the generic
+ * path with an initial or final state needs about 2.2 KB of data per
+ * head-token at d = dv = 64) fails with HLA_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on a GPU shares that GPU's array, which keeps the
+ * previous call's contents (a control block that each call leaves valid for
+ * the next, and flags that only ever hold launch epochs; nothing needs
+ * clearing): calls that overlap in
  * time on one GPU (two streams or two host threads) race and must not be
  * made; calls ordered on one stream are fine, captured into a HIP graph
  * too. */
@@ -319,10 +329,12 @@ typedef struct {
 } hla_third_state;
 
 /* Workspace bytes of the AHLA / third-order forward; 0 for an invalid p.
- * As for hla_forward_chunked, zero-fill the workspace once before its first
- * use and write nothing in it afterwards: its first 8 KB are a control block
- * and the flags that follow it are tagged with the launch epoch kept there,
- * both kept valid from call to call (a call never clears them).  bf16 calls with d = dv = 64, chunk 64, every decay >= 0.75,
+ * As for hla_forward_chunked: its first 8 KB are a control block, the flags
+ * that follow are tagged with the launch epoch kept there (both kept valid
+ * from call to call: a call never clears them), and no path's data reaches
+ * the flags; zero-fill the workspace once before its first use, write
+ * nothing in it afterwards, and zero-fill it again before calls with other
+ * params or of the other order.  bf16 calls with d = dv = 64, chunk 64, every decay >= 0.75,
  * no denominator, ratio or state run one-launch kernels (AHLA as first-order
  * attention applied twice, third order as second-order HLA over first-order
  * attention values); every other call runs the chunked fp32 kernels. */

@@ -36,11 +36,13 @@ hipError_t la_backward(const BwdProblem &, hipStream_t) { reached("la_backward")
 size_t backward_workspace_bytes(int BH, int n, int d, int dv, int w) { return generic_backward_workspace_bytes(BH, n, d, dv, w); }
 hla_status noalloc_scratch(void **) { reached("noalloc_scratch"); }
 bool fast64_supported(const FwdProblem &) { return false; }
-size_t fast64_workspace_bytes(int BH, int n) { return fixed_size(BH, n, 64, 64); }
-hipError_t fast64_forward(const FwdProblem &, uint32_t *, void *, hipStream_t) { reached("fast64_forward"); }
+size_t fast64_flag_bytes(int BH, int n) { return fixed_size(BH, n, 1, 1); }
+size_t fast64_data_bytes(int BH, int n) { return fixed_size(BH, n, 64, 64); }
+hipError_t fast64_forward(const FwdProblem &, uint32_t *, uint32_t *, void *, hipStream_t) { reached("fast64_forward"); }
 bool fused128_supported(const FwdProblem &) { return false; }
-size_t fused128_workspace_bytes(int BH, int n) { return fixed_size(BH, n, 128, 128); }
-hipError_t fused128_forward(const FwdProblem &, uint32_t *, void *, hipStream_t) { reached("fused128_forward"); }
+size_t fused128_flag_bytes(int BH, int n) { return fixed_size(BH, n, 1, 1); }
+size_t fused128_data_bytes(int BH, int n) { return fixed_size(BH, n, 128, 128); }
+hipError_t fused128_forward(const FwdProblem &, uint32_t *, uint32_t *, void *, hipStream_t) { reached("fused128_forward"); }
 hipError_t decode_step(const DecodeProblem &, hipStream_t) { reached("decode_step"); }
 hipError_t decode_step_mq(const DecodeMqProblem &, hipStream_t) { reached("decode_step_mq"); }
 hipError_t key_moment_pack(int, int, const float *, float *, bool, hipStream_t) { reached("key_moment_pack"); }
