@@ -3,8 +3,9 @@ on the same inputs: the same kernels run on the library's static scratch
 instead of a caller's workspace, so the outputs must be the same bits.  Two
 calls in a row, the second with a smaller input, on every kernel path (the
 one-launch d = 64 and d = 128 forwards, the d = 64 kernel with initial and
-final states, and the generic path with a final state), then a call too large for the scratch, which must fail before
-anything is enqueued."""
+final states, and the generic path with a final state), calls with other
+params one after the other, then a call too large for the scratch, which must
+fail before anything is enqueued."""
 import sys
 
 import pytest
@@ -73,6 +74,19 @@ def test_noalloc_d128_then_generic_with_state():
     both(q, k, v, gamma=inputs.gamma_list_fp32([0.999] * 16))
     q2, k2, v2 = (x.to(DEV) for x in inputs.qkv(1, 2, 300, 32, 32, torch.float32, seed=94))
     both(q2, k2, v2, gamma=[0.97, 1.0], return_state=True, return_den=True)
+
+
+def test_noalloc_generic_state_call_then_one_launch():
+    """Calls with other params share the one scratch: a generic-path call (fp32
+    inputs, an initial and a final state) keeps its data past the scratch's
+    fixed flag region, so the one-launch call that follows (bf16 d = 64) finds
+    only launch epochs in its flags.  Both match the caller-workspace path bit
+    for bit."""
+    q, k, v = (x.to(DEV) for x in inputs.qkv(2, 4, 1000, 64, 64, torch.float32, seed=99))
+    init = hla.State(*(t.to(DEV).contiguous() for t in inputs.random_state_fp32(8, 64, 64, seed=100, scale=0.1)))
+    both(q, k, v, chunk=64, gamma=[0.97, 0.9, 1.0, 0.99], init=init, return_state=True)
+    q2, k2, v2 = (x.to(DEV) for x in inputs.qkv(4, 8, 2048, 64, 64, torch.bfloat16, seed=101))
+    both(q2, k2, v2, chunk=64)
 
 
 def test_noalloc_in_a_graph():
