@@ -138,9 +138,11 @@ size_t hla_forward_workspace_size(const hla_params *p);
  *   final_state  NULL, or receives the state after token n-1, with
  *         rho = (init rho or 1) * g^n.  The scan carries X = S C - G and
  *         y = S m - h and returns G = S C - X, h = S m - y, so G and h are
- *         accurate to fp32 rounding relative to the size of S C and S m,
- *         not to their own (after one token G is exactly zero, and the
- *         value returned is a rounding residue of S C).
+ *         accurate relative to the size of S C and S m (fp32 rounding on
+ *         the chunked fp32 path, about 1e-5 of it on the one-launch bf16
+ *         kernels, whose products split fp32 operands into bf16 pairs), not
+ *         to their own: after one token G is exactly zero, and the value
+ *         returned is a rounding residue of S C.
  *   workspace    device memory of at least hla_forward_workspace_size(p)
  *         bytes (may be NULL when that size is 0).
  * out and den must not overlap q, k, v, init or the workspace; init and
