@@ -114,8 +114,8 @@ typedef struct {
  *
  * The one-launch kernels (bf16 with every decay >= 0.75: d = dv = 64, chunk
  * 64, every option and state; d = dv = 128 without ridge, den or ratio, with
- * an initial or final state while B*H times the segments per head is at
- * most 256) hand partial sums between workgroups of one launch when a head is cut into
+ * an initial or final state when each head is one segment or B*H times
+ * the segments per head is at most 256) hand partial sums between workgroups of one launch when a head is cut into
  * several segments: a segment waits for the sums of the earlier segments of
  * its head.  Both kernels then hand segments out by ticket, in increasing
  * order, so a segment only ever waits on segments that running workgroups
