@@ -133,3 +133,22 @@ def test_fast_backward_deterministic_causal_and_reusable():
     for x in c:
         assert torch.count_nonzero(x[:, :, t + 1:]) == 0
         assert torch.count_nonzero(x[:, :, :t + 1]) > 0
+
+
+def test_fast_backward_soak_bitwise():
+    """100 calls of the bench shape (B4 H8 n2048, decay per head) on one
+    workspace, each compared bitwise with the first; the loop stops at the
+    first mismatch.  Every call hands segment sums between workgroups in each
+    of its maps, so a lost or early hand-off would show as a difference."""
+    B, H, n = 4, 8, 2048
+    q, k, v = (x.to(DEV) for x in inputs.qkv(B, H, n, 64, 64, BF, seed=1990))
+    dout = inputs.upstream(B, H, n, 64, seed=1991).to(DEV)
+    g = gammas("per_head", H)
+    ws = torch.empty(hla.backward_workspace_size(B, H, n, 64, 64, chunk=64, gamma=g), dtype=torch.uint8, device=DEV)
+    ref = [x.clone() for x in hla.backward_chunked(q, k, v, dout, gamma=g, chunk=64, workspace=ws)]
+    for i in range(100):
+        got = hla.backward_chunked(q, k, v, dout, gamma=g, chunk=64, workspace=ws)
+        for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(x, r), f"call {i}: {name} differs"
+    words = ws[:16].view(torch.int32).cpu().tolist()
+    assert words[3] == 0, words

@@ -202,3 +202,28 @@ def test_fast_backward_segments_chain_to_the_whole_sequence():
     torch.cuda.synchronize()
     got = [torch.cat([a.cpu(), b.cpu()], dim=2) for a, b in zip(gA, gB)]
     check(got, ob.backward(q, k, v, dout, g))
+
+
+def test_fast_backward_with_states_soak_bitwise():
+    """50 calls of the shard backward at the bench shape (initial state,
+    dfinal in, dinit out) on one workspace, each compared bitwise with the
+    first; the loop stops at the first mismatch."""
+    B, H, n = 4, 8, 2048
+    N = B * H
+    q, k, v = (x.to(DEV) for x in inputs.qkv(B, H, n, 64, 64, BF, seed=2600))
+    dout = inputs.upstream(B, H, n, 64, seed=2601).to(DEV)
+    g = gammas("per_head", H)
+    init, dfin = dev_state(make_state(N, 2602, True)), dev_state(make_state(N, 2610, False))
+    ws = torch.empty(hla.backward_workspace_size(B, H, n, 64, 64, chunk=64, gamma=g), dtype=torch.uint8, device=DEV)
+
+    def call():
+        dini = hla.State.empty(N, 64, 64, DEV)
+        got = hla.backward_chunked(q, k, v, dout, gamma=g, chunk=64, workspace=ws, init=init, dfinal=dfin, dinit=dini)
+        return list(got) + [t for t in dini.tensors() if t is not None]
+
+    ref = [x.clone() for x in call()]
+    for i in range(50):
+        for j, (x, r) in enumerate(zip(call(), ref)):
+            assert torch.equal(x, r), f"call {i}: output {j} differs"
+    words = ws[:16].view(torch.int32).cpu().tolist()
+    assert words[3] == 0, words
