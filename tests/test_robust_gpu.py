@@ -7,8 +7,9 @@ depend on what else runs on the device, and failures that are never silent.
 * Two forward calls on two streams whose grids cannot be resident together
   (each one-launch grid holds a workgroup per CU) give the same bits as the
   same calls made one after the other.
-* A bounded soak of repeated bench-shape calls, compared bitwise, stops at its
-  first mismatch.
+* Bounded soaks of repeated calls (the bench shape, the d = 128 kernel, the
+  d = 64 kernel with states, AHLA's chained map), compared bitwise, stop at
+  their first mismatch.
 * A wait that gives up (forced from the host through control word 4) turns
   the outputs that depend on it into NaN, never into wrong numbers.
 * Compose at its full size (4096 pairs, d = dv = 128) against the oracle, and
@@ -196,6 +197,39 @@ def test_soak_bench_shape_bitwise():
         hla.forward_chunked(q, k, v, chunk=64, workspace=ws, out=out)
         assert torch.equal(out, ref), f"call {i} differs"
     assert ctrl_words(ws)[3] == 0
+
+
+def _soak(call, reps):
+    ref = [x.clone() for x in call()]
+    for i in range(reps):
+        for j, (x, r) in enumerate(zip(call(), ref)):
+            assert torch.equal(x, r), f"call {i}: output {j} differs"
+
+
+def test_soak_other_one_launch_kernels_bitwise():
+    """Bounded soaks, compared bitwise with the first call and stopping at the
+    first mismatch, of the other kernels that hand sums between workgroups:
+    the d = 128 forward (16 segments per head), the d = 64 forward with
+    initial and final states, and AHLA's chained map (two hand-offs per
+    segment)."""
+    g16 = inputs.gamma_list_fp32([0.999] * 16)
+    q, k, v = (x.to(DEV) for x in inputs.qkv(1, 16, 16384, 128, 128, torch.bfloat16, seed=75))
+    ws = torch.zeros(hla.workspace_size(1, 16, 16384, 128, 128, gamma=g16), dtype=torch.uint8, device=DEV)
+    _soak(lambda: [hla.forward_chunked(q, k, v, gamma=g16, workspace=ws)[0]], 30)
+    assert ctrl_words(ws)[3] == 0
+
+    g8 = inputs.gamma_list_fp32([0.97, 0.9, 1.0, 0.99, 0.75, 0.8, 0.95, 0.999])
+    q, k, v = (x.to(DEV) for x in inputs.qkv(4, 8, 2048, 64, 64, torch.bfloat16, seed=76))
+    init = hla.State(*(t.to(DEV).contiguous() for t in inputs.random_state_fp32(32, 64, 64, seed=77, scale=0.1)))
+    ws = torch.zeros(hla.workspace_size(4, 8, 2048, 64, 64, chunk=64, gamma=g8), dtype=torch.uint8, device=DEV)
+
+    def with_states():
+        out, _, fin = hla.forward_chunked(q, k, v, gamma=g8, chunk=64, init=init, return_state=True, workspace=ws)
+        return [out] + [t for t in fin.tensors() if t is not None]
+
+    _soak(with_states, 30)
+    assert ctrl_words(ws)[3] == 0
+    _soak(lambda: [hla.ahla_forward(q, k, v, gamma=g8, chunk=64)[0]], 30)
 
 
 @pytest.mark.parametrize("d,B,H,n", [(64, 4, 8, 2048), (128, 1, 16, 4096)])
