@@ -639,6 +639,7 @@ hipError_t generic_backward(const BwdProblem &p, hipStream_t st) {
     fw.init = f.init;  // the left carries start from it (held constant)
     fw.fin = hla_state{};
     fw.carries_only = f.normalize ? 0 : 1;  // out and den only enter the ratio's gradient
+    fw.own_prefix = 0;                      // the slots below are read as prefixes
     hipError_t e = generic_forward(fw, st);
     if (e != hipSuccess) return e;
     const GenericSlots sl = generic_slots(fw);

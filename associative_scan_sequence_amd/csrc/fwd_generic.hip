@@ -52,6 +52,7 @@ struct GenArgs {
     float ridge;
     int normalize;
     int carries_only;
+    int own_prefix;  // the prefix scans are not launched: consumers sum the slots (see prefix_of)
     const void *q, *k, *v;
     float *out, *den;
     hla_state init, fin;
@@ -61,6 +62,32 @@ struct GenArgs {
 
 __device__ __forceinline__ size_t slot_index(const GenArgs &a, int bh, int slot) {
     return static_cast<size_t>(bh) * (a.nc + 1) + slot;
+}
+
+// Few chunks, narrow heads: the two prefix scans cost a launch each, more
+// than the sums themselves.  Then the slots keep the chunks' own increments
+// and each consumer forms the prefix it needs, slot c = the state before
+// chunk c, with the scan kernel's recurrence in the same order (the same
+// bits): run = slot 0 (the initial state, or zero), then run = r run + slot
+// j+1 for j < c, with r = g^(power w), g^(power L_last) for the last chunk.
+constexpr int kOwnPrefixChunks = 16;
+
+template <int E>
+__device__ void prefix_of(const GenArgs &a, int bh, const float *slots, int c, int power, float *dst) {
+    const float g = head_gamma(a.gam, bh % a.H);
+    const int Llast = a.n - (a.nc - 1) * a.w;
+    const float rf = gpow(g, power * a.w), rl = gpow(g, power * Llast);
+    const float *p = slots + slot_index(a, bh, 0) * E;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        float x[kOwnPrefixChunks];  // every slot's load in flight at once
+#pragma unroll
+        for (int j = 0; j < kOwnPrefixChunks; ++j) x[j] = j < c ? p[static_cast<size_t>(j + 1) * E + e] : 0.0f;
+        float run = a.init.S != nullptr ? p[e] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kOwnPrefixChunks; ++j)
+            if (j < c) run = (j == a.nc - 1 ? rl : rf) * run + x[j];
+        dst[e] = run;
+    }
 }
 
 // Out = S*C - In and outv = S*m - inv for one head; S [D][D], C/In/Out [D][DV].
@@ -211,9 +238,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_uz(GenArgs a) {
     const T *q = static_cast<const T *>(a.q) + tok * D;
     const T *k = static_cast<const T *>(a.k) + tok * D;
     const T *v = static_cast<const T *>(a.v) + tok * DV;
+    constexpr bool OWN = D <= 32 && DV <= 32;  // the only widths that may skip the prefix scans
+    __shared__ float own_s[OWN ? D * D : 1];
     const float *S0 = a.ws.S + slot_index(a, bh, c) * D * D;
     const int tid = threadIdx.x;
     for (int i = tid; i <= 2 * a.w; i += kThreads) gt[i] = gpow(g, i);
+    if constexpr (OWN) {
+        if (a.own_prefix) {
+            prefix_of<D * D>(a, bh, a.ws.S, c, 1, own_s);
+            S0 = own_s;
+        }
+    }
     __syncthreads();
     auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
     auto ke = [&](int t, int l) { return Elem<T>::get(k, static_cast<size_t>(t) * D + l); };
@@ -257,8 +292,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(GenArgs a) {
     const size_t sl = slot_index(a, bh, c);
     const float *X0 = a.ws.X + sl * D * DV, *C0 = a.ws.C + sl * D * DV;
     const float *y0 = a.ws.y + sl * D, *m0 = a.ws.m + sl * D;
+    constexpr bool OWN = D <= 32 && DV <= 32;  // the only widths that may skip the prefix scans
+    __shared__ float own_x[OWN ? D * DV : 1], own_c[OWN ? D * DV : 1], own_y[OWN ? D : 1], own_m[OWN ? D : 1];
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     for (int i = tid; i <= 2 * a.w; i += kThreads) gt[i] = gpow(g, i);
+    if constexpr (OWN) {
+        if (a.own_prefix) {
+            prefix_of<D * DV>(a, bh, a.ws.X, c, 2, own_x);
+            prefix_of<D * DV>(a, bh, a.ws.C, c, 1, own_c);
+            prefix_of<D>(a, bh, a.ws.y, c, 2, own_y);
+            prefix_of<D>(a, bh, a.ws.m, c, 1, own_m);
+            X0 = own_x; C0 = own_c; y0 = own_y; m0 = own_m;
+        }
+    }
     __syncthreads();
     auto qe = [&](int t, int l) { return Elem<T>::get(q, static_cast<size_t>(t) * D + l); };
     auto ve = [&](int t, int l) { return Elem<T>::get(v, static_cast<size_t>(t) * DV + l); };
@@ -315,6 +361,20 @@ __global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
     const size_t sl = slot_index(a, bh, a.nc);
     const float *S = a.ws.S + sl * D * D, *C = a.ws.C + sl * D * DV, *m = a.ws.m + sl * D;
     const float *X = a.ws.X + sl * D * DV, *y = a.ws.y + sl * D;
+    constexpr bool OWN = D <= 32 && DV <= 32;  // the only widths that may skip the prefix scans
+    __shared__ float own_s[OWN ? D * D : 1], own_c[OWN ? D * DV : 1], own_x[OWN ? D * DV : 1];
+    __shared__ float own_m[OWN ? D : 1], own_y[OWN ? D : 1];
+    if constexpr (OWN) {
+        if (a.own_prefix) {
+            prefix_of<D * D>(a, bh, a.ws.S, a.nc, 1, own_s);
+            prefix_of<D * DV>(a, bh, a.ws.C, a.nc, 1, own_c);
+            prefix_of<D>(a, bh, a.ws.m, a.nc, 1, own_m);
+            prefix_of<D * DV>(a, bh, a.ws.X, a.nc, 2, own_x);
+            prefix_of<D>(a, bh, a.ws.y, a.nc, 2, own_y);
+            S = own_s; C = own_c; m = own_m; X = own_x; y = own_y;
+            __syncthreads();
+        }
+    }
     float *fS = a.fin.S + static_cast<size_t>(bh) * D * D;
     float *fC = a.fin.C + static_cast<size_t>(bh) * D * DV;
     float *fm = a.fin.m + static_cast<size_t>(bh) * D;
@@ -332,23 +392,26 @@ __global__ __launch_bounds__(kThreads) void k_final(GenArgs a) {
 }
 
 template <typename T, int D, int DV>
-hipError_t launch_all(const GenArgs &a, int BH, hipStream_t st) {
+hipError_t launch_all(GenArgs a, int BH, hipStream_t st) {
     const dim3 blk(kThreads);
+    // a forward call (not the backward's recompute, which reads the prefix
+    // slots afterwards) with few chunks and narrow heads skips the scans
+    a.own_prefix = a.own_prefix && !a.carries_only && a.nc <= kOwnPrefixChunks && D <= 32 && DV <= 32;
     if (a.init.S != nullptr || a.nc == 0) hipLaunchKernelGGL((k_init_slot<D, DV>), dim3(BH), blk, 0, st, a);
     if (a.nc > 0) {
         hipLaunchKernelGGL((k_chunk_sums<T, D, DV>), dim3(a.nc, BH), blk, 0, st, a);
         const ScanSeg sS{a.ws.S, D * D}, sC{a.ws.C, D * DV}, sm{a.ws.m, D};
         const int e1 = D * D + D * DV + D;
-        hipLaunchKernelGGL(k_prefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sS, sC,
-                           sm, 1);
+        if (!a.own_prefix)
+            hipLaunchKernelGGL(k_prefix, dim3((e1 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sS, sC, sm, 1);
         if (a.w > 64)
             hipLaunchKernelGGL((k_chunk_uz<T, D, DV, 8>), dim3(a.nc, BH), blk, 0, st, a);
         else
             hipLaunchKernelGGL((k_chunk_uz<T, D, DV, 4>), dim3(a.nc, BH), blk, 0, st, a);
         const ScanSeg sX{a.ws.X, D * DV}, sy{a.ws.y, D}, none{nullptr, 0};
         const int e2 = D * DV + D;
-        hipLaunchKernelGGL(k_prefix, dim3((e2 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sX, sy,
-                           none, 2);
+        if (!a.own_prefix)
+            hipLaunchKernelGGL(k_prefix, dim3((e2 + kThreads - 1) / kThreads, BH), blk, 0, st, a, sX, sy, none, 2);
         if (a.carries_only) return hipGetLastError();
         if (a.w > 64)
             hipLaunchKernelGGL((k_chunk_out<T, D, DV, 8>), dim3(a.nc, BH), blk, 0, st, a);
@@ -422,7 +485,7 @@ hipError_t generic_forward(const FwdProblem &p, hipStream_t st) {
     char *base = static_cast<char *>(p.ws);
     GenArgs a{};
     a.H = p.H; a.n = p.n; a.d = p.d; a.dv = p.dv; a.w = p.w; a.nc = p.nc;
-    a.ridge = p.ridge; a.normalize = p.normalize; a.carries_only = p.carries_only;
+    a.ridge = p.ridge; a.normalize = p.normalize; a.carries_only = p.carries_only; a.own_prefix = p.own_prefix;
     a.q = p.q; a.k = p.k; a.v = p.v; a.out = p.out; a.den = p.den;
     a.init = p.init; a.fin = p.fin; a.gam = p.gam;
     a.ws.S = reinterpret_cast<float *>(base + L.S);

@@ -338,6 +338,7 @@ hla_status forward_impl(const hla_params *p, const void *q, const void *k, const
     } else {
         fp.ws = data;
         fp.ws_bytes = workspace_bytes - hla::kCtrlBytes - area;
+        fp.own_prefix = 1;  // nothing reads the slots after this call
         e = hla::generic_forward(fp, stream);
     }
     if (e != hipSuccess) return fail(HLA_ERR_DEVICE, "forward launch: %s", hipGetErrorString(e));

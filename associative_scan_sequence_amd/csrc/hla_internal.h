@@ -37,6 +37,7 @@ struct FwdProblem {
     void *ws;
     size_t ws_bytes;
     int carries_only;  // generic path: stop after the carries and U (no out, den or final state)
+    int own_prefix;    // generic path: the slots need not hold prefixes afterwards (a forward call)
 };
 
 // Every forward workspace starts with a control block of kCtrlBytes: words
