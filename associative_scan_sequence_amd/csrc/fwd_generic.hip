@@ -28,6 +28,8 @@
 //                 n > 0) the scans write slot 0's zeros themselves
 //   k_chunk_sums  K^T diag(f) K, Q^T diag(f) V, Q^T f     -> slot c+1
 //   k_prefix      per head, elementwise: slot c+1 = rho^p slot c + slot c+1
+//                 (not launched for a forward call with at most 16 chunks at
+//                 d, dv <= 32: the kernels below then sum the slots, prefix_of)
 //   k_chunk_uz    A, U (kept for the output pass), U^T diag(f^2) V, U^T f^2
 //   k_chunk_out   P, num, den, ratio
 //   k_final       per head: final (S, C, m), G = S C - X, h = S m - y, rho
