@@ -65,10 +65,6 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void k_zero_words(uint32_t *p, size_t n) {
-    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
-        p[i] = 0u;
-}
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -107,11 +103,11 @@ __device__ __forceinline__ float bf16_word(const u32x4 &w, int e) {  // element 
     return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
 }
 
-// partial sums over token ranges of g^(n-1-t) q_t (for m_n): thread (rows
+// partial sum over token range sp of g^(n-1-t) q_t (for m_n): thread (rows
 // tid/8 + 32i, columns 8 (tid % 8) ..), its loads issued together
-__global__ __launch_bounds__(256) void k_msum(const uint16_t *q, int n, int H, GammaTab gam, float *mpart) {
-    __shared__ float red[32][kBw + 1];
-    const int bh = blockIdx.x, sp = blockIdx.y, cg = threadIdx.x & 7, tr = threadIdx.x >> 3;
+__device__ __forceinline__ void msum_block(const uint16_t *q, int n, int H, GammaTab gam, float *mpart, int bh, int sp,
+                                           float (*red)[kBw + 1]) {
+    const int cg = threadIdx.x & 7, tr = threadIdx.x >> 3;
     const float lg = log2f(head_gamma(gam, bh % H));
     const int per = (n + kMSplits - 1) / kMSplits, t0 = sp * per, t1 = min(n, t0 + per);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -139,6 +135,22 @@ __global__ __launch_bounds__(256) void k_msum(const uint16_t *q, int n, int H, G
         for (int i = 0; i < 32; ++i) sum += red[i][threadIdx.x];
         mpart[(static_cast<size_t>(bh) * kMSplits + sp) * kBw + threadIdx.x] = sum;
     }
+}
+
+// One launch clears the control block and the maps' flags (blocks from
+// nsum on, a grid-stride fill) and, when the final state has a gradient,
+// forms the query sums (the first nsum = BH kMSplits blocks, head-major):
+// the two touch disjoint words and both finish before the first map.
+__global__ __launch_bounds__(256) void k_clear_msum(uint32_t *p, size_t words, const uint16_t *q, int n, int H,
+                                                    GammaTab gam, float *mpart, int nsum) {
+    __shared__ float red[32][kBw + 1];
+    const int b = blockIdx.x;
+    if (b < nsum) {
+        msum_block(q, n, H, gam, mpart, b / kMSplits, b % kMSplits, red);
+        return;
+    }
+    const size_t stride = static_cast<size_t>(gridDim.x - nsum) * 256;
+    for (size_t i = static_cast<size_t>(b - nsum) * 256 + threadIdx.x; i < words; i += stride) p[i] = 0u;
 }
 
 typedef float Lmat[kBw][kBw];  // a 64 x 64 matrix in LDS
@@ -301,10 +313,10 @@ __global__ __launch_bounds__(256) void k_shard_prep(ShardArgs a) {
 // 64-token block, wave w forms features 16w.. on the MFMA as (M x^T)^T, so
 // that a lane holds four consecutive features of one token (v and q are
 // exact bf16, D_C enters as a bf16 pair).
-__global__ __launch_bounds__(256) void k_shard_corr(const uint16_t *q, const uint16_t *v, int n, int H, GammaTab gam,
-                                                    const float *dc, const float *dcT, const float *dm, float *dq,
-                                                    float *dv) {
-    const int bh = blockIdx.x, tb0 = blockIdx.y * kBw, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+__device__ __forceinline__ void corr_block(const uint16_t *q, const uint16_t *v, int n, int H, GammaTab gam,
+                                           const float *dc, const float *dcT, const float *dm, float *dq, float *dv,
+                                           int bh, int tb0) {
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int r = l & 15, g4 = l >> 4, c0 = 16 * wave;
     const float lg = log2f(head_gamma(gam, bh % H));
     const size_t mo = static_cast<size_t>(bh) * kMat, head = static_cast<size_t>(bh) * n;
@@ -342,13 +354,12 @@ __global__ __launch_bounds__(256) void k_shard_corr(const uint16_t *q, const uin
 }
 
 // The initial state's gradient (see the header) from M_W, M_K and the folded
-// terms, per head (blockIdx.x) and job (blockIdx.y):
+// terms, per head and job:
 //   job 0: dS = g M_K + g^2 C_0 M_W + m_0 dY'_0^T
 //   job 1: dC = g^n D_C + g^2 S_0 M_W^T, dG = -g^2 M_W^T, dm = g^n D_m + S_0 dY'_0, dh = -dY'_0
-__global__ __launch_bounds__(256) void k_shard_finish(ShardArgs a, hla_state dinit) {
-    __shared__ Lmat L[2];
-    __shared__ float dyv[kBw];
-    const int bh = blockIdx.x, job = blockIdx.y, tid = threadIdx.x;
+__device__ __forceinline__ void finish_block(const ShardArgs &a, const hla_state &dinit, int bh, int job, Lmat *L,
+                                             float *dyv) {
+    const int tid = threadIdx.x;
     const Blk b = blk_of(tid);
     const float g = head_gamma(a.gam, bh % a.H), lg = log2f(g);
     const float g2 = g * g, gn = exp2f(static_cast<float>(a.n) * lg), g2n = gn * gn;
@@ -406,6 +417,21 @@ __global__ __launch_bounds__(256) void k_shard_finish(ShardArgs a, hla_state din
     }
 }
 
+__global__ __launch_bounds__(256) void k_shard_corr(const uint16_t *q, const uint16_t *v, int n, int H, GammaTab gam,
+                                                    const float *dc, const float *dcT, const float *dm, float *dq,
+                                                    float *dv) {
+    corr_block(q, v, n, H, gam, dc, dcT, dm, dq, dv, blockIdx.x, blockIdx.y * kBw);
+}
+
+// Per head (blockIdx.x) and job (blockIdx.y).  A launch of its own: sharing a
+// grid with the corrections above (its LDS and registers imposed on every
+// block) made the pair 2.4 times slower than the two launches.
+__global__ __launch_bounds__(256) void k_shard_finish(ShardArgs a, hla_state dinit) {
+    __shared__ Lmat L[2];
+    __shared__ float dyv[kBw];
+    finish_block(a, dinit, blockIdx.x, blockIdx.y, L, dyv);
+}
+
 BwdLaLayout bwd_la_layout(int BH, int n) {
     const size_t pair = static_cast<size_t>(BH) * n * kBw * sizeof(uint16_t);
     BwdLaLayout L{};
@@ -461,10 +487,21 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
     auto pair = [&](size_t off) { return reinterpret_cast<uint16_t *>(base + off); };
     uint16_t *uh = pair(L.uh), *ul = pair(L.ul), *wh = pair(L.wh), *wl = pair(L.wl);
     // the control block and both maps' flags start clear (every launch below
-    // then leaves them valid for the next)
+    // then leaves them valid for the next); with a final-state gradient the
+    // same launch forms the decayed query sums
+    const bool states = f.init.S != nullptr || p.dfinal.S != nullptr || p.dinit.S != nullptr;
+    const bool ini = f.init.S != nullptr, fin = p.dfinal.S != nullptr, dini = p.dinit.S != nullptr;
+    ShardArgs sh{};
+    sh.H = f.H; sh.n = f.n; sh.gam = f.gam;
+    if (ini) sh.init = f.init;
+    if (fin) sh.dfin = p.dfinal;
+    sh.b = shard_bufs(base + L.state, BH);
+    const uint16_t *q16 = static_cast<const uint16_t *>(f.q), *v16 = static_cast<const uint16_t *>(f.v);
     const size_t words = (kCtrlBytes + 2 * fb) / sizeof(uint32_t);
-    hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
-                       dim3(256), 0, st, ctrl, words);
+    const int nsum = fin ? BH * kMSplits : 0;
+    const size_t zb = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+    hipLaunchKernelGGL(k_clear_msum, dim3(static_cast<unsigned>(nsum + zb)), dim3(256), 0, st, ctrl, words, q16, f.n,
+                       f.H, f.gam, sh.b.mpart, nsum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     auto map = [&](bool rev, bool gsq) {
@@ -473,7 +510,6 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
         m.rev = rev; m.gsq = gsq;
         return m;
     };
-    const bool states = f.init.S != nullptr || p.dfinal.S != nullptr || p.dinit.S != nullptr;
     if (!states) {
         // W = LA^rev (V, dO, Q; g^2), as a pair
         LaProblem w = map(true, true);
@@ -494,21 +530,11 @@ hipError_t la_backward(const BwdProblem &p, hipStream_t st) {
     }
 
     // ---- with states (the header's second identity) ----
-    const bool ini = f.init.S != nullptr, fin = p.dfinal.S != nullptr, dini = p.dinit.S != nullptr;
-    ShardArgs sh{};
-    sh.H = f.H; sh.n = f.n; sh.gam = f.gam;
-    if (ini) sh.init = f.init;
-    if (fin) sh.dfin = p.dfinal;
-    sh.b = shard_bufs(base + L.state, BH);
-    const uint16_t *q16 = static_cast<const uint16_t *>(f.q), *v16 = static_cast<const uint16_t *>(f.v);
     // U from S_0 (its final carry S_n), and C_n from a map that forms no output
     LaProblem u = map(false, false);
     u.q = f.q; u.k = f.k; u.v = f.k; u.mode = 2; u.oh = uh; u.ol = ul;
     u.init = ini ? f.init.S : nullptr;
     if (fin) {
-        hipLaunchKernelGGL(k_msum, dim3(static_cast<unsigned>(BH), kMSplits), dim3(256), 0, st, q16, f.n, f.H, f.gam,
-                           sh.b.mpart);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
         u.fin = sh.b.sfin;
         LaProblem cn = map(false, false);
         cn.q = f.q; cn.k = f.q; cn.v = f.v; cn.mode = 3; cn.init = ini ? f.init.C : nullptr; cn.fin = sh.b.cfin;
