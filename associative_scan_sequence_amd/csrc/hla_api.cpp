@@ -132,7 +132,7 @@ hla_status check_common(int H, int d, int dv, int dtype, const float *gamma, flo
 int default_chunk(int d) { return d <= 16 ? 16 : (d <= 32 ? 32 : (d <= 64 ? 64 : 128)); }
 
 // Kernel path for a forward call.  init/fin/den only matter for the choice.
-enum class FwdPath { Generic, Fast64, Fused128 };
+enum class FwdPath { Generic, Fast64, Fused128, Small };
 
 
 struct Geometry {
@@ -165,6 +165,7 @@ FwdPath choose_path(const hla_params *p, const Geometry &geo, const hla_state *i
     if (fin) fp.fin = *fin;
     if (hla::fast64_supported(fp)) return FwdPath::Fast64;
     if (hla::fused128_supported(fp)) return FwdPath::Fused128;
+    if (hla::small_supported(fp)) return FwdPath::Small;
     return FwdPath::Generic;
 }
 
@@ -191,6 +192,8 @@ size_t workspace_need(const hla_params *p, const Geometry &geo) {
     if (p->dtype == HLA_BF16 && p->d == 64 && p->dv == 64 && geo.w == 64 && p->n > 0)
         fused = hla::fast64_data_bytes(BH, p->n);
     if (p->dtype == HLA_BF16 && p->d == 128 && p->dv == 128 && p->n > 0) fused = hla::fused128_data_bytes(BH, p->n);
+    const size_t small = hla::small_data_bytes(BH, p->n, p->d);  // never above gen; kept for clarity
+    if (small > fused) fused = small;
     return hla::kCtrlBytes + flag_area(p, geo) + (gen > fused ? gen : fused);
 }
 
@@ -204,6 +207,7 @@ PathNeed path_need(const hla_params *p, const Geometry &geo, FwdPath path) {
     if (path == FwdPath::Fast64) return PathNeed{hla::fast64_flag_bytes(BH, p->n), hla::fast64_data_bytes(BH, p->n)};
     if (path == FwdPath::Fused128)
         return PathNeed{hla::fused128_flag_bytes(BH, p->n), hla::fused128_data_bytes(BH, p->n)};
+    if (path == FwdPath::Small) return PathNeed{0, hla::small_data_bytes(BH, p->n, p->d)};
     return PathNeed{0, hla::generic_workspace_bytes(BH, p->n, p->d, p->dv, geo.w)};
 }
 
@@ -335,6 +339,8 @@ hla_status forward_impl(const hla_params *p, const void *q, const void *k, const
         e = hla::fast64_forward(fp, ctrl, flags, data, stream);
     } else if (path == FwdPath::Fused128) {
         e = hla::fused128_forward(fp, ctrl, flags, data, stream);
+    } else if (path == FwdPath::Small) {
+        e = hla::small_forward(fp, data, stream);
     } else {
         fp.ws = data;
         fp.ws_bytes = workspace_bytes - hla::kCtrlBytes - area;

@@ -131,6 +131,14 @@ size_t fused128_flag_bytes(int BH, int n);
 size_t fused128_data_bytes(int BH, int n);
 hipError_t fused128_forward(const FwdProblem &p, uint32_t *ctrl, uint32_t *flags, void *data, hipStream_t s);
 
+// Two-launch forward for short sequences (fwd_small.hip): n <= 256, d and dv
+// in {16, 32}, fp32 or bf16, any decays, no ridge, denominator,
+// normalisation or states (any chunk setting: the result does not depend on
+// it).  Its data is the fp32 map U, [BH][n][d].
+bool small_supported(const FwdProblem &p);
+size_t small_data_bytes(int BH, int n, int d);
+hipError_t small_forward(const FwdProblem &p, void *data, hipStream_t s);
+
 struct DecodeProblem {
     int B, H, d, dv;
     hla_dtype dtype;

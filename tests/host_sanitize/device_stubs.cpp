@@ -43,6 +43,9 @@ bool fused128_supported(const FwdProblem &) { return false; }
 size_t fused128_flag_bytes(int BH, int n) { return fixed_size(BH, n, 1, 1); }
 size_t fused128_data_bytes(int BH, int n) { return fixed_size(BH, n, 128, 128); }
 hipError_t fused128_forward(const FwdProblem &, uint32_t *, uint32_t *, void *, hipStream_t) { reached("fused128_forward"); }
+bool small_supported(const FwdProblem &) { return false; }
+size_t small_data_bytes(int BH, int n, int d) { return fixed_size(BH, n, d, 1); }
+hipError_t small_forward(const FwdProblem &, void *, hipStream_t) { reached("small_forward"); }
 hipError_t decode_step(const DecodeProblem &, hipStream_t) { reached("decode_step"); }
 hipError_t decode_step_mq(const DecodeMqProblem &, hipStream_t) { reached("decode_step_mq"); }
 hipError_t key_moment_pack(int, int, const float *, float *, bool, hipStream_t) { reached("key_moment_pack"); }
