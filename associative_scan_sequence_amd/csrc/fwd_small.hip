@@ -2,7 +2,8 @@
 // (n <= 256, d and dv in {16, 32}) as two causal first-order maps, with no
 // chunks and no carries.
 //
-// Higher-order Linear Attention, paperlayer.ai summary sec. 4: the masked
+// Higher-order Linear Attention, paperlayer.ai summary sec. 3.1 (the mask
+// keeps j <= t) and sec. 4.3 (a fixed decay attenuates each step): the masked
 // numerator q_t^T (S_t C_t - G_t) keeps, of all pairs of the key moment and
 // the query-value moment, those whose key comes no later than its query:
 // it is the sum of (q_t . k_i)(k_i . q_j) v_j over i <= j <= t, each term

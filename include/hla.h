@@ -124,7 +124,17 @@ typedef struct {
  * (about 4M polls, seconds) gives up and adds one to word 3, and the carry
  * it waited for is made NaN: every output that depends on it (that
  * segment's and the later segments' of the head) is then NaN, never a wrong
- * number. */
+ * number.
+ *
+ * Short sequences (n <= 256, d and dv in {16, 32}, fp32 or bf16, any decays,
+ * no ridge, den, normalisation or states) take neither the chunks nor the
+ * flags: the masked numerator is the sum of (q_t . k_i)(k_i . q_j) v_j over
+ * i <= j <= t, decayed by g^(2t - i - j) (the equivalent form above: [SUM] sec. 3.1 and
+ * 4.3), computed as two
+ * direct causal maps, U_j = sum over i <= j of g^(j-i) (q_j . k_i) k_i and
+ * out_t = sum over j <= t of g^(2(t-j)) (q_t . U_j) v_j, in fp32, with U
+ * (B*H*n*d floats) kept in the workspace's data.  The chunk setting does not
+ * change their result. */
 size_t hla_forward_workspace_size(const hla_params *p);
 
 /* Chunk-parallel masked forward ([SUM] sec. 4 and 5: token deltas feed an

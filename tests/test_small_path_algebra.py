@@ -1,7 +1,8 @@
 """The short-sequence forward computes the masked second-order numerator as
 two causal first-order maps (Higher-order Linear Attention, paperlayer.ai
-summary sec. 4: the masked output keeps the pairs of the key moment and the
-query-value moment whose key comes no later than its query).  With
+summary sec. 3.1, the mask, and sec. 4.3, the decay: the masked output keeps
+the pairs of the key moment and the query-value moment whose key comes no
+later than its query).  With
 LA(A, B, C; r)_t = sum over s <= t of r^(t-s) (a_t . b_s) c_s:
 
     U = LA(Q, K, K; g),   out = LA(Q, U, V; g^2).
