@@ -76,6 +76,17 @@ def test_noalloc_d128_then_generic_with_state():
     both(q2, k2, v2, gamma=[0.97, 1.0], return_state=True, return_den=True)
 
 
+def test_noalloc_short_sequences():
+    """The short-sequence path (two direct maps) keeps its fp32 U in the
+    scratch's data: the small fp32 workload, then a smaller bf16 call with
+    other widths and per-head decay."""
+    w = inputs.SMALL_FP32
+    q, k, v = (x.to(DEV) for x in inputs.workload_qkv(w, 102))
+    both(q, k, v)
+    q2, k2, v2 = (x.to(DEV) for x in inputs.qkv(2, 3, 100, 32, 16, torch.bfloat16, seed=103))
+    both(q2, k2, v2, gamma=inputs.gamma_list_fp32([0.9, 1.0, 0.5]))
+
+
 def test_noalloc_generic_state_call_then_one_launch():
     """Calls with other params share the one scratch: a generic-path call (fp32
     inputs, an initial and a final state) keeps its data past the scratch's
