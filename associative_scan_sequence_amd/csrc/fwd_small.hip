@@ -50,8 +50,9 @@ struct Rows {
         }
     }
     // widened to fp32, into LDS rows of stride D + 4: 16-byte aligned, and
-    // the rows 32 apart that 16 lanes of a token read with 16-byte loads
-    // cover the 64 banks once (D = 16: 80 bytes apart; D = 32: 144)
+    // the consecutive rows that 16 consecutive lanes read with 16-byte loads
+    // (lane l reads row l + 64 i) cover the 64 banks once (D = 16: rows 80
+    // bytes apart; D = 32: 144)
     __device__ __forceinline__ void store(int rows, float *dst) const {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
